@@ -1,0 +1,190 @@
+/*
+ * tbe.h -- C ABI of libtbe_hip.so, the MI355X (gfx950) Table Batched
+ * Embedding hot path.
+ *
+ * What the library computes (FBTriton TBE page, "Modernizing Table Batched
+ * Embeddings with FBTriton", sections "Why redesign a sparse operator?",
+ * "Forward", "Backward", "Fewer reads and synchronizations", "Fusion
+ * boundaries"; HugeCTR DistributedSlotSparseEmbeddingHash backward
+ * walkthrough, steps 1 to 5):
+ *
+ *   forward   out[b, c_t + d] = (1/L if mean) * sum_{p in bag(t,b)} S[p] * W_t[I[p], d]
+ *   backward  per touched row r of table t, once:
+ *             g[d] = sum over the row's lookups of S[p] * grad_out[b(p), c_t + d] * (1/L if mean)
+ *             M_t[r] += (sum_d g[d]^2) / D_t
+ *             W_t[r, d] -= lr * g[d] / (sqrt(M_t[r]) + eps)        (exact row-wise Adagrad)
+ *
+ * Conventions shared by every entry point
+ *  - T tables; table t has R_t rows of width D_t (4 <= D_t <= 1024, D_t % 4 == 0),
+ *    sum or mean pooling, weights W_t (device, R_t x D_t row-major, 16-byte
+ *    aligned, one storage type for all tables) and row-wise momentum M_t
+ *    (device, R_t floats).
+ *  - B bags per table, table-major: bag j = t*B + b.  offsets (device, T*B+1
+ *    entries, the index type) are CSR: bag j holds lookups
+ *    [offsets[j], offsets[j+1]); offsets[0] = 0, non-decreasing,
+ *    offsets[T*B] = num_lookups.  indices (device, num_lookups entries) are
+ *    rows of the bag's table.  Empty bags pool to 0.
+ *  - out and grad_out are [B, Dtot] float32 row-major (device, 16-byte
+ *    aligned); table t occupies columns [c_t, c_t + D_t), c_t = sum of the
+ *    earlier D.
+ *  - per_sample_weights (device float32, num_lookups entries) is optional
+ *    (NULL = all ones); each contribution is scaled before grouping by row.
+ *  - Index type: TBE_I32 or TBE_I64 for both indices and offsets.  int32 is
+ *    accepted only while num_lookups < 2^31 and sum_t R_t < 2^31 (the
+ *    linearized row range, FBTriton page, "Forward").
+ *  - stream is a hipStream_t (as void*); every entry point except plan
+ *    creation only enqueues work on it: no allocation, no host
+ *    synchronization, no device-to-host copy.  Counts that only the device
+ *    knows (runs, long runs, chunks) stay in the workspace (FBTriton page,
+ *    "Fewer reads and synchronizations").
+ *  - Ownership: the caller owns every device buffer (weights, momentum,
+ *    indices, offsets, per-sample weights, out, grad_out, workspace).  The
+ *    plan owns only its small metadata.  A plan is immutable after creation
+ *    and may be shared by calls on several streams; a workspace serves one
+ *    call sequence at a time.
+ *  - Errors: every function returns TBE_OK or a negative code, detected on
+ *    the host before anything is enqueued (except TBE_E_HIP, reported from
+ *    the launch).  Nothing is printed.  Input contract violations on the
+ *    device (offsets not monotone, an index outside [0, R_t)) are not checked
+ *    (bounds checks are off by default on the pages) and give undefined
+ *    results.
+ */
+#ifndef TBE_H
+#define TBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define TBE_OK 0
+#define TBE_E_ARG (-1)          /* null / misaligned pointer, negative size, bad enum */
+#define TBE_E_UNSUPPORTED (-2)  /* D limits, table count, histogram forced on an ineligible shape */
+#define TBE_E_WORKSPACE (-3)    /* workspace too small or not 256-byte aligned */
+#define TBE_E_RANGE (-4)        /* int32 indices with num_lookups or sum R_t >= 2^31; sizes >= 2^32 */
+#define TBE_E_HIP (-5)          /* the HIP runtime reported an error */
+#define TBE_E_ALLOC (-6)        /* plan creation could not allocate */
+
+/* weight storage types */
+#define TBE_F32 0
+#define TBE_F16 1
+#define TBE_BF16 2
+/* index and offset types */
+#define TBE_I32 0
+#define TBE_I64 1
+/* pooling */
+#define TBE_SUM 0
+#define TBE_MEAN 1
+
+/* tbe_forward flags */
+#define TBE_FWD_NO_HIST 0x1u       /* never take the small-table histogram path */
+#define TBE_FWD_REQUIRE_HIST 0x2u  /* fail with TBE_E_UNSUPPORTED unless the histogram path applies */
+/* tbe_backward_rowwise_adagrad flags */
+#define TBE_BWD_PREPROCESSED 0x1u  /* the workspace already holds tbe_preprocess of these inputs */
+#define TBE_BWD_FUSED_LONG 0x2u    /* long runs: fused fence + countdown instead of a second launch */
+
+typedef struct tbe_plan tbe_plan;
+
+/* Byte offsets, inside a workspace, of the preprocessing results (for tests
+ * and tools; the layout depends only on the plan, B and num_lookups).
+ * Linear row keys are uint32: key = key_base[t] + row, with tables ordered by
+ * D bucket, then by table id (tbe_plan_key_bases).  Positions and bag ids are
+ * uint32. */
+typedef struct {
+  size_t sorted_key;   /* num_lookups keys, ascending */
+  size_t sorted_pos;   /* num_lookups lookup positions, stable (ties ascending) */
+  size_t bag;          /* num_lookups bag ids j, indexed by lookup position */
+  size_t run_start;    /* U+1 entries: first sorted slot of each run, then num_lookups */
+  size_t run_key;      /* U keys, one per run */
+  size_t short_task;   /* n_short uint32x4 {start, len, row, table}: runs with SL < 256 */
+  size_t long_task;    /* n_long uint32x4 {start, len, row, table}: runs with SL >= 256 */
+  size_t long_cbeg;    /* n_long first chunk index of each long run */
+  size_t chunk_task;   /* n_chunks uint32x4 {start, len, table, long index}: 256-lookup chunks */
+  size_t counters;     /* uint32 {U, n_short, n_long, n_chunks,
+                          short_begin[nb+1], long_begin[nb+1], chunk_begin[nb+1]} per D bucket */
+  size_t total;        /* bytes needed */
+  int32_t num_buckets; /* nb */
+} tbe_ws_views;
+
+/* Create a plan over T tables (host arrays of length T; weights[t] and
+ * momentum[t] are device pointers).  Tables are bucketed by next_pow2(D_t)
+ * (FBTriton page, "Fewer reads and synchronizations").  The only entry point
+ * that allocates (a few KB of device metadata) and synchronizes.
+ * Errors: TBE_E_ARG, TBE_E_UNSUPPORTED (T > 4096, D outside [4, 1024] or not
+ * a multiple of 4, R_t < 1), TBE_E_RANGE (sum R_t >= 2^32), TBE_E_ALLOC. */
+int tbe_plan_create(tbe_plan** out, int32_t T, const int64_t* rows, const int32_t* dims,
+                    const int32_t* pooling, int32_t wdtype, void* const* weights,
+                    float* const* momentum);
+
+/* Free the plan's metadata; never touches caller buffers.  NULL is a no-op. */
+int tbe_plan_destroy(tbe_plan* plan);
+
+/* Host copy of the linear key base of each table (T entries). */
+int tbe_plan_key_bases(const tbe_plan* plan, int64_t* key_base);
+
+/* Bytes of workspace needed for B bags per table and num_lookups lookups.
+ * The bound uses only host-known sizes (runs <= N, chunks <= N/256 + long runs). */
+int tbe_workspace_size(const tbe_plan* plan, int64_t B, int64_t num_lookups, size_t* bytes);
+
+/* Offsets of the preprocessing results inside such a workspace. */
+int tbe_workspace_views(const tbe_plan* plan, int64_t B, int64_t num_lookups,
+                        tbe_ws_views* out);
+
+/* Forward pooling (FBTriton page, "Forward"; HugeCTR forward_sum / mean).
+ * Writes every element of out[B, Dtot].  Accumulates in float32 for 16-bit
+ * weights and in float64 for float32 weights.  A single table with at most
+ * 64 rows, 64 <= D <= 128, float16 weights, no per-sample weights and an
+ * average bag length >= 64 takes the histogram path (row counts of 16 bags
+ * times the table on the matrix cores) unless TBE_FWD_NO_HIST is set. */
+int tbe_forward(const tbe_plan* plan, int64_t B, int32_t itype, const void* indices,
+                const void* offsets, int64_t num_lookups, const float* per_sample_weights,
+                float* out, uint32_t flags, void* stream);
+
+/* Backward preprocessing only (FBTriton page, "Backward": transposition,
+ * sort, run-length encoding; classification of runs at SL 256 and task-list
+ * compaction with device-resident counts).  Fills the workspace for a later
+ * tbe_backward_rowwise_adagrad(..., TBE_BWD_PREPROCESSED) with the same
+ * indices and offsets, in stream order.  ws: device, >= tbe_workspace_size
+ * bytes, 256-byte aligned. */
+int tbe_preprocess(const tbe_plan* plan, int64_t B, int32_t itype, const void* indices,
+                   const void* offsets, int64_t num_lookups, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/* Backward with exact row-wise Adagrad applied once per touched row.
+ * Preprocesses unless TBE_BWD_PREPROCESSED, then updates runs with SL < 256
+ * in one owner pass and runs with SL >= 256 through 256-lookup chunk partial
+ * sums plus an update pass (or, with TBE_BWD_FUSED_LONG, a device-scope fence
+ * and countdown so the last chunk of a run updates it; both give bit-identical
+ * weights).  Weights and momentum of touched rows are updated in place;
+ * untouched rows are not written.  debug_row_updates (device, nullable): one
+ * uint32 per linear key, incremented once per row update. */
+int tbe_backward_rowwise_adagrad(const tbe_plan* plan, int64_t B, int32_t itype,
+                                 const void* indices, const void* offsets, int64_t num_lookups,
+                                 const float* per_sample_weights, const float* grad_out, float lr,
+                                 float eps, void* ws, size_t ws_bytes, uint32_t flags,
+                                 uint32_t* debug_row_updates, void* stream);
+
+/* Kernel timing for benchmarks and tools, off by default.  While enabled,
+ * every kernel launch of the library is bracketed by two HIP events recorded
+ * on the stream it is launched on (adds a little enqueue work per launch).
+ * tbe_prof_read waits for the recorded events, writes per-kernel-family
+ * totals (name, launches, summed milliseconds) for up to max_kernels
+ * families, sets *count to the number of families seen, and clears the
+ * records.  names: max_kernels x TBE_PROF_NAME_LEN bytes, NUL-terminated.
+ * Both are host-side calls; tbe_prof_read synchronizes on the events. */
+#define TBE_PROF_NAME_LEN 32
+int tbe_prof_enable(int enable);
+int tbe_prof_read(int32_t max_kernels, char* names, int64_t* launches, double* total_ms,
+                  int32_t* count);
+
+/* Static text for a status code. */
+const char* tbe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TBE_H */

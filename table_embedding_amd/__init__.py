@@ -1,0 +1,87 @@
+"""MI355X-native Table Batched Embedding (TBE) hot path.
+
+The work runs in libtbe_hip.so (hand-written HIP for gfx950, C ABI in
+include/tbe.h).  This package holds its ctypes binding (`_lib`, same names
+as the C entry points) and `TBE`, a small owner of one plan, its tables'
+tensors and a workspace.  PyTorch provides device memory and streams only.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import torch
+
+from ._lib import (  # noqa: F401
+    EXPORTS, LIB_PATH, TBE_BF16, TBE_BWD_FUSED_LONG, TBE_BWD_PREPROCESSED, TBE_E_ALLOC,
+    TBE_E_ARG, TBE_E_HIP, TBE_E_RANGE, TBE_E_UNSUPPORTED, TBE_E_WORKSPACE, TBE_F16, TBE_F32,
+    TBE_FWD_NO_HIST, TBE_FWD_REQUIRE_HIST, TBE_I32, TBE_I64, TBE_MEAN, TBE_OK, TBE_SUM,
+    TBEError, lib, tbe_backward_rowwise_adagrad, tbe_forward, tbe_plan_create,
+    tbe_plan_destroy, tbe_plan_key_bases, tbe_preprocess, tbe_prof_enable, tbe_prof_read,
+    tbe_status_string,
+    tbe_workspace_size, tbe_workspace_views)
+
+
+class TBE:
+    """One plan over caller-owned tables plus a reusable workspace.
+
+    weights[t]: device [R_t, D_t] float32/float16/bfloat16; momentum[t]: device
+    [R_t] float32.  Both are updated in place by `backward`.
+    """
+
+    def __init__(self, rows: Sequence[int], dims: Sequence[int], pooling: Sequence[int],
+                 weights: Sequence[torch.Tensor], momentum: Sequence[torch.Tensor]):
+        self.rows = [int(r) for r in rows]
+        self.dims = [int(d) for d in dims]
+        self.pooling = [int(p) for p in pooling]
+        self.weights = list(weights)
+        self.momentum = list(momentum)
+        self.T = len(self.rows)
+        self.dtot = sum(self.dims)
+        self.plan = tbe_plan_create(self.rows, self.dims, self.pooling, self.weights,
+                                    self.momentum)
+        self._ws: Optional[torch.Tensor] = None
+
+    def close(self):
+        if self.plan is not None:
+            tbe_plan_destroy(self.plan)
+            self.plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def key_bases(self):
+        return tbe_plan_key_bases(self.plan, self.T)
+
+    def workspace(self, B: int, num_lookups: int) -> torch.Tensor:
+        """A workspace large enough for B bags and num_lookups lookups (grown on demand)."""
+        need = tbe_workspace_size(self.plan, B, num_lookups)
+        if self._ws is None or self._ws.numel() < need:
+            dev = self.weights[0].device
+            self._ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        return self._ws
+
+    def forward(self, B: int, indices: torch.Tensor, offsets: torch.Tensor,
+                per_sample_weights: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None, flags: int = 0) -> torch.Tensor:
+        if out is None:
+            out = torch.empty((B, self.dtot), dtype=torch.float32, device=offsets.device)
+        tbe_forward(self.plan, B, indices, offsets, indices.numel(), per_sample_weights, out,
+                    flags)
+        return out
+
+    def preprocess(self, B: int, indices: torch.Tensor, offsets: torch.Tensor) -> torch.Tensor:
+        ws = self.workspace(B, indices.numel())
+        tbe_preprocess(self.plan, B, indices, offsets, indices.numel(), ws)
+        return ws
+
+    def backward(self, B: int, indices: torch.Tensor, offsets: torch.Tensor,
+                 per_sample_weights: Optional[torch.Tensor], grad_out: torch.Tensor,
+                 lr: float, eps: float, flags: int = 0,
+                 debug_row_updates: Optional[torch.Tensor] = None) -> None:
+        ws = self.workspace(B, indices.numel())
+        tbe_backward_rowwise_adagrad(self.plan, B, indices, offsets, indices.numel(),
+                                     per_sample_weights, grad_out, lr, eps, ws, flags,
+                                     debug_row_updates)

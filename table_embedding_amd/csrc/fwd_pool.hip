@@ -1,0 +1,141 @@
+// Generic forward gather-pool (FBTriton TBE page, "Forward": each bag gathers
+// its indexed rows and pools them; 16-bit weights accumulate in float32 and
+// float32 weights in float64; tables are bucketed by next_pow2(D) so narrow
+// tables do not idle lanes sized for the widest one, section "Fewer reads and
+// synchronizations").
+//
+// Lane mapping: one subgroup of `lpr` lanes per bag; lane k covers columns
+// k*VEC + c*lpr*VEC (c < NC) with 16-byte (VEC elements) row loads, so a row
+// of the bucket width is read by consecutive lanes in one coalesced sweep.
+// Eight rows are kept in flight per lane (independent index loads, then
+// independent row loads) to hide HBM latency; the sum is taken in lookup
+// order.  Memory-bound: every lookup moves one index and one row.
+#include "tbe_common.h"
+
+namespace tbe {
+namespace {
+
+constexpr int kInFlight = 8;
+
+template <int WD>
+struct Acc {
+  using T = float;
+};
+template <>
+struct Acc<WD_F32> {
+  using T = double;
+};
+
+template <int WD, int VEC, int NC>
+__global__ __launch_bounds__(kThreads) void fwd_pool_kernel(FwdArgs a, BucketDev bk) {
+  using AT = typename Acc<WD>::T;
+  const uint32_t lpr = bk.lpr;
+  const uint32_t lane_in = threadIdx.x & (lpr - 1);
+  const uint64_t sg = ((uint64_t)blockIdx.x * kThreads + threadIdx.x) >> bk.lpr_log2;
+  const uint64_t nbags = (uint64_t)bk.ntables * (uint64_t)a.B;
+  if (sg >= nbags) return;
+  const uint32_t slot = (uint32_t)(sg / (uint64_t)a.B);
+  const int64_t b = (int64_t)(sg - (uint64_t)slot * (uint64_t)a.B);
+  const uint32_t t = bk.tables[slot];
+  const TableDev td = a.tables[t];
+  const int64_t j = (int64_t)t * a.B + b;
+  const int64_t lo = load_idx(a.offsets, a.itype, j);
+  const int64_t hi = load_idx(a.offsets, a.itype, j + 1);
+  const uint32_t D = td.dim;
+
+  AT acc[NC][VEC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[c][v] = AT(0);
+
+  bool act[NC];
+  uint32_t colc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    colc[c] = (lane_in + (uint32_t)c * lpr) * VEC;
+    act[c] = colc[c] < D;
+  }
+
+  int64_t p = lo;
+  for (; p + kInFlight <= hi; p += kInFlight) {
+    int64_t row[kInFlight];
+    float s[kInFlight];
+#pragma unroll
+    for (int k = 0; k < kInFlight; ++k) {
+      row[k] = load_idx(a.indices, a.itype, p + k);
+      s[k] = a.psw ? a.psw[p + k] : 1.0f;
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (!act[c]) continue;
+      float v[kInFlight][VEC];
+#pragma unroll
+      for (int k = 0; k < kInFlight; ++k) load_w<WD, VEC>(td.w, row[k] * D + colc[c], v[k]);
+#pragma unroll
+      for (int k = 0; k < kInFlight; ++k)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[c][e] += AT(s[k]) * AT(v[k][e]);
+    }
+  }
+  for (; p < hi; ++p) {
+    const int64_t row = load_idx(a.indices, a.itype, p);
+    const float s = a.psw ? a.psw[p] : 1.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (!act[c]) continue;
+      float v[VEC];
+      load_w<WD, VEC>(td.w, row * D + colc[c], v);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[c][e] += AT(s) * AT(v[e]);
+    }
+  }
+
+  const bool mean = td.pooling == POOL_MEAN && hi > lo;
+  const AT L = AT(hi - lo);
+  float* orow = a.out + b * (int64_t)a.dtot + td.col;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (!act[c]) continue;
+    float o[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) o[e] = (float)(mean ? acc[c][e] / L : acc[c][e]);
+    store_f32<VEC>(orow + colc[c], o);
+  }
+}
+
+template <int WD, int VEC, int NC>
+hipError_t launch(const FwdArgs& a, const BucketDev& bk, hipStream_t s) {
+  const uint64_t nbags = (uint64_t)bk.ntables * (uint64_t)a.B;
+  const uint64_t per_block = kThreads / bk.lpr;
+  const uint64_t grid = (nbags + per_block - 1) / per_block;
+  if (grid == 0) return hipSuccess;
+  TBE_LAUNCH("fwd_pool", (fwd_pool_kernel<WD, VEC, NC>), dim3((uint32_t)grid), dim3(kThreads), s,
+             a, bk);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_forward_bucket(const FwdArgs& a, const BucketDev& bk, int wd, int vec, int nc,
+                                 hipStream_t s) {
+#define TBE_FWD_CASE(W, V, N) \
+  if (wd == W && vec == V && nc == N) return launch<W, V, N>(a, bk, s);
+  TBE_FWD_CASE(WD_F32, 4, 1)
+  TBE_FWD_CASE(WD_F32, 4, 2)
+  TBE_FWD_CASE(WD_F32, 4, 4)
+  TBE_FWD_CASE(WD_F16, 4, 1)
+  TBE_FWD_CASE(WD_F16, 4, 2)
+  TBE_FWD_CASE(WD_F16, 4, 4)
+  TBE_FWD_CASE(WD_F16, 8, 1)
+  TBE_FWD_CASE(WD_F16, 8, 2)
+  TBE_FWD_CASE(WD_BF16, 4, 1)
+  TBE_FWD_CASE(WD_BF16, 4, 2)
+  TBE_FWD_CASE(WD_BF16, 4, 4)
+  TBE_FWD_CASE(WD_BF16, 8, 1)
+  TBE_FWD_CASE(WD_BF16, 8, 2)
+#undef TBE_FWD_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tbe

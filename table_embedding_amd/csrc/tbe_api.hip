@@ -1,0 +1,528 @@
+// C-ABI layer of libtbe_hip.so (declared in include/tbe.h): plan metadata,
+// workspace layout, host-side argument checks and the launch sequences of
+// forward, preprocessing and backward.  Every check happens before anything
+// is enqueued; nothing here reads device memory back or synchronizes, except
+// plan creation, which uploads a few KB of metadata.
+#include <algorithm>
+#include <atomic>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "../../include/tbe.h"
+#include "tbe_common.h"
+
+using namespace tbe;
+
+namespace {
+
+struct Bucket {
+  uint32_t width;  // next_pow2(D) of its tables
+  int vec, nc;
+  uint32_t lpr, lpr_log2;
+  std::vector<uint32_t> tables;
+  uint32_t* d_tables;
+};
+
+}  // namespace
+
+struct tbe_plan {
+  int32_t T;
+  int wdtype;
+  std::vector<int64_t> rows;
+  std::vector<int32_t> dims, pooling;
+  std::vector<uint32_t> key_base, col;
+  uint32_t dtot;
+  uint64_t sum_rows;
+  int key_bits;
+  std::vector<Bucket> buckets;
+  uint32_t pstride;
+  TableDev* d_tables;
+  uint32_t* d_order;
+  uint32_t* d_bkb;
+  void* d_mem;
+  int num_cus;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+uint32_t next_pow2(uint32_t x) {
+  uint32_t p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// smallest l with 2^l >= x
+int ilog2(uint64_t x) {
+  int l = 0;
+  while ((1ull << l) < x) ++l;
+  return l;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+WsLayout layout(const tbe_plan* P, int64_t N) {
+  WsLayout L{};
+  const uint64_t n = (uint64_t)N;
+  L.ntiles = (uint32_t)((n + kTile - 1) / kTile);
+  L.max_long = (uint32_t)(n / kLongRun + 1);
+  L.max_chunks = (uint32_t)(n / kChunk + L.max_long + 1);
+  L.pstride = P->pstride;
+  L.npass = std::max(1, (P->key_bits + kRadixBits - 1) / kRadixBits);
+  L.final_in_b = L.npass % 2;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes ? bytes : 1);
+    return o;
+  };
+  L.key_a = take(n * 4);
+  L.key_b = take(n * 4);
+  L.val_a = take(n * 4);
+  L.val_b = take(n * 4);
+  L.bag = take(n * 4);
+  L.hist = take((size_t)256 * L.ntiles * 4);
+  L.rowtot = take(256 * 4);
+  L.tile_cnt = take((size_t)L.ntiles * 4);
+  L.tile_cls = take((size_t)3 * L.ntiles * 4);
+  L.run_start = take((n + 1) * 4);
+  L.run_key = take(n * 4);
+  L.short_task = take(n * 16);
+  L.long_task = take((size_t)L.max_long * 16);
+  L.long_cbeg = take((size_t)L.max_long * 4);
+  L.remaining = take((size_t)L.max_long * 4);
+  L.chunk_task = take((size_t)L.max_chunks * 16);
+  L.partial = take((size_t)L.max_chunks * L.pstride * 4);
+  L.counters = take((size_t)(kCntBegins + 3 * (P->buckets.size() + 1)) * 4);
+  L.total = off;
+  return L;
+}
+
+// Shared checks of the per-call lookup arguments.
+int check_lookups(const tbe_plan* P, int64_t B, int32_t itype, const void* indices,
+                  const void* offsets, int64_t N) {
+  if (!P || B < 0 || N < 0) return TBE_E_ARG;
+  if (itype != TBE_I32 && itype != TBE_I64) return TBE_E_ARG;
+  const size_t isz = itype == TBE_I32 ? 4 : 8;
+  if (!offsets || !aligned(offsets, isz)) return TBE_E_ARG;
+  if (N > 0 && (!indices || !aligned(indices, isz))) return TBE_E_ARG;
+  if ((uint64_t)P->T * (uint64_t)B >= (1ull << 32) - 1) return TBE_E_RANGE;
+  if (N >= (int64_t)(1ll << 31) - 1) return TBE_E_RANGE;
+  if (itype == TBE_I32 && P->sum_rows >= (1ull << 31)) return TBE_E_RANGE;
+  return TBE_OK;
+}
+
+int check_ws(const tbe_plan* P, int64_t N, const void* ws, size_t ws_bytes) {
+  if (!ws || !aligned(ws, kAlign)) return TBE_E_WORKSPACE;
+  if (ws_bytes < layout(P, N).total) return TBE_E_WORKSPACE;
+  return TBE_OK;
+}
+
+bool hist_eligible(const tbe_plan* P, int64_t B, int64_t N, const float* psw) {
+  return P->T == 1 && P->rows[0] <= 64 && P->dims[0] >= 64 && P->dims[0] <= 128 &&
+         P->wdtype == TBE_F16 && psw == nullptr && B > 0 && N >= 64 * B;
+}
+
+int persistent_grid(const tbe_plan* P, uint64_t work_items, uint32_t items_per_block) {
+  const uint64_t need = (work_items + items_per_block - 1) / items_per_block;
+  const uint64_t cap = (uint64_t)P->num_cus * 8;
+  return (int)std::max<uint64_t>(1, std::min(need, cap));
+}
+
+PrepArgs prep_args(const tbe_plan* P, int64_t B, int32_t itype, const void* indices,
+                   const void* offsets, int64_t N, void* ws, const WsLayout* L) {
+  PrepArgs a{};
+  a.tables = P->d_tables;
+  a.bucket_key_begin = P->d_bkb;
+  a.order = P->d_order;
+  a.T = (uint32_t)P->T;
+  a.nb = (uint32_t)P->buckets.size();
+  a.B = B;
+  a.itype = itype;
+  a.indices = indices;
+  a.offsets = offsets;
+  a.N = (uint32_t)N;
+  a.ws = reinterpret_cast<uint8_t*>(ws);
+  a.L = L;
+  a.key_bits = P->key_bits;
+  return a;
+}
+
+// ------------------------------------------------------------ kernel timing
+
+struct ProfRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+
+std::atomic<bool> g_prof_on{false};
+std::mutex g_prof_mu;
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+}  // namespace
+
+namespace tbe {
+
+void prof_begin(hipStream_t s, const char* name) {
+  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  ProfRec r{name, prof_event(), prof_event()};
+  if (!r.start || !r.stop) return;
+  (void)hipEventRecord(r.start, s);
+  g_prof_recs.push_back(r);
+}
+
+void prof_end(hipStream_t s) {
+  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_recs.empty()) (void)hipEventRecord(g_prof_recs.back().stop, s);
+}
+
+}  // namespace tbe
+
+extern "C" {
+
+int tbe_prof_enable(int enable) {
+  g_prof_on.store(enable != 0);
+  return TBE_OK;
+}
+
+int tbe_prof_read(int32_t max_kernels, char* names, int64_t* launches, double* total_ms,
+                  int32_t* count) {
+  if (max_kernels < 0 || !count || (max_kernels > 0 && (!names || !launches || !total_ms)))
+    return TBE_E_ARG;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  std::vector<const char*> keys;
+  std::vector<int64_t> n;
+  std::vector<double> ms;
+  int rc = TBE_OK;
+  for (ProfRec& r : g_prof_recs) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess ||
+        hipEventElapsedTime(&t, r.start, r.stop) != hipSuccess)
+      rc = TBE_E_HIP;
+    size_t k = 0;
+    while (k < keys.size() && std::strcmp(keys[k], r.name) != 0) ++k;
+    if (k == keys.size()) {
+      keys.push_back(r.name);
+      n.push_back(0);
+      ms.push_back(0.0);
+    }
+    n[k] += 1;
+    ms[k] += (double)t;
+    g_prof_pool.push_back(r.start);
+    g_prof_pool.push_back(r.stop);
+  }
+  g_prof_recs.clear();
+  const int m = std::min<int>((int)keys.size(), max_kernels);
+  for (int k = 0; k < m; ++k) {
+    std::strncpy(names + (size_t)k * TBE_PROF_NAME_LEN, keys[k], TBE_PROF_NAME_LEN - 1);
+    names[(size_t)k * TBE_PROF_NAME_LEN + TBE_PROF_NAME_LEN - 1] = 0;
+    launches[k] = n[k];
+    total_ms[k] = ms[k];
+  }
+  *count = (int32_t)keys.size();
+  return rc;
+}
+
+const char* tbe_status_string(int s) {
+  switch (s) {
+    case TBE_OK: return "ok";
+    case TBE_E_ARG: return "invalid argument";
+    case TBE_E_UNSUPPORTED: return "unsupported shape or option";
+    case TBE_E_WORKSPACE: return "workspace too small or misaligned";
+    case TBE_E_RANGE: return "size or index range too large for the index type";
+    case TBE_E_HIP: return "HIP runtime error";
+    case TBE_E_ALLOC: return "allocation failed";
+  }
+  return "unknown status";
+}
+
+int tbe_plan_create(tbe_plan** out, int32_t T, const int64_t* rows, const int32_t* dims,
+                    const int32_t* pooling, int32_t wdtype, void* const* weights,
+                    float* const* momentum) {
+  if (!out) return TBE_E_ARG;
+  *out = nullptr;
+  if (T < 1 || !rows || !dims || !pooling || !weights || !momentum) return TBE_E_ARG;
+  if (wdtype != TBE_F32 && wdtype != TBE_F16 && wdtype != TBE_BF16) return TBE_E_ARG;
+  if (T > kMaxTables) return TBE_E_UNSUPPORTED;
+  uint64_t sum_rows = 0, dtot = 0;
+  for (int t = 0; t < T; ++t) {
+    if (pooling[t] != TBE_SUM && pooling[t] != TBE_MEAN) return TBE_E_ARG;
+    if (!weights[t] || !aligned(weights[t], 16) || !momentum[t] || !aligned(momentum[t], 4))
+      return TBE_E_ARG;
+    if (rows[t] < 1) return TBE_E_UNSUPPORTED;
+    if (dims[t] < 4 || dims[t] > 1024 || dims[t] % 4) return TBE_E_UNSUPPORTED;
+    sum_rows += (uint64_t)rows[t];
+    dtot += (uint64_t)dims[t];
+    if (sum_rows >= (1ull << 32)) return TBE_E_RANGE;
+  }
+  tbe_plan* P = new (std::nothrow) tbe_plan();
+  if (!P) return TBE_E_ALLOC;
+  P->T = T;
+  P->wdtype = wdtype;
+  P->rows.assign(rows, rows + T);
+  P->dims.assign(dims, dims + T);
+  P->pooling.assign(pooling, pooling + T);
+  P->sum_rows = sum_rows;
+  P->dtot = (uint32_t)dtot;
+  P->key_bits = sum_rows <= 1 ? 0 : ilog2(sum_rows);
+
+  // buckets by next_pow2(D), ascending width; tables keep ascending id inside a bucket
+  std::vector<uint32_t> widths;
+  for (int t = 0; t < T; ++t) widths.push_back(next_pow2((uint32_t)dims[t]));
+  std::vector<uint32_t> uw = widths;
+  std::sort(uw.begin(), uw.end());
+  uw.erase(std::unique(uw.begin(), uw.end()), uw.end());
+  P->pstride = 0;
+  for (uint32_t w : uw) {
+    Bucket bk{};
+    bk.width = w;
+    bool all8 = wdtype != TBE_F32 && w >= 8;
+    for (int t = 0; t < T; ++t)
+      if (widths[t] == w) {
+        bk.tables.push_back((uint32_t)t);
+        if (dims[t] % 8) all8 = false;
+      }
+    bk.vec = all8 ? 8 : 4;
+    const uint32_t lanes = w / (uint32_t)bk.vec;
+    bk.lpr = std::min<uint32_t>(lanes, kWave);
+    bk.nc = (int)(lanes / bk.lpr);
+    bk.lpr_log2 = (uint32_t)ilog2(bk.lpr);
+    P->pstride = std::max(P->pstride, w);
+    P->buckets.push_back(bk);
+  }
+  // linear keys: tables in bucket order, then id
+  std::vector<uint32_t> order;
+  for (auto& bk : P->buckets) order.insert(order.end(), bk.tables.begin(), bk.tables.end());
+  P->key_base.assign(T, 0);
+  P->col.assign(T, 0);
+  {
+    uint64_t kb = 0;
+    for (uint32_t t : order) {
+      P->key_base[t] = (uint32_t)kb;
+      kb += (uint64_t)rows[t];
+    }
+    uint32_t c = 0;
+    for (int t = 0; t < T; ++t) {
+      P->col[t] = c;
+      c += (uint32_t)dims[t];
+    }
+  }
+  std::vector<TableDev> td(T);
+  for (int t = 0; t < T; ++t) {
+    td[t].w = weights[t];
+    td[t].m = momentum[t];
+    td[t].dim = (uint32_t)dims[t];
+    td[t].pooling = (uint32_t)pooling[t];
+    td[t].col = P->col[t];
+    td[t].key_base = P->key_base[t];
+    td[t].rows = (uint32_t)rows[t];
+  }
+  const uint32_t nb = (uint32_t)P->buckets.size();
+  std::vector<uint32_t> bkb(nb + 1);
+  for (uint32_t b = 0; b < nb; ++b) {
+    bkb[b] = P->key_base[P->buckets[b].tables[0]];
+    for (uint32_t t : P->buckets[b].tables) td[t].bucket = b;
+  }
+  bkb[nb] = (uint32_t)std::min<uint64_t>(sum_rows, 0xffffffffull);
+
+  // one device allocation: tables | order | bucket key bounds | bucket table lists
+  const size_t sz_td = align_up(sizeof(TableDev) * T);
+  const size_t sz_order = align_up(4 * (size_t)T);
+  const size_t sz_bkb = align_up(4 * (size_t)(nb + 1));
+  const size_t sz_lists = align_up(4 * (size_t)T);
+  void* mem = nullptr;
+  if (hipMalloc(&mem, sz_td + sz_order + sz_bkb + sz_lists) != hipSuccess) {
+    delete P;
+    return TBE_E_ALLOC;
+  }
+  uint8_t* base = reinterpret_cast<uint8_t*>(mem);
+  P->d_mem = mem;
+  P->d_tables = reinterpret_cast<TableDev*>(base);
+  P->d_order = reinterpret_cast<uint32_t*>(base + sz_td);
+  P->d_bkb = reinterpret_cast<uint32_t*>(base + sz_td + sz_order);
+  uint32_t* lists = reinterpret_cast<uint32_t*>(base + sz_td + sz_order + sz_bkb);
+  bool ok = hipMemcpy(P->d_tables, td.data(), sizeof(TableDev) * T, hipMemcpyHostToDevice) ==
+                hipSuccess &&
+            hipMemcpy(P->d_order, order.data(), 4 * (size_t)T, hipMemcpyHostToDevice) ==
+                hipSuccess &&
+            hipMemcpy(P->d_bkb, bkb.data(), 4 * (size_t)(nb + 1), hipMemcpyHostToDevice) ==
+                hipSuccess &&
+            hipMemcpy(lists, order.data(), 4 * (size_t)T, hipMemcpyHostToDevice) == hipSuccess;
+  size_t pos = 0;
+  for (auto& bk : P->buckets) {
+    bk.d_tables = lists + pos;
+    pos += bk.tables.size();
+  }
+  int dev = 0, cus = 0;
+  ok = ok && hipGetDevice(&dev) == hipSuccess &&
+       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess;
+  P->num_cus = cus > 0 ? cus : 256;
+  if (!ok) {
+    (void)hipFree(mem);
+    delete P;
+    return TBE_E_HIP;
+  }
+  *out = P;
+  return TBE_OK;
+}
+
+int tbe_plan_destroy(tbe_plan* P) {
+  if (!P) return TBE_OK;
+  const hipError_t e = hipFree(P->d_mem);
+  delete P;
+  return e == hipSuccess ? TBE_OK : TBE_E_HIP;
+}
+
+int tbe_plan_key_bases(const tbe_plan* P, int64_t* key_base) {
+  if (!P || !key_base) return TBE_E_ARG;
+  for (int t = 0; t < P->T; ++t) key_base[t] = (int64_t)P->key_base[t];
+  return TBE_OK;
+}
+
+int tbe_workspace_size(const tbe_plan* P, int64_t B, int64_t N, size_t* bytes) {
+  if (!P || !bytes || B < 0 || N < 0) return TBE_E_ARG;
+  if (N >= (int64_t)(1ll << 31) - 1) return TBE_E_RANGE;
+  *bytes = layout(P, N).total;
+  return TBE_OK;
+}
+
+int tbe_workspace_views(const tbe_plan* P, int64_t B, int64_t N, tbe_ws_views* v) {
+  if (!P || !v || B < 0 || N < 0) return TBE_E_ARG;
+  if (N >= (int64_t)(1ll << 31) - 1) return TBE_E_RANGE;
+  const WsLayout L = layout(P, N);
+  v->sorted_key = L.final_in_b ? L.key_b : L.key_a;
+  v->sorted_pos = L.final_in_b ? L.val_b : L.val_a;
+  v->bag = L.bag;
+  v->run_start = L.run_start;
+  v->run_key = L.run_key;
+  v->short_task = L.short_task;
+  v->long_task = L.long_task;
+  v->long_cbeg = L.long_cbeg;
+  v->chunk_task = L.chunk_task;
+  v->counters = L.counters;
+  v->total = L.total;
+  v->num_buckets = (int32_t)P->buckets.size();
+  return TBE_OK;
+}
+
+int tbe_forward(const tbe_plan* P, int64_t B, int32_t itype, const void* indices,
+                const void* offsets, int64_t N, const float* psw, float* out, uint32_t flags,
+                void* stream) {
+  int rc = check_lookups(P, B, itype, indices, offsets, N);
+  if (rc) return rc;
+  if (flags & ~(TBE_FWD_NO_HIST | TBE_FWD_REQUIRE_HIST)) return TBE_E_ARG;
+  if ((flags & TBE_FWD_NO_HIST) && (flags & TBE_FWD_REQUIRE_HIST)) return TBE_E_ARG;
+  if (B > 0 && (!out || !aligned(out, 16))) return TBE_E_ARG;
+  if (psw && !aligned(psw, 4)) return TBE_E_ARG;
+  const bool hist = hist_eligible(P, B, N, psw);
+  if ((flags & TBE_FWD_REQUIRE_HIST) && !hist) return TBE_E_UNSUPPORTED;
+  if (B == 0) return TBE_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  FwdArgs a{P->d_tables, B, itype, indices, offsets, psw, out, P->dtot};
+  hipError_t e = hipSuccess;
+  if (hist && !(flags & TBE_FWD_NO_HIST)) {
+    e = launch_forward_hist(a, (uint32_t)P->rows[0], (uint32_t)P->dims[0],
+                            P->pooling[0] == TBE_MEAN, P->num_cus * 4, s);
+  } else {
+    for (const Bucket& bk : P->buckets) {
+      BucketDev bd{bk.d_tables, (uint32_t)bk.tables.size(), bk.lpr, bk.lpr_log2};
+      e = launch_forward_bucket(a, bd, P->wdtype, bk.vec, bk.nc, s);
+      if (e != hipSuccess) break;
+    }
+  }
+  return e == hipSuccess ? TBE_OK : TBE_E_HIP;
+}
+
+int tbe_preprocess(const tbe_plan* P, int64_t B, int32_t itype, const void* indices,
+                   const void* offsets, int64_t N, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_lookups(P, B, itype, indices, offsets, N);
+  if (rc) return rc;
+  rc = check_ws(P, N, ws, ws_bytes);
+  if (rc) return rc;
+  if (N == 0) return TBE_OK;
+  const WsLayout L = layout(P, N);
+  PrepArgs a = prep_args(P, B, itype, indices, offsets, N, ws, &L);
+  const hipError_t e =
+      launch_preprocess(a, P->num_cus * 8, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TBE_OK : TBE_E_HIP;
+}
+
+int tbe_backward_rowwise_adagrad(const tbe_plan* P, int64_t B, int32_t itype,
+                                 const void* indices, const void* offsets, int64_t N,
+                                 const float* psw, const float* grad_out, float lr, float eps,
+                                 void* ws, size_t ws_bytes, uint32_t flags,
+                                 uint32_t* debug_row_updates, void* stream) {
+  int rc = check_lookups(P, B, itype, indices, offsets, N);
+  if (rc) return rc;
+  rc = check_ws(P, N, ws, ws_bytes);
+  if (rc) return rc;
+  if (flags & ~(TBE_BWD_PREPROCESSED | TBE_BWD_FUSED_LONG)) return TBE_E_ARG;
+  if (B > 0 && (!grad_out || !aligned(grad_out, 16))) return TBE_E_ARG;
+  if (psw && !aligned(psw, 4)) return TBE_E_ARG;
+  if (debug_row_updates && !aligned(debug_row_updates, 4)) return TBE_E_ARG;
+  if (N == 0) return TBE_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const WsLayout L = layout(P, N);
+  uint8_t* w = reinterpret_cast<uint8_t*>(ws);
+  if (!(flags & TBE_BWD_PREPROCESSED)) {
+    PrepArgs pa = prep_args(P, B, itype, indices, offsets, N, ws, &L);
+    if (launch_preprocess(pa, P->num_cus * 8, s) != hipSuccess) return TBE_E_HIP;
+  }
+  BwdArgs a{};
+  a.tables = P->d_tables;
+  a.B = B;
+  a.itype = itype;
+  a.offsets = offsets;
+  a.psw = psw;
+  a.grad = grad_out;
+  a.dtot = P->dtot;
+  a.lr = lr;
+  a.eps = eps;
+  a.sorted_pos = reinterpret_cast<const uint32_t*>(w + (L.final_in_b ? L.val_b : L.val_a));
+  a.bag = reinterpret_cast<const uint32_t*>(w + L.bag);
+  a.short_task = reinterpret_cast<const uint4*>(w + L.short_task);
+  a.long_task = reinterpret_cast<const uint4*>(w + L.long_task);
+  a.long_cbeg = reinterpret_cast<const uint32_t*>(w + L.long_cbeg);
+  a.remaining = reinterpret_cast<uint32_t*>(w + L.remaining);
+  a.chunk_task = reinterpret_cast<const uint4*>(w + L.chunk_task);
+  a.partial = reinterpret_cast<float*>(w + L.partial);
+  a.pstride = L.pstride;
+  a.counters = reinterpret_cast<const uint32_t*>(w + L.counters);
+  a.nb = (uint32_t)P->buckets.size();
+  a.debug_count = debug_row_updates;
+  a.N = (uint32_t)N;
+  a.T = (uint32_t)P->T;
+  a.max_short = (uint32_t)N;
+  a.max_long = L.max_long;
+  a.max_chunks = L.max_chunks;
+  const bool fused = flags & TBE_BWD_FUSED_LONG;
+  for (uint32_t b = 0; b < P->buckets.size(); ++b) {
+    const Bucket& bk = P->buckets[b];
+    BucketDev bd{bk.d_tables, (uint32_t)bk.tables.size(), bk.lpr, bk.lpr_log2};
+    const int grid = persistent_grid(P, (uint64_t)N, kThreads / bk.lpr);
+    if (launch_backward_bucket(a, bd, b, P->wdtype, bk.vec, bk.nc, fused, grid, s) != hipSuccess)
+      return TBE_E_HIP;
+  }
+  return TBE_OK;
+}
+
+}  // extern "C"

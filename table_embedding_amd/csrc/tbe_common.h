@@ -1,0 +1,242 @@
+// Internal declarations shared by the HIP sources of libtbe_hip.so.
+// Device descriptors, storage-format helpers, wave64 subgroup reductions and
+// the host-side launchers each kernel file provides to the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tbe {
+
+constexpr int kThreads = 256;       // every kernel runs 256-thread workgroups (4 waves)
+constexpr int kWave = 64;
+constexpr int kTile = 4096;         // keys per workgroup in the sort / scan passes
+constexpr int kLongRun = 256;       // SL >= 256 takes the chunked long-run path
+constexpr int kChunk = 256;         // lookups per long-run chunk
+constexpr int kRadixBits = 8;
+constexpr int kMaxTables = 4096;
+
+enum : int { WD_F32 = 0, WD_F16 = 1, WD_BF16 = 2 };
+enum : int { IT_I32 = 0, IT_I64 = 1 };
+enum : int { POOL_SUM = 0, POOL_MEAN = 1 };
+
+// Per-table descriptor, one array of T entries in device memory.
+struct TableDev {
+  void* w;            // weights, rows x dim, row-major, storage type of the plan
+  float* m;           // row-wise Adagrad momentum, rows
+  uint32_t dim;       // D_t
+  uint32_t pooling;   // POOL_SUM / POOL_MEAN
+  uint32_t col;       // first column of the table in out / grad_out rows
+  uint32_t key_base;  // first linear row key of the table (tables ordered by bucket, then t)
+  uint32_t rows;      // R_t
+  uint32_t bucket;    // bucket id (tables bucketed by next_pow2(D))
+};
+
+// Lane mapping of one bucket: a row of up to `width` columns is covered by
+// `lpr` lanes, each holding `nc` chunks of `vec` consecutive columns.
+struct BucketDev {
+  const uint32_t* tables;  // table ids of this bucket, ascending
+  uint32_t ntables;
+  uint32_t lpr;            // lanes per row, power of two <= 64
+  uint32_t lpr_log2;
+};
+
+// Workspace layout: byte offsets from the workspace base (all 256-B aligned).
+struct WsLayout {
+  size_t key_a, key_b, val_a, val_b, bag;
+  size_t hist, rowtot, tile_cnt, tile_cls;
+  size_t run_start, run_key;
+  size_t short_task, long_task, long_cbeg, remaining, chunk_task;
+  size_t partial, counters;
+  size_t total;
+  uint32_t ntiles;          // ceil(N / kTile)
+  uint32_t max_long;        // capacity of the long-run lists
+  uint32_t max_chunks;      // capacity of the chunk list
+  uint32_t pstride;         // floats per partial row
+  int npass;                // radix passes
+  int final_in_b;           // sorted keys end in key_b/val_b
+};
+
+// Counter block: [U, n_short, n_long, n_chunks, sbeg[nb+1], lbeg[nb+1], cbeg[nb+1]]
+constexpr int kCntU = 0, kCntShort = 1, kCntLong = 2, kCntChunks = 3, kCntBegins = 4;
+
+// ------------------------------------------------------------- device helpers
+
+__device__ __forceinline__ float f16_bits_to_float(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) {
+  return __builtin_bit_cast(float, h << 16);
+}
+// round-to-nearest-even float -> binary16 bits
+__device__ __forceinline__ uint16_t float_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+// round-to-nearest-even float -> bfloat16 bits (NaN stays a quiet NaN)
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Load VEC consecutive weights starting at element e of a row-major table.
+template <int WD, int VEC>
+__device__ __forceinline__ void load_w(const void* w, int64_t e, float* v) {
+  if constexpr (WD == WD_F32) {
+    static_assert(VEC == 4, "f32 rows are read 4 at a time");
+    float4 x = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(w) + e);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  } else {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(w) + e;
+    uint32_t words[VEC / 2];
+    if constexpr (VEC == 8) {
+      uint4 x = *reinterpret_cast<const uint4*>(p);
+      words[0] = x.x; words[1] = x.y; words[2] = x.z; words[3] = x.w;
+    } else {
+      uint2 x = *reinterpret_cast<const uint2*>(p);
+      words[0] = x.x; words[1] = x.y;
+    }
+#pragma unroll
+    for (int i = 0; i < VEC / 2; ++i) {
+      if constexpr (WD == WD_F16) {
+        v[2 * i] = f16_bits_to_float(words[i] & 0xffffu);
+        v[2 * i + 1] = f16_bits_to_float(words[i] >> 16);
+      } else {
+        v[2 * i] = bf16_bits_to_float(words[i] & 0xffffu);
+        v[2 * i + 1] = bf16_bits_to_float(words[i] >> 16);
+      }
+    }
+  }
+}
+
+// Store VEC floats, rounded to the storage type, at element e.
+template <int WD, int VEC>
+__device__ __forceinline__ void store_w(void* w, int64_t e, const float* v) {
+  if constexpr (WD == WD_F32) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(w) + e) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    uint32_t words[VEC / 2];
+#pragma unroll
+    for (int i = 0; i < VEC / 2; ++i) {
+      uint32_t lo, hi;
+      if constexpr (WD == WD_F16) {
+        lo = float_to_f16_bits(v[2 * i]);
+        hi = float_to_f16_bits(v[2 * i + 1]);
+      } else {
+        lo = float_to_bf16_bits(v[2 * i]);
+        hi = float_to_bf16_bits(v[2 * i + 1]);
+      }
+      words[i] = lo | (hi << 16);
+    }
+    uint16_t* p = reinterpret_cast<uint16_t*>(w) + e;
+    if constexpr (VEC == 8)
+      *reinterpret_cast<uint4*>(p) = make_uint4(words[0], words[1], words[2], words[3]);
+    else
+      *reinterpret_cast<uint2*>(p) = make_uint2(words[0], words[1]);
+  }
+}
+
+template <int VEC>
+__device__ __forceinline__ void load_f32(const float* p, float* v) {
+#pragma unroll
+  for (int i = 0; i < VEC; i += 4) {
+    float4 x = *reinterpret_cast<const float4*>(p + i);
+    v[i] = x.x; v[i + 1] = x.y; v[i + 2] = x.z; v[i + 3] = x.w;
+  }
+}
+template <int VEC>
+__device__ __forceinline__ void store_f32(float* p, const float* v) {
+#pragma unroll
+  for (int i = 0; i < VEC; i += 4)
+    *reinterpret_cast<float4*>(p + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+}
+
+__device__ __forceinline__ int64_t load_idx(const void* a, int itype, int64_t i) {
+  return itype == IT_I32 ? (int64_t)reinterpret_cast<const int32_t*>(a)[i]
+                         : reinterpret_cast<const int64_t*>(a)[i];
+}
+
+// Sum over the `lpr` lanes of a subgroup (lpr a power of two, subgroups aligned).
+__device__ __forceinline__ float subgroup_sum(float v, uint32_t lpr) {
+  for (uint32_t m = 1; m < lpr; m <<= 1) v += __shfl_xor(v, (int)m, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & (kWave - 1); }
+
+// ------------------------------------------------------------ host launchers
+
+// Optional per-kernel timing (tbe_prof_enable): when on, every launch is
+// bracketed by two HIP events recorded on the launch stream.
+void prof_begin(hipStream_t s, const char* name);
+void prof_end(hipStream_t s);
+
+#define TBE_LAUNCH(name, kernel, grid, block, stream, ...)                   \
+  do {                                                                       \
+    ::tbe::prof_begin((stream), (name));                                     \
+    hipLaunchKernelGGL(kernel, (grid), (block), 0, (stream), __VA_ARGS__);   \
+    ::tbe::prof_end((stream));                                               \
+  } while (0)
+
+struct FwdArgs {
+  const TableDev* tables;
+  int64_t B;
+  int itype;
+  const void* indices;
+  const void* offsets;
+  const float* psw;
+  float* out;
+  uint32_t dtot;
+};
+
+struct PrepArgs {
+  const TableDev* tables;
+  const uint32_t* bucket_key_begin;  // nb+1 linear key bounds of the buckets
+  const uint32_t* order;             // table ids in ascending key_base order
+  uint32_t T, nb;
+  int64_t B;
+  int itype;
+  const void* indices;
+  const void* offsets;
+  uint32_t N;
+  uint8_t* ws;
+  const WsLayout* L;                 // host pointer (layout), kernels get offsets by value
+  int key_bits;
+};
+
+struct BwdArgs {
+  const TableDev* tables;
+  int64_t B;
+  int itype;
+  const void* offsets;
+  const float* psw;
+  const float* grad;
+  uint32_t dtot;
+  float lr, eps;
+  const uint32_t* sorted_pos;
+  const uint32_t* bag;
+  const uint4* short_task;
+  const uint4* long_task;
+  const uint32_t* long_cbeg;
+  uint32_t* remaining;
+  const uint4* chunk_task;
+  float* partial;
+  uint32_t pstride;
+  const uint32_t* counters;
+  uint32_t nb;
+  uint32_t* debug_count;     // nullable, per linear key
+  uint32_t N, T;             // lookups and tables (task sanity bounds)
+  uint32_t max_short, max_long, max_chunks;  // list capacities
+};
+
+hipError_t launch_forward_bucket(const FwdArgs& a, const BucketDev& bk, int wd, int vec, int nc,
+                                 hipStream_t s);
+hipError_t launch_forward_hist(const FwdArgs& a, uint32_t E, uint32_t D, int mean, int grid,
+                               hipStream_t s);
+hipError_t launch_preprocess(const PrepArgs& a, int grid_persist, hipStream_t s);
+hipError_t launch_backward_bucket(const BwdArgs& a, const BucketDev& bk, uint32_t bucket, int wd,
+                                  int vec, int nc, bool fused, int grid_persist, hipStream_t s);
+
+}  // namespace tbe

@@ -1,0 +1,237 @@
+"""Shared helpers of the GPU parity tests: upload a workload, run the HIP path
+through the C ABI, run the oracle on the same inputs, compare."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import tbe_workloads as wl
+
+TORCH_WD = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def tolerance_weights(a_st, b_st, wdtype, ref_f64=None):
+    """Max violation of the weight tolerance: 2 storage ulp for 16-bit types,
+    1e-6*max(1,|ref|) for float32.  Returns the worst ulp distance or scaled error."""
+    if wdtype == "f32":
+        a = a_st.view(np.float32).astype(np.float64)
+        b = b_st.view(np.float32).astype(np.float64)
+        return float(np.max(np.abs(a - b) / np.maximum(1.0, np.abs(b)), initial=0.0))
+    a = a_st.astype(np.int64)
+    b = b_st.astype(np.int64)
+    a = np.where(a & 0x8000, -(a & 0x7FFF), a)
+    b = np.where(b & 0x8000, -(b & 0x7FFF), b)
+    return float(np.max(np.abs(a - b), initial=0))
+
+
+def weights_ok(a_st, b_st, wdtype):
+    v = tolerance_weights(a_st, b_st, wdtype)
+    return v <= (1e-6 if wdtype == "f32" else 2), v
+
+
+def to_host_storage(t: torch.Tensor, wdtype: str) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if wdtype == "f32":
+        return t.numpy().copy()
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def from_host_storage(a: np.ndarray, wdtype: str, device="cuda") -> torch.Tensor:
+    if wdtype == "f32":
+        return torch.from_numpy(a.copy()).to(device)
+    return torch.from_numpy(a.view(np.int16).copy()).to(device).view(TORCH_WD[wdtype])
+
+
+class Case:
+    """Host inputs of one workload plus their device copies."""
+
+    def __init__(self, spec: wl.Spec, m_nonzero=False, device="cuda"):
+        self.spec = spec
+        self.off = spec.offsets()
+        self.idx = spec.indices()
+        self.psw = spec.per_sample_weights()
+        self.G = spec.grad_out()
+        self.W = [wl.to_storage(spec.weights_f32(t), spec.wdtype) for t in range(spec.T)]
+        self.M = [spec.momentum(t, nonzero=m_nonzero) for t in range(spec.T)]
+        self.N = int(self.off[-1])
+        d = device
+        self.d_off = torch.from_numpy(self.off).to(d)
+        self.d_idx = torch.from_numpy(self.idx).to(d)
+        self.d_psw = None if self.psw is None else torch.from_numpy(self.psw).to(d)
+        self.d_G = torch.from_numpy(self.G).to(d)
+        self.reset_tables()
+
+    def reset_tables(self):
+        self.d_W = [from_host_storage(w, self.spec.wdtype) for w in self.W]
+        self.d_M = [torch.from_numpy(m.copy()).cuda() for m in self.M]
+
+    def tbe(self):
+        import table_embedding_amd as te
+        return te.TBE(self.spec.rows, self.spec.dims, self.spec.pooling, self.d_W, self.d_M)
+
+    # ------------------------------------------------------------- oracle
+    def oracle_forward(self):
+        s = self.spec
+        return oracle.forward(s.rows, s.dims, s.pooling, s.wdtype, self.W, s.B, s.itype,
+                              self.idx, self.off, self.psw)
+
+    def oracle_backward(self):
+        s = self.spec
+        W = [w.copy() for w in self.W]
+        M = [m.copy() for m in self.M]
+        oracle.backward_rowwise_adagrad(s.rows, s.dims, s.pooling, s.wdtype, W, M, s.B, s.itype,
+                                        self.idx, self.off, self.psw, self.G, s.lr, s.eps)
+        return W, M
+
+    def oracle_preprocess(self):
+        return oracle.preprocess(self.spec.rows, self.spec.B, self.spec.itype, self.idx, self.off)
+
+
+def read_u32(ws: torch.Tensor, offset: int, count: int) -> np.ndarray:
+    if count == 0:
+        return np.zeros(0, np.uint32)
+    return ws[offset:offset + 4 * count].cpu().numpy().view(np.uint32).copy()
+
+
+def read_u32x4(ws, offset, count):
+    return read_u32(ws, offset, 4 * count).reshape(count, 4)
+
+
+def check_forward(case: Case, out_gpu: torch.Tensor):
+    ref = case.oracle_forward().astype(np.float64)
+    got = out_gpu.cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref) / np.maximum(1.0, np.abs(ref))
+    assert np.all(np.isfinite(got))
+    worst = float(err.max(initial=0.0))
+    assert worst <= 1e-4, f"forward max scaled error {worst}"
+    return worst
+
+
+def touched_rows(case: Case, t: int) -> np.ndarray:
+    s = case.spec
+    lo, hi = int(case.off[t * s.B]), int(case.off[(t + 1) * s.B])
+    return np.unique(case.idx[lo:hi].astype(np.int64))
+
+
+def check_backward(case: Case, tbe_obj):
+    """Touched rows within tolerance of the oracle, untouched rows bit-identical."""
+    Wr, Mr = case.oracle_backward()
+    s = case.spec
+    worst_w, worst_m = 0.0, 0.0
+    for t in range(s.T):
+        Wg = to_host_storage(tbe_obj.weights[t], s.wdtype).reshape(s.rows[t], s.dims[t])
+        Mg = tbe_obj.momentum[t].cpu().numpy()
+        W0 = case.W[t].reshape(s.rows[t], s.dims[t])
+        rows = touched_rows(case, t)
+        mask = np.zeros(s.rows[t], bool)
+        mask[rows] = True
+        assert Wg[~mask].tobytes() == W0[~mask].tobytes(), f"table {t}: untouched rows changed"
+        assert Mg[~mask].tobytes() == case.M[t][~mask].tobytes(), f"table {t}: untouched M"
+        ok, v = weights_ok(Wg[mask], Wr[t].reshape(s.rows[t], s.dims[t])[mask], s.wdtype)
+        assert ok, f"table {t}: weight tolerance exceeded ({v})"
+        worst_w = max(worst_w, v)
+        rel = np.abs(Mg[mask].astype(np.float64) - Mr[t][mask]) / np.maximum(
+            np.abs(Mr[t][mask].astype(np.float64)), 1e-30)
+        worst = float(rel.max(initial=0.0))
+        assert worst <= 1e-5, f"table {t}: momentum rel error {worst}"
+        worst_m = max(worst_m, worst)
+    return worst_w, worst_m
+
+
+def bucket_of_table(spec) -> np.ndarray:
+    w = [1 << max(0, (d - 1).bit_length()) for d in spec.dims]
+    uw = sorted(set(w))
+    return np.array([uw.index(x) for x in w], np.int64)
+
+
+def gpu_preprocess_views(tbe_obj, case: Case):
+    """Read the workspace after tbe_preprocess and map it to the oracle's key order."""
+    import table_embedding_amd as te
+    s = case.spec
+    v = te.tbe_workspace_views(tbe_obj.plan, s.B, case.N)
+    ws = tbe_obj._ws
+    N = case.N
+    nb = v["num_buckets"]
+    cnt = read_u32(ws, v["counters"], 4 + 3 * (nb + 1))
+    U, ns, nl, nc = (int(x) for x in cnt[:4])
+    out = dict(
+        sorted_key=read_u32(ws, v["sorted_key"], N).astype(np.int64),
+        sorted_pos=read_u32(ws, v["sorted_pos"], N).astype(np.int64),
+        bag=read_u32(ws, v["bag"], N).astype(np.int64),
+        run_start=read_u32(ws, v["run_start"], U + 1).astype(np.int64),
+        run_key=read_u32(ws, v["run_key"], U).astype(np.int64),
+        short_task=read_u32x4(ws, v["short_task"], ns).astype(np.int64),
+        long_task=read_u32x4(ws, v["long_task"], nl).astype(np.int64),
+        long_cbeg=read_u32(ws, v["long_cbeg"], nl).astype(np.int64),
+        chunk_task=read_u32x4(ws, v["chunk_task"], nc).astype(np.int64),
+        U=U, n_short=ns, n_long=nl, n_chunks=nc, nb=nb,
+        begins=cnt[4:].reshape(3, nb + 1).astype(np.int64))
+    kb = np.array(tbe_obj.key_bases(), np.int64)
+    out["key_base"] = kb
+    return out
+
+
+def check_preprocess(case: Case, tbe_obj):
+    """Bit-exact comparison of every integer output of the preprocessing."""
+    s = case.spec
+    g = gpu_preprocess_views(tbe_obj, case)
+    r = case.oracle_preprocess()
+    kb = g["key_base"]
+    base = np.concatenate([[0], np.cumsum(s.rows)[:-1]]).astype(np.int64)
+    order = np.argsort(kb, kind="stable")       # tables by linear key
+    kb_sorted = kb[order]
+
+    def to_oracle_key(k):
+        i = np.searchsorted(kb_sorted, k, side="right") - 1
+        t = order[i]
+        return base[t] + (k - kb[t]), t
+
+    assert np.array_equal(g["bag"], r["bag"]), "bag ids differ"
+    okey, _ = to_oracle_key(g["sorted_key"])
+    # GPU keys are ordered by (bucket, table); a stable re-sort by the oracle's table-major key
+    # gives the oracle's order if and only if every table segment matches
+    perm = np.argsort(okey, kind="stable")
+    assert np.array_equal(okey[perm], r["sorted_key"].astype(np.int64)), "sorted keys differ"
+    assert np.array_equal(g["sorted_pos"][perm], r["sorted_pos"]), "sorted positions differ"
+    # run starts point at the first slot of each run in the GPU order
+    assert g["U"] == r["U"]
+    assert g["run_start"][-1] == case.N
+    assert np.array_equal(g["sorted_key"][g["run_start"][:-1]], g["run_key"])
+    lens_g = np.diff(g["run_start"])
+    rk_o, _ = to_oracle_key(g["run_key"])
+    p = np.argsort(rk_o, kind="stable")
+    assert np.array_equal(rk_o[p], r["run_key"].astype(np.int64)), "run keys differ"
+    assert np.array_equal(lens_g[p], np.diff(r["run_start"])), "run lengths differ"
+    assert (g["n_short"], g["n_long"], g["n_chunks"]) == (r["n_short"], r["n_long"],
+                                                            r["n_chunks"])
+    # tasks: every run appears once, in ascending key order, with its table and row
+    st = g["short_task"]
+    lt = g["long_task"]
+    if len(st):
+        assert np.all(st[:, 1] < 256)
+        assert np.array_equal(kb[st[:, 3]] + st[:, 2], g["sorted_key"][st[:, 0]])
+        assert np.all(np.diff(kb[st[:, 3]] + st[:, 2]) > 0)
+        assert np.array_equal(st[:, 0], g["run_start"][:-1][lens_g < 256])
+        assert np.array_equal(st[:, 1], lens_g[lens_g < 256])
+    if len(lt):
+        assert np.all(lt[:, 1] >= 256)
+        assert np.array_equal(lt[:, 0], g["run_start"][:-1][lens_g >= 256])
+        assert np.array_equal(lt[:, 1], lens_g[lens_g >= 256])
+        assert np.array_equal(kb[lt[:, 3]] + lt[:, 2], g["sorted_key"][lt[:, 0]])
+        nch = (lt[:, 1] + 255) // 256
+        assert np.array_equal(g["long_cbeg"], np.concatenate([[0], np.cumsum(nch)[:-1]]))
+        ct = g["chunk_task"]
+        want = []
+        for l, (st0, ln, row, t) in enumerate(lt):
+            for k in range(int((ln + 255) // 256)):
+                want.append([st0 + 256 * k, min(256, ln - 256 * k), t, l])
+        assert np.array_equal(ct, np.array(want, np.int64).reshape(-1, 4)), "chunk tasks differ"
+    # per-bucket begins split the three lists exactly at bucket changes
+    bt = bucket_of_table(s)
+    for k, (tasks, tcol) in enumerate(((st, 3), (lt, 3), (g["chunk_task"], 2))):
+        b = g["begins"][k]
+        assert b[0] == 0 and b[-1] == len(tasks)
+        for q in range(g["nb"]):
+            assert np.all(bt[tasks[b[q]:b[q + 1], tcol]] == q) if len(tasks) else True
+    return g, r

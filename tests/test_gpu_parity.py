@@ -1,0 +1,210 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Workloads are the five configurations with every distribution kept and the
+sizes scaled so the oracle finishes in seconds while still spanning several
+4096-key tiles with a ragged tail, plus edge cases: empty bags, an all-empty
+batch, B = 1, a one-row table, runs of exactly 255/256/257 lookups, D = 4 and
+D = 1024, D not a multiple of 8, many tables over every bucket, int32 indices,
+mean pooling with per-sample weights, non-zero initial momentum.
+
+Bars: integer outputs bit-exact; pooled outputs |d| <= 1e-4 max(1,|ref|);
+16-bit weights within 2 ulp, float32 weights within 1e-6 max(1,|ref|);
+momentum within 1e-5 relative; untouched rows bit-identical; fused and
+two-launch long-run paths bit-identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+import tbe_workloads as wl
+from tests import support as S
+
+pytestmark = pytest.mark.gpu
+
+
+def _spec(name):
+    if name == "C1":
+        return wl.config("C1")
+    if name == "C2s":
+        return wl.config("C2", rows=20000, B=512, T=4)
+    if name == "C3s":
+        return wl.config("C3", rows=50000, B=256, T=10)
+    if name == "C4s":
+        return wl.config("C4", B=2048)
+    if name == "C5s":
+        return wl.config("C5", rows=200000, B=2048, T=3)
+    if name == "empty_bags":
+        return wl.Spec("empty_bags", 2001, [100, 37, 60], [8, 36, 4], [0, 1, 1], "f16", 33,
+                       "list:0,3,0,5,1,0,0,9", "uniform", "i64", True)
+    if name == "all_empty":
+        return wl.Spec("all_empty", 2002, [10, 10], [16, 32], [0, 1], "bf16", 7, "list:0",
+                       "uniform", "i64", False)
+    if name == "one_bag":
+        return wl.Spec("one_bag", 2003, [1000], [128], [1], "f16", 1, "fixed:700",
+                       "zipf:1.3", "i32", True)
+    if name == "one_row":
+        return wl.Spec("one_row", 2004, [1], [16], [0], "f32", 3, "fixed:300", "uniform",
+                       "i64", False)
+    if name.startswith("const"):
+        n = int(name[5:])
+        return wl.Spec(name, 2005, [9], [64], [0], "bf16", n, "fixed:1", "const:5", "i64",
+                       True)
+    if name == "wide_f32":
+        return wl.Spec("wide_f32", 2006, [300, 50], [1024, 512], [0, 1], "f32", 64,
+                       "uniform:0:40", "zipf:1.2", "i64", True)
+    if name == "wide_bf16":
+        return wl.Spec("wide_bf16", 2007, [300, 20], [1024, 4], [1, 0], "bf16", 64,
+                       "uniform:1:30", "zipf:1.1", "i32", False)
+    if name == "many_tables":
+        dims = [4, 12, 64, 100, 128, 256, 512, 1024, 36, 8]
+        T = 40
+        return wl.Spec("many_tables", 2008, [int(50 + 37 * t) for t in range(T)],
+                       [dims[t % len(dims)] for t in range(T)], [t % 2 for t in range(T)],
+                       "f16", 40, "uniform:0:12", "zipf:1.05", "i32", True)
+    raise KeyError(name)
+
+
+MAIN = ["C1", "C2s", "C3s", "C4s", "C5s"]
+EDGE = ["empty_bags", "all_empty", "one_bag", "one_row", "const255", "const256", "const257",
+        "wide_f32", "wide_bf16", "many_tables"]
+
+
+def _announce(name, what):
+    print(f"[gpu] {what} case={name}", flush=True)
+
+
+@pytest.mark.parametrize("name", MAIN + EDGE)
+def test_forward_parity(name):
+    _announce(name, "forward")
+    case = S.Case(_spec(name))
+    tb = case.tbe()
+    import table_embedding_amd as te
+    out = tb.forward(case.spec.B, case.d_idx, case.d_off, case.d_psw, flags=te.TBE_FWD_NO_HIST)
+    torch.cuda.synchronize()
+    S.check_forward(case, out)
+
+
+@pytest.mark.parametrize("name", MAIN + EDGE)
+def test_preprocess_bit_exact(name):
+    _announce(name, "preprocess")
+    case = S.Case(_spec(name))
+    if case.N == 0:
+        pytest.skip("no lookups: preprocessing enqueues nothing")
+    tb = case.tbe()
+    tb.preprocess(case.spec.B, case.d_idx, case.d_off)
+    torch.cuda.synchronize()
+    S.check_preprocess(case, tb)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("name", MAIN + EDGE)
+def test_backward_parity(name, fused):
+    _announce(name, f"backward fused={fused}")
+    import table_embedding_amd as te
+    case = S.Case(_spec(name), m_nonzero=(name in ("C2s", "C3s", "wide_f32")))
+    tb = case.tbe()
+    flags = te.TBE_BWD_FUSED_LONG if fused else 0
+    tb.backward(case.spec.B, case.d_idx, case.d_off, case.d_psw, case.d_G, case.spec.lr,
+                case.spec.eps, flags=flags)
+    torch.cuda.synchronize()
+    S.check_backward(case, tb)
+
+
+@pytest.mark.parametrize("name", ["C2s", "C3s", "C4s", "const257", "one_row"])
+def test_fused_equals_two_launch_bitwise(name):
+    _announce(name, "fused-vs-two-launch")
+    import table_embedding_amd as te
+    case = S.Case(_spec(name), m_nonzero=True)
+    res = []
+    for flags in (0, te.TBE_BWD_FUSED_LONG, te.TBE_BWD_FUSED_LONG, 0):
+        case.reset_tables()
+        tb = case.tbe()
+        tb.backward(case.spec.B, case.d_idx, case.d_off, case.d_psw, case.d_G, case.spec.lr,
+                    case.spec.eps, flags=flags)
+        torch.cuda.synchronize()
+        res.append([S.to_host_storage(w, case.spec.wdtype).tobytes() for w in tb.weights] +
+                   [m.cpu().numpy().tobytes() for m in tb.momentum])
+        tb.close()
+    assert res[0] == res[1] == res[2] == res[3]
+
+
+@pytest.mark.parametrize("name", ["C2s", "C3s", "C5s"])
+def test_every_touched_row_updated_once(name):
+    _announce(name, "debug-count")
+    case = S.Case(_spec(name))
+    tb = case.tbe()
+    nkeys = sum(case.spec.rows)
+    cnt = torch.zeros(nkeys, dtype=torch.int32, device="cuda")
+    tb.backward(case.spec.B, case.d_idx, case.d_off, case.d_psw, case.d_G, case.spec.lr,
+                case.spec.eps, debug_row_updates=cnt)
+    torch.cuda.synchronize()
+    c = cnt.cpu().numpy()
+    kb = tb.key_bases()
+    for t in range(case.spec.T):
+        seg = c[kb[t]:kb[t] + case.spec.rows[t]]
+        want = np.zeros(case.spec.rows[t], np.int32)
+        want[S.touched_rows(case, t)] = 1
+        assert np.array_equal(seg, want), f"table {t}"
+
+
+def test_preprocessed_flag_and_reuse():
+    """tbe_preprocess then backward(PREPROCESSED) equals a self-preprocessing backward;
+    the fused countdowns are re-armed, so a second fused backward on the same
+    preprocessed workspace is still exact."""
+    import table_embedding_amd as te
+    case = S.Case(_spec("C2s"))
+    tb = case.tbe()
+    tb.preprocess(case.spec.B, case.d_idx, case.d_off)
+    tb.backward(case.spec.B, case.d_idx, case.d_off, None, case.d_G, case.spec.lr,
+                case.spec.eps, flags=te.TBE_BWD_PREPROCESSED | te.TBE_BWD_FUSED_LONG)
+    torch.cuda.synchronize()
+    S.check_backward(case, tb)
+    a = [S.to_host_storage(w, "f16").tobytes() for w in tb.weights]
+    case.reset_tables()
+    tb2 = case.tbe()
+    tb2._ws = tb._ws  # same preprocessed workspace, second fused use
+    tb2.backward(case.spec.B, case.d_idx, case.d_off, None, case.d_G, case.spec.lr,
+                 case.spec.eps, flags=te.TBE_BWD_PREPROCESSED | te.TBE_BWD_FUSED_LONG)
+    torch.cuda.synchronize()
+    assert [S.to_host_storage(w, "f16").tobytes() for w in tb2.weights] == a
+
+
+def test_histogram_path_forward():
+    import table_embedding_amd as te
+    for name in ("C4s",):
+        _announce(name, "histogram forward")
+        case = S.Case(_spec(name))
+        tb = case.tbe()
+        out = tb.forward(case.spec.B, case.d_idx, case.d_off, None,
+                         flags=te.TBE_FWD_REQUIRE_HIST)
+        torch.cuda.synchronize()
+        S.check_forward(case, out)
+
+
+def test_histogram_path_long_bags_and_mean():
+    """Bags longer than the 256 counted lookups (scalar remainder), ragged B, mean pooling."""
+    import table_embedding_amd as te
+    spec = wl.Spec("hist_long", 2010, [50], [96], [1], "f16", 37, "uniform:64:700", "uniform",
+                   "i64", False)
+    case = S.Case(spec)
+    tb = case.tbe()
+    out = tb.forward(spec.B, case.d_idx, case.d_off, None, flags=te.TBE_FWD_REQUIRE_HIST)
+    torch.cuda.synchronize()
+    S.check_forward(case, out)
+
+
+def test_repeat_runs_bitwise_identical():
+    import table_embedding_amd as te
+    case = S.Case(_spec("C3s"))
+    outs, ws = [], []
+    for _ in range(3):
+        case.reset_tables()
+        tb = case.tbe()
+        o = tb.forward(case.spec.B, case.d_idx, case.d_off, case.d_psw)
+        tb.backward(case.spec.B, case.d_idx, case.d_off, case.d_psw, case.d_G, case.spec.lr,
+                    case.spec.eps)
+        torch.cuda.synchronize()
+        outs.append(o.cpu().numpy().tobytes())
+        ws.append([S.to_host_storage(w, "bf16").tobytes() for w in tb.weights])
+    assert outs[0] == outs[1] == outs[2]
+    assert ws[0] == ws[1] == ws[2]
