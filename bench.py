@@ -1,0 +1,343 @@
+#!/usr/bin/env python3
+"""TBE forward + backward (row-wise Adagrad) throughput on one MI355X.
+
+One step = tbe_forward + tbe_backward_rowwise_adagrad (which runs the whole
+preprocessing: transposition, radix sort, run-length encoding, classification)
+over one batch of the workload; inputs are resident in HBM before timing.
+Prints one JSON line with lookups/s, the roofline of the dominant kernel and
+the single-threaded CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--steps K] [--warmup W] [--config C2] [--fused]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TBE fwd+bwd lookups/sec and achieved HBM GB/s (% of MI355X peak)"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = {
+    "fwd_pool": "fwd_pool.hip", "fwd_hist": "fwd_hist.hip", "bwd_short": "bwd.hip",
+    "bwd_chunk": "bwd.hip", "bwd_long_update": "bwd.hip", "bwd_chunk_fused": "bwd.hip",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="C2", choices=["C1", "C2", "C3", "C4", "C5"])
+    ap.add_argument("--fused", action="store_true", help="fused long-run countdown path")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-lookups", type=int, default=3_000_000,
+                    help="cap on lookups in the CPU oracle sample (whole tables)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ inputs
+
+def device_inputs(spec, torch):
+    """Index structure from the seeded numpy generators; weights, grads and
+    per-sample weights drawn on the device with seeded torch generators."""
+    dev = "cuda"
+    off = spec.offsets()
+    idx = spec.indices()
+    d_off = torch.from_numpy(off).to(dev)
+    d_idx = torch.from_numpy(idx).to(dev)
+    wd = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[spec.wdtype]
+    W, M = [], []
+    for t in range(spec.T):
+        g = torch.Generator(device=dev).manual_seed(spec.seed * 1000 + 500 + t)
+        w = torch.rand((spec.rows[t], spec.dims[t]), generator=g, device=dev) * 0.2 - 0.1
+        W.append(w.to(wd).contiguous())
+        M.append(torch.zeros(spec.rows[t], dtype=torch.float32, device=dev))
+    g = torch.Generator(device=dev).manual_seed(spec.seed * 1000 + 400)
+    G = torch.randn((spec.B, spec.dtot), generator=g, device=dev)
+    psw = None
+    if spec.weighted:
+        g = torch.Generator(device=dev).manual_seed(spec.seed * 1000 + 300)
+        psw = torch.rand(int(off[-1]), generator=g, device=dev)
+    return off, idx, d_off, d_idx, W, M, G, psw
+
+
+# --------------------------------------------------------------- byte model
+
+def workload_stats(spec, off, idx):
+    """Per-table lookups, unique rows and run-length split (host, from the inputs)."""
+    B = spec.B
+    st = []
+    for t in range(spec.T):
+        lo, hi = int(off[t * B]), int(off[(t + 1) * B])
+        _, cnt = np.unique(idx[lo:hi], return_counts=True)
+        long_ = cnt >= 256
+        st.append(dict(n=hi - lo, U=int(cnt.size), n_short=int((~long_).sum()),
+                       n_long=int(long_.sum()), N_short=int(cnt[~long_].sum()),
+                       N_long=int(cnt[long_].sum()),
+                       chunks=int(((cnt[long_] + 255) // 256).sum()), D=spec.dims[t],
+                       mean=spec.pooling[t] == 1))
+    return st
+
+
+def byte_model(spec, st, hist_path):
+    """Compulsory bytes per kernel family per step: each stream read or written
+    once and each unique weight row once (a lower bound on HBM traffic), and the
+    logical bytes of every access the method makes."""
+    si = 4 if spec.itype == "i32" else 8
+    sw = 4 if spec.wdtype == "f32" else 2
+    psi = 1 if spec.weighted else 0
+    T, B = spec.T, spec.B
+    N = sum(s["n"] for s in st)
+    U = sum(s["U"] for s in st)
+    ntiles = -(-N // 4096)
+    key_bits = max(1, int(np.ceil(np.log2(max(2, sum(spec.rows))))))
+    npass = max(1, -(-key_bits // 8))
+    out_bytes = B * spec.dtot * 4
+    G_bytes = B * spec.dtot * 4
+    comp, logi = {}, {}
+    if hist_path:
+        E, D = spec.rows[0], spec.dims[0]
+        comp["fwd_hist"] = N * si + (B + 1) * si + E * D * sw + out_bytes
+        logi["fwd_hist"] = N * si + (B + 1) * si + N * D * sw + out_bytes
+    else:
+        comp["fwd_pool"] = (N * (si + 4 * psi) + (T * B + 1) * si + out_bytes
+                            + sum(s["U"] * s["D"] * sw for s in st))
+        logi["fwd_pool"] = (N * (si + 4 * psi) + (T * B + 1) * si + out_bytes
+                            + sum(s["n"] * s["D"] * sw for s in st))
+    comp["transpose"] = N * si + (T * B + 1) * si + 8 * N
+    comp["radix_upsweep"] = npass * 4 * N
+    comp["radix_scan"] = npass * 2 * 256 * ntiles * 4
+    comp["radix_downsweep"] = (12 + 16 * (npass - 1)) * N
+    comp["rle_count"] = 4 * N
+    comp["rle_scan"] = 8 * ntiles
+    comp["rle_write"] = 4 * N + 8 * U
+    comp["cls_count"] = 4 * (U + 1)
+    comp["cls_scan"] = 24 * ntiles
+    n_long = sum(s["n_long"] for s in st)
+    n_chunks = sum(s["chunks"] for s in st)
+    comp["cls_write"] = 8 * U + 16 * U + 24 * n_long + 16 * n_chunks
+    for k in list(comp):
+        logi.setdefault(k, comp[k])
+    cs = cl = cu = 0
+    ls = ll = 0
+    for s in st:
+        D = s["D"]
+        meta = 8 + 4 * psi + (2 * si if s["mean"] else 0)
+        g_share_s = G_bytes * s["N_short"] / max(N, 1)
+        g_share_l = G_bytes * s["N_long"] / max(N, 1)
+        cs += 16 * s["n_short"] + s["N_short"] * meta + g_share_s + s["n_short"] * (2 * D * sw + 8)
+        ls += 16 * s["n_short"] + s["N_short"] * (meta + 4 * D) + s["n_short"] * (2 * D * sw + 8)
+        cl += 16 * s["chunks"] + s["N_long"] * meta + g_share_l + 4 * s["chunks"] * D
+        ll += 16 * s["chunks"] + s["N_long"] * (meta + 4 * D) + 4 * s["chunks"] * D
+        cu += 16 * s["n_long"] + 4 * s["chunks"] * D + s["n_long"] * (2 * D * sw + 8)
+    comp["bwd_short"], logi["bwd_short"] = cs, ls
+    comp["bwd_chunk"], logi["bwd_chunk"] = cl, ll
+    comp["bwd_long_update"] = logi["bwd_long_update"] = cu
+    comp["bwd_chunk_fused"] = cl + cu
+    logi["bwd_chunk_fused"] = ll + cu
+    return comp, logi
+
+
+def source_hash(kernel):
+    f = KERNEL_SOURCES.get(kernel)
+    if f is None:
+        f = "prep.hip"
+    p = os.path.join(ROOT, "table_embedding_amd", "csrc", f)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def counter_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+        e = d[workload][kernel]
+    except (KeyError, ValueError):
+        return None
+    if e.get("source_sha256_16") != source_hash(kernel):
+        return None
+    return e.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------- CPU leg
+
+def cpu_baseline(spec, off, idx, W_dev, G_dev, psw_dev, cap, torch):
+    """The oracle (single-threaded C) on whole tables of the same workload."""
+    import oracle
+    B = spec.B
+    tables, n = [], 0
+    for t in range(spec.T):
+        nt = int(off[(t + 1) * B] - off[t * B])
+        if tables and n + nt > cap:
+            break
+        tables.append(t)
+        n += nt
+    sub = [t for t in tables]
+    rows = [spec.rows[t] for t in sub]
+    dims = [spec.dims[t] for t in sub]
+    pooling = [spec.pooling[t] for t in sub]
+    lo, hi = int(off[sub[0] * B]), int(off[(sub[-1] + 1) * B])
+    o = (off[sub[0] * B:(sub[-1] + 1) * B + 1].astype(np.int64) - lo).astype(off.dtype)
+    ix = idx[lo:hi]
+    col = spec.col_offsets()
+    c0, c1 = int(col[sub[0]]), int(col[sub[-1]]) + spec.dims[sub[-1]]
+    G = np.ascontiguousarray(G_dev[:, c0:c1].cpu().numpy())
+    psw = None if psw_dev is None else psw_dev[lo:hi].cpu().numpy()
+
+    def host(w):
+        w = w.detach().cpu()
+        return w.numpy().copy() if spec.wdtype == "f32" else w.view(torch.int16).numpy().view(np.uint16).copy()
+
+    W = [host(W_dev[t]) for t in sub]
+    M = [np.zeros(spec.rows[t], np.float32) for t in sub]
+    oracle.build(force=False)
+    t0 = time.perf_counter()
+    oracle.forward(rows, dims, pooling, spec.wdtype, W, B, spec.itype, ix, o, psw)
+    oracle.backward_rowwise_adagrad(rows, dims, pooling, spec.wdtype, W, M, B, spec.itype, ix, o,
+                                    psw, G, spec.lr, spec.eps)
+    dt = time.perf_counter() - t0
+    return {"value": (hi - lo) / dt, "unit": "lookups/s", "cores": 1, "kind": "oracle",
+            "sample": f"tables {sub[0]}..{sub[-1]} of {spec.T} ({hi - lo} lookups, all {B} bags), "
+                      f"one forward + backward pass, {dt:.2f} s on 1 of {os.cpu_count()} host "
+                      f"threads"}
+
+
+# -------------------------------------------------------------------- main
+
+def calibrate_copy(torch):
+    n = 1 << 30
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": n, "launches": 3}))
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (no multi-GPU path); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import table_embedding_amd as te
+    import tbe_workloads as wl
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    te.lib()  # fail loudly if the HIP library is missing
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
+    spec = wl.config(args.config)
+    print(f"[bench] generating {args.config}: {wl.DESCRIPTIONS[args.config]}", file=sys.stderr,
+          flush=True)
+    off, idx, d_off, d_idx, W, M, G, psw = device_inputs(spec, torch)
+    N = int(off[-1])
+    tb = te.TBE(spec.rows, spec.dims, spec.pooling, W, M)
+    ws = tb.workspace(spec.B, N)
+    out = torch.empty((spec.B, spec.dtot), dtype=torch.float32, device="cuda")
+    flags = te.TBE_BWD_FUSED_LONG if args.fused else 0
+    hist = (spec.T == 1 and spec.rows[0] <= 64 and 64 <= spec.dims[0] <= 128
+            and spec.wdtype == "f16" and not spec.weighted and N >= 64 * spec.B)
+
+    def step():
+        te.tbe_forward(tb.plan, spec.B, d_idx, d_off, N, psw, out)
+        te.tbe_backward_rowwise_adagrad(tb.plan, spec.B, d_idx, d_off, N, psw, G, spec.lr,
+                                        spec.eps, ws, flags)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps), timing {args.steps}", file=sys.stderr,
+          flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel durations: HIP events around each launch, on the launch stream
+    te.tbe_prof_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    prof = te.tbe_prof_read()
+    te.tbe_prof_enable(False)
+
+    st = workload_stats(spec, off, idx)
+    comp, logi = byte_model(spec, st, hist)
+    kernels = {}
+    for k, (n, tot) in prof.items():
+        per_step_ms = tot / args.steps
+        kernels[k] = {"launches_per_step": n / args.steps, "ms_per_step": round(per_step_ms, 5),
+                      "avg_launch_us": round(1000 * tot / n, 3),
+                      "compulsory_bytes_per_step": int(comp.get(k, 0)),
+                      "gbs_compulsory": round(comp.get(k, 0) / (per_step_ms * 1e6), 1)}
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    dk = kernels[dom]
+    launches = dk["launches_per_step"]
+    bytes_per_launch = comp.get(dom, 0) / launches
+    achieved = bytes_per_launch / (dk["avg_launch_us"] * 1e3)  # GB/s
+    traffic = counter_traffic(dom, args.config)
+    step_comp = sum(comp[k] for k in kernels if k in comp)
+    step_logi = sum(logi[k] for k in kernels if k in logi)
+    lookups_s = N / (ms / 1e3)
+    res = {
+        "metric": METRIC,
+        "value": round(lookups_s, 1),
+        "unit": "lookups/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.wdtype,
+        "data": "synthetic (seeded Zipf / uniform indices, device-drawn weights and grads)",
+        "config": {"workload": args.config, "description": wl.DESCRIPTIONS[args.config],
+                   "lookups": N, "tables": spec.T, "bags_per_table": spec.B,
+                   "index_type": spec.itype, "long_run_path": "fused" if args.fused else
+                   "two-launch", "step": "tbe_forward + tbe_backward_rowwise_adagrad"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "hbm": {"compulsory_bytes_per_step": int(step_comp),
+                "achieved_gbs_compulsory": round(step_comp / (ms * 1e6), 1),
+                "frac_of_peak_compulsory": round(step_comp / (ms * 1e6) / HBM_PEAK_GBS, 4),
+                "logical_bytes_per_step": int(step_logi),
+                "effective_gbs_logical": round(step_logi / (ms * 1e6), 1)},
+        "kernels": kernels,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(spec, off, idx, W, G, psw, args.cpu_sample_lookups,
+                                           torch)
+    tb.close()
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()
