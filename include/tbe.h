@@ -95,16 +95,20 @@ typedef struct tbe_plan tbe_plan;
  * uint32. */
 typedef struct {
   size_t sorted_key;   /* num_lookups keys, ascending */
-  size_t sorted_pos;   /* num_lookups lookup positions, stable (ties ascending) */
-  size_t bag;          /* num_lookups bag ids j, indexed by lookup position */
+  size_t sorted_bag;   /* num_lookups bag ids j of the sorted lookups; the sort is stable,
+                          so equal keys keep lookup-position order */
+  size_t sorted_scale; /* num_lookups float S[p]*(1/L if mean) of the sorted lookups; written
+                          only with per-sample weights or a mean table */
   size_t run_start;    /* U+1 entries: first sorted slot of each run, then num_lookups */
   size_t run_key;      /* U keys, one per run */
-  size_t short_task;   /* n_short uint32x4 {start, len, row, table}: runs with SL < 256 */
+  size_t tiny_task;    /* n_tiny uint32x4 {start, row, table<<16 | len, bag of the first
+                          lookup}: short runs with SL < 32 */
+  size_t medium_task;  /* n_medium uint32x4 {start, len, row, table}: short runs, 32 <= SL < 256 */
   size_t long_task;    /* n_long uint32x4 {start, len, row, table}: runs with SL >= 256 */
   size_t long_cbeg;    /* n_long first chunk index of each long run */
   size_t chunk_task;   /* n_chunks uint32x4 {start, len, table, long index}: 256-lookup chunks */
-  size_t counters;     /* uint32 {U, n_short, n_long, n_chunks,
-                          short_begin[nb+1], long_begin[nb+1], chunk_begin[nb+1]} per D bucket */
+  size_t counters;     /* uint32 {U, n_tiny, n_medium, n_long, n_chunks, then for each of
+                          the four lists its nb+1 per-D-bucket begins} */
   size_t total;        /* bytes needed */
   int32_t num_buckets; /* nb */
 } tbe_ws_views;
@@ -147,15 +151,17 @@ int tbe_forward(const tbe_plan* plan, int64_t B, int32_t itype, const void* indi
  * sort, run-length encoding; classification of runs at SL 256 and task-list
  * compaction with device-resident counts).  Fills the workspace for a later
  * tbe_backward_rowwise_adagrad(..., TBE_BWD_PREPROCESSED) with the same
- * indices and offsets, in stream order.  ws: device, >= tbe_workspace_size
- * bytes, 256-byte aligned. */
+ * indices, offsets and per-sample weights, in stream order (the contribution
+ * scale S[p]*(1/L if mean) is folded in here).  ws: device,
+ * >= tbe_workspace_size bytes, 256-byte aligned. */
 int tbe_preprocess(const tbe_plan* plan, int64_t B, int32_t itype, const void* indices,
-                   const void* offsets, int64_t num_lookups, void* ws, size_t ws_bytes,
-                   void* stream);
+                   const void* offsets, int64_t num_lookups, const float* per_sample_weights,
+                   void* ws, size_t ws_bytes, void* stream);
 
 /* Backward with exact row-wise Adagrad applied once per touched row.
- * Preprocesses unless TBE_BWD_PREPROCESSED, then updates runs with SL < 256
- * in one owner pass and runs with SL >= 256 through 256-lookup chunk partial
+ * Preprocesses unless TBE_BWD_PREPROCESSED, then updates each run with
+ * SL < 256 in one owning program (a lane subgroup below SL 32, a workgroup
+ * from 32 to 255) and runs with SL >= 256 through 256-lookup chunk partial
  * sums plus an update pass (or, with TBE_BWD_FUSED_LONG, a device-scope fence
  * and countdown so the last chunk of a run updates it; both give bit-identical
  * weights).  Weights and momentum of touched rows are updated in place;

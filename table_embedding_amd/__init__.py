@@ -72,9 +72,10 @@ class TBE:
                     flags)
         return out
 
-    def preprocess(self, B: int, indices: torch.Tensor, offsets: torch.Tensor) -> torch.Tensor:
+    def preprocess(self, B: int, indices: torch.Tensor, offsets: torch.Tensor,
+                   per_sample_weights: Optional[torch.Tensor] = None) -> torch.Tensor:
         ws = self.workspace(B, indices.numel())
-        tbe_preprocess(self.plan, B, indices, offsets, indices.numel(), ws)
+        tbe_preprocess(self.plan, B, indices, offsets, indices.numel(), per_sample_weights, ws)
         return ws
 
     def backward(self, B: int, indices: torch.Tensor, offsets: torch.Tensor,

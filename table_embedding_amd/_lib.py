@@ -43,8 +43,9 @@ class TBEError(RuntimeError):
 
 
 class WsViews(C.Structure):
-    _fields_ = [(n, C.c_size_t) for n in ("sorted_key", "sorted_pos", "bag", "run_start",
-                                           "run_key", "short_task", "long_task", "long_cbeg",
+    _fields_ = [(n, C.c_size_t) for n in ("sorted_key", "sorted_bag",
+                                           "sorted_scale", "run_start", "run_key", "tiny_task",
+                                           "medium_task", "long_task", "long_cbeg",
                                            "chunk_task", "counters", "total")] + [
         ("num_buckets", C.c_int32)]
 
@@ -67,7 +68,7 @@ def lib() -> C.CDLL:
         L.tbe_workspace_size.argtypes = [vp, i64, i64, C.POINTER(C.c_size_t)]
         L.tbe_workspace_views.argtypes = [vp, i64, i64, C.POINTER(WsViews)]
         L.tbe_forward.argtypes = [vp, i64, i32, vp, vp, i64, vp, vp, u32, vp]
-        L.tbe_preprocess.argtypes = [vp, i64, i32, vp, vp, i64, vp, C.c_size_t, vp]
+        L.tbe_preprocess.argtypes = [vp, i64, i32, vp, vp, i64, vp, vp, C.c_size_t, vp]
         L.tbe_backward_rowwise_adagrad.argtypes = [vp, i64, i32, vp, vp, i64, vp, vp,
                                                    C.c_float, C.c_float, vp, C.c_size_t, u32,
                                                    vp, vp]
@@ -180,11 +181,12 @@ def tbe_forward(plan, B: int, indices, offsets, num_lookups: int, per_sample_wei
     _check("tbe_forward", rc)
 
 
-def tbe_preprocess(plan, B: int, indices, offsets, num_lookups: int, ws: torch.Tensor,
-                   stream=None) -> None:
+def tbe_preprocess(plan, B: int, indices, offsets, num_lookups: int, per_sample_weights,
+                   ws: torch.Tensor, stream=None) -> None:
     it = _itype(indices, offsets)
     rc = lib().tbe_preprocess(plan, int(B), it, _dptr(indices, None, "indices"),
                               _dptr(offsets, None, "offsets"), int(num_lookups),
+                              _dptr(per_sample_weights, torch.float32, "per_sample_weights"),
                               _dptr(ws, None, "ws"), ws.numel() * ws.element_size(),
                               _stream(stream))
     _check("tbe_preprocess", rc)

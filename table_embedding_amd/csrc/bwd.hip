@@ -1,131 +1,164 @@
 // Backward with exact row-wise Adagrad, once per touched row (FBTriton TBE
-// page, "Backward": runs with SL < 256 are gathered, accumulated in registers
-// and updated by one owner with plain stores; runs with SL >= 256 are cut into
-// 256-lookup chunks whose partial sums are stored and then reduced by a second
-// kernel, or, in the fused form, each chunk fences its partial and decrements a
-// countdown so that only the last chunk updates the row.  Section "Fusion
-// boundaries": per-sample weights scale each contribution before grouping and
-// the optimizer runs as the epilogue).
+// page, "Backward": a run with SL < 256 is gathered, accumulated and updated by
+// one program that owns the row and writes it with plain stores; a run with
+// SL >= 256 is cut into 256-lookup chunks whose partial sums are stored and
+// reduced by a second kernel, or, in the fused form, each chunk fences its
+// partial and decrements a countdown so that only the last chunk updates the
+// row.  Section "Fusion boundaries": per-sample weights scale each
+// contribution before grouping and the optimizer runs as the epilogue).
 //
-// Every kernel is persistent over a task list whose length lives in device
-// memory (no host readback).  Row updates read the gradient rows of the bags
-// that used the row (random 16-byte column slices of grad_out), so the path is
-// HBM/L2 bandwidth- and latency-bound; gathers keep four lookups in flight.
+// Programs.  Short runs with SL < 32 are owned by a subgroup of `lpr` lanes
+// (one row of the bucket width); short runs with 32 <= SL < 256 by a whole
+// 256-thread workgroup whose subgroups split the lookups; chunks and long-run
+// updates by a workgroup.  Every kernel is persistent over a task list whose
+// length it reads from device memory (no host readback).
 //
-// Determinism: a long run's gradient is the sum of its chunk partials, chunk
-// k folded into subgroup (k mod nsg) in ascending k, subgroups combined in
-// ascending order, the square-sum reduced in a fixed tree.  The two-launch
-// update and the fused last-chunk update call the same workgroup routine, so
-// the two give bit-identical weights.
+// Memory.  Per lookup the kernels read the bag id (and the contribution scale)
+// of the sorted lookup with the sorted order, then one 16-byte column slice of
+// the bag's grad_out row; eight lookups are kept in flight per lane.  A tiny
+// task carries the bag of its first lookup, so an SL = 1 run costs one task
+// load, then the grad_out row, weight row and momentum in parallel.
+//
+// Determinism.  Sums run in lookup order inside a subgroup; workgroup sums
+// combine subgroups in ascending order; the square sum is reduced in a fixed
+// tree.  A long run's gradient is the sum of its chunk partials, chunk k folded
+// into subgroup (k mod nsg) in ascending k.  The two-launch update and the
+// fused last-chunk update call the same workgroup routine, so the two give
+// bit-identical weights.
 #include "tbe_common.h"
 
 namespace tbe {
 namespace {
 
-constexpr int kGatherInFlight = 4;
+constexpr int kInFlight = 8;
+constexpr int kTdCache = 128;  // table descriptors cached in LDS by the tiny-run kernel
 
-// Per-lookup contribution scale S[p] * (1/L if mean) and grad_out row.
-__device__ __forceinline__ void lookup_meta(const BwdArgs& a, uint32_t pos, int64_t tB, bool mean,
-                                            float& sc, int64_t& b) {
-  const uint32_t j = a.bag[pos];
-  b = (int64_t)j - tB;
-  sc = a.psw ? a.psw[pos] : 1.0f;
-  if (mean) {
-    const int64_t L = load_idx(a.offsets, a.itype, (int64_t)j + 1) - load_idx(a.offsets, a.itype, j);
-    sc = sc / (float)L;
+// Accumulate sorted slots [i0, i1) with stride `step` into g (this lane's
+// columns `cold`, already clamped into the row for idle lanes).  Eight lookups
+// per batch: bag ids (and scales), then the eight grad_out slices, then the
+// sums in lookup order; scheduling barriers keep the loads of a batch in
+// flight together.  A partial batch repeats the last slot and drops the
+// repeats with a select (no branches inside the batch).
+template <int VEC, int NC, bool SCALE>
+__device__ __forceinline__ void gather_t(const BwdArgs& a, const TableDev& td, int64_t tB,
+                                         uint32_t i0, uint32_t i1, uint32_t step,
+                                         const uint32_t* cold, float (*g)[VEC]) {
+  const float* gbase = a.grad + td.col;
+  for (uint32_t i = i0; i < i1; i += kInFlight * step) {
+    int64_t b[kInFlight];
+    float sc[kInFlight];
+    bool ok[kInFlight];
+#pragma unroll
+    for (int k = 0; k < kInFlight; ++k) {
+      const uint32_t q0 = i + (uint32_t)k * step;
+      ok[k] = q0 < i1;
+      const uint32_t q = ok[k] ? q0 : i1 - 1;
+      b[k] = (int64_t)a.sorted_bag[q] - tB;
+      sc[k] = SCALE ? a.sorted_scale[q] : 1.0f;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float v[kInFlight][VEC];
+#pragma unroll
+      for (int k = 0; k < kInFlight; ++k)
+        load_f32<VEC>(gbase + b[k] * (int64_t)a.dtot + cold[c], v[k]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < kInFlight; ++k)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) g[c][e] += ok[k] ? sc[k] * v[k][e] : 0.0f;
+    }
   }
 }
 
-// Accumulate lookups [i0, i1) with stride `step` of sorted slots into g.
 template <int VEC, int NC>
 __device__ __forceinline__ void gather(const BwdArgs& a, const TableDev& td, int64_t tB,
                                        uint32_t i0, uint32_t i1, uint32_t step,
-                                       const uint32_t* colc, const bool* act, float (*g)[VEC]) {
-  const bool mean = td.pooling == POOL_MEAN;
-  const float* gbase = a.grad + td.col;
-  uint32_t i = i0;
-  for (; i + (kGatherInFlight - 1) * step < i1; i += kGatherInFlight * step) {
-    uint32_t pos[kGatherInFlight];
-#pragma unroll
-    for (int k = 0; k < kGatherInFlight; ++k) pos[k] = a.sorted_pos[i + k * step];
-    float sc[kGatherInFlight];
-    int64_t b[kGatherInFlight];
-#pragma unroll
-    for (int k = 0; k < kGatherInFlight; ++k) lookup_meta(a, pos[k], tB, mean, sc[k], b[k]);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (!act[c]) continue;
-      float v[kGatherInFlight][VEC];
-#pragma unroll
-      for (int k = 0; k < kGatherInFlight; ++k)
-        load_f32<VEC>(gbase + b[k] * (int64_t)a.dtot + colc[c], v[k]);
-#pragma unroll
-      for (int k = 0; k < kGatherInFlight; ++k)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) g[c][e] += sc[k] * v[k][e];
-    }
-  }
-  for (; i < i1; i += step) {
-    const uint32_t pos = a.sorted_pos[i];
-    float sc;
-    int64_t b;
-    lookup_meta(a, pos, tB, mean, sc, b);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (!act[c]) continue;
-      float v[VEC];
-      load_f32<VEC>(gbase + b * (int64_t)a.dtot + colc[c], v);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) g[c][e] += sc * v[e];
-    }
-  }
+                                       const uint32_t* cold, float (*g)[VEC]) {
+  if (a.sorted_scale)
+    gather_t<VEC, NC, true>(a, td, tB, i0, i1, step, cold, g);
+  else
+    gather_t<VEC, NC, false>(a, td, tB, i0, i1, step, cold, g);
 }
 
 // Sanity bounds of list entries (they hold for every list the preprocessing
 // writes; a stale or foreign workspace is skipped instead of read out of bounds).
+__device__ __forceinline__ bool span_ok(const BwdArgs& a, uint32_t start, uint32_t len,
+                                        uint32_t t, uint32_t row) {
+  return t < a.T && start <= a.N && len <= a.N - start && row < a.tables[t].rows;
+}
 __device__ __forceinline__ bool chunk_ok(const BwdArgs& a, uint4 task) {
   return task.z < a.T && task.x <= a.N && task.y <= a.N - task.x && task.y <= (uint32_t)kChunk &&
          task.w < a.max_long;
 }
 __device__ __forceinline__ bool long_ok(const BwdArgs& a, uint32_t l) {
   const uint4 t = a.long_task[l];
-  if (t.w >= a.T || t.x > a.N || t.y > a.N - t.x || t.z >= a.tables[t.w].rows) return false;
+  if (!span_ok(a, t.x, t.y, t.w, t.z)) return false;
   const uint32_t nch = (t.y + kChunk - 1) / kChunk;
   const uint32_t cb = a.long_cbeg[l];
   return cb <= a.max_chunks && nch <= a.max_chunks - cb;
 }
 
-// --------------------------------------------------------------- short runs
-// One subgroup of lpr lanes owns a run: gather, Adagrad, plain stores.
+__device__ __forceinline__ uint32_t list_begin(const BwdArgs& a, int list, uint32_t bucket) {
+  return a.counters[kCntBegins + list * (a.nb + 1) + bucket];
+}
+
+// --------------------------------------------------------- tiny short runs
+// One subgroup of lpr lanes owns a run with SL < 32: gather, Adagrad, plain stores.
 template <int WD, int VEC, int NC>
-__global__ __launch_bounds__(kThreads) void bwd_short_kernel(BwdArgs a, BucketDev bk,
-                                                             uint32_t bucket) {
+__global__ __launch_bounds__(kThreads) void bwd_tiny_kernel(BwdArgs a, BucketDev bk,
+                                                            uint32_t bucket) {
   const uint32_t lpr = bk.lpr;
   const uint32_t lane_in = threadIdx.x & (lpr - 1);
   const uint32_t nsg_grid = (gridDim.x * kThreads) >> bk.lpr_log2;
   const uint32_t sg = (blockIdx.x * kThreads + threadIdx.x) >> bk.lpr_log2;
-  const uint32_t beg = a.counters[kCntBegins + bucket];
-  const uint32_t end = min(a.counters[kCntBegins + bucket + 1], a.max_short);
-  for (uint32_t s = beg + sg; s < end; s += nsg_grid) {
-    const uint4 task = a.short_task[s];  // {start, len, row, table}
-    if (task.w >= a.T || task.x > a.N || task.y > a.N - task.x) continue;  // never for valid lists
-    const TableDev td = a.tables[task.w];
-    if (task.z >= td.rows) continue;
+  // descriptors of the first kTdCache tables live in LDS (one load per task saved)
+  __shared__ TableDev s_td[kTdCache];
+  for (uint32_t i = threadIdx.x; i < a.T && i < (uint32_t)kTdCache; i += kThreads)
+    s_td[i] = a.tables[i];
+  __syncthreads();
+  const uint32_t beg = list_begin(a, 0, bucket);
+  const uint32_t end = min(list_begin(a, 0, bucket + 1), a.max_tiny);
+  uint32_t s = beg + sg;
+  uint4 next = s < end ? a.tiny_task[s] : make_uint4(0, 0, 0, 0);
+  for (; s < end; s += nsg_grid) {
+    const uint4 task = next;  // {start, row, table << 16 | len, bag of the first lookup}
+    if (s + nsg_grid < end) next = a.tiny_task[s + nsg_grid];
+    const uint32_t start = task.x, t = task.z >> 16, len = task.z & 0xffffu;
+    const int64_t row = task.y;
+    // sanity bounds, never false for lists the preprocessing wrote
+    if (len == 0 || t >= a.T || start > a.N || len > a.N - start) continue;
+    const TableDev td = t < (uint32_t)kTdCache ? s_td[t] : a.tables[t];
+    if (task.y >= td.rows) continue;
     const uint32_t D = td.dim;
-    const int64_t row = task.z;
-    uint32_t colc[NC];
+    const int64_t tB = (int64_t)t * a.B;
+    uint32_t colc[NC], cold[NC];
     bool act[NC];
     float w[NC][VEC], g[NC][VEC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       colc[c] = (lane_in + (uint32_t)c * lpr) * VEC;
       act[c] = colc[c] < D;
-      if (act[c]) load_w<WD, VEC>(td.w, row * D + colc[c], w[c]);
+      cold[c] = act[c] ? colc[c] : 0u;
+      load_w<WD, VEC>(td.w, row * D + cold[c], w[c]);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) g[c][e] = 0.f;
     }
     const float m0 = td.m[row];
-    gather<VEC, NC>(a, td, (int64_t)task.w * a.B, task.x, task.x + task.y, 1u, colc, act, g);
+    if (len == 1) {
+      // the task carries the only lookup's bag: no dependent load before grad_out
+      const int64_t b0 = (int64_t)task.w - tB;
+      const float sc0 = a.sorted_scale ? a.sorted_scale[start] : 1.0f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        load_f32<VEC>(a.grad + b0 * (int64_t)a.dtot + td.col + cold[c], g[c]);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) g[c][e] *= sc0;
+      }
+    } else {
+      gather<VEC, NC>(a, td, tB, start, start + len, 1u, cold, g);
+    }
     float sq = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
@@ -150,37 +183,35 @@ __global__ __launch_bounds__(kThreads) void bwd_short_kernel(BwdArgs a, BucketDe
   }
 }
 
-// ---------------------------------------------------------------- long runs
+// ------------------------------------------------------ workgroup routines
 
 template <int VEC, int NC>
-struct LongSmem {
-  float red[kThreads * VEC * NC];  // [nsg][bucket width] per-subgroup sums
-  float gsum[kThreads * VEC * NC / 1];
+struct WgSmem {
+  float red[kThreads * VEC * NC];   // [nsg][bucket width] per-subgroup sums
+  float gsum[kThreads * VEC * NC];  // the row gradient
   float wsq[kThreads / kWave];
   uint32_t last;
 };
 
-// Chunk partial: the workgroup sums the chunk's <= 256 lookups; subgroup sg
-// takes slots start+sg, start+sg+nsg, ...; subgroups are combined in order.
+// Subgroup sg accumulates sorted slots i0+sg, i0+sg+nsg, ... < i1 into sm.red.
 template <int VEC, int NC>
-__device__ __forceinline__ void chunk_partial(const BwdArgs& a, const BucketDev& bk, uint4 task,
-                                              LongSmem<VEC, NC>& sm) {
+__device__ __forceinline__ void wg_gather(const BwdArgs& a, const BucketDev& bk,
+                                          const TableDev& td, uint32_t t, uint32_t i0,
+                                          uint32_t i1, WgSmem<VEC, NC>& sm) {
   const uint32_t lpr = bk.lpr, lane_in = threadIdx.x & (lpr - 1);
   const uint32_t sg = threadIdx.x >> bk.lpr_log2, nsg = kThreads >> bk.lpr_log2;
   const uint32_t width = lpr * VEC * NC;
-  const TableDev td = a.tables[task.z];
   const uint32_t D = td.dim;
-  uint32_t colc[NC];
-  bool act[NC];
+  uint32_t colc[NC], cold[NC];
   float g[NC][VEC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     colc[c] = (lane_in + (uint32_t)c * lpr) * VEC;
-    act[c] = colc[c] < D;
+    cold[c] = colc[c] < D ? colc[c] : 0u;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) g[c][e] = 0.f;
   }
-  gather<VEC, NC>(a, td, (int64_t)task.z * a.B, task.x + sg, task.x + task.y, nsg, colc, act, g);
+  gather<VEC, NC>(a, td, (int64_t)t * a.B, i0 + sg, i1, nsg, cold, g);
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -188,25 +219,53 @@ __device__ __forceinline__ void chunk_partial(const BwdArgs& a, const BucketDev&
   __syncthreads();
 }
 
-// Write the combined chunk partial (ascending subgroup order) to partial[c].
+// Column sums of sm.red in ascending subgroup order into sm.gsum; returns this
+// thread's share of sum_d g[d]^2.
 template <int VEC, int NC>
-__device__ __forceinline__ void chunk_store(const BwdArgs& a, const BucketDev& bk, uint32_t D,
-                                            uint32_t c, LongSmem<VEC, NC>& sm) {
+__device__ __forceinline__ float red_to_gsum(const BucketDev& bk, uint32_t D,
+                                             WgSmem<VEC, NC>& sm) {
   const uint32_t nsg = kThreads >> bk.lpr_log2;
   const uint32_t width = bk.lpr * VEC * NC;
-  float* dst = a.partial + (size_t)c * a.pstride;
+  float sqp = 0.f;
   for (uint32_t col = threadIdx.x; col < D; col += kThreads) {
     float s = 0.f;
     for (uint32_t k = 0; k < nsg; ++k) s += sm.red[k * width + col];
-    dst[col] = s;
+    sm.gsum[col] = s;
+    sqp += s * s;
+  }
+  return sqp;
+}
+
+// Row-wise Adagrad of one row from sm.gsum, all threads of the workgroup.
+template <int WD, int VEC, int NC>
+__device__ __forceinline__ void wg_row_update(const BwdArgs& a, const TableDev& td, int64_t row,
+                                              float sqp, WgSmem<VEC, NC>& sm) {
+  const uint32_t D = td.dim;
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) sqp += __shfl_xor(sqp, o, kWave);
+  if (lane_id() == 0) sm.wsq[threadIdx.x / kWave] = sqp;
+  __syncthreads();
+  const float sq = ((sm.wsq[0] + sm.wsq[1]) + sm.wsq[2]) + sm.wsq[3];
+  const float m = td.m[row] + sq / (float)D;
+  const float den = sqrtf(m) + a.eps;
+  for (uint32_t col = threadIdx.x * VEC; col < D; col += kThreads * VEC) {
+    float w[VEC], o[VEC];
+    load_w<WD, VEC>(td.w, row * D + col, w);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) o[e] = w[e] - (a.lr * sm.gsum[col + e]) / den;
+    store_w<WD, VEC>(td.w, row * D + col, o);
+  }
+  __syncthreads();  // every thread has read td.m[row] and sm before they change
+  if (threadIdx.x == 0) {
+    td.m[row] = m;
+    if (a.debug_count) atomicAdd(&a.debug_count[td.key_base + (uint32_t)row], 1u);
   }
 }
 
 // Long-run update: reduce the run's chunk partials, then row-wise Adagrad.
-// All 256 threads of the workgroup take part.
 template <int WD, int VEC, int NC>
 __device__ __forceinline__ void long_update(const BwdArgs& a, const BucketDev& bk, uint32_t l,
-                                            LongSmem<VEC, NC>& sm) {
+                                            WgSmem<VEC, NC>& sm) {
   const uint32_t lpr = bk.lpr, lane_in = threadIdx.x & (lpr - 1);
   const uint32_t sg = threadIdx.x >> bk.lpr_log2, nsg = kThreads >> bk.lpr_log2;
   const uint32_t width = lpr * VEC * NC;
@@ -215,7 +274,6 @@ __device__ __forceinline__ void long_update(const BwdArgs& a, const BucketDev& b
   const uint32_t nch = (task.y + kChunk - 1) / kChunk;
   const TableDev td = a.tables[task.w];
   const uint32_t D = td.dim;
-  const int64_t row = task.z;
   float g[NC][VEC];
   uint32_t colc[NC];
 #pragma unroll
@@ -240,47 +298,57 @@ __device__ __forceinline__ void long_update(const BwdArgs& a, const BucketDev& b
 #pragma unroll
     for (int e = 0; e < VEC; ++e) sm.red[sg * width + colc[c] + e] = g[c][e];
   __syncthreads();
-  float sqp = 0.f;
+  const float sqp = red_to_gsum<VEC, NC>(bk, D, sm);
+  wg_row_update<WD, VEC, NC>(a, td, (int64_t)task.z, sqp, sm);
+}
+
+// Write the combined chunk partial (ascending subgroup order) to partial[c].
+template <int VEC, int NC>
+__device__ __forceinline__ void chunk_store(const BwdArgs& a, const BucketDev& bk, uint32_t D,
+                                            uint32_t c, WgSmem<VEC, NC>& sm) {
+  const uint32_t nsg = kThreads >> bk.lpr_log2;
+  const uint32_t width = bk.lpr * VEC * NC;
+  float* dst = a.partial + (size_t)c * a.pstride;
   for (uint32_t col = threadIdx.x; col < D; col += kThreads) {
     float s = 0.f;
     for (uint32_t k = 0; k < nsg; ++k) s += sm.red[k * width + col];
-    sm.gsum[col] = s;
-    sqp += s * s;
-  }
-  // fixed-order reduction of the square sum: butterfly in the wave, waves in order
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) sqp += __shfl_xor(sqp, o, kWave);
-  if (lane_id() == 0) sm.wsq[threadIdx.x / kWave] = sqp;
-  __syncthreads();
-  const float sq = ((sm.wsq[0] + sm.wsq[1]) + sm.wsq[2]) + sm.wsq[3];
-  const float m = td.m[row] + sq / (float)D;
-  const float den = sqrtf(m) + a.eps;
-  for (uint32_t col = threadIdx.x * VEC; col < D; col += kThreads * VEC) {
-    float w[VEC], o[VEC];
-    load_w<WD, VEC>(td.w, row * D + col, w);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) o[e] = w[e] - (a.lr * sm.gsum[col + e]) / den;
-    store_w<WD, VEC>(td.w, row * D + col, o);
-  }
-  __syncthreads();  // every thread has read td.m[row] and gsum before they change
-  if (threadIdx.x == 0) {
-    td.m[row] = m;
-    if (a.debug_count) atomicAdd(&a.debug_count[td.key_base + (uint32_t)row], 1u);
+    dst[col] = s;
   }
 }
+
+// ------------------------------------------------------- medium short runs
+// One workgroup owns a run with 32 <= SL < 256: its subgroups split the
+// lookups, the workgroup combines them in LDS and updates the row.
+template <int WD, int VEC, int NC>
+__global__ __launch_bounds__(kThreads) void bwd_medium_kernel(BwdArgs a, BucketDev bk,
+                                                              uint32_t bucket) {
+  __shared__ WgSmem<VEC, NC> sm;
+  const uint32_t beg = list_begin(a, 1, bucket);
+  const uint32_t end = min(list_begin(a, 1, bucket + 1), a.max_med);
+  for (uint32_t m = beg + blockIdx.x; m < end; m += gridDim.x) {
+    const uint4 task = a.med_task[m];  // {start, len, row, table}
+    if (!span_ok(a, task.x, task.y, task.w, task.z)) continue;  // uniform; never for valid lists
+    const TableDev td = a.tables[task.w];
+    wg_gather<VEC, NC>(a, bk, td, task.w, task.x, task.x + task.y, sm);
+    const float sqp = red_to_gsum<VEC, NC>(bk, td.dim, sm);
+    wg_row_update<WD, VEC, NC>(a, td, (int64_t)task.z, sqp, sm);
+  }
+}
+
+// ---------------------------------------------------------------- long runs
 
 template <int WD, int VEC, int NC>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a, BucketDev bk,
                                                              uint32_t bucket) {
-  __shared__ LongSmem<VEC, NC> sm;
-  const uint32_t nb1 = a.nb + 1;
-  const uint32_t beg = a.counters[kCntBegins + 2 * nb1 + bucket];
-  const uint32_t end = min(a.counters[kCntBegins + 2 * nb1 + bucket + 1], a.max_chunks);
+  __shared__ WgSmem<VEC, NC> sm;
+  const uint32_t beg = list_begin(a, 3, bucket);
+  const uint32_t end = min(list_begin(a, 3, bucket + 1), a.max_chunks);
   for (uint32_t c = beg + blockIdx.x; c < end; c += gridDim.x) {
     const uint4 task = a.chunk_task[c];  // {start, len, table, long index}
     if (!chunk_ok(a, task)) continue;    // uniform per workgroup; never for valid lists
-    chunk_partial<VEC, NC>(a, bk, task, sm);
-    chunk_store<VEC, NC>(a, bk, a.tables[task.z].dim, c, sm);
+    const TableDev td = a.tables[task.z];
+    wg_gather<VEC, NC>(a, bk, td, task.z, task.x, task.x + task.y, sm);
+    chunk_store<VEC, NC>(a, bk, td.dim, c, sm);
     __syncthreads();
   }
 }
@@ -288,10 +356,9 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a, BucketDe
 template <int WD, int VEC, int NC>
 __global__ __launch_bounds__(kThreads) void bwd_long_update_kernel(BwdArgs a, BucketDev bk,
                                                                    uint32_t bucket) {
-  __shared__ LongSmem<VEC, NC> sm;
-  const uint32_t nb1 = a.nb + 1;
-  const uint32_t beg = a.counters[kCntBegins + nb1 + bucket];
-  const uint32_t end = min(a.counters[kCntBegins + nb1 + bucket + 1], a.max_long);
+  __shared__ WgSmem<VEC, NC> sm;
+  const uint32_t beg = list_begin(a, 2, bucket);
+  const uint32_t end = min(list_begin(a, 2, bucket + 1), a.max_long);
   for (uint32_t l = beg + blockIdx.x; l < end; l += gridDim.x) {
     if (!long_ok(a, l)) continue;  // uniform per workgroup; never for valid lists
     long_update<WD, VEC, NC>(a, bk, l, sm);
@@ -304,15 +371,15 @@ __global__ __launch_bounds__(kThreads) void bwd_long_update_kernel(BwdArgs a, Bu
 template <int WD, int VEC, int NC>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_fused_kernel(BwdArgs a, BucketDev bk,
                                                                    uint32_t bucket) {
-  __shared__ LongSmem<VEC, NC> sm;
-  const uint32_t nb1 = a.nb + 1;
-  const uint32_t beg = a.counters[kCntBegins + 2 * nb1 + bucket];
-  const uint32_t end = min(a.counters[kCntBegins + 2 * nb1 + bucket + 1], a.max_chunks);
+  __shared__ WgSmem<VEC, NC> sm;
+  const uint32_t beg = list_begin(a, 3, bucket);
+  const uint32_t end = min(list_begin(a, 3, bucket + 1), a.max_chunks);
   for (uint32_t c = beg + blockIdx.x; c < end; c += gridDim.x) {
     const uint4 task = a.chunk_task[c];  // {start, len, table, long index}
     if (!chunk_ok(a, task) || !long_ok(a, task.w)) continue;  // uniform; never for valid lists
-    chunk_partial<VEC, NC>(a, bk, task, sm);
-    chunk_store<VEC, NC>(a, bk, a.tables[task.z].dim, c, sm);
+    const TableDev td = a.tables[task.z];
+    wg_gather<VEC, NC>(a, bk, td, task.z, task.x, task.x + task.y, sm);
+    chunk_store<VEC, NC>(a, bk, td.dim, c, sm);
     __threadfence();  // this thread's partial stores are visible device-wide
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -335,17 +402,19 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_fused_kernel(BwdArgs a, Bu
 }
 
 template <int WD, int VEC, int NC>
-hipError_t launch(const BwdArgs& a, const BucketDev& bk, uint32_t bucket, bool fused, int grid,
-                  hipStream_t s) {
-  TBE_LAUNCH("bwd_short", (bwd_short_kernel<WD, VEC, NC>), dim3(grid), dim3(kThreads), s, a, bk,
+hipError_t launch(const BwdArgs& a, const BucketDev& bk, uint32_t bucket, bool fused,
+                  const BwdGrids& g, hipStream_t s) {
+  TBE_LAUNCH("bwd_tiny", (bwd_tiny_kernel<WD, VEC, NC>), dim3(g.tiny), dim3(kThreads), s, a, bk,
              bucket);
+  TBE_LAUNCH("bwd_medium", (bwd_medium_kernel<WD, VEC, NC>), dim3(g.medium), dim3(kThreads), s,
+             a, bk, bucket);
   if (fused) {
-    TBE_LAUNCH("bwd_chunk_fused", (bwd_chunk_fused_kernel<WD, VEC, NC>), dim3(grid),
+    TBE_LAUNCH("bwd_chunk_fused", (bwd_chunk_fused_kernel<WD, VEC, NC>), dim3(g.chunk),
                dim3(kThreads), s, a, bk, bucket);
   } else {
-    TBE_LAUNCH("bwd_chunk", (bwd_chunk_kernel<WD, VEC, NC>), dim3(grid), dim3(kThreads), s, a,
+    TBE_LAUNCH("bwd_chunk", (bwd_chunk_kernel<WD, VEC, NC>), dim3(g.chunk), dim3(kThreads), s, a,
                bk, bucket);
-    TBE_LAUNCH("bwd_long_update", (bwd_long_update_kernel<WD, VEC, NC>), dim3(grid),
+    TBE_LAUNCH("bwd_long_update", (bwd_long_update_kernel<WD, VEC, NC>), dim3(g.longrun),
                dim3(kThreads), s, a, bk, bucket);
   }
   return hipGetLastError();
@@ -354,9 +423,9 @@ hipError_t launch(const BwdArgs& a, const BucketDev& bk, uint32_t bucket, bool f
 }  // namespace
 
 hipError_t launch_backward_bucket(const BwdArgs& a, const BucketDev& bk, uint32_t bucket, int wd,
-                                  int vec, int nc, bool fused, int grid, hipStream_t s) {
+                                  int vec, int nc, bool fused, const BwdGrids& g, hipStream_t s) {
 #define TBE_BWD_CASE(W, V, N) \
-  if (wd == W && vec == V && nc == N) return launch<W, V, N>(a, bk, bucket, fused, grid, s);
+  if (wd == W && vec == V && nc == N) return launch<W, V, N>(a, bk, bucket, fused, g, s);
   TBE_BWD_CASE(WD_F32, 4, 1)
   TBE_BWD_CASE(WD_F32, 4, 2)
   TBE_BWD_CASE(WD_F32, 4, 4)

@@ -7,9 +7,13 @@
 // Lane mapping: one subgroup of `lpr` lanes per bag; lane k covers columns
 // k*VEC + c*lpr*VEC (c < NC) with 16-byte (VEC elements) row loads, so a row
 // of the bucket width is read by consecutive lanes in one coalesced sweep.
-// Eight rows are kept in flight per lane (independent index loads, then
-// independent row loads) to hide HBM latency; the sum is taken in lookup
-// order.  Memory-bound: every lookup moves one index and one row.
+//
+// Memory-level parallelism: lookups are taken eight at a time.  The eight
+// indices are loaded, then the eight rows, then the eight rows are
+// accumulated in lookup order; scheduling barriers keep the compiler from
+// sinking each row load next to its use, which would leave one row in flight.
+// A partial last batch repeats the bag's last index and drops the repeats with
+// a select, so the batch has no branches (the repeated row is a cache hit).
 #include "tbe_common.h"
 
 namespace tbe {
@@ -26,7 +30,7 @@ struct Acc<WD_F32> {
   using T = double;
 };
 
-template <int WD, int VEC, int NC>
+template <int WD, int VEC, int NC, typename IT, bool PSW>
 __global__ __launch_bounds__(kThreads) void fwd_pool_kernel(FwdArgs a, BucketDev bk) {
   using AT = typename Acc<WD>::T;
   const uint32_t lpr = bk.lpr;
@@ -38,56 +42,47 @@ __global__ __launch_bounds__(kThreads) void fwd_pool_kernel(FwdArgs a, BucketDev
   const int64_t b = (int64_t)(sg - (uint64_t)slot * (uint64_t)a.B);
   const uint32_t t = bk.tables[slot];
   const TableDev td = a.tables[t];
+  const IT* __restrict__ I = reinterpret_cast<const IT*>(a.indices);
+  const IT* __restrict__ O = reinterpret_cast<const IT*>(a.offsets);
   const int64_t j = (int64_t)t * a.B + b;
-  const int64_t lo = load_idx(a.offsets, a.itype, j);
-  const int64_t hi = load_idx(a.offsets, a.itype, j + 1);
+  const int64_t lo = O[j];
+  const int64_t hi = O[j + 1];
   const uint32_t D = td.dim;
 
   AT acc[NC][VEC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[c][v] = AT(0);
-
   bool act[NC];
-  uint32_t colc[NC];
+  uint32_t colc[NC], cold[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[c][v] = AT(0);
     colc[c] = (lane_in + (uint32_t)c * lpr) * VEC;
     act[c] = colc[c] < D;
+    cold[c] = act[c] ? colc[c] : 0u;  // idle lanes read column 0 and discard it
   }
 
-  int64_t p = lo;
-  for (; p + kInFlight <= hi; p += kInFlight) {
+  for (int64_t p = lo; p < hi; p += kInFlight) {
     int64_t row[kInFlight];
     float s[kInFlight];
+    bool ok[kInFlight];
 #pragma unroll
     for (int k = 0; k < kInFlight; ++k) {
-      row[k] = load_idx(a.indices, a.itype, p + k);
-      s[k] = a.psw ? a.psw[p + k] : 1.0f;
+      ok[k] = p + k < hi;
+      const int64_t q = ok[k] ? p + k : hi - 1;
+      row[k] = (int64_t)I[q];
+      s[k] = PSW ? a.psw[q] : 1.0f;
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      if (!act[c]) continue;
       float v[kInFlight][VEC];
 #pragma unroll
-      for (int k = 0; k < kInFlight; ++k) load_w<WD, VEC>(td.w, row[k] * D + colc[c], v[k]);
+      for (int k = 0; k < kInFlight; ++k) load_w<WD, VEC>(td.w, row[k] * D + cold[c], v[k]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 0; k < kInFlight; ++k)
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[c][e] += AT(s[k]) * AT(v[k][e]);
-    }
-  }
-  for (; p < hi; ++p) {
-    const int64_t row = load_idx(a.indices, a.itype, p);
-    const float s = a.psw ? a.psw[p] : 1.0f;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (!act[c]) continue;
-      float v[VEC];
-      load_w<WD, VEC>(td.w, row * D + colc[c], v);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[c][e] += AT(s) * AT(v[e]);
+        for (int e = 0; e < VEC; ++e) acc[c][e] += ok[k] ? AT(s[k]) * AT(v[k][e]) : AT(0);
     }
   }
 
@@ -104,15 +99,24 @@ __global__ __launch_bounds__(kThreads) void fwd_pool_kernel(FwdArgs a, BucketDev
   }
 }
 
-template <int WD, int VEC, int NC>
-hipError_t launch(const FwdArgs& a, const BucketDev& bk, hipStream_t s) {
+template <int WD, int VEC, int NC, typename IT, bool PSW>
+hipError_t launch_t(const FwdArgs& a, const BucketDev& bk, hipStream_t s) {
   const uint64_t nbags = (uint64_t)bk.ntables * (uint64_t)a.B;
   const uint64_t per_block = kThreads / bk.lpr;
   const uint64_t grid = (nbags + per_block - 1) / per_block;
   if (grid == 0) return hipSuccess;
-  TBE_LAUNCH("fwd_pool", (fwd_pool_kernel<WD, VEC, NC>), dim3((uint32_t)grid), dim3(kThreads), s,
-             a, bk);
+  TBE_LAUNCH("fwd_pool", (fwd_pool_kernel<WD, VEC, NC, IT, PSW>), dim3((uint32_t)grid),
+             dim3(kThreads), s, a, bk);
   return hipGetLastError();
+}
+
+template <int WD, int VEC, int NC>
+hipError_t launch(const FwdArgs& a, const BucketDev& bk, hipStream_t s) {
+  if (a.itype == IT_I32)
+    return a.psw ? launch_t<WD, VEC, NC, int32_t, true>(a, bk, s)
+                 : launch_t<WD, VEC, NC, int32_t, false>(a, bk, s);
+  return a.psw ? launch_t<WD, VEC, NC, int64_t, true>(a, bk, s)
+               : launch_t<WD, VEC, NC, int64_t, false>(a, bk, s);
 }
 
 }  // namespace

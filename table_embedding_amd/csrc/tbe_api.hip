@@ -70,6 +70,7 @@ WsLayout layout(const tbe_plan* P, int64_t N) {
   WsLayout L{};
   const uint64_t n = (uint64_t)N;
   L.ntiles = (uint32_t)((n + kTile - 1) / kTile);
+  L.max_med = (uint32_t)(n / kTinyRun + 1);
   L.max_long = (uint32_t)(n / kLongRun + 1);
   L.max_chunks = (uint32_t)(n / kChunk + L.max_long + 1);
   L.pstride = P->pstride;
@@ -85,20 +86,22 @@ WsLayout layout(const tbe_plan* P, int64_t N) {
   L.key_b = take(n * 4);
   L.val_a = take(n * 4);
   L.val_b = take(n * 4);
-  L.bag = take(n * 4);
+  L.sc_a = take(n * 4);
+  L.sc_b = take(n * 4);
   L.hist = take((size_t)256 * L.ntiles * 4);
   L.rowtot = take(256 * 4);
   L.tile_cnt = take((size_t)L.ntiles * 4);
-  L.tile_cls = take((size_t)3 * L.ntiles * 4);
+  L.tile_cls = take((size_t)kNumLists * L.ntiles * 4);
   L.run_start = take((n + 1) * 4);
   L.run_key = take(n * 4);
-  L.short_task = take(n * 16);
+  L.tiny_task = take(n * 16);
+  L.med_task = take((size_t)L.max_med * 16);
   L.long_task = take((size_t)L.max_long * 16);
   L.long_cbeg = take((size_t)L.max_long * 4);
   L.remaining = take((size_t)L.max_long * 4);
   L.chunk_task = take((size_t)L.max_chunks * 16);
   L.partial = take((size_t)L.max_chunks * L.pstride * 4);
-  L.counters = take((size_t)(kCntBegins + 3 * (P->buckets.size() + 1)) * 4);
+  L.counters = take((size_t)(kCntBegins + kNumLists * (P->buckets.size() + 1)) * 4);
   L.total = off;
   return L;
 }
@@ -134,8 +137,15 @@ int persistent_grid(const tbe_plan* P, uint64_t work_items, uint32_t items_per_b
   return (int)std::max<uint64_t>(1, std::min(need, cap));
 }
 
+bool any_mean(const tbe_plan* P) {
+  for (int32_t p : P->pooling)
+    if (p == TBE_MEAN) return true;
+  return false;
+}
+
 PrepArgs prep_args(const tbe_plan* P, int64_t B, int32_t itype, const void* indices,
-                   const void* offsets, int64_t N, void* ws, const WsLayout* L) {
+                   const void* offsets, int64_t N, const float* psw, void* ws,
+                   const WsLayout* L) {
   PrepArgs a{};
   a.tables = P->d_tables;
   a.bucket_key_begin = P->d_bkb;
@@ -146,6 +156,8 @@ PrepArgs prep_args(const tbe_plan* P, int64_t B, int32_t itype, const void* indi
   a.itype = itype;
   a.indices = indices;
   a.offsets = offsets;
+  a.psw = psw;
+  a.need_scale = (psw != nullptr || any_mean(P)) ? 1 : 0;
   a.N = (uint32_t)N;
   a.ws = reinterpret_cast<uint8_t*>(ws);
   a.L = L;
@@ -410,11 +422,12 @@ int tbe_workspace_views(const tbe_plan* P, int64_t B, int64_t N, tbe_ws_views* v
   if (N >= (int64_t)(1ll << 31) - 1) return TBE_E_RANGE;
   const WsLayout L = layout(P, N);
   v->sorted_key = L.final_in_b ? L.key_b : L.key_a;
-  v->sorted_pos = L.final_in_b ? L.val_b : L.val_a;
-  v->bag = L.bag;
+  v->sorted_bag = L.final_in_b ? L.val_b : L.val_a;
+  v->sorted_scale = L.final_in_b ? L.sc_b : L.sc_a;
   v->run_start = L.run_start;
   v->run_key = L.run_key;
-  v->short_task = L.short_task;
+  v->tiny_task = L.tiny_task;
+  v->medium_task = L.med_task;
   v->long_task = L.long_task;
   v->long_cbeg = L.long_cbeg;
   v->chunk_task = L.chunk_task;
@@ -453,14 +466,16 @@ int tbe_forward(const tbe_plan* P, int64_t B, int32_t itype, const void* indices
 }
 
 int tbe_preprocess(const tbe_plan* P, int64_t B, int32_t itype, const void* indices,
-                   const void* offsets, int64_t N, void* ws, size_t ws_bytes, void* stream) {
+                   const void* offsets, int64_t N, const float* psw, void* ws, size_t ws_bytes,
+                   void* stream) {
   int rc = check_lookups(P, B, itype, indices, offsets, N);
   if (rc) return rc;
   rc = check_ws(P, N, ws, ws_bytes);
   if (rc) return rc;
+  if (psw && !aligned(psw, 4)) return TBE_E_ARG;
   if (N == 0) return TBE_OK;
   const WsLayout L = layout(P, N);
-  PrepArgs a = prep_args(P, B, itype, indices, offsets, N, ws, &L);
+  PrepArgs a = prep_args(P, B, itype, indices, offsets, N, psw, ws, &L);
   const hipError_t e =
       launch_preprocess(a, P->num_cus * 8, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? TBE_OK : TBE_E_HIP;
@@ -484,7 +499,7 @@ int tbe_backward_rowwise_adagrad(const tbe_plan* P, int64_t B, int32_t itype,
   const WsLayout L = layout(P, N);
   uint8_t* w = reinterpret_cast<uint8_t*>(ws);
   if (!(flags & TBE_BWD_PREPROCESSED)) {
-    PrepArgs pa = prep_args(P, B, itype, indices, offsets, N, ws, &L);
+    PrepArgs pa = prep_args(P, B, itype, indices, offsets, N, psw, ws, &L);
     if (launch_preprocess(pa, P->num_cus * 8, s) != hipSuccess) return TBE_E_HIP;
   }
   BwdArgs a{};
@@ -497,9 +512,12 @@ int tbe_backward_rowwise_adagrad(const tbe_plan* P, int64_t B, int32_t itype,
   a.dtot = P->dtot;
   a.lr = lr;
   a.eps = eps;
-  a.sorted_pos = reinterpret_cast<const uint32_t*>(w + (L.final_in_b ? L.val_b : L.val_a));
-  a.bag = reinterpret_cast<const uint32_t*>(w + L.bag);
-  a.short_task = reinterpret_cast<const uint4*>(w + L.short_task);
+  a.sorted_bag = reinterpret_cast<const uint32_t*>(w + (L.final_in_b ? L.val_b : L.val_a));
+  a.sorted_scale = (psw || any_mean(P))
+                       ? reinterpret_cast<const float*>(w + (L.final_in_b ? L.sc_b : L.sc_a))
+                       : nullptr;
+  a.tiny_task = reinterpret_cast<const uint4*>(w + L.tiny_task);
+  a.med_task = reinterpret_cast<const uint4*>(w + L.med_task);
   a.long_task = reinterpret_cast<const uint4*>(w + L.long_task);
   a.long_cbeg = reinterpret_cast<const uint32_t*>(w + L.long_cbeg);
   a.remaining = reinterpret_cast<uint32_t*>(w + L.remaining);
@@ -511,15 +529,20 @@ int tbe_backward_rowwise_adagrad(const tbe_plan* P, int64_t B, int32_t itype,
   a.debug_count = debug_row_updates;
   a.N = (uint32_t)N;
   a.T = (uint32_t)P->T;
-  a.max_short = (uint32_t)N;
+  a.max_tiny = (uint32_t)N;
+  a.max_med = L.max_med;
   a.max_long = L.max_long;
   a.max_chunks = L.max_chunks;
   const bool fused = flags & TBE_BWD_FUSED_LONG;
   for (uint32_t b = 0; b < P->buckets.size(); ++b) {
     const Bucket& bk = P->buckets[b];
     BucketDev bd{bk.d_tables, (uint32_t)bk.tables.size(), bk.lpr, bk.lpr_log2};
-    const int grid = persistent_grid(P, (uint64_t)N, kThreads / bk.lpr);
-    if (launch_backward_bucket(a, bd, b, P->wdtype, bk.vec, bk.nc, fused, grid, s) != hipSuccess)
+    BwdGrids g;
+    g.tiny = (uint32_t)persistent_grid(P, (uint64_t)N, kThreads / bk.lpr);
+    g.medium = (uint32_t)persistent_grid(P, L.max_med, 1);
+    g.chunk = (uint32_t)persistent_grid(P, L.max_chunks, 1);
+    g.longrun = (uint32_t)persistent_grid(P, L.max_long, 1);
+    if (launch_backward_bucket(a, bd, b, P->wdtype, bk.vec, bk.nc, fused, g, s) != hipSuccess)
       return TBE_E_HIP;
   }
   return TBE_OK;

@@ -13,6 +13,7 @@ constexpr int kThreads = 256;       // every kernel runs 256-thread workgroups (
 constexpr int kWave = 64;
 constexpr int kTile = 4096;         // keys per workgroup in the sort / scan passes
 constexpr int kLongRun = 256;       // SL >= 256 takes the chunked long-run path
+constexpr int kTinyRun = 32;        // short runs below this are owned by a lane subgroup
 constexpr int kChunk = 256;         // lookups per long-run chunk
 constexpr int kRadixBits = 8;
 constexpr int kMaxTables = 4096;
@@ -44,13 +45,14 @@ struct BucketDev {
 
 // Workspace layout: byte offsets from the workspace base (all 256-B aligned).
 struct WsLayout {
-  size_t key_a, key_b, val_a, val_b, bag;
+  size_t key_a, key_b, val_a, val_b, sc_a, sc_b;  // sort ping-pong: key, bag id, scale
   size_t hist, rowtot, tile_cnt, tile_cls;
   size_t run_start, run_key;
-  size_t short_task, long_task, long_cbeg, remaining, chunk_task;
+  size_t tiny_task, med_task, long_task, long_cbeg, remaining, chunk_task;
   size_t partial, counters;
   size_t total;
   uint32_t ntiles;          // ceil(N / kTile)
+  uint32_t max_med;         // capacity of the medium short-run list
   uint32_t max_long;        // capacity of the long-run lists
   uint32_t max_chunks;      // capacity of the chunk list
   uint32_t pstride;         // floats per partial row
@@ -58,8 +60,11 @@ struct WsLayout {
   int final_in_b;           // sorted keys end in key_b/val_b
 };
 
-// Counter block: [U, n_short, n_long, n_chunks, sbeg[nb+1], lbeg[nb+1], cbeg[nb+1]]
-constexpr int kCntU = 0, kCntShort = 1, kCntLong = 2, kCntChunks = 3, kCntBegins = 4;
+// Counter block: [U, n_tiny, n_medium, n_long, n_chunks, then per list k the
+// nb+1 bucket begins at kCntBegins + k*(nb+1)]
+constexpr int kNumLists = 4;  // tiny short runs, medium short runs, long runs, chunks
+constexpr int kCntU = 0, kCntTiny = 1, kCntMed = 2, kCntLong = 3, kCntChunks = 4,
+              kCntBegins = 5;
 
 // ------------------------------------------------------------- device helpers
 
@@ -200,6 +205,8 @@ struct PrepArgs {
   int itype;
   const void* indices;
   const void* offsets;
+  const float* psw;                  // nullable per-sample weights
+  int need_scale;                    // per-sample weights or a mean table: scale per lookup
   uint32_t N;
   uint8_t* ws;
   const WsLayout* L;                 // host pointer (layout), kernels get offsets by value
@@ -215,9 +222,10 @@ struct BwdArgs {
   const float* grad;
   uint32_t dtot;
   float lr, eps;
-  const uint32_t* sorted_pos;
-  const uint32_t* bag;
-  const uint4* short_task;
+  const uint32_t* sorted_bag;   // bag id of each sorted lookup
+  const float* sorted_scale;    // nullable: S[p] * (1/L if mean) of each sorted lookup
+  const uint4* tiny_task;
+  const uint4* med_task;
   const uint4* long_task;
   const uint32_t* long_cbeg;
   uint32_t* remaining;
@@ -228,7 +236,7 @@ struct BwdArgs {
   uint32_t nb;
   uint32_t* debug_count;     // nullable, per linear key
   uint32_t N, T;             // lookups and tables (task sanity bounds)
-  uint32_t max_short, max_long, max_chunks;  // list capacities
+  uint32_t max_tiny, max_med, max_long, max_chunks;  // list capacities
 };
 
 hipError_t launch_forward_bucket(const FwdArgs& a, const BucketDev& bk, int wd, int vec, int nc,
@@ -236,7 +244,12 @@ hipError_t launch_forward_bucket(const FwdArgs& a, const BucketDev& bk, int wd, 
 hipError_t launch_forward_hist(const FwdArgs& a, uint32_t E, uint32_t D, int mean, int grid,
                                hipStream_t s);
 hipError_t launch_preprocess(const PrepArgs& a, int grid_persist, hipStream_t s);
+// Persistent grid sizes of the backward kernels of one bucket.
+struct BwdGrids {
+  uint32_t tiny, medium, chunk, longrun;
+};
+
 hipError_t launch_backward_bucket(const BwdArgs& a, const BucketDev& bk, uint32_t bucket, int wd,
-                                  int vec, int nc, bool fused, int grid_persist, hipStream_t s);
+                                  int vec, int nc, bool fused, const BwdGrids& g, hipStream_t s);
 
 }  // namespace tbe

@@ -25,9 +25,27 @@ def tolerance_weights(a_st, b_st, wdtype, ref_f64=None):
     return float(np.max(np.abs(a - b), initial=0))
 
 
-def weights_ok(a_st, b_st, wdtype):
-    v = tolerance_weights(a_st, b_st, wdtype)
-    return v <= (1e-6 if wdtype == "f32" else 2), v
+def storage_ulp(mag, wdtype):
+    """Spacing of the storage format at magnitude mag (subnormal spacing below)."""
+    p, emin = {"f32": (24, -126), "f16": (11, -14), "bf16": (8, -126)}[wdtype]
+    e = np.floor(np.log2(np.maximum(mag, np.ldexp(1.0, emin))))
+    return np.ldexp(1.0, (e - (p - 1)).astype(np.int64))
+
+
+def weights_ok(a_st, b_st, wdtype, old_st=None):
+    """Updated weights: 2 storage ulp (float32: 1e-6 max(1,|ref|)).  The ulp is taken at
+    max(|W_before|, |W_ref|): an update that cancels the weight to near zero is judged at
+    the scale of its operands, where the float32 step itself rounds."""
+    if wdtype == "f32" or old_st is None:
+        v = tolerance_weights(a_st, b_st, wdtype)
+        return v <= (1e-6 if wdtype == "f32" else 2), v
+    import tbe_workloads as wl_
+    a = wl_.storage_to_f64(a_st, wdtype)
+    b = wl_.storage_to_f64(b_st, wdtype)
+    o = wl_.storage_to_f64(old_st, wdtype)
+    u = storage_ulp(np.maximum(np.abs(b), np.abs(o)), wdtype)
+    v = float(np.max(np.abs(a - b) / u, initial=0.0))
+    return v <= 2, v
 
 
 def to_host_storage(t: torch.Tensor, wdtype: str) -> np.ndarray:
@@ -128,7 +146,8 @@ def check_backward(case: Case, tbe_obj):
         mask[rows] = True
         assert Wg[~mask].tobytes() == W0[~mask].tobytes(), f"table {t}: untouched rows changed"
         assert Mg[~mask].tobytes() == case.M[t][~mask].tobytes(), f"table {t}: untouched M"
-        ok, v = weights_ok(Wg[mask], Wr[t].reshape(s.rows[t], s.dims[t])[mask], s.wdtype)
+        ok, v = weights_ok(Wg[mask], Wr[t].reshape(s.rows[t], s.dims[t])[mask], s.wdtype,
+                           W0[mask])
         assert ok, f"table {t}: weight tolerance exceeded ({v})"
         worst_w = max(worst_w, v)
         rel = np.abs(Mg[mask].astype(np.float64) - Mr[t][mask]) / np.maximum(
@@ -153,20 +172,21 @@ def gpu_preprocess_views(tbe_obj, case: Case):
     ws = tbe_obj._ws
     N = case.N
     nb = v["num_buckets"]
-    cnt = read_u32(ws, v["counters"], 4 + 3 * (nb + 1))
-    U, ns, nl, nc = (int(x) for x in cnt[:4])
+    cnt = read_u32(ws, v["counters"], 5 + 4 * (nb + 1))
+    U, nt, nm, nl, nc = (int(x) for x in cnt[:5])
     out = dict(
         sorted_key=read_u32(ws, v["sorted_key"], N).astype(np.int64),
-        sorted_pos=read_u32(ws, v["sorted_pos"], N).astype(np.int64),
-        bag=read_u32(ws, v["bag"], N).astype(np.int64),
+        sorted_bag=read_u32(ws, v["sorted_bag"], N).astype(np.int64),
+        sorted_scale=read_u32(ws, v["sorted_scale"], N).view(np.float32),
         run_start=read_u32(ws, v["run_start"], U + 1).astype(np.int64),
         run_key=read_u32(ws, v["run_key"], U).astype(np.int64),
-        short_task=read_u32x4(ws, v["short_task"], ns).astype(np.int64),
+        tiny_task=read_u32x4(ws, v["tiny_task"], nt).astype(np.int64),
+        medium_task=read_u32x4(ws, v["medium_task"], nm).astype(np.int64),
         long_task=read_u32x4(ws, v["long_task"], nl).astype(np.int64),
         long_cbeg=read_u32(ws, v["long_cbeg"], nl).astype(np.int64),
         chunk_task=read_u32x4(ws, v["chunk_task"], nc).astype(np.int64),
-        U=U, n_short=ns, n_long=nl, n_chunks=nc, nb=nb,
-        begins=cnt[4:].reshape(3, nb + 1).astype(np.int64))
+        U=U, n_tiny=nt, n_medium=nm, n_long=nl, n_chunks=nc, nb=nb,
+        begins=cnt[5:].reshape(4, nb + 1).astype(np.int64))
     kb = np.array(tbe_obj.key_bases(), np.int64)
     out["key_base"] = kb
     return out
@@ -187,13 +207,14 @@ def check_preprocess(case: Case, tbe_obj):
         t = order[i]
         return base[t] + (k - kb[t]), t
 
-    assert np.array_equal(g["bag"], r["bag"]), "bag ids differ"
     okey, _ = to_oracle_key(g["sorted_key"])
     # GPU keys are ordered by (bucket, table); a stable re-sort by the oracle's table-major key
     # gives the oracle's order if and only if every table segment matches
     perm = np.argsort(okey, kind="stable")
     assert np.array_equal(okey[perm], r["sorted_key"].astype(np.int64)), "sorted keys differ"
-    assert np.array_equal(g["sorted_pos"][perm], r["sorted_pos"]), "sorted positions differ"
+    # the sort is stable and each bag's lookups are contiguous, so the bag ids of the sorted
+    # lookups are the oracle's bag[sorted_pos] (equal keys in ascending position)
+    assert np.array_equal(g["sorted_bag"][perm], r["bag"][r["sorted_pos"]]), "sorted bags differ"
     # run starts point at the first slot of each run in the GPU order
     assert g["U"] == r["U"]
     assert g["run_start"][-1] == case.N
@@ -203,17 +224,38 @@ def check_preprocess(case: Case, tbe_obj):
     p = np.argsort(rk_o, kind="stable")
     assert np.array_equal(rk_o[p], r["run_key"].astype(np.int64)), "run keys differ"
     assert np.array_equal(lens_g[p], np.diff(r["run_start"])), "run lengths differ"
-    assert (g["n_short"], g["n_long"], g["n_chunks"]) == (r["n_short"], r["n_long"],
-                                                            r["n_chunks"])
+    olens = np.diff(r["run_start"])
+    assert g["n_tiny"] == int((olens < 32).sum()), "tiny short-run count differs"
+    assert g["n_tiny"] + g["n_medium"] == r["n_short"], "short-run count differs"
+    assert (g["n_long"], g["n_chunks"]) == (r["n_long"], r["n_chunks"])
+    # bag and contribution scale of every sorted lookup
+    if case.psw is not None or any(p == wl.POOL_MEAN for p in s.pooling):
+        L = np.diff(case.off.astype(np.int64))
+        j = r["bag"][r["sorted_pos"]]
+        sp = (np.ones(len(j), np.float32) if case.psw is None
+              else case.psw[r["sorted_pos"]].astype(np.float32))
+        mean = np.array(s.pooling)[j // s.B] == wl.POOL_MEAN
+        want = np.where(mean, sp / L[j].astype(np.float32), sp).astype(np.float32)
+        np.testing.assert_allclose(g["sorted_scale"][perm], want, rtol=2.5e-7, atol=0)
     # tasks: every run appears once, in ascending key order, with its table and row
-    st = g["short_task"]
+    tt = g["tiny_task"]       # {start, row, table << 16 | len, bag of first lookup}
+    mt = g["medium_task"]     # {start, len, row, table}
     lt = g["long_task"]
-    if len(st):
-        assert np.all(st[:, 1] < 256)
-        assert np.array_equal(kb[st[:, 3]] + st[:, 2], g["sorted_key"][st[:, 0]])
-        assert np.all(np.diff(kb[st[:, 3]] + st[:, 2]) > 0)
-        assert np.array_equal(st[:, 0], g["run_start"][:-1][lens_g < 256])
-        assert np.array_equal(st[:, 1], lens_g[lens_g < 256])
+    rs = g["run_start"][:-1]
+    if len(tt):
+        t_t, t_len = tt[:, 2] >> 16, tt[:, 2] & 0xFFFF
+        assert np.all(t_len < 32) and np.all(t_len > 0)
+        assert np.array_equal(kb[t_t] + tt[:, 1], g["sorted_key"][tt[:, 0]])
+        assert np.all(np.diff(kb[t_t] + tt[:, 1]) > 0)
+        assert np.array_equal(tt[:, 0], rs[lens_g < 32])
+        assert np.array_equal(t_len, lens_g[lens_g < 32])
+        assert np.array_equal(tt[:, 3], g["sorted_bag"][tt[:, 0]])
+    med = (lens_g >= 32) & (lens_g < 256)
+    if len(mt):
+        assert np.array_equal(mt[:, 0], rs[med]) and np.array_equal(mt[:, 1], lens_g[med])
+        assert np.array_equal(kb[mt[:, 3]] + mt[:, 2], g["sorted_key"][mt[:, 0]])
+    else:
+        assert not med.any()
     if len(lt):
         assert np.all(lt[:, 1] >= 256)
         assert np.array_equal(lt[:, 0], g["run_start"][:-1][lens_g >= 256])
@@ -227,11 +269,14 @@ def check_preprocess(case: Case, tbe_obj):
             for k in range(int((ln + 255) // 256)):
                 want.append([st0 + 256 * k, min(256, ln - 256 * k), t, l])
         assert np.array_equal(ct, np.array(want, np.int64).reshape(-1, 4)), "chunk tasks differ"
-    # per-bucket begins split the three lists exactly at bucket changes
+    # per-bucket begins split the four lists exactly at bucket changes
     bt = bucket_of_table(s)
-    for k, (tasks, tcol) in enumerate(((st, 3), (lt, 3), (g["chunk_task"], 2))):
+    tiny_t = (tt[:, 2] >> 16) if len(tt) else np.zeros(0, np.int64)
+    for k, tab in enumerate((tiny_t, mt[:, 3] if len(mt) else tiny_t[:0],
+                             lt[:, 3] if len(lt) else tiny_t[:0],
+                             g["chunk_task"][:, 2] if g["n_chunks"] else tiny_t[:0])):
         b = g["begins"][k]
-        assert b[0] == 0 and b[-1] == len(tasks)
+        assert b[0] == 0 and b[-1] == len(tab)
         for q in range(g["nb"]):
-            assert np.all(bt[tasks[b[q]:b[q + 1], tcol]] == q) if len(tasks) else True
+            assert np.all(bt[tab[b[q]:b[q + 1]]] == q)
     return g, r

@@ -65,8 +65,8 @@ def _spec(name):
 
 
 MAIN = ["C1", "C2s", "C3s", "C4s", "C5s"]
-EDGE = ["empty_bags", "all_empty", "one_bag", "one_row", "const255", "const256", "const257",
-        "wide_f32", "wide_bf16", "many_tables"]
+EDGE = ["empty_bags", "all_empty", "one_bag", "one_row", "const31", "const32", "const255",
+        "const256", "const257", "wide_f32", "wide_bf16", "many_tables"]
 
 
 def _announce(name, what):
@@ -91,7 +91,7 @@ def test_preprocess_bit_exact(name):
     if case.N == 0:
         pytest.skip("no lookups: preprocessing enqueues nothing")
     tb = case.tbe()
-    tb.preprocess(case.spec.B, case.d_idx, case.d_off)
+    tb.preprocess(case.spec.B, case.d_idx, case.d_off, case.d_psw)
     torch.cuda.synchronize()
     S.check_preprocess(case, tb)
 
@@ -167,6 +167,18 @@ def test_preprocessed_flag_and_reuse():
                  case.spec.eps, flags=te.TBE_BWD_PREPROCESSED | te.TBE_BWD_FUSED_LONG)
     torch.cuda.synchronize()
     assert [S.to_host_storage(w, "f16").tobytes() for w in tb2.weights] == a
+
+
+def test_preprocessed_flag_with_weights_and_mean():
+    """Per-sample weights and mean pooling are folded into the preprocessing."""
+    import table_embedding_amd as te
+    case = S.Case(_spec("C3s"))
+    tb = case.tbe()
+    tb.preprocess(case.spec.B, case.d_idx, case.d_off, case.d_psw)
+    tb.backward(case.spec.B, case.d_idx, case.d_off, case.d_psw, case.d_G, case.spec.lr,
+                case.spec.eps, flags=te.TBE_BWD_PREPROCESSED)
+    torch.cuda.synchronize()
+    S.check_backward(case, tb)
 
 
 def test_histogram_path_forward():
