@@ -101,14 +101,14 @@ typedef struct {
                           only with per-sample weights or a mean table */
   size_t run_start;    /* U+1 entries: first sorted slot of each run, then num_lookups */
   size_t run_key;      /* U keys, one per run */
-  size_t tiny_task;    /* n_tiny uint32x4 {start, row, table<<16 | len, bag of the first
-                          lookup}: short runs with SL < 32 */
+  size_t single_task;  /* n_single uint32x4 {start, row, table, bag}: runs with SL = 1 */
+  size_t tiny_task;    /* n_tiny uint32x4 {start, len, row, table}: short runs, 2 <= SL < 32 */
   size_t medium_task;  /* n_medium uint32x4 {start, len, row, table}: short runs, 32 <= SL < 256 */
   size_t long_task;    /* n_long uint32x4 {start, len, row, table}: runs with SL >= 256 */
   size_t long_cbeg;    /* n_long first chunk index of each long run */
   size_t chunk_task;   /* n_chunks uint32x4 {start, len, table, long index}: 256-lookup chunks */
-  size_t counters;     /* uint32 {U, n_tiny, n_medium, n_long, n_chunks, then for each of
-                          the four lists its nb+1 per-D-bucket begins} */
+  size_t counters;     /* uint32 {U, n_single, n_tiny, n_medium, n_long, n_chunks, then for
+                          each of the five lists its nb+1 per-D-bucket begins} */
   size_t total;        /* bytes needed */
   int32_t num_buckets; /* nb */
 } tbe_ws_views;

@@ -44,7 +44,7 @@ class TBEError(RuntimeError):
 
 class WsViews(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in ("sorted_key", "sorted_bag",
-                                           "sorted_scale", "run_start", "run_key", "tiny_task",
+                                           "sorted_scale", "run_start", "run_key", "single_task", "tiny_task",
                                            "medium_task", "long_task", "long_cbeg",
                                            "chunk_task", "counters", "total")] + [
         ("num_buckets", C.c_int32)]

@@ -7,17 +7,18 @@
 // row.  Section "Fusion boundaries": per-sample weights scale each
 // contribution before grouping and the optimizer runs as the epilogue).
 //
-// Programs.  Short runs with SL < 32 are owned by a subgroup of `lpr` lanes
-// (one row of the bucket width); short runs with 32 <= SL < 256 by a whole
+// Programs.  Short runs with SL = 1 are owned, two at a time, by a subgroup of
+// `lpr` lanes (one row of the bucket width); short runs with 2 <= SL < 32 by a
+// subgroup each; short runs with 32 <= SL < 256 by a whole
 // 256-thread workgroup whose subgroups split the lookups; chunks and long-run
 // updates by a workgroup.  Every kernel is persistent over a task list whose
 // length it reads from device memory (no host readback).
 //
 // Memory.  Per lookup the kernels read the bag id (and the contribution scale)
 // of the sorted lookup with the sorted order, then one 16-byte column slice of
-// the bag's grad_out row; eight lookups are kept in flight per lane.  A tiny
-// task carries the bag of its first lookup, so an SL = 1 run costs one task
-// load, then the grad_out row, weight row and momentum in parallel.
+// the bag's grad_out row; eight lookups are kept in flight per lane.  A
+// single-lookup task carries its bag, so an SL = 1 run costs one task load,
+// then the grad_out row, weight row and momentum in parallel.
 //
 // Determinism.  Sums run in lookup order inside a subgroup; workgroup sums
 // combine subgroups in ascending order; the square sum is reduced in a fixed
@@ -104,82 +105,152 @@ __device__ __forceinline__ uint32_t list_begin(const BwdArgs& a, int list, uint3
   return a.counters[kCntBegins + list * (a.nb + 1) + bucket];
 }
 
-// --------------------------------------------------------- tiny short runs
-// One subgroup of lpr lanes owns a run with SL < 32: gather, Adagrad, plain stores.
+// Table descriptor: from the LDS copy when the plan has at most kTdCache
+// tables (TDL), else from global memory.  A compile-time choice, so the
+// compiler never emits a generic (flat) load that would wait on both counters.
+template <bool TDL>
+__device__ __forceinline__ void load_td_cache(const BwdArgs& a, TableDev* s_td) {
+  if (TDL) {
+    for (uint32_t i = threadIdx.x; i < a.T; i += kThreads) s_td[i] = a.tables[i];
+    __syncthreads();
+  }
+}
+template <bool TDL>
+__device__ __forceinline__ TableDev get_td(const BwdArgs& a, const TableDev* s_td, uint32_t t) {
+  return TDL ? s_td[t] : a.tables[t];
+}
+
+// Row-wise Adagrad of one row owned by a subgroup (g: this lane's columns).
 template <int WD, int VEC, int NC>
-__global__ __launch_bounds__(kThreads) void bwd_tiny_kernel(BwdArgs a, BucketDev bk,
-                                                            uint32_t bucket) {
+__device__ __forceinline__ void subgroup_row_update(const BwdArgs& a, const TableDev& td,
+                                                    int64_t row, float m0, const float (*w)[VEC],
+                                                    const float (*g)[VEC], const uint32_t* colc,
+                                                    uint32_t lpr, uint32_t lane_in, bool store) {
+  const uint32_t D = td.dim;
+  float sq = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    if (colc[c] < D)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) sq += g[c][e] * g[c][e];
+  sq = subgroup_sum(sq, lpr);
+  if (!store) return;
+  const float m = m0 + sq / (float)D;
+  if (lane_in == 0) {
+    td.m[row] = m;
+    if (a.debug_count) atomicAdd(&a.debug_count[td.key_base + (uint32_t)row], 1u);
+  }
+  const float den = sqrtf(m) + a.eps;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (colc[c] >= D) continue;
+    float o[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) o[e] = w[c][e] - (a.lr * g[c][e]) / den;
+    store_w<WD, VEC>(td.w, row * D + colc[c], o);
+  }
+}
+
+// ------------------------------------------------------- single-lookup runs
+// Most runs have one lookup.  A subgroup takes two of them per iteration: the
+// task records (which carry the lookup's bag), then both weight rows, momenta,
+// grad_out slices and scales are loaded before the first use -- one memory
+// round trip per pair of runs after the task load.
+template <int WD, int VEC, int NC, bool SCALE, bool TDL>
+__global__ __launch_bounds__(kThreads) void bwd_single_kernel(BwdArgs a, BucketDev bk,
+                                                              uint32_t bucket) {
+  __shared__ TableDev s_td[TDL ? kTdCache : 1];
+  load_td_cache<TDL>(a, s_td);
   const uint32_t lpr = bk.lpr;
   const uint32_t lane_in = threadIdx.x & (lpr - 1);
   const uint32_t nsg_grid = (gridDim.x * kThreads) >> bk.lpr_log2;
   const uint32_t sg = (blockIdx.x * kThreads + threadIdx.x) >> bk.lpr_log2;
-  // descriptors of the first kTdCache tables live in LDS (one load per task saved)
-  __shared__ TableDev s_td[kTdCache];
-  for (uint32_t i = threadIdx.x; i < a.T && i < (uint32_t)kTdCache; i += kThreads)
-    s_td[i] = a.tables[i];
-  __syncthreads();
   const uint32_t beg = list_begin(a, 0, bucket);
-  const uint32_t end = min(list_begin(a, 0, bucket + 1), a.max_tiny);
+  const uint32_t end = min(list_begin(a, 0, bucket + 1), a.max_single);
+  for (uint32_t s = beg + sg; s < end; s += 2 * nsg_grid) {
+    const uint32_t s1 = (s + nsg_grid < end) ? s + nsg_grid : s;
+    uint4 tk[2];  // {start, row, table, bag}
+    tk[0] = a.single_task[s];
+    tk[1] = a.single_task[s1];
+    TableDev td[2];
+    bool ok[2];
+    int64_t row[2], b[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      // sanity bounds, never false for lists the preprocessing wrote
+      const uint32_t t = tk[u].z < a.T ? tk[u].z : 0u;
+      td[u] = get_td<TDL>(a, s_td, t);
+      const int64_t bb = (int64_t)tk[u].w - (int64_t)t * a.B;
+      ok[u] = tk[u].z < a.T && tk[u].x < a.N && tk[u].y < td[u].rows && bb >= 0 && bb < a.B;
+      row[u] = ok[u] ? (int64_t)tk[u].y : 0;
+      b[u] = ok[u] ? bb : 0;
+    }
+    uint32_t colc[2][NC], cold[2][NC];
+    float w[2][NC][VEC], g[2][NC][VEC], m0[2], sc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        colc[u][c] = (lane_in + (uint32_t)c * lpr) * VEC;
+        cold[u][c] = colc[u][c] < td[u].dim ? colc[u][c] : 0u;
+        load_w<WD, VEC>(td[u].w, row[u] * td[u].dim + cold[u][c], w[u][c]);
+        load_f32<VEC>(a.grad + b[u] * (int64_t)a.dtot + td[u].col + cold[u][c], g[u][c]);
+      }
+      m0[u] = td[u].m[row[u]];
+      sc[u] = SCALE ? a.sorted_scale[ok[u] ? tk[u].x : 0u] : 1.0f;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (SCALE)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) g[u][c][e] *= sc[u];
+      subgroup_row_update<WD, VEC, NC>(a, td[u], row[u], m0[u], w[u], g[u], colc[u], lpr,
+                                       lane_in, ok[u] && (u == 0 || s1 != s));
+    }
+  }
+}
+
+// ----------------------------------------------------- tiny short runs
+// One subgroup of lpr lanes owns a run with 2 <= SL < 32: gather, Adagrad,
+// plain stores.  The next task record is prefetched.
+template <int WD, int VEC, int NC, bool TDL>
+__global__ __launch_bounds__(kThreads) void bwd_tiny_kernel(BwdArgs a, BucketDev bk,
+                                                            uint32_t bucket) {
+  __shared__ TableDev s_td[TDL ? kTdCache : 1];
+  load_td_cache<TDL>(a, s_td);
+  const uint32_t lpr = bk.lpr;
+  const uint32_t lane_in = threadIdx.x & (lpr - 1);
+  const uint32_t nsg_grid = (gridDim.x * kThreads) >> bk.lpr_log2;
+  const uint32_t sg = (blockIdx.x * kThreads + threadIdx.x) >> bk.lpr_log2;
+  const uint32_t beg = list_begin(a, 1, bucket);
+  const uint32_t end = min(list_begin(a, 1, bucket + 1), a.max_tiny);
   uint32_t s = beg + sg;
   uint4 next = s < end ? a.tiny_task[s] : make_uint4(0, 0, 0, 0);
   for (; s < end; s += nsg_grid) {
-    const uint4 task = next;  // {start, row, table << 16 | len, bag of the first lookup}
+    const uint4 task = next;  // {start, len, row, table}
     if (s + nsg_grid < end) next = a.tiny_task[s + nsg_grid];
-    const uint32_t start = task.x, t = task.z >> 16, len = task.z & 0xffffu;
-    const int64_t row = task.y;
+    const uint32_t start = task.x, len = task.y, t = task.w;
     // sanity bounds, never false for lists the preprocessing wrote
     if (len == 0 || t >= a.T || start > a.N || len > a.N - start) continue;
-    const TableDev td = t < (uint32_t)kTdCache ? s_td[t] : a.tables[t];
-    if (task.y >= td.rows) continue;
-    const uint32_t D = td.dim;
-    const int64_t tB = (int64_t)t * a.B;
+    const TableDev td = get_td<TDL>(a, s_td, t);
+    if (task.z >= td.rows) continue;
+    const int64_t row = task.z;
     uint32_t colc[NC], cold[NC];
-    bool act[NC];
     float w[NC][VEC], g[NC][VEC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       colc[c] = (lane_in + (uint32_t)c * lpr) * VEC;
-      act[c] = colc[c] < D;
-      cold[c] = act[c] ? colc[c] : 0u;
-      load_w<WD, VEC>(td.w, row * D + cold[c], w[c]);
+      cold[c] = colc[c] < td.dim ? colc[c] : 0u;
+      load_w<WD, VEC>(td.w, row * td.dim + cold[c], w[c]);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) g[c][e] = 0.f;
     }
     const float m0 = td.m[row];
-    if (len == 1) {
-      // the task carries the only lookup's bag: no dependent load before grad_out
-      const int64_t b0 = (int64_t)task.w - tB;
-      const float sc0 = a.sorted_scale ? a.sorted_scale[start] : 1.0f;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        load_f32<VEC>(a.grad + b0 * (int64_t)a.dtot + td.col + cold[c], g[c]);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) g[c][e] *= sc0;
-      }
-    } else {
-      gather<VEC, NC>(a, td, tB, start, start + len, 1u, cold, g);
-    }
-    float sq = 0.f;
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-      if (act[c])
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) sq += g[c][e] * g[c][e];
-    sq = subgroup_sum(sq, lpr);
-    const float m = m0 + sq / (float)D;
-    if (lane_in == 0) {
-      td.m[row] = m;
-      if (a.debug_count) atomicAdd(&a.debug_count[td.key_base + (uint32_t)row], 1u);
-    }
-    const float den = sqrtf(m) + a.eps;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (!act[c]) continue;
-      float o[VEC];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) o[e] = w[c][e] - (a.lr * g[c][e]) / den;
-      store_w<WD, VEC>(td.w, row * D + colc[c], o);
-    }
+    gather<VEC, NC>(a, td, (int64_t)t * a.B, start, start + len, 1u, cold, g);
+    subgroup_row_update<WD, VEC, NC>(a, td, row, m0, w, g, colc, lpr, lane_in, true);
   }
 }
 
@@ -323,8 +394,8 @@ template <int WD, int VEC, int NC>
 __global__ __launch_bounds__(kThreads) void bwd_medium_kernel(BwdArgs a, BucketDev bk,
                                                               uint32_t bucket) {
   __shared__ WgSmem<VEC, NC> sm;
-  const uint32_t beg = list_begin(a, 1, bucket);
-  const uint32_t end = min(list_begin(a, 1, bucket + 1), a.max_med);
+  const uint32_t beg = list_begin(a, 2, bucket);
+  const uint32_t end = min(list_begin(a, 2, bucket + 1), a.max_med);
   for (uint32_t m = beg + blockIdx.x; m < end; m += gridDim.x) {
     const uint4 task = a.med_task[m];  // {start, len, row, table}
     if (!span_ok(a, task.x, task.y, task.w, task.z)) continue;  // uniform; never for valid lists
@@ -341,8 +412,8 @@ template <int WD, int VEC, int NC>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a, BucketDev bk,
                                                              uint32_t bucket) {
   __shared__ WgSmem<VEC, NC> sm;
-  const uint32_t beg = list_begin(a, 3, bucket);
-  const uint32_t end = min(list_begin(a, 3, bucket + 1), a.max_chunks);
+  const uint32_t beg = list_begin(a, 4, bucket);
+  const uint32_t end = min(list_begin(a, 4, bucket + 1), a.max_chunks);
   for (uint32_t c = beg + blockIdx.x; c < end; c += gridDim.x) {
     const uint4 task = a.chunk_task[c];  // {start, len, table, long index}
     if (!chunk_ok(a, task)) continue;    // uniform per workgroup; never for valid lists
@@ -357,8 +428,8 @@ template <int WD, int VEC, int NC>
 __global__ __launch_bounds__(kThreads) void bwd_long_update_kernel(BwdArgs a, BucketDev bk,
                                                                    uint32_t bucket) {
   __shared__ WgSmem<VEC, NC> sm;
-  const uint32_t beg = list_begin(a, 2, bucket);
-  const uint32_t end = min(list_begin(a, 2, bucket + 1), a.max_long);
+  const uint32_t beg = list_begin(a, 3, bucket);
+  const uint32_t end = min(list_begin(a, 3, bucket + 1), a.max_long);
   for (uint32_t l = beg + blockIdx.x; l < end; l += gridDim.x) {
     if (!long_ok(a, l)) continue;  // uniform per workgroup; never for valid lists
     long_update<WD, VEC, NC>(a, bk, l, sm);
@@ -372,8 +443,8 @@ template <int WD, int VEC, int NC>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_fused_kernel(BwdArgs a, BucketDev bk,
                                                                    uint32_t bucket) {
   __shared__ WgSmem<VEC, NC> sm;
-  const uint32_t beg = list_begin(a, 3, bucket);
-  const uint32_t end = min(list_begin(a, 3, bucket + 1), a.max_chunks);
+  const uint32_t beg = list_begin(a, 4, bucket);
+  const uint32_t end = min(list_begin(a, 4, bucket + 1), a.max_chunks);
   for (uint32_t c = beg + blockIdx.x; c < end; c += gridDim.x) {
     const uint4 task = a.chunk_task[c];  // {start, len, table, long index}
     if (!chunk_ok(a, task) || !long_ok(a, task.w)) continue;  // uniform; never for valid lists
@@ -401,11 +472,27 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_fused_kernel(BwdArgs a, Bu
   }
 }
 
+template <int WD, int VEC, int NC, bool TDL>
+hipError_t launch_small(const BwdArgs& a, const BucketDev& bk, uint32_t bucket,
+                        const BwdGrids& g, hipStream_t s) {
+  if (a.sorted_scale)
+    TBE_LAUNCH("bwd_single", (bwd_single_kernel<WD, VEC, NC, true, TDL>), dim3(g.single),
+               dim3(kThreads), s, a, bk, bucket);
+  else
+    TBE_LAUNCH("bwd_single", (bwd_single_kernel<WD, VEC, NC, false, TDL>), dim3(g.single),
+               dim3(kThreads), s, a, bk, bucket);
+  TBE_LAUNCH("bwd_tiny", (bwd_tiny_kernel<WD, VEC, NC, TDL>), dim3(g.tiny), dim3(kThreads), s, a,
+             bk, bucket);
+  return hipSuccess;
+}
+
 template <int WD, int VEC, int NC>
 hipError_t launch(const BwdArgs& a, const BucketDev& bk, uint32_t bucket, bool fused,
                   const BwdGrids& g, hipStream_t s) {
-  TBE_LAUNCH("bwd_tiny", (bwd_tiny_kernel<WD, VEC, NC>), dim3(g.tiny), dim3(kThreads), s, a, bk,
-             bucket);
+  if (a.T <= (uint32_t)kTdCache)
+    (void)launch_small<WD, VEC, NC, true>(a, bk, bucket, g, s);
+  else
+    (void)launch_small<WD, VEC, NC, false>(a, bk, bucket, g, s);
   TBE_LAUNCH("bwd_medium", (bwd_medium_kernel<WD, VEC, NC>), dim3(g.medium), dim3(kThreads), s,
              a, bk, bucket);
   if (fused) {

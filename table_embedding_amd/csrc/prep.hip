@@ -369,6 +369,7 @@ struct ClsDev {
   uint32_t* counters;
   uint32_t* tile_cls;        // kNumLists rows x ntiles
   uint32_t ntiles;
+  uint4* single_task;
   uint4* tiny_task;
   uint4* med_task;
   uint4* long_task;
@@ -379,16 +380,18 @@ struct ClsDev {
   const uint32_t* order;     // table ids in ascending key_base order
   const uint32_t* bkb;       // nb+1 bucket key bounds
   uint32_t T, nb;
-  uint32_t N, max_med, max_long, max_chunks;  // list capacities
+  uint32_t N, max_tiny, max_med, max_long, max_chunks;  // list capacities
 };
 
-// per-run counts of the four lists: tiny, medium, long, chunks
+// per-run counts of the five lists: SL = 1, 2 <= SL < 32, 32 <= SL < 256,
+// long runs, chunks
 __device__ __forceinline__ void run_class(uint32_t len, uint32_t* c) {
   const bool lg = len >= (uint32_t)kLongRun;
-  c[0] = len < (uint32_t)kTinyRun ? 1u : 0u;
-  c[1] = (!lg && len >= (uint32_t)kTinyRun) ? 1u : 0u;
-  c[2] = lg ? 1u : 0u;
-  c[3] = lg ? (len + kChunk - 1) / kChunk : 0u;
+  c[0] = len == 1u ? 1u : 0u;
+  c[1] = (len >= 2u && len < (uint32_t)kTinyRun) ? 1u : 0u;
+  c[2] = (!lg && len >= (uint32_t)kTinyRun) ? 1u : 0u;
+  c[3] = lg ? 1u : 0u;
+  c[4] = lg ? (len + kChunk - 1) / kChunk : 0u;
 }
 
 // run lengths of runs u0 .. u0+15 (0 past U): run_start has U+1 entries
@@ -410,7 +413,7 @@ __global__ __launch_bounds__(kThreads) void cls_count(ClsDev a) {
   __shared__ uint32_t sh4[4];
   const uint32_t U = a.counters[kCntU];
   const uint64_t u0 = (uint64_t)blockIdx.x * kTile + (uint64_t)threadIdx.x * kItems;
-  uint32_t acc[kNumLists] = {0u, 0u, 0u, 0u};
+  uint32_t acc[kNumLists] = {0u, 0u, 0u, 0u, 0u};
   if (u0 < U) {
     uint32_t start[kItems], len[kItems];
     run_lengths(a.run_start, u0, U, start, len);
@@ -442,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void cls_scan(ClsDev a) {
   if (threadIdx.x == 0) {
     for (int k = 0; k < kNumLists; ++k) {
       tot[k] = t4[k];
-      a.counters[kCntTiny + k] = t4[k];
+      a.counters[kCntSingle + k] = t4[k];
     }
   }
   __syncthreads();
@@ -480,7 +483,7 @@ __global__ __launch_bounds__(kThreads) void cls_write(ClsDev a) {
   }
   for (uint32_t i = threadIdx.x; i <= a.nb; i += kThreads) s_bkb[i] = a.bkb[i];
 
-  uint32_t acc[kNumLists] = {0u, 0u, 0u, 0u};
+  uint32_t acc[kNumLists] = {0u, 0u, 0u, 0u, 0u};
   if (mine) {
 #pragma unroll
     for (int e = 0; e < kItems; ++e) {
@@ -515,16 +518,19 @@ __global__ __launch_bounds__(kThreads) void cls_write(ClsDev a) {
     for (int b = bprev + 1; b <= bcur; ++b)
       for (int q = 0; q < kNumLists; ++q) a.counters[kCntBegins + q * (a.nb + 1) + b] = pos[q];
     bprev = bcur;
-    if (ln < (uint32_t)kTinyRun) {
-      // {start, row, table << 16 | len, bag of the first lookup}
-      if (pos[0] < a.N) a.tiny_task[pos[0]] = make_uint4(st, row, (t << 16) | ln, bag0[e]);
+    if (ln == 1u) {
+      // {start, row, table, bag of the lookup}
+      if (pos[0] < a.N) a.single_task[pos[0]] = make_uint4(st, row, t, bag0[e]);
       ++pos[0];
-    } else if (ln < (uint32_t)kLongRun) {
-      if (pos[1] < a.max_med) a.med_task[pos[1]] = make_uint4(st, ln, row, t);
+    } else if (ln < (uint32_t)kTinyRun) {
+      if (pos[1] < a.max_tiny) a.tiny_task[pos[1]] = make_uint4(st, ln, row, t);
       ++pos[1];
+    } else if (ln < (uint32_t)kLongRun) {
+      if (pos[2] < a.max_med) a.med_task[pos[2]] = make_uint4(st, ln, row, t);
+      ++pos[2];
     } else {
       const uint32_t nch = (ln + kChunk - 1) / kChunk;
-      const uint32_t pl = pos[2], pc = pos[3];
+      const uint32_t pl = pos[3], pc = pos[4];
       if (pl < a.max_long) {
         a.long_task[pl] = make_uint4(st, ln, row, t);
         a.long_cbeg[pl] = pc;
@@ -535,8 +541,8 @@ __global__ __launch_bounds__(kThreads) void cls_write(ClsDev a) {
                                                                       : (uint32_t)kChunk;
         a.chunk_task[pc + q] = make_uint4(st + q * kChunk, cl_len, t, pl);
       }
-      pos[3] += nch;
-      ++pos[2];
+      pos[4] += nch;
+      ++pos[3];
     }
   }
 }
@@ -595,10 +601,11 @@ hipError_t launch_preprocess(const PrepArgs& p, int /*grid_persist*/, hipStream_
 
   ClsDev c{u32p(L.run_start), u32p(L.run_key), sbag, u32p(L.counters),
            u32p(L.tile_cls), L.ntiles,
-           reinterpret_cast<uint4*>(ws + L.tiny_task), reinterpret_cast<uint4*>(ws + L.med_task),
+           reinterpret_cast<uint4*>(ws + L.single_task), reinterpret_cast<uint4*>(ws + L.tiny_task),
+           reinterpret_cast<uint4*>(ws + L.med_task),
            reinterpret_cast<uint4*>(ws + L.long_task), u32p(L.long_cbeg), u32p(L.remaining),
            reinterpret_cast<uint4*>(ws + L.chunk_task), p.tables, p.order, p.bucket_key_begin,
-           p.T, p.nb, p.N, L.max_med, L.max_long, L.max_chunks};
+           p.T, p.nb, p.N, L.max_tiny, L.max_med, L.max_long, L.max_chunks};
   TBE_LAUNCH("cls_count", cls_count, dim3(L.ntiles), dim3(kThreads), s, c);
   TBE_LAUNCH("cls_scan", cls_scan, dim3(1), dim3(kThreads), s, c);
   TBE_LAUNCH("cls_write", cls_write, dim3(L.ntiles), dim3(kThreads), s, c);

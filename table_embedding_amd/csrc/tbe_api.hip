@@ -70,6 +70,7 @@ WsLayout layout(const tbe_plan* P, int64_t N) {
   WsLayout L{};
   const uint64_t n = (uint64_t)N;
   L.ntiles = (uint32_t)((n + kTile - 1) / kTile);
+  L.max_tiny = (uint32_t)(n / 2 + 1);
   L.max_med = (uint32_t)(n / kTinyRun + 1);
   L.max_long = (uint32_t)(n / kLongRun + 1);
   L.max_chunks = (uint32_t)(n / kChunk + L.max_long + 1);
@@ -94,7 +95,8 @@ WsLayout layout(const tbe_plan* P, int64_t N) {
   L.tile_cls = take((size_t)kNumLists * L.ntiles * 4);
   L.run_start = take((n + 1) * 4);
   L.run_key = take(n * 4);
-  L.tiny_task = take(n * 16);
+  L.single_task = take(n * 16);
+  L.tiny_task = take((size_t)L.max_tiny * 16);
   L.med_task = take((size_t)L.max_med * 16);
   L.long_task = take((size_t)L.max_long * 16);
   L.long_cbeg = take((size_t)L.max_long * 4);
@@ -426,6 +428,7 @@ int tbe_workspace_views(const tbe_plan* P, int64_t B, int64_t N, tbe_ws_views* v
   v->sorted_scale = L.final_in_b ? L.sc_b : L.sc_a;
   v->run_start = L.run_start;
   v->run_key = L.run_key;
+  v->single_task = L.single_task;
   v->tiny_task = L.tiny_task;
   v->medium_task = L.med_task;
   v->long_task = L.long_task;
@@ -516,6 +519,7 @@ int tbe_backward_rowwise_adagrad(const tbe_plan* P, int64_t B, int32_t itype,
   a.sorted_scale = (psw || any_mean(P))
                        ? reinterpret_cast<const float*>(w + (L.final_in_b ? L.sc_b : L.sc_a))
                        : nullptr;
+  a.single_task = reinterpret_cast<const uint4*>(w + L.single_task);
   a.tiny_task = reinterpret_cast<const uint4*>(w + L.tiny_task);
   a.med_task = reinterpret_cast<const uint4*>(w + L.med_task);
   a.long_task = reinterpret_cast<const uint4*>(w + L.long_task);
@@ -529,7 +533,8 @@ int tbe_backward_rowwise_adagrad(const tbe_plan* P, int64_t B, int32_t itype,
   a.debug_count = debug_row_updates;
   a.N = (uint32_t)N;
   a.T = (uint32_t)P->T;
-  a.max_tiny = (uint32_t)N;
+  a.max_single = (uint32_t)N;
+  a.max_tiny = L.max_tiny;
   a.max_med = L.max_med;
   a.max_long = L.max_long;
   a.max_chunks = L.max_chunks;
@@ -538,7 +543,8 @@ int tbe_backward_rowwise_adagrad(const tbe_plan* P, int64_t B, int32_t itype,
     const Bucket& bk = P->buckets[b];
     BucketDev bd{bk.d_tables, (uint32_t)bk.tables.size(), bk.lpr, bk.lpr_log2};
     BwdGrids g;
-    g.tiny = (uint32_t)persistent_grid(P, (uint64_t)N, kThreads / bk.lpr);
+    g.single = (uint32_t)persistent_grid(P, (uint64_t)N, 2 * (kThreads / bk.lpr));
+    g.tiny = (uint32_t)persistent_grid(P, L.max_tiny, kThreads / bk.lpr);
     g.medium = (uint32_t)persistent_grid(P, L.max_med, 1);
     g.chunk = (uint32_t)persistent_grid(P, L.max_chunks, 1);
     g.longrun = (uint32_t)persistent_grid(P, L.max_long, 1);

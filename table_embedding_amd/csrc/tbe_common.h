@@ -48,10 +48,11 @@ struct WsLayout {
   size_t key_a, key_b, val_a, val_b, sc_a, sc_b;  // sort ping-pong: key, bag id, scale
   size_t hist, rowtot, tile_cnt, tile_cls;
   size_t run_start, run_key;
-  size_t tiny_task, med_task, long_task, long_cbeg, remaining, chunk_task;
+  size_t single_task, tiny_task, med_task, long_task, long_cbeg, remaining, chunk_task;
   size_t partial, counters;
   size_t total;
   uint32_t ntiles;          // ceil(N / kTile)
+  uint32_t max_tiny;        // capacity of the 2 <= SL < 32 list
   uint32_t max_med;         // capacity of the medium short-run list
   uint32_t max_long;        // capacity of the long-run lists
   uint32_t max_chunks;      // capacity of the chunk list
@@ -62,9 +63,9 @@ struct WsLayout {
 
 // Counter block: [U, n_tiny, n_medium, n_long, n_chunks, then per list k the
 // nb+1 bucket begins at kCntBegins + k*(nb+1)]
-constexpr int kNumLists = 4;  // tiny short runs, medium short runs, long runs, chunks
-constexpr int kCntU = 0, kCntTiny = 1, kCntMed = 2, kCntLong = 3, kCntChunks = 4,
-              kCntBegins = 5;
+// lists: short runs with SL = 1, 2 <= SL < 32, 32 <= SL < 256; long runs; chunks
+constexpr int kNumLists = 5;
+constexpr int kCntU = 0, kCntSingle = 1, kCntBegins = 1 + kNumLists;
 
 // ------------------------------------------------------------- device helpers
 
@@ -224,6 +225,7 @@ struct BwdArgs {
   float lr, eps;
   const uint32_t* sorted_bag;   // bag id of each sorted lookup
   const float* sorted_scale;    // nullable: S[p] * (1/L if mean) of each sorted lookup
+  const uint4* single_task;
   const uint4* tiny_task;
   const uint4* med_task;
   const uint4* long_task;
@@ -236,7 +238,7 @@ struct BwdArgs {
   uint32_t nb;
   uint32_t* debug_count;     // nullable, per linear key
   uint32_t N, T;             // lookups and tables (task sanity bounds)
-  uint32_t max_tiny, max_med, max_long, max_chunks;  // list capacities
+  uint32_t max_single, max_tiny, max_med, max_long, max_chunks;  // list capacities
 };
 
 hipError_t launch_forward_bucket(const FwdArgs& a, const BucketDev& bk, int wd, int vec, int nc,
@@ -246,7 +248,7 @@ hipError_t launch_forward_hist(const FwdArgs& a, uint32_t E, uint32_t D, int mea
 hipError_t launch_preprocess(const PrepArgs& a, int grid_persist, hipStream_t s);
 // Persistent grid sizes of the backward kernels of one bucket.
 struct BwdGrids {
-  uint32_t tiny, medium, chunk, longrun;
+  uint32_t single, tiny, medium, chunk, longrun;
 };
 
 hipError_t launch_backward_bucket(const BwdArgs& a, const BucketDev& bk, uint32_t bucket, int wd,

@@ -172,21 +172,22 @@ def gpu_preprocess_views(tbe_obj, case: Case):
     ws = tbe_obj._ws
     N = case.N
     nb = v["num_buckets"]
-    cnt = read_u32(ws, v["counters"], 5 + 4 * (nb + 1))
-    U, nt, nm, nl, nc = (int(x) for x in cnt[:5])
+    cnt = read_u32(ws, v["counters"], 6 + 5 * (nb + 1))
+    U, n1, nt, nm, nl, nc = (int(x) for x in cnt[:6])
     out = dict(
         sorted_key=read_u32(ws, v["sorted_key"], N).astype(np.int64),
         sorted_bag=read_u32(ws, v["sorted_bag"], N).astype(np.int64),
         sorted_scale=read_u32(ws, v["sorted_scale"], N).view(np.float32),
         run_start=read_u32(ws, v["run_start"], U + 1).astype(np.int64),
         run_key=read_u32(ws, v["run_key"], U).astype(np.int64),
+        single_task=read_u32x4(ws, v["single_task"], n1).astype(np.int64),
         tiny_task=read_u32x4(ws, v["tiny_task"], nt).astype(np.int64),
         medium_task=read_u32x4(ws, v["medium_task"], nm).astype(np.int64),
         long_task=read_u32x4(ws, v["long_task"], nl).astype(np.int64),
         long_cbeg=read_u32(ws, v["long_cbeg"], nl).astype(np.int64),
         chunk_task=read_u32x4(ws, v["chunk_task"], nc).astype(np.int64),
-        U=U, n_tiny=nt, n_medium=nm, n_long=nl, n_chunks=nc, nb=nb,
-        begins=cnt[5:].reshape(4, nb + 1).astype(np.int64))
+        U=U, n_single=n1, n_tiny=nt, n_medium=nm, n_long=nl, n_chunks=nc, nb=nb,
+        begins=cnt[6:].reshape(5, nb + 1).astype(np.int64))
     kb = np.array(tbe_obj.key_bases(), np.int64)
     out["key_base"] = kb
     return out
@@ -225,8 +226,9 @@ def check_preprocess(case: Case, tbe_obj):
     assert np.array_equal(rk_o[p], r["run_key"].astype(np.int64)), "run keys differ"
     assert np.array_equal(lens_g[p], np.diff(r["run_start"])), "run lengths differ"
     olens = np.diff(r["run_start"])
-    assert g["n_tiny"] == int((olens < 32).sum()), "tiny short-run count differs"
-    assert g["n_tiny"] + g["n_medium"] == r["n_short"], "short-run count differs"
+    assert g["n_single"] == int((olens == 1).sum()), "single-lookup run count differs"
+    assert g["n_tiny"] == int(((olens >= 2) & (olens < 32)).sum()), "tiny run count differs"
+    assert g["n_single"] + g["n_tiny"] + g["n_medium"] == r["n_short"], "short-run count differs"
     assert (g["n_long"], g["n_chunks"]) == (r["n_long"], r["n_chunks"])
     # bag and contribution scale of every sorted lookup
     if case.psw is not None or any(p == wl.POOL_MEAN for p in s.pooling):
@@ -238,24 +240,27 @@ def check_preprocess(case: Case, tbe_obj):
         want = np.where(mean, sp / L[j].astype(np.float32), sp).astype(np.float32)
         np.testing.assert_allclose(g["sorted_scale"][perm], want, rtol=2.5e-7, atol=0)
     # tasks: every run appears once, in ascending key order, with its table and row
-    tt = g["tiny_task"]       # {start, row, table << 16 | len, bag of first lookup}
+    st = g["single_task"]     # {start, row, table, bag}
+    tt = g["tiny_task"]       # {start, len, row, table}
     mt = g["medium_task"]     # {start, len, row, table}
     lt = g["long_task"]
     rs = g["run_start"][:-1]
-    if len(tt):
-        t_t, t_len = tt[:, 2] >> 16, tt[:, 2] & 0xFFFF
-        assert np.all(t_len < 32) and np.all(t_len > 0)
-        assert np.array_equal(kb[t_t] + tt[:, 1], g["sorted_key"][tt[:, 0]])
-        assert np.all(np.diff(kb[t_t] + tt[:, 1]) > 0)
-        assert np.array_equal(tt[:, 0], rs[lens_g < 32])
-        assert np.array_equal(t_len, lens_g[lens_g < 32])
-        assert np.array_equal(tt[:, 3], g["sorted_bag"][tt[:, 0]])
-    med = (lens_g >= 32) & (lens_g < 256)
-    if len(mt):
-        assert np.array_equal(mt[:, 0], rs[med]) and np.array_equal(mt[:, 1], lens_g[med])
-        assert np.array_equal(kb[mt[:, 3]] + mt[:, 2], g["sorted_key"][mt[:, 0]])
+    one = lens_g == 1
+    if len(st):
+        assert np.array_equal(st[:, 0], rs[one])
+        assert np.array_equal(kb[st[:, 2]] + st[:, 1], g["sorted_key"][st[:, 0]])
+        assert np.all(np.diff(kb[st[:, 2]] + st[:, 1]) > 0)
+        assert np.array_equal(st[:, 3], g["sorted_bag"][st[:, 0]])
     else:
-        assert not med.any()
+        assert not one.any()
+    for tasks, sel in ((tt, (lens_g >= 2) & (lens_g < 32)), (mt, (lens_g >= 32) & (lens_g < 256))):
+        if len(tasks):
+            assert np.array_equal(tasks[:, 0], rs[sel])
+            assert np.array_equal(tasks[:, 1], lens_g[sel])
+            assert np.array_equal(kb[tasks[:, 3]] + tasks[:, 2], g["sorted_key"][tasks[:, 0]])
+            assert np.all(np.diff(kb[tasks[:, 3]] + tasks[:, 2]) > 0)
+        else:
+            assert not sel.any()
     if len(lt):
         assert np.all(lt[:, 1] >= 256)
         assert np.array_equal(lt[:, 0], g["run_start"][:-1][lens_g >= 256])
@@ -269,12 +274,12 @@ def check_preprocess(case: Case, tbe_obj):
             for k in range(int((ln + 255) // 256)):
                 want.append([st0 + 256 * k, min(256, ln - 256 * k), t, l])
         assert np.array_equal(ct, np.array(want, np.int64).reshape(-1, 4)), "chunk tasks differ"
-    # per-bucket begins split the four lists exactly at bucket changes
+    # per-bucket begins split the five lists exactly at bucket changes
     bt = bucket_of_table(s)
-    tiny_t = (tt[:, 2] >> 16) if len(tt) else np.zeros(0, np.int64)
-    for k, tab in enumerate((tiny_t, mt[:, 3] if len(mt) else tiny_t[:0],
-                             lt[:, 3] if len(lt) else tiny_t[:0],
-                             g["chunk_task"][:, 2] if g["n_chunks"] else tiny_t[:0])):
+    z = np.zeros(0, np.int64)
+    for k, tab in enumerate((st[:, 2] if len(st) else z, tt[:, 3] if len(tt) else z,
+                             mt[:, 3] if len(mt) else z, lt[:, 3] if len(lt) else z,
+                             g["chunk_task"][:, 2] if g["n_chunks"] else z)):
         b = g["begins"][k]
         assert b[0] == 0 and b[-1] == len(tab)
         for q in range(g["nb"]):
