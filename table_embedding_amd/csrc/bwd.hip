@@ -45,17 +45,26 @@ __device__ __forceinline__ void gather_t(const BwdArgs& a, const TableDev& td, i
                                          uint32_t i0, uint32_t i1, uint32_t step,
                                          const uint32_t* cold, float (*g)[VEC]) {
   const float* gbase = a.grad + td.col;
+  if (i0 >= i1) return;
+  // software pipeline: bag ids of batch i+1 load while the rows of batch i are in flight
+  uint32_t nbag[kInFlight];
+  float nsc[kInFlight];
+#pragma unroll
+  for (int k = 0; k < kInFlight; ++k) {
+    const uint32_t q0 = i0 + (uint32_t)k * step;
+    const uint32_t q = q0 < i1 ? q0 : i1 - 1;
+    nbag[k] = a.sorted_bag[q];
+    nsc[k] = SCALE ? a.sorted_scale[q] : 1.0f;
+  }
   for (uint32_t i = i0; i < i1; i += kInFlight * step) {
     int64_t b[kInFlight];
     float sc[kInFlight];
     bool ok[kInFlight];
 #pragma unroll
     for (int k = 0; k < kInFlight; ++k) {
-      const uint32_t q0 = i + (uint32_t)k * step;
-      ok[k] = q0 < i1;
-      const uint32_t q = ok[k] ? q0 : i1 - 1;
-      b[k] = (int64_t)a.sorted_bag[q] - tB;
-      sc[k] = SCALE ? a.sorted_scale[q] : 1.0f;
+      ok[k] = i + (uint32_t)k * step < i1;
+      b[k] = (int64_t)nbag[k] - tB;
+      sc[k] = nsc[k];
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -64,6 +73,15 @@ __device__ __forceinline__ void gather_t(const BwdArgs& a, const TableDev& td, i
 #pragma unroll
       for (int k = 0; k < kInFlight; ++k)
         load_f32<VEC>(gbase + b[k] * (int64_t)a.dtot + cold[c], v[k]);
+      if (c == 0) {
+#pragma unroll
+        for (int k = 0; k < kInFlight; ++k) {
+          const uint32_t q0 = i + (uint32_t)(kInFlight + k) * step;
+          const uint32_t q = q0 < i1 ? q0 : i1 - 1;
+          nbag[k] = a.sorted_bag[q];
+          nsc[k] = SCALE ? a.sorted_scale[q] : 1.0f;
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 0; k < kInFlight; ++k)
@@ -157,14 +175,16 @@ __device__ __forceinline__ void subgroup_row_update(const BwdArgs& a, const Tabl
 // grad_out slices and scales are loaded before the first use -- one memory
 // round trip per pair of runs after the task load.
 template <int WD, int VEC, int NC, bool SCALE, bool TDL>
-__global__ __launch_bounds__(kThreads) void bwd_single_kernel(BwdArgs a, BucketDev bk,
-                                                              uint32_t bucket) {
+__global__ __launch_bounds__(kThreads) void bwd_single_kernel(BwdArgs a, BucketSet S) {
+  BucketDev bk;
+  uint32_t bucket, lb, lg;
+  set_pick(S, bk, bucket, lb, lg);
   __shared__ TableDev s_td[TDL ? kTdCache : 1];
   load_td_cache<TDL>(a, s_td);
   const uint32_t lpr = bk.lpr;
   const uint32_t lane_in = threadIdx.x & (lpr - 1);
-  const uint32_t nsg_grid = (gridDim.x * kThreads) >> bk.lpr_log2;
-  const uint32_t sg = (blockIdx.x * kThreads + threadIdx.x) >> bk.lpr_log2;
+  const uint32_t nsg_grid = (lg * kThreads) >> bk.lpr_log2;
+  const uint32_t sg = (lb * kThreads + threadIdx.x) >> bk.lpr_log2;
   const uint32_t beg = list_begin(a, 0, bucket);
   const uint32_t end = min(list_begin(a, 0, bucket + 1), a.max_single);
   for (uint32_t s = beg + sg; s < end; s += 2 * nsg_grid) {
@@ -217,14 +237,16 @@ __global__ __launch_bounds__(kThreads) void bwd_single_kernel(BwdArgs a, BucketD
 // One subgroup of lpr lanes owns a run with 2 <= SL < 32: gather, Adagrad,
 // plain stores.  The next task record is prefetched.
 template <int WD, int VEC, int NC, bool TDL>
-__global__ __launch_bounds__(kThreads) void bwd_tiny_kernel(BwdArgs a, BucketDev bk,
-                                                            uint32_t bucket) {
+__global__ __launch_bounds__(kThreads) void bwd_tiny_kernel(BwdArgs a, BucketSet S) {
+  BucketDev bk;
+  uint32_t bucket, lb, lg;
+  set_pick(S, bk, bucket, lb, lg);
   __shared__ TableDev s_td[TDL ? kTdCache : 1];
   load_td_cache<TDL>(a, s_td);
   const uint32_t lpr = bk.lpr;
   const uint32_t lane_in = threadIdx.x & (lpr - 1);
-  const uint32_t nsg_grid = (gridDim.x * kThreads) >> bk.lpr_log2;
-  const uint32_t sg = (blockIdx.x * kThreads + threadIdx.x) >> bk.lpr_log2;
+  const uint32_t nsg_grid = (lg * kThreads) >> bk.lpr_log2;
+  const uint32_t sg = (lb * kThreads + threadIdx.x) >> bk.lpr_log2;
   const uint32_t beg = list_begin(a, 1, bucket);
   const uint32_t end = min(list_begin(a, 1, bucket + 1), a.max_tiny);
   uint32_t s = beg + sg;
@@ -391,12 +413,14 @@ __device__ __forceinline__ void chunk_store(const BwdArgs& a, const BucketDev& b
 // One workgroup owns a run with 32 <= SL < 256: its subgroups split the
 // lookups, the workgroup combines them in LDS and updates the row.
 template <int WD, int VEC, int NC>
-__global__ __launch_bounds__(kThreads) void bwd_medium_kernel(BwdArgs a, BucketDev bk,
-                                                              uint32_t bucket) {
+__global__ __launch_bounds__(kThreads) void bwd_medium_kernel(BwdArgs a, BucketSet S) {
+  BucketDev bk;
+  uint32_t bucket, lb, lg;
+  set_pick(S, bk, bucket, lb, lg);
   __shared__ WgSmem<VEC, NC> sm;
   const uint32_t beg = list_begin(a, 2, bucket);
   const uint32_t end = min(list_begin(a, 2, bucket + 1), a.max_med);
-  for (uint32_t m = beg + blockIdx.x; m < end; m += gridDim.x) {
+  for (uint32_t m = beg + lb; m < end; m += lg) {
     const uint4 task = a.med_task[m];  // {start, len, row, table}
     if (!span_ok(a, task.x, task.y, task.w, task.z)) continue;  // uniform; never for valid lists
     const TableDev td = a.tables[task.w];
@@ -409,12 +433,14 @@ __global__ __launch_bounds__(kThreads) void bwd_medium_kernel(BwdArgs a, BucketD
 // ---------------------------------------------------------------- long runs
 
 template <int WD, int VEC, int NC>
-__global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a, BucketDev bk,
-                                                             uint32_t bucket) {
+__global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a, BucketSet S) {
+  BucketDev bk;
+  uint32_t bucket, lb, lg;
+  set_pick(S, bk, bucket, lb, lg);
   __shared__ WgSmem<VEC, NC> sm;
   const uint32_t beg = list_begin(a, 4, bucket);
   const uint32_t end = min(list_begin(a, 4, bucket + 1), a.max_chunks);
-  for (uint32_t c = beg + blockIdx.x; c < end; c += gridDim.x) {
+  for (uint32_t c = beg + lb; c < end; c += lg) {
     const uint4 task = a.chunk_task[c];  // {start, len, table, long index}
     if (!chunk_ok(a, task)) continue;    // uniform per workgroup; never for valid lists
     const TableDev td = a.tables[task.z];
@@ -425,12 +451,14 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a, BucketDe
 }
 
 template <int WD, int VEC, int NC>
-__global__ __launch_bounds__(kThreads) void bwd_long_update_kernel(BwdArgs a, BucketDev bk,
-                                                                   uint32_t bucket) {
+__global__ __launch_bounds__(kThreads) void bwd_long_update_kernel(BwdArgs a, BucketSet S) {
+  BucketDev bk;
+  uint32_t bucket, lb, lg;
+  set_pick(S, bk, bucket, lb, lg);
   __shared__ WgSmem<VEC, NC> sm;
   const uint32_t beg = list_begin(a, 3, bucket);
   const uint32_t end = min(list_begin(a, 3, bucket + 1), a.max_long);
-  for (uint32_t l = beg + blockIdx.x; l < end; l += gridDim.x) {
+  for (uint32_t l = beg + lb; l < end; l += lg) {
     if (!long_ok(a, l)) continue;  // uniform per workgroup; never for valid lists
     long_update<WD, VEC, NC>(a, bk, l, sm);
   }
@@ -440,12 +468,14 @@ __global__ __launch_bounds__(kThreads) void bwd_long_update_kernel(BwdArgs a, Bu
 // down the run's remaining chunks; the workgroup that takes the count to zero
 // acquires and performs the update, then re-arms the countdown.
 template <int WD, int VEC, int NC>
-__global__ __launch_bounds__(kThreads) void bwd_chunk_fused_kernel(BwdArgs a, BucketDev bk,
-                                                                   uint32_t bucket) {
+__global__ __launch_bounds__(kThreads) void bwd_chunk_fused_kernel(BwdArgs a, BucketSet S) {
+  BucketDev bk;
+  uint32_t bucket, lb, lg;
+  set_pick(S, bk, bucket, lb, lg);
   __shared__ WgSmem<VEC, NC> sm;
   const uint32_t beg = list_begin(a, 4, bucket);
   const uint32_t end = min(list_begin(a, 4, bucket + 1), a.max_chunks);
-  for (uint32_t c = beg + blockIdx.x; c < end; c += gridDim.x) {
+  for (uint32_t c = beg + lb; c < end; c += lg) {
     const uint4 task = a.chunk_task[c];  // {start, len, table, long index}
     if (!chunk_ok(a, task) || !long_ok(a, task.w)) continue;  // uniform; never for valid lists
     const TableDev td = a.tables[task.z];
@@ -472,47 +502,82 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_fused_kernel(BwdArgs a, Bu
   }
 }
 
+// Co-resident workgroups of a kernel on the whole device (queried once per
+// instantiation).  A persistent grid larger than this would leave its last
+// workgroups waiting for earlier ones to retire, a tail.
+template <typename K>
+uint32_t resident(K kernel, int num_cus) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  return (uint32_t)per_cu * (uint32_t)num_cus;
+}
+
+// Fill S.gbeg: bucket k gets min(need_k, cap / n) workgroups (at least 1).
+uint32_t set_grid(BucketSet& S, const BwdGrids* g, uint32_t BwdGrids::*field, uint32_t cap) {
+  const uint32_t share = cap / S.n > 0 ? cap / S.n : 1u;
+  S.gbeg[0] = 0;
+  for (uint32_t k = 0; k < S.n; ++k) {
+    const uint32_t need = g[k].*field > 0 ? g[k].*field : 1u;
+    S.gbeg[k + 1] = S.gbeg[k] + (need < share ? need : share);
+  }
+  for (uint32_t k = S.n + 1; k <= (uint32_t)kMaxBuckets; ++k) S.gbeg[k] = S.gbeg[S.n];
+  return S.gbeg[S.n];
+}
+
 template <int WD, int VEC, int NC, bool TDL>
-hipError_t launch_small(const BwdArgs& a, const BucketDev& bk, uint32_t bucket,
-                        const BwdGrids& g, hipStream_t s) {
-  if (a.sorted_scale)
-    TBE_LAUNCH("bwd_single", (bwd_single_kernel<WD, VEC, NC, true, TDL>), dim3(g.single),
-               dim3(kThreads), s, a, bk, bucket);
-  else
-    TBE_LAUNCH("bwd_single", (bwd_single_kernel<WD, VEC, NC, false, TDL>), dim3(g.single),
-               dim3(kThreads), s, a, bk, bucket);
-  TBE_LAUNCH("bwd_tiny", (bwd_tiny_kernel<WD, VEC, NC, TDL>), dim3(g.tiny), dim3(kThreads), s, a,
-             bk, bucket);
-  return hipSuccess;
+void launch_small(const BwdArgs& a, BucketSet S, const BwdGrids* g, int cus, hipStream_t s) {
+  if (a.sorted_scale) {
+    static const uint32_t cap = resident(bwd_single_kernel<WD, VEC, NC, true, TDL>, cus);
+    const uint32_t grid = set_grid(S, g, &BwdGrids::single, cap);
+    TBE_LAUNCH("bwd_single", (bwd_single_kernel<WD, VEC, NC, true, TDL>), dim3(grid),
+               dim3(kThreads), s, a, S);
+  } else {
+    static const uint32_t cap = resident(bwd_single_kernel<WD, VEC, NC, false, TDL>, cus);
+    const uint32_t grid = set_grid(S, g, &BwdGrids::single, cap);
+    TBE_LAUNCH("bwd_single", (bwd_single_kernel<WD, VEC, NC, false, TDL>), dim3(grid),
+               dim3(kThreads), s, a, S);
+  }
+  static const uint32_t cap_t = resident(bwd_tiny_kernel<WD, VEC, NC, TDL>, cus);
+  const uint32_t grid = set_grid(S, g, &BwdGrids::tiny, cap_t);
+  TBE_LAUNCH("bwd_tiny", (bwd_tiny_kernel<WD, VEC, NC, TDL>), dim3(grid), dim3(kThreads), s, a,
+             S);
 }
 
 template <int WD, int VEC, int NC>
-hipError_t launch(const BwdArgs& a, const BucketDev& bk, uint32_t bucket, bool fused,
-                  const BwdGrids& g, hipStream_t s) {
+hipError_t launch(const BwdArgs& a, BucketSet S, const BwdGrids* g, bool fused, int cus,
+                  hipStream_t s) {
   if (a.T <= (uint32_t)kTdCache)
-    (void)launch_small<WD, VEC, NC, true>(a, bk, bucket, g, s);
+    launch_small<WD, VEC, NC, true>(a, S, g, cus, s);
   else
-    (void)launch_small<WD, VEC, NC, false>(a, bk, bucket, g, s);
-  TBE_LAUNCH("bwd_medium", (bwd_medium_kernel<WD, VEC, NC>), dim3(g.medium), dim3(kThreads), s,
-             a, bk, bucket);
+    launch_small<WD, VEC, NC, false>(a, S, g, cus, s);
+  static const uint32_t cap_m = resident(bwd_medium_kernel<WD, VEC, NC>, cus);
+  uint32_t grid = set_grid(S, g, &BwdGrids::medium, cap_m);
+  TBE_LAUNCH("bwd_medium", (bwd_medium_kernel<WD, VEC, NC>), dim3(grid), dim3(kThreads), s, a, S);
   if (fused) {
-    TBE_LAUNCH("bwd_chunk_fused", (bwd_chunk_fused_kernel<WD, VEC, NC>), dim3(g.chunk),
-               dim3(kThreads), s, a, bk, bucket);
+    static const uint32_t cap_f = resident(bwd_chunk_fused_kernel<WD, VEC, NC>, cus);
+    grid = set_grid(S, g, &BwdGrids::chunk, cap_f);
+    TBE_LAUNCH("bwd_chunk_fused", (bwd_chunk_fused_kernel<WD, VEC, NC>), dim3(grid),
+               dim3(kThreads), s, a, S);
   } else {
-    TBE_LAUNCH("bwd_chunk", (bwd_chunk_kernel<WD, VEC, NC>), dim3(g.chunk), dim3(kThreads), s, a,
-               bk, bucket);
-    TBE_LAUNCH("bwd_long_update", (bwd_long_update_kernel<WD, VEC, NC>), dim3(g.longrun),
-               dim3(kThreads), s, a, bk, bucket);
+    static const uint32_t cap_c = resident(bwd_chunk_kernel<WD, VEC, NC>, cus);
+    grid = set_grid(S, g, &BwdGrids::chunk, cap_c);
+    TBE_LAUNCH("bwd_chunk", (bwd_chunk_kernel<WD, VEC, NC>), dim3(grid), dim3(kThreads), s, a, S);
+    static const uint32_t cap_l = resident(bwd_long_update_kernel<WD, VEC, NC>, cus);
+    grid = set_grid(S, g, &BwdGrids::longrun, cap_l);
+    TBE_LAUNCH("bwd_long_update", (bwd_long_update_kernel<WD, VEC, NC>), dim3(grid),
+               dim3(kThreads), s, a, S);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_backward_bucket(const BwdArgs& a, const BucketDev& bk, uint32_t bucket, int wd,
-                                  int vec, int nc, bool fused, const BwdGrids& g, hipStream_t s) {
+hipError_t launch_backward_set(const BwdArgs& a, BucketSet S, const BwdGrids* g, int wd, int vec,
+                               int nc, bool fused, int num_cus, hipStream_t s) {
 #define TBE_BWD_CASE(W, V, N) \
-  if (wd == W && vec == V && nc == N) return launch<W, V, N>(a, bk, bucket, fused, g, s);
+  if (wd == W && vec == V && nc == N) return launch<W, V, N>(a, S, g, fused, num_cus, s);
   TBE_BWD_CASE(WD_F32, 4, 1)
   TBE_BWD_CASE(WD_F32, 4, 2)
   TBE_BWD_CASE(WD_F32, 4, 4)

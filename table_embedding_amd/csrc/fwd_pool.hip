@@ -31,11 +31,14 @@ struct Acc<WD_F32> {
 };
 
 template <int WD, int VEC, int NC, typename IT, bool PSW>
-__global__ __launch_bounds__(kThreads) void fwd_pool_kernel(FwdArgs a, BucketDev bk) {
+__global__ __launch_bounds__(kThreads) void fwd_pool_kernel(FwdArgs a, BucketSet S) {
   using AT = typename Acc<WD>::T;
+  BucketDev bk;
+  uint32_t bucket_id, lb, lg;
+  set_pick(S, bk, bucket_id, lb, lg);
   const uint32_t lpr = bk.lpr;
   const uint32_t lane_in = threadIdx.x & (lpr - 1);
-  const uint64_t sg = ((uint64_t)blockIdx.x * kThreads + threadIdx.x) >> bk.lpr_log2;
+  const uint64_t sg = ((uint64_t)lb * kThreads + threadIdx.x) >> bk.lpr_log2;
   const uint64_t nbags = (uint64_t)bk.ntables * (uint64_t)a.B;
   if (sg >= nbags) return;
   const uint32_t slot = (uint32_t)(sg / (uint64_t)a.B);
@@ -61,16 +64,27 @@ __global__ __launch_bounds__(kThreads) void fwd_pool_kernel(FwdArgs a, BucketDev
     cold[c] = act[c] ? colc[c] : 0u;  // idle lanes read column 0 and discard it
   }
 
+  // software pipeline: the indices of batch i+1 are loaded while the rows of
+  // batch i are in flight, so a batch costs one memory round trip
+  int64_t nrow[kInFlight];
+  float ns[kInFlight];
+  if (lo < hi) {
+#pragma unroll
+    for (int k = 0; k < kInFlight; ++k) {
+      const int64_t q = lo + k < hi ? lo + k : hi - 1;
+      nrow[k] = (int64_t)I[q];
+      ns[k] = PSW ? a.psw[q] : 1.0f;
+    }
+  }
   for (int64_t p = lo; p < hi; p += kInFlight) {
     int64_t row[kInFlight];
     float s[kInFlight];
     bool ok[kInFlight];
 #pragma unroll
     for (int k = 0; k < kInFlight; ++k) {
+      row[k] = nrow[k];
+      s[k] = ns[k];
       ok[k] = p + k < hi;
-      const int64_t q = ok[k] ? p + k : hi - 1;
-      row[k] = (int64_t)I[q];
-      s[k] = PSW ? a.psw[q] : 1.0f;
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -78,6 +92,14 @@ __global__ __launch_bounds__(kThreads) void fwd_pool_kernel(FwdArgs a, BucketDev
       float v[kInFlight][VEC];
 #pragma unroll
       for (int k = 0; k < kInFlight; ++k) load_w<WD, VEC>(td.w, row[k] * D + cold[c], v[k]);
+      if (c == 0) {
+#pragma unroll
+        for (int k = 0; k < kInFlight; ++k) {
+          const int64_t q = p + kInFlight + k < hi ? p + kInFlight + k : hi - 1;
+          nrow[k] = (int64_t)I[q];
+          ns[k] = PSW ? a.psw[q] : 1.0f;
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 0; k < kInFlight; ++k)
@@ -100,29 +122,27 @@ __global__ __launch_bounds__(kThreads) void fwd_pool_kernel(FwdArgs a, BucketDev
 }
 
 template <int WD, int VEC, int NC, typename IT, bool PSW>
-hipError_t launch_t(const FwdArgs& a, const BucketDev& bk, hipStream_t s) {
-  const uint64_t nbags = (uint64_t)bk.ntables * (uint64_t)a.B;
-  const uint64_t per_block = kThreads / bk.lpr;
-  const uint64_t grid = (nbags + per_block - 1) / per_block;
+hipError_t launch_t(const FwdArgs& a, const BucketSet& S, hipStream_t s) {
+  const uint32_t grid = S.gbeg[S.n];
   if (grid == 0) return hipSuccess;
-  TBE_LAUNCH("fwd_pool", (fwd_pool_kernel<WD, VEC, NC, IT, PSW>), dim3((uint32_t)grid),
-             dim3(kThreads), s, a, bk);
+  TBE_LAUNCH("fwd_pool", (fwd_pool_kernel<WD, VEC, NC, IT, PSW>), dim3(grid), dim3(kThreads), s,
+             a, S);
   return hipGetLastError();
 }
 
 template <int WD, int VEC, int NC>
-hipError_t launch(const FwdArgs& a, const BucketDev& bk, hipStream_t s) {
+hipError_t launch(const FwdArgs& a, const BucketSet& S, hipStream_t s) {
   if (a.itype == IT_I32)
-    return a.psw ? launch_t<WD, VEC, NC, int32_t, true>(a, bk, s)
-                 : launch_t<WD, VEC, NC, int32_t, false>(a, bk, s);
-  return a.psw ? launch_t<WD, VEC, NC, int64_t, true>(a, bk, s)
-               : launch_t<WD, VEC, NC, int64_t, false>(a, bk, s);
+    return a.psw ? launch_t<WD, VEC, NC, int32_t, true>(a, S, s)
+                 : launch_t<WD, VEC, NC, int32_t, false>(a, S, s);
+  return a.psw ? launch_t<WD, VEC, NC, int64_t, true>(a, S, s)
+               : launch_t<WD, VEC, NC, int64_t, false>(a, S, s);
 }
 
 }  // namespace
 
-hipError_t launch_forward_bucket(const FwdArgs& a, const BucketDev& bk, int wd, int vec, int nc,
-                                 hipStream_t s) {
+hipError_t launch_forward_set(const FwdArgs& a, const BucketSet& bk, int wd, int vec, int nc,
+                              hipStream_t s) {
 #define TBE_FWD_CASE(W, V, N) \
   if (wd == W && vec == V && nc == N) return launch<W, V, N>(a, bk, s);
   TBE_FWD_CASE(WD_F32, 4, 1)

@@ -133,16 +133,39 @@ bool hist_eligible(const tbe_plan* P, int64_t B, int64_t N, const float* psw) {
          P->wdtype == TBE_F16 && psw == nullptr && B > 0 && N >= 64 * B;
 }
 
-int persistent_grid(const tbe_plan* P, uint64_t work_items, uint32_t items_per_block) {
-  const uint64_t need = (work_items + items_per_block - 1) / items_per_block;
-  const uint64_t cap = (uint64_t)P->num_cus * 8;
-  return (int)std::max<uint64_t>(1, std::min(need, cap));
-}
-
 bool any_mean(const tbe_plan* P) {
   for (int32_t p : P->pooling)
     if (p == TBE_MEAN) return true;
   return false;
+}
+
+// Buckets that share one kernel instantiation (vec, nc), in bucket order.
+std::vector<std::vector<uint32_t>> bucket_groups(const tbe_plan* P) {
+  std::vector<std::vector<uint32_t>> groups;
+  for (uint32_t b = 0; b < P->buckets.size(); ++b) {
+    bool placed = false;
+    for (auto& g : groups) {
+      const Bucket& h = P->buckets[g[0]];
+      if (h.vec == P->buckets[b].vec && h.nc == P->buckets[b].nc) {
+        g.push_back(b);
+        placed = true;
+        break;
+      }
+    }
+    if (!placed) groups.push_back({b});
+  }
+  return groups;
+}
+
+BucketSet bucket_set(const tbe_plan* P, const std::vector<uint32_t>& grp) {
+  BucketSet S{};
+  S.n = (uint32_t)grp.size();
+  for (uint32_t k = 0; k < S.n; ++k) {
+    const Bucket& bk = P->buckets[grp[k]];
+    S.bk[k] = BucketDev{bk.d_tables, (uint32_t)bk.tables.size(), bk.lpr, bk.lpr_log2};
+    S.id[k] = grp[k];
+  }
+  return S;
 }
 
 PrepArgs prep_args(const tbe_plan* P, int64_t B, int32_t itype, const void* indices,
@@ -459,9 +482,17 @@ int tbe_forward(const tbe_plan* P, int64_t B, int32_t itype, const void* indices
     e = launch_forward_hist(a, (uint32_t)P->rows[0], (uint32_t)P->dims[0],
                             P->pooling[0] == TBE_MEAN, P->num_cus * 4, s);
   } else {
-    for (const Bucket& bk : P->buckets) {
-      BucketDev bd{bk.d_tables, (uint32_t)bk.tables.size(), bk.lpr, bk.lpr_log2};
-      e = launch_forward_bucket(a, bd, P->wdtype, bk.vec, bk.nc, s);
+    for (const auto& grp : bucket_groups(P)) {
+      BucketSet S = bucket_set(P, grp);
+      S.gbeg[0] = 0;
+      for (uint32_t k = 0; k < S.n; ++k) {
+        const uint64_t nbags = (uint64_t)S.bk[k].ntables * (uint64_t)B;
+        const uint64_t per_block = kThreads / S.bk[k].lpr;
+        S.gbeg[k + 1] = S.gbeg[k] + (uint32_t)((nbags + per_block - 1) / per_block);
+      }
+      for (uint32_t k = S.n + 1; k <= (uint32_t)kMaxBuckets; ++k) S.gbeg[k] = S.gbeg[S.n];
+      const Bucket& b0 = P->buckets[grp[0]];
+      e = launch_forward_set(a, S, P->wdtype, b0.vec, b0.nc, s);
       if (e != hipSuccess) break;
     }
   }
@@ -539,16 +570,20 @@ int tbe_backward_rowwise_adagrad(const tbe_plan* P, int64_t B, int32_t itype,
   a.max_long = L.max_long;
   a.max_chunks = L.max_chunks;
   const bool fused = flags & TBE_BWD_FUSED_LONG;
-  for (uint32_t b = 0; b < P->buckets.size(); ++b) {
-    const Bucket& bk = P->buckets[b];
-    BucketDev bd{bk.d_tables, (uint32_t)bk.tables.size(), bk.lpr, bk.lpr_log2};
-    BwdGrids g;
-    g.single = (uint32_t)persistent_grid(P, (uint64_t)N, 2 * (kThreads / bk.lpr));
-    g.tiny = (uint32_t)persistent_grid(P, L.max_tiny, kThreads / bk.lpr);
-    g.medium = (uint32_t)persistent_grid(P, L.max_med, 1);
-    g.chunk = (uint32_t)persistent_grid(P, L.max_chunks, 1);
-    g.longrun = (uint32_t)persistent_grid(P, L.max_long, 1);
-    if (launch_backward_bucket(a, bd, b, P->wdtype, bk.vec, bk.nc, fused, g, s) != hipSuccess)
+  for (const auto& grp : bucket_groups(P)) {
+    BucketSet S = bucket_set(P, grp);
+    BwdGrids g[kMaxBuckets];
+    for (uint32_t k = 0; k < S.n; ++k) {
+      const uint64_t sgs = kThreads / S.bk[k].lpr;  // subgroups per workgroup
+      g[k].single = (uint32_t)std::min<uint64_t>((uint64_t)N / (2 * sgs) + 1, 1u << 30);
+      g[k].tiny = (uint32_t)std::min<uint64_t>(L.max_tiny / sgs + 1, 1u << 30);
+      g[k].medium = L.max_med;
+      g[k].chunk = L.max_chunks;
+      g[k].longrun = L.max_long;
+    }
+    const Bucket& b0 = P->buckets[grp[0]];
+    if (launch_backward_set(a, S, g, P->wdtype, b0.vec, b0.nc, fused, P->num_cus, s) !=
+        hipSuccess)
       return TBE_E_HIP;
   }
   return TBE_OK;

@@ -43,6 +43,41 @@ struct BucketDev {
   uint32_t lpr_log2;
 };
 
+constexpr int kMaxBuckets = 9;  // next_pow2 widths 4 .. 1024
+
+// Buckets that share one kernel instantiation are served by one launch:
+// workgroups [gbeg[k], gbeg[k+1]) work on bucket id[k] with lane mapping bk[k].
+struct BucketSet {
+  uint32_t n;
+  uint32_t gbeg[kMaxBuckets + 1];
+  uint32_t id[kMaxBuckets];
+  BucketDev bk[kMaxBuckets];
+};
+
+// This workgroup's bucket, its index inside the bucket's range and the range
+// size.  Selection with constant indices only (scalar selects, no indexing of
+// the argument block).
+__device__ __forceinline__ void set_pick(const BucketSet& S, BucketDev& bk, uint32_t& id,
+                                         uint32_t& lb, uint32_t& lg) {
+  uint32_t k = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxBuckets; ++i)
+    if (i < (int)S.n && blockIdx.x >= S.gbeg[i]) k = (uint32_t)i;
+  bk = S.bk[0];
+  id = S.id[0];
+  uint32_t g0 = S.gbeg[0], g1 = S.gbeg[1];
+#pragma unroll
+  for (int i = 1; i < kMaxBuckets; ++i)
+    if ((uint32_t)i == k) {
+      bk = S.bk[i];
+      id = S.id[i];
+      g0 = S.gbeg[i];
+      g1 = S.gbeg[i + 1];
+    }
+  lb = blockIdx.x - g0;
+  lg = g1 - g0;
+}
+
 // Workspace layout: byte offsets from the workspace base (all 256-B aligned).
 struct WsLayout {
   size_t key_a, key_b, val_a, val_b, sc_a, sc_b;  // sort ping-pong: key, bag id, scale
@@ -241,17 +276,22 @@ struct BwdArgs {
   uint32_t max_single, max_tiny, max_med, max_long, max_chunks;  // list capacities
 };
 
-hipError_t launch_forward_bucket(const FwdArgs& a, const BucketDev& bk, int wd, int vec, int nc,
-                                 hipStream_t s);
+// One forward launch for the buckets of S (S.gbeg filled: bags of bucket k
+// over workgroups [gbeg[k], gbeg[k+1])).
+hipError_t launch_forward_set(const FwdArgs& a, const BucketSet& S, int wd, int vec, int nc,
+                              hipStream_t s);
 hipError_t launch_forward_hist(const FwdArgs& a, uint32_t E, uint32_t D, int mean, int grid,
                                hipStream_t s);
 hipError_t launch_preprocess(const PrepArgs& a, int grid_persist, hipStream_t s);
-// Persistent grid sizes of the backward kernels of one bucket.
+// Most workgroups each backward kernel of one bucket can use (upper bounds
+// from host-known sizes); launches clamp them to the co-resident capacity.
 struct BwdGrids {
   uint32_t single, tiny, medium, chunk, longrun;
 };
 
-hipError_t launch_backward_bucket(const BwdArgs& a, const BucketDev& bk, uint32_t bucket, int wd,
-                                  int vec, int nc, bool fused, const BwdGrids& g, hipStream_t s);
+// One launch per backward kernel for the buckets of S (S.gbeg is filled here
+// from the per-bucket grids g[0 .. S.n-1]).
+hipError_t launch_backward_set(const BwdArgs& a, BucketSet S, const BwdGrids* g, int wd, int vec,
+                               int nc, bool fused, int num_cus, hipStream_t s);
 
 }  // namespace tbe
