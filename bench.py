@@ -26,8 +26,9 @@ sys.path.insert(0, ROOT)
 METRIC = "TBE fwd+bwd lookups/sec and achieved HBM GB/s (% of MI355X peak)"
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = {
-    "fwd_pool": "fwd_pool.hip", "fwd_hist": "fwd_hist.hip", "bwd_short": "bwd.hip",
-    "bwd_chunk": "bwd.hip", "bwd_long_update": "bwd.hip", "bwd_chunk_fused": "bwd.hip",
+    "fwd_pool": "fwd_pool.hip", "fwd_hist": "fwd_hist.hip", "bwd_single": "bwd.hip",
+    "bwd_tiny": "bwd.hip", "bwd_medium": "bwd.hip", "bwd_chunk": "bwd.hip",
+    "bwd_long_update": "bwd.hip", "bwd_chunk_fused": "bwd.hip",
 }
 
 
@@ -74,19 +75,24 @@ def device_inputs(spec, torch):
 
 # --------------------------------------------------------------- byte model
 
+SL_CLASSES = (("single", 1, 2), ("tiny", 2, 32), ("medium", 32, 256), ("long", 256, None))
+
+
 def workload_stats(spec, off, idx):
-    """Per-table lookups, unique rows and run-length split (host, from the inputs)."""
+    """Per-table lookups, unique rows and the run-length classes the backward
+    splits runs into (host, from the inputs)."""
     B = spec.B
     st = []
     for t in range(spec.T):
         lo, hi = int(off[t * B]), int(off[(t + 1) * B])
         _, cnt = np.unique(idx[lo:hi], return_counts=True)
-        long_ = cnt >= 256
-        st.append(dict(n=hi - lo, U=int(cnt.size), n_short=int((~long_).sum()),
-                       n_long=int(long_.sum()), N_short=int(cnt[~long_].sum()),
-                       N_long=int(cnt[long_].sum()),
-                       chunks=int(((cnt[long_] + 255) // 256).sum()), D=spec.dims[t],
-                       mean=spec.pooling[t] == 1))
+        s = dict(n=hi - lo, U=int(cnt.size), D=spec.dims[t], mean=spec.pooling[t] == 1)
+        for name, a, b in SL_CLASSES:
+            m = (cnt >= a) if b is None else ((cnt >= a) & (cnt < b))
+            s["n_" + name] = int(m.sum())
+            s["N_" + name] = int(cnt[m].sum())
+        s["chunks"] = int(((cnt[cnt >= 256] + 255) // 256).sum())
+        st.append(s)
     return st
 
 
@@ -97,6 +103,7 @@ def byte_model(spec, st, hist_path):
     si = 4 if spec.itype == "i32" else 8
     sw = 4 if spec.wdtype == "f32" else 2
     psi = 1 if spec.weighted else 0
+    sc = 1 if (spec.weighted or any(p == 1 for p in spec.pooling)) else 0
     T, B = spec.T, spec.B
     N = sum(s["n"] for s in st)
     U = sum(s["U"] for s in st)
@@ -115,37 +122,45 @@ def byte_model(spec, st, hist_path):
                             + sum(s["U"] * s["D"] * sw for s in st))
         logi["fwd_pool"] = (N * (si + 4 * psi) + (T * B + 1) * si + out_bytes
                             + sum(s["n"] * s["D"] * sw for s in st))
-    comp["transpose"] = N * si + (T * B + 1) * si + 8 * N
-    comp["radix_upsweep"] = npass * 4 * N
+    rec = 8 + 4 * sc  # sorted key + bag id (+ contribution scale)
+    n = {c: sum(s["n_" + c] for s in st) for c, _, _ in SL_CLASSES}
+    n_chunks = sum(s["chunks"] for s in st)
+    comp["transpose"] = N * (si + 4 * psi) + (T * B + 1) * si + N * rec
+    comp["radix_upsweep"] = npass * (4 * N + 256 * 4 * ntiles)
     comp["radix_scan"] = npass * 2 * 256 * ntiles * 4
-    comp["radix_downsweep"] = (12 + 16 * (npass - 1)) * N
-    comp["rle_count"] = 4 * N
+    comp["radix_downsweep"] = npass * (2 * rec * N + 256 * 4 * ntiles)
+    comp["rle_count"] = 4 * N + 4 * ntiles
     comp["rle_scan"] = 8 * ntiles
-    comp["rle_write"] = 4 * N + 8 * U
+    comp["rle_write"] = 4 * N + 8 * U + 4
     comp["cls_count"] = 4 * (U + 1)
     comp["cls_scan"] = 24 * ntiles
-    n_long = sum(s["n_long"] for s in st)
-    n_chunks = sum(s["chunks"] for s in st)
-    comp["cls_write"] = 8 * U + 16 * U + 24 * n_long + 16 * n_chunks
+    comp["cls_write"] = (8 * U + 4 + 4 * n["single"] + 16 * (U + n_chunks) + 4 * n["long"])
     for k in list(comp):
         logi.setdefault(k, comp[k])
-    cs = cl = cu = 0
-    ls = ll = 0
+    per_lookup = 4 + 4 * sc  # sorted bag id (+ scale)
+    c = {k: 0.0 for k in ("bwd_single", "bwd_tiny", "bwd_medium", "bwd_chunk",
+                          "bwd_long_update")}
+    lg = dict(c)
     for s in st:
         D = s["D"]
-        meta = 8 + 4 * psi + (2 * si if s["mean"] else 0)
-        g_share_s = G_bytes * s["N_short"] / max(N, 1)
-        g_share_l = G_bytes * s["N_long"] / max(N, 1)
-        cs += 16 * s["n_short"] + s["N_short"] * meta + g_share_s + s["n_short"] * (2 * D * sw + 8)
-        ls += 16 * s["n_short"] + s["N_short"] * (meta + 4 * D) + s["n_short"] * (2 * D * sw + 8)
-        cl += 16 * s["chunks"] + s["N_long"] * meta + g_share_l + 4 * s["chunks"] * D
-        ll += 16 * s["chunks"] + s["N_long"] * (meta + 4 * D) + 4 * s["chunks"] * D
-        cu += 16 * s["n_long"] + 4 * s["chunks"] * D + s["n_long"] * (2 * D * sw + 8)
-    comp["bwd_short"], logi["bwd_short"] = cs, ls
-    comp["bwd_chunk"], logi["bwd_chunk"] = cl, ll
-    comp["bwd_long_update"] = logi["bwd_long_update"] = cu
-    comp["bwd_chunk_fused"] = cl + cu
-    logi["bwd_chunk_fused"] = ll + cu
+        rmw = 2 * D * sw + 8  # weight row and momentum, read and written once
+        for cls, kern in (("single", "bwd_single"), ("tiny", "bwd_tiny"),
+                          ("medium", "bwd_medium")):
+            runs, lk = s["n_" + cls], s["N_" + cls]
+            g_share = G_bytes * lk / max(N, 1)
+            meta = 16 * runs + (4 * sc * lk if cls == "single" else per_lookup * lk)
+            c[kern] += meta + g_share + runs * rmw
+            lg[kern] += meta + lk * 4 * D + runs * rmw
+        lk, ch = s["N_long"], s["chunks"]
+        c["bwd_chunk"] += 16 * ch + per_lookup * lk + G_bytes * lk / max(N, 1) + 4 * ch * D
+        lg["bwd_chunk"] += 16 * ch + per_lookup * lk + 4 * D * lk + 4 * ch * D
+        upd = 20 * s["n_long"] + 4 * ch * D + s["n_long"] * rmw
+        c["bwd_long_update"] += upd
+        lg["bwd_long_update"] += upd
+    comp.update(c)
+    logi.update(lg)
+    comp["bwd_chunk_fused"] = c["bwd_chunk"] + c["bwd_long_update"]
+    logi["bwd_chunk_fused"] = lg["bwd_chunk"] + lg["bwd_long_update"]
     return comp, logi
 
 
@@ -278,9 +293,13 @@ def main():
 
     # per-kernel durations: HIP events around each launch, on the launch stream
     te.tbe_prof_enable(True)
+    torch.cuda.synchronize()
+    e0.record()
     for _ in range(args.steps):
         step()
+    e1.record()
     torch.cuda.synchronize()
+    ms_prof = e0.elapsed_time(e1) / args.steps
     prof = te.tbe_prof_read()
     te.tbe_prof_enable(False)
 
@@ -328,6 +347,9 @@ def main():
                 "frac_of_peak_compulsory": round(step_comp / (ms * 1e6) / HBM_PEAK_GBS, 4),
                 "logical_bytes_per_step": int(step_logi),
                 "effective_gbs_logical": round(step_logi / (ms * 1e6), 1)},
+        "kernel_timing": {"method": "HIP events around every launch on its own stream, "
+                                    "over a second pass of the same steps",
+                          "ms_per_step_with_events": round(ms_prof, 5)},
         "kernels": kernels,
         "cpu_baseline": None,
     }
