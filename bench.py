@@ -125,16 +125,20 @@ def byte_model(spec, st, hist_path):
     rec = 8 + 4 * sc  # sorted key + bag id (+ contribution scale)
     n = {c: sum(s["n_" + c] for s in st) for c, _, _ in SL_CLASSES}
     n_chunks = sum(s["chunks"] for s in st)
+    ncls = -(-N // 2048)
+    st_words = 2 * ntiles * 256 + ntiles + ncls * 8  # look-back status words
     comp["transpose"] = N * (si + 4 * psi) + (T * B + 1) * si + N * rec
-    comp["radix_upsweep"] = npass * (4 * N + 256 * 4 * ntiles)
-    comp["radix_scan"] = npass * 2 * 256 * ntiles * 4
-    comp["radix_downsweep"] = npass * (2 * rec * N + 256 * 4 * ntiles)
-    comp["rle_count"] = 4 * N + 4 * ntiles
-    comp["rle_scan"] = 8 * ntiles
-    comp["rle_write"] = 4 * N + 8 * U + 4
-    comp["cls_count"] = 4 * (U + 1)
-    comp["cls_scan"] = 24 * ntiles
-    comp["cls_write"] = (8 * U + 4 + 4 * n["single"] + 16 * (U + n_chunks) + 4 * n["long"])
+    # one read of the keys gives the per-tile digit counts of every pass; the
+    # look-back status words are cleared here
+    comp["radix_upsweep"] = 4 * N + npass * 256 * 4 * ntiles + 8 * st_words
+    comp["radix_scan"] = npass * 256 * 4 * ntiles + 256 * 4 * ntiles
+    # per pass: the records read and written once; the look-back passes also
+    # publish each tile's 256 status words twice and clear a row for later
+    comp["radix_downsweep"] = 2 * rec * N + 256 * 4 * ntiles
+    comp["sort_pass"] = (npass - 1) * (2 * rec * N + 3 * 8 * 256 * ntiles)
+    comp["rle"] = 4 * N + 8 * U + 4 + 16 * ntiles
+    comp["classify"] = (8 * U + 4 + 4 * n["single"] + 16 * (U + n_chunks) + 8 * n["long"]
+                        + 16 * 8 * ncls)
     for k in list(comp):
         logi.setdefault(k, comp[k])
     per_lookup = 4 + 4 * sc  # sorted bag id (+ scale)

@@ -109,6 +109,8 @@ typedef struct {
   size_t chunk_task;   /* n_chunks uint32x4 {start, len, table, long index}: 256-lookup chunks */
   size_t counters;     /* uint32 {U, n_single, n_tiny, n_medium, n_long, n_chunks, then for
                           each of the five lists its nb+1 per-D-bucket begins} */
+  size_t prep_error;   /* uint32, 0 after a good preprocessing; nonzero if a cross-workgroup
+                          wait of the scans gave up after its poll limit (results invalid) */
   size_t total;        /* bytes needed */
   int32_t num_buckets; /* nb */
 } tbe_ws_views;

@@ -46,7 +46,7 @@ class WsViews(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in ("sorted_key", "sorted_bag",
                                            "sorted_scale", "run_start", "run_key", "single_task", "tiny_task",
                                            "medium_task", "long_task", "long_cbeg",
-                                           "chunk_task", "counters", "total")] + [
+                                           "chunk_task", "counters", "prep_error", "total")] + [
         ("num_buckets", C.c_int32)]
 
 

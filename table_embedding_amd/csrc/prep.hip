@@ -1,48 +1,131 @@
-// Backward preprocessing on the device (FBTriton TBE page, "Backward":
-// transposition, sorting and run-length encoding regroup "rows a sample used"
-// into "samples that used a row"; runs shorter than 256 lookups and longer
-// runs take different paths; section "Fewer reads and synchronizations": the
-// number of long runs is known only at run time, so task lists are compacted
-// on the GPU and later kernels read device-resident counts).  HugeCTR's
-// walkthrough prints the same pipeline (sample-id expansion, radix sort by
-// row with the end bit trimmed to the vocabulary, run flags + inclusive scan +
-// run offsets).
+// Backward preprocessing on the device (FBTriton TBE page, "Backward": the
+// lookups are transposed from bag order to row order by sorting them on their
+// row and run-length encoding the sorted rows; runs shorter than 256 lookups
+// and longer runs take different paths; section "Fewer reads and
+// synchronizations": how many long runs there are is known only on the
+// device, so the task lists are compacted there and later kernels read
+// device-resident counts).  HugeCTR's backward walkthrough has the same
+// pipeline (sample ids expanded per lookup, radix sort by row with the end
+// bit cut to the vocabulary, run flags, scan, run offsets).
 //
-// Kernels, in launch order (all 256 threads, no host readback anywhere):
-//   transpose      key[p] = key_base[t] + I[p], bag[p] = j, and, with
-//                  per-sample weights or a mean table, scale[p] = S[p]*(1/L)
-//   radix passes   stable LSD sort by key over bits [0, ceil(log2(sum R))),
-//                  8-bit digits, payload = bag id (+ scale): upsweep (LDS digit
-//                  histogram per tile) -> scan (one workgroup per digit) ->
-//                  downsweep (wave-ballot ranking, LDS reorder, coalesced
-//                  scatter).  The payload rides along, so the sorted bag ids
-//                  come out of the last pass without a gather.
-//   rle_count / rle_scan / rle_write   run heads -> run_start, run_key, U
-//   cls_count / cls_scan / cls_write   tiny / medium short-run tasks, long
-//                                      tasks, chunk tasks, per-bucket begins,
-//                                      fused countdowns
+// Kernels, in launch order (256 threads each, no host readback anywhere):
+//   prep_init      zeroes the control block (digit histograms, tile tickets,
+//                  error flag) and the look-back status words of the first
+//                  sort pass, the run-length pass and the classification pass
+//   transpose      key[p] = key_base[t] + I[p], bag[p] = j and, with
+//                  per-sample weights or a mean table, scale[p] = S[p]*(1/L);
+//                  also counts every radix digit of every pass (LDS
+//                  histograms, one global add per bin and workgroup)
+//   sort_pass      one launch per 8-bit digit, least significant first: a
+//                  stable scatter of 4096-key tiles whose global offsets come
+//                  from the digit totals plus a decoupled look-back over the
+//                  earlier tiles' per-digit counts (no separate upsweep or scan)
+//   rle            run heads of the sorted keys -> run_start, run_key, U (tile
+//                  offsets by look-back)
+//   classify       one-lookup / tiny / medium short-run tasks, long-run tasks,
+//                  256-lookup chunk tasks, per-bucket begins and the fused
+//                  countdowns (five list offsets by look-back)
 //
-// Every tile kernel loads its whole tile (16 values per thread, clamped at the
-// ragged end) before it computes, so the loads of a thread are in flight
-// together instead of one memory round trip per element.
+// Look-back protocol: a workgroup takes its tile number from an atomic ticket,
+// so every smaller tile belongs to a workgroup that is already running and
+// never waits on a larger one; every wait therefore ends.  It publishes its own
+// count ("aggregate"), adds the published values of the tiles before it until
+// it meets an inclusive prefix, then publishes its own inclusive prefix.  The
+// status words are read and written with relaxed device-scope atomics; they
+// carry the counts themselves, so no other memory needs ordering.  A wait is
+// bounded: past kSpinLimit polls it sets the error flag and goes on, which
+// spoils the result but lets the kernel finish.
 #include "tbe_common.h"
 
 namespace tbe {
 namespace {
 
 constexpr int kItems = kTile / kThreads;  // 16 keys per thread
+constexpr int kClsItems = kClsTile / kThreads;  // 4 runs per thread
+
+constexpr uint64_t kStAgg = 1ull << 62;  // the tile's own count is published
+constexpr uint64_t kStPre = 2ull << 62;  // the inclusive prefix through the tile is published
+constexpr uint64_t kStFlags = 3ull << 62;
+constexpr uint32_t kSpinLimit = 1u << 20;
 
 struct PrepDev {
   const TableDev* tables;
   uint32_t T, nb;
   int64_t B;
-  int itype;
   const void* indices;
   const void* offsets;
   const float* psw;
   uint32_t N;
-  uint32_t ntiles;
 };
+
+__device__ __forceinline__ void st_publish(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t st_read(uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Sum of the counts of tiles [0, tile) in column `col` of a status table with
+// `stride` words per tile.  W predecessors are read per round trip; the ready
+// ones nearest the tile are consumed up to the first inclusive prefix.
+template <int W>
+__device__ uint32_t look_back(uint64_t* st, uint32_t tile, uint32_t stride, uint32_t col,
+                              uint32_t* err) {
+  uint32_t excl = 0, spins = 0;
+  uint32_t t = tile;  // tiles [0, t) are still to be summed
+  while (t > 0) {
+    uint64_t v[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w)
+      v[w] = (t > (uint32_t)w) ? st_read(st + (size_t)(t - 1 - w) * stride + col) : kStPre;
+    uint32_t sum = 0, used = 0;
+    bool done = false, stall = false;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      if (done || stall) continue;
+      if (t <= (uint32_t)w) {  // past tile 0: nothing more to add
+        done = true;
+        continue;
+      }
+      const uint64_t f = v[w] & kStFlags;
+      if (f == 0) {
+        stall = true;
+        continue;
+      }
+      sum += (uint32_t)v[w];
+      ++used;
+      if (f == kStPre) done = true;
+    }
+    excl += sum;
+    t -= used;
+    if (done) break;
+    if (stall) {
+      if (++spins >= kSpinLimit) {
+        atomicOr(err, 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  return excl;
+}
+
+// Publish a tile's count, look back, publish its inclusive prefix; returns the
+// exclusive prefix.
+template <int W>
+__device__ __forceinline__ uint32_t publish_and_look_back(uint64_t* st, uint32_t tile,
+                                                          uint32_t stride, uint32_t col,
+                                                          uint32_t count, uint32_t* err) {
+  uint64_t* mine = st + (size_t)tile * stride + col;
+  if (tile == 0) {
+    st_publish(mine, kStPre | count);
+    return 0;
+  }
+  st_publish(mine, kStAgg | count);
+  const uint32_t excl = look_back<W>(st, tile, stride, col, err);
+  st_publish(mine, kStPre | (uint64_t)(uint32_t)(excl + count));
+  return excl;
+}
 
 // Exclusive scan of one value per thread over the 256-thread workgroup.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh4, uint32_t& total) {
@@ -67,31 +150,42 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh4, u
   return wp + x - v;
 }
 
-// 16 consecutive values a[i0 .. i0+15] (i0 a multiple of 16); entries at or
-// past n repeat a[n-1] (n >= 1).  Four 16-byte loads for a full group.
-__device__ __forceinline__ void load16(const uint32_t* __restrict__ a, uint64_t i0, uint64_t n,
-                                       uint32_t* v) {
-  if (i0 + kItems <= n) {
+// NI consecutive values a[i0 .. i0+NI-1] (i0 a multiple of NI, NI a multiple
+// of 4); entries at or past n repeat a[n-1] (n >= 1).  16-byte loads for a
+// full group.
+template <int NI>
+__device__ __forceinline__ void loadn(const uint32_t* __restrict__ a, uint64_t i0, uint64_t n,
+                                      uint32_t* v) {
+  if (i0 + NI <= n) {
     const uint4* p = reinterpret_cast<const uint4*>(a + i0);
 #pragma unroll
-    for (int q = 0; q < kItems / 4; ++q) {
+    for (int q = 0; q < NI / 4; ++q) {
       const uint4 x = p[q];
       v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < kItems; ++e) v[e] = a[(i0 + e < n) ? i0 + e : n - 1];
+    for (int e = 0; e < NI; ++e) v[e] = a[(i0 + e < n) ? i0 + e : n - 1];
   }
+}
+
+// The workgroup's tile number, in the order workgroups start.
+__device__ __forceinline__ uint32_t take_ticket(uint32_t* ticket, uint32_t* s_tile) {
+  if (threadIdx.x == 0) *s_tile = atomicAdd(ticket, 1u);
+  __syncthreads();
+  return *s_tile;
 }
 
 // ------------------------------------------------------------ transposition
 // 16 lanes per bag write its lookups' keys and bag id with contiguous stores.
 // With per-sample weights or mean pooling it also writes the contribution
 // scale of each lookup, S[p] * (1/L if mean) (FBTriton page, "Fusion
-// boundaries": weights scale each contribution before grouping).
+// boundaries": the weights scale each contribution before the grouping by
+// row).
 template <typename IT>
-__global__ __launch_bounds__(kThreads) void transpose_kernel(PrepDev a, uint32_t* key,
-                                                             uint32_t* bag, float* scale) {
+__global__ __launch_bounds__(kThreads) void transpose_kernel(PrepDev a, uint32_t* __restrict__ key,
+                                                             uint32_t* __restrict__ bag,
+                                                             float* __restrict__ scale) {
   const uint32_t lane16 = threadIdx.x & 15;
   const uint64_t j = ((uint64_t)blockIdx.x * kThreads + threadIdx.x) >> 4;
   if (j >= (uint64_t)a.T * (uint64_t)a.B) return;
@@ -113,75 +207,114 @@ __global__ __launch_bounds__(kThreads) void transpose_kernel(PrepDev a, uint32_t
 }
 
 // ------------------------------------------------------------- radix sort
-
+// Digit counts of every pass for every 4096-key tile of the transposed keys,
+// digit-major: cnt[(pass*256 + d) * ntiles + tile].  The digit totals of a
+// pass do not depend on the order of the keys, so one read of the keys gives
+// them for all passes.  This kernel also clears the look-back state of the
+// later kernels (tickets, error flag, status words).
 __global__ __launch_bounds__(kThreads) void radix_upsweep(const uint32_t* __restrict__ keys,
-                                                          uint32_t N, uint32_t shift,
-                                                          uint32_t* __restrict__ hist,
-                                                          uint32_t ntiles) {
-  __shared__ uint32_t h[kThreads / kWave][256];
+                                                          uint32_t N, uint32_t npass,
+                                                          uint32_t* __restrict__ cnt,
+                                                          uint32_t ntiles, uint32_t* __restrict__ ctl,
+                                                          uint64_t* __restrict__ st, uint64_t nst) {
+  __shared__ uint32_t h[kMaxPass][kThreads / kWave][256];
   const uint32_t wave = threadIdx.x / kWave;
   const uint64_t i0 = (uint64_t)blockIdx.x * kTile + (uint64_t)threadIdx.x * kItems;
   uint32_t k[kItems];
-  if (i0 < N) load16(keys, i0, N, k);
-  for (uint32_t i = threadIdx.x; i < 4 * 256; i += kThreads) (&h[0][0])[i] = 0u;
+  if (i0 < N) loadn<kItems>(keys, i0, N, k);
+  for (uint32_t i = threadIdx.x; i < (uint32_t)(kMaxPass * 4 * 256); i += kThreads)
+    (&h[0][0][0])[i] = 0u;
   __syncthreads();
 #pragma unroll
   for (int e = 0; e < kItems; ++e)
-    if (i0 + e < N) atomicAdd(&h[wave][(k[e] >> shift) & 255u], 1u);
+    if (i0 + e < N)
+      for (uint32_t q = 0; q < npass; ++q)
+        atomicAdd(&h[q][wave][(k[e] >> (q * kRadixBits)) & 255u], 1u);
   __syncthreads();
-  const uint32_t d = threadIdx.x;
-  hist[(size_t)d * ntiles + blockIdx.x] = h[0][d] + h[1][d] + h[2][d] + h[3][d];
-}
-
-// One workgroup per digit: exclusive scan of that digit's per-tile counts.
-__global__ __launch_bounds__(kThreads) void radix_scan(uint32_t* __restrict__ hist,
-                                                       uint32_t ntiles,
-                                                       uint32_t* __restrict__ rowtot) {
-  __shared__ uint32_t sh4[4];
-  uint32_t* row = hist + (size_t)blockIdx.x * ntiles;
-  uint32_t running = 0;
-  for (uint32_t c = 0; c < ntiles; c += kThreads * 4) {
-    uint32_t v[4], s = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t i = c + threadIdx.x * 4 + e;
-      v[e] = i < ntiles ? row[i] : 0u;
-      s += v[e];
-    }
-    uint32_t total;
-    uint32_t x = block_excl_scan(s, sh4, total) + running;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t i = c + threadIdx.x * 4 + e;
-      if (i < ntiles) row[i] = x;
-      x += v[e];
-    }
-    running += total;
+  for (uint32_t i = threadIdx.x; i < npass * 256u; i += kThreads) {
+    const uint32_t q = i >> 8, d = i & 255u;
+    cnt[(size_t)i * ntiles + blockIdx.x] = h[q][0][d] + h[q][1][d] + h[q][2][d] + h[q][3][d];
   }
-  if (threadIdx.x == 0) rowtot[blockIdx.x] = running;
+  if (blockIdx.x == 0)
+    for (uint32_t i = threadIdx.x; i < (uint32_t)kCtlHist; i += kThreads) ctl[i] = 0u;
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < nst; i += stride)
+    st[i] = 0ull;
 }
 
-// Stable scatter of one tile.  Wave w owns the contiguous 1024 keys
+// One workgroup per digit d: exclusive scan over the tiles of the pass-0
+// counts of d (in place), and the totals of d for every pass.
+__global__ __launch_bounds__(kThreads) void radix_scan(uint32_t* __restrict__ cnt, uint32_t ntiles,
+                                                       uint32_t npass,
+                                                       uint32_t* __restrict__ totals) {
+  __shared__ uint32_t sh4[4];
+  const uint32_t d = blockIdx.x;
+  for (uint32_t q = 0; q < npass; ++q) {
+    uint32_t* row = cnt + (size_t)(q * 256 + d) * ntiles;
+    uint32_t running = 0;
+    for (uint32_t c = 0; c < ntiles; c += kThreads * 4) {
+      uint32_t v[4], sum = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t i = c + threadIdx.x * 4 + e;
+        v[e] = i < ntiles ? row[i] : 0u;
+        sum += v[e];
+      }
+      uint32_t total;
+      uint32_t x = block_excl_scan(sum, sh4, total) + running;
+      if (q == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t i = c + threadIdx.x * 4 + e;
+          if (i < ntiles) row[i] = x;
+          x += v[e];
+        }
+      }
+      running += total;
+    }
+    if (threadIdx.x == 0) totals[q * 256 + d] = running;
+  }
+}
+
+
+struct SortPass {
+  const uint32_t* kin;
+  const uint32_t* vin;
+  const float* sin;
+  uint32_t* kout;
+  uint32_t* vout;
+  float* sout;
+  uint32_t N, shift;
+  const uint32_t* hist;       // 256 digit totals of this pass
+  const uint32_t* tile_excl;  // first pass: per digit and tile, the count in earlier tiles
+  uint32_t ntiles;
+  uint64_t* st;               // later passes: ntiles x 256 status words of this pass
+  uint64_t* st_next;          // the other status buffer: this tile's row is cleared for the pass after
+  uint32_t* ticket;
+  uint32_t* err;
+};
+
+// Stable scatter of one tile.  The first pass takes the offsets of its tile
+// among the earlier tiles from the scan (LB false); later passes find them by
+// look-back (LB true).  Wave w holds the contiguous 1024 keys
 // [tile + w*1024, tile + (w+1)*1024); in round r lane l holds key
 // tile + w*1024 + r*64 + l, so (wave, round, lane) is the position order and
-// ranking by wave-private digit counters keeps the sort stable.  The bag id
-// (and the contribution scale, when SC) travel with the key.
-template <bool SC>
-__global__ __launch_bounds__(kThreads) void radix_downsweep(
-    const uint32_t* __restrict__ kin, const uint32_t* __restrict__ vin,
-    const float* __restrict__ sin, uint32_t* __restrict__ kout, uint32_t* __restrict__ vout,
-    float* __restrict__ sout, uint32_t N, uint32_t shift, const uint32_t* __restrict__ hist,
-    const uint32_t* __restrict__ rowtot, uint32_t ntiles) {
-  __shared__ uint32_t s_key[kTile];
-  __shared__ uint32_t s_val[kTile];
-  __shared__ float s_sc[SC ? kTile : 1];
+// ranking by wave-private digit counters keeps the sort stable.  Keys, bag
+// ids and scales pass through one LDS buffer in turn on their way to their
+// coalesced global stores.
+template <bool SC, bool LB>
+__global__ __launch_bounds__(kThreads) void sort_pass_kernel(SortPass p) {
+  __shared__ uint32_t s_buf[kTile];
   __shared__ uint32_t wcnt[kThreads / kWave][256];
   __shared__ uint32_t gbase[256];
   __shared__ uint32_t lstart[256];
   __shared__ uint32_t sh4[4];
+  __shared__ uint32_t s_tile;
 
   const uint32_t lane = lane_id(), wave = threadIdx.x / kWave;
-  const uint32_t tile = blockIdx.x;
+  for (uint32_t i = threadIdx.x; i < 4 * 256; i += kThreads) (&wcnt[0][0])[i] = 0u;
+  const uint32_t tile = LB ? take_ticket(p.ticket, &s_tile) : blockIdx.x;
+  const uint64_t N = p.N;
   const uint64_t wbase = (uint64_t)tile * kTile + (uint64_t)wave * (kTile / 4);
   // the whole tile is loaded before any ranking
   uint32_t k[kItems], v[kItems], rk[kItems];
@@ -190,25 +323,20 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep(
   for (int r = 0; r < kItems; ++r) {
     const uint64_t i = wbase + (uint64_t)r * kWave + lane;
     const uint64_t ii = i < N ? i : N - 1;
-    k[r] = kin[ii];
-    v[r] = vin[ii];
-    if (SC) sc[r] = sin[ii];
+    k[r] = p.kin[ii];
+    v[r] = p.vin[ii];
+    if (SC) sc[r] = p.sin[ii];
   }
   __builtin_amdgcn_sched_barrier(0);
-  for (uint32_t i = threadIdx.x; i < 4 * 256; i += kThreads) (&wcnt[0][0])[i] = 0u;
-  {
-    uint32_t total;
-    const uint32_t d = threadIdx.x;
-    const uint32_t dp = block_excl_scan(rowtot[d], sh4, total);
-    gbase[d] = dp + hist[(size_t)d * ntiles + tile];
-  }
-  __syncthreads();
+  const uint32_t d_me = threadIdx.x;  // the digit this thread publishes and looks back for
+  uint32_t total;
+  const uint32_t digit_excl = block_excl_scan(p.hist[d_me], sh4, total);  // ends with a barrier
 
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int r = 0; r < kItems; ++r) {
     const bool valid = wbase + (uint64_t)r * kWave + lane < N;
-    const uint32_t d = (k[r] >> shift) & 255u;
+    const uint32_t d = (k[r] >> p.shift) & 255u;
     uint64_t peers = __ballot(valid);
 #pragma unroll
     for (int bit = 0; bit < kRadixBits; ++bit) {
@@ -222,130 +350,115 @@ __global__ __launch_bounds__(kThreads) void radix_downsweep(
     if (valid && before == 0) wcnt[wave][d] = prev + (uint32_t)__popcll(peers);
   }
   __syncthreads();
-  {
-    const uint32_t d = threadIdx.x;
-    uint32_t run = 0;
+  uint32_t cnt = 0;
 #pragma unroll
-    for (int w = 0; w < kThreads / kWave; ++w) {
-      const uint32_t c = wcnt[w][d];
-      wcnt[w][d] = run;
-      run += c;
-    }
-    uint32_t total;
-    lstart[d] = block_excl_scan(run, sh4, total);
+  for (int w = 0; w < kThreads / kWave; ++w) {
+    const uint32_t c = wcnt[w][d_me];
+    wcnt[w][d_me] = cnt;
+    cnt += c;
   }
+  uint64_t* mine = p.st + (size_t)tile * 256 + d_me;
+  if (LB) st_publish(mine, (tile == 0 ? kStPre : kStAgg) | cnt);
+  const uint32_t ls = block_excl_scan(cnt, sh4, total);
+  lstart[d_me] = ls;
   __syncthreads();
+  // tile-local slots, keys into LDS while the look-back runs
 #pragma unroll
   for (int r = 0; r < kItems; ++r) {
-    const uint64_t i = wbase + (uint64_t)r * kWave + lane;
-    if (i < N) {
-      const uint32_t d = (k[r] >> shift) & 255u;
-      const uint32_t slot = lstart[d] + wcnt[wave][d] + rk[r];
-      if (slot < (uint32_t)kTile) {  // always true for a consistent ranking
-        s_key[slot] = k[r];
-        s_val[slot] = v[r];
-        if (SC) s_sc[slot] = sc[r];
+    const bool valid = wbase + (uint64_t)r * kWave + lane < N;
+    const uint32_t d = (k[r] >> p.shift) & 255u;
+    const uint32_t slot = lstart[d] + wcnt[wave][d] + rk[r];
+    rk[r] = (valid && slot < (uint32_t)kTile) ? slot : 0xffffffffu;  // always in range when valid
+    if (rk[r] != 0xffffffffu) s_buf[rk[r]] = k[r];
+  }
+  uint32_t excl = 0;
+  if (!LB) {
+    excl = p.tile_excl[(size_t)d_me * p.ntiles + tile];
+  } else if (tile > 0) {
+    excl = look_back<8>(p.st, tile, 256, d_me, p.err);
+    st_publish(mine, kStPre | (uint64_t)(uint32_t)(excl + cnt));
+  }
+  gbase[d_me] = digit_excl + excl - ls;  // destination = gbase[digit] + tile slot
+  __syncthreads();
+
+  const uint64_t tbase = (uint64_t)tile * kTile;
+  const uint32_t n = (uint32_t)((N - tbase) < (uint64_t)kTile ? (N - tbase) : (uint64_t)kTile);
+  uint32_t dst[kItems];
+#pragma unroll
+  for (int r = 0; r < kItems; ++r) {
+    const uint32_t s = threadIdx.x + (uint32_t)r * kThreads;
+    dst[r] = 0xffffffffu;
+    if (s < n) {
+      const uint32_t key = s_buf[s];
+      const uint32_t g = gbase[(key >> p.shift) & 255u] + s;
+      if (g < p.N) {  // always true for consistent digit counts
+        dst[r] = g;
+        p.kout[g] = key;
       }
     }
   }
   __syncthreads();
-  const uint64_t tbase = (uint64_t)tile * kTile;
-  const uint32_t n = (uint32_t)((N - tbase) < (uint64_t)kTile ? (N - tbase) : (uint64_t)kTile);
-  for (uint32_t s = threadIdx.x; s < n; s += kThreads) {
-    const uint32_t key = s_key[s];
-    const uint32_t d = (key >> shift) & 255u;
-    const uint32_t dst = gbase[d] + (s - lstart[d]);
-    if (dst < N) {  // always true for consistent digit counts
-      kout[dst] = key;
-      vout[dst] = s_val[s];
-      if (SC) sout[dst] = s_sc[s];
-    }
+#pragma unroll
+  for (int r = 0; r < kItems; ++r)
+    if (rk[r] != 0xffffffffu) s_buf[rk[r]] = v[r];
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kItems; ++r)
+    if (dst[r] != 0xffffffffu) p.vout[dst[r]] = s_buf[threadIdx.x + (uint32_t)r * kThreads];
+  if (SC) {
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kItems; ++r)
+      if (rk[r] != 0xffffffffu) s_buf[rk[r]] = __builtin_bit_cast(uint32_t, sc[r]);
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kItems; ++r)
+      if (dst[r] != 0xffffffffu)
+        p.sout[dst[r]] = __builtin_bit_cast(float, s_buf[threadIdx.x + (uint32_t)r * kThreads]);
   }
+  // the pass after next uses the other status buffer; nobody reads this row of it now
+  if (LB) p.st_next[(size_t)tile * 256 + d_me] = 0ull;
 }
 
 // --------------------------------------------------- run-length encoding
 // Blocked layout: thread h of a tile owns sorted slots [tile + 16h, tile + 16h + 16).
 
-__device__ __forceinline__ uint32_t head_mask(const uint32_t* __restrict__ key, uint64_t i0,
-                                              uint32_t N) {
-  if (i0 >= N) return 0u;
+__global__ __launch_bounds__(kThreads) void rle_kernel(const uint32_t* __restrict__ key, uint32_t N,
+                                                       uint32_t ntiles, uint32_t* ticket,
+                                                       uint64_t* st, uint32_t* err,
+                                                       uint32_t* __restrict__ counters,
+                                                       uint32_t* __restrict__ run_start,
+                                                       uint32_t* __restrict__ run_key) {
+  __shared__ uint32_t sh4[4];
+  __shared__ uint32_t s_tile, s_excl;
+  const uint32_t tile = take_ticket(ticket, &s_tile);
+  const uint64_t i0 = (uint64_t)tile * kTile + (uint64_t)threadIdx.x * kItems;
   uint32_t k[kItems];
-  const uint32_t prev0 = i0 == 0 ? 0u : key[i0 - 1];
-  load16(key, i0, N, k);
-  __builtin_amdgcn_sched_barrier(0);
   uint32_t m = 0;
-  uint32_t prev = prev0;
+  if (i0 < N) {
+    const uint32_t prev0 = i0 == 0 ? 0u : key[i0 - 1];
+    loadn<kItems>(key, i0, N, k);
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t prev = prev0;
 #pragma unroll
-  for (int e = 0; e < kItems; ++e) {
-    const uint64_t i = i0 + e;
-    if (i < N && (i == 0 || k[e] != prev)) m |= 1u << e;
-    prev = k[e];
-  }
-  return m;
-}
-
-__global__ __launch_bounds__(kThreads) void rle_count(const uint32_t* __restrict__ key, uint32_t N,
-                                                      uint32_t* __restrict__ tile_cnt) {
-  __shared__ uint32_t sh4[4];
-  const uint64_t i0 = (uint64_t)blockIdx.x * kTile + (uint64_t)threadIdx.x * kItems;
-  const uint32_t c = __popc(head_mask(key, i0, N));
-  uint32_t total;
-  block_excl_scan(c, sh4, total);
-  if (threadIdx.x == 0) tile_cnt[blockIdx.x] = total;
-}
-
-// Single workgroup: exclusive scan of `rows` rows of `n` counters each (in
-// place); row totals to `totals`.
-__device__ void scan_rows_single_block(uint32_t* data, uint32_t n, int rows, uint32_t* totals) {
-  __shared__ uint32_t sh4[4];
-  for (int rr = 0; rr < rows; ++rr) {
-    uint32_t* row = data + (size_t)rr * n;
-    uint32_t running = 0;
-    for (uint32_t c = 0; c < n; c += kThreads * 4) {
-      uint32_t v[4], s = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t i = c + threadIdx.x * 4 + e;
-        v[e] = i < n ? row[i] : 0u;
-        s += v[e];
-      }
-      uint32_t total;
-      uint32_t x = block_excl_scan(s, sh4, total) + running;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t i = c + threadIdx.x * 4 + e;
-        if (i < n) row[i] = x;
-        x += v[e];
-      }
-      running += total;
+    for (int e = 0; e < kItems; ++e) {
+      const uint64_t i = i0 + e;
+      if (i < N && (i == 0 || k[e] != prev)) m |= 1u << e;
+      prev = k[e];
     }
-    totals[rr] = running;
   }
-}
-
-__global__ __launch_bounds__(kThreads) void rle_scan(uint32_t* tile_cnt, uint32_t ntiles,
-                                                     uint32_t N, uint32_t* counters,
-                                                     uint32_t* run_start) {
-  uint32_t U;
-  scan_rows_single_block(tile_cnt, ntiles, 1, &U);
-  if (threadIdx.x == 0) {
-    counters[kCntU] = U;
-    run_start[U] = N;
-  }
-}
-
-__global__ __launch_bounds__(kThreads) void rle_write(const uint32_t* __restrict__ key, uint32_t N,
-                                                      const uint32_t* __restrict__ tile_base,
-                                                      uint32_t* __restrict__ run_start,
-                                                      uint32_t* __restrict__ run_key) {
-  __shared__ uint32_t sh4[4];
-  const uint64_t i0 = (uint64_t)blockIdx.x * kTile + (uint64_t)threadIdx.x * kItems;
-  const uint32_t m = head_mask(key, i0, N);
   uint32_t total;
-  uint32_t u = tile_base[blockIdx.x] + block_excl_scan(__popc(m), sh4, total);
-  if (m == 0u) return;
-  uint32_t k[kItems];
-  load16(key, i0, N, k);
+  const uint32_t local = block_excl_scan(__popc(m), sh4, total);
+  if (threadIdx.x == 0) {
+    const uint32_t excl = publish_and_look_back<16>(st, tile, 1, 0, total, err);
+    s_excl = excl;
+    if (tile == ntiles - 1) {
+      counters[kCntU] = excl + total;
+      run_start[excl + total] = N;
+    }
+  }
+  __syncthreads();
+  uint32_t u = s_excl + local;
 #pragma unroll
   for (int e = 0; e < kItems; ++e) {
     if (m & (1u << e)) {
@@ -357,18 +470,19 @@ __global__ __launch_bounds__(kThreads) void rle_write(const uint32_t* __restrict
 }
 
 // ----------------------------------------------------------- classification
-// Runs are listed by length: SL < kTinyRun and kTinyRun <= SL < 256 are both
-// short runs (one program owns the row and updates it with plain stores); the
-// split only picks the program size (a lane subgroup or a whole workgroup).
-// SL >= 256 are long runs, cut into chunks of 256.
+// Runs are listed by length: SL = 1, 2 <= SL < kTinyRun and kTinyRun <= SL <
+// 256 are short runs (one program owns the row and updates it with plain
+// stores); the split only picks the program shape.  SL >= 256 are long runs,
+// cut into chunks of 256.
 
 struct ClsDev {
   const uint32_t* run_start;
   const uint32_t* run_key;
   const uint32_t* sorted_bag;
   uint32_t* counters;
-  uint32_t* tile_cls;        // kNumLists rows x ntiles
-  uint32_t ntiles;
+  uint32_t* ticket;
+  uint64_t* st;              // ncls_tiles x kClsStride status words
+  uint32_t* err;
   uint4* single_task;
   uint4* tiny_task;
   uint4* med_task;
@@ -394,41 +508,18 @@ __device__ __forceinline__ void run_class(uint32_t len, uint32_t* c) {
   c[4] = lg ? (len + kChunk - 1) / kChunk : 0u;
 }
 
-// run lengths of runs u0 .. u0+15 (0 past U): run_start has U+1 entries
+// lengths of runs u0 .. u0+kClsItems-1 (0 past U): run_start has U+1 entries
 __device__ __forceinline__ void run_lengths(const uint32_t* __restrict__ run_start, uint64_t u0,
                                             uint32_t U, uint32_t* start, uint32_t* len) {
-  uint32_t s[kItems];
-  load16(run_start, u0, (uint64_t)U + 1, s);
-  const uint32_t last = run_start[(u0 + kItems <= U) ? u0 + kItems : U];
+  uint32_t s[kClsItems];
+  loadn<kClsItems>(run_start, u0, (uint64_t)U + 1, s);
+  const uint32_t last = run_start[(u0 + kClsItems <= U) ? u0 + kClsItems : U];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int e = 0; e < kItems; ++e) {
-    const uint32_t nxt = e + 1 < kItems ? s[e + 1] : last;
+  for (int e = 0; e < kClsItems; ++e) {
+    const uint32_t nxt = e + 1 < kClsItems ? s[e + 1] : last;
     start[e] = s[e];
     len[e] = (u0 + e < U) ? nxt - s[e] : 0u;
-  }
-}
-
-__global__ __launch_bounds__(kThreads) void cls_count(ClsDev a) {
-  __shared__ uint32_t sh4[4];
-  const uint32_t U = a.counters[kCntU];
-  const uint64_t u0 = (uint64_t)blockIdx.x * kTile + (uint64_t)threadIdx.x * kItems;
-  uint32_t acc[kNumLists] = {0u, 0u, 0u, 0u, 0u};
-  if (u0 < U) {
-    uint32_t start[kItems], len[kItems];
-    run_lengths(a.run_start, u0, U, start, len);
-#pragma unroll
-    for (int e = 0; e < kItems; ++e) {
-      uint32_t c[kNumLists];
-      run_class(len[e], c);
-      const uint32_t in = (u0 + e < U) ? 1u : 0u;
-      for (int q = 0; q < kNumLists; ++q) acc[q] += in * c[q];
-    }
-  }
-  for (int q = 0; q < kNumLists; ++q) {
-    uint32_t tot;
-    block_excl_scan(acc[q], sh4, tot);
-    if (threadIdx.x == 0) a.tile_cls[q * a.ntiles + blockIdx.x] = tot;
   }
 }
 
@@ -438,43 +529,29 @@ __device__ __forceinline__ uint32_t bucket_of_key(const uint32_t* bkb, uint32_t 
   return b;
 }
 
-__global__ __launch_bounds__(kThreads) void cls_scan(ClsDev a) {
-  __shared__ uint32_t tot[kNumLists];
-  uint32_t t4[kNumLists];
-  scan_rows_single_block(a.tile_cls, a.ntiles, kNumLists, t4);
-  if (threadIdx.x == 0) {
-    for (int k = 0; k < kNumLists; ++k) {
-      tot[k] = t4[k];
-      a.counters[kCntSingle + k] = t4[k];
-    }
-  }
-  __syncthreads();
-  // begins of the buckets after the last run's bucket (all of them when U == 0)
-  const uint32_t U = a.counters[kCntU];
-  const int first = U == 0 ? 0 : (int)bucket_of_key(a.bkb, a.nb, a.run_key[U - 1]) + 1;
-  for (int b = first + (int)threadIdx.x; b <= (int)a.nb; b += kThreads) {
-    for (int k = 0; k < kNumLists; ++k) a.counters[kCntBegins + k * (a.nb + 1) + b] = tot[k];
-  }
-}
-
-__global__ __launch_bounds__(kThreads) void cls_write(ClsDev a) {
+__global__ __launch_bounds__(kThreads) void classify_kernel(ClsDev a) {
   __shared__ uint32_t s_kb[kMaxTables];
   __shared__ uint32_t s_ord[kMaxTables];
-  __shared__ uint32_t s_bkb[64];
+  __shared__ uint32_t s_bkb[kMaxBuckets + 1];
   __shared__ uint32_t sh4[4];
+  __shared__ uint32_t s_tile;
+  __shared__ uint32_t s_tot[kNumLists], s_excl[kNumLists];
   const uint32_t U = a.counters[kCntU];
-  const uint64_t tile0 = (uint64_t)blockIdx.x * kTile;
-  if (tile0 >= U) return;  // uniform per workgroup: no barrier is skipped by part of it
-  const uint64_t u0 = tile0 + (uint64_t)threadIdx.x * kItems;
-  uint32_t start[kItems], len[kItems], key[kItems], bag0[kItems];
+  // workgroups past the last run leave before taking a ticket, so the tickets
+  // go to exactly the tiles that hold runs
+  if ((uint64_t)blockIdx.x * kClsTile >= U) return;
+  const uint32_t tile = take_ticket(a.ticket, &s_tile);
+  const uint64_t tile0 = (uint64_t)tile * kClsTile;
+  const uint64_t u0 = tile0 + (uint64_t)threadIdx.x * kClsItems;
+  uint32_t start[kClsItems], len[kClsItems], key[kClsItems], bag0[kClsItems];
   uint32_t keyprev = 0;
   const bool mine = u0 < U;
   if (mine) {
     run_lengths(a.run_start, u0, U, start, len);
-    load16(a.run_key, u0, U, key);
+    loadn<kClsItems>(a.run_key, u0, U, key);
     keyprev = u0 == 0 ? 0u : a.run_key[u0 - 1];
 #pragma unroll
-    for (int e = 0; e < kItems; ++e) bag0[e] = a.sorted_bag[start[e] < a.N ? start[e] : a.N - 1];
+    for (int e = 0; e < kClsItems; ++e) bag0[e] = a.sorted_bag[start[e] < a.N ? start[e] : a.N - 1];
   }
   for (uint32_t i = threadIdx.x; i < a.T; i += kThreads) {
     const uint32_t t = a.order[i];
@@ -486,7 +563,7 @@ __global__ __launch_bounds__(kThreads) void cls_write(ClsDev a) {
   uint32_t acc[kNumLists] = {0u, 0u, 0u, 0u, 0u};
   if (mine) {
 #pragma unroll
-    for (int e = 0; e < kItems; ++e) {
+    for (int e = 0; e < kClsItems; ++e) {
       uint32_t c[kNumLists];
       run_class(len[e], c);
       const uint32_t in = (u0 + e < U) ? 1u : 0u;
@@ -496,13 +573,30 @@ __global__ __launch_bounds__(kThreads) void cls_write(ClsDev a) {
   uint32_t pos[kNumLists];
   for (int q = 0; q < kNumLists; ++q) {
     uint32_t tot;
-    pos[q] = a.tile_cls[q * a.ntiles + blockIdx.x] + block_excl_scan(acc[q], sh4, tot);
+    pos[q] = block_excl_scan(acc[q], sh4, tot);
+    if (threadIdx.x == 0) s_tot[q] = tot;
   }
-  // block_excl_scan ends with a barrier, so the LDS tables above are visible
+  __syncthreads();
+  if (threadIdx.x < (uint32_t)kNumLists) {
+    const uint32_t q = threadIdx.x;
+    s_excl[q] = publish_and_look_back<16>(a.st, tile, kClsStride, q, s_tot[q], a.err);
+  }
+  __syncthreads();
+  const bool last_tile = tile0 + kClsTile >= U;
+  if (last_tile) {
+    // list totals, and the begins of every bucket after the last run's bucket
+    if (threadIdx.x < (uint32_t)kNumLists)
+      a.counters[kCntSingle + threadIdx.x] = s_excl[threadIdx.x] + s_tot[threadIdx.x];
+    const int first = (int)bucket_of_key(s_bkb, a.nb, a.run_key[U - 1]) + 1;
+    for (int b = first + (int)threadIdx.x; b <= (int)a.nb; b += kThreads)
+      for (int q = 0; q < kNumLists; ++q)
+        a.counters[kCntBegins + q * (a.nb + 1) + b] = s_excl[q] + s_tot[q];
+  }
   if (!mine) return;
+  for (int q = 0; q < kNumLists; ++q) pos[q] += s_excl[q];
 
   int bprev = u0 == 0 ? -1 : (int)bucket_of_key(s_bkb, a.nb, keyprev);
-  for (int e = 0; e < kItems; ++e) {
+  for (int e = 0; e < kClsItems; ++e) {
     if (u0 + e >= U) break;
     const uint32_t k = key[e], ln = len[e], st = start[e];
     // table of the key: last table whose key_base <= key
@@ -549,66 +643,74 @@ __global__ __launch_bounds__(kThreads) void cls_write(ClsDev a) {
 
 }  // namespace
 
-hipError_t launch_preprocess(const PrepArgs& p, int /*grid_persist*/, hipStream_t s) {
+hipError_t launch_preprocess(const PrepArgs& p, int /*num_cus*/, hipStream_t s) {
   const WsLayout& L = *p.L;
   if (p.N == 0) return hipSuccess;
   uint8_t* ws = p.ws;
   auto u32p = [&](size_t off) { return reinterpret_cast<uint32_t*>(ws + off); };
   auto f32p = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
-  PrepDev d{p.tables, p.T, p.nb, p.B, p.itype, p.indices, p.offsets, p.psw, p.N, L.ntiles};
+  auto u64p = [&](size_t off) { return reinterpret_cast<uint64_t*>(ws + off); };
+  uint32_t* ctl = u32p(L.ctl);
+  uint32_t* err = ctl + kCtlErr;
   const bool sc = p.need_scale != 0;
 
+  PrepDev d{p.tables, p.T, p.nb, p.B, p.indices, p.offsets, p.psw, p.N};
   const uint64_t nbag = (uint64_t)p.T * (uint64_t)p.B;
-  const uint64_t tgrid = (nbag * 16 + kThreads - 1) / kThreads;
+  const uint32_t tgrid = (uint32_t)((nbag * 16 + kThreads - 1) / kThreads);
   if (p.itype == IT_I32)
-    TBE_LAUNCH("transpose", transpose_kernel<int32_t>, dim3((uint32_t)tgrid), dim3(kThreads), s,
-               d, u32p(L.key_a), u32p(L.val_a), sc ? f32p(L.sc_a) : nullptr);
+    TBE_LAUNCH("transpose", transpose_kernel<int32_t>, dim3(tgrid), dim3(kThreads), s, d,
+               u32p(L.key_a), u32p(L.val_a), sc ? f32p(L.sc_a) : nullptr);
   else
-    TBE_LAUNCH("transpose", transpose_kernel<int64_t>, dim3((uint32_t)tgrid), dim3(kThreads), s,
-               d, u32p(L.key_a), u32p(L.val_a), sc ? f32p(L.sc_a) : nullptr);
+    TBE_LAUNCH("transpose", transpose_kernel<int64_t>, dim3(tgrid), dim3(kThreads), s, d,
+               u32p(L.key_a), u32p(L.val_a), sc ? f32p(L.sc_a) : nullptr);
+
+  const uint64_t nst = (L.st_end - L.st_sort0) / 8;
+  TBE_LAUNCH("radix_upsweep", radix_upsweep, dim3(L.ntiles), dim3(kThreads), s, u32p(L.key_a),
+             p.N, (uint32_t)L.npass, u32p(L.tile_cnt), L.ntiles, ctl, u64p(L.st_sort0), nst);
+  TBE_LAUNCH("radix_scan", radix_scan, dim3(256), dim3(kThreads), s, u32p(L.tile_cnt), L.ntiles,
+             (uint32_t)L.npass, ctl + kCtlHist);
 
   // ping-pong a -> b -> a ...; the final buffers are b for an odd pass count
   for (int pass = 0; pass < L.npass; ++pass) {
     const bool ab = (pass % 2) == 0;
-    const uint32_t* kin = u32p(ab ? L.key_a : L.key_b);
-    const uint32_t* vin = u32p(ab ? L.val_a : L.val_b);
-    const float* sin = f32p(ab ? L.sc_a : L.sc_b);
-    uint32_t* kout = u32p(ab ? L.key_b : L.key_a);
-    uint32_t* vout = u32p(ab ? L.val_b : L.val_a);
-    float* sout = f32p(ab ? L.sc_b : L.sc_a);
-    const uint32_t shift = (uint32_t)(pass * kRadixBits);
-    TBE_LAUNCH("radix_upsweep", radix_upsweep, dim3(L.ntiles), dim3(kThreads), s, kin, p.N,
-               shift, u32p(L.hist), L.ntiles);
-    TBE_LAUNCH("radix_scan", radix_scan, dim3(256), dim3(kThreads), s, u32p(L.hist), L.ntiles,
-               u32p(L.rowtot));
-    if (sc)
-      TBE_LAUNCH("radix_downsweep", radix_downsweep<true>, dim3(L.ntiles), dim3(kThreads), s,
-                 kin, vin, sin, kout, vout, sout, p.N, shift, u32p(L.hist), u32p(L.rowtot),
-                 L.ntiles);
-    else
-      TBE_LAUNCH("radix_downsweep", radix_downsweep<false>, dim3(L.ntiles), dim3(kThreads), s,
-                 kin, vin, sin, kout, vout, sout, p.N, shift, u32p(L.hist), u32p(L.rowtot),
-                 L.ntiles);
+    const bool odd = (pass % 2) == 1;  // later passes alternate between two status buffers
+    SortPass sp{u32p(ab ? L.key_a : L.key_b), u32p(ab ? L.val_a : L.val_b),
+                f32p(ab ? L.sc_a : L.sc_b),   u32p(ab ? L.key_b : L.key_a),
+                u32p(ab ? L.val_b : L.val_a), f32p(ab ? L.sc_b : L.sc_a),
+                p.N, (uint32_t)(pass * kRadixBits), ctl + kCtlHist + pass * 256,
+                u32p(L.tile_cnt), L.ntiles,
+                u64p(odd ? L.st_sort0 : L.st_sort1), u64p(odd ? L.st_sort1 : L.st_sort0),
+                ctl + kCtlTicket + pass, err};
+    if (pass == 0) {
+      if (sc)
+        TBE_LAUNCH("radix_downsweep", (sort_pass_kernel<true, false>), dim3(L.ntiles),
+                   dim3(kThreads), s, sp);
+      else
+        TBE_LAUNCH("radix_downsweep", (sort_pass_kernel<false, false>), dim3(L.ntiles),
+                   dim3(kThreads), s, sp);
+    } else {
+      if (sc)
+        TBE_LAUNCH("sort_pass", (sort_pass_kernel<true, true>), dim3(L.ntiles), dim3(kThreads),
+                   s, sp);
+      else
+        TBE_LAUNCH("sort_pass", (sort_pass_kernel<false, true>), dim3(L.ntiles), dim3(kThreads),
+                   s, sp);
+    }
   }
   const uint32_t* skey = u32p(L.final_in_b ? L.key_b : L.key_a);
   const uint32_t* sbag = u32p(L.final_in_b ? L.val_b : L.val_a);
-  TBE_LAUNCH("rle_count", rle_count, dim3(L.ntiles), dim3(kThreads), s, skey, p.N,
-             u32p(L.tile_cnt));
-  TBE_LAUNCH("rle_scan", rle_scan, dim3(1), dim3(kThreads), s, u32p(L.tile_cnt), L.ntiles, p.N,
-             u32p(L.counters), u32p(L.run_start));
-  TBE_LAUNCH("rle_write", rle_write, dim3(L.ntiles), dim3(kThreads), s, skey, p.N,
-             u32p(L.tile_cnt), u32p(L.run_start), u32p(L.run_key));
+  TBE_LAUNCH("rle", rle_kernel, dim3(L.ntiles), dim3(kThreads), s, skey, p.N, L.ntiles,
+             ctl + kCtlTicket + kMaxPass, u64p(L.st_rle), err, u32p(L.counters),
+             u32p(L.run_start), u32p(L.run_key));
 
   ClsDev c{u32p(L.run_start), u32p(L.run_key), sbag, u32p(L.counters),
-           u32p(L.tile_cls), L.ntiles,
+           ctl + kCtlTicket + kMaxPass + 1, u64p(L.st_cls), err,
            reinterpret_cast<uint4*>(ws + L.single_task), reinterpret_cast<uint4*>(ws + L.tiny_task),
            reinterpret_cast<uint4*>(ws + L.med_task),
            reinterpret_cast<uint4*>(ws + L.long_task), u32p(L.long_cbeg), u32p(L.remaining),
            reinterpret_cast<uint4*>(ws + L.chunk_task), p.tables, p.order, p.bucket_key_begin,
            p.T, p.nb, p.N, L.max_tiny, L.max_med, L.max_long, L.max_chunks};
-  TBE_LAUNCH("cls_count", cls_count, dim3(L.ntiles), dim3(kThreads), s, c);
-  TBE_LAUNCH("cls_scan", cls_scan, dim3(1), dim3(kThreads), s, c);
-  TBE_LAUNCH("cls_write", cls_write, dim3(L.ntiles), dim3(kThreads), s, c);
+  TBE_LAUNCH("classify", classify_kernel, dim3(L.ncls_tiles), dim3(kThreads), s, c);
   return hipGetLastError();
 }
 

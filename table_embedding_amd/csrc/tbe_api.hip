@@ -70,6 +70,7 @@ WsLayout layout(const tbe_plan* P, int64_t N) {
   WsLayout L{};
   const uint64_t n = (uint64_t)N;
   L.ntiles = (uint32_t)((n + kTile - 1) / kTile);
+  L.ncls_tiles = (uint32_t)((n + kClsTile - 1) / kClsTile);
   L.max_tiny = (uint32_t)(n / 2 + 1);
   L.max_med = (uint32_t)(n / kTinyRun + 1);
   L.max_long = (uint32_t)(n / kLongRun + 1);
@@ -89,10 +90,14 @@ WsLayout layout(const tbe_plan* P, int64_t N) {
   L.val_b = take(n * 4);
   L.sc_a = take(n * 4);
   L.sc_b = take(n * 4);
-  L.hist = take((size_t)256 * L.ntiles * 4);
-  L.rowtot = take(256 * 4);
-  L.tile_cnt = take((size_t)L.ntiles * 4);
-  L.tile_cls = take((size_t)kNumLists * L.ntiles * 4);
+  L.ctl = take((size_t)kCtlWords * 4);
+  L.tile_cnt = take((size_t)L.npass * 256 * L.ntiles * 4);
+  L.st_sort0 = off;
+  L.st_sort1 = L.st_sort0 + (size_t)L.ntiles * 256 * 8;
+  L.st_rle = L.st_sort1 + (size_t)L.ntiles * 256 * 8;
+  L.st_cls = L.st_rle + (size_t)L.ntiles * 8;
+  L.st_end = L.st_cls + (size_t)L.ncls_tiles * kClsStride * 8;
+  take(L.st_end - L.st_sort0);
   L.run_start = take((n + 1) * 4);
   L.run_key = take(n * 4);
   L.single_task = take(n * 16);
@@ -458,6 +463,7 @@ int tbe_workspace_views(const tbe_plan* P, int64_t B, int64_t N, tbe_ws_views* v
   v->long_cbeg = L.long_cbeg;
   v->chunk_task = L.chunk_task;
   v->counters = L.counters;
+  v->prep_error = L.ctl + (size_t)kCtlErr * 4;
   v->total = L.total;
   v->num_buckets = (int32_t)P->buckets.size();
   return TBE_OK;
@@ -511,7 +517,7 @@ int tbe_preprocess(const tbe_plan* P, int64_t B, int32_t itype, const void* indi
   const WsLayout L = layout(P, N);
   PrepArgs a = prep_args(P, B, itype, indices, offsets, N, psw, ws, &L);
   const hipError_t e =
-      launch_preprocess(a, P->num_cus * 8, reinterpret_cast<hipStream_t>(stream));
+      launch_preprocess(a, P->num_cus, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? TBE_OK : TBE_E_HIP;
 }
 
@@ -534,7 +540,7 @@ int tbe_backward_rowwise_adagrad(const tbe_plan* P, int64_t B, int32_t itype,
   uint8_t* w = reinterpret_cast<uint8_t*>(ws);
   if (!(flags & TBE_BWD_PREPROCESSED)) {
     PrepArgs pa = prep_args(P, B, itype, indices, offsets, N, psw, ws, &L);
-    if (launch_preprocess(pa, P->num_cus * 8, s) != hipSuccess) return TBE_E_HIP;
+    if (launch_preprocess(pa, P->num_cus, s) != hipSuccess) return TBE_E_HIP;
   }
   BwdArgs a{};
   a.tables = P->d_tables;

@@ -11,11 +11,13 @@ namespace tbe {
 
 constexpr int kThreads = 256;       // every kernel runs 256-thread workgroups (4 waves)
 constexpr int kWave = 64;
-constexpr int kTile = 4096;         // keys per workgroup in the sort / scan passes
+constexpr int kTile = 4096;         // keys per workgroup in the sort / run-length passes
+constexpr int kClsTile = 2048;      // runs per workgroup in the classification pass
 constexpr int kLongRun = 256;       // SL >= 256 takes the chunked long-run path
 constexpr int kTinyRun = 32;        // short runs below this are owned by a lane subgroup
 constexpr int kChunk = 256;         // lookups per long-run chunk
 constexpr int kRadixBits = 8;
+constexpr int kMaxPass = 4;         // 32-bit keys: at most four 8-bit digits
 constexpr int kMaxTables = 4096;
 
 enum : int { WD_F32 = 0, WD_F16 = 1, WD_BF16 = 2 };
@@ -55,25 +57,26 @@ struct BucketSet {
 };
 
 // This workgroup's bucket, its index inside the bucket's range and the range
-// size.  Selection with constant indices only (scalar selects, no indexing of
-// the argument block).
+// size.  The ranges are ascending, so a chain of selects that takes every
+// range starting at or before this workgroup ends on its own; no element is
+// picked by a computed index (which would send the argument block through
+// scratch memory).
 __device__ __forceinline__ void set_pick(const BucketSet& S, BucketDev& bk, uint32_t& id,
                                          uint32_t& lb, uint32_t& lg) {
-  uint32_t k = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxBuckets; ++i)
-    if (i < (int)S.n && blockIdx.x >= S.gbeg[i]) k = (uint32_t)i;
   bk = S.bk[0];
   id = S.id[0];
   uint32_t g0 = S.gbeg[0], g1 = S.gbeg[1];
 #pragma unroll
-  for (int i = 1; i < kMaxBuckets; ++i)
-    if ((uint32_t)i == k) {
-      bk = S.bk[i];
-      id = S.id[i];
-      g0 = S.gbeg[i];
-      g1 = S.gbeg[i + 1];
-    }
+  for (int i = 1; i < kMaxBuckets; ++i) {
+    const bool take = i < (int)S.n && blockIdx.x >= S.gbeg[i];
+    bk.tables = take ? S.bk[i].tables : bk.tables;
+    bk.ntables = take ? S.bk[i].ntables : bk.ntables;
+    bk.lpr = take ? S.bk[i].lpr : bk.lpr;
+    bk.lpr_log2 = take ? S.bk[i].lpr_log2 : bk.lpr_log2;
+    id = take ? S.id[i] : id;
+    g0 = take ? S.gbeg[i] : g0;
+    g1 = take ? S.gbeg[i + 1] : g1;
+  }
   lb = blockIdx.x - g0;
   lg = g1 - g0;
 }
@@ -81,12 +84,18 @@ __device__ __forceinline__ void set_pick(const BucketSet& S, BucketDev& bk, uint
 // Workspace layout: byte offsets from the workspace base (all 256-B aligned).
 struct WsLayout {
   size_t key_a, key_b, val_a, val_b, sc_a, sc_b;  // sort ping-pong: key, bag id, scale
-  size_t hist, rowtot, tile_cnt, tile_cls;
+  size_t ctl;                                      // control block, kCtlWords uint32
+  size_t tile_cnt;  // npass x 256 x ntiles per-tile digit counts (pass 0: exclusive prefixes)
+  // look-back status words (uint64), contiguous in [st_sort0, st_end): two
+  // sort-pass buffers (ntiles x 256 each), the run-length pass (ntiles) and
+  // the classification pass (ncls_tiles x kClsStride)
+  size_t st_sort0, st_sort1, st_rle, st_cls, st_end;
   size_t run_start, run_key;
   size_t single_task, tiny_task, med_task, long_task, long_cbeg, remaining, chunk_task;
   size_t partial, counters;
   size_t total;
   uint32_t ntiles;          // ceil(N / kTile)
+  uint32_t ncls_tiles;      // ceil(N / kClsTile): runs are at most N
   uint32_t max_tiny;        // capacity of the 2 <= SL < 32 list
   uint32_t max_med;         // capacity of the medium short-run list
   uint32_t max_long;        // capacity of the long-run lists
@@ -101,6 +110,13 @@ struct WsLayout {
 // lists: short runs with SL = 1, 2 <= SL < 32, 32 <= SL < 256; long runs; chunks
 constexpr int kNumLists = 5;
 constexpr int kCntU = 0, kCntSingle = 1, kCntBegins = 1 + kNumLists;
+
+// Control block of the preprocessing: tile tickets (sort passes, then the
+// run-length and classification passes), the look-back error flag and the
+// digit totals of every sort pass.
+constexpr int kCtlTicket = 0, kCtlErr = 8, kCtlHist = 16;
+constexpr int kCtlWords = kCtlHist + kMaxPass * 256;
+constexpr int kClsStride = 8;  // status words per classification tile (five used)
 
 // ------------------------------------------------------------- device helpers
 
@@ -282,7 +298,7 @@ hipError_t launch_forward_set(const FwdArgs& a, const BucketSet& S, int wd, int 
                               hipStream_t s);
 hipError_t launch_forward_hist(const FwdArgs& a, uint32_t E, uint32_t D, int mean, int grid,
                                hipStream_t s);
-hipError_t launch_preprocess(const PrepArgs& a, int grid_persist, hipStream_t s);
+hipError_t launch_preprocess(const PrepArgs& a, int num_cus, hipStream_t s);
 // Most workgroups each backward kernel of one bucket can use (upper bounds
 // from host-known sizes); launches clamp them to the co-resident capacity.
 struct BwdGrids {

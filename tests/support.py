@@ -173,6 +173,7 @@ def gpu_preprocess_views(tbe_obj, case: Case):
     N = case.N
     nb = v["num_buckets"]
     cnt = read_u32(ws, v["counters"], 6 + 5 * (nb + 1))
+    assert int(read_u32(ws, v["prep_error"], 1)[0]) == 0, "a look-back wait gave up"
     U, n1, nt, nm, nl, nc = (int(x) for x in cnt[:6])
     out = dict(
         sorted_key=read_u32(ws, v["sorted_key"], N).astype(np.int64),
