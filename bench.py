@@ -39,6 +39,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="C2", choices=["C1", "C2", "C3", "C4", "C5"])
     ap.add_argument("--fused", action="store_true", help="fused long-run countdown path")
+    ap.add_argument("--schedule", default="serial", choices=["overlap", "fork", "serial"],
+                    help="overlap: tbe_preprocess on a side stream during tbe_forward, then "
+                         "tbe_backward_rowwise_adagrad on preprocessed data with its run "
+                         "classes on three streams; fork: tbe_forward, then "
+                         "tbe_backward_rowwise_adagrad (which preprocesses) with its run classes "
+                         "on three streams; serial: all on one stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-lookups", type=int, default=3_000_000,
                     help="cap on lookups in the CPU oracle sample (whole tables)")
@@ -273,13 +279,20 @@ def main():
     ws = tb.workspace(spec.B, N)
     out = torch.empty((spec.B, spec.dtot), dtype=torch.float32, device="cuda")
     flags = te.TBE_BWD_FUSED_LONG if args.fused else 0
+    overlap = args.schedule == "overlap"
+    conc = 0 if args.schedule == "serial" else te.TBE_BWD_CONCURRENT
     hist = (spec.T == 1 and spec.rows[0] <= 64 and 64 <= spec.dims[0] <= 128
             and spec.wdtype == "f16" and not spec.weighted and N >= 64 * spec.B)
 
     def step():
-        te.tbe_forward(tb.plan, spec.B, d_idx, d_off, N, psw, out)
-        te.tbe_backward_rowwise_adagrad(tb.plan, spec.B, d_idx, d_off, N, psw, G, spec.lr,
-                                        spec.eps, ws, flags)
+        if overlap:
+            tb.forward_and_preprocess(spec.B, d_idx, d_off, psw, out)
+            te.tbe_backward_rowwise_adagrad(tb.plan, spec.B, d_idx, d_off, N, psw, G, spec.lr,
+                                            spec.eps, ws, flags | conc | te.TBE_BWD_PREPROCESSED)
+        else:
+            te.tbe_forward(tb.plan, spec.B, d_idx, d_off, N, psw, out)
+            te.tbe_backward_rowwise_adagrad(tb.plan, spec.B, d_idx, d_off, N, psw, G, spec.lr,
+                                            spec.eps, ws, flags | conc)
 
     for _ in range(args.warmup):
         step()
@@ -341,7 +354,15 @@ def main():
         "config": {"workload": args.config, "description": wl.DESCRIPTIONS[args.config],
                    "lookups": N, "tables": spec.T, "bags_per_table": spec.B,
                    "index_type": spec.itype, "long_run_path": "fused" if args.fused else
-                   "two-launch", "step": "tbe_forward + tbe_backward_rowwise_adagrad"},
+                   "two-launch", "schedule": args.schedule,
+                   "step": {"overlap": "tbe_forward || tbe_preprocess (side stream), then "
+                                       "tbe_backward_rowwise_adagrad(PREPROCESSED) with medium "
+                                       "runs and long runs on two side streams",
+                            "fork": "tbe_forward, then tbe_backward_rowwise_adagrad "
+                                    "(preprocessing inside) with medium runs and long runs on "
+                                    "two side streams",
+                            "serial": "tbe_forward, then tbe_backward_rowwise_adagrad "
+                                      "(preprocessing inside), one stream"}[args.schedule]},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -351,8 +372,10 @@ def main():
                 "frac_of_peak_compulsory": round(step_comp / (ms * 1e6) / HBM_PEAK_GBS, 4),
                 "logical_bytes_per_step": int(step_logi),
                 "effective_gbs_logical": round(step_logi / (ms * 1e6), 1)},
-        "kernel_timing": {"method": "HIP events around every launch on its own stream, "
-                                    "over a second pass of the same steps",
+        "kernel_timing": {"method": "HIP events around every launch on the stream it is "
+                                    "launched on, over a second pass of the same steps (with "
+                                    "the overlapped schedule a kernel's span includes time "
+                                    "shared with kernels on other streams)",
                           "ms_per_step_with_events": round(ms_prof, 5)},
         "kernels": kernels,
         "cpu_baseline": None,

@@ -39,9 +39,10 @@
  *    "Fewer reads and synchronizations").
  *  - Ownership: the caller owns every device buffer (weights, momentum,
  *    indices, offsets, per-sample weights, out, grad_out, workspace).  The
- *    plan owns only its small metadata.  A plan is immutable after creation
- *    and may be shared by calls on several streams; a workspace serves one
- *    call sequence at a time.
+ *    plan owns only its small metadata, two side streams and three events
+ *    of its own.  A plan is immutable after creation and may be shared by
+ *    calls on several streams; a workspace serves one call sequence at a
+ *    time.
  *  - Errors: every function returns TBE_OK or a negative code, detected on
  *    the host before anything is enqueued (except TBE_E_HIP, reported from
  *    the launch).  Nothing is printed.  Input contract violations on the
@@ -85,6 +86,7 @@ extern "C" {
 /* tbe_backward_rowwise_adagrad flags */
 #define TBE_BWD_PREPROCESSED 0x1u  /* the workspace already holds tbe_preprocess of these inputs */
 #define TBE_BWD_FUSED_LONG 0x2u    /* long runs: fused fence + countdown instead of a second launch */
+#define TBE_BWD_CONCURRENT 0x4u    /* run classes on three streams (fork from and join into `stream`) */
 
 typedef struct tbe_plan tbe_plan;
 
@@ -118,7 +120,8 @@ typedef struct {
 /* Create a plan over T tables (host arrays of length T; weights[t] and
  * momentum[t] are device pointers).  Tables are bucketed by next_pow2(D_t)
  * (FBTriton page, "Fewer reads and synchronizations").  The only entry point
- * that allocates (a few KB of device metadata) and synchronizes.
+ * that allocates (a few KB of device metadata, two default-priority side
+ * streams and three events for the backward) and synchronizes.
  * Errors: TBE_E_ARG, TBE_E_UNSUPPORTED (T > 4096, D outside [4, 1024] or not
  * a multiple of 4, R_t < 1), TBE_E_RANGE (sum R_t >= 2^32), TBE_E_ALLOC. */
 int tbe_plan_create(tbe_plan** out, int32_t T, const int64_t* rows, const int32_t* dims,
@@ -168,7 +171,15 @@ int tbe_preprocess(const tbe_plan* plan, int64_t B, int32_t itype, const void* i
  * and countdown so the last chunk of a run updates it; both give bit-identical
  * weights).  Weights and momentum of touched rows are updated in place;
  * untouched rows are not written.  debug_row_updates (device, nullable): one
- * uint32 per linear key, incremented once per row update. */
+ * uint32 per linear key, incremented once per row update.
+ * By default every kernel runs on `stream`, one after another.  The run
+ * classes own disjoint rows, so with TBE_BWD_CONCURRENT the call forks from
+ * `stream` onto the plan's two side streams (medium runs on one, chunks and
+ * long-run updates on the other, the rest on `stream`) and joins them back
+ * into `stream` before it returns: work enqueued later on `stream` sees
+ * every update, and the results are bit-identical to the one-stream order.
+ * Calls that share a plan enqueue this fork and join one at a time (a
+ * host-side lock). */
 int tbe_backward_rowwise_adagrad(const tbe_plan* plan, int64_t B, int32_t itype,
                                  const void* indices, const void* offsets, int64_t num_lookups,
                                  const float* per_sample_weights, const float* grad_out, float lr,

@@ -12,7 +12,8 @@ from typing import Optional, Sequence
 import torch
 
 from ._lib import (  # noqa: F401
-    EXPORTS, LIB_PATH, TBE_BF16, TBE_BWD_FUSED_LONG, TBE_BWD_PREPROCESSED, TBE_E_ALLOC,
+    EXPORTS, LIB_PATH, TBE_BF16, TBE_BWD_CONCURRENT, TBE_BWD_FUSED_LONG, TBE_BWD_PREPROCESSED,
+    TBE_E_ALLOC,
     TBE_E_ARG, TBE_E_HIP, TBE_E_RANGE, TBE_E_UNSUPPORTED, TBE_E_WORKSPACE, TBE_F16, TBE_F32,
     TBE_FWD_NO_HIST, TBE_FWD_REQUIRE_HIST, TBE_I32, TBE_I64, TBE_MEAN, TBE_OK, TBE_SUM,
     TBEError, lib, tbe_backward_rowwise_adagrad, tbe_forward, tbe_plan_create,
@@ -40,6 +41,7 @@ class TBE:
         self.plan = tbe_plan_create(self.rows, self.dims, self.pooling, self.weights,
                                     self.momentum)
         self._ws: Optional[torch.Tensor] = None
+        self._side: Optional[torch.cuda.Stream] = None
 
     def close(self):
         if self.plan is not None:
@@ -70,6 +72,31 @@ class TBE:
             out = torch.empty((B, self.dtot), dtype=torch.float32, device=offsets.device)
         tbe_forward(self.plan, B, indices, offsets, indices.numel(), per_sample_weights, out,
                     flags)
+        return out
+
+    def forward_and_preprocess(self, B: int, indices: torch.Tensor, offsets: torch.Tensor,
+                               per_sample_weights: Optional[torch.Tensor] = None,
+                               out: Optional[torch.Tensor] = None, flags: int = 0
+                               ) -> torch.Tensor:
+        """tbe_forward on the current stream and, at the same time, tbe_preprocess of the
+        same lookups on a side stream (default priority); the current stream then waits
+        for both.  A later backward(..., flags=TBE_BWD_PREPROCESSED) on the current stream
+        reuses the workspace (FBTriton page, "Backward": the preprocessing can move into
+        forward).  Only the order of launches differs from forward() then preprocess()."""
+        main = torch.cuda.current_stream(offsets.device)
+        if self._side is None:
+            self._side = torch.cuda.Stream(device=offsets.device)
+        side = self._side
+        ws = self.workspace(B, indices.numel())
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            tbe_preprocess(self.plan, B, indices, offsets, indices.numel(), per_sample_weights,
+                           ws)
+        for t in (indices, offsets, per_sample_weights, ws):
+            if t is not None:
+                t.record_stream(side)
+        out = self.forward(B, indices, offsets, per_sample_weights, out, flags)
+        main.wait_stream(side)
         return out
 
     def preprocess(self, B: int, indices: torch.Tensor, offsets: torch.Tensor,

@@ -24,7 +24,7 @@ TBE_F32, TBE_F16, TBE_BF16 = 0, 1, 2
 TBE_I32, TBE_I64 = 0, 1
 TBE_SUM, TBE_MEAN = 0, 1
 TBE_FWD_NO_HIST, TBE_FWD_REQUIRE_HIST = 0x1, 0x2
-TBE_BWD_PREPROCESSED, TBE_BWD_FUSED_LONG = 0x1, 0x2
+TBE_BWD_PREPROCESSED, TBE_BWD_FUSED_LONG, TBE_BWD_CONCURRENT = 0x1, 0x2, 0x4
 
 EXPORTS = ("tbe_plan_create", "tbe_plan_destroy", "tbe_plan_key_bases", "tbe_workspace_size",
            "tbe_workspace_views", "tbe_forward", "tbe_preprocess",

@@ -432,6 +432,27 @@ __global__ __launch_bounds__(kThreads) void bwd_medium_kernel(BwdArgs a, BucketS
 
 // ---------------------------------------------------------------- long runs
 
+// Chunk positions this workgroup takes.  Workgroups are dispatched to the
+// eight XCDs round-robin (workgroup i on XCD i mod 8) and each XCD has its own
+// L2.  The chunk list places the chunks of a long run so that position c
+// reads grad_out rows of about the (c mod 8)-th eighth of the table's bags
+// (see the classification), so the workgroups of XCD x take the positions
+// c = x (mod 8) and each XCD's L2 holds one eighth of the grad_out columns
+// of the table whose long runs are passing through.  The bucket's workgroups
+// come in groups of eight starting at a multiple of eight, so lb mod 8 is the
+// workgroup's XCD and lb / 8 its rank among the bucket's workgroups there.
+__device__ __forceinline__ void chunk_walk(uint32_t lb, uint32_t lg, uint32_t beg, uint32_t& c,
+                                           uint32_t& step) {
+  if (lg & 7u) {  // not launched in groups of eight: plain striding
+    c = beg + lb;
+    step = lg;
+    return;
+  }
+  const uint32_t xcd = lb & 7u, rank = lb >> 3, nx = lg >> 3;
+  c = beg + ((xcd - beg) & 7u) + 8u * rank;
+  step = 8u * nx;
+}
+
 template <int WD, int VEC, int NC>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a, BucketSet S) {
   BucketDev bk;
@@ -440,7 +461,9 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a, BucketSe
   __shared__ WgSmem<VEC, NC> sm;
   const uint32_t beg = list_begin(a, 4, bucket);
   const uint32_t end = min(list_begin(a, 4, bucket + 1), a.max_chunks);
-  for (uint32_t c = beg + lb; c < end; c += lg) {
+  uint32_t c, cstep;
+  chunk_walk(lb, lg, beg, c, cstep);
+  for (; c < end; c += cstep) {
     const uint4 task = a.chunk_task[c];  // {start, len, table, long index}
     if (!chunk_ok(a, task)) continue;    // uniform per workgroup; never for valid lists
     const TableDev td = a.tables[task.z];
@@ -475,7 +498,9 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_fused_kernel(BwdArgs a, Bu
   __shared__ WgSmem<VEC, NC> sm;
   const uint32_t beg = list_begin(a, 4, bucket);
   const uint32_t end = min(list_begin(a, 4, bucket + 1), a.max_chunks);
-  for (uint32_t c = beg + lb; c < end; c += lg) {
+  uint32_t c, cstep;
+  chunk_walk(lb, lg, beg, c, cstep);
+  for (; c < end; c += cstep) {
     const uint4 task = a.chunk_task[c];  // {start, len, table, long index}
     if (!chunk_ok(a, task) || !long_ok(a, task.w)) continue;  // uniform; never for valid lists
     const TableDev td = a.tables[task.z];
@@ -514,12 +539,17 @@ uint32_t resident(K kernel, int num_cus) {
   return (uint32_t)per_cu * (uint32_t)num_cus;
 }
 
-// Fill S.gbeg: bucket k gets min(need_k, cap / n) workgroups (at least 1).
-uint32_t set_grid(BucketSet& S, const BwdGrids* g, uint32_t BwdGrids::*field, uint32_t cap) {
-  const uint32_t share = cap / S.n > 0 ? cap / S.n : 1u;
+// Fill S.gbeg: bucket k gets min(need_k, cap / n) workgroups (at least 1);
+// with mult = 8 every bucket's count is a multiple of eight (at least eight),
+// so each bucket's range starts on an XCD boundary of the round-robin dispatch.
+uint32_t set_grid(BucketSet& S, const BwdGrids* g, uint32_t BwdGrids::*field, uint32_t cap,
+                  uint32_t mult = 1) {
+  uint32_t share = cap / S.n > 0 ? cap / S.n : 1u;
+  share = share / mult * mult > 0 ? share / mult * mult : mult;
   S.gbeg[0] = 0;
   for (uint32_t k = 0; k < S.n; ++k) {
-    const uint32_t need = g[k].*field > 0 ? g[k].*field : 1u;
+    uint32_t need = g[k].*field > 0 ? g[k].*field : 1u;
+    need = (need + mult - 1) / mult * mult;
     S.gbeg[k + 1] = S.gbeg[k] + (need < share ? need : share);
   }
   for (uint32_t k = S.n + 1; k <= (uint32_t)kMaxBuckets; ++k) S.gbeg[k] = S.gbeg[S.n];
@@ -547,22 +577,24 @@ void launch_small(const BwdArgs& a, BucketSet S, const BwdGrids* g, int cus, hip
 
 template <int WD, int VEC, int NC>
 hipError_t launch(const BwdArgs& a, BucketSet S, const BwdGrids* g, bool fused, int cus,
-                  hipStream_t s) {
+                  const hipStream_t* ss) {
   if (a.T <= (uint32_t)kTdCache)
-    launch_small<WD, VEC, NC, true>(a, S, g, cus, s);
+    launch_small<WD, VEC, NC, true>(a, S, g, cus, ss[0]);
   else
-    launch_small<WD, VEC, NC, false>(a, S, g, cus, s);
+    launch_small<WD, VEC, NC, false>(a, S, g, cus, ss[0]);
   static const uint32_t cap_m = resident(bwd_medium_kernel<WD, VEC, NC>, cus);
   uint32_t grid = set_grid(S, g, &BwdGrids::medium, cap_m);
-  TBE_LAUNCH("bwd_medium", (bwd_medium_kernel<WD, VEC, NC>), dim3(grid), dim3(kThreads), s, a, S);
+  TBE_LAUNCH("bwd_medium", (bwd_medium_kernel<WD, VEC, NC>), dim3(grid), dim3(kThreads), ss[1],
+             a, S);
+  const hipStream_t s = ss[2];
   if (fused) {
     static const uint32_t cap_f = resident(bwd_chunk_fused_kernel<WD, VEC, NC>, cus);
-    grid = set_grid(S, g, &BwdGrids::chunk, cap_f);
+    grid = set_grid(S, g, &BwdGrids::chunk, cap_f, 8);
     TBE_LAUNCH("bwd_chunk_fused", (bwd_chunk_fused_kernel<WD, VEC, NC>), dim3(grid),
                dim3(kThreads), s, a, S);
   } else {
     static const uint32_t cap_c = resident(bwd_chunk_kernel<WD, VEC, NC>, cus);
-    grid = set_grid(S, g, &BwdGrids::chunk, cap_c);
+    grid = set_grid(S, g, &BwdGrids::chunk, cap_c, 8);
     TBE_LAUNCH("bwd_chunk", (bwd_chunk_kernel<WD, VEC, NC>), dim3(grid), dim3(kThreads), s, a, S);
     static const uint32_t cap_l = resident(bwd_long_update_kernel<WD, VEC, NC>, cus);
     grid = set_grid(S, g, &BwdGrids::longrun, cap_l);
@@ -575,7 +607,7 @@ hipError_t launch(const BwdArgs& a, BucketSet S, const BwdGrids* g, bool fused, 
 }  // namespace
 
 hipError_t launch_backward_set(const BwdArgs& a, BucketSet S, const BwdGrids* g, int wd, int vec,
-                               int nc, bool fused, int num_cus, hipStream_t s) {
+                               int nc, bool fused, int num_cus, const hipStream_t* s) {
 #define TBE_BWD_CASE(W, V, N) \
   if (wd == W && vec == V && nc == N) return launch<W, V, N>(a, S, g, fused, num_cus, s);
   TBE_BWD_CASE(WD_F32, 4, 1)

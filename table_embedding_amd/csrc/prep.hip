@@ -529,6 +529,15 @@ __device__ __forceinline__ uint32_t bucket_of_key(const uint32_t* bkb, uint32_t 
   return b;
 }
 
+// Chunk placement.  A long run's nch chunks take list positions [cb, cb + nch),
+// and the backward gives position c to a workgroup on XCD c mod 8 (each XCD has
+// its own L2).  A long run's lookups are sorted by position, hence by bag, and
+// spread over the bags, so chunk k reads grad_out rows of about the k/nch-th
+// slice of the bags.  The positions of residue 0 (mod 8) take the first chunks,
+// those of residue 1 the next ones, and so on: the chunks a residue class holds
+// are consecutive, so XCD x reads about the x-th eighth of the bags for every
+// long run of a table, and a run's partial sums stay contiguous.
+
 __global__ __launch_bounds__(kThreads) void classify_kernel(ClsDev a) {
   __shared__ uint32_t s_kb[kMaxTables];
   __shared__ uint32_t s_ord[kMaxTables];
@@ -630,10 +639,15 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClsDev a) {
         a.long_cbeg[pl] = pc;
         a.remaining[pl] = nch;
       }
-      for (uint32_t q = 0; q < nch && pc + q < a.max_chunks; ++q) {
-        const uint32_t cl_len = (ln - q * kChunk) < (uint32_t)kChunk ? (ln - q * kChunk)
-                                                                      : (uint32_t)kChunk;
-        a.chunk_task[pc + q] = make_uint4(st + q * kChunk, cl_len, t, pl);
+      // chunk placement (above): walk the positions residue class by residue
+      // class, handing out chunk numbers q in turn
+      uint32_t q = 0;
+      for (uint32_t x = 0; x < 8u; ++x) {
+        for (uint32_t cp = pc + ((x - pc) & 7u); cp < pc + nch; cp += 8u, ++q) {
+          const uint32_t cl_len = (ln - q * kChunk) < (uint32_t)kChunk ? (ln - q * kChunk)
+                                                                        : (uint32_t)kChunk;
+          if (cp < a.max_chunks) a.chunk_task[cp] = make_uint4(st + q * kChunk, cl_len, t, pl);
+        }
       }
       pos[4] += nch;
       ++pos[3];

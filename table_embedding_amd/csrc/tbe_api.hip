@@ -43,6 +43,12 @@ struct tbe_plan {
   uint32_t* d_bkb;
   void* d_mem;
   int num_cus;
+  // backward fork/join: two default-priority side streams and their events;
+  // the lock keeps the record/wait sequence of one call from interleaving
+  // with another call's on the same plan
+  hipStream_t side[2];
+  hipEvent_t ev_fork, ev_join[2];
+  mutable std::mutex mu;
 };
 
 namespace {
@@ -418,9 +424,14 @@ int tbe_plan_create(tbe_plan** out, int32_t T, const int64_t* rows, const int32_
   ok = ok && hipGetDevice(&dev) == hipSuccess &&
        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess;
   P->num_cus = cus > 0 ? cus : 256;
+  P->side[0] = P->side[1] = nullptr;
+  P->ev_fork = P->ev_join[0] = P->ev_join[1] = nullptr;
+  for (int i = 0; i < 2 && ok; ++i)
+    ok = hipStreamCreateWithFlags(&P->side[i], hipStreamNonBlocking) == hipSuccess &&
+         hipEventCreateWithFlags(&P->ev_join[i], hipEventDisableTiming) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&P->ev_fork, hipEventDisableTiming) == hipSuccess;
   if (!ok) {
-    (void)hipFree(mem);
-    delete P;
+    (void)tbe_plan_destroy(P);
     return TBE_E_HIP;
   }
   *out = P;
@@ -429,9 +440,14 @@ int tbe_plan_create(tbe_plan** out, int32_t T, const int64_t* rows, const int32_
 
 int tbe_plan_destroy(tbe_plan* P) {
   if (!P) return TBE_OK;
-  const hipError_t e = hipFree(P->d_mem);
+  bool ok = hipFree(P->d_mem) == hipSuccess;
+  for (int i = 0; i < 2; ++i) {
+    if (P->side[i]) ok = hipStreamDestroy(P->side[i]) == hipSuccess && ok;
+    if (P->ev_join[i]) ok = hipEventDestroy(P->ev_join[i]) == hipSuccess && ok;
+  }
+  if (P->ev_fork) ok = hipEventDestroy(P->ev_fork) == hipSuccess && ok;
   delete P;
-  return e == hipSuccess ? TBE_OK : TBE_E_HIP;
+  return ok ? TBE_OK : TBE_E_HIP;
 }
 
 int tbe_plan_key_bases(const tbe_plan* P, int64_t* key_base) {
@@ -530,7 +546,7 @@ int tbe_backward_rowwise_adagrad(const tbe_plan* P, int64_t B, int32_t itype,
   if (rc) return rc;
   rc = check_ws(P, N, ws, ws_bytes);
   if (rc) return rc;
-  if (flags & ~(TBE_BWD_PREPROCESSED | TBE_BWD_FUSED_LONG)) return TBE_E_ARG;
+  if (flags & ~(TBE_BWD_PREPROCESSED | TBE_BWD_FUSED_LONG | TBE_BWD_CONCURRENT)) return TBE_E_ARG;
   if (B > 0 && (!grad_out || !aligned(grad_out, 16))) return TBE_E_ARG;
   if (psw && !aligned(psw, 4)) return TBE_E_ARG;
   if (debug_row_updates && !aligned(debug_row_updates, 4)) return TBE_E_ARG;
@@ -576,6 +592,19 @@ int tbe_backward_rowwise_adagrad(const tbe_plan* P, int64_t B, int32_t itype,
   a.max_long = L.max_long;
   a.max_chunks = L.max_chunks;
   const bool fused = flags & TBE_BWD_FUSED_LONG;
+  const bool fork = (flags & TBE_BWD_CONCURRENT) != 0;
+  std::unique_lock<std::mutex> lk(P->mu, std::defer_lock);
+  hipStream_t ss[3] = {s, s, s};
+  if (fork) {
+    lk.lock();
+    ss[1] = P->side[0];
+    ss[2] = P->side[1];
+    if (hipEventRecord(P->ev_fork, s) != hipSuccess ||
+        hipStreamWaitEvent(ss[1], P->ev_fork, 0) != hipSuccess ||
+        hipStreamWaitEvent(ss[2], P->ev_fork, 0) != hipSuccess)
+      return TBE_E_HIP;
+  }
+  int rc_launch = TBE_OK;
   for (const auto& grp : bucket_groups(P)) {
     BucketSet S = bucket_set(P, grp);
     BwdGrids g[kMaxBuckets];
@@ -588,11 +617,19 @@ int tbe_backward_rowwise_adagrad(const tbe_plan* P, int64_t B, int32_t itype,
       g[k].longrun = L.max_long;
     }
     const Bucket& b0 = P->buckets[grp[0]];
-    if (launch_backward_set(a, S, g, P->wdtype, b0.vec, b0.nc, fused, P->num_cus, s) !=
-        hipSuccess)
-      return TBE_E_HIP;
+    if (launch_backward_set(a, S, g, P->wdtype, b0.vec, b0.nc, fused, P->num_cus, ss) !=
+        hipSuccess) {
+      rc_launch = TBE_E_HIP;
+      break;
+    }
   }
-  return TBE_OK;
+  if (fork) {  // join even after a failed launch, so `s` never runs ahead of the side streams
+    for (int i = 0; i < 2; ++i)
+      if (hipEventRecord(P->ev_join[i], ss[1 + i]) != hipSuccess ||
+          hipStreamWaitEvent(s, P->ev_join[i], 0) != hipSuccess)
+        rc_launch = TBE_E_HIP;
+  }
+  return rc_launch;
 }
 
 }  // extern "C"

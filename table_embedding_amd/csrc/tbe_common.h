@@ -307,7 +307,10 @@ struct BwdGrids {
 
 // One launch per backward kernel for the buckets of S (S.gbeg is filled here
 // from the per-bucket grids g[0 .. S.n-1]).
+// Streams of the backward: short runs of one lane subgroup (SL < 32) on
+// s[0], medium runs on s[1], chunks and long-run updates on s[2] (all three
+// may be the same stream).
 hipError_t launch_backward_set(const BwdArgs& a, BucketSet S, const BwdGrids* g, int wd, int vec,
-                               int nc, bool fused, int num_cus, hipStream_t s);
+                               int nc, bool fused, int num_cus, const hipStream_t* s);
 
 }  // namespace tbe

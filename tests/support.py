@@ -270,11 +270,17 @@ def check_preprocess(case: Case, tbe_obj):
         nch = (lt[:, 1] + 255) // 256
         assert np.array_equal(g["long_cbeg"], np.concatenate([[0], np.cumsum(nch)[:-1]]))
         ct = g["chunk_task"]
-        want = []
+        # a run's chunks fill its positions [cbeg, cbeg + nch); the positions are taken in
+        # order of (position mod 8, position) and receive chunks 0, 1, 2, ... in turn, so
+        # the chunks a residue class holds are consecutive in the run
+        want = np.full((g["n_chunks"], 4), -1, np.int64)
         for l, (st0, ln, row, t) in enumerate(lt):
-            for k in range(int((ln + 255) // 256)):
-                want.append([st0 + 256 * k, min(256, ln - 256 * k), t, l])
-        assert np.array_equal(ct, np.array(want, np.int64).reshape(-1, 4)), "chunk tasks differ"
+            nch = int((ln + 255) // 256)
+            cb = int(g["long_cbeg"][l])
+            slots = sorted(range(cb, cb + nch), key=lambda q: (q % 8, q))
+            for k, q in enumerate(slots):
+                want[q] = [st0 + 256 * k, min(256, ln - 256 * k), t, l]
+        assert np.array_equal(ct, want), "chunk tasks differ"
     # per-bucket begins split the five lists exactly at bucket changes
     bt = bucket_of_table(s)
     z = np.zeros(0, np.int64)

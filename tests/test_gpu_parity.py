@@ -220,3 +220,56 @@ def test_repeat_runs_bitwise_identical():
         ws.append([S.to_host_storage(w, "bf16").tobytes() for w in tb.weights])
     assert outs[0] == outs[1] == outs[2]
     assert ws[0] == ws[1] == ws[2]
+
+
+def _tables_bytes(tb, wdtype):
+    return ([S.to_host_storage(w, wdtype).tobytes() for w in tb.weights] +
+            [m.cpu().numpy().tobytes() for m in tb.momentum])
+
+
+@pytest.mark.parametrize("name", ["C2s", "C3s", "C5s", "many_tables", "const257"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_concurrent_backward_equals_one_stream(name, fused):
+    """The run classes on three streams give the same bits as one stream: they
+    own disjoint rows and every sum is in a data-determined order."""
+    _announce(name, f"concurrent-vs-one-stream fused={fused}")
+    import table_embedding_amd as te
+    case = S.Case(_spec(name), m_nonzero=True)
+    res = []
+    base = te.TBE_BWD_FUSED_LONG if fused else 0
+    for flags in (base, base | te.TBE_BWD_CONCURRENT, base):
+        case.reset_tables()
+        tb = case.tbe()
+        tb.backward(case.spec.B, case.d_idx, case.d_off, case.d_psw, case.d_G, case.spec.lr,
+                    case.spec.eps, flags=flags)
+        torch.cuda.synchronize()
+        res.append(_tables_bytes(tb, case.spec.wdtype))
+        tb.close()
+    assert res[0] == res[1] == res[2]
+
+
+@pytest.mark.parametrize("name", ["C2s", "C3s", "empty_bags", "wide_f32"])
+def test_forward_and_preprocess_schedule(name):
+    """Forward with the preprocessing on a side stream, then backward on the
+    preprocessed workspace: same output and tables as forward then a
+    self-preprocessing backward on one stream, and within the oracle's bars."""
+    _announce(name, "forward||preprocess schedule")
+    import table_embedding_amd as te
+    case = S.Case(_spec(name), m_nonzero=True)
+    if case.N == 0:
+        pytest.skip("no lookups")
+    B = case.spec.B
+    tb = case.tbe()
+    out = tb.forward_and_preprocess(B, case.d_idx, case.d_off, case.d_psw)
+    tb.backward(B, case.d_idx, case.d_off, case.d_psw, case.d_G, case.spec.lr, case.spec.eps,
+                flags=te.TBE_BWD_PREPROCESSED | te.TBE_BWD_CONCURRENT)
+    torch.cuda.synchronize()
+    S.check_forward(case, out)
+    S.check_backward(case, tb)
+    got = (out.cpu().numpy().tobytes(), _tables_bytes(tb, case.spec.wdtype))
+    case.reset_tables()
+    tb2 = case.tbe()
+    out2 = tb2.forward(B, case.d_idx, case.d_off, case.d_psw)
+    tb2.backward(B, case.d_idx, case.d_off, case.d_psw, case.d_G, case.spec.lr, case.spec.eps)
+    torch.cuda.synchronize()
+    assert got == (out2.cpu().numpy().tobytes(), _tables_bytes(tb2, case.spec.wdtype))
