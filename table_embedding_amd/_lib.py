@@ -23,7 +23,7 @@ TBE_OK, TBE_E_ARG, TBE_E_UNSUPPORTED, TBE_E_WORKSPACE, TBE_E_RANGE, TBE_E_HIP, T
 TBE_F32, TBE_F16, TBE_BF16 = 0, 1, 2
 TBE_I32, TBE_I64 = 0, 1
 TBE_SUM, TBE_MEAN = 0, 1
-TBE_FWD_NO_HIST, TBE_FWD_REQUIRE_HIST = 0x1, 0x2
+TBE_FWD_NO_HIST, TBE_FWD_REQUIRE_HIST, TBE_FWD_BALANCE, TBE_FWD_NO_BALANCE = 0x1, 0x2, 0x4, 0x8
 TBE_BWD_PREPROCESSED, TBE_BWD_FUSED_LONG, TBE_BWD_CONCURRENT = 0x1, 0x2, 0x4
 
 EXPORTS = ("tbe_plan_create", "tbe_plan_destroy", "tbe_plan_key_bases", "tbe_workspace_size",

@@ -4,16 +4,28 @@
 // tables do not idle lanes sized for the widest one, section "Fewer reads and
 // synchronizations").
 //
-// Lane mapping: one subgroup of `lpr` lanes per bag; lane k covers columns
-// k*VEC + c*lpr*VEC (c < NC) with 16-byte (VEC elements) row loads, so a row
-// of the bucket width is read by consecutive lanes in one coalesced sweep.
+// Lane mapping: a subgroup of `lpr` lanes covers one row; lane k holds
+// columns k*VEC + c*lpr*VEC (c < NC), read with 16-byte (VEC element) loads,
+// so a row of the bucket width is one coalesced sweep of the subgroup.
+//
+// Balance (fwd_bal_kernel, bps > 1): a wave owns G = fwd_group_bags(lpr, bps)
+// consecutive bags of one
+// table (their lookups are contiguous) and gives each of its 64/lpr
+// subgroups a contiguous run of whole bags holding about 1/(64/lpr) of the
+// group's lookups: bag q goes to subgroup floor((O[q] - O[first]) / share).
+// With one bag per subgroup a wave lasts as long as its longest bag while the
+// other subgroups idle; with a few bags per subgroup the runs even out, at
+// the price of fewer waves, so the host picks bps from the batch size.  A
+// subgroup streams its lookups in order and writes a bag's pooled row when
+// the bag ends, so every bag has one owner and plain stores.
 //
 // Memory-level parallelism: lookups are taken eight at a time.  The eight
 // indices are loaded, then the eight rows, then the eight rows are
 // accumulated in lookup order; scheduling barriers keep the compiler from
 // sinking each row load next to its use, which would leave one row in flight.
-// A partial last batch repeats the bag's last index and drops the repeats with
-// a select, so the batch has no branches (the repeated row is a cache hit).
+// A partial last batch repeats the last index and drops the repeats with a
+// select (the repeated row is a cache hit).  The indices of the next batch
+// load while the rows of the current one are in flight.
 #include "tbe_common.h"
 
 namespace tbe {
@@ -30,6 +42,170 @@ struct Acc<WD_F32> {
   using T = double;
 };
 
+// acc + s*v with one rounding, written out so that every forward kernel
+// rounds the same way whatever the compiler would contract (a padded slot
+// has s = 0 and leaves acc unchanged).
+__device__ __forceinline__ float fma_acc(float s, float v, float acc) {
+  return __builtin_fmaf(s, v, acc);
+}
+__device__ __forceinline__ double fma_acc(double s, float v, double acc) {
+  return __builtin_fma(s, (double)v, acc);
+}
+
+// LDS visibility inside one wave: every lane's stores before any lane's loads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int WD, int VEC, int NC, typename IT, bool PSW>
+__global__ __launch_bounds__(kThreads) void fwd_bal_kernel(FwdArgs a, BucketSet S) {
+  using AT = typename Acc<WD>::T;
+  constexpr uint32_t kWaves = kThreads / kWave;
+  __shared__ uint32_t s_off[kWaves][kWave + 1];
+  BucketDev bk;
+  uint32_t bucket_id, lb, lg;
+  set_pick(S, bk, bucket_id, lb, lg);
+  const uint32_t lane = lane_id(), wave = threadIdx.x / kWave;
+  const uint32_t lpr = bk.lpr, lg2 = bk.lpr_log2;
+  const uint32_t nsub = (uint32_t)kWave >> lg2;
+  const uint32_t sgi = lane >> lg2, lane_in = lane & (lpr - 1);
+  const uint32_t G = fwd_group_bags(lpr, a.bps);
+  const uint64_t B = (uint64_t)a.B;
+  const uint64_t gpt = (B + G - 1) / G;  // bag groups per table
+  const uint64_t wv = (uint64_t)lb * kWaves + wave;
+  if (wv >= gpt * (uint64_t)bk.ntables) return;  // the whole wave; only wave-level syncs follow
+  const uint32_t slot = (uint32_t)(wv / gpt);
+  const uint64_t g0 = (wv - (uint64_t)slot * gpt) * G;
+  const uint32_t nbw = (uint32_t)((B - g0) < (uint64_t)G ? (B - g0) : (uint64_t)G);
+  const uint32_t t = bk.tables[slot];
+  const TableDev td = a.tables[t];
+  const IT* __restrict__ I = reinterpret_cast<const IT*>(a.indices);
+  const IT* __restrict__ O = reinterpret_cast<const IT*>(a.offsets);
+  const uint64_t j0 = (uint64_t)t * B + g0;
+  const uint32_t D = td.dim;
+
+  // offsets of the group's bags: off[q] = O[j0 + q], q = 0 .. nbw (positions < 2^31)
+  uint32_t* off = s_off[wave];
+  if (lane <= nbw) off[lane] = (uint32_t)O[j0 + lane];
+  if (nbw == (uint32_t)kWave && lane == 0) off[kWave] = (uint32_t)O[j0 + kWave];
+  wave_lds_sync();
+
+  // this subgroup's bags [sb_lo, sb_hi)
+  uint32_t sb_lo, sb_hi;
+  if (G <= nsub) {
+    sb_lo = sgi < nbw ? sgi : nbw;
+    sb_hi = sgi + 1 < nbw ? sgi + 1 : nbw;
+  } else {
+    const uint32_t P0 = off[0];
+    const uint32_t tot = off[nbw] - P0;
+    uint32_t share = (tot + nsub - 1) / nsub;
+    share = share > 0 ? share : 1u;
+    uint32_t own = 0;
+    if (lane < nbw) {
+      own = (off[lane] - P0) / share;
+      own = own < nsub - 1 ? own : nsub - 1;
+    }
+    sb_lo = 0;
+    sb_hi = nbw;
+    for (uint32_t i = 1; i < nsub; ++i) {  // s_i = #bags owned below subgroup i
+      const uint32_t si = (uint32_t)__popcll(__ballot(lane < nbw && own < i));
+      if (sgi == i) sb_lo = si;
+      if (sgi + 1 == i) sb_hi = si;
+    }
+  }
+  const uint32_t pb = off[sb_lo], pe = off[sb_hi];
+
+  AT acc[NC][VEC];
+  bool act[NC];
+  uint32_t colc[NC], cold[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[c][v] = AT(0);
+    colc[c] = (lane_in + (uint32_t)c * lpr) * VEC;
+    act[c] = colc[c] < D;
+    cold[c] = act[c] ? colc[c] : 0u;  // idle lanes read column 0 and discard it
+  }
+  const bool mean = td.pooling == POOL_MEAN;
+  // write bag q's pooled row (mean: divided by its length) and clear the sums
+  auto flush = [&](uint32_t q) {
+    const uint32_t L = off[q + 1] - off[q];
+    float* orow = a.out + (int64_t)(g0 + q) * (int64_t)a.dtot + td.col;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (act[c]) {
+        float o[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          o[e] = (float)((mean && L > 0) ? acc[c][e] / AT(L) : acc[c][e]);
+        store_f32<VEC>(orow + colc[c], o);
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[c][e] = AT(0);
+    }
+  };
+
+  uint32_t cur = sb_lo;                            // bag being summed
+  uint32_t nxt = cur < sb_hi ? off[cur + 1] : pe;  // its end
+  int64_t nrow[kInFlight];
+  float ns[kInFlight];
+  if (pb < pe) {
+#pragma unroll
+    for (int k = 0; k < kInFlight; ++k) {
+      const uint32_t q = pb + k < pe ? pb + k : pe - 1;
+      nrow[k] = (int64_t)I[q];
+      ns[k] = PSW ? a.psw[q] : 1.0f;
+    }
+  }
+  for (uint32_t p = pb; p < pe; p += kInFlight) {
+    int64_t row[kInFlight];
+    float s[kInFlight];
+    bool ok[kInFlight];
+#pragma unroll
+    for (int k = 0; k < kInFlight; ++k) {
+      row[k] = nrow[k];
+      s[k] = ns[k];
+      ok[k] = p + k < pe;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // NC > 1 only for rows that take all 64 lanes, which get one bag per wave,
+    // so a bag can only end inside the c = 0 sweep when NC == 1
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float v[kInFlight][VEC];
+#pragma unroll
+      for (int k = 0; k < kInFlight; ++k) load_w<WD, VEC>(td.w, row[k] * D + cold[c], v[k]);
+      if (c == 0) {
+#pragma unroll
+        for (int k = 0; k < kInFlight; ++k) {
+          const uint32_t q = p + kInFlight + k < pe ? p + kInFlight + k : pe - 1;
+          nrow[k] = (int64_t)I[q];
+          ns[k] = PSW ? a.psw[q] : 1.0f;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < kInFlight; ++k) {
+        if (NC == 1 && ok[k]) {
+          while (p + k >= nxt) {  // lookup p+k opens a later bag: finish the current one(s)
+            flush(cur);
+            ++cur;
+            nxt = off[cur + 1];
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          acc[c][e] = fma_acc(ok[k] ? AT(s[k]) : AT(0), v[k][e], acc[c][e]);
+      }
+    }
+  }
+  for (; cur < sb_hi; ++cur) flush(cur);  // the last bag and any empty ones after it
+}
+
+// One bag per lane subgroup (bps == 1): subgroup sg of the launch pools bag sg
+// of the bucket; the offsets and indices load straight from global memory.
 template <int WD, int VEC, int NC, typename IT, bool PSW>
 __global__ __launch_bounds__(kThreads) void fwd_pool_kernel(FwdArgs a, BucketSet S) {
   using AT = typename Acc<WD>::T;
@@ -104,7 +280,8 @@ __global__ __launch_bounds__(kThreads) void fwd_pool_kernel(FwdArgs a, BucketSet
 #pragma unroll
       for (int k = 0; k < kInFlight; ++k)
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[c][e] += ok[k] ? AT(s[k]) * AT(v[k][e]) : AT(0);
+        for (int e = 0; e < VEC; ++e)
+          acc[c][e] = fma_acc(ok[k] ? AT(s[k]) : AT(0), v[k][e], acc[c][e]);
     }
   }
 
@@ -125,8 +302,12 @@ template <int WD, int VEC, int NC, typename IT, bool PSW>
 hipError_t launch_t(const FwdArgs& a, const BucketSet& S, hipStream_t s) {
   const uint32_t grid = S.gbeg[S.n];
   if (grid == 0) return hipSuccess;
-  TBE_LAUNCH("fwd_pool", (fwd_pool_kernel<WD, VEC, NC, IT, PSW>), dim3(grid), dim3(kThreads), s,
-             a, S);
+  if (a.bps > 1)
+    TBE_LAUNCH("fwd_pool", (fwd_bal_kernel<WD, VEC, NC, IT, PSW>), dim3(grid), dim3(kThreads), s,
+               a, S);
+  else
+    TBE_LAUNCH("fwd_pool", (fwd_pool_kernel<WD, VEC, NC, IT, PSW>), dim3(grid), dim3(kThreads), s,
+               a, S);
   return hipGetLastError();
 }
 

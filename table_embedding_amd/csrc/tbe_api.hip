@@ -144,6 +144,22 @@ bool hist_eligible(const tbe_plan* P, int64_t B, int64_t N, const float* psw) {
          P->wdtype == TBE_F16 && psw == nullptr && B > 0 && N >= 64 * B;
 }
 
+// Bags per lane subgroup of the generic forward.  Four bags per subgroup
+// even out the bag lengths inside a wave but leave a quarter of the waves:
+// measured on MI355X it pays (3-6%) once one bag per subgroup would give at
+// least kFwdBalanceWavesPerCu waves per CU, and costs 6-10% below that,
+// where the batch is too small to keep the memory system busy with fewer
+// waves.
+constexpr uint64_t kFwdBalanceWavesPerCu = 64;
+uint32_t fwd_bags_per_subgroup(const tbe_plan* P, int64_t B) {
+  uint64_t waves = 0;  // with one bag per subgroup
+  for (const Bucket& bk : P->buckets) {
+    const uint64_t nsub = (uint64_t)kWave / bk.lpr;
+    waves += (uint64_t)bk.tables.size() * (((uint64_t)B + nsub - 1) / nsub);
+  }
+  return waves >= kFwdBalanceWavesPerCu * (uint64_t)P->num_cus ? 4u : 1u;
+}
+
 bool any_mean(const tbe_plan* P) {
   for (int32_t p : P->pooling)
     if (p == TBE_MEAN) return true;
@@ -490,27 +506,34 @@ int tbe_forward(const tbe_plan* P, int64_t B, int32_t itype, const void* indices
                 void* stream) {
   int rc = check_lookups(P, B, itype, indices, offsets, N);
   if (rc) return rc;
-  if (flags & ~(TBE_FWD_NO_HIST | TBE_FWD_REQUIRE_HIST)) return TBE_E_ARG;
+  if (flags & ~(TBE_FWD_NO_HIST | TBE_FWD_REQUIRE_HIST | TBE_FWD_BALANCE | TBE_FWD_NO_BALANCE))
+    return TBE_E_ARG;
   if ((flags & TBE_FWD_NO_HIST) && (flags & TBE_FWD_REQUIRE_HIST)) return TBE_E_ARG;
+  if ((flags & TBE_FWD_BALANCE) && (flags & TBE_FWD_NO_BALANCE)) return TBE_E_ARG;
   if (B > 0 && (!out || !aligned(out, 16))) return TBE_E_ARG;
   if (psw && !aligned(psw, 4)) return TBE_E_ARG;
   const bool hist = hist_eligible(P, B, N, psw);
   if ((flags & TBE_FWD_REQUIRE_HIST) && !hist) return TBE_E_UNSUPPORTED;
   if (B == 0) return TBE_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  FwdArgs a{P->d_tables, B, itype, indices, offsets, psw, out, P->dtot};
+  FwdArgs a{P->d_tables, B, itype, indices, offsets, psw, out, P->dtot, 1u};
   hipError_t e = hipSuccess;
   if (hist && !(flags & TBE_FWD_NO_HIST)) {
     e = launch_forward_hist(a, (uint32_t)P->rows[0], (uint32_t)P->dims[0],
                             P->pooling[0] == TBE_MEAN, P->num_cus * 4, s);
   } else {
+    a.bps = (flags & TBE_FWD_BALANCE)      ? 4u
+            : (flags & TBE_FWD_NO_BALANCE) ? 1u
+                                           : fwd_bags_per_subgroup(P, B);
     for (const auto& grp : bucket_groups(P)) {
       BucketSet S = bucket_set(P, grp);
       S.gbeg[0] = 0;
       for (uint32_t k = 0; k < S.n; ++k) {
-        const uint64_t nbags = (uint64_t)S.bk[k].ntables * (uint64_t)B;
-        const uint64_t per_block = kThreads / S.bk[k].lpr;
-        S.gbeg[k + 1] = S.gbeg[k] + (uint32_t)((nbags + per_block - 1) / per_block);
+        // one wave per group of fwd_group_bags(lpr, bps) consecutive bags of a table
+        const uint64_t G = fwd_group_bags(S.bk[k].lpr, a.bps);
+        const uint64_t waves = (uint64_t)S.bk[k].ntables * (((uint64_t)B + G - 1) / G);
+        const uint64_t per_block = kThreads / kWave;
+        S.gbeg[k + 1] = S.gbeg[k] + (uint32_t)((waves + per_block - 1) / per_block);
       }
       for (uint32_t k = S.n + 1; k <= (uint32_t)kMaxBuckets; ++k) S.gbeg[k] = S.gbeg[S.n];
       const Bucket& b0 = P->buckets[grp[0]];

@@ -237,6 +237,18 @@ void prof_end(hipStream_t s);
     ::tbe::prof_end((stream));                                               \
   } while (0)
 
+// Forward: bags per wave.  A wave owns this many consecutive bags of one
+// table and splits them among its 64/lpr lane subgroups into contiguous runs
+// of whole bags with about equal lookup counts (about `bps` bags per
+// subgroup, at most 64 per wave: one offset per lane).  A bucket whose rows
+// take all 64 lanes (one subgroup per wave) keeps one bag per wave.
+__host__ __device__ inline uint32_t fwd_group_bags(uint32_t lpr, uint32_t bps) {
+  const uint32_t nsub = (uint32_t)kWave / lpr;
+  if (nsub <= 1u) return 1u;
+  const uint32_t g = nsub * bps;
+  return g < (uint32_t)kWave ? g : (uint32_t)kWave;
+}
+
 struct FwdArgs {
   const TableDev* tables;
   int64_t B;
@@ -246,6 +258,7 @@ struct FwdArgs {
   const float* psw;
   float* out;
   uint32_t dtot;
+  uint32_t bps;  // bags per lane subgroup in the generic forward (1 .. 4)
 };
 
 struct PrepArgs {

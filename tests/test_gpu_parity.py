@@ -73,15 +73,31 @@ def _announce(name, what):
     print(f"[gpu] {what} case={name}", flush=True)
 
 
+@pytest.mark.parametrize("split", ["one_bag", "balanced"])
 @pytest.mark.parametrize("name", MAIN + EDGE)
-def test_forward_parity(name):
-    _announce(name, "forward")
+def test_forward_parity(name, split):
+    _announce(name, f"forward {split}")
     case = S.Case(_spec(name))
     tb = case.tbe()
     import table_embedding_amd as te
-    out = tb.forward(case.spec.B, case.d_idx, case.d_off, case.d_psw, flags=te.TBE_FWD_NO_HIST)
+    f = te.TBE_FWD_NO_BALANCE if split == "one_bag" else te.TBE_FWD_BALANCE
+    out = tb.forward(case.spec.B, case.d_idx, case.d_off, case.d_psw,
+                     flags=te.TBE_FWD_NO_HIST | f)
     torch.cuda.synchronize()
     S.check_forward(case, out)
+
+
+@pytest.mark.parametrize("name", ["C2s", "C3s", "empty_bags", "many_tables", "wide_f32"])
+def test_forward_split_bitwise_equal(name):
+    """Both bag splits sum each bag in lookup order in one subgroup: same bits."""
+    _announce(name, "forward split equality")
+    import table_embedding_amd as te
+    case = S.Case(_spec(name))
+    tb = case.tbe()
+    outs = [tb.forward(case.spec.B, case.d_idx, case.d_off, case.d_psw,
+                       flags=te.TBE_FWD_NO_HIST | f).cpu().numpy().tobytes()
+            for f in (te.TBE_FWD_NO_BALANCE, te.TBE_FWD_BALANCE, 0)]
+    assert outs[0] == outs[1] == outs[2]
 
 
 @pytest.mark.parametrize("name", MAIN + EDGE)
