@@ -8,18 +8,32 @@
 // pipeline (sample ids expanded per lookup, radix sort by row with the end
 // bit cut to the vocabulary, run flags, scan, run offsets).
 //
+// Segments.  The lookups of table t are contiguous (table-major bags), so
+// sorting by linear key is sorting each table's lookups by row and placing the
+// tables in key order.  Each table is a segment sorted on its own: the radix
+// passes cover only the bits of the largest table's row range (C5: 23 bits,
+// three 8-bit passes, instead of 29 bits of linear key) and tiles never
+// straddle two segments.  Tile offsets come from one prefix over all tiles:
+// the count of a digit in the segments before a tile's segment is that prefix
+// at the segment's first tile, and is subtracted.
+//
 // Kernels, in launch order (256 threads each, no host readback anywhere):
-//   prep_init      zeroes the control block (digit histograms, tile tickets,
-//                  error flag) and the look-back status words of the first
-//                  sort pass, the run-length pass and the classification pass
-//   transpose      key[p] = key_base[t] + I[p], bag[p] = j and, with
-//                  per-sample weights or a mean table, scale[p] = S[p]*(1/L);
-//                  also counts every radix digit of every pass (LDS
-//                  histograms, one global add per bin and workgroup)
-//   sort_pass      one launch per 8-bit digit, least significant first: a
-//                  stable scatter of 4096-key tiles whose global offsets come
-//                  from the digit totals plus a decoupled look-back over the
-//                  earlier tiles' per-digit counts (no separate upsweep or scan)
+//   seg_setup      one workgroup: per segment (tables in key order) its
+//                  lookup count, output base and first tile; the segment of
+//                  every tile; clears the control block (tickets, error flag)
+//   transpose      key = key_base[t] + I[p], bag = j and, with per-sample
+//                  weights or a mean table, scale = S[p]*(1/L), written at
+//                  the lookup's slot in its table's segment
+//   then per 8-bit digit, least significant first:
+//   radix_upsweep  per tile, the count of each value of the digit of
+//                  (key - key_base) in the pass's input; the first one also
+//                  clears the look-back status words of rle and classify
+//   radix_scan     per digit value, the exclusive prefix over all tiles (in
+//                  place) and the total
+//   radix_downsweep  a stable scatter of each 4096-key tile to the offsets
+//                  of the scan (a decoupled look-back instead of the count
+//                  and scan was measured 2-4x slower per pass on MI355X at 34k
+//                  tiles: C5, three passes)
 //   rle            run heads of the sorted keys -> run_start, run_key, U (tile
 //                  offsets by look-back)
 //   classify       one-lookup / tiny / medium short-run tasks, long-run tasks,
@@ -56,6 +70,8 @@ struct PrepDev {
   const void* offsets;
   const float* psw;
   uint32_t N;
+  const uint32_t* tseg;  // segment (position in key order) of each table
+  const uint4* seg;      // per segment {lookups, output base, first tile, key base}
 };
 
 __device__ __forceinline__ void st_publish(uint64_t* p, uint64_t v) {
@@ -65,9 +81,9 @@ __device__ __forceinline__ uint64_t st_read(uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Sum of the counts of tiles [0, tile) in column `col` of a status table with
-// `stride` words per tile.  W predecessors are read per round trip; the ready
-// ones nearest the tile are consumed up to the first inclusive prefix.
+// Sum of the counts of tiles [0, tile) in column `col` of a status table
+// with `stride` words per tile.  W predecessors are read per round trip; the
+// ready ones nearest the tile are consumed up to the first inclusive prefix.
 template <int W>
 __device__ uint32_t look_back(uint64_t* st, uint32_t tile, uint32_t stride, uint32_t col,
                               uint32_t* err) {
@@ -176,12 +192,54 @@ __device__ __forceinline__ uint32_t take_ticket(uint32_t* ticket, uint32_t* s_ti
   return *s_tile;
 }
 
+// ------------------------------------------------------------ segments
+
+// One workgroup.  Segment s is table order[s] (tables in key order); its
+// lookups are [O[t*B], O[(t+1)*B]).  Writes {lookups, output base, first
+// tile, key base} per segment, the segment of every tile, the tile total
+// (ctl[kCtlTiles]) and clears the tickets and the error flag.
+template <typename IT>
+__global__ __launch_bounds__(kThreads) void seg_setup_kernel(PrepDev a,
+                                                             const uint32_t* __restrict__ order,
+                                                             uint4* __restrict__ seg,
+                                                             uint32_t* __restrict__ tile_seg,
+                                                             uint32_t ntiles_max,
+                                                             uint32_t* __restrict__ ctl) {
+  __shared__ uint32_t sh4[4];
+  const IT* __restrict__ O = reinterpret_cast<const IT*>(a.offsets);
+  for (uint32_t i = threadIdx.x; i < (uint32_t)kCtlTiles; i += kThreads) ctl[i] = 0u;
+  uint32_t run_n = 0, run_t = 0;
+  for (uint32_t s0 = 0; s0 < a.T; s0 += kThreads) {
+    const uint32_t s = s0 + threadIdx.x;
+    uint32_t n = 0, t = 0;
+    if (s < a.T) {
+      t = order[s];
+      n = (uint32_t)(O[(int64_t)(t + 1) * a.B] - O[(int64_t)t * a.B]);
+    }
+    uint32_t tot_n, tot_t;
+    const uint64_t on_raw = (uint64_t)run_n + block_excl_scan(n, sh4, tot_n);
+    // offsets that keep the contract (O[T*B] = N) are unchanged by the clamps;
+    // others still give segments inside [0, N) and at most ntiles_max tiles
+    const uint32_t on = on_raw < a.N ? (uint32_t)on_raw : a.N;
+    const uint32_t nc = on_raw < a.N ? (n < a.N - on ? n : a.N - on) : 0u;
+    const uint32_t nt = (nc + kTile - 1) / kTile;
+    const uint32_t ot = run_t + block_excl_scan(nt, sh4, tot_t);
+    if (s < a.T) {
+      seg[s] = make_uint4(nc, on, ot, a.tables[t].key_base);
+      for (uint32_t k = 0; k < nt && ot + k < ntiles_max; ++k) tile_seg[ot + k] = s;
+    }
+    run_n += tot_n;
+    run_t += tot_t;
+  }
+  if (threadIdx.x == 0) ctl[kCtlTiles] = run_t < ntiles_max ? run_t : ntiles_max;
+}
+
 // ------------------------------------------------------------ transposition
-// 16 lanes per bag write its lookups' keys and bag id with contiguous stores.
-// With per-sample weights or mean pooling it also writes the contribution
-// scale of each lookup, S[p] * (1/L if mean) (FBTriton page, "Fusion
-// boundaries": the weights scale each contribution before the grouping by
-// row).
+// 16 lanes per bag write its lookups' keys and bag id with contiguous stores,
+// at the lookups' slots in the table's segment.  With per-sample weights or
+// mean pooling it also writes the contribution scale of each lookup,
+// S[p] * (1/L if mean) (FBTriton page, "Fusion boundaries": the weights
+// scale each contribution before the grouping by row).
 template <typename IT>
 __global__ __launch_bounds__(kThreads) void transpose_kernel(PrepDev a, uint32_t* __restrict__ key,
                                                              uint32_t* __restrict__ bag,
@@ -195,85 +253,117 @@ __global__ __launch_bounds__(kThreads) void transpose_kernel(PrepDev a, uint32_t
   const IT* __restrict__ O = reinterpret_cast<const IT*>(a.offsets);
   const int64_t lo = O[j];
   const int64_t hi = O[j + 1];
+  // slot of lookup p: the segment's output base plus p's rank inside the table
+  const int64_t shift = (int64_t)a.seg[a.tseg[t]].y - (int64_t)O[(int64_t)t * a.B];
   const bool mean = td.pooling == POOL_MEAN;
   for (int64_t p = lo + lane16; p < hi; p += 16) {
-    key[p] = td.key_base + (uint32_t)I[p];
-    bag[p] = (uint32_t)j;
+    const int64_t d = p + shift;
+    if ((uint64_t)d >= (uint64_t)a.N) continue;  // only for offsets that break the contract
+    key[d] = td.key_base + (uint32_t)I[p];
+    bag[d] = (uint32_t)j;
     if (scale) {
       const float sp = a.psw ? a.psw[p] : 1.0f;
-      scale[p] = mean ? sp / (float)(hi - lo) : sp;
+      scale[d] = mean ? sp / (float)(hi - lo) : sp;
     }
   }
 }
 
 // ------------------------------------------------------------- radix sort
-// Digit counts of every pass for every 4096-key tile of the transposed keys,
-// digit-major: cnt[(pass*256 + d) * ntiles + tile].  The digit totals of a
-// pass do not depend on the order of the keys, so one read of the keys gives
-// them for all passes.  This kernel also clears the look-back state of the
-// later kernels (tickets, error flag, status words).
+
+// Tile `tile` of the segmented layout: its segment sid, and its slots [b, e).
+__device__ __forceinline__ uint4 tile_span(const uint4* __restrict__ seg,
+                                           const uint32_t* __restrict__ tile_seg, uint32_t tile,
+                                           uint32_t& sid, uint32_t& b, uint32_t& e) {
+  sid = tile_seg[tile];
+  const uint4 sg = seg[sid];  // {lookups, output base, first tile, key base}
+  b = sg.y + (tile - sg.z) * (uint32_t)kTile;
+  const uint32_t se = sg.y + sg.x;
+  e = (se - b) < (uint32_t)kTile ? se : b + (uint32_t)kTile;
+  return sg;
+}
+
+// Counts of each digit value of one pass for every tile of the pass's input,
+// digit-major: cnt[d * ntiles + tile], digits of the row (key - key_base).
+// A wave whose 64 keys share one digit (a tile inside a hot row's run) adds
+// them in one step instead of 64 conflicting LDS atomics.  With nst > 0 the
+// kernel also clears nst look-back status words of the later kernels.
 __global__ __launch_bounds__(kThreads) void radix_upsweep(const uint32_t* __restrict__ keys,
-                                                          uint32_t N, uint32_t npass,
+                                                          const uint4* __restrict__ seg,
+                                                          const uint32_t* __restrict__ tile_seg,
+                                                          const uint32_t* __restrict__ ctl,
+                                                          uint32_t shift,
                                                           uint32_t* __restrict__ cnt,
-                                                          uint32_t ntiles, uint32_t* __restrict__ ctl,
+                                                          uint32_t ntiles,
                                                           uint64_t* __restrict__ st, uint64_t nst) {
-  __shared__ uint32_t h[kMaxPass][kThreads / kWave][256];
-  const uint32_t wave = threadIdx.x / kWave;
-  const uint64_t i0 = (uint64_t)blockIdx.x * kTile + (uint64_t)threadIdx.x * kItems;
-  uint32_t k[kItems];
-  if (i0 < N) loadn<kItems>(keys, i0, N, k);
-  for (uint32_t i = threadIdx.x; i < (uint32_t)(kMaxPass * 4 * 256); i += kThreads)
-    (&h[0][0][0])[i] = 0u;
+  __shared__ uint32_t h[kThreads / kWave][256];
+  const uint32_t wave = threadIdx.x / kWave, lane = lane_id();
+  const uint32_t tile = blockIdx.x;
+  const bool live = tile < ctl[kCtlTiles];
+  for (uint32_t i = threadIdx.x; i < (uint32_t)(4 * 256); i += kThreads) (&h[0][0])[i] = 0u;
   __syncthreads();
+  if (live) {
+    uint32_t sid, b, e;
+    const uint4 sg = tile_span(seg, tile_seg, tile, sid, b, e);
+    const uint32_t wb = b + wave * (kTile / 4);
+    uint32_t k[kItems];
 #pragma unroll
-  for (int e = 0; e < kItems; ++e)
-    if (i0 + e < N)
-      for (uint32_t q = 0; q < npass; ++q)
-        atomicAdd(&h[q][wave][(k[e] >> (q * kRadixBits)) & 255u], 1u);
-  __syncthreads();
-  for (uint32_t i = threadIdx.x; i < npass * 256u; i += kThreads) {
-    const uint32_t q = i >> 8, d = i & 255u;
-    cnt[(size_t)i * ntiles + blockIdx.x] = h[q][0][d] + h[q][1][d] + h[q][2][d] + h[q][3][d];
+    for (int r = 0; r < kItems; ++r) {
+      const uint32_t i = wb + (uint32_t)r * kWave + lane;
+      k[r] = i < e ? keys[i] : 0u;
+    }
+#pragma unroll
+    for (int r = 0; r < kItems; ++r) {
+      const bool valid = wb + (uint32_t)r * kWave + lane < e;
+      const uint32_t d = ((k[r] - sg.w) >> shift) & 255u;
+      const uint32_t d0 = __builtin_amdgcn_readfirstlane(d);
+      const uint64_t in = __ballot(valid);
+      if (__ballot(valid && d != d0) == 0) {
+        if (lane == 0 && in != 0) h[wave][d0] += (uint32_t)__popcll(in);
+      } else if (valid) {
+        atomicAdd(&h[wave][d], 1u);
+      }
+    }
   }
-  if (blockIdx.x == 0)
-    for (uint32_t i = threadIdx.x; i < (uint32_t)kCtlHist; i += kThreads) ctl[i] = 0u;
+  __syncthreads();
+  if (live) {
+    const uint32_t d = threadIdx.x;
+    cnt[(size_t)d * ntiles + tile] = h[0][d] + h[1][d] + h[2][d] + h[3][d];
+  }
   const uint64_t stride = (uint64_t)gridDim.x * kThreads;
   for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < nst; i += stride)
     st[i] = 0ull;
 }
 
-// One workgroup per digit d: exclusive scan over the tiles of the pass-0
-// counts of d (in place), and the totals of d for every pass.
+// One workgroup per digit value d: the exclusive prefix over all tiles of the
+// counts of d (in place) and the total of d.  At a segment's first tile the
+// prefix is the count of d in all earlier segments.
 __global__ __launch_bounds__(kThreads) void radix_scan(uint32_t* __restrict__ cnt, uint32_t ntiles,
-                                                       uint32_t npass,
+                                                       const uint32_t* __restrict__ ctl,
                                                        uint32_t* __restrict__ totals) {
   __shared__ uint32_t sh4[4];
   const uint32_t d = blockIdx.x;
-  for (uint32_t q = 0; q < npass; ++q) {
-    uint32_t* row = cnt + (size_t)(q * 256 + d) * ntiles;
-    uint32_t running = 0;
-    for (uint32_t c = 0; c < ntiles; c += kThreads * 4) {
-      uint32_t v[4], sum = 0;
+  const uint32_t nt = ctl[kCtlTiles];
+  uint32_t* row = cnt + (size_t)d * ntiles;
+  uint32_t running = 0;
+  for (uint32_t c = 0; c < nt; c += kThreads * 4) {
+    uint32_t v[4], sum = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t i = c + threadIdx.x * 4 + e;
-        v[e] = i < ntiles ? row[i] : 0u;
-        sum += v[e];
-      }
-      uint32_t total;
-      uint32_t x = block_excl_scan(sum, sh4, total) + running;
-      if (q == 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t i = c + threadIdx.x * 4 + e;
-          if (i < ntiles) row[i] = x;
-          x += v[e];
-        }
-      }
-      running += total;
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t i = c + threadIdx.x * 4 + e;
+      v[e] = i < nt ? row[i] : 0u;
+      sum += v[e];
     }
-    if (threadIdx.x == 0) totals[q * 256 + d] = running;
+    uint32_t total;
+    uint32_t x = block_excl_scan(sum, sh4, total) + running;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t i = c + threadIdx.x * 4 + e;
+      if (i < nt) row[i] = x;
+      x += v[e];
+    }
+    running += total;
   }
+  if (threadIdx.x == 0) totals[d] = running;
 }
 
 
@@ -284,59 +374,66 @@ struct SortPass {
   uint32_t* kout;
   uint32_t* vout;
   float* sout;
-  uint32_t N, shift;
-  const uint32_t* hist;       // 256 digit totals of this pass
-  const uint32_t* tile_excl;  // first pass: per digit and tile, the count in earlier tiles
+  uint32_t shift;
+  const uint4* seg;           // per segment {lookups, output base, first tile, key base}
+  const uint32_t* tile_seg;   // segment of each tile
+  const uint32_t* tiles;      // number of tiles (ctl[kCtlTiles])
+  const uint32_t* totals;     // 256 digit totals of this pass over all segments
+  const uint32_t* tile_excl;  // per digit and tile, the count in earlier tiles
   uint32_t ntiles;
-  uint64_t* st;               // later passes: ntiles x 256 status words of this pass
-  uint64_t* st_next;          // the other status buffer: this tile's row is cleared for the pass after
-  uint32_t* ticket;
-  uint32_t* err;
 };
 
-// Stable scatter of one tile.  The first pass takes the offsets of its tile
-// among the earlier tiles from the scan (LB false); later passes find them by
-// look-back (LB true).  Wave w holds the contiguous 1024 keys
-// [tile + w*1024, tile + (w+1)*1024); in round r lane l holds key
-// tile + w*1024 + r*64 + l, so (wave, round, lane) is the position order and
-// ranking by wave-private digit counters keeps the sort stable.  Keys, bag
-// ids and scales pass through one LDS buffer in turn on their way to their
-// coalesced global stores.
-template <bool SC, bool LB>
+// Stable scatter of one tile to the offsets of the scan: the count of each
+// digit in all earlier tiles, minus the prefix at the segment's first tile,
+// is the count in the earlier tiles of the same segment.  Wave w holds the contiguous 1024
+// slots [b + w*1024, b + (w+1)*1024) of the tile [b, e); in round r lane l
+// holds slot b + w*1024 + r*64 + l, so (wave, round, lane) is the position
+// order and ranking by wave-private digit counters keeps the sort stable.
+// The digit is taken from the row, key - key_base.  Keys, bag ids and scales
+// pass through one LDS buffer in turn on their way to their coalesced global
+// stores.
+template <bool SC>
 __global__ __launch_bounds__(kThreads) void sort_pass_kernel(SortPass p) {
   __shared__ uint32_t s_buf[kTile];
   __shared__ uint32_t wcnt[kThreads / kWave][256];
   __shared__ uint32_t gbase[256];
   __shared__ uint32_t lstart[256];
   __shared__ uint32_t sh4[4];
-  __shared__ uint32_t s_tile;
 
   const uint32_t lane = lane_id(), wave = threadIdx.x / kWave;
+  const uint32_t tile = blockIdx.x;
+  if (tile >= *p.tiles) return;  // the grid is sized for the most tiles segments can need
   for (uint32_t i = threadIdx.x; i < 4 * 256; i += kThreads) (&wcnt[0][0])[i] = 0u;
-  const uint32_t tile = LB ? take_ticket(p.ticket, &s_tile) : blockIdx.x;
-  const uint64_t N = p.N;
-  const uint64_t wbase = (uint64_t)tile * kTile + (uint64_t)wave * (kTile / 4);
+  uint32_t sid, b, e;
+  const uint4 sg = tile_span(p.seg, p.tile_seg, tile, sid, b, e);
+  const uint32_t wbase = b + wave * (kTile / 4);
   // the whole tile is loaded before any ranking
   uint32_t k[kItems], v[kItems], rk[kItems];
   float sc[kItems];
 #pragma unroll
   for (int r = 0; r < kItems; ++r) {
-    const uint64_t i = wbase + (uint64_t)r * kWave + lane;
-    const uint64_t ii = i < N ? i : N - 1;
+    const uint32_t i = wbase + (uint32_t)r * kWave + lane;
+    const uint32_t ii = i < e ? i : e - 1;
     k[r] = p.kin[ii];
     v[r] = p.vin[ii];
     if (SC) sc[r] = p.sin[ii];
   }
   __builtin_amdgcn_sched_barrier(0);
   const uint32_t d_me = threadIdx.x;  // the digit this thread publishes and looks back for
+  // count of d_me in the segments before this one, and in this segment
+  const uint32_t* row = p.tile_excl + (size_t)d_me * p.ntiles;
+  const uint32_t z_next = sg.z + (sg.x + kTile - 1) / kTile;
+  const uint32_t before_seg = row[sg.z];
+  const uint32_t in_seg = (z_next < *p.tiles ? row[z_next] : p.totals[d_me]) - before_seg;
   uint32_t total;
-  const uint32_t digit_excl = block_excl_scan(p.hist[d_me], sh4, total);  // ends with a barrier
+  // segment base plus the digits below d_me (ends with a barrier)
+  const uint32_t digit_excl = sg.y + block_excl_scan(in_seg, sh4, total);
 
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int r = 0; r < kItems; ++r) {
-    const bool valid = wbase + (uint64_t)r * kWave + lane < N;
-    const uint32_t d = (k[r] >> p.shift) & 255u;
+    const bool valid = wbase + (uint32_t)r * kWave + lane < e;
+    const uint32_t d = ((k[r] - sg.w) >> p.shift) & 255u;
     uint64_t peers = __ballot(valid);
 #pragma unroll
     for (int bit = 0; bit < kRadixBits; ++bit) {
@@ -357,41 +454,34 @@ __global__ __launch_bounds__(kThreads) void sort_pass_kernel(SortPass p) {
     wcnt[w][d_me] = cnt;
     cnt += c;
   }
-  uint64_t* mine = p.st + (size_t)tile * 256 + d_me;
-  if (LB) st_publish(mine, (tile == 0 ? kStPre : kStAgg) | cnt);
   const uint32_t ls = block_excl_scan(cnt, sh4, total);
   lstart[d_me] = ls;
   __syncthreads();
   // tile-local slots, keys into LDS while the look-back runs
 #pragma unroll
   for (int r = 0; r < kItems; ++r) {
-    const bool valid = wbase + (uint64_t)r * kWave + lane < N;
-    const uint32_t d = (k[r] >> p.shift) & 255u;
+    const bool valid = wbase + (uint32_t)r * kWave + lane < e;
+    const uint32_t d = ((k[r] - sg.w) >> p.shift) & 255u;
     const uint32_t slot = lstart[d] + wcnt[wave][d] + rk[r];
     rk[r] = (valid && slot < (uint32_t)kTile) ? slot : 0xffffffffu;  // always in range when valid
     if (rk[r] != 0xffffffffu) s_buf[rk[r]] = k[r];
   }
-  uint32_t excl = 0;
-  if (!LB) {
-    excl = p.tile_excl[(size_t)d_me * p.ntiles + tile];
-  } else if (tile > 0) {
-    excl = look_back<8>(p.st, tile, 256, d_me, p.err);
-    st_publish(mine, kStPre | (uint64_t)(uint32_t)(excl + cnt));
-  }
-  gbase[d_me] = digit_excl + excl - ls;  // destination = gbase[digit] + tile slot
+  const uint32_t excl = row[tile];  // count of d_me in all earlier tiles
+  // destination = gbase[digit] + tile slot
+  gbase[d_me] = digit_excl + (excl - before_seg) - ls;
   __syncthreads();
 
-  const uint64_t tbase = (uint64_t)tile * kTile;
-  const uint32_t n = (uint32_t)((N - tbase) < (uint64_t)kTile ? (N - tbase) : (uint64_t)kTile);
+  const uint32_t n = e - b;
+  const uint32_t send = sg.y + sg.x;
   uint32_t dst[kItems];
 #pragma unroll
   for (int r = 0; r < kItems; ++r) {
-    const uint32_t s = threadIdx.x + (uint32_t)r * kThreads;
+    const uint32_t sl = threadIdx.x + (uint32_t)r * kThreads;
     dst[r] = 0xffffffffu;
-    if (s < n) {
-      const uint32_t key = s_buf[s];
-      const uint32_t g = gbase[(key >> p.shift) & 255u] + s;
-      if (g < p.N) {  // always true for consistent digit counts
+    if (sl < n) {
+      const uint32_t key = s_buf[sl];
+      const uint32_t g = gbase[((key - sg.w) >> p.shift) & 255u] + sl;
+      if (g >= sg.y && g < send) {  // always true for consistent digit counts
         dst[r] = g;
         p.kout[g] = key;
       }
@@ -416,8 +506,6 @@ __global__ __launch_bounds__(kThreads) void sort_pass_kernel(SortPass p) {
       if (dst[r] != 0xffffffffu)
         p.sout[dst[r]] = __builtin_bit_cast(float, s_buf[threadIdx.x + (uint32_t)r * kThreads]);
   }
-  // the pass after next uses the other status buffer; nobody reads this row of it now
-  if (LB) p.st_next[(size_t)tile * 256 + d_me] = 0ull;
 }
 
 // --------------------------------------------------- run-length encoding
@@ -668,7 +756,16 @@ hipError_t launch_preprocess(const PrepArgs& p, int /*num_cus*/, hipStream_t s) 
   uint32_t* err = ctl + kCtlErr;
   const bool sc = p.need_scale != 0;
 
-  PrepDev d{p.tables, p.T, p.nb, p.B, p.indices, p.offsets, p.psw, p.N};
+  uint4* seg = reinterpret_cast<uint4*>(ws + L.seg);
+  uint32_t* tile_seg = u32p(L.tile_seg);
+  uint32_t* totals = u32p(L.totals);
+  PrepDev d{p.tables, p.T, p.nb, p.B, p.indices, p.offsets, p.psw, p.N, p.tseg, seg};
+  if (p.itype == IT_I32)
+    TBE_LAUNCH("seg_setup", seg_setup_kernel<int32_t>, dim3(1), dim3(kThreads), s, d, p.order,
+               seg, tile_seg, L.ntiles_max, ctl);
+  else
+    TBE_LAUNCH("seg_setup", seg_setup_kernel<int64_t>, dim3(1), dim3(kThreads), s, d, p.order,
+               seg, tile_seg, L.ntiles_max, ctl);
   const uint64_t nbag = (uint64_t)p.T * (uint64_t)p.B;
   const uint32_t tgrid = (uint32_t)((nbag * 16 + kThreads - 1) / kThreads);
   if (p.itype == IT_I32)
@@ -678,38 +775,26 @@ hipError_t launch_preprocess(const PrepArgs& p, int /*num_cus*/, hipStream_t s) 
     TBE_LAUNCH("transpose", transpose_kernel<int64_t>, dim3(tgrid), dim3(kThreads), s, d,
                u32p(L.key_a), u32p(L.val_a), sc ? f32p(L.sc_a) : nullptr);
 
-  const uint64_t nst = (L.st_end - L.st_sort0) / 8;
-  TBE_LAUNCH("radix_upsweep", radix_upsweep, dim3(L.ntiles), dim3(kThreads), s, u32p(L.key_a),
-             p.N, (uint32_t)L.npass, u32p(L.tile_cnt), L.ntiles, ctl, u64p(L.st_sort0), nst);
-  TBE_LAUNCH("radix_scan", radix_scan, dim3(256), dim3(kThreads), s, u32p(L.tile_cnt), L.ntiles,
-             (uint32_t)L.npass, ctl + kCtlHist);
-
   // ping-pong a -> b -> a ...; the final buffers are b for an odd pass count
+  const uint64_t nst = (L.st_end - L.st_rle) / 8;
   for (int pass = 0; pass < L.npass; ++pass) {
     const bool ab = (pass % 2) == 0;
-    const bool odd = (pass % 2) == 1;  // later passes alternate between two status buffers
     SortPass sp{u32p(ab ? L.key_a : L.key_b), u32p(ab ? L.val_a : L.val_b),
                 f32p(ab ? L.sc_a : L.sc_b),   u32p(ab ? L.key_b : L.key_a),
                 u32p(ab ? L.val_b : L.val_a), f32p(ab ? L.sc_b : L.sc_a),
-                p.N, (uint32_t)(pass * kRadixBits), ctl + kCtlHist + pass * 256,
-                u32p(L.tile_cnt), L.ntiles,
-                u64p(odd ? L.st_sort0 : L.st_sort1), u64p(odd ? L.st_sort1 : L.st_sort0),
-                ctl + kCtlTicket + pass, err};
-    if (pass == 0) {
-      if (sc)
-        TBE_LAUNCH("radix_downsweep", (sort_pass_kernel<true, false>), dim3(L.ntiles),
-                   dim3(kThreads), s, sp);
-      else
-        TBE_LAUNCH("radix_downsweep", (sort_pass_kernel<false, false>), dim3(L.ntiles),
-                   dim3(kThreads), s, sp);
-    } else {
-      if (sc)
-        TBE_LAUNCH("sort_pass", (sort_pass_kernel<true, true>), dim3(L.ntiles), dim3(kThreads),
-                   s, sp);
-      else
-        TBE_LAUNCH("sort_pass", (sort_pass_kernel<false, true>), dim3(L.ntiles), dim3(kThreads),
-                   s, sp);
-    }
+                (uint32_t)(pass * kRadixBits), seg, tile_seg, ctl + kCtlTiles,
+                totals, u32p(L.tile_cnt), L.ntiles_max};
+    TBE_LAUNCH("radix_upsweep", radix_upsweep, dim3(L.ntiles_max), dim3(kThreads), s, sp.kin,
+               seg, tile_seg, ctl, sp.shift, u32p(L.tile_cnt), L.ntiles_max,
+               u64p(L.st_rle), pass == 0 ? nst : (uint64_t)0);
+    TBE_LAUNCH("radix_scan", radix_scan, dim3(256), dim3(kThreads), s, u32p(L.tile_cnt),
+               L.ntiles_max, ctl, totals);
+    if (sc)
+      TBE_LAUNCH("radix_downsweep", sort_pass_kernel<true>, dim3(L.ntiles_max), dim3(kThreads),
+                 s, sp);
+    else
+      TBE_LAUNCH("radix_downsweep", sort_pass_kernel<false>, dim3(L.ntiles_max), dim3(kThreads),
+                 s, sp);
   }
   const uint32_t* skey = u32p(L.final_in_b ? L.key_b : L.key_a);
   const uint32_t* sbag = u32p(L.final_in_b ? L.val_b : L.val_a);

@@ -35,11 +35,12 @@ struct tbe_plan {
   std::vector<uint32_t> key_base, col;
   uint32_t dtot;
   uint64_t sum_rows;
-  int key_bits;
+  int row_bits;  // bits of the largest table's row range: the radix passes sort rows
   std::vector<Bucket> buckets;
   uint32_t pstride;
   TableDev* d_tables;
   uint32_t* d_order;
+  uint32_t* d_tseg;
   uint32_t* d_bkb;
   void* d_mem;
   int num_cus;
@@ -82,7 +83,8 @@ WsLayout layout(const tbe_plan* P, int64_t N) {
   L.max_long = (uint32_t)(n / kLongRun + 1);
   L.max_chunks = (uint32_t)(n / kChunk + L.max_long + 1);
   L.pstride = P->pstride;
-  L.npass = std::max(1, (P->key_bits + kRadixBits - 1) / kRadixBits);
+  L.ntiles_max = L.ntiles + (uint32_t)P->T;
+  L.npass = std::max(1, (P->row_bits + kRadixBits - 1) / kRadixBits);
   L.final_in_b = L.npass % 2;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -97,13 +99,14 @@ WsLayout layout(const tbe_plan* P, int64_t N) {
   L.sc_a = take(n * 4);
   L.sc_b = take(n * 4);
   L.ctl = take((size_t)kCtlWords * 4);
-  L.tile_cnt = take((size_t)L.npass * 256 * L.ntiles * 4);
-  L.st_sort0 = off;
-  L.st_sort1 = L.st_sort0 + (size_t)L.ntiles * 256 * 8;
-  L.st_rle = L.st_sort1 + (size_t)L.ntiles * 256 * 8;
+  L.seg = take((size_t)P->T * 16);
+  L.tile_seg = take((size_t)L.ntiles_max * 4);
+  L.totals = take(256 * 4);
+  L.tile_cnt = take((size_t)256 * L.ntiles_max * 4);
+  L.st_rle = off;
   L.st_cls = L.st_rle + (size_t)L.ntiles * 8;
   L.st_end = L.st_cls + (size_t)L.ncls_tiles * kClsStride * 8;
-  take(L.st_end - L.st_sort0);
+  take(L.st_end - L.st_rle);
   L.run_start = take((n + 1) * 4);
   L.run_key = take(n * 4);
   L.single_task = take(n * 16);
@@ -213,7 +216,7 @@ PrepArgs prep_args(const tbe_plan* P, int64_t B, int32_t itype, const void* indi
   a.N = (uint32_t)N;
   a.ws = reinterpret_cast<uint8_t*>(ws);
   a.L = L;
-  a.key_bits = P->key_bits;
+  a.tseg = P->d_tseg;
   return a;
 }
 
@@ -347,7 +350,8 @@ int tbe_plan_create(tbe_plan** out, int32_t T, const int64_t* rows, const int32_
   P->pooling.assign(pooling, pooling + T);
   P->sum_rows = sum_rows;
   P->dtot = (uint32_t)dtot;
-  P->key_bits = sum_rows <= 1 ? 0 : ilog2(sum_rows);
+  P->row_bits = 0;
+  for (int t = 0; t < T; ++t) P->row_bits = std::max(P->row_bits, ilog2((uint64_t)rows[t]));
 
   // buckets by next_pow2(D), ascending width; tables keep ascending id inside a bucket
   std::vector<uint32_t> widths;
@@ -408,13 +412,18 @@ int tbe_plan_create(tbe_plan** out, int32_t T, const int64_t* rows, const int32_
   }
   bkb[nb] = (uint32_t)std::min<uint64_t>(sum_rows, 0xffffffffull);
 
-  // one device allocation: tables | order | bucket key bounds | bucket table lists
+  // segment of each table: its position in key order
+  std::vector<uint32_t> tseg(T);
+  for (uint32_t s = 0; s < (uint32_t)T; ++s) tseg[order[s]] = s;
+
+  // one device allocation: tables | order | segments | bucket key bounds | bucket table lists
   const size_t sz_td = align_up(sizeof(TableDev) * T);
   const size_t sz_order = align_up(4 * (size_t)T);
+  const size_t sz_tseg = align_up(4 * (size_t)T);
   const size_t sz_bkb = align_up(4 * (size_t)(nb + 1));
   const size_t sz_lists = align_up(4 * (size_t)T);
   void* mem = nullptr;
-  if (hipMalloc(&mem, sz_td + sz_order + sz_bkb + sz_lists) != hipSuccess) {
+  if (hipMalloc(&mem, sz_td + sz_order + sz_tseg + sz_bkb + sz_lists) != hipSuccess) {
     delete P;
     return TBE_E_ALLOC;
   }
@@ -422,11 +431,14 @@ int tbe_plan_create(tbe_plan** out, int32_t T, const int64_t* rows, const int32_
   P->d_mem = mem;
   P->d_tables = reinterpret_cast<TableDev*>(base);
   P->d_order = reinterpret_cast<uint32_t*>(base + sz_td);
-  P->d_bkb = reinterpret_cast<uint32_t*>(base + sz_td + sz_order);
-  uint32_t* lists = reinterpret_cast<uint32_t*>(base + sz_td + sz_order + sz_bkb);
+  P->d_tseg = reinterpret_cast<uint32_t*>(base + sz_td + sz_order);
+  P->d_bkb = reinterpret_cast<uint32_t*>(base + sz_td + sz_order + sz_tseg);
+  uint32_t* lists = reinterpret_cast<uint32_t*>(base + sz_td + sz_order + sz_tseg + sz_bkb);
   bool ok = hipMemcpy(P->d_tables, td.data(), sizeof(TableDev) * T, hipMemcpyHostToDevice) ==
                 hipSuccess &&
             hipMemcpy(P->d_order, order.data(), 4 * (size_t)T, hipMemcpyHostToDevice) ==
+                hipSuccess &&
+            hipMemcpy(P->d_tseg, tseg.data(), 4 * (size_t)T, hipMemcpyHostToDevice) ==
                 hipSuccess &&
             hipMemcpy(P->d_bkb, bkb.data(), 4 * (size_t)(nb + 1), hipMemcpyHostToDevice) ==
                 hipSuccess &&

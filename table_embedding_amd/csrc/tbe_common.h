@@ -17,7 +17,7 @@ constexpr int kLongRun = 256;       // SL >= 256 takes the chunked long-run path
 constexpr int kTinyRun = 32;        // short runs below this are owned by a lane subgroup
 constexpr int kChunk = 256;         // lookups per long-run chunk
 constexpr int kRadixBits = 8;
-constexpr int kMaxPass = 4;         // 32-bit keys: at most four 8-bit digits
+constexpr int kMaxPass = 4;         // 32-bit rows: at most four 8-bit digits
 constexpr int kMaxTables = 4096;
 
 enum : int { WD_F32 = 0, WD_F16 = 1, WD_BF16 = 2 };
@@ -85,16 +85,21 @@ __device__ __forceinline__ void set_pick(const BucketSet& S, BucketDev& bk, uint
 struct WsLayout {
   size_t key_a, key_b, val_a, val_b, sc_a, sc_b;  // sort ping-pong: key, bag id, scale
   size_t ctl;                                      // control block, kCtlWords uint32
-  size_t tile_cnt;  // npass x 256 x ntiles per-tile digit counts (pass 0: exclusive prefixes)
-  // look-back status words (uint64), contiguous in [st_sort0, st_end): two
-  // sort-pass buffers (ntiles x 256 each), the run-length pass (ntiles) and
-  // the classification pass (ncls_tiles x kClsStride)
-  size_t st_sort0, st_sort1, st_rle, st_cls, st_end;
+  size_t seg;       // T uint4 {lookups, output base, first tile, key base}, tables in key order
+  size_t tile_seg;  // ntiles_max uint32: segment of each sort tile
+  size_t totals;    // 256 digit totals of the current pass
+  size_t tile_cnt;  // 256 x ntiles_max per-tile digit counts of the current pass, then their
+                    // exclusive prefixes over all tiles
+  // look-back status words (uint64), contiguous in [st_rle, st_end): the
+  // run-length pass (ntiles) and the classification pass (ncls_tiles x
+  // kClsStride)
+  size_t st_rle, st_cls, st_end;
   size_t run_start, run_key;
   size_t single_task, tiny_task, med_task, long_task, long_cbeg, remaining, chunk_task;
   size_t partial, counters;
   size_t total;
-  uint32_t ntiles;          // ceil(N / kTile)
+  uint32_t ntiles;          // ceil(N / kTile): tiles of the run-length pass
+  uint32_t ntiles_max;      // ceil(N / kTile) + T: bound on the sort tiles of the segments
   uint32_t ncls_tiles;      // ceil(N / kClsTile): runs are at most N
   uint32_t max_tiny;        // capacity of the 2 <= SL < 32 list
   uint32_t max_med;         // capacity of the medium short-run list
@@ -111,11 +116,11 @@ struct WsLayout {
 constexpr int kNumLists = 5;
 constexpr int kCntU = 0, kCntSingle = 1, kCntBegins = 1 + kNumLists;
 
-// Control block of the preprocessing: tile tickets (sort passes, then the
-// run-length and classification passes), the look-back error flag and the
-// digit totals of every sort pass.
-constexpr int kCtlTicket = 0, kCtlErr = 8, kCtlHist = 16;
-constexpr int kCtlWords = kCtlHist + kMaxPass * 256;
+// Control block of the preprocessing: tile tickets (words kCtlTicket +
+// kMaxPass and + kMaxPass + 1: the run-length and classification passes),
+// the look-back error flag and the number of sort tiles of the segments.
+constexpr int kCtlTicket = 0, kCtlErr = 8, kCtlTiles = 9;
+constexpr int kCtlWords = 16;
 constexpr int kClsStride = 8;  // status words per classification tile (five used)
 
 // ------------------------------------------------------------- device helpers
@@ -275,7 +280,7 @@ struct PrepArgs {
   uint32_t N;
   uint8_t* ws;
   const WsLayout* L;                 // host pointer (layout), kernels get offsets by value
-  int key_bits;
+  const uint32_t* tseg;              // segment (position in key order) of each table
 };
 
 struct BwdArgs {
