@@ -114,8 +114,10 @@ def byte_model(spec, st, hist_path):
     N = sum(s["n"] for s in st)
     U = sum(s["U"] for s in st)
     ntiles = -(-N // 4096)
-    key_bits = max(1, int(np.ceil(np.log2(max(2, sum(spec.rows))))))
-    npass = max(1, -(-key_bits // 8))
+    # radix passes sort the rows of each table's segment: bits of the largest table
+    row_bits = max(int(np.ceil(np.log2(r))) if r > 1 else 0 for r in spec.rows)
+    npass = max(1, -(-row_bits // 8))
+    stiles = sum(-(-s["n"] // 4096) for s in st)  # sort tiles: one table per tile
     out_bytes = B * spec.dtot * 4
     G_bytes = B * spec.dtot * 4
     comp, logi = {}, {}
@@ -132,17 +134,17 @@ def byte_model(spec, st, hist_path):
     n = {c: sum(s["n_" + c] for s in st) for c, _, _ in SL_CLASSES}
     n_chunks = sum(s["chunks"] for s in st)
     ncls = -(-N // 2048)
-    st_words = 2 * ntiles * 256 + ntiles + ncls * 8  # look-back status words
+    nrle = -(-N // 16384)  # run-length tiles
+    st_words = nrle + ncls * 8  # look-back status words of rle and classify
+    comp["seg_setup"] = 2 * T * si + 16 * T + 4 * stiles
     comp["transpose"] = N * (si + 4 * psi) + (T * B + 1) * si + N * rec
-    # one read of the keys gives the per-tile digit counts of every pass; the
-    # look-back status words are cleared here
-    comp["radix_upsweep"] = 4 * N + npass * 256 * 4 * ntiles + 8 * st_words
-    comp["radix_scan"] = npass * 256 * 4 * ntiles + 256 * 4 * ntiles
-    # per pass: the records read and written once; the look-back passes also
-    # publish each tile's 256 status words twice and clear a row for later
-    comp["radix_downsweep"] = 2 * rec * N + 256 * 4 * ntiles
-    comp["sort_pass"] = (npass - 1) * (2 * rec * N + 3 * 8 * 256 * ntiles)
-    comp["rle"] = 4 * N + 8 * U + 4 + 16 * ntiles
+    # per pass: the keys read once for the digit counts (the first pass also
+    # clears the status words); the counts scanned in place; the records read
+    # and written once by the scatter, plus each tile's 256 prefixes
+    comp["radix_upsweep"] = npass * (4 * N + 256 * 4 * stiles) + 8 * st_words
+    comp["radix_scan"] = npass * 2 * 256 * 4 * stiles
+    comp["radix_downsweep"] = npass * (2 * rec * N + 256 * 4 * stiles)
+    comp["rle"] = 4 * N + 8 * U + 4 + 16 * nrle
     comp["classify"] = (8 * U + 4 + 4 * n["single"] + 16 * (U + n_chunks) + 8 * n["long"]
                         + 16 * 8 * ncls)
     for k in list(comp):

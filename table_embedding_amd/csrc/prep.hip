@@ -509,7 +509,10 @@ __global__ __launch_bounds__(kThreads) void sort_pass_kernel(SortPass p) {
 }
 
 // --------------------------------------------------- run-length encoding
-// Blocked layout: thread h of a tile owns sorted slots [tile + 16h, tile + 16h + 16).
+// A tile is kRleGroups consecutive groups of 4096 sorted slots; in group g
+// thread h owns slots [tile + g*4096 + 16h, ... + 16), so every load is
+// coalesced, and runs are numbered group by group in slot order.  Four
+// groups per tile make the look-back chain a quarter as long.
 
 __global__ __launch_bounds__(kThreads) void rle_kernel(const uint32_t* __restrict__ key, uint32_t N,
                                                        uint32_t ntiles, uint32_t* ticket,
@@ -520,23 +523,32 @@ __global__ __launch_bounds__(kThreads) void rle_kernel(const uint32_t* __restric
   __shared__ uint32_t sh4[4];
   __shared__ uint32_t s_tile, s_excl;
   const uint32_t tile = take_ticket(ticket, &s_tile);
-  const uint64_t i0 = (uint64_t)tile * kTile + (uint64_t)threadIdx.x * kItems;
-  uint32_t k[kItems];
-  uint32_t m = 0;
-  if (i0 < N) {
-    const uint32_t prev0 = i0 == 0 ? 0u : key[i0 - 1];
-    loadn<kItems>(key, i0, N, k);
-    __builtin_amdgcn_sched_barrier(0);
-    uint32_t prev = prev0;
+  uint32_t k[kRleGroups][kItems];
+  uint32_t m[kRleGroups];  // run heads among this thread's 16 slots of each group
 #pragma unroll
-    for (int e = 0; e < kItems; ++e) {
-      const uint64_t i = i0 + e;
-      if (i < N && (i == 0 || k[e] != prev)) m |= 1u << e;
-      prev = k[e];
+  for (int g = 0; g < kRleGroups; ++g) {
+    const uint64_t i0 = (uint64_t)tile * kRleTile + (uint64_t)g * kTile +
+                        (uint64_t)threadIdx.x * kItems;
+    m[g] = 0;
+    if (i0 < N) {
+      const uint32_t prev0 = i0 == 0 ? 0u : key[i0 - 1];
+      loadn<kItems>(key, i0, N, k[g]);
+      uint32_t prev = prev0;
+#pragma unroll
+      for (int e = 0; e < kItems; ++e) {
+        const uint64_t i = i0 + e;
+        if (i < N && (i == 0 || k[g][e] != prev)) m[g] |= 1u << e;
+        prev = k[g][e];
+      }
     }
   }
-  uint32_t total;
-  const uint32_t local = block_excl_scan(__popc(m), sh4, total);
+  uint32_t local[kRleGroups], total = 0;
+#pragma unroll
+  for (int g = 0; g < kRleGroups; ++g) {
+    uint32_t tg;
+    local[g] = total + block_excl_scan(__popc(m[g]), sh4, tg);
+    total += tg;
+  }
   if (threadIdx.x == 0) {
     const uint32_t excl = publish_and_look_back<16>(st, tile, 1, 0, total, err);
     s_excl = excl;
@@ -546,13 +558,18 @@ __global__ __launch_bounds__(kThreads) void rle_kernel(const uint32_t* __restric
     }
   }
   __syncthreads();
-  uint32_t u = s_excl + local;
 #pragma unroll
-  for (int e = 0; e < kItems; ++e) {
-    if (m & (1u << e)) {
-      run_start[u] = (uint32_t)(i0 + e);
-      run_key[u] = k[e];
-      ++u;
+  for (int g = 0; g < kRleGroups; ++g) {
+    const uint64_t i0 = (uint64_t)tile * kRleTile + (uint64_t)g * kTile +
+                        (uint64_t)threadIdx.x * kItems;
+    uint32_t u = s_excl + local[g];
+#pragma unroll
+    for (int e = 0; e < kItems; ++e) {
+      if (m[g] & (1u << e)) {
+        run_start[u] = (uint32_t)(i0 + e);
+        run_key[u] = k[g][e];
+        ++u;
+      }
     }
   }
 }
@@ -798,7 +815,7 @@ hipError_t launch_preprocess(const PrepArgs& p, int /*num_cus*/, hipStream_t s) 
   }
   const uint32_t* skey = u32p(L.final_in_b ? L.key_b : L.key_a);
   const uint32_t* sbag = u32p(L.final_in_b ? L.val_b : L.val_a);
-  TBE_LAUNCH("rle", rle_kernel, dim3(L.ntiles), dim3(kThreads), s, skey, p.N, L.ntiles,
+  TBE_LAUNCH("rle", rle_kernel, dim3(L.nrle_tiles), dim3(kThreads), s, skey, p.N, L.nrle_tiles,
              ctl + kCtlTicket + kMaxPass, u64p(L.st_rle), err, u32p(L.counters),
              u32p(L.run_start), u32p(L.run_key));
 

@@ -77,6 +77,7 @@ WsLayout layout(const tbe_plan* P, int64_t N) {
   WsLayout L{};
   const uint64_t n = (uint64_t)N;
   L.ntiles = (uint32_t)((n + kTile - 1) / kTile);
+  L.nrle_tiles = (uint32_t)((n + kRleTile - 1) / kRleTile);
   L.ncls_tiles = (uint32_t)((n + kClsTile - 1) / kClsTile);
   L.max_tiny = (uint32_t)(n / 2 + 1);
   L.max_med = (uint32_t)(n / kTinyRun + 1);
@@ -104,7 +105,7 @@ WsLayout layout(const tbe_plan* P, int64_t N) {
   L.totals = take(256 * 4);
   L.tile_cnt = take((size_t)256 * L.ntiles_max * 4);
   L.st_rle = off;
-  L.st_cls = L.st_rle + (size_t)L.ntiles * 8;
+  L.st_cls = L.st_rle + (size_t)L.nrle_tiles * 8;
   L.st_end = L.st_cls + (size_t)L.ncls_tiles * kClsStride * 8;
   take(L.st_end - L.st_rle);
   L.run_start = take((n + 1) * 4);

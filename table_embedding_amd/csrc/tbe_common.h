@@ -13,6 +13,8 @@ constexpr int kThreads = 256;       // every kernel runs 256-thread workgroups (
 constexpr int kWave = 64;
 constexpr int kTile = 4096;         // keys per workgroup in the sort / run-length passes
 constexpr int kClsTile = 2048;      // runs per workgroup in the classification pass
+constexpr int kRleGroups = 4;       // 4096-key groups per run-length tile
+constexpr int kRleTile = kRleGroups * kTile;
 constexpr int kLongRun = 256;       // SL >= 256 takes the chunked long-run path
 constexpr int kTinyRun = 32;        // short runs below this are owned by a lane subgroup
 constexpr int kChunk = 256;         // lookups per long-run chunk
@@ -91,14 +93,15 @@ struct WsLayout {
   size_t tile_cnt;  // 256 x ntiles_max per-tile digit counts of the current pass, then their
                     // exclusive prefixes over all tiles
   // look-back status words (uint64), contiguous in [st_rle, st_end): the
-  // run-length pass (ntiles) and the classification pass (ncls_tiles x
+  // run-length pass (nrle_tiles) and the classification pass (ncls_tiles x
   // kClsStride)
   size_t st_rle, st_cls, st_end;
   size_t run_start, run_key;
   size_t single_task, tiny_task, med_task, long_task, long_cbeg, remaining, chunk_task;
   size_t partial, counters;
   size_t total;
-  uint32_t ntiles;          // ceil(N / kTile): tiles of the run-length pass
+  uint32_t ntiles;          // ceil(N / kTile)
+  uint32_t nrle_tiles;      // ceil(N / kRleTile): tiles of the run-length pass
   uint32_t ntiles_max;      // ceil(N / kTile) + T: bound on the sort tiles of the segments
   uint32_t ncls_tiles;      // ceil(N / kClsTile): runs are at most N
   uint32_t max_tiny;        // capacity of the 2 <= SL < 32 list
