@@ -320,15 +320,24 @@ def main():
     torch.cuda.synchronize()
     ms_prof = e0.elapsed_time(e1) / args.steps
     prof = te.tbe_prof_read()
+    # what the two events around a launch cost by themselves (dispatch latency
+    # included): empty kernels bracketed the same way
+    te.tbe_prof_calibrate(200)
+    torch.cuda.synchronize()
+    n_e, t_e = te.tbe_prof_read()["empty"]
+    bracket_us = 1000 * t_e / n_e
     te.tbe_prof_enable(False)
 
     st = workload_stats(spec, off, idx)
     comp, logi = byte_model(spec, st, hist)
     kernels = {}
     for k, (n, tot) in prof.items():
-        per_step_ms = tot / args.steps
+        # kernel time = bracketed time minus the bracket's own cost
+        kern_us = max(1000 * tot / n - bracket_us, 1e-3)
+        per_step_ms = kern_us * n / args.steps / 1000
         kernels[k] = {"launches_per_step": n / args.steps, "ms_per_step": round(per_step_ms, 5),
-                      "avg_launch_us": round(1000 * tot / n, 3),
+                      "avg_launch_us": round(kern_us, 3),
+                      "avg_bracketed_us": round(1000 * tot / n, 3),
                       "compulsory_bytes_per_step": int(comp.get(k, 0)),
                       "gbs_compulsory": round(comp.get(k, 0) / (per_step_ms * 1e6), 1)}
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
@@ -375,9 +384,12 @@ def main():
                 "logical_bytes_per_step": int(step_logi),
                 "effective_gbs_logical": round(step_logi / (ms * 1e6), 1)},
         "kernel_timing": {"method": "HIP events around every launch on the stream it is "
-                                    "launched on, over a second pass of the same steps (with "
-                                    "the overlapped schedule a kernel's span includes time "
-                                    "shared with kernels on other streams)",
+                                    "launched on, over a second pass of the same steps; "
+                                    "avg_launch_us is the bracketed time minus the average "
+                                    "bracketed time of an empty kernel (with the overlapped "
+                                    "schedule a kernel's span includes time shared with "
+                                    "kernels on other streams)",
+                          "bracket_us": round(bracket_us, 3),
                           "ms_per_step_with_events": round(ms_prof, 5)},
         "kernels": kernels,
         "cpu_baseline": None,

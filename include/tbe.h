@@ -206,6 +206,11 @@ int tbe_backward_rowwise_adagrad(const tbe_plan* plan, int64_t B, int32_t itype,
 int tbe_prof_enable(int enable);
 int tbe_prof_read(int32_t max_kernels, char* names, int64_t* launches, double* total_ms,
                   int32_t* count);
+/* Enqueue `launches` empty kernels (one 64-thread workgroup each) on stream,
+ * bracketed like every library launch while timing is enabled, under the
+ * family name "empty": their average is the cost of the bracket itself
+ * (dispatch latency included), to subtract from the other families'. */
+int tbe_prof_calibrate(int32_t launches, void* stream);
 
 /* Static text for a status code. */
 const char* tbe_status_string(int status);

@@ -17,7 +17,8 @@ from ._lib import (  # noqa: F401
     TBE_E_ARG, TBE_E_HIP, TBE_E_RANGE, TBE_E_UNSUPPORTED, TBE_E_WORKSPACE, TBE_F16, TBE_F32,
     TBE_FWD_BALANCE, TBE_FWD_NO_BALANCE, TBE_FWD_NO_HIST, TBE_FWD_REQUIRE_HIST, TBE_I32, TBE_I64, TBE_MEAN, TBE_OK, TBE_SUM,
     TBEError, lib, tbe_backward_rowwise_adagrad, tbe_forward, tbe_plan_create,
-    tbe_plan_destroy, tbe_plan_key_bases, tbe_preprocess, tbe_prof_enable, tbe_prof_read,
+    tbe_plan_destroy, tbe_plan_key_bases, tbe_preprocess, tbe_prof_calibrate, tbe_prof_enable,
+    tbe_prof_read,
     tbe_status_string,
     tbe_workspace_size, tbe_workspace_views)
 

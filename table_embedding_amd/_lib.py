@@ -29,7 +29,7 @@ TBE_BWD_PREPROCESSED, TBE_BWD_FUSED_LONG, TBE_BWD_CONCURRENT = 0x1, 0x2, 0x4
 EXPORTS = ("tbe_plan_create", "tbe_plan_destroy", "tbe_plan_key_bases", "tbe_workspace_size",
            "tbe_workspace_views", "tbe_forward", "tbe_preprocess",
            "tbe_backward_rowwise_adagrad", "tbe_prof_enable", "tbe_prof_read",
-           "tbe_status_string")
+           "tbe_prof_calibrate", "tbe_status_string")
 TBE_PROF_NAME_LEN = 32
 
 WDTYPE_OF_TORCH = {torch.float32: TBE_F32, torch.float16: TBE_F16, torch.bfloat16: TBE_BF16}
@@ -74,6 +74,7 @@ def lib() -> C.CDLL:
                                                    vp, vp]
         L.tbe_prof_enable.argtypes = [C.c_int]
         L.tbe_prof_read.argtypes = [i32, vp, vp, vp, C.POINTER(i32)]
+        L.tbe_prof_calibrate.argtypes = [i32, vp]
         L.tbe_status_string.argtypes = [C.c_int]
         L.tbe_status_string.restype = C.c_char_p
         for n in EXPORTS[:-1]:  # every entry point but the status text returns a status
@@ -209,6 +210,10 @@ def tbe_backward_rowwise_adagrad(plan, B: int, indices, offsets, num_lookups: in
 
 def tbe_prof_enable(enable: bool) -> None:
     _check("tbe_prof_enable", lib().tbe_prof_enable(1 if enable else 0))
+
+
+def tbe_prof_calibrate(launches: int, stream=None) -> None:
+    _check("tbe_prof_calibrate", lib().tbe_prof_calibrate(int(launches), _stream(stream)))
 
 
 def tbe_prof_read(max_kernels: int = 64) -> dict:

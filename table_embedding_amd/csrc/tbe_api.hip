@@ -228,6 +228,8 @@ struct ProfRec {
   hipEvent_t start, stop;
 };
 
+__global__ void empty_kernel() {}
+
 std::atomic<bool> g_prof_on{false};
 std::mutex g_prof_mu;
 std::vector<ProfRec> g_prof_recs;
@@ -308,6 +310,14 @@ int tbe_prof_read(int32_t max_kernels, char* names, int64_t* launches, double* t
   }
   *count = (int32_t)keys.size();
   return rc;
+}
+
+int tbe_prof_calibrate(int32_t launches, void* stream) {
+  if (launches < 0) return TBE_E_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  for (int32_t i = 0; i < launches; ++i)
+    TBE_LAUNCH("empty", empty_kernel, dim3(1), dim3(64), s);
+  return hipGetLastError() == hipSuccess ? TBE_OK : TBE_E_HIP;
 }
 
 const char* tbe_status_string(int s) {
