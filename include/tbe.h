@@ -89,6 +89,8 @@ extern "C" {
 #define TBE_BWD_PREPROCESSED 0x1u  /* the workspace already holds tbe_preprocess of these inputs */
 #define TBE_BWD_FUSED_LONG 0x2u    /* long runs: fused fence + countdown instead of a second launch */
 #define TBE_BWD_CONCURRENT 0x4u    /* run classes on three streams (fork from and join into `stream`) */
+#define TBE_BWD_ORDER_CHUNKS 0x8u  /* always walk each table's chunks in bag order (see below) */
+#define TBE_BWD_NO_ORDER_CHUNKS 0x10u /* never: walk chunks in list order */
 
 typedef struct tbe_plan tbe_plan;
 
@@ -111,6 +113,8 @@ typedef struct {
   size_t long_task;    /* n_long uint32x4 {start, len, row, table}: runs with SL >= 256 */
   size_t long_cbeg;    /* n_long first chunk index of each long run */
   size_t chunk_task;   /* n_chunks uint32x4 {start, len, table, long index}: 256-lookup chunks */
+  size_t chunk_perm;   /* n_chunks uint32: chunk list position taken at each walk position when
+                          the backward walks chunks in bag order (written by the backward) */
   size_t counters;     /* uint32 {U, n_single, n_tiny, n_medium, n_long, n_chunks, then for
                           each of the five lists its nb+1 per-D-bucket begins} */
   size_t prep_error;   /* uint32, 0 after a good preprocessing; nonzero if a cross-workgroup
@@ -187,7 +191,13 @@ int tbe_preprocess(const tbe_plan* plan, int64_t B, int32_t itype, const void* i
  * into `stream` before it returns: work enqueued later on `stream` sees
  * every update, and the results are bit-identical to the one-stream order.
  * Calls that share a plan enqueue this fork and join one at a time (a
- * host-side lock). */
+ * host-side lock).
+ * Chunk walk order: the chunks of a table that one XCD takes read about one
+ * eighth of the table's grad_out rows; walking them by the bag of their first
+ * lookup keeps the rows in use within that XCD's L2.  This is done when
+ * grad_out (B x sum D x 4 bytes) exceeds 256 MiB, or always with
+ * TBE_BWD_ORDER_CHUNKS, never with TBE_BWD_NO_ORDER_CHUNKS (both: TBE_E_ARG); the order changes
+ * no result bit. */
 int tbe_backward_rowwise_adagrad(const tbe_plan* plan, int64_t B, int32_t itype,
                                  const void* indices, const void* offsets, int64_t num_lookups,
                                  const float* per_sample_weights, const float* grad_out, float lr,

@@ -25,6 +25,7 @@ TBE_I32, TBE_I64 = 0, 1
 TBE_SUM, TBE_MEAN = 0, 1
 TBE_FWD_NO_HIST, TBE_FWD_REQUIRE_HIST, TBE_FWD_BALANCE, TBE_FWD_NO_BALANCE = 0x1, 0x2, 0x4, 0x8
 TBE_BWD_PREPROCESSED, TBE_BWD_FUSED_LONG, TBE_BWD_CONCURRENT = 0x1, 0x2, 0x4
+TBE_BWD_ORDER_CHUNKS, TBE_BWD_NO_ORDER_CHUNKS = 0x8, 0x10
 
 EXPORTS = ("tbe_plan_create", "tbe_plan_destroy", "tbe_plan_key_bases", "tbe_workspace_size",
            "tbe_workspace_views", "tbe_forward", "tbe_preprocess",
@@ -46,7 +47,8 @@ class WsViews(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in ("sorted_key", "sorted_bag",
                                            "sorted_scale", "run_start", "run_key", "single_task", "tiny_task",
                                            "medium_task", "long_task", "long_cbeg",
-                                           "chunk_task", "counters", "prep_error", "total")] + [
+                                           "chunk_task", "chunk_perm", "counters", "prep_error",
+                                           "total")] + [
         ("num_buckets", C.c_int32)]
 
 

@@ -453,6 +453,71 @@ __device__ __forceinline__ void chunk_walk(uint32_t lb, uint32_t lg, uint32_t be
   step = 8u * nx;
 }
 
+// Chunk order.  The chunks of one table on one XCD read that XCD's eighth of
+// the table's grad_out rows.  Walked in list order (run after run) the
+// workgroups of an XCD sweep the whole eighth at once, more than its L2 holds;
+// ordered by the bag of their first lookup they sweep it front to back, and
+// the rows in reach at a time are few.  One workgroup per (table, residue mod
+// 8) counting-sorts that class's positions by kChunkBins bins of the first
+// bag and writes the permutation chunk_perm (positions of one bin in any
+// order: the order changes no result, since a chunk's partial goes to its own
+// slot and is summed in chunk order).  Chunk lists are in ascending table
+// order inside a bucket, so the table's positions are found by binary search.
+constexpr uint32_t kChunkBins = 256;
+
+__global__ __launch_bounds__(kThreads) void chunk_order_kernel(BwdArgs a) {
+  __shared__ uint32_t hist[kChunkBins];
+  __shared__ uint32_t sh4[4];
+  const uint32_t t = blockIdx.x >> 3, x = blockIdx.x & 7u;
+  if (t >= a.T) return;
+  const uint32_t bucket = a.tables[t].bucket;
+  const uint32_t bb = list_begin(a, 4, bucket);
+  const uint32_t be = min(list_begin(a, 4, bucket + 1), a.max_chunks);
+  auto lower = [&](uint32_t v) {  // first position in [bb, be) whose table is >= v
+    uint32_t lo = bb, hi = be;
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if (a.chunk_task[mid].z < v) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+  };
+  const uint32_t cs = lower(t), ce = lower(t + 1);
+  const uint32_t first = cs + ((x - cs) & 7u);  // first position of residue x
+  if (first >= ce) return;
+  const uint32_t n = (ce - first + 7u) / 8u;
+  const int64_t tB = (int64_t)t * a.B;
+  auto bin_of = [&](uint32_t c) {
+    const uint32_t st = a.chunk_task[c].x;
+    const int64_t j = (st < a.N ? (int64_t)a.sorted_bag[st] : tB) - tB;
+    const uint64_t b = (uint64_t)(j < 0 ? 0 : j) * kChunkBins / (uint64_t)(a.B > 0 ? a.B : 1);
+    return (uint32_t)(b < kChunkBins ? b : kChunkBins - 1);
+  };
+  hist[threadIdx.x] = 0u;
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < n; i += kThreads) atomicAdd(&hist[bin_of(first + 8u * i)], 1u);
+  __syncthreads();
+  {  // exclusive scan of the bins (one per thread)
+    const uint32_t v = hist[threadIdx.x];
+    uint32_t incl = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint32_t y = __shfl_up(incl, o, kWave);
+      if (lane_id() >= (uint32_t)o) incl += y;
+    }
+    if (lane_id() == kWave - 1) sh4[threadIdx.x / kWave] = incl;
+    __syncthreads();
+    uint32_t wbase = 0;
+    for (uint32_t w = 0; w < threadIdx.x / kWave; ++w) wbase += sh4[w];
+    hist[threadIdx.x] = wbase + incl - v;
+  }
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < n; i += kThreads) {
+    const uint32_t c = first + 8u * i;
+    const uint32_t r = atomicAdd(&hist[bin_of(c)], 1u);
+    a.chunk_perm[first + 8u * r] = c;
+  }
+}
+
 template <int WD, int VEC, int NC>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a, BucketSet S) {
   BucketDev bk;
@@ -464,11 +529,12 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a, BucketSe
   uint32_t c, cstep;
   chunk_walk(lb, lg, beg, c, cstep);
   for (; c < end; c += cstep) {
-    const uint4 task = a.chunk_task[c];  // {start, len, table, long index}
-    if (!chunk_ok(a, task)) continue;    // uniform per workgroup; never for valid lists
+    const uint32_t cp = a.chunk_perm ? a.chunk_perm[c] : c;  // position of the chunk taken
+    const uint4 task = a.chunk_task[cp];  // {start, len, table, long index}
+    if (cp < beg || cp >= end || !chunk_ok(a, task)) continue;  // uniform; never for valid lists
     const TableDev td = a.tables[task.z];
     wg_gather<VEC, NC>(a, bk, td, task.z, task.x, task.x + task.y, sm);
-    chunk_store<VEC, NC>(a, bk, td.dim, c, sm);
+    chunk_store<VEC, NC>(a, bk, td.dim, cp, sm);
     __syncthreads();
   }
 }
@@ -501,11 +567,13 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_fused_kernel(BwdArgs a, Bu
   uint32_t c, cstep;
   chunk_walk(lb, lg, beg, c, cstep);
   for (; c < end; c += cstep) {
-    const uint4 task = a.chunk_task[c];  // {start, len, table, long index}
-    if (!chunk_ok(a, task) || !long_ok(a, task.w)) continue;  // uniform; never for valid lists
+    const uint32_t cp = a.chunk_perm ? a.chunk_perm[c] : c;  // position of the chunk taken
+    const uint4 task = a.chunk_task[cp];  // {start, len, table, long index}
+    if (cp < beg || cp >= end || !chunk_ok(a, task) || !long_ok(a, task.w))
+      continue;  // uniform per workgroup; never for valid lists
     const TableDev td = a.tables[task.z];
     wg_gather<VEC, NC>(a, bk, td, task.z, task.x, task.x + task.y, sm);
-    chunk_store<VEC, NC>(a, bk, td.dim, c, sm);
+    chunk_store<VEC, NC>(a, bk, td.dim, cp, sm);
     __threadfence();  // this thread's partial stores are visible device-wide
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -605,6 +673,12 @@ hipError_t launch(const BwdArgs& a, BucketSet S, const BwdGrids* g, bool fused, 
 }
 
 }  // namespace
+
+hipError_t launch_chunk_order(const BwdArgs& a, hipStream_t s) {
+  if (a.T == 0 || !a.chunk_perm) return hipSuccess;
+  TBE_LAUNCH("chunk_order", chunk_order_kernel, dim3(a.T * 8u), dim3(kThreads), s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_backward_set(const BwdArgs& a, BucketSet S, const BwdGrids* g, int wd, int vec,
                                int nc, bool fused, int num_cus, const hipStream_t* s) {

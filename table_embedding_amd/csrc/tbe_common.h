@@ -21,6 +21,8 @@ constexpr int kChunk = 256;         // lookups per long-run chunk
 constexpr int kRadixBits = 8;
 constexpr int kMaxPass = 4;         // 32-bit rows: at most four 8-bit digits
 constexpr int kMaxTables = 4096;
+// grad_out larger than this (the MALL) takes the bag-ordered chunk walk
+constexpr uint64_t kChunkOrderMinGradBytes = 256ull << 20;
 
 enum : int { WD_F32 = 0, WD_F16 = 1, WD_BF16 = 2 };
 enum : int { IT_I32 = 0, IT_I64 = 1 };
@@ -99,6 +101,7 @@ struct WsLayout {
   size_t run_start, run_key;
   size_t single_task, tiny_task, med_task, long_task, long_cbeg, remaining, chunk_task;
   size_t partial, counters;
+  size_t chunk_perm;  // max_chunks uint32: chunk list position taken at each walk position
   size_t total;
   uint32_t ntiles;          // ceil(N / kTile)
   uint32_t nrle_tiles;      // ceil(N / kRleTile): tiles of the run-length pass
@@ -304,6 +307,7 @@ struct BwdArgs {
   const uint32_t* long_cbeg;
   uint32_t* remaining;
   const uint4* chunk_task;
+  uint32_t* chunk_perm;         // nullable: walk order of the chunk list (identity if null)
   float* partial;
   uint32_t pstride;
   const uint32_t* counters;
@@ -333,5 +337,8 @@ struct BwdGrids {
 // may be the same stream).
 hipError_t launch_backward_set(const BwdArgs& a, BucketSet S, const BwdGrids* g, int wd, int vec,
                                int nc, bool fused, int num_cus, const hipStream_t* s);
+// Orders each (table, XCD residue) class of the chunk list by the bag of the
+// chunks' first lookups into a.chunk_perm (no-op when a.chunk_perm is null).
+hipError_t launch_chunk_order(const BwdArgs& a, hipStream_t s);
 
 }  // namespace tbe

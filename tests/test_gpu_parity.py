@@ -289,3 +289,43 @@ def test_forward_and_preprocess_schedule(name):
     tb2.backward(B, case.d_idx, case.d_off, case.d_psw, case.d_G, case.spec.lr, case.spec.eps)
     torch.cuda.synchronize()
     assert got == (out2.cpu().numpy().tobytes(), _tables_bytes(tb2, case.spec.wdtype))
+
+
+@pytest.mark.parametrize("name", ["C3s", "C5s", "many_tables", "const257"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_chunk_order_changes_no_bit(name, fused):
+    """Walking each table's chunks in bag order (forced; by default only when
+    grad_out exceeds 256 MiB) gives the same bits as list order, within the
+    oracle's bars; the walk order is a permutation of each (table, position
+    mod 8) class, by non-decreasing bag of the chunk's first lookup."""
+    _announce(name, f"chunk-order fused={fused}")
+    import table_embedding_amd as te
+    case = S.Case(_spec(name), m_nonzero=True)
+    base = te.TBE_BWD_FUSED_LONG if fused else 0
+    res = []
+    for flags in (base | te.TBE_BWD_NO_ORDER_CHUNKS, base | te.TBE_BWD_ORDER_CHUNKS):
+        case.reset_tables()
+        tb = case.tbe()
+        tb.backward(case.spec.B, case.d_idx, case.d_off, case.d_psw, case.d_G, case.spec.lr,
+                    case.spec.eps, flags=flags)
+        torch.cuda.synchronize()
+        res.append(_tables_bytes(tb, case.spec.wdtype))
+        if flags & te.TBE_BWD_ORDER_CHUNKS:
+            S.check_backward(case, tb)
+            g = S.gpu_preprocess_views(tb, case)
+            v = te.tbe_workspace_views(tb.plan, case.spec.B, case.N)
+            nc = g["n_chunks"]
+            perm = S.read_u32(tb._ws, v["chunk_perm"], nc).astype(np.int64)
+            ct = g["chunk_task"]
+            B = case.spec.B
+            for t in np.unique(ct[:, 2]) if nc else []:
+                pos = np.nonzero(ct[:, 2] == t)[0]
+                for x in range(8):
+                    cls = pos[pos % 8 == x]
+                    got = perm[cls]
+                    assert np.array_equal(np.sort(got), cls), "not a permutation of the class"
+                    bag = g["sorted_bag"][ct[got, 0]] - t * B
+                    bins = bag * 256 // B
+                    assert np.all(np.diff(bins) >= 0), "walk not in bag order"
+        tb.close()
+    assert res[0] == res[1]
