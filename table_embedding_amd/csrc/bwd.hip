@@ -2,10 +2,12 @@
 // page, "Backward": a run with SL < 256 is gathered, accumulated and updated by
 // one program that owns the row and writes it with plain stores; a run with
 // SL >= 256 is cut into 256-lookup chunks whose partial sums are stored and
-// reduced by a second kernel, or, in the fused form, each chunk fences its
+// reduced by a second kernel, or, in the fused form, each chunk publishes its
 // partial and decrements a countdown so that only the last chunk updates the
-// row.  Section "Fusion boundaries": per-sample weights scale each
-// contribution before grouping and the optimizer runs as the epilogue).
+// row; the pages order the two with a fence, here the partials cross XCDs
+// with write-through atomic stores and loads instead, since a gfx950 fence
+// flushes a whole L2.  Section "Fusion boundaries": per-sample weights scale
+// each contribution before grouping and the optimizer runs as the epilogue).
 //
 // Programs.  Short runs with SL = 1 are owned, two at a time, by a subgroup of
 // `lpr` lanes (one row of the bucket width); short runs with 2 <= SL < 32 by a
@@ -356,7 +358,10 @@ __device__ __forceinline__ void wg_row_update(const BwdArgs& a, const TableDev& 
 }
 
 // Long-run update: reduce the run's chunk partials, then row-wise Adagrad.
-template <int WD, int VEC, int NC>
+// COH: the partials were written by workgroups of other XCDs during this
+// kernel, so they are read with agent-scope atomic loads, which bypass this
+// XCD's L2 (the two-launch update reads them after a kernel boundary).
+template <int WD, int VEC, int NC, bool COH>
 __device__ __forceinline__ void long_update(const BwdArgs& a, const BucketDev& bk, uint32_t l,
                                             WgSmem<VEC, NC>& sm) {
   const uint32_t lpr = bk.lpr, lane_in = threadIdx.x & (lpr - 1);
@@ -381,7 +386,13 @@ __device__ __forceinline__ void long_update(const BwdArgs& a, const BucketDev& b
     for (int c = 0; c < NC; ++c) {
       if (colc[c] >= D) continue;
       float v[VEC];
-      load_f32<VEC>(src + colc[c], v);
+      if (COH) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          v[e] = __hip_atomic_load(src + colc[c] + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        load_f32<VEC>(src + colc[c], v);
+      }
 #pragma unroll
       for (int e = 0; e < VEC; ++e) g[c][e] += v[e];
     }
@@ -395,8 +406,9 @@ __device__ __forceinline__ void long_update(const BwdArgs& a, const BucketDev& b
   wg_row_update<WD, VEC, NC>(a, td, (int64_t)task.z, sqp, sm);
 }
 
-// Write the combined chunk partial (ascending subgroup order) to partial[c].
-template <int VEC, int NC>
+// Write the combined chunk partial (ascending subgroup order) to partial[c];
+// COH: with agent-scope atomic stores, which write through this XCD's L2.
+template <int VEC, int NC, bool COH>
 __device__ __forceinline__ void chunk_store(const BwdArgs& a, const BucketDev& bk, uint32_t D,
                                             uint32_t c, WgSmem<VEC, NC>& sm) {
   const uint32_t nsg = kThreads >> bk.lpr_log2;
@@ -405,7 +417,10 @@ __device__ __forceinline__ void chunk_store(const BwdArgs& a, const BucketDev& b
   for (uint32_t col = threadIdx.x; col < D; col += kThreads) {
     float s = 0.f;
     for (uint32_t k = 0; k < nsg; ++k) s += sm.red[k * width + col];
-    dst[col] = s;
+    if (COH)
+      __hip_atomic_store(dst + col, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      dst[col] = s;
   }
 }
 
@@ -534,7 +549,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a, BucketSe
     if (cp < beg || cp >= end || !chunk_ok(a, task)) continue;  // uniform; never for valid lists
     const TableDev td = a.tables[task.z];
     wg_gather<VEC, NC>(a, bk, td, task.z, task.x, task.x + task.y, sm);
-    chunk_store<VEC, NC>(a, bk, td.dim, cp, sm);
+    chunk_store<VEC, NC, false>(a, bk, td.dim, cp, sm);
     __syncthreads();
   }
 }
@@ -549,13 +564,23 @@ __global__ __launch_bounds__(kThreads) void bwd_long_update_kernel(BwdArgs a, Bu
   const uint32_t end = min(list_begin(a, 3, bucket + 1), a.max_long);
   for (uint32_t l = beg + lb; l < end; l += lg) {
     if (!long_ok(a, l)) continue;  // uniform per workgroup; never for valid lists
-    long_update<WD, VEC, NC>(a, bk, l, sm);
+    long_update<WD, VEC, NC, false>(a, bk, l, sm);
   }
 }
 
-// Fused: each chunk publishes its partial (device-scope release), then counts
-// down the run's remaining chunks; the workgroup that takes the count to zero
-// acquires and performs the update, then re-arms the countdown.
+// Fused: each chunk publishes its partial, then counts down the run's
+// remaining chunks; the workgroup that takes the count to zero performs the
+// update, then re-arms the countdown.  Each XCD has its own L2, which is not
+// coherent with the others, and an agent-scope fence on gfx950 writes back and
+// invalidates the whole L2 -- per chunk, that made this path 20-25x slower than
+// the two-launch one.  So the partial is written with agent-scope atomic
+// stores (write-through to the device-coherent level), every thread waits for
+// its stores to complete (s_waitcnt 0), the workgroup meets at a barrier, and
+// only then is the countdown decremented (an agent-scope atomic, performed at
+// the coherent level); the last workgroup reads the partials with agent-scope
+// atomic loads (read from the coherent level, not from a stale cache).  This
+// is the release/acquire pair without the whole-cache operations, which only
+// serve to publish ordinary cached stores; none is published here.
 template <int WD, int VEC, int NC>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_fused_kernel(BwdArgs a, BucketSet S) {
   BucketDev bk;
@@ -573,18 +598,17 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_fused_kernel(BwdArgs a, Bu
       continue;  // uniform per workgroup; never for valid lists
     const TableDev td = a.tables[task.z];
     wg_gather<VEC, NC>(a, bk, td, task.z, task.x, task.x + task.y, sm);
-    chunk_store<VEC, NC>(a, bk, td.dim, cp, sm);
-    __threadfence();  // this thread's partial stores are visible device-wide
+    chunk_store<VEC, NC, true>(a, bk, td.dim, cp, sm);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's write-through stores have completed
     __syncthreads();
     if (threadIdx.x == 0) {
       const uint32_t old = __hip_atomic_fetch_add(&a.remaining[task.w], 0xffffffffu,
-                                                  __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       sm.last = (old == 1u) ? 1u : 0u;
     }
     __syncthreads();
     if (sm.last) {
-      __threadfence();  // acquire: other chunks' partials
-      long_update<WD, VEC, NC>(a, bk, task.w, sm);
+      long_update<WD, VEC, NC, true>(a, bk, task.w, sm);
       if (threadIdx.x == 0) {
         const uint32_t len = a.long_task[task.w].y;
         __hip_atomic_store(&a.remaining[task.w], (len + kChunk - 1) / kChunk, __ATOMIC_RELAXED,
