@@ -82,64 +82,75 @@ __device__ __forceinline__ uint64_t st_read(uint64_t* p) {
 }
 
 // Sum of the counts of tiles [0, tile) in column `col` of a status table
-// with `stride` words per tile.  W predecessors are read per round trip; the
-// ready ones nearest the tile are consumed up to the first inclusive prefix.
-template <int W>
+// with `stride` words per tile.  The wave is split into groups of GL lanes,
+// each looking back for its own column (all 64 lanes call this; `col` is
+// uniform in a group): lane i of a group reads predecessor tile - 1 - i, so
+// one round trip covers GL tiles.  The ready words nearest the tile are
+// consumed up to the first inclusive prefix; an unpublished one stops the
+// window there and is polled again.  (One lane reading 16 words per round trip
+// made the prefix frontier the limit of the run-length and classification
+// passes at C5's ~10k tiles.)
+template <int GL>
 __device__ uint32_t look_back(uint64_t* st, uint32_t tile, uint32_t stride, uint32_t col,
                               uint32_t* err) {
+  static_assert(GL == 16 || GL == 32 || GL == 64, "groups of 16, 32 or 64 lanes");
+  const uint32_t lane = lane_id();
+  const uint32_t i = lane & (GL - 1), base = lane & ~(uint32_t)(GL - 1);
+  const uint64_t gmask = GL == 64 ? ~0ull : ((1ull << GL) - 1ull);
   uint32_t excl = 0, spins = 0;
-  uint32_t t = tile;  // tiles [0, t) are still to be summed
-  while (t > 0) {
-    uint64_t v[W];
+  uint32_t t = tile;  // tiles [0, t) are still to be summed (uniform in the group)
+  bool fin = t == 0;
+  while (__ballot(!fin)) {
+    const bool have = !fin && t > i;
+    const uint64_t v = have ? st_read(st + (size_t)(t - 1 - i) * stride + col) : 0ull;
+    const uint64_t f = v & kStFlags;
+    const uint64_t unpub = (__ballot(have && f == 0) >> base) & gmask;
+    const uint64_t pre = (__ballot(have && f == kStPre) >> base) & gmask;
+    const uint32_t first_unpub = unpub ? (uint32_t)__builtin_ctzll(unpub) : (uint32_t)GL;
+    const uint32_t first_pre = pre ? (uint32_t)__builtin_ctzll(pre) : (uint32_t)GL;
+    const uint32_t navail = t < (uint32_t)GL ? t : (uint32_t)GL;  // predecessors in the window
+    // lanes consumed: through the first prefix if no gap comes before it,
+    // else up to the first gap, else the whole window
+    const bool done = first_pre < first_unpub || (first_unpub == (uint32_t)GL && navail == t);
+    const uint32_t used = fin ? 0u
+                          : first_pre < first_unpub ? first_pre + 1u
+                          : (first_unpub < navail ? first_unpub : navail);
+    uint32_t c = (i < used) ? (uint32_t)v : 0u;
 #pragma unroll
-    for (int w = 0; w < W; ++w)
-      v[w] = (t > (uint32_t)w) ? st_read(st + (size_t)(t - 1 - w) * stride + col) : kStPre;
-    uint32_t sum = 0, used = 0;
-    bool done = false, stall = false;
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      if (done || stall) continue;
-      if (t <= (uint32_t)w) {  // past tile 0: nothing more to add
-        done = true;
-        continue;
+    for (int o = GL / 2; o > 0; o >>= 1) c += __shfl_xor(c, o, kWave);
+    if (!fin) {
+      excl += c;
+      t -= used;
+      if (done) {
+        fin = true;
+      } else if (used == 0u) {  // the nearest predecessor has not published yet
+        if (++spins >= kSpinLimit) {
+          if (i == 0) atomicOr(err, 1u);
+          fin = true;
+        }
       }
-      const uint64_t f = v[w] & kStFlags;
-      if (f == 0) {
-        stall = true;
-        continue;
-      }
-      sum += (uint32_t)v[w];
-      ++used;
-      if (f == kStPre) done = true;
     }
-    excl += sum;
-    t -= used;
-    if (done) break;
-    if (stall) {
-      if (++spins >= kSpinLimit) {
-        atomicOr(err, 1u);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
+    if (__ballot(!fin && used == 0u)) __builtin_amdgcn_s_sleep(1);
   }
   return excl;
 }
 
 // Publish a tile's count, look back, publish its inclusive prefix; returns the
-// exclusive prefix.
-template <int W>
+// exclusive prefix.  Called by a whole wave; the first lane of each GL-lane
+// group publishes its column.
+template <int GL>
 __device__ __forceinline__ uint32_t publish_and_look_back(uint64_t* st, uint32_t tile,
                                                           uint32_t stride, uint32_t col,
                                                           uint32_t count, uint32_t* err) {
   uint64_t* mine = st + (size_t)tile * stride + col;
+  const bool first = (lane_id() & (GL - 1)) == 0;
   if (tile == 0) {
-    st_publish(mine, kStPre | count);
+    if (first) st_publish(mine, kStPre | count);
     return 0;
   }
-  st_publish(mine, kStAgg | count);
-  const uint32_t excl = look_back<W>(st, tile, stride, col, err);
-  st_publish(mine, kStPre | (uint64_t)(uint32_t)(excl + count));
+  if (first) st_publish(mine, kStAgg | count);
+  const uint32_t excl = look_back<GL>(st, tile, stride, col, err);
+  if (first) st_publish(mine, kStPre | (uint64_t)(uint32_t)(excl + count));
   return excl;
 }
 
@@ -185,9 +196,21 @@ __device__ __forceinline__ void loadn(const uint32_t* __restrict__ a, uint64_t i
   }
 }
 
-// The workgroup's tile number, in the order workgroups start.
-__device__ __forceinline__ uint32_t take_ticket(uint32_t* ticket, uint32_t* s_tile) {
-  if (threadIdx.x == 0) *s_tile = atomicAdd(ticket, 1u);
+// The workgroup's tile number, in the order workgroups start.  One counter
+// per class c = workgroup index mod 8, and tile = 8 * ticket + c: workgroups
+// go to the eight XCDs round-robin by index, so a class is an XCD, and one
+// counter for all workgroups would serialize them (an atomic on one address
+// costs about 11 ns per workgroup on MI355X: 0.4 ms for 35k workgroups).  A
+// grid of n workgroups has as many members of class c as there are tiles
+// below n in that class, so every tile is taken once.  Waits still end: the
+// smallest tile not finished is either running (then everything it waits on
+// is finished) or not yet taken, and then its XCD runs only workgroups with
+// smaller tiles, which finish and make room for it.
+__device__ __forceinline__ uint32_t take_ticket(uint32_t* tickets, uint32_t* s_tile) {
+  if (threadIdx.x == 0) {
+    const uint32_t c = blockIdx.x & 7u;
+    *s_tile = atomicAdd(tickets + c * kTicketStride, 1u) * 8u + c;
+  }
   __syncthreads();
   return *s_tile;
 }
@@ -207,7 +230,8 @@ __global__ __launch_bounds__(kThreads) void seg_setup_kernel(PrepDev a,
                                                              uint32_t* __restrict__ ctl) {
   __shared__ uint32_t sh4[4];
   const IT* __restrict__ O = reinterpret_cast<const IT*>(a.offsets);
-  for (uint32_t i = threadIdx.x; i < (uint32_t)kCtlTiles; i += kThreads) ctl[i] = 0u;
+  for (uint32_t i = threadIdx.x; i < (uint32_t)kCtlWords; i += kThreads)
+    if (i != (uint32_t)kCtlTiles) ctl[i] = 0u;
   uint32_t run_n = 0, run_t = 0;
   for (uint32_t s0 = 0; s0 < a.T; s0 += kThreads) {
     const uint32_t s = s0 + threadIdx.x;
@@ -549,12 +573,14 @@ __global__ __launch_bounds__(kThreads) void rle_kernel(const uint32_t* __restric
     local[g] = total + block_excl_scan(__popc(m[g]), sh4, tg);
     total += tg;
   }
-  if (threadIdx.x == 0) {
-    const uint32_t excl = publish_and_look_back<16>(st, tile, 1, 0, total, err);
-    s_excl = excl;
-    if (tile == ntiles - 1) {
-      counters[kCntU] = excl + total;
-      run_start[excl + total] = N;
+  if (threadIdx.x < (uint32_t)kWave) {  // wave 0
+    const uint32_t excl = publish_and_look_back<64>(st, tile, 1, 0, total, err);
+    if (threadIdx.x == 0) {
+      s_excl = excl;
+      if (tile == ntiles - 1) {
+        counters[kCntU] = excl + total;
+        run_start[excl + total] = N;
+      }
     }
   }
   __syncthreads();
@@ -691,10 +717,21 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClsDev a) {
     if (threadIdx.x == 0) s_tot[q] = tot;
   }
   __syncthreads();
-  if (threadIdx.x < (uint32_t)kNumLists) {
-    const uint32_t q = threadIdx.x;
-    s_excl[q] = publish_and_look_back<16>(a.st, tile, kClsStride, q, s_tot[q], a.err);
+  // wave 0 looks back for lists 0-3 with 16 lanes each, wave 1 for list 4
+  // with 64 lanes, at once (whole waves polling every list read more status
+  // words per round trip than the coherent level serves quickly)
+  {
+    const uint32_t w = threadIdx.x / kWave;
+    if (w == 0) {
+      const uint32_t q = lane_id() / 16u;
+      const uint32_t e = publish_and_look_back<16>(a.st, tile, kClsStride, q, s_tot[q], a.err);
+      if ((lane_id() & 15u) == 0) s_excl[q] = e;
+    } else if (w == 1) {
+      const uint32_t e = publish_and_look_back<64>(a.st, tile, kClsStride, 4, s_tot[4], a.err);
+      if (lane_id() == 0) s_excl[4] = e;
+    }
   }
+  static_assert(kNumLists == 5 && kThreads / kWave == 4, "list-to-wave map of the look-back");
   __syncthreads();
   const bool last_tile = tile0 + kClsTile >= U;
   if (last_tile) {
@@ -816,11 +853,11 @@ hipError_t launch_preprocess(const PrepArgs& p, int /*num_cus*/, hipStream_t s) 
   const uint32_t* skey = u32p(L.final_in_b ? L.key_b : L.key_a);
   const uint32_t* sbag = u32p(L.final_in_b ? L.val_b : L.val_a);
   TBE_LAUNCH("rle", rle_kernel, dim3(L.nrle_tiles), dim3(kThreads), s, skey, p.N, L.nrle_tiles,
-             ctl + kCtlTicket + kMaxPass, u64p(L.st_rle), err, u32p(L.counters),
+             ctl + kCtlRleTickets, u64p(L.st_rle), err, u32p(L.counters),
              u32p(L.run_start), u32p(L.run_key));
 
   ClsDev c{u32p(L.run_start), u32p(L.run_key), sbag, u32p(L.counters),
-           ctl + kCtlTicket + kMaxPass + 1, u64p(L.st_cls), err,
+           ctl + kCtlClsTickets, u64p(L.st_cls), err,
            reinterpret_cast<uint4*>(ws + L.single_task), reinterpret_cast<uint4*>(ws + L.tiny_task),
            reinterpret_cast<uint4*>(ws + L.med_task),
            reinterpret_cast<uint4*>(ws + L.long_task), u32p(L.long_cbeg), u32p(L.remaining),

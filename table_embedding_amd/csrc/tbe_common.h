@@ -122,11 +122,15 @@ struct WsLayout {
 constexpr int kNumLists = 5;
 constexpr int kCntU = 0, kCntSingle = 1, kCntBegins = 1 + kNumLists;
 
-// Control block of the preprocessing: tile tickets (words kCtlTicket +
-// kMaxPass and + kMaxPass + 1: the run-length and classification passes),
-// the look-back error flag and the number of sort tiles of the segments.
-constexpr int kCtlTicket = 0, kCtlErr = 8, kCtlTiles = 9;
-constexpr int kCtlWords = 16;
+// Control block of the preprocessing: the look-back error flag, the number
+// of sort tiles of the segments, and the tile tickets of the run-length and
+// classification passes: eight counters each (one per workgroup index mod 8),
+// 128 bytes apart.
+constexpr int kCtlErr = 8, kCtlTiles = 9;
+constexpr int kTicketStride = 32;
+constexpr int kCtlRleTickets = 32;
+constexpr int kCtlClsTickets = kCtlRleTickets + 8 * kTicketStride;
+constexpr int kCtlWords = kCtlClsTickets + 8 * kTicketStride;
 constexpr int kClsStride = 8;  // status words per classification tile (five used)
 
 // ------------------------------------------------------------- device helpers
