@@ -259,35 +259,79 @@ __global__ __launch_bounds__(kThreads) void seg_setup_kernel(PrepDev a,
 }
 
 // ------------------------------------------------------------ transposition
-// 16 lanes per bag write its lookups' keys and bag id with contiguous stores,
-// at the lookups' slots in the table's segment.  With per-sample weights or
-// mean pooling it also writes the contribution scale of each lookup,
-// S[p] * (1/L if mean) (FBTriton page, "Fusion boundaries": the weights
-// scale each contribution before the grouping by row).
+// A workgroup takes `nbp` consecutive bags (at most 256, as many as keep
+// about 2048 workgroups; table-major, so their lookups are one contiguous
+// range) and streams that range: thread i handles positions first + i,
+// first + i + 256, ..., finds each position's bag by binary search over the
+// nbp + 1 offsets held in LDS, and writes the lookup's key and bag id (and,
+// with per-sample weights or mean pooling, its contribution scale
+// S[p] * (1/L if mean); FBTriton page, "Fusion boundaries": the weights scale
+// each contribution before the grouping by row) at its slot in its table's
+// segment.  Index loads and key / bag stores are coalesced runs, four
+// positions in flight per thread (one lane group per bag left each wave with
+// four short dependent chains in flight).
+constexpr uint32_t kTrBags = 256;
+
 template <typename IT>
-__global__ __launch_bounds__(kThreads) void transpose_kernel(PrepDev a, uint32_t* __restrict__ key,
+__global__ __launch_bounds__(kThreads) void transpose_kernel(PrepDev a, uint32_t nbp,
+                                                             uint32_t* __restrict__ key,
                                                              uint32_t* __restrict__ bag,
                                                              float* __restrict__ scale) {
-  const uint32_t lane16 = threadIdx.x & 15;
-  const uint64_t j = ((uint64_t)blockIdx.x * kThreads + threadIdx.x) >> 4;
-  if (j >= (uint64_t)a.T * (uint64_t)a.B) return;
-  const uint32_t t = (uint32_t)(j / (uint64_t)a.B);
-  const TableDev td = a.tables[t];
+  __shared__ int64_t s_off[kTrBags + 1];
+  __shared__ int64_t s_shift[kTrBags];  // slot of position p: p + shift (its table's)
+  __shared__ uint32_t s_kb[kTrBags];
+  __shared__ uint32_t s_mean[kTrBags];
+  const uint64_t nbag = (uint64_t)a.T * (uint64_t)a.B;
+  const uint64_t j0 = (uint64_t)blockIdx.x * nbp;
+  if (j0 >= nbag || nbp > kTrBags) return;
+  const uint32_t nb = (uint32_t)min((uint64_t)nbp, nbag - j0);
   const IT* __restrict__ I = reinterpret_cast<const IT*>(a.indices);
   const IT* __restrict__ O = reinterpret_cast<const IT*>(a.offsets);
-  const int64_t lo = O[j];
-  const int64_t hi = O[j + 1];
-  // slot of lookup p: the segment's output base plus p's rank inside the table
-  const int64_t shift = (int64_t)a.seg[a.tseg[t]].y - (int64_t)O[(int64_t)t * a.B];
-  const bool mean = td.pooling == POOL_MEAN;
-  for (int64_t p = lo + lane16; p < hi; p += 16) {
-    const int64_t d = p + shift;
-    if ((uint64_t)d >= (uint64_t)a.N) continue;  // only for offsets that break the contract
-    key[d] = td.key_base + (uint32_t)I[p];
-    bag[d] = (uint32_t)j;
-    if (scale) {
-      const float sp = a.psw ? a.psw[p] : 1.0f;
-      scale[d] = mean ? sp / (float)(hi - lo) : sp;
+  for (uint32_t i = threadIdx.x; i <= nb; i += kThreads) s_off[i] = (int64_t)O[j0 + i];
+  if (threadIdx.x < nb) {
+    const uint64_t j = j0 + threadIdx.x;
+    const uint32_t t = (uint32_t)(j / (uint64_t)a.B);
+    const TableDev td = a.tables[t];
+    s_shift[threadIdx.x] = (int64_t)a.seg[a.tseg[t]].y - (int64_t)O[(int64_t)t * a.B];
+    s_kb[threadIdx.x] = td.key_base;
+    s_mean[threadIdx.x] = td.pooling == POOL_MEAN ? 1u : 0u;
+  }
+  __syncthreads();
+  const int64_t first = s_off[0], last = s_off[nb];
+  constexpr int U = 4;
+  for (int64_t p0 = first + threadIdx.x; p0 < last; p0 += (int64_t)U * kThreads) {
+    int64_t p[U];
+    uint32_t q[U];  // bag index in this workgroup's range
+    IT iv[U];
+    float sp[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      p[u] = p0 + (int64_t)u * kThreads;
+      const bool in = p[u] < last && p[u] >= 0 && p[u] < (int64_t)a.N;
+      iv[u] = in ? I[p[u]] : (IT)0;
+      sp[u] = (scale && a.psw && in) ? a.psw[p[u]] : 1.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // last bag q with s_off[q] <= p (empty bags share an offset with the next)
+      uint32_t lo = 0, hi = nb;  // s_off[lo] <= p < s_off[hi]
+      while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (s_off[mid] <= p[u]) lo = mid; else hi = mid;
+      }
+      q[u] = lo;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (p[u] >= last || p[u] < 0 || p[u] >= (int64_t)a.N) continue;
+      const int64_t d = p[u] + s_shift[q[u]];
+      if ((uint64_t)d >= (uint64_t)a.N) continue;  // only for offsets that break the contract
+      key[d] = s_kb[q[u]] + (uint32_t)iv[u];
+      bag[d] = (uint32_t)(j0 + q[u]);
+      if (scale) {
+        const int64_t L = s_off[q[u] + 1] - s_off[q[u]];
+        scale[d] = s_mean[q[u]] ? sp[u] / (float)L : sp[u];
+      }
     }
   }
 }
@@ -821,12 +865,13 @@ hipError_t launch_preprocess(const PrepArgs& p, int /*num_cus*/, hipStream_t s) 
     TBE_LAUNCH("seg_setup", seg_setup_kernel<int64_t>, dim3(1), dim3(kThreads), s, d, p.order,
                seg, tile_seg, L.ntiles_max, ctl);
   const uint64_t nbag = (uint64_t)p.T * (uint64_t)p.B;
-  const uint32_t tgrid = (uint32_t)((nbag * 16 + kThreads - 1) / kThreads);
+  const uint32_t nbp = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(kTrBags, nbag / 2048));
+  const uint32_t tgrid = (uint32_t)((nbag + nbp - 1) / nbp);
   if (p.itype == IT_I32)
-    TBE_LAUNCH("transpose", transpose_kernel<int32_t>, dim3(tgrid), dim3(kThreads), s, d,
+    TBE_LAUNCH("transpose", transpose_kernel<int32_t>, dim3(tgrid), dim3(kThreads), s, d, nbp,
                u32p(L.key_a), u32p(L.val_a), sc ? f32p(L.sc_a) : nullptr);
   else
-    TBE_LAUNCH("transpose", transpose_kernel<int64_t>, dim3(tgrid), dim3(kThreads), s, d,
+    TBE_LAUNCH("transpose", transpose_kernel<int64_t>, dim3(tgrid), dim3(kThreads), s, d, nbp,
                u32p(L.key_a), u32p(L.val_a), sc ? f32p(L.sc_a) : nullptr);
 
   // ping-pong a -> b -> a ...; the final buffers are b for an odd pass count

@@ -61,12 +61,16 @@ def _spec(name):
         return wl.Spec("many_tables", 2008, [int(50 + 37 * t) for t in range(T)],
                        [dims[t % len(dims)] for t in range(T)], [t % 2 for t in range(T)],
                        "f16", 40, "uniform:0:12", "zipf:1.05", "i32", True)
+    if name == "many_bags":
+        # 12000 bags: the transposition gives each workgroup several bags
+        return wl.Spec("many_bags", 2009, [3000, 500], [16, 64], [0, 1], "f16", 6000,
+                       "uniform:0:20", "zipf:1.1", "i32", True)
     raise KeyError(name)
 
 
 MAIN = ["C1", "C2s", "C3s", "C4s", "C5s"]
 EDGE = ["empty_bags", "all_empty", "one_bag", "one_row", "const31", "const32", "const255",
-        "const256", "const257", "wide_f32", "wide_bf16", "many_tables"]
+        "const256", "const257", "wide_f32", "wide_bf16", "many_tables", "many_bags"]
 
 
 def _announce(name, what):
