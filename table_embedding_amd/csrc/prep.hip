@@ -219,8 +219,11 @@ __device__ __forceinline__ uint32_t take_ticket(uint32_t* tickets, uint32_t* s_t
 
 // One workgroup.  Segment s is table order[s] (tables in key order); its
 // lookups are [O[t*B], O[(t+1)*B]).  Writes {lookups, output base, first
-// tile, key base} per segment, the segment of every tile, the tile total
-// (ctl[kCtlTiles]) and clears the tickets and the error flag.
+// tile, key base} per segment, the segment of every tile (a segment of at
+// most eight tiles by its own thread, a larger one by all threads in turn:
+// one thread per segment wrote 2048 tiles in 124 us for a single table of
+// 8.4M lookups), the tile total (ctl[kCtlTiles]) and clears the tickets and
+// the error flag.
 template <typename IT>
 __global__ __launch_bounds__(kThreads) void seg_setup_kernel(PrepDev a,
                                                              const uint32_t* __restrict__ order,
@@ -229,6 +232,7 @@ __global__ __launch_bounds__(kThreads) void seg_setup_kernel(PrepDev a,
                                                              uint32_t ntiles_max,
                                                              uint32_t* __restrict__ ctl) {
   __shared__ uint32_t sh4[4];
+  __shared__ uint32_t s_ot[kThreads], s_nt[kThreads];  // first tile and tiles of the batch's segments
   const IT* __restrict__ O = reinterpret_cast<const IT*>(a.offsets);
   for (uint32_t i = threadIdx.x; i < (uint32_t)kCtlWords; i += kThreads)
     if (i != (uint32_t)kCtlTiles) ctl[i] = 0u;
@@ -250,8 +254,21 @@ __global__ __launch_bounds__(kThreads) void seg_setup_kernel(PrepDev a,
     const uint32_t ot = run_t + block_excl_scan(nt, sh4, tot_t);
     if (s < a.T) {
       seg[s] = make_uint4(nc, on, ot, a.tables[t].key_base);
-      for (uint32_t k = 0; k < nt && ot + k < ntiles_max; ++k) tile_seg[ot + k] = s;
+      if (nt <= 8u)
+        for (uint32_t k = 0; k < nt && ot + k < ntiles_max; ++k) tile_seg[ot + k] = s;
     }
+    s_ot[threadIdx.x] = ot;
+    s_nt[threadIdx.x] = s < a.T ? nt : 0u;
+    __syncthreads();
+    const uint32_t nseg = a.T - s0 < kThreads ? a.T - s0 : kThreads;
+    for (uint32_t i = 0; i < nseg; ++i) {
+      const uint32_t n_i = s_nt[i];
+      if (n_i <= 8u) continue;
+      const uint32_t o_i = s_ot[i];
+      for (uint32_t k = threadIdx.x; k < n_i && o_i + k < ntiles_max; k += kThreads)
+        tile_seg[o_i + k] = s0 + i;
+    }
+    __syncthreads();  // s_ot / s_nt are rewritten by the next batch
     run_n += tot_n;
     run_t += tot_t;
   }
@@ -713,6 +730,8 @@ __device__ __forceinline__ uint32_t bucket_of_key(const uint32_t* bkb, uint32_t 
 // are consecutive, so XCD x reads about the x-th eighth of the bags for every
 // long run of a table, and a run's partial sums stay contiguous.
 
+constexpr uint32_t kHeavyChunks = 4096;
+
 __global__ __launch_bounds__(kThreads) void classify_kernel(ClsDev a) {
   __shared__ uint32_t s_kb[kMaxTables];
   __shared__ uint32_t s_ord[kMaxTables];
@@ -720,6 +739,10 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClsDev a) {
   __shared__ uint32_t sh4[4];
   __shared__ uint32_t s_tile;
   __shared__ uint32_t s_tot[kNumLists], s_excl[kNumLists];
+  // one step's long runs: first chunk position, long index, table, first slot,
+  // length, and the exclusive prefix of their chunk counts
+  __shared__ uint32_t s_lr_pc[kThreads], s_lr_pl[kThreads], s_lr_t[kThreads];
+  __shared__ uint32_t s_lr_st[kThreads], s_lr_ln[kThreads], s_lr_cb[kThreads + 1];
   const uint32_t U = a.counters[kCntU];
   // workgroups past the last run leave before taking a ticket, so the tickets
   // go to exactly the tiles that hold runs
@@ -727,7 +750,7 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClsDev a) {
   const uint32_t tile = take_ticket(a.ticket, &s_tile);
   const uint64_t tile0 = (uint64_t)tile * kClsTile;
   const uint64_t u0 = tile0 + (uint64_t)threadIdx.x * kClsItems;
-  uint32_t start[kClsItems], len[kClsItems], key[kClsItems], bag0[kClsItems];
+  uint32_t start[kClsItems] = {}, len[kClsItems] = {}, key[kClsItems] = {}, bag0[kClsItems] = {};
   uint32_t keyprev = 0;
   const bool mine = u0 < U;
   if (mine) {
@@ -787,56 +810,125 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClsDev a) {
       for (int q = 0; q < kNumLists; ++q)
         a.counters[kCntBegins + q * (a.nb + 1) + b] = s_excl[q] + s_tot[q];
   }
-  if (!mine) return;
-  for (int q = 0; q < kNumLists; ++q) pos[q] += s_excl[q];
-
+  if (mine)
+    for (int q = 0; q < kNumLists; ++q) pos[q] += s_excl[q];
   int bprev = u0 == 0 ? -1 : (int)bucket_of_key(s_bkb, a.nb, keyprev);
+  // Every thread takes every step (no early exit), so that each step's long
+  // runs can be placed by the whole wave or workgroup.
+  const bool heavy = s_tot[4] >= kHeavyChunks;  // uniform
+#pragma unroll
   for (int e = 0; e < kClsItems; ++e) {
-    if (u0 + e >= U) break;
+    const bool valid = mine && u0 + e < U;
+    uint32_t lp_pc = 0xffffffffu, lp_pl = 0, lp_t = 0;  // this step's long run, if any
     const uint32_t k = key[e], ln = len[e], st = start[e];
-    // table of the key: last table whose key_base <= key
-    uint32_t lo = 0, hi = a.T;  // invariant: s_kb[lo] <= key < s_kb[hi] (s_kb[T] = +inf)
-    while (hi - lo > 1) {
-      const uint32_t mid = (lo + hi) >> 1;
-      if (s_kb[mid] <= k) lo = mid; else hi = mid;
-    }
-    const uint32_t t = s_ord[lo];
-    const uint32_t row = k - s_kb[lo];
-    // bucket begins: this run opens buckets (bucket(prev run), bucket(this run)]
-    const int bcur = (int)bucket_of_key(s_bkb, a.nb, k);
-    for (int b = bprev + 1; b <= bcur; ++b)
-      for (int q = 0; q < kNumLists; ++q) a.counters[kCntBegins + q * (a.nb + 1) + b] = pos[q];
-    bprev = bcur;
-    if (ln == 1u) {
-      // {start, row, table, bag of the lookup}
-      if (pos[0] < a.N) a.single_task[pos[0]] = make_uint4(st, row, t, bag0[e]);
-      ++pos[0];
-    } else if (ln < (uint32_t)kTinyRun) {
-      if (pos[1] < a.max_tiny) a.tiny_task[pos[1]] = make_uint4(st, ln, row, t);
-      ++pos[1];
-    } else if (ln < (uint32_t)kLongRun) {
-      if (pos[2] < a.max_med) a.med_task[pos[2]] = make_uint4(st, ln, row, t);
-      ++pos[2];
-    } else {
-      const uint32_t nch = (ln + kChunk - 1) / kChunk;
-      const uint32_t pl = pos[3], pc = pos[4];
-      if (pl < a.max_long) {
-        a.long_task[pl] = make_uint4(st, ln, row, t);
-        a.long_cbeg[pl] = pc;
-        a.remaining[pl] = nch;
+    if (valid) {
+      // table of the key: last table whose key_base <= key
+      uint32_t lo = 0, hi = a.T;  // invariant: s_kb[lo] <= key < s_kb[hi] (s_kb[T] = +inf)
+      while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (s_kb[mid] <= k) lo = mid; else hi = mid;
       }
-      // chunk placement (above): walk the positions residue class by residue
-      // class, handing out chunk numbers q in turn
-      uint32_t q = 0;
-      for (uint32_t x = 0; x < 8u; ++x) {
-        for (uint32_t cp = pc + ((x - pc) & 7u); cp < pc + nch; cp += 8u, ++q) {
-          const uint32_t cl_len = (ln - q * kChunk) < (uint32_t)kChunk ? (ln - q * kChunk)
-                                                                        : (uint32_t)kChunk;
-          if (cp < a.max_chunks) a.chunk_task[cp] = make_uint4(st + q * kChunk, cl_len, t, pl);
+      const uint32_t t = s_ord[lo];
+      const uint32_t row = k - s_kb[lo];
+      // bucket begins: this run opens buckets (bucket(prev run), bucket(this run)]
+      const int bcur = (int)bucket_of_key(s_bkb, a.nb, k);
+      for (int b = bprev + 1; b <= bcur; ++b)
+        for (int q = 0; q < kNumLists; ++q) a.counters[kCntBegins + q * (a.nb + 1) + b] = pos[q];
+      bprev = bcur;
+      if (ln == 1u) {
+        // {start, row, table, bag of the lookup}
+        if (pos[0] < a.N) a.single_task[pos[0]] = make_uint4(st, row, t, bag0[e]);
+        ++pos[0];
+      } else if (ln < (uint32_t)kTinyRun) {
+        if (pos[1] < a.max_tiny) a.tiny_task[pos[1]] = make_uint4(st, ln, row, t);
+        ++pos[1];
+      } else if (ln < (uint32_t)kLongRun) {
+        if (pos[2] < a.max_med) a.med_task[pos[2]] = make_uint4(st, ln, row, t);
+        ++pos[2];
+      } else {
+        const uint32_t nch = (ln + kChunk - 1) / kChunk;
+        const uint32_t pl = pos[3], pc = pos[4];
+        if (pl < a.max_long) {
+          a.long_task[pl] = make_uint4(st, ln, row, t);
+          a.long_cbeg[pl] = pc;
+          a.remaining[pl] = nch;
+        }
+        lp_pc = pc;  // its chunks are placed below, by the whole wave
+        lp_pl = pl;
+        lp_t = t;
+        pos[4] += nch;
+        ++pos[3];
+      }
+    }
+    // Chunk placement (above): position cp of a run with positions
+    // [pc, pc + nch) gets chunk number q, positions taken residue class by
+    // residue class (x = 0..7), a class's in ascending order.  One thread per
+    // run wrote 512 chunks of each of a table's 64 runs in 240 us; here a tile
+    // with at least kHeavyChunks chunks places each step's long runs with the
+    // whole workgroup (listed in LDS with the prefix of their chunk counts;
+    // thread i takes chunks i, i + 256, ... and finds its run by binary
+    // search), any other tile with the whole wave, one run at a time (no
+    // barriers).
+    const bool has = lp_pc != 0xffffffffu;
+    if (!heavy) {
+      uint64_t lm = __ballot(has);
+      while (lm) {
+        const uint32_t l = (uint32_t)__builtin_ctzll(lm);
+        lm &= lm - 1;
+        const uint32_t pc = (uint32_t)__shfl((int)lp_pc, (int)l, kWave);
+        const uint32_t pl = (uint32_t)__shfl((int)lp_pl, (int)l, kWave);
+        const uint32_t t = (uint32_t)__shfl((int)lp_t, (int)l, kWave);
+        const uint32_t rst = (uint32_t)__shfl((int)st, (int)l, kWave);
+        const uint32_t rln = (uint32_t)__shfl((int)ln, (int)l, kWave);
+        const uint32_t nch = (rln + kChunk - 1) / kChunk;
+        for (uint32_t cp = pc + lane_id(); cp < pc + nch; cp += kWave) {
+          const uint32_t x = cp & 7u;
+          uint32_t q = (cp - (pc + ((x - pc) & 7u))) / 8u;  // rank inside its class
+          for (uint32_t xx = 0; xx < x; ++xx) {             // plus the earlier classes
+            const uint32_t f = (xx - pc) & 7u;
+            q += f < nch ? (nch - 1u - f) / 8u + 1u : 0u;
+          }
+          const uint32_t cl_len = (rln - q * kChunk) < (uint32_t)kChunk ? (rln - q * kChunk)
+                                                                          : (uint32_t)kChunk;
+          if (cp < a.max_chunks) a.chunk_task[cp] = make_uint4(rst + q * kChunk, cl_len, t, pl);
         }
       }
-      pos[4] += nch;
-      ++pos[3];
+    } else if (__syncthreads_count(has) > 0) {  // uniform
+      uint32_t nlr, nchunk;
+      const uint32_t r = block_excl_scan(has ? 1u : 0u, sh4, nlr);
+      const uint32_t my_nch = has ? (ln + kChunk - 1) / kChunk : 0u;
+      const uint32_t cb = block_excl_scan(my_nch, sh4, nchunk);
+      if (has) {
+        s_lr_pc[r] = lp_pc;
+        s_lr_pl[r] = lp_pl;
+        s_lr_t[r] = lp_t;
+        s_lr_st[r] = st;
+        s_lr_ln[r] = ln;
+        s_lr_cb[r] = cb;
+      }
+      if (threadIdx.x == 0) s_lr_cb[nlr] = nchunk;
+      __syncthreads();
+      for (uint32_t i = threadIdx.x; i < nchunk; i += kThreads) {
+        uint32_t lo = 0, hi = nlr;  // s_lr_cb[lo] <= i < s_lr_cb[hi]
+        while (hi - lo > 1) {
+          const uint32_t mid = (lo + hi) >> 1;
+          if (s_lr_cb[mid] <= i) lo = mid; else hi = mid;
+        }
+        const uint32_t pc = s_lr_pc[lo], rln = s_lr_ln[lo];
+        const uint32_t nch = (rln + kChunk - 1) / kChunk;
+        const uint32_t cp = pc + (i - s_lr_cb[lo]);
+        const uint32_t x = cp & 7u;
+        uint32_t q = (cp - (pc + ((x - pc) & 7u))) / 8u;  // rank inside its class
+        for (uint32_t xx = 0; xx < x; ++xx) {             // plus the earlier classes
+          const uint32_t f = (xx - pc) & 7u;
+          q += f < nch ? (nch - 1u - f) / 8u + 1u : 0u;
+        }
+        const uint32_t cl_len = (rln - q * kChunk) < (uint32_t)kChunk ? (rln - q * kChunk)
+                                                                        : (uint32_t)kChunk;
+        if (cp < a.max_chunks)
+          a.chunk_task[cp] = make_uint4(s_lr_st[lo] + q * kChunk, cl_len, s_lr_t[lo], s_lr_pl[lo]);
+      }
+      __syncthreads();  // the list is rewritten by the next step
     }
   }
 }

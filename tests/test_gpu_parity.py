@@ -65,12 +65,18 @@ def _spec(name):
         # 12000 bags: the transposition gives each workgroup several bags
         return wl.Spec("many_bags", 2009, [3000, 500], [16, 64], [0, 1], "f16", 6000,
                        "uniform:0:20", "zipf:1.1", "i32", True)
+    if name == "heavy_chunks":
+        # 32 runs of 32768 lookups: one classification tile with 4096 chunks,
+        # which the whole workgroup places
+        return wl.Spec("heavy_chunks", 2010, [32], [16], [0], "f32", 4096, "fixed:256",
+                       "uniform", "i32", False)
     raise KeyError(name)
 
 
 MAIN = ["C1", "C2s", "C3s", "C4s", "C5s"]
 EDGE = ["empty_bags", "all_empty", "one_bag", "one_row", "const31", "const32", "const255",
-        "const256", "const257", "wide_f32", "wide_bf16", "many_tables", "many_bags"]
+        "const256", "const257", "wide_f32", "wide_bf16", "many_tables", "many_bags",
+        "heavy_chunks"]
 
 
 def _announce(name, what):
