@@ -7,7 +7,7 @@ over one batch of the workload; inputs are resident in HBM before timing.
 Prints one JSON line with lookups/s, the roofline of the dominant kernel and
 the single-threaded CPU oracle timed on a bounded sample of the same workload.
 
-Usage: python bench.py [--steps K] [--warmup W] [--config C2] [--fused]
+Usage: python bench.py [--steps K] [--warmup W] [--config C2] [--fused] [--bwd-hist]
 """
 from __future__ import annotations
 
@@ -29,6 +29,7 @@ KERNEL_SOURCES = {
     "fwd_pool": "fwd_pool.hip", "fwd_hist": "fwd_hist.hip", "bwd_single": "bwd.hip",
     "bwd_tiny": "bwd.hip", "bwd_medium": "bwd.hip", "bwd_chunk": "bwd.hip",
     "bwd_long_update": "bwd.hip", "bwd_chunk_fused": "bwd.hip",
+    "bwd_hist_partial": "bwd_hist.hip", "bwd_hist_update": "bwd_hist.hip",
 }
 
 
@@ -39,6 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="C2", choices=["C1", "C2", "C3", "C4", "C5"])
     ap.add_argument("--fused", action="store_true", help="fused long-run countdown path")
+    ap.add_argument("--bwd-hist", action="store_true",
+                    help="histogram-reuse backward (one small table: C4), no preprocessing")
     ap.add_argument("--schedule", default="serial", choices=["overlap", "fork", "serial"],
                     help="overlap: tbe_preprocess on a side stream during tbe_forward, then "
                          "tbe_backward_rowwise_adagrad on preprocessed data with its run "
@@ -171,6 +174,16 @@ def byte_model(spec, st, hist_path):
         lg["bwd_long_update"] += upd
     comp.update(c)
     logi.update(lg)
+    # histogram-reuse backward (one table): indices, offsets, (per-sample weights),
+    # grad_out once, the partials written and read once, each touched row updated
+    if T == 1:
+        D, E = spec.dims[0], spec.rows[0]
+        nwg = min(1024, -(-B // 128))
+        comp["bwd_hist_partial"] = (N * (si + 4 * psi) + (B + 1) * si + B * D * 4
+                                    + nwg * E * (D + 1) * 4)
+        comp["bwd_hist_update"] = nwg * E * (D + 1) * 4 + U * (2 * D * sw + 8)
+        logi["bwd_hist_partial"] = comp["bwd_hist_partial"]
+        logi["bwd_hist_update"] = comp["bwd_hist_update"]
     comp["bwd_chunk_fused"] = c["bwd_chunk"] + c["bwd_long_update"]
     logi["bwd_chunk_fused"] = lg["bwd_chunk"] + lg["bwd_long_update"]
     return comp, logi
@@ -280,7 +293,7 @@ def main():
     tb = te.TBE(spec.rows, spec.dims, spec.pooling, W, M)
     ws = tb.workspace(spec.B, N)
     out = torch.empty((spec.B, spec.dtot), dtype=torch.float32, device="cuda")
-    flags = te.TBE_BWD_FUSED_LONG if args.fused else 0
+    flags = (te.TBE_BWD_FUSED_LONG if args.fused else 0) | (te.TBE_BWD_HIST if args.bwd_hist else 0)
     overlap = args.schedule == "overlap"
     conc = 0 if args.schedule == "serial" else te.TBE_BWD_CONCURRENT
     hist = (spec.T == 1 and spec.rows[0] <= 64 and 64 <= spec.dims[0] <= 128
@@ -366,6 +379,7 @@ def main():
                    "lookups": N, "tables": spec.T, "bags_per_table": spec.B,
                    "index_type": spec.itype, "long_run_path": "fused" if args.fused else
                    "two-launch", "schedule": args.schedule,
+                   "backward": "histogram-reuse contraction" if args.bwd_hist else "run pipeline",
                    "step": {"overlap": "tbe_forward || tbe_preprocess (side stream), then "
                                        "tbe_backward_rowwise_adagrad(PREPROCESSED) with medium "
                                        "runs and long runs on two side streams",

@@ -91,6 +91,7 @@ extern "C" {
 #define TBE_BWD_CONCURRENT 0x4u    /* run classes on three streams (fork from and join into `stream`) */
 #define TBE_BWD_ORDER_CHUNKS 0x8u  /* always walk each table's chunks in bag order (see below) */
 #define TBE_BWD_NO_ORDER_CHUNKS 0x10u /* never: walk chunks in list order */
+#define TBE_BWD_HIST 0x20u       /* histogram-reuse backward (one small table; see below) */
 
 typedef struct tbe_plan tbe_plan;
 
@@ -197,7 +198,15 @@ int tbe_preprocess(const tbe_plan* plan, int64_t B, int32_t itype, const void* i
  * lookup keeps the rows in use within that XCD's L2.  This is done when
  * grad_out (B x sum D x 4 bytes) exceeds 256 MiB, or always with
  * TBE_BWD_ORDER_CHUNKS, never with TBE_BWD_NO_ORDER_CHUNKS (both: TBE_E_ARG); the order changes
- * no result bit. */
+ * no result bit.
+ * TBE_BWD_HIST: for a plan with one table of at most 64 rows and D a
+ * multiple of 16 up to 128 (else TBE_E_UNSUPPORTED), the weight gradient is
+ * computed as one contraction over the bags, grad[e][d] = sum_j C[j][e] *
+ * grad_out[j][d] with C the per-bag sums of S[p] * (1/L if mean) of row e's
+ * lookups, on the matrix cores (fp32 inputs), then row-wise Adagrad on the
+ * rows with a lookup; no preprocessing (the workspace's preprocessing results
+ * are neither used nor written).  Sums run in another order than the run
+ * pipeline's, so the two agree within rounding, not bit for bit. */
 int tbe_backward_rowwise_adagrad(const tbe_plan* plan, int64_t B, int32_t itype,
                                  const void* indices, const void* offsets, int64_t num_lookups,
                                  const float* per_sample_weights, const float* grad_out, float lr,

@@ -39,6 +39,7 @@ struct tbe_plan {
   std::vector<Bucket> buckets;
   uint32_t pstride;
   TableDev* d_tables;
+  std::vector<TableDev> h_tables;  // host copy of the table descriptors
   uint32_t* d_order;
   uint32_t* d_tseg;
   uint32_t* d_bkb;
@@ -72,6 +73,12 @@ int ilog2(uint64_t x) {
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Plans the histogram-reuse backward serves: one table of at most 64 rows,
+// D a multiple of 16 up to 128.
+bool bwd_hist_capable(const tbe_plan* P) {
+  return P->T == 1 && P->rows[0] <= 64 && P->dims[0] % 16 == 0 && P->dims[0] <= 128;
+}
 
 WsLayout layout(const tbe_plan* P, int64_t N) {
   WsLayout L{};
@@ -120,6 +127,9 @@ WsLayout layout(const tbe_plan* P, int64_t N) {
   L.partial = take((size_t)L.max_chunks * L.pstride * 4);
   L.counters = take((size_t)(kCntBegins + kNumLists * (P->buckets.size() + 1)) * 4);
   L.chunk_perm = take((size_t)L.max_chunks * 4);
+  const bool hc = bwd_hist_capable(P);
+  L.hist_part = take(hc ? (size_t)kHistMaxWorkgroups * 64 * L.pstride * 4 : 0);
+  L.hist_cnt = take(hc ? (size_t)kHistMaxWorkgroups * 64 * 4 : 0);
   L.total = off;
   return L;
 }
@@ -423,6 +433,7 @@ int tbe_plan_create(tbe_plan** out, int32_t T, const int64_t* rows, const int32_
     for (uint32_t t : P->buckets[b].tables) td[t].bucket = b;
   }
   bkb[nb] = (uint32_t)std::min<uint64_t>(sum_rows, 0xffffffffull);
+  P->h_tables = td;
 
   // segment of each table: its position in key order
   std::vector<uint32_t> tseg(T);
@@ -595,8 +606,9 @@ int tbe_backward_rowwise_adagrad(const tbe_plan* P, int64_t B, int32_t itype,
   rc = check_ws(P, N, ws, ws_bytes);
   if (rc) return rc;
   if (flags & ~(TBE_BWD_PREPROCESSED | TBE_BWD_FUSED_LONG | TBE_BWD_CONCURRENT |
-                TBE_BWD_ORDER_CHUNKS | TBE_BWD_NO_ORDER_CHUNKS))
+                TBE_BWD_ORDER_CHUNKS | TBE_BWD_NO_ORDER_CHUNKS | TBE_BWD_HIST))
     return TBE_E_ARG;
+  if ((flags & TBE_BWD_HIST) && !bwd_hist_capable(P)) return TBE_E_UNSUPPORTED;
   if ((flags & TBE_BWD_ORDER_CHUNKS) && (flags & TBE_BWD_NO_ORDER_CHUNKS)) return TBE_E_ARG;
   if (B > 0 && (!grad_out || !aligned(grad_out, 16))) return TBE_E_ARG;
   if (psw && !aligned(psw, 4)) return TBE_E_ARG;
@@ -605,6 +617,29 @@ int tbe_backward_rowwise_adagrad(const tbe_plan* P, int64_t B, int32_t itype,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const WsLayout L = layout(P, N);
   uint8_t* w = reinterpret_cast<uint8_t*>(ws);
+  if (flags & TBE_BWD_HIST) {  // no preprocessing: one contraction and a row update
+    HistArgs h{};
+    h.table = P->h_tables[0];
+    h.B = B;
+    h.indices = indices;
+    h.offsets = offsets;
+    h.psw = psw;
+    h.grad = grad_out;
+    h.dtot = P->dtot;
+    h.col = P->col[0];
+    h.N = (uint32_t)N;
+    h.E = (uint32_t)P->rows[0];
+    h.D = (uint32_t)P->dims[0];
+    h.mean = P->pooling[0] == TBE_MEAN;
+    h.lr = lr;
+    h.eps = eps;
+    h.part = reinterpret_cast<float*>(w + L.hist_part);
+    h.pcnt = reinterpret_cast<uint32_t*>(w + L.hist_cnt);
+    h.pstride = L.pstride;
+    h.nwg = (uint32_t)std::min<int64_t>(kHistMaxWorkgroups, (B + 127) / 128);
+    h.debug_count = debug_row_updates;
+    return launch_backward_hist(h, itype, P->wdtype, s) == hipSuccess ? TBE_OK : TBE_E_HIP;
+  }
   if (!(flags & TBE_BWD_PREPROCESSED)) {
     PrepArgs pa = prep_args(P, B, itype, indices, offsets, N, psw, ws, &L);
     if (launch_preprocess(pa, P->num_cus, s) != hipSuccess) return TBE_E_HIP;

@@ -102,6 +102,7 @@ struct WsLayout {
   size_t single_task, tiny_task, med_task, long_task, long_cbeg, remaining, chunk_task;
   size_t partial, counters;
   size_t chunk_perm;  // max_chunks uint32: chunk list position taken at each walk position
+  size_t hist_part, hist_cnt;  // histogram backward: partial rows and row counts (or 0 bytes)
   size_t total;
   uint32_t ntiles;          // ceil(N / kTile)
   uint32_t nrle_tiles;      // ceil(N / kRleTile): tiles of the run-length pass
@@ -321,6 +322,26 @@ struct BwdArgs {
   uint32_t max_single, max_tiny, max_med, max_long, max_chunks;  // list capacities
 };
 
+// Histogram-reuse backward of a plan with one table of at most 64 rows and
+// D <= 128, D a multiple of 16.
+struct HistArgs {
+  TableDev table;
+  int64_t B;
+  const void* indices;
+  const void* offsets;
+  const float* psw;       // nullable
+  const float* grad;
+  uint32_t dtot, col;     // grad_out row stride and the table's first column
+  uint32_t N, E, D;
+  int mean;
+  float lr, eps;
+  float* part;            // nwg x E partial rows of pstride floats
+  uint32_t* pcnt;         // nwg x E lookup counts
+  uint32_t pstride, nwg;
+  uint32_t* debug_count;  // nullable, per linear key
+};
+constexpr uint32_t kHistMaxWorkgroups = 1024;
+
 // One forward launch for the buckets of S (S.gbeg filled: bags of bucket k
 // over workgroups [gbeg[k], gbeg[k+1])).
 hipError_t launch_forward_set(const FwdArgs& a, const BucketSet& S, int wd, int vec, int nc,
@@ -341,6 +362,7 @@ struct BwdGrids {
 // may be the same stream).
 hipError_t launch_backward_set(const BwdArgs& a, BucketSet S, const BwdGrids* g, int wd, int vec,
                                int nc, bool fused, int num_cus, const hipStream_t* s);
+hipError_t launch_backward_hist(const HistArgs& h, int itype, int wd, hipStream_t s);
 // Orders each (table, XCD residue) class of the chunk list by the bag of the
 // chunks' first lookups into a.chunk_perm (no-op when a.chunk_perm is null).
 hipError_t launch_chunk_order(const BwdArgs& a, hipStream_t s);

@@ -339,3 +339,65 @@ def test_chunk_order_changes_no_bit(name, fused):
                     assert np.all(np.diff(bins) >= 0), "walk not in bag order"
         tb.close()
     assert res[0] == res[1]
+
+
+def _hist_spec(name):
+    # one small table: E rows, D a multiple of 16 up to 128
+    if name == "hist_c4":
+        return wl.config("C4", B=2048)
+    if name == "hist_mean_psw":
+        return wl.Spec("hist_mean_psw", 2011, [37], [48], [1], "bf16", 777, "uniform:0:150",
+                       "uniform", "i64", True)
+    if name == "hist_f32_d16":
+        return wl.Spec("hist_f32_d16", 2012, [64], [16], [0], "f32", 300, "poisson:20:+1",
+                       "zipf:1.2", "i32", False)
+    if name == "hist_one_row":
+        return wl.Spec("hist_one_row", 2013, [1], [128], [0], "f16", 129, "fixed:3", "uniform",
+                       "i32", True)
+    if name == "hist_many_bags":
+        # more bags than 256 workgroups x 128: every workgroup takes several blocks
+        return wl.Spec("hist_many_bags", 2014, [50], [32], [1], "f16", 40000, "uniform:0:6",
+                       "zipf:1.05", "i32", False)
+    raise KeyError(name)
+
+
+HIST = ["hist_c4", "hist_mean_psw", "hist_f32_d16", "hist_one_row", "hist_many_bags"]
+
+
+@pytest.mark.parametrize("name", HIST)
+def test_backward_hist_parity(name):
+    """Histogram-reuse backward (one contraction over the bags on the matrix
+    cores) against the oracle: weights within 2 ulp (16-bit) / 1e-6 (fp32),
+    momentum within 1e-5 relative, untouched rows bit-identical, every
+    touched row updated once, repeated calls bit-identical."""
+    _announce(name, "backward hist")
+    import table_embedding_amd as te
+    case = S.Case(_hist_spec(name), m_nonzero=True)
+    res = []
+    for rep in range(2):
+        case.reset_tables()
+        tb = case.tbe()
+        dbg = torch.zeros(sum(case.spec.rows), dtype=torch.int32, device="cuda")
+        tb.backward(case.spec.B, case.d_idx, case.d_off, case.d_psw, case.d_G, case.spec.lr,
+                    case.spec.eps, flags=te.TBE_BWD_HIST, debug_row_updates=dbg)
+        torch.cuda.synchronize()
+        if rep == 0:
+            S.check_backward(case, tb)
+            want = np.zeros(case.spec.rows[0], np.int32)
+            want[S.touched_rows(case, 0)] = 1
+            assert np.array_equal(dbg.cpu().numpy(), want), "each touched row once"
+        res.append(_tables_bytes(tb, case.spec.wdtype))
+        tb.close()
+    assert res[0] == res[1]
+
+
+def test_backward_hist_unsupported():
+    """A plan the histogram backward does not serve is refused before any launch."""
+    import table_embedding_amd as te
+    case = S.Case(_spec("C2s"))
+    tb = case.tbe()
+    with pytest.raises(te.TBEError) as ei:
+        tb.backward(case.spec.B, case.d_idx, case.d_off, case.d_psw, case.d_G, case.spec.lr,
+                    case.spec.eps, flags=te.TBE_BWD_HIST)
+    assert ei.value.code == te.TBE_E_UNSUPPORTED
+    tb.close()
