@@ -30,6 +30,7 @@ KERNEL_SOURCES = {
     "bwd_tiny": "bwd.hip", "bwd_medium": "bwd.hip", "bwd_chunk": "bwd.hip",
     "bwd_long_update": "bwd.hip", "bwd_chunk_fused": "bwd.hip",
     "bwd_hist_partial": "bwd_hist.hip", "bwd_hist_update": "bwd_hist.hip",
+    "validate_check": "validate.hip",
 }
 
 
@@ -40,6 +41,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="C2", choices=["C1", "C2", "C3", "C4", "C5"])
     ap.add_argument("--fused", action="store_true", help="fused long-run countdown path")
+    ap.add_argument("--validate", action="store_true",
+                    help="run tbe_validate (check only) at the start of every step")
     ap.add_argument("--bwd-hist", action="store_true",
                     help="histogram-reuse backward (one small table: C4), no preprocessing")
     ap.add_argument("--schedule", default="serial", choices=["overlap", "fork", "serial"],
@@ -184,6 +187,8 @@ def byte_model(spec, st, hist_path):
         comp["bwd_hist_update"] = nwg * E * (D + 1) * 4 + U * (2 * D * sw + 8)
         logi["bwd_hist_partial"] = comp["bwd_hist_partial"]
         logi["bwd_hist_update"] = comp["bwd_hist_update"]
+    comp["validate_clear"] = 16
+    comp["validate_check"] = N * si + (T * B + 1) * si + 16
     comp["bwd_chunk_fused"] = c["bwd_chunk"] + c["bwd_long_update"]
     logi["bwd_chunk_fused"] = lg["bwd_chunk"] + lg["bwd_long_update"]
     return comp, logi
@@ -299,7 +304,11 @@ def main():
     hist = (spec.T == 1 and spec.rows[0] <= 64 and 64 <= spec.dims[0] <= 128
             and spec.wdtype == "f16" and not spec.weighted and N >= 64 * spec.B)
 
+    err = torch.zeros(te.TBE_VALIDATE_WORDS, dtype=torch.int32, device="cuda")
+
     def step():
+        if args.validate:
+            te.tbe_validate(tb.plan, spec.B, d_idx, d_off, N, err)
         if overlap:
             tb.forward_and_preprocess(spec.B, d_idx, d_off, psw, out)
             te.tbe_backward_rowwise_adagrad(tb.plan, spec.B, d_idx, d_off, N, psw, G, spec.lr,
@@ -380,6 +389,7 @@ def main():
                    "index_type": spec.itype, "long_run_path": "fused" if args.fused else
                    "two-launch", "schedule": args.schedule,
                    "backward": "histogram-reuse contraction" if args.bwd_hist else "run pipeline",
+                   "input_validation": bool(args.validate),
                    "step": {"overlap": "tbe_forward || tbe_preprocess (side stream), then "
                                        "tbe_backward_rowwise_adagrad(PREPROCESSED) with medium "
                                        "runs and long runs on two side streams",

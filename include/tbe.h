@@ -213,6 +213,34 @@ int tbe_backward_rowwise_adagrad(const tbe_plan* plan, int64_t B, int32_t itype,
                                  float eps, void* ws, size_t ws_bytes, uint32_t flags,
                                  uint32_t* debug_row_updates, void* stream);
 
+/* Input validation and optional repair (FBTriton page, "Forward": the kernels
+ * assume their inputs; an optional bounds check and offset repair is a
+ * separate pass).  Checks the contract every other entry point assumes:
+ * O[0] = 0, O[T*B] = num_lookups, O non-decreasing, offsets in
+ * [0, num_lookups], and every index of table t's bags in [0, R_t).  err:
+ * device, TBE_VALIDATE_WORDS uint32, overwritten: [0] OR of the
+ * TBE_INVALID_* bits found (0: the inputs keep the contract), [1] number of
+ * indices out of range (every position once, against the table whose start
+ * offset O[t*B], clamped into [0, num_lookups], is the last at or before it),
+ * [2] first bag j (table-major) with a finding (the start offset counts as
+ * bag 0's, the end offset as the last bag's), [3] first position p of an
+ * index out of range (0xffffffff if none).  With TBE_VALIDATE_REPAIR the
+ * inputs are then rewritten in place: every index out of range becomes row 0
+ * of its table (bags keep their lengths), offsets are clamped into
+ * [0, num_lookups] with O[0] = 0 and O[T*B] = num_lookups; offsets out of
+ * order are reported, not repaired.  Reads every offset and index once; every
+ * access is clamped, so invalid inputs are read safely.  Errors: TBE_E_ARG,
+ * TBE_E_RANGE (as tbe_forward), TBE_E_HIP. */
+#define TBE_VALIDATE_REPAIR 0x1u
+#define TBE_VALIDATE_WORDS 4
+#define TBE_INVALID_OFFSET_START 0x1u  /* O[0] != 0 */
+#define TBE_INVALID_OFFSET_END 0x2u    /* O[T*B] != num_lookups */
+#define TBE_INVALID_OFFSET_ORDER 0x4u  /* some O[j] > O[j+1] */
+#define TBE_INVALID_OFFSET_RANGE 0x8u  /* some offset outside [0, num_lookups] */
+#define TBE_INVALID_INDEX 0x10u        /* some index outside [0, R_t) */
+int tbe_validate(const tbe_plan* plan, int64_t B, int32_t itype, void* indices, void* offsets,
+                 int64_t num_lookups, uint32_t* err, uint32_t flags, void* stream);
+
 /* Kernel timing for benchmarks and tools, off by default.  While enabled,
  * every kernel launch of the library is bracketed by two HIP events recorded
  * on the stream it is launched on (adds a little enqueue work per launch).

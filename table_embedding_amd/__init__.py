@@ -20,7 +20,9 @@ from ._lib import (  # noqa: F401
     TBEError, lib, tbe_backward_rowwise_adagrad, tbe_forward, tbe_plan_create,
     tbe_plan_destroy, tbe_plan_key_bases, tbe_preprocess, tbe_prof_calibrate, tbe_prof_enable,
     tbe_prof_read,
-    tbe_status_string,
+    tbe_status_string, tbe_validate, TBE_VALIDATE_REPAIR, TBE_VALIDATE_WORDS,
+    TBE_INVALID_OFFSET_START, TBE_INVALID_OFFSET_END, TBE_INVALID_OFFSET_ORDER,
+    TBE_INVALID_OFFSET_RANGE, TBE_INVALID_INDEX,
     tbe_workspace_size, tbe_workspace_views)
 
 

@@ -30,7 +30,7 @@ TBE_BWD_HIST = 0x20
 
 EXPORTS = ("tbe_plan_create", "tbe_plan_destroy", "tbe_plan_key_bases", "tbe_workspace_size",
            "tbe_workspace_views", "tbe_forward", "tbe_preprocess",
-           "tbe_backward_rowwise_adagrad", "tbe_prof_enable", "tbe_prof_read",
+           "tbe_backward_rowwise_adagrad", "tbe_validate", "tbe_prof_enable", "tbe_prof_read",
            "tbe_prof_calibrate", "tbe_status_string")
 TBE_PROF_NAME_LEN = 32
 
@@ -75,6 +75,7 @@ def lib() -> C.CDLL:
         L.tbe_backward_rowwise_adagrad.argtypes = [vp, i64, i32, vp, vp, i64, vp, vp,
                                                    C.c_float, C.c_float, vp, C.c_size_t, u32,
                                                    vp, vp]
+        L.tbe_validate.argtypes = [vp, i64, i32, vp, vp, i64, vp, u32, vp]
         L.tbe_prof_enable.argtypes = [C.c_int]
         L.tbe_prof_read.argtypes = [i32, vp, vp, vp, C.POINTER(i32)]
         L.tbe_prof_calibrate.argtypes = [i32, vp]
@@ -183,6 +184,25 @@ def tbe_forward(plan, B: int, indices, offsets, num_lookups: int, per_sample_wei
                            _dptr(per_sample_weights, torch.float32, "per_sample_weights"),
                            _dptr(out, torch.float32, "out"), int(flags), _stream(stream))
     _check("tbe_forward", rc)
+
+
+TBE_VALIDATE_REPAIR = 0x1
+TBE_VALIDATE_WORDS = 4
+TBE_INVALID_OFFSET_START, TBE_INVALID_OFFSET_END, TBE_INVALID_OFFSET_ORDER = 0x1, 0x2, 0x4
+TBE_INVALID_OFFSET_RANGE, TBE_INVALID_INDEX = 0x8, 0x10
+
+
+def tbe_validate(plan, B: int, indices, offsets, num_lookups: int, err: torch.Tensor,
+                 flags: int = 0, stream=None) -> None:
+    """Check (and with TBE_VALIDATE_REPAIR repair in place) the lookup
+    contract; err: device int32 tensor of TBE_VALIDATE_WORDS words."""
+    it = _itype(indices, offsets)
+    if err.numel() < TBE_VALIDATE_WORDS:
+        raise ValueError("err needs TBE_VALIDATE_WORDS words")
+    rc = lib().tbe_validate(plan, int(B), it, _dptr(indices, None, "indices"),
+                            _dptr(offsets, None, "offsets"), int(num_lookups),
+                            _dptr(err, None, "err"), int(flags), _stream(stream))
+    _check("tbe_validate", rc)
 
 
 def tbe_preprocess(plan, B: int, indices, offsets, num_lookups: int, per_sample_weights,

@@ -580,6 +580,24 @@ int tbe_forward(const tbe_plan* P, int64_t B, int32_t itype, const void* indices
   return e == hipSuccess ? TBE_OK : TBE_E_HIP;
 }
 
+int tbe_validate(const tbe_plan* P, int64_t B, int32_t itype, void* indices, void* offsets,
+                 int64_t N, uint32_t* err, uint32_t flags, void* stream) {
+  static_assert(kValWords == TBE_VALIDATE_WORDS && kValOffsetStart == TBE_INVALID_OFFSET_START &&
+                    kValOffsetEnd == TBE_INVALID_OFFSET_END &&
+                    kValOffsetOrder == TBE_INVALID_OFFSET_ORDER &&
+                    kValOffsetRange == TBE_INVALID_OFFSET_RANGE &&
+                    kValIndexRange == TBE_INVALID_INDEX,
+                "validation words and bits of the header");
+  int rc = check_lookups(P, B, itype, indices, offsets, N);
+  if (rc) return rc;
+  if (!err || !aligned(err, 4)) return TBE_E_ARG;
+  if (flags & ~TBE_VALIDATE_REPAIR) return TBE_E_ARG;
+  ValArgs v{P->d_tables, (uint32_t)P->T, B, indices, offsets, N};
+  const hipError_t e = launch_validate(v, itype, err, (flags & TBE_VALIDATE_REPAIR) != 0,
+                                       reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TBE_OK : TBE_E_HIP;
+}
+
 int tbe_preprocess(const tbe_plan* P, int64_t B, int32_t itype, const void* indices,
                    const void* offsets, int64_t N, const float* psw, void* ws, size_t ws_bytes,
                    void* stream) {

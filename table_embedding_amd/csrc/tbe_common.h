@@ -342,6 +342,22 @@ struct HistArgs {
 };
 constexpr uint32_t kHistMaxWorkgroups = 1024;
 
+// Input validation (tbe_validate): error block words and bits.
+constexpr int kValWords = 4;
+constexpr int kValBits = 0, kValBadIndices = 1, kValFirstBag = 2, kValFirstPos = 3;
+constexpr uint32_t kValOffsetStart = 0x1u, kValOffsetEnd = 0x2u, kValOffsetOrder = 0x4u,
+                   kValOffsetRange = 0x8u, kValIndexRange = 0x10u;
+struct ValArgs {
+  const TableDev* tables;
+  uint32_t T;
+  int64_t B;
+  void* indices;
+  void* offsets;
+  int64_t N;
+};
+hipError_t launch_validate(const ValArgs& v, int itype, uint32_t* err, bool repair,
+                           hipStream_t s);
+
 // One forward launch for the buckets of S (S.gbeg filled: bags of bucket k
 // over workgroups [gbeg[k], gbeg[k+1])).
 hipError_t launch_forward_set(const FwdArgs& a, const BucketSet& S, int wd, int vec, int nc,

@@ -35,6 +35,15 @@ def test_library_exports_every_declared_symbol():
     assert set(declared_functions()) == set(te.EXPORTS)
 
 
+def test_every_entry_point_has_declared_argument_types():
+    """Without argtypes ctypes passes Python ints as C int, masked to 32 bits:
+    a device pointer would reach the library truncated."""
+    import table_embedding_amd as te
+    L = te.lib()
+    for n in te.EXPORTS:
+        assert getattr(L, n).argtypes is not None, n
+
+
 def test_status_strings():
     import table_embedding_amd as te
     assert te.tbe_status_string(0) == "ok"
