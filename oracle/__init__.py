@@ -59,6 +59,10 @@ def lib():
         L.oracle_backward_rowwise_adagrad.argtypes = (
             [i32, vp, vp, vp, i32, vp, vp, i64, i32, vp, vp, vp, vp, i64, C.c_float, C.c_float])
         L.oracle_backward_rowwise_adagrad.restype = C.c_int
+        L.oracle_backward.argtypes = (
+            [i32, vp, vp, vp, i32, vp, vp, i64, i32, vp, vp, vp, vp, i64, i32, C.c_float,
+             C.c_float])
+        L.oracle_backward.restype = C.c_int
         _lib = L
     return _lib
 
@@ -153,6 +157,38 @@ def preprocess(rows, B, itype, indices, offsets):
                 run_start=rstart[:U + 1], run_key=rkey[:U], short_list=sl[:ns],
                 long_list=ll[:nl], chunk_long=cl[:nc], chunk_start=cs[:nc], chunk_len=cn[:nc],
                 U=U, n_short=ns, n_long=nl, n_chunks=nc)
+
+
+OPTIMIZERS = {"rowwise_adagrad": 0, "adagrad": 1, "sgd": 2}
+
+
+def backward(rows, dims, pooling, wdtype, weights, state, B, itype, indices, offsets, psw, grad,
+             lr, eps, optimizer="rowwise_adagrad", grad_stride=None):
+    """Updates weights (storage arrays) and the optimizer state in place:
+    rowwise_adagrad: state[t] float32 [R_t]; adagrad (element-wise): float32
+    [R_t, D_t]; sgd: state ignored (None)."""
+    T = len(rows)
+    rows_a = np.asarray(rows, np.int64)
+    dims_a = np.asarray(dims, np.int32)
+    pool_a = np.asarray(pooling, np.int32)
+    for a in weights:
+        assert a.flags["C_CONTIGUOUS"] and a.dtype == _storage(wdtype)
+    opt = OPTIMIZERS[optimizer]
+    if opt == 2:
+        state = [np.zeros(1, np.float32) for _ in range(T)]
+    for t, a in enumerate(state):
+        assert a.flags["C_CONTIGUOUS"] and a.dtype == np.float32
+        need = rows[t] * (dims[t] if opt == 1 else 1) if opt != 2 else 0
+        assert a.size >= need
+    grad = np.ascontiguousarray(grad, np.float32)
+    stride = grad_stride if grad_stride is not None else grad.shape[-1]
+    psw_a = None if psw is None else np.ascontiguousarray(psw, np.float32)
+    rc = lib().oracle_backward(
+        T, _p(rows_a), _p(dims_a), _p(pool_a), WD[wdtype], _ptr_array(weights),
+        _ptr_array(state), B, IT[itype], _p(np.ascontiguousarray(indices)),
+        _p(np.ascontiguousarray(offsets)), _p(psw_a), _p(grad), stride, opt,
+        C.c_float(lr), C.c_float(eps))
+    _check(rc, "backward")
 
 
 def backward_rowwise_adagrad(rows, dims, pooling, wdtype, weights, momentum, B, itype, indices,

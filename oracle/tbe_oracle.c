@@ -324,13 +324,27 @@ int oracle_preprocess(int32_t T, const int64_t *rows, int64_t B, int32_t itype,
  * The momentum is updated first and the new value is used; eps is outside
  * the square root.  Rows no lookup touched are left as they are.
  * ---------------------------------------------------------------------- */
-int oracle_backward_rowwise_adagrad(int32_t T, const int64_t *rows, const int32_t *dims,
-                                    const int32_t *pooling, int32_t wdtype,
-                                    void *const *weights, float *const *momentum, int64_t B,
-                                    int32_t itype, const void *indices, const void *offsets,
-                                    const float *psw, const float *grad, int64_t grad_stride,
-                                    float lr, float eps)
+/* Optimizer epilogues applied once per touched row r of table t to its
+ * gradient g[0..D) (accumulated in double):
+ *  OR_OPT_ROWWISE_ADAGRAD  (FBTriton page, "Backward"; HugeCTR step 5 as the
+ *      row-wise variant): state M[r] += mean_d g[d]^2, stored as float; then
+ *      w[d] -= lr * g[d] / (sqrt(M[r]) + eps).
+ *  OR_OPT_ADAGRAD  (HugeCTR walkthrough, step 5, the element-wise Adagrad
+ *      kernel): state A[r*D + d] += g[d]^2, stored as float; then
+ *      w[d] -= lr * g[d] / (sqrt(A[r*D + d]) + eps).
+ *  OR_OPT_SGD: w[d] -= lr * g[d]; no state.
+ * The square root and the step use the stored (float) state, as the row-wise
+ * case does. */
+enum { OR_OPT_ROWWISE_ADAGRAD = 0, OR_OPT_ADAGRAD = 1, OR_OPT_SGD = 2 };
+
+int oracle_backward(int32_t T, const int64_t *rows, const int32_t *dims,
+                    const int32_t *pooling, int32_t wdtype, void *const *weights,
+                    float *const *state, int64_t B, int32_t itype, const void *indices,
+                    const void *offsets, const float *psw, const float *grad,
+                    int64_t grad_stride, int32_t optimizer, float lr, float eps)
 {
+    if (optimizer < OR_OPT_ROWWISE_ADAGRAD || optimizer > OR_OPT_SGD)
+        return -8;
     int rc = validate(T, rows, B, itype, indices, offsets);
     if (rc)
         return rc;
@@ -389,15 +403,30 @@ int oracle_backward_rowwise_adagrad(int32_t T, const int64_t *rows, const int32_
             for (int64_t d = 0; d < D; ++d)
                 g[d] += s * (double)grad[b * grad_stride + col[t] + d];
         }
-        double sq = 0.0;
-        for (int64_t d = 0; d < D; ++d)
-            sq += g[d] * g[d];
-        float *M = momentum[t];
-        M[r] = (float)((double)M[r] + sq / (double)D);
-        double denom = sqrt((double)M[r]) + (double)eps;
-        for (int64_t d = 0; d < D; ++d) {
-            double w = oracle_decode(wdtype, weights[t], r * D + d);
-            oracle_store(wdtype, weights[t], r * D + d, w - (double)lr * g[d] / denom);
+        if (optimizer == OR_OPT_ROWWISE_ADAGRAD) {
+            double sq = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                sq += g[d] * g[d];
+            float *M = state[t];
+            M[r] = (float)((double)M[r] + sq / (double)D);
+            double denom = sqrt((double)M[r]) + (double)eps;
+            for (int64_t d = 0; d < D; ++d) {
+                double w = oracle_decode(wdtype, weights[t], r * D + d);
+                oracle_store(wdtype, weights[t], r * D + d, w - (double)lr * g[d] / denom);
+            }
+        } else if (optimizer == OR_OPT_ADAGRAD) {
+            float *A = state[t];
+            for (int64_t d = 0; d < D; ++d) {
+                A[r * D + d] = (float)((double)A[r * D + d] + g[d] * g[d]);
+                double denom = sqrt((double)A[r * D + d]) + (double)eps;
+                double w = oracle_decode(wdtype, weights[t], r * D + d);
+                oracle_store(wdtype, weights[t], r * D + d, w - (double)lr * g[d] / denom);
+            }
+        } else {
+            for (int64_t d = 0; d < D; ++d) {
+                double w = oracle_decode(wdtype, weights[t], r * D + d);
+                oracle_store(wdtype, weights[t], r * D + d, w - (double)lr * g[d]);
+            }
         }
     }
     rc = 0;
@@ -405,4 +434,15 @@ done:
     free(key); free(skey); free(rkey); free(bag); free(spos); free(rstart); free(sl);
     free(ll); free(cl); free(cs); free(cn); free(base); free(col); free(g);
     return rc;
+}
+
+int oracle_backward_rowwise_adagrad(int32_t T, const int64_t *rows, const int32_t *dims,
+                                    const int32_t *pooling, int32_t wdtype,
+                                    void *const *weights, float *const *momentum, int64_t B,
+                                    int32_t itype, const void *indices, const void *offsets,
+                                    const float *psw, const float *grad, int64_t grad_stride,
+                                    float lr, float eps)
+{
+    return oracle_backward(T, rows, dims, pooling, wdtype, weights, momentum, B, itype, indices,
+                           offsets, psw, grad, grad_stride, OR_OPT_ROWWISE_ADAGRAD, lr, eps);
 }

@@ -78,3 +78,25 @@ def adagrad(p):
         for d in range(D):
             W[t][r, d] = W[t][r, d] - lr * g[d] / den
     return W, M, set(grads)
+
+
+def update(p, optimizer, state0=None):
+    """SGD or element-wise Adagrad applied once per touched row (HugeCTR
+    walkthrough, step 5: the element-wise accumulator A[r, d] += g[d]^2,
+    stored as float32, eps outside the root).  Returns (W float64 before
+    storage rounding, state float64 or None, touched keys)."""
+    grads = row_gradients(p)
+    W = [w.copy() for w in p["Wf64"]]
+    A = None if optimizer == "sgd" else [a.astype(np.float64).copy() for a in state0]
+    lr = float(np.float32(p["lr"]))
+    eps = float(np.float32(p["eps"]))
+    for (t, r), g in grads.items():
+        D = p["dims"][t]
+        for d in range(D):
+            if optimizer == "sgd":
+                W[t][r, d] = W[t][r, d] - lr * g[d]
+            else:
+                a = float(np.float32(A[t][r, d] + g[d] * g[d]))
+                A[t][r, d] = a
+                W[t][r, d] = W[t][r, d] - lr * g[d] / (math.sqrt(a) + eps)
+    return W, A, set(grads)

@@ -148,6 +148,64 @@ def test_worked_example_adagrad_closed_form(m0, eps):
         np.testing.assert_array_equal(W[r], want.astype(np.float32))
 
 
+@pytest.mark.parametrize("a0,eps", [(0.0, 1e-8), (2.0, 0.5)])
+def test_worked_example_elementwise_adagrad_and_sgd_closed_form(a0, eps):
+    """With every entry of a row gradient equal to c: element-wise Adagrad
+    A' = A + c^2 per entry and W' = W - lr*c/(sqrt(A') + eps); SGD W' = W - lr*c;
+    untouched rows (and their state) unchanged."""
+    off, idx = _we()
+    R, D, B = GOLD["rows"], GOLD["dim"], GOLD["B"]
+    rng = np.random.default_rng(5)
+    W0 = (rng.random((R, D), dtype=np.float32) * 0.2 - 0.1).astype(np.float32)
+    G = np.repeat(np.arange(1, B + 1, dtype=np.float32)[:, None], D, axis=1)
+    lr = 0.01
+    W = W0.copy()
+    A = np.full((R, D), a0, np.float32)
+    oracle.backward([R], [D], [0], "f32", [W], [A], B, "i64", idx, off, None, G, lr, eps,
+                    optimizer="adagrad")
+    assert W[0].tobytes() == W0[0].tobytes() and np.all(A[0] == np.float32(a0))
+    for r, c in ROW_GRAD.items():
+        a = np.float32(a0 + c * c)
+        assert np.all(A[r] == a)
+        want = (W0[r].astype(np.float64)
+                - float(np.float32(lr)) * c / (math.sqrt(float(a)) + float(np.float32(eps))))
+        np.testing.assert_array_equal(W[r], want.astype(np.float32))
+    W = W0.copy()
+    oracle.backward([R], [D], [0], "f32", [W], None, B, "i64", idx, off, None, G, lr, eps,
+                    optimizer="sgd")
+    assert W[0].tobytes() == W0[0].tobytes()
+    for r, c in ROW_GRAD.items():
+        want = W0[r].astype(np.float64) - float(np.float32(lr)) * c
+        np.testing.assert_array_equal(W[r], want.astype(np.float32))
+
+
+@pytest.mark.parametrize("optimizer", ["adagrad", "sgd"])
+@pytest.mark.parametrize("chunk", range(3))
+def test_brute_force_tiny_other_optimizers(optimizer, chunk):
+    for seed in range(chunk * 40, chunk * 40 + 40):
+        p = wl.random_tiny(seed)
+        W_st = _tiny_to_oracle(p)
+        Wn = [w.copy() for w in W_st]
+        A0 = [(np.abs(np.random.default_rng(seed).standard_normal((r, d))) * 0.1).astype(np.float32)
+              for r, d in zip(p["rows"], p["dims"])]
+        An = [a.copy() for a in A0]
+        oracle.backward(p["rows"], p["dims"], p["pooling"], p["wdtype"], Wn,
+                        An if optimizer == "adagrad" else None, p["B"], p["itype"], p["indices"],
+                        p["offsets"], p["psw"], p["G"], p["lr"], p["eps"], optimizer=optimizer)
+        Wref, Aref, touched = brute.update(p, optimizer, A0)
+        for t in range(p["T"]):
+            rows_t = sorted(r for (tt, r) in touched if tt == t)
+            untouched = np.setdiff1d(np.arange(p["rows"][t]), rows_t)
+            assert Wn[t][untouched].tobytes() == W_st[t][untouched].tobytes(), seed
+            if optimizer == "adagrad":
+                assert An[t][untouched].tobytes() == A0[t][untouched].tobytes(), seed
+            if rows_t:
+                if optimizer == "adagrad":
+                    np.testing.assert_allclose(An[t][rows_t], Aref[t][rows_t], rtol=1e-6)
+                want = wl.to_storage(Wref[t][rows_t].astype(np.float32), p["wdtype"])
+                assert ulp_diff(Wn[t][rows_t], want, p["wdtype"]).max() <= 1, seed
+
+
 def test_worked_example_mean_pooling_gradient():
     """Mean pooling scales each bag's gradient by 1/L (bag lengths 4, 3, 2, 1)."""
     off, idx = _we()
