@@ -213,6 +213,28 @@ int tbe_backward_rowwise_adagrad(const tbe_plan* plan, int64_t B, int32_t itype,
                                  float eps, void* ws, size_t ws_bytes, uint32_t flags,
                                  uint32_t* debug_row_updates, void* stream);
 
+/* Backward with a choice of optimizer epilogue: the same preprocessing and
+ * run pipeline as tbe_backward_rowwise_adagrad (which is this call with
+ * TBE_OPT_ROWWISE_ADAGRAD), only the per-row update changes.  The plan's
+ * momentum[t] buffers hold the optimizer state:
+ *  TBE_OPT_ROWWISE_ADAGRAD  R_t floats: M[r] += mean_d g^2,
+ *                           w -= lr g / (sqrt(M[r]) + eps);
+ *  TBE_OPT_ADAGRAD          element-wise (HugeCTR walkthrough, step 5):
+ *                           R_t x D_t floats, row-major, 16-byte aligned:
+ *                           A[r][d] += g[d]^2, w[d] -= lr g[d] / (sqrt(A[r][d]) + eps);
+ *  TBE_OPT_SGD              w -= lr g; the buffers are not touched.
+ * Each touched row is updated once; untouched rows and their state are not
+ * written.  TBE_BWD_HIST takes row-wise Adagrad only (else
+ * TBE_E_UNSUPPORTED).  Errors: those of tbe_backward_rowwise_adagrad, and
+ * TBE_E_ARG for another optimizer code. */
+#define TBE_OPT_ROWWISE_ADAGRAD 0
+#define TBE_OPT_ADAGRAD 1
+#define TBE_OPT_SGD 2
+int tbe_backward(const tbe_plan* plan, int64_t B, int32_t itype, const void* indices,
+                 const void* offsets, int64_t num_lookups, const float* per_sample_weights,
+                 const float* grad_out, int32_t optimizer, float lr, float eps, void* ws,
+                 size_t ws_bytes, uint32_t flags, uint32_t* debug_row_updates, void* stream);
+
 /* Input validation and optional repair (FBTriton page, "Forward": the kernels
  * assume their inputs; an optional bounds check and offset repair is a
  * separate pass).  Checks the contract every other entry point assumes:

@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     tbe_plan_destroy, tbe_plan_key_bases, tbe_preprocess, tbe_prof_calibrate, tbe_prof_enable,
     tbe_prof_read,
     tbe_status_string, tbe_validate, TBE_VALIDATE_REPAIR, TBE_VALIDATE_WORDS,
+    tbe_backward, TBE_OPT_ROWWISE_ADAGRAD, TBE_OPT_ADAGRAD, TBE_OPT_SGD,
     TBE_INVALID_OFFSET_START, TBE_INVALID_OFFSET_END, TBE_INVALID_OFFSET_ORDER,
     TBE_INVALID_OFFSET_RANGE, TBE_INVALID_INDEX,
     tbe_workspace_size, tbe_workspace_views)
@@ -30,7 +31,8 @@ class TBE:
     """One plan over caller-owned tables plus a reusable workspace.
 
     weights[t]: device [R_t, D_t] float32/float16/bfloat16; momentum[t]: device
-    [R_t] float32.  Both are updated in place by `backward`.
+    float32 optimizer state, [R_t] (row-wise Adagrad, SGD) or [R_t, D_t]
+    (element-wise Adagrad).  Both are updated in place by `backward`.
     """
 
     def __init__(self, rows: Sequence[int], dims: Sequence[int], pooling: Sequence[int],
@@ -112,8 +114,16 @@ class TBE:
     def backward(self, B: int, indices: torch.Tensor, offsets: torch.Tensor,
                  per_sample_weights: Optional[torch.Tensor], grad_out: torch.Tensor,
                  lr: float, eps: float, flags: int = 0,
-                 debug_row_updates: Optional[torch.Tensor] = None) -> None:
+                 debug_row_updates: Optional[torch.Tensor] = None,
+                 optimizer: int = TBE_OPT_ROWWISE_ADAGRAD) -> None:
+        """optimizer: TBE_OPT_ROWWISE_ADAGRAD (momentum[t] of R_t floats),
+        TBE_OPT_ADAGRAD (element-wise: momentum[t] of R_t x D_t floats) or
+        TBE_OPT_SGD (momentum untouched)."""
         ws = self.workspace(B, indices.numel())
-        tbe_backward_rowwise_adagrad(self.plan, B, indices, offsets, indices.numel(),
-                                     per_sample_weights, grad_out, lr, eps, ws, flags,
-                                     debug_row_updates)
+        if optimizer == TBE_OPT_ROWWISE_ADAGRAD:
+            tbe_backward_rowwise_adagrad(self.plan, B, indices, offsets, indices.numel(),
+                                         per_sample_weights, grad_out, lr, eps, ws, flags,
+                                         debug_row_updates)
+        else:
+            tbe_backward(self.plan, B, indices, offsets, indices.numel(), per_sample_weights,
+                         grad_out, optimizer, lr, eps, ws, flags, debug_row_updates)

@@ -30,7 +30,8 @@ TBE_BWD_HIST = 0x20
 
 EXPORTS = ("tbe_plan_create", "tbe_plan_destroy", "tbe_plan_key_bases", "tbe_workspace_size",
            "tbe_workspace_views", "tbe_forward", "tbe_preprocess",
-           "tbe_backward_rowwise_adagrad", "tbe_validate", "tbe_prof_enable", "tbe_prof_read",
+           "tbe_backward_rowwise_adagrad", "tbe_backward", "tbe_validate", "tbe_prof_enable",
+           "tbe_prof_read",
            "tbe_prof_calibrate", "tbe_status_string")
 TBE_PROF_NAME_LEN = 32
 
@@ -76,6 +77,8 @@ def lib() -> C.CDLL:
                                                    C.c_float, C.c_float, vp, C.c_size_t, u32,
                                                    vp, vp]
         L.tbe_validate.argtypes = [vp, i64, i32, vp, vp, i64, vp, u32, vp]
+        L.tbe_backward.argtypes = [vp, i64, i32, vp, vp, i64, vp, vp, i32, C.c_float, C.c_float,
+                                   vp, C.c_size_t, u32, vp, vp]
         L.tbe_prof_enable.argtypes = [C.c_int]
         L.tbe_prof_read.argtypes = [i32, vp, vp, vp, C.POINTER(i32)]
         L.tbe_prof_calibrate.argtypes = [i32, vp]
@@ -139,8 +142,9 @@ def tbe_plan_create(rows: Sequence[int], dims: Sequence[int], pooling: Sequence[
             raise TypeError("all tables must share one weight dtype")
         if tuple(weights[t].shape) != (int(rows[t]), int(dims[t])):
             raise ValueError(f"weights[{t}] must be [{rows[t]}, {dims[t]}]")
-        if tuple(momentum[t].shape) != (int(rows[t]),):
-            raise ValueError(f"momentum[{t}] must be [{rows[t]}]")
+        if tuple(momentum[t].shape) not in ((int(rows[t]),), (int(rows[t]), int(dims[t]))):
+            # [R_t] for row-wise Adagrad (and SGD), [R_t, D_t] for element-wise Adagrad
+            raise ValueError(f"momentum[{t}] must be [{rows[t]}] or [{rows[t]}, {dims[t]}]")
     rows_a = (C.c_int64 * T)(*[int(r) for r in rows])
     dims_a = (C.c_int32 * T)(*[int(d) for d in dims])
     pool_a = (C.c_int32 * T)(*[int(p) for p in pooling])
@@ -229,6 +233,23 @@ def tbe_backward_rowwise_adagrad(plan, B: int, indices, offsets, num_lookups: in
         _dptr(ws, None, "ws"), ws.numel() * ws.element_size(), int(flags),
         _dptr(debug_row_updates, torch.int32, "debug_row_updates"), _stream(stream))
     _check("tbe_backward_rowwise_adagrad", rc)
+
+
+TBE_OPT_ROWWISE_ADAGRAD, TBE_OPT_ADAGRAD, TBE_OPT_SGD = 0, 1, 2
+
+
+def tbe_backward(plan, B: int, indices, offsets, num_lookups: int, per_sample_weights,
+                 grad_out: torch.Tensor, optimizer: int, lr: float, eps: float,
+                 ws: torch.Tensor, flags: int = 0,
+                 debug_row_updates: Optional[torch.Tensor] = None, stream=None) -> None:
+    it = _itype(indices, offsets)
+    rc = lib().tbe_backward(
+        plan, int(B), it, _dptr(indices, None, "indices"), _dptr(offsets, None, "offsets"),
+        int(num_lookups), _dptr(per_sample_weights, torch.float32, "per_sample_weights"),
+        _dptr(grad_out, torch.float32, "grad_out"), int(optimizer), float(lr), float(eps),
+        _dptr(ws, None, "ws"), ws.numel() * ws.element_size(), int(flags),
+        _dptr(debug_row_updates, torch.int32, "debug_row_updates"), _stream(stream))
+    _check("tbe_backward", rc)
 
 
 def tbe_prof_enable(enable: bool) -> None:

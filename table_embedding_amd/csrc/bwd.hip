@@ -140,13 +140,42 @@ __device__ __forceinline__ TableDev get_td(const BwdArgs& a, const TableDev* s_t
   return TDL ? s_td[t] : a.tables[t];
 }
 
-// Row-wise Adagrad of one row owned by a subgroup (g: this lane's columns).
+// The update of one row owned by a subgroup (g: this lane's columns; m0:
+// the row's momentum, read by the caller for row-wise Adagrad only).
+// Row-wise Adagrad: M += mean_d g^2, w -= lr g / (sqrt(M) + eps).  Element-
+// wise Adagrad (HugeCTR walkthrough, step 5): A[row][d] += g[d]^2 per column,
+// w -= lr g / (sqrt(A) + eps).  SGD: w -= lr g, no state.
 template <int WD, int VEC, int NC>
 __device__ __forceinline__ void subgroup_row_update(const BwdArgs& a, const TableDev& td,
                                                     int64_t row, float m0, const float (*w)[VEC],
                                                     const float (*g)[VEC], const uint32_t* colc,
                                                     uint32_t lpr, uint32_t lane_in, bool store) {
   const uint32_t D = td.dim;
+  if (a.opt != OPT_ROWWISE_ADAGRAD) {  // uniform
+    if (!store) return;
+    if (lane_in == 0 && a.debug_count)
+      atomicAdd(&a.debug_count[td.key_base + (uint32_t)row], 1u);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (colc[c] >= D) continue;
+      float o[VEC];
+      if (a.opt == OPT_ADAGRAD) {
+        float acc[VEC];
+        load_f32<VEC>(td.m + row * D + colc[c], acc);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          acc[e] += g[c][e] * g[c][e];
+          o[e] = w[c][e] - (a.lr * g[c][e]) / (sqrtf(acc[e]) + a.eps);
+        }
+        store_f32<VEC>(td.m + row * D + colc[c], acc);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[e] = w[c][e] - a.lr * g[c][e];
+      }
+      store_w<WD, VEC>(td.w, row * D + colc[c], o);
+    }
+    return;
+  }
   float sq = 0.f;
 #pragma unroll
   for (int c = 0; c < NC; ++c)
@@ -218,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void bwd_single_kernel(BwdArgs a, BucketS
         load_w<WD, VEC>(td[u].w, row[u] * td[u].dim + cold[u][c], w[u][c]);
         load_f32<VEC>(a.grad + b[u] * (int64_t)a.dtot + td[u].col + cold[u][c], g[u][c]);
       }
-      m0[u] = td[u].m[row[u]];
+      m0[u] = a.opt == OPT_ROWWISE_ADAGRAD ? td[u].m[row[u]] : 0.f;
       sc[u] = SCALE ? a.sorted_scale[ok[u] ? tk[u].x : 0u] : 1.0f;
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -272,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void bwd_tiny_kernel(BwdArgs a, BucketSet
 #pragma unroll
       for (int e = 0; e < VEC; ++e) g[c][e] = 0.f;
     }
-    const float m0 = td.m[row];
+    const float m0 = a.opt == OPT_ROWWISE_ADAGRAD ? td.m[row] : 0.f;
     gather<VEC, NC>(a, td, (int64_t)t * a.B, start, start + len, 1u, cold, g);
     subgroup_row_update<WD, VEC, NC>(a, td, row, m0, w, g, colc, lpr, lane_in, true);
   }
@@ -331,11 +360,37 @@ __device__ __forceinline__ float red_to_gsum(const BucketDev& bk, uint32_t D,
   return sqp;
 }
 
-// Row-wise Adagrad of one row from sm.gsum, all threads of the workgroup.
+// The update of one row from sm.gsum, all threads of the workgroup (the
+// optimizers of subgroup_row_update).
 template <int WD, int VEC, int NC>
 __device__ __forceinline__ void wg_row_update(const BwdArgs& a, const TableDev& td, int64_t row,
                                               float sqp, WgSmem<VEC, NC>& sm) {
   const uint32_t D = td.dim;
+  if (a.opt != OPT_ROWWISE_ADAGRAD) {  // uniform
+    for (uint32_t col = threadIdx.x * VEC; col < D; col += kThreads * VEC) {
+      float w[VEC], o[VEC];
+      load_w<WD, VEC>(td.w, row * D + col, w);
+      if (a.opt == OPT_ADAGRAD) {
+        float acc[VEC];
+        load_f32<VEC>(td.m + row * D + col, acc);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float gv = sm.gsum[col + e];
+          acc[e] += gv * gv;
+          o[e] = w[e] - (a.lr * gv) / (sqrtf(acc[e]) + a.eps);
+        }
+        store_f32<VEC>(td.m + row * D + col, acc);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[e] = w[e] - a.lr * sm.gsum[col + e];
+      }
+      store_w<WD, VEC>(td.w, row * D + col, o);
+    }
+    __syncthreads();  // every thread has read sm before it changes
+    if (threadIdx.x == 0 && a.debug_count)
+      atomicAdd(&a.debug_count[td.key_base + (uint32_t)row], 1u);
+    return;
+  }
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) sqp += __shfl_xor(sqp, o, kWave);
   if (lane_id() == 0) sm.wsq[threadIdx.x / kWave] = sqp;

@@ -614,11 +614,16 @@ int tbe_preprocess(const tbe_plan* P, int64_t B, int32_t itype, const void* indi
   return e == hipSuccess ? TBE_OK : TBE_E_HIP;
 }
 
-int tbe_backward_rowwise_adagrad(const tbe_plan* P, int64_t B, int32_t itype,
-                                 const void* indices, const void* offsets, int64_t N,
-                                 const float* psw, const float* grad_out, float lr, float eps,
-                                 void* ws, size_t ws_bytes, uint32_t flags,
-                                 uint32_t* debug_row_updates, void* stream) {
+int tbe_backward(const tbe_plan* P, int64_t B, int32_t itype, const void* indices,
+                 const void* offsets, int64_t N, const float* psw, const float* grad_out,
+                 int32_t optimizer, float lr, float eps, void* ws, size_t ws_bytes,
+                 uint32_t flags, uint32_t* debug_row_updates, void* stream) {
+  static_assert(OPT_ROWWISE_ADAGRAD == TBE_OPT_ROWWISE_ADAGRAD && OPT_ADAGRAD == TBE_OPT_ADAGRAD &&
+                    OPT_SGD == TBE_OPT_SGD,
+                "optimizer codes of the header");
+  if (optimizer != TBE_OPT_ROWWISE_ADAGRAD && optimizer != TBE_OPT_ADAGRAD &&
+      optimizer != TBE_OPT_SGD)
+    return TBE_E_ARG;
   int rc = check_lookups(P, B, itype, indices, offsets, N);
   if (rc) return rc;
   rc = check_ws(P, N, ws, ws_bytes);
@@ -626,7 +631,8 @@ int tbe_backward_rowwise_adagrad(const tbe_plan* P, int64_t B, int32_t itype,
   if (flags & ~(TBE_BWD_PREPROCESSED | TBE_BWD_FUSED_LONG | TBE_BWD_CONCURRENT |
                 TBE_BWD_ORDER_CHUNKS | TBE_BWD_NO_ORDER_CHUNKS | TBE_BWD_HIST))
     return TBE_E_ARG;
-  if ((flags & TBE_BWD_HIST) && !bwd_hist_capable(P)) return TBE_E_UNSUPPORTED;
+  if ((flags & TBE_BWD_HIST) && (!bwd_hist_capable(P) || optimizer != TBE_OPT_ROWWISE_ADAGRAD))
+    return TBE_E_UNSUPPORTED;
   if ((flags & TBE_BWD_ORDER_CHUNKS) && (flags & TBE_BWD_NO_ORDER_CHUNKS)) return TBE_E_ARG;
   if (B > 0 && (!grad_out || !aligned(grad_out, 16))) return TBE_E_ARG;
   if (psw && !aligned(psw, 4)) return TBE_E_ARG;
@@ -672,6 +678,7 @@ int tbe_backward_rowwise_adagrad(const tbe_plan* P, int64_t B, int32_t itype,
   a.dtot = P->dtot;
   a.lr = lr;
   a.eps = eps;
+  a.opt = optimizer;
   a.sorted_bag = reinterpret_cast<const uint32_t*>(w + (L.final_in_b ? L.val_b : L.val_a));
   a.sorted_scale = (psw || any_mean(P))
                        ? reinterpret_cast<const float*>(w + (L.final_in_b ? L.sc_b : L.sc_a))
@@ -742,6 +749,15 @@ int tbe_backward_rowwise_adagrad(const tbe_plan* P, int64_t B, int32_t itype,
         rc_launch = TBE_E_HIP;
   }
   return rc_launch;
+}
+
+int tbe_backward_rowwise_adagrad(const tbe_plan* P, int64_t B, int32_t itype,
+                                 const void* indices, const void* offsets, int64_t N,
+                                 const float* psw, const float* grad_out, float lr, float eps,
+                                 void* ws, size_t ws_bytes, uint32_t flags,
+                                 uint32_t* debug_row_updates, void* stream) {
+  return tbe_backward(P, B, itype, indices, offsets, N, psw, grad_out, TBE_OPT_ROWWISE_ADAGRAD, lr,
+                      eps, ws, ws_bytes, flags, debug_row_updates, stream);
 }
 
 }  // extern "C"

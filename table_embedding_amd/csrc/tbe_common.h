@@ -27,6 +27,7 @@ constexpr uint64_t kChunkOrderMinGradBytes = 256ull << 20;
 enum : int { WD_F32 = 0, WD_F16 = 1, WD_BF16 = 2 };
 enum : int { IT_I32 = 0, IT_I64 = 1 };
 enum : int { POOL_SUM = 0, POOL_MEAN = 1 };
+enum : int { OPT_ROWWISE_ADAGRAD = 0, OPT_ADAGRAD = 1, OPT_SGD = 2 };
 
 // Per-table descriptor, one array of T entries in device memory.
 struct TableDev {
@@ -303,6 +304,7 @@ struct BwdArgs {
   const float* grad;
   uint32_t dtot;
   float lr, eps;
+  int opt;                      // OPT_ROWWISE_ADAGRAD / OPT_ADAGRAD (element-wise) / OPT_SGD
   const uint32_t* sorted_bag;   // bag id of each sorted lookup
   const float* sorted_scale;    // nullable: S[p] * (1/L if mean) of each sorted lookup
   const uint4* single_task;
