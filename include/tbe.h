@@ -83,8 +83,8 @@ extern "C" {
 /* tbe_forward flags */
 #define TBE_FWD_NO_HIST 0x1u       /* never take the small-table histogram path */
 #define TBE_FWD_REQUIRE_HIST 0x2u  /* fail with TBE_E_UNSUPPORTED unless the histogram path applies */
-#define TBE_FWD_BALANCE 0x4u       /* generic path: always split bag groups by lookup count */
-#define TBE_FWD_NO_BALANCE 0x8u    /* generic path: always one bag per lane subgroup */
+#define TBE_FWD_BALANCE 0x4u       /* generic path: split bag groups into equal pieces (default) */
+#define TBE_FWD_NO_BALANCE 0x8u    /* generic path: one whole bag per lane subgroup */
 /* tbe_backward_rowwise_adagrad flags */
 #define TBE_BWD_PREPROCESSED 0x1u  /* the workspace already holds tbe_preprocess of these inputs */
 #define TBE_BWD_FUSED_LONG 0x2u    /* long runs: fused fence + countdown instead of a second launch */
@@ -155,12 +155,13 @@ int tbe_workspace_views(const tbe_plan* plan, int64_t B, int64_t num_lookups,
  * 64 rows, 64 <= D <= 128, float16 weights, no per-sample weights and an
  * average bag length >= 64 takes the histogram path (row counts of 16 bags
  * times the table on the matrix cores) unless TBE_FWD_NO_HIST is set.
- * The generic path either gives each lane subgroup one bag or, for batches
- * with many bags, gives each wave a group of consecutive bags split into
- * contiguous runs of about equal lookup count (so short and long bags share
- * a wave evenly); TBE_FWD_BALANCE / TBE_FWD_NO_BALANCE force one or the
- * other.  Both give identical sums: each bag is summed by one subgroup in
- * lookup order. */
+ * The generic path gives each wave a group of consecutive bags and splits
+ * their lookups into equal pieces, one per lane subgroup (a bag cut by the
+ * pieces is summed per piece and the parts are added in piece order), or,
+ * with TBE_FWD_NO_BALANCE, gives each lane subgroup one bag, summed in
+ * lookup order.  TBE_FWD_BALANCE asks for the first explicitly (the default).
+ * Both are deterministic (the order of every sum follows from the offsets),
+ * and they differ only in the rounding of bags that the pieces cut. */
 int tbe_forward(const tbe_plan* plan, int64_t B, int32_t itype, const void* indices,
                 const void* offsets, int64_t num_lookups, const float* per_sample_weights,
                 float* out, uint32_t flags, void* stream);

@@ -8,16 +8,22 @@
 // columns k*VEC + c*lpr*VEC (c < NC), read with 16-byte (VEC element) loads,
 // so a row of the bucket width is one coalesced sweep of the subgroup.
 //
-// Balance (fwd_bal_kernel, bps > 1): a wave owns G = fwd_group_bags(lpr, bps)
-// consecutive bags of one
-// table (their lookups are contiguous) and gives each of its 64/lpr
-// subgroups a contiguous run of whole bags holding about 1/(64/lpr) of the
-// group's lookups: bag q goes to subgroup floor((O[q] - O[first]) / share).
-// With one bag per subgroup a wave lasts as long as its longest bag while the
-// other subgroups idle; with a few bags per subgroup the runs even out, at
-// the price of fewer waves, so the host picks bps from the batch size.  A
-// subgroup streams its lookups in order and writes a bag's pooled row when
-// the bag ends, so every bag has one owner and plain stores.
+// Balance (fwd_bal_kernel, the default): a wave owns G = fwd_group_bags(lpr,
+// bps) consecutive bags of one table (their lookups are contiguous) and
+// splits the group's lookups into 64/lpr equal pieces in lookup order, one
+// per subgroup, cutting through bags.  With one bag per subgroup a wave lasts
+// as long as its longest bag while the other subgroups idle (C2's lengths,
+// uniform in [1, 64], leave about half the lanes idle); with equal pieces
+// every subgroup issues the same number of loads.  A subgroup streams its
+// piece in order.  A bag that starts and ends in the piece is written by it
+// directly; a bag cut by piece boundaries is summed per piece (the piece
+// where it starts and every piece it fills keep their part in LDS, the piece
+// where it ends adds those parts in piece order to its own and writes the
+// row), so every bag has one writer, plain stores, and a sum order fixed by
+// the offsets alone: repeated calls give the same bits.  bps (1, 2 or 4 bags
+// per subgroup and wave) trades evenness for the number of waves; the host
+// picks it from the batch size.  fwd_pool_kernel (TBE_FWD_NO_BALANCE) gives
+// each subgroup one whole bag and sums it in lookup order.
 //
 // Memory-level parallelism: lookups are taken eight at a time.  The eight
 // indices are loaded, then the eight rows, then the eight rows are
@@ -63,11 +69,17 @@ template <int WD, int VEC, int NC, typename IT, bool PSW>
 __global__ __launch_bounds__(kThreads) void fwd_bal_kernel(FwdArgs a, BucketSet S) {
   using AT = typename Acc<WD>::T;
   constexpr uint32_t kWaves = kThreads / kWave;
+  // fragments exist only with two or more subgroups per wave, hence NC == 1
+  constexpr uint32_t kFrag = NC == 1 ? (uint32_t)kWave * VEC : 1u;
   __shared__ uint32_t s_off[kWaves][kWave + 1];
+  __shared__ AT s_tail[kWaves][kFrag];  // [subgroup * width + column]
+  __shared__ AT s_head[kWaves][kFrag];
   BucketDev bk;
   uint32_t bucket_id, lb, lg;
   set_pick(S, bk, bucket_id, lb, lg);
-  const uint32_t lane = lane_id(), wave = threadIdx.x / kWave;
+  // the wave index is uniform: say so, so that the table descriptor and the
+  // buffer descriptors built from it live in scalar registers
+  const uint32_t lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const uint32_t lpr = bk.lpr, lg2 = bk.lpr_log2;
   const uint32_t nsub = (uint32_t)kWave >> lg2;
   const uint32_t sgi = lane >> lg2, lane_in = lane & (lpr - 1);
@@ -81,7 +93,6 @@ __global__ __launch_bounds__(kThreads) void fwd_bal_kernel(FwdArgs a, BucketSet 
   const uint32_t nbw = (uint32_t)((B - g0) < (uint64_t)G ? (B - g0) : (uint64_t)G);
   const uint32_t t = bk.tables[slot];
   const TableDev td = a.tables[t];
-  const IT* __restrict__ I = reinterpret_cast<const IT*>(a.indices);
   const IT* __restrict__ O = reinterpret_cast<const IT*>(a.offsets);
   const uint64_t j0 = (uint64_t)t * B + g0;
   const uint32_t D = td.dim;
@@ -92,30 +103,30 @@ __global__ __launch_bounds__(kThreads) void fwd_bal_kernel(FwdArgs a, BucketSet 
   if (nbw == (uint32_t)kWave && lane == 0) off[kWave] = (uint32_t)O[j0 + kWave];
   wave_lds_sync();
 
-  // this subgroup's bags [sb_lo, sb_hi)
-  uint32_t sb_lo, sb_hi;
-  if (G <= nsub) {
-    sb_lo = sgi < nbw ? sgi : nbw;
-    sb_hi = sgi + 1 < nbw ? sgi + 1 : nbw;
-  } else {
-    const uint32_t P0 = off[0];
-    const uint32_t tot = off[nbw] - P0;
-    uint32_t share = (tot + nsub - 1) / nsub;
-    share = share > 0 ? share : 1u;
-    uint32_t own = 0;
-    if (lane < nbw) {
-      own = (off[lane] - P0) / share;
-      own = own < nsub - 1 ? own : nsub - 1;
-    }
-    sb_lo = 0;
-    sb_hi = nbw;
-    for (uint32_t i = 1; i < nsub; ++i) {  // s_i = #bags owned below subgroup i
-      const uint32_t si = (uint32_t)__popcll(__ballot(lane < nbw && own < i));
-      if (sgi == i) sb_lo = si;
-      if (sgi + 1 == i) sb_hi = si;
+  // This subgroup's piece [plo, phi) of the group's lookups: equal shares in
+  // lookup order, cutting through bags.  Its bag ends are the bags whose last
+  // lookup lies in the piece (and subgroup 0 also the empty bags at the start;
+  // the last non-empty piece the empty bags at the end).
+  const uint32_t P0 = off[0], Pe = off[nbw];
+  const uint32_t tot = Pe - P0;
+  uint32_t share = (tot + nsub - 1) / nsub;
+  share = share > 0 ? share : 1u;
+  const uint32_t plo = sgi * share < tot ? P0 + sgi * share : Pe;
+  const uint32_t phi = (sgi + 1) * share < tot ? P0 + (sgi + 1) * share : Pe;
+  uint32_t cur = 0;  // bag being summed
+  if (sgi > 0) {
+    if (plo < phi) {  // the bag holding position plo: the last q with off[q] <= plo
+      uint32_t lo = 0, hi = nbw;
+      while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (off[mid] <= plo) lo = mid; else hi = mid;
+      }
+      cur = lo;
+    } else {
+      cur = nbw;  // an empty piece past the end: nothing to do
     }
   }
-  const uint32_t pb = off[sb_lo], pe = off[sb_hi];
+  uint32_t nxt = cur < nbw ? off[cur + 1] : Pe;  // its end
 
   AT acc[NC][VEC];
   bool act[NC];
@@ -129,38 +140,64 @@ __global__ __launch_bounds__(kThreads) void fwd_bal_kernel(FwdArgs a, BucketSet 
     cold[c] = act[c] ? colc[c] : 0u;  // idle lanes read column 0 and discard it
   }
   const bool mean = td.pooling == POOL_MEAN;
-  // write bag q's pooled row (mean: divided by its length) and clear the sums
-  auto flush = [&](uint32_t q) {
+  const uint32_t fbase = sgi * lpr * VEC;  // this subgroup's fragment slot
+  // 32-bit byte offsets (the host sends tables and index arrays under 4 GiB
+  // here); an int64 index is read as its low word (rows < 2^32)
+  constexpr uint32_t kEs = WD == WD_F32 ? 4u : 2u;
+  const __amdgpu_buffer_rsrc_t wres = buf_rsrc(td.w, td.rows * D * kEs);
+  const __amdgpu_buffer_rsrc_t ires = buf_rsrc(a.indices, a.n * (uint32_t)sizeof(IT));
+  const __amdgpu_buffer_rsrc_t pres = buf_rsrc(a.psw, PSW ? a.n * 4u : 0u);
+  const uint32_t rowb = D * kEs;
+  uint32_t colb[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) colb[c] = cold[c] * kEs;
+  // write bag q's pooled row from its sums v (mean: divided by its length)
+  auto write_row = [&](uint32_t q, const AT (*v)[VEC]) {
     const uint32_t L = off[q + 1] - off[q];
     float* orow = a.out + (int64_t)(g0 + q) * (int64_t)a.dtot + td.col;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      if (act[c]) {
-        float o[VEC];
+      if (!act[c]) continue;
+      float o[VEC];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e)
-          o[e] = (float)((mean && L > 0) ? acc[c][e] / AT(L) : acc[c][e]);
-        store_f32<VEC>(orow + colc[c], o);
-      }
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[c][e] = AT(0);
+      for (int e = 0; e < VEC; ++e)
+        o[e] = (float)((mean && L > 0) ? v[c][e] / AT(L) : v[c][e]);
+      store_f32<VEC>(orow + colc[c], o);
     }
   };
+  // bag q ends in this piece: written out if it started in the piece, else
+  // its last part is kept for the combination below
+  uint32_t head_bag = nbw;
+  auto end_bag = [&](uint32_t q) {
+    bool whole = true;
+    if constexpr (NC == 1) {
+      if (off[q] < plo) {
+        head_bag = q;
+        whole = false;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) s_head[wave][fbase + colc[0] + e] = acc[0][e];
+      }
+    }
+    if (whole) write_row(q, acc);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[c][e] = AT(0);
+  };
 
-  uint32_t cur = sb_lo;                            // bag being summed
-  uint32_t nxt = cur < sb_hi ? off[cur + 1] : pe;  // its end
-  int64_t nrow[kInFlight];
+  const uint32_t pb = plo, pe = phi;
+  uint32_t nrow[kInFlight];
   float ns[kInFlight];
   if (pb < pe) {
 #pragma unroll
     for (int k = 0; k < kInFlight; ++k) {
       const uint32_t q = pb + k < pe ? pb + k : pe - 1;
-      nrow[k] = (int64_t)I[q];
-      ns[k] = PSW ? a.psw[q] : 1.0f;
+      nrow[k] = buf_u32(ires, q * (uint32_t)sizeof(IT));
+      ns[k] = PSW ? __builtin_bit_cast(float, buf_u32(pres, q * 4u)) : 1.0f;
     }
   }
   for (uint32_t p = pb; p < pe; p += kInFlight) {
-    int64_t row[kInFlight];
+    uint32_t row[kInFlight];
     float s[kInFlight];
     bool ok[kInFlight];
 #pragma unroll
@@ -176,13 +213,13 @@ __global__ __launch_bounds__(kThreads) void fwd_bal_kernel(FwdArgs a, BucketSet 
     for (int c = 0; c < NC; ++c) {
       float v[kInFlight][VEC];
 #pragma unroll
-      for (int k = 0; k < kInFlight; ++k) load_w<WD, VEC>(td.w, row[k] * D + cold[c], v[k]);
+      for (int k = 0; k < kInFlight; ++k) load_w_buf<WD, VEC>(wres, row[k] * rowb + colb[c], v[k]);
       if (c == 0) {
 #pragma unroll
         for (int k = 0; k < kInFlight; ++k) {
           const uint32_t q = p + kInFlight + k < pe ? p + kInFlight + k : pe - 1;
-          nrow[k] = (int64_t)I[q];
-          ns[k] = PSW ? a.psw[q] : 1.0f;
+          nrow[k] = buf_u32(ires, q * (uint32_t)sizeof(IT));
+          ns[k] = PSW ? __builtin_bit_cast(float, buf_u32(pres, q * 4u)) : 1.0f;
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -190,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bal_kernel(FwdArgs a, BucketSet 
       for (int k = 0; k < kInFlight; ++k) {
         if (NC == 1 && ok[k]) {
           while (p + k >= nxt) {  // lookup p+k opens a later bag: finish the current one(s)
-            flush(cur);
+            end_bag(cur);
             ++cur;
             nxt = off[cur + 1];
           }
@@ -201,7 +238,31 @@ __global__ __launch_bounds__(kThreads) void fwd_bal_kernel(FwdArgs a, BucketSet 
       }
     }
   }
-  for (; cur < sb_hi; ++cur) flush(cur);  // the last bag and any empty ones after it
+  // the bags ending at the end of the piece, empty ones included
+  for (; cur < nbw && off[cur + 1] <= phi; ++cur) end_bag(cur);
+  if constexpr (NC == 1) {
+    if (cur < nbw) {  // the current bag goes on: this piece's part of it
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) s_tail[wave][fbase + colc[0] + e] = acc[0][e];
+    }
+    if (nsub == 1) return;
+    wave_lds_sync();
+    if (head_bag < nbw) {
+      // a bag that began in piece i0 < sgi: the parts of pieces i0 .. sgi-1
+      // (each ends inside the bag) and this piece's part, in piece order
+      uint32_t i0 = (off[head_bag] - P0) / share;
+      i0 = i0 < sgi ? i0 : sgi;
+      AT sum[NC][VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) sum[0][e] = AT(0);
+      for (uint32_t k = i0; k < sgi; ++k)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) sum[0][e] += s_tail[wave][k * lpr * VEC + colc[0] + e];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) sum[0][e] += s_head[wave][fbase + colc[0] + e];
+      write_row(head_bag, sum);
+    }
+  }
 }
 
 // One bag per lane subgroup (bps == 1): subgroup sg of the launch pools bag sg
@@ -302,7 +363,7 @@ template <int WD, int VEC, int NC, typename IT, bool PSW>
 hipError_t launch_t(const FwdArgs& a, const BucketSet& S, hipStream_t s) {
   const uint32_t grid = S.gbeg[S.n];
   if (grid == 0) return hipSuccess;
-  if (a.bps > 1)
+  if (a.split)
     TBE_LAUNCH("fwd_pool", (fwd_bal_kernel<WD, VEC, NC, IT, PSW>), dim3(grid), dim3(kThreads), s,
                a, S);
   else

@@ -159,20 +159,34 @@ bool hist_eligible(const tbe_plan* P, int64_t B, int64_t N, const float* psw) {
          P->wdtype == TBE_F16 && psw == nullptr && B > 0 && N >= 64 * B;
 }
 
-// Bags per lane subgroup of the generic forward.  Four bags per subgroup
-// even out the bag lengths inside a wave but leave a quarter of the waves:
-// measured on MI355X it pays (3-6%) once one bag per subgroup would give at
-// least kFwdBalanceWavesPerCu waves per CU, and costs 6-10% below that,
-// where the batch is too small to keep the memory system busy with fewer
-// waves.
-constexpr uint64_t kFwdBalanceWavesPerCu = 64;
+// Bags per lane subgroup of the generic forward (the wave's group holds
+// 64/lpr * bps consecutive bags whose lookups its subgroups split evenly).
+// More bags per wave even out more but leave fewer waves; measured on MI355X
+// (forward alone): 8 tables x 8192 bags, 48 waves per CU with one bag per
+// subgroup: bps 1 / 2 / 4 = 47.3 / 48.8 / 49.5 us; 16 x 16384 bags, ~200
+// waves per CU: 538 / 512 / 518 us; 64 x 65536 bags, 4096 waves per CU:
+// 3271 / 2905 / 2827 us.
+constexpr uint64_t kFwdTwoBagsWavesPerCu = 64;
+constexpr uint64_t kFwdFourBagsWavesPerCu = 1024;
 uint32_t fwd_bags_per_subgroup(const tbe_plan* P, int64_t B) {
   uint64_t waves = 0;  // with one bag per subgroup
   for (const Bucket& bk : P->buckets) {
     const uint64_t nsub = (uint64_t)kWave / bk.lpr;
     waves += (uint64_t)bk.tables.size() * (((uint64_t)B + nsub - 1) / nsub);
   }
-  return waves >= kFwdBalanceWavesPerCu * (uint64_t)P->num_cus ? 4u : 1u;
+  const uint64_t cus = (uint64_t)P->num_cus;
+  return waves >= kFwdFourBagsWavesPerCu * cus ? 4u : waves >= kFwdTwoBagsWavesPerCu * cus ? 2u : 1u;
+}
+
+// The equal-piece forward reads rows and indices with 32-bit byte offsets:
+// every table and the index array under 4 GiB (else one bag per subgroup).
+bool fwd_split_fits(const tbe_plan* P, int64_t N, int32_t itype) {
+  const uint64_t es = P->wdtype == TBE_F32 ? 4 : 2;
+  const uint64_t lim = 1ull << 32;
+  if ((uint64_t)N * (itype == TBE_I64 ? 8u : 4u) >= lim) return false;
+  for (int t = 0; t < P->T; ++t)
+    if ((uint64_t)P->rows[t] * (uint64_t)P->dims[t] * es >= lim) return false;
+  return true;
 }
 
 bool any_mean(const tbe_plan* P) {
@@ -558,9 +572,9 @@ int tbe_forward(const tbe_plan* P, int64_t B, int32_t itype, const void* indices
     e = launch_forward_hist(a, (uint32_t)P->rows[0], (uint32_t)P->dims[0],
                             P->pooling[0] == TBE_MEAN, P->num_cus * 4, s);
   } else {
-    a.bps = (flags & TBE_FWD_BALANCE)      ? 4u
-            : (flags & TBE_FWD_NO_BALANCE) ? 1u
-                                           : fwd_bags_per_subgroup(P, B);
+    a.split = (flags & TBE_FWD_NO_BALANCE) || !fwd_split_fits(P, N, itype) ? 0u : 1u;
+    a.n = (uint32_t)N;
+    a.bps = a.split ? fwd_bags_per_subgroup(P, B) : 1u;
     for (const auto& grp : bucket_groups(P)) {
       BucketSet S = bucket_set(P, grp);
       S.gbeg[0] = 0;

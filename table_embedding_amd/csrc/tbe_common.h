@@ -185,6 +185,54 @@ __device__ __forceinline__ void load_w(const void* w, int64_t e, float* v) {
   }
 }
 
+// Buffer loads: a 32-bit byte offset per lane against a base held in scalar
+// registers (a buffer descriptor) instead of a 64-bit address per lane, which
+// saves address registers and 64-bit arithmetic in the gather loops; a read at
+// or past `bytes` returns zeros instead of faulting.  The descriptor's fourth
+// dword for a raw gfx9 buffer selects the 32-bit data format.
+constexpr int kBufDword3 = 0x00020000;
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufDword3);
+}
+__device__ __forceinline__ uint32_t buf_u32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
+}
+// load_w through a buffer descriptor: VEC weights at byte offset byte_off.
+template <int WD, int VEC>
+__device__ __forceinline__ void load_w_buf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float* v) {
+  if constexpr (WD == WD_F32) {
+    static_assert(VEC == 4, "f32 rows are read 4 at a time");
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+    // components to scalars first: a bit cast of a vector element expression
+    // (x.y) reads component 0 with this compiler
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __builtin_bit_cast(float, w[i]);
+  } else {
+    uint32_t words[VEC / 2];
+    if constexpr (VEC == 8) {
+      const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+      words[0] = x.x; words[1] = x.y; words[2] = x.z; words[3] = x.w;
+    } else {
+      const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0);
+      words[0] = x.x; words[1] = x.y;
+    }
+#pragma unroll
+    for (int i = 0; i < VEC / 2; ++i) {
+      if constexpr (WD == WD_F16) {
+        v[2 * i] = f16_bits_to_float(words[i] & 0xffffu);
+        v[2 * i + 1] = f16_bits_to_float(words[i] >> 16);
+      } else {
+        v[2 * i] = bf16_bits_to_float(words[i] & 0xffffu);
+        v[2 * i + 1] = bf16_bits_to_float(words[i] >> 16);
+      }
+    }
+  }
+}
+
 // Store VEC floats, rounded to the storage type, at element e.
 template <int WD, int VEC>
 __device__ __forceinline__ void store_w(void* w, int64_t e, const float* v) {
@@ -275,7 +323,9 @@ struct FwdArgs {
   const float* psw;
   float* out;
   uint32_t dtot;
-  uint32_t bps;  // bags per lane subgroup in the generic forward (1 .. 4)
+  uint32_t bps;    // generic forward: bags per lane subgroup in a wave's group (1 .. 4)
+  uint32_t split;  // 1: the group's lookups split evenly over its subgroups; 0: one bag each
+  uint32_t n;      // lookups N (the equal-piece split needs N * index bytes < 2^32)
 };
 
 struct PrepArgs {

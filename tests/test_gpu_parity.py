@@ -65,6 +65,13 @@ def _spec(name):
         # 12000 bags: the transposition gives each workgroup several bags
         return wl.Spec("many_bags", 2009, [3000, 500], [16, 64], [0, 1], "f16", 6000,
                        "uniform:0:20", "zipf:1.1", "i32", True)
+    if name == "cut_bags":
+        # bags of 0 .. 900 lookups next to each other: the forward's equal
+        # pieces cut long bags many times and fall on empty bags (32 and 64
+        # subgroups per wave with D = 16 and D = 8 f16 rows)
+        return wl.Spec("cut_bags", 2011, [700, 90, 400], [16, 16, 8], [0, 1, 0], "f16", 200,
+                       "list:0,0,1,900,0,2,0,0,150,3,0,64,0,0,0,0,33,1,1,2000,7",
+                       "zipf:1.05", "i32", True)
     if name == "heavy_chunks":
         # 32 runs of 32768 lookups: one classification tile with 4096 chunks,
         # which the whole workgroup places
@@ -76,7 +83,7 @@ def _spec(name):
 MAIN = ["C1", "C2s", "C3s", "C4s", "C5s"]
 EDGE = ["empty_bags", "all_empty", "one_bag", "one_row", "const31", "const32", "const255",
         "const256", "const257", "wide_f32", "wide_bf16", "many_tables", "many_bags",
-        "heavy_chunks"]
+        "heavy_chunks", "cut_bags"]
 
 
 def _announce(name, what):
@@ -97,17 +104,24 @@ def test_forward_parity(name, split):
     S.check_forward(case, out)
 
 
-@pytest.mark.parametrize("name", ["C2s", "C3s", "empty_bags", "many_tables", "wide_f32"])
-def test_forward_split_bitwise_equal(name):
-    """Both bag splits sum each bag in lookup order in one subgroup: same bits."""
-    _announce(name, "forward split equality")
+@pytest.mark.parametrize("name", ["C2s", "C3s", "empty_bags", "many_tables", "wide_f32",
+                                  "cut_bags"])
+def test_forward_deterministic(name):
+    """The order of every forward sum follows from the offsets alone: repeated
+    calls give the same bits with either bag split, and the default is the
+    equal-piece split."""
+    _announce(name, "forward determinism")
     import table_embedding_amd as te
     case = S.Case(_spec(name))
     tb = case.tbe()
-    outs = [tb.forward(case.spec.B, case.d_idx, case.d_off, case.d_psw,
-                       flags=te.TBE_FWD_NO_HIST | f).cpu().numpy().tobytes()
-            for f in (te.TBE_FWD_NO_BALANCE, te.TBE_FWD_BALANCE, 0)]
-    assert outs[0] == outs[1] == outs[2]
+
+    def run(f):
+        return tb.forward(case.spec.B, case.d_idx, case.d_off, case.d_psw,
+                          flags=te.TBE_FWD_NO_HIST | f).cpu().numpy().tobytes()
+    one, bal, dflt = run(te.TBE_FWD_NO_BALANCE), run(te.TBE_FWD_BALANCE), run(0)
+    assert run(te.TBE_FWD_NO_BALANCE) == one
+    assert run(te.TBE_FWD_BALANCE) == bal
+    assert dflt == bal
 
 
 @pytest.mark.parametrize("name", MAIN + EDGE)
