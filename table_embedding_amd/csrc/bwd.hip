@@ -33,7 +33,10 @@
 namespace tbe {
 namespace {
 
-constexpr int kInFlight = 8;
+// Lookups in flight per lane in the gathers: 8, or 4 where the kernel's
+// register use at 8 would cost occupancy that a short launch needs (the host
+// picks; see the launchers).
+constexpr int kInFlightDeep = 8, kInFlightShallow = 4;
 constexpr int kTdCache = 128;  // table descriptors cached in LDS by the tiny-run kernel
 
 // Accumulate sorted slots [i0, i1) with stride `step` into g (this lane's
@@ -42,7 +45,7 @@ constexpr int kTdCache = 128;  // table descriptors cached in LDS by the tiny-ru
 // sums in lookup order; scheduling barriers keep the loads of a batch in
 // flight together.  A partial batch repeats the last slot and drops the
 // repeats with a select (no branches inside the batch).
-template <int VEC, int NC, bool SCALE>
+template <int VEC, int NC, bool SCALE, int kInFlight>
 __device__ __forceinline__ void gather_t(const BwdArgs& a, const TableDev& td, int64_t tB,
                                          uint32_t i0, uint32_t i1, uint32_t step,
                                          const uint32_t* cold, float (*g)[VEC]) {
@@ -93,14 +96,14 @@ __device__ __forceinline__ void gather_t(const BwdArgs& a, const TableDev& td, i
   }
 }
 
-template <int VEC, int NC>
+template <int VEC, int NC, int IF>
 __device__ __forceinline__ void gather(const BwdArgs& a, const TableDev& td, int64_t tB,
                                        uint32_t i0, uint32_t i1, uint32_t step,
                                        const uint32_t* cold, float (*g)[VEC]) {
   if (a.sorted_scale)
-    gather_t<VEC, NC, true>(a, td, tB, i0, i1, step, cold, g);
+    gather_t<VEC, NC, true, IF>(a, td, tB, i0, i1, step, cold, g);
   else
-    gather_t<VEC, NC, false>(a, td, tB, i0, i1, step, cold, g);
+    gather_t<VEC, NC, false, IF>(a, td, tB, i0, i1, step, cold, g);
 }
 
 // Sanity bounds of list entries (they hold for every list the preprocessing
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void bwd_single_kernel(BwdArgs a, BucketS
 // ----------------------------------------------------- tiny short runs
 // One subgroup of lpr lanes owns a run with 2 <= SL < 32: gather, Adagrad,
 // plain stores.  The next task record is prefetched.
-template <int WD, int VEC, int NC, bool TDL>
+template <int WD, int VEC, int NC, bool TDL, int IF>
 __global__ __launch_bounds__(kThreads) void bwd_tiny_kernel(BwdArgs a, BucketSet S) {
   BucketDev bk;
   uint32_t bucket, lb, lg;
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void bwd_tiny_kernel(BwdArgs a, BucketSet
       for (int e = 0; e < VEC; ++e) g[c][e] = 0.f;
     }
     const float m0 = a.opt == OPT_ROWWISE_ADAGRAD ? td.m[row] : 0.f;
-    gather<VEC, NC>(a, td, (int64_t)t * a.B, start, start + len, 1u, cold, g);
+    gather<VEC, NC, IF>(a, td, (int64_t)t * a.B, start, start + len, 1u, cold, g);
     subgroup_row_update<WD, VEC, NC>(a, td, row, m0, w, g, colc, lpr, lane_in, true);
   }
 }
@@ -318,7 +321,7 @@ struct WgSmem {
 };
 
 // Subgroup sg accumulates sorted slots i0+sg, i0+sg+nsg, ... < i1 into sm.red.
-template <int VEC, int NC>
+template <int VEC, int NC, int IF>
 __device__ __forceinline__ void wg_gather(const BwdArgs& a, const BucketDev& bk,
                                           const TableDev& td, uint32_t t, uint32_t i0,
                                           uint32_t i1, WgSmem<VEC, NC>& sm) {
@@ -335,7 +338,7 @@ __device__ __forceinline__ void wg_gather(const BwdArgs& a, const BucketDev& bk,
 #pragma unroll
     for (int e = 0; e < VEC; ++e) g[c][e] = 0.f;
   }
-  gather<VEC, NC>(a, td, (int64_t)t * a.B, i0 + sg, i1, nsg, cold, g);
+  gather<VEC, NC, IF>(a, td, (int64_t)t * a.B, i0 + sg, i1, nsg, cold, g);
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -494,7 +497,7 @@ __global__ __launch_bounds__(kThreads) void bwd_medium_kernel(BwdArgs a, BucketS
     const uint4 task = a.med_task[m];  // {start, len, row, table}
     if (!span_ok(a, task.x, task.y, task.w, task.z)) continue;  // uniform; never for valid lists
     const TableDev td = a.tables[task.w];
-    wg_gather<VEC, NC>(a, bk, td, task.w, task.x, task.x + task.y, sm);
+    wg_gather<VEC, NC, kInFlightShallow>(a, bk, td, task.w, task.x, task.x + task.y, sm);
     const float sqp = red_to_gsum<VEC, NC>(bk, td.dim, sm);
     wg_row_update<WD, VEC, NC>(a, td, (int64_t)task.z, sqp, sm);
   }
@@ -588,7 +591,7 @@ __global__ __launch_bounds__(kThreads) void chunk_order_kernel(BwdArgs a) {
   }
 }
 
-template <int WD, int VEC, int NC>
+template <int WD, int VEC, int NC, int IF>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a, BucketSet S) {
   BucketDev bk;
   uint32_t bucket, lb, lg;
@@ -603,7 +606,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a, BucketSe
     const uint4 task = a.chunk_task[cp];  // {start, len, table, long index}
     if (cp < beg || cp >= end || !chunk_ok(a, task)) continue;  // uniform; never for valid lists
     const TableDev td = a.tables[task.z];
-    wg_gather<VEC, NC>(a, bk, td, task.z, task.x, task.x + task.y, sm);
+    wg_gather<VEC, NC, IF>(a, bk, td, task.z, task.x, task.x + task.y, sm);
     chunk_store<VEC, NC, false>(a, bk, td.dim, cp, sm);
     __syncthreads();
   }
@@ -636,7 +639,7 @@ __global__ __launch_bounds__(kThreads) void bwd_long_update_kernel(BwdArgs a, Bu
 // atomic loads (read from the coherent level, not from a stale cache).  This
 // is the release/acquire pair without the whole-cache operations, which only
 // serve to publish ordinary cached stores; none is published here.
-template <int WD, int VEC, int NC>
+template <int WD, int VEC, int NC, int IF>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_fused_kernel(BwdArgs a, BucketSet S) {
   BucketDev bk;
   uint32_t bucket, lb, lg;
@@ -652,7 +655,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_fused_kernel(BwdArgs a, Bu
     if (cp < beg || cp >= end || !chunk_ok(a, task) || !long_ok(a, task.w))
       continue;  // uniform per workgroup; never for valid lists
     const TableDev td = a.tables[task.z];
-    wg_gather<VEC, NC>(a, bk, td, task.z, task.x, task.x + task.y, sm);
+    wg_gather<VEC, NC, IF>(a, bk, td, task.z, task.x, task.x + task.y, sm);
     chunk_store<VEC, NC, true>(a, bk, td.dim, cp, sm);
     __builtin_amdgcn_s_waitcnt(0);  // this thread's write-through stores have completed
     __syncthreads();
@@ -703,7 +706,17 @@ uint32_t set_grid(BucketSet& S, const BwdGrids* g, uint32_t BwdGrids::*field, ui
   return S.gbeg[S.n];
 }
 
-template <int WD, int VEC, int NC, bool TDL>
+// Lookups in flight of the tiny-run and chunk gathers.  Four lift the
+// occupancy of both kernels (tiny 136 -> 92 VGPRs, chunk 116 -> 69) and pay
+// while the launches are short and latency-bound; on a deep batch the kernels
+// already keep the memory system busy and eight cut the round trips per run.
+// Measured on MI355X (tiny / chunk, us per step, 8 -> 4 in flight): 2.1 M
+// lookups 40.0 -> 34.6 / 21.5 -> 18.4; 17 M lookups 292 -> 233 / 578 -> 463;
+// 138 M lookups 2408 -> 2545 / 3685 -> 3848.  Medium runs gather with four
+// always (at the same three sizes: 24.8 -> 20.5, 179 -> 146, 1449 -> 1189).
+constexpr uint32_t kBwdDeepLookups = 64u << 20;
+
+template <int WD, int VEC, int NC, bool TDL, int IF>
 void launch_small(const BwdArgs& a, BucketSet S, const BwdGrids* g, int cus, hipStream_t s) {
   if (a.sorted_scale) {
     static const uint32_t cap = resident(bwd_single_kernel<WD, VEC, NC, true, TDL>, cus);
@@ -716,38 +729,56 @@ void launch_small(const BwdArgs& a, BucketSet S, const BwdGrids* g, int cus, hip
     TBE_LAUNCH("bwd_single", (bwd_single_kernel<WD, VEC, NC, false, TDL>), dim3(grid),
                dim3(kThreads), s, a, S);
   }
-  static const uint32_t cap_t = resident(bwd_tiny_kernel<WD, VEC, NC, TDL>, cus);
+  static const uint32_t cap_t = resident(bwd_tiny_kernel<WD, VEC, NC, TDL, IF>, cus);
   const uint32_t grid = set_grid(S, g, &BwdGrids::tiny, cap_t);
-  TBE_LAUNCH("bwd_tiny", (bwd_tiny_kernel<WD, VEC, NC, TDL>), dim3(grid), dim3(kThreads), s, a,
-             S);
+  TBE_LAUNCH("bwd_tiny", (bwd_tiny_kernel<WD, VEC, NC, TDL, IF>), dim3(grid), dim3(kThreads), s,
+             a, S);
 }
 
-template <int WD, int VEC, int NC>
-hipError_t launch(const BwdArgs& a, BucketSet S, const BwdGrids* g, bool fused, int cus,
-                  const hipStream_t* ss) {
-  if (a.T <= (uint32_t)kTdCache)
-    launch_small<WD, VEC, NC, true>(a, S, g, cus, ss[0]);
-  else
-    launch_small<WD, VEC, NC, false>(a, S, g, cus, ss[0]);
-  static const uint32_t cap_m = resident(bwd_medium_kernel<WD, VEC, NC>, cus);
-  uint32_t grid = set_grid(S, g, &BwdGrids::medium, cap_m);
-  TBE_LAUNCH("bwd_medium", (bwd_medium_kernel<WD, VEC, NC>), dim3(grid), dim3(kThreads), ss[1],
-             a, S);
-  const hipStream_t s = ss[2];
+template <int WD, int VEC, int NC, int IF>
+void launch_long(const BwdArgs& a, BucketSet S, const BwdGrids* g, bool fused, int cus,
+                 hipStream_t s) {
+  uint32_t grid;
   if (fused) {
-    static const uint32_t cap_f = resident(bwd_chunk_fused_kernel<WD, VEC, NC>, cus);
+    static const uint32_t cap_f = resident(bwd_chunk_fused_kernel<WD, VEC, NC, IF>, cus);
     grid = set_grid(S, g, &BwdGrids::chunk, cap_f, 8);
-    TBE_LAUNCH("bwd_chunk_fused", (bwd_chunk_fused_kernel<WD, VEC, NC>), dim3(grid),
+    TBE_LAUNCH("bwd_chunk_fused", (bwd_chunk_fused_kernel<WD, VEC, NC, IF>), dim3(grid),
                dim3(kThreads), s, a, S);
   } else {
-    static const uint32_t cap_c = resident(bwd_chunk_kernel<WD, VEC, NC>, cus);
+    static const uint32_t cap_c = resident(bwd_chunk_kernel<WD, VEC, NC, IF>, cus);
     grid = set_grid(S, g, &BwdGrids::chunk, cap_c, 8);
-    TBE_LAUNCH("bwd_chunk", (bwd_chunk_kernel<WD, VEC, NC>), dim3(grid), dim3(kThreads), s, a, S);
+    TBE_LAUNCH("bwd_chunk", (bwd_chunk_kernel<WD, VEC, NC, IF>), dim3(grid), dim3(kThreads), s,
+               a, S);
     static const uint32_t cap_l = resident(bwd_long_update_kernel<WD, VEC, NC>, cus);
     grid = set_grid(S, g, &BwdGrids::longrun, cap_l);
     TBE_LAUNCH("bwd_long_update", (bwd_long_update_kernel<WD, VEC, NC>), dim3(grid),
                dim3(kThreads), s, a, S);
   }
+}
+
+template <int WD, int VEC, int NC>
+hipError_t launch(const BwdArgs& a, BucketSet S, const BwdGrids* g, bool fused, int cus,
+                  const hipStream_t* ss) {
+  const bool deep = a.N >= kBwdDeepLookups;
+  if (a.T <= (uint32_t)kTdCache) {
+    if (deep)
+      launch_small<WD, VEC, NC, true, kInFlightDeep>(a, S, g, cus, ss[0]);
+    else
+      launch_small<WD, VEC, NC, true, kInFlightShallow>(a, S, g, cus, ss[0]);
+  } else {
+    if (deep)
+      launch_small<WD, VEC, NC, false, kInFlightDeep>(a, S, g, cus, ss[0]);
+    else
+      launch_small<WD, VEC, NC, false, kInFlightShallow>(a, S, g, cus, ss[0]);
+  }
+  static const uint32_t cap_m = resident(bwd_medium_kernel<WD, VEC, NC>, cus);
+  const uint32_t grid = set_grid(S, g, &BwdGrids::medium, cap_m);
+  TBE_LAUNCH("bwd_medium", (bwd_medium_kernel<WD, VEC, NC>), dim3(grid), dim3(kThreads), ss[1],
+             a, S);
+  if (deep)
+    launch_long<WD, VEC, NC, kInFlightDeep>(a, S, g, fused, cus, ss[2]);
+  else
+    launch_long<WD, VEC, NC, kInFlightShallow>(a, S, g, fused, cus, ss[2]);
   return hipGetLastError();
 }
 
