@@ -166,6 +166,21 @@ int tbe_forward(const tbe_plan* plan, int64_t B, int32_t itype, const void* indi
                 const void* offsets, int64_t num_lookups, const float* per_sample_weights,
                 float* out, uint32_t flags, void* stream);
 
+/* Forward and backward preprocessing of the same lookups in one call
+ * (FBTriton page, "Backward": the preprocessing can move into the forward).
+ * The forward runs on `stream` exactly as tbe_forward; the preprocessing of
+ * tbe_preprocess is launched at the same time on one of the plan's side
+ * streams (default priority), forked from `stream` before the forward, and
+ * `stream` waits for it before any later work.  A tbe_backward(...,
+ * TBE_BWD_PREPROCESSED) on `stream` then uses the workspace.  Arguments,
+ * ownership and errors as tbe_forward and tbe_preprocess (ws: device, >=
+ * tbe_workspace_size bytes, 256-byte aligned).  Calls on one plan are
+ * serialized on the host (the fork and join events are the plan's). */
+int tbe_forward_preprocess(const tbe_plan* plan, int64_t B, int32_t itype, const void* indices,
+                           const void* offsets, int64_t num_lookups,
+                           const float* per_sample_weights, float* out, uint32_t flags, void* ws,
+                           size_t ws_bytes, void* stream);
+
 /* Backward preprocessing only (FBTriton page, "Backward": transposition,
  * sort, run-length encoding; classification of runs at SL 256 and task-list
  * compaction with device-resident counts).  Fills the workspace for a later

@@ -17,7 +17,8 @@ from ._lib import (  # noqa: F401
     TBE_E_ALLOC,
     TBE_E_ARG, TBE_E_HIP, TBE_E_RANGE, TBE_E_UNSUPPORTED, TBE_E_WORKSPACE, TBE_F16, TBE_F32,
     TBE_FWD_BALANCE, TBE_FWD_NO_BALANCE, TBE_FWD_NO_HIST, TBE_FWD_REQUIRE_HIST, TBE_I32, TBE_I64, TBE_MEAN, TBE_OK, TBE_SUM,
-    TBEError, lib, tbe_backward_rowwise_adagrad, tbe_forward, tbe_plan_create,
+    TBEError, lib, tbe_backward_rowwise_adagrad, tbe_forward, tbe_forward_preprocess,
+    tbe_plan_create,
     tbe_plan_destroy, tbe_plan_key_bases, tbe_preprocess, tbe_prof_calibrate, tbe_prof_enable,
     tbe_prof_read,
     tbe_status_string, tbe_validate, TBE_VALIDATE_REPAIR, TBE_VALIDATE_WORDS,
@@ -47,7 +48,6 @@ class TBE:
         self.plan = tbe_plan_create(self.rows, self.dims, self.pooling, self.weights,
                                     self.momentum)
         self._ws: Optional[torch.Tensor] = None
-        self._side: Optional[torch.cuda.Stream] = None
 
     def close(self):
         if self.plan is not None:
@@ -84,25 +84,17 @@ class TBE:
                                per_sample_weights: Optional[torch.Tensor] = None,
                                out: Optional[torch.Tensor] = None, flags: int = 0
                                ) -> torch.Tensor:
-        """tbe_forward on the current stream and, at the same time, tbe_preprocess of the
-        same lookups on a side stream (default priority); the current stream then waits
-        for both.  A later backward(..., flags=TBE_BWD_PREPROCESSED) on the current stream
-        reuses the workspace (FBTriton page, "Backward": the preprocessing can move into
-        forward).  Only the order of launches differs from forward() then preprocess()."""
-        main = torch.cuda.current_stream(offsets.device)
-        if self._side is None:
-            self._side = torch.cuda.Stream(device=offsets.device)
-        side = self._side
+        """tbe_forward_preprocess: the forward on the current stream and, at the same
+        time, tbe_preprocess of the same lookups on a side stream of the plan (default
+        priority); the current stream then waits for both.  A later backward(...,
+        flags=TBE_BWD_PREPROCESSED) on the current stream reuses the workspace (FBTriton
+        page, "Backward": the preprocessing can move into forward).  Only the order of
+        launches differs from forward() then preprocess()."""
+        if out is None:
+            out = torch.empty((B, self.dtot), dtype=torch.float32, device=offsets.device)
         ws = self.workspace(B, indices.numel())
-        side.wait_stream(main)
-        with torch.cuda.stream(side):
-            tbe_preprocess(self.plan, B, indices, offsets, indices.numel(), per_sample_weights,
-                           ws)
-        for t in (indices, offsets, per_sample_weights, ws):
-            if t is not None:
-                t.record_stream(side)
-        out = self.forward(B, indices, offsets, per_sample_weights, out, flags)
-        main.wait_stream(side)
+        tbe_forward_preprocess(self.plan, B, indices, offsets, indices.numel(),
+                               per_sample_weights, out, ws, flags)
         return out
 
     def preprocess(self, B: int, indices: torch.Tensor, offsets: torch.Tensor,

@@ -29,7 +29,7 @@ TBE_BWD_ORDER_CHUNKS, TBE_BWD_NO_ORDER_CHUNKS = 0x8, 0x10
 TBE_BWD_HIST = 0x20
 
 EXPORTS = ("tbe_plan_create", "tbe_plan_destroy", "tbe_plan_key_bases", "tbe_workspace_size",
-           "tbe_workspace_views", "tbe_forward", "tbe_preprocess",
+           "tbe_workspace_views", "tbe_forward", "tbe_forward_preprocess", "tbe_preprocess",
            "tbe_backward_rowwise_adagrad", "tbe_backward", "tbe_validate", "tbe_prof_enable",
            "tbe_prof_read",
            "tbe_prof_calibrate", "tbe_status_string")
@@ -73,6 +73,8 @@ def lib() -> C.CDLL:
         L.tbe_workspace_views.argtypes = [vp, i64, i64, C.POINTER(WsViews)]
         L.tbe_forward.argtypes = [vp, i64, i32, vp, vp, i64, vp, vp, u32, vp]
         L.tbe_preprocess.argtypes = [vp, i64, i32, vp, vp, i64, vp, vp, C.c_size_t, vp]
+        L.tbe_forward_preprocess.argtypes = [vp, i64, i32, vp, vp, i64, vp, vp, u32, vp,
+                                             C.c_size_t, vp]
         L.tbe_backward_rowwise_adagrad.argtypes = [vp, i64, i32, vp, vp, i64, vp, vp,
                                                    C.c_float, C.c_float, vp, C.c_size_t, u32,
                                                    vp, vp]
@@ -207,6 +209,22 @@ def tbe_validate(plan, B: int, indices, offsets, num_lookups: int, err: torch.Te
                             _dptr(offsets, None, "offsets"), int(num_lookups),
                             _dptr(err, None, "err"), int(flags), _stream(stream))
     _check("tbe_validate", rc)
+
+
+def tbe_forward_preprocess(plan, B: int, indices, offsets, num_lookups: int,
+                           per_sample_weights, out: torch.Tensor, ws: torch.Tensor,
+                           flags: int = 0, stream=None) -> None:
+    """tbe_forward on `stream` and tbe_preprocess into ws on a side stream of the
+    plan, forked from and joined into `stream` (one native call)."""
+    it = _itype(indices, offsets)
+    rc = lib().tbe_forward_preprocess(plan, int(B), it, _dptr(indices, None, "indices"),
+                                      _dptr(offsets, None, "offsets"), int(num_lookups),
+                                      _dptr(per_sample_weights, torch.float32,
+                                            "per_sample_weights"),
+                                      _dptr(out, torch.float32, "out"), int(flags),
+                                      _dptr(ws, None, "ws"), ws.numel() * ws.element_size(),
+                                      _stream(stream))
+    _check("tbe_forward_preprocess", rc)
 
 
 def tbe_preprocess(plan, B: int, indices, offsets, num_lookups: int, per_sample_weights,

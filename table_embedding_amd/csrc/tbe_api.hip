@@ -551,9 +551,10 @@ int tbe_workspace_views(const tbe_plan* P, int64_t B, int64_t N, tbe_ws_views* v
   return TBE_OK;
 }
 
-int tbe_forward(const tbe_plan* P, int64_t B, int32_t itype, const void* indices,
-                const void* offsets, int64_t N, const float* psw, float* out, uint32_t flags,
-                void* stream) {
+namespace {
+// Arguments of tbe_forward (TBE_OK or the error code).
+int check_forward(const tbe_plan* P, int64_t B, int32_t itype, const void* indices,
+                  const void* offsets, int64_t N, const float* psw, float* out, uint32_t flags) {
   int rc = check_lookups(P, B, itype, indices, offsets, N);
   if (rc) return rc;
   if (flags & ~(TBE_FWD_NO_HIST | TBE_FWD_REQUIRE_HIST | TBE_FWD_BALANCE | TBE_FWD_NO_BALANCE))
@@ -562,10 +563,16 @@ int tbe_forward(const tbe_plan* P, int64_t B, int32_t itype, const void* indices
   if ((flags & TBE_FWD_BALANCE) && (flags & TBE_FWD_NO_BALANCE)) return TBE_E_ARG;
   if (B > 0 && (!out || !aligned(out, 16))) return TBE_E_ARG;
   if (psw && !aligned(psw, 4)) return TBE_E_ARG;
+  if ((flags & TBE_FWD_REQUIRE_HIST) && !hist_eligible(P, B, N, psw)) return TBE_E_UNSUPPORTED;
+  return TBE_OK;
+}
+
+// The forward's launches on s (arguments already checked).
+int launch_forward(const tbe_plan* P, int64_t B, int32_t itype, const void* indices,
+                   const void* offsets, int64_t N, const float* psw, float* out, uint32_t flags,
+                   hipStream_t s) {
   const bool hist = hist_eligible(P, B, N, psw);
-  if ((flags & TBE_FWD_REQUIRE_HIST) && !hist) return TBE_E_UNSUPPORTED;
   if (B == 0) return TBE_OK;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   FwdArgs a{P->d_tables, B, itype, indices, offsets, psw, out, P->dtot, 1u};
   hipError_t e = hipSuccess;
   if (hist && !(flags & TBE_FWD_NO_HIST)) {
@@ -592,6 +599,44 @@ int tbe_forward(const tbe_plan* P, int64_t B, int32_t itype, const void* indices
     }
   }
   return e == hipSuccess ? TBE_OK : TBE_E_HIP;
+}
+}  // namespace
+
+int tbe_forward(const tbe_plan* P, int64_t B, int32_t itype, const void* indices,
+                const void* offsets, int64_t N, const float* psw, float* out, uint32_t flags,
+                void* stream) {
+  const int rc = check_forward(P, B, itype, indices, offsets, N, psw, out, flags);
+  if (rc) return rc;
+  return launch_forward(P, B, itype, indices, offsets, N, psw, out, flags,
+                        reinterpret_cast<hipStream_t>(stream));
+}
+
+int tbe_forward_preprocess(const tbe_plan* P, int64_t B, int32_t itype, const void* indices,
+                           const void* offsets, int64_t N, const float* psw, float* out,
+                           uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_forward(P, B, itype, indices, offsets, N, psw, out, flags);
+  if (rc) return rc;
+  rc = check_ws(P, N, ws, ws_bytes);
+  if (rc) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (N == 0) return launch_forward(P, B, itype, indices, offsets, N, psw, out, flags, s);
+  // fork before the forward, so that the side stream waits for the work
+  // before it, not for it; the forward is enqueued first (one launch), then
+  // the preprocessing's launches on the side stream; `s` joins at the end
+  std::lock_guard<std::mutex> lk(P->mu);
+  hipStream_t side = P->side[0];
+  if (hipEventRecord(P->ev_fork, s) != hipSuccess ||
+      hipStreamWaitEvent(side, P->ev_fork, 0) != hipSuccess)
+    return TBE_E_HIP;
+  rc = launch_forward(P, B, itype, indices, offsets, N, psw, out, flags, s);
+  const WsLayout L = layout(P, N);
+  PrepArgs a = prep_args(P, B, itype, indices, offsets, N, psw, ws, &L);
+  if (launch_preprocess(a, P->num_cus, side) != hipSuccess && rc == TBE_OK) rc = TBE_E_HIP;
+  // join even after a failed launch, so `s` never runs ahead of the side stream
+  if (hipEventRecord(P->ev_join[0], side) != hipSuccess ||
+      hipStreamWaitEvent(s, P->ev_join[0], 0) != hipSuccess)
+    rc = TBE_E_HIP;
+  return rc;
 }
 
 int tbe_validate(const tbe_plan* P, int64_t B, int32_t itype, void* indices, void* offsets,

@@ -290,9 +290,12 @@ def test_concurrent_backward_equals_one_stream(name, fused):
 
 @pytest.mark.parametrize("name", ["C2s", "C3s", "empty_bags", "wide_f32"])
 def test_forward_and_preprocess_schedule(name):
-    """Forward with the preprocessing on a side stream, then backward on the
-    preprocessed workspace: same output and tables as forward then a
-    self-preprocessing backward on one stream, and within the oracle's bars."""
+    """Forward with the preprocessing on a side stream (tbe_forward_preprocess),
+    then backward on the preprocessed workspace: same output and tables as
+    forward then a self-preprocessing backward on one stream, and within the
+    oracle's bars.  Then two more steps of each, enqueued without waiting: the
+    next step's preprocessing must wait for the backward that reads the
+    workspace, so the bits still match step for step."""
     _announce(name, "forward||preprocess schedule")
     import table_embedding_amd as te
     case = S.Case(_spec(name), m_nonzero=True)
@@ -300,19 +303,34 @@ def test_forward_and_preprocess_schedule(name):
         pytest.skip("no lookups")
     B = case.spec.B
     tb = case.tbe()
-    out = tb.forward_and_preprocess(B, case.d_idx, case.d_off, case.d_psw)
-    tb.backward(B, case.d_idx, case.d_off, case.d_psw, case.d_G, case.spec.lr, case.spec.eps,
-                flags=te.TBE_BWD_PREPROCESSED | te.TBE_BWD_CONCURRENT)
+
+    def overlapped():
+        o = tb.forward_and_preprocess(B, case.d_idx, case.d_off, case.d_psw)
+        tb.backward(B, case.d_idx, case.d_off, case.d_psw, case.d_G, case.spec.lr,
+                    case.spec.eps, flags=te.TBE_BWD_PREPROCESSED | te.TBE_BWD_CONCURRENT)
+        return o
+    out = overlapped()
     torch.cuda.synchronize()
     S.check_forward(case, out)
     S.check_backward(case, tb)
-    got = (out.cpu().numpy().tobytes(), _tables_bytes(tb, case.spec.wdtype))
+    got = [(out.cpu().numpy().tobytes(), _tables_bytes(tb, case.spec.wdtype))]
+    outs = [overlapped() for _ in range(2)]
+    torch.cuda.synchronize()
+    got.append((outs[-1].cpu().numpy().tobytes(), _tables_bytes(tb, case.spec.wdtype)))
     case.reset_tables()
     tb2 = case.tbe()
-    out2 = tb2.forward(B, case.d_idx, case.d_off, case.d_psw)
-    tb2.backward(B, case.d_idx, case.d_off, case.d_psw, case.d_G, case.spec.lr, case.spec.eps)
+
+    def serial():
+        o = tb2.forward(B, case.d_idx, case.d_off, case.d_psw)
+        tb2.backward(B, case.d_idx, case.d_off, case.d_psw, case.d_G, case.spec.lr,
+                     case.spec.eps)
+        return o
+    out2 = serial()
     torch.cuda.synchronize()
-    assert got == (out2.cpu().numpy().tobytes(), _tables_bytes(tb2, case.spec.wdtype))
+    assert got[0] == (out2.cpu().numpy().tobytes(), _tables_bytes(tb2, case.spec.wdtype))
+    outs2 = [serial() for _ in range(2)]
+    torch.cuda.synchronize()
+    assert got[1] == (outs2[-1].cpu().numpy().tobytes(), _tables_bytes(tb2, case.spec.wdtype))
 
 
 @pytest.mark.parametrize("name", ["C3s", "C5s", "many_tables", "const257"])

@@ -76,4 +76,6 @@ def test_host_argument_errors_need_no_gpu():
     n = C.c_size_t()
     assert L.tbe_workspace_size(None, 1, 1, C.byref(n)) == te.TBE_E_ARG
     assert L.tbe_forward(None, 1, 0, None, None, 0, None, None, 0, None) == te.TBE_E_ARG
+    assert L.tbe_forward_preprocess(None, 1, 0, None, None, 0, None, None, 0, None, 0,
+                                    None) == te.TBE_E_ARG
     assert L.tbe_plan_destroy(None) == te.TBE_OK
