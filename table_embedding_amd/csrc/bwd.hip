@@ -204,10 +204,56 @@ __device__ __forceinline__ void subgroup_row_update(const BwdArgs& a, const Tabl
 }
 
 // ------------------------------------------------------- single-lookup runs
-// Most runs have one lookup.  A subgroup takes two of them per iteration: the
-// task records (which carry the lookup's bag), then both weight rows, momenta,
+// Most runs have one lookup.  A subgroup takes two of them per step: the task
+// records (which carry the lookup's bag), then both weight rows, momenta,
 // grad_out slices and scales are loaded before the first use -- one memory
 // round trip per pair of runs after the task load.
+template <int WD, int VEC, int NC, bool SCALE, bool TDL>
+__device__ __forceinline__ void single_pair(const BwdArgs& a, const TableDev* s_td, uint4 tk0,
+                                            uint4 tk1, bool two, uint32_t lpr,
+                                            uint32_t lane_in) {
+  uint4 tk[2] = {tk0, tk1};  // {start, row, table, bag}
+  TableDev td[2];
+  bool ok[2];
+  int64_t row[2], b[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    // sanity bounds, never false for lists the preprocessing wrote
+    const uint32_t t = tk[u].z < a.T ? tk[u].z : 0u;
+    td[u] = get_td<TDL>(a, s_td, t);
+    const int64_t bb = (int64_t)tk[u].w - (int64_t)t * a.B;
+    ok[u] = tk[u].z < a.T && tk[u].x < a.N && tk[u].y < td[u].rows && bb >= 0 && bb < a.B;
+    row[u] = ok[u] ? (int64_t)tk[u].y : 0;
+    b[u] = ok[u] ? bb : 0;
+  }
+  uint32_t colc[2][NC], cold[2][NC];
+  float w[2][NC][VEC], g[2][NC][VEC], m0[2], sc[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      colc[u][c] = (lane_in + (uint32_t)c * lpr) * VEC;
+      cold[u][c] = colc[u][c] < td[u].dim ? colc[u][c] : 0u;
+      load_w<WD, VEC>(td[u].w, row[u] * td[u].dim + cold[u][c], w[u][c]);
+      load_f32<VEC>(a.grad + b[u] * (int64_t)a.dtot + td[u].col + cold[u][c], g[u][c]);
+    }
+    m0[u] = a.opt == OPT_ROWWISE_ADAGRAD ? td[u].m[row[u]] : 0.f;
+    sc[u] = SCALE ? a.sorted_scale[ok[u] ? tk[u].x : 0u] : 1.0f;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if (SCALE)
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) g[u][c][e] *= sc[u];
+    subgroup_row_update<WD, VEC, NC>(a, td[u], row[u], m0[u], w[u], g[u], colc[u], lpr, lane_in,
+                                     ok[u] && (u == 0 || two));
+  }
+}
+
+// In list order: subgroup sg of the launch takes positions sg, sg + nsg, ...
 template <int WD, int VEC, int NC, bool SCALE, bool TDL>
 __global__ __launch_bounds__(kThreads) void bwd_single_kernel(BwdArgs a, BucketSet S) {
   BucketDev bk;
@@ -223,47 +269,8 @@ __global__ __launch_bounds__(kThreads) void bwd_single_kernel(BwdArgs a, BucketS
   const uint32_t end = min(list_begin(a, 0, bucket + 1), a.max_single);
   for (uint32_t s = beg + sg; s < end; s += 2 * nsg_grid) {
     const uint32_t s1 = (s + nsg_grid < end) ? s + nsg_grid : s;
-    uint4 tk[2];  // {start, row, table, bag}
-    tk[0] = a.single_task[s];
-    tk[1] = a.single_task[s1];
-    TableDev td[2];
-    bool ok[2];
-    int64_t row[2], b[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      // sanity bounds, never false for lists the preprocessing wrote
-      const uint32_t t = tk[u].z < a.T ? tk[u].z : 0u;
-      td[u] = get_td<TDL>(a, s_td, t);
-      const int64_t bb = (int64_t)tk[u].w - (int64_t)t * a.B;
-      ok[u] = tk[u].z < a.T && tk[u].x < a.N && tk[u].y < td[u].rows && bb >= 0 && bb < a.B;
-      row[u] = ok[u] ? (int64_t)tk[u].y : 0;
-      b[u] = ok[u] ? bb : 0;
-    }
-    uint32_t colc[2][NC], cold[2][NC];
-    float w[2][NC][VEC], g[2][NC][VEC], m0[2], sc[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        colc[u][c] = (lane_in + (uint32_t)c * lpr) * VEC;
-        cold[u][c] = colc[u][c] < td[u].dim ? colc[u][c] : 0u;
-        load_w<WD, VEC>(td[u].w, row[u] * td[u].dim + cold[u][c], w[u][c]);
-        load_f32<VEC>(a.grad + b[u] * (int64_t)a.dtot + td[u].col + cold[u][c], g[u][c]);
-      }
-      m0[u] = a.opt == OPT_ROWWISE_ADAGRAD ? td[u].m[row[u]] : 0.f;
-      sc[u] = SCALE ? a.sorted_scale[ok[u] ? tk[u].x : 0u] : 1.0f;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (SCALE)
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) g[u][c][e] *= sc[u];
-      subgroup_row_update<WD, VEC, NC>(a, td[u], row[u], m0[u], w[u], g[u], colc[u], lpr,
-                                       lane_in, ok[u] && (u == 0 || s1 != s));
-    }
+    single_pair<WD, VEC, NC, SCALE, TDL>(a, s_td, a.single_task[s], a.single_task[s1], s1 != s,
+                                         lpr, lane_in);
   }
 }
 

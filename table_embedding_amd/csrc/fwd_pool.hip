@@ -58,13 +58,6 @@ __device__ __forceinline__ double fma_acc(double s, float v, double acc) {
   return __builtin_fma(s, (double)v, acc);
 }
 
-// LDS visibility inside one wave: every lane's stores before any lane's loads.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 template <int WD, int VEC, int NC, typename IT, bool PSW>
 __global__ __launch_bounds__(kThreads) void fwd_bal_kernel(FwdArgs a, BucketSet S) {
   using AT = typename Acc<WD>::T;

@@ -288,6 +288,13 @@ __device__ __forceinline__ float subgroup_sum(float v, uint32_t lpr) {
 
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & (kWave - 1); }
 
+// LDS visibility inside one wave: every lane's stores before any lane's loads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ------------------------------------------------------------ host launchers
 
 // Optional per-kernel timing (tbe_prof_enable): when on, every launch is
