@@ -723,16 +723,27 @@ uint32_t set_grid(BucketSet& S, const BwdGrids* g, uint32_t BwdGrids::*field, ui
 // always (at the same three sizes: 24.8 -> 20.5, 179 -> 146, 1449 -> 1189).
 constexpr uint32_t kBwdDeepLookups = 64u << 20;
 
+// Single-lookup runs of a deep batch: the persistent grid at half the
+// resident workgroups.  The workgroups sweep the row-sorted list together, so
+// the grid size sets how wide a window of weight rows is read and rewritten at
+// once; on 64 tables of 5 M rows a window half as wide is faster (MI355X,
+// us per launch at 1 / 0.83 / 0.67 / 0.5 / 0.33 / 0.25 of the resident grid:
+// 3588 / 3613 / 3212 / 3054 / 3376 / 4236 over two runs), while the short
+// launches need every workgroup (2.1 M lookups: 50.4 at 1, 61.2 at 0.5;
+// 17 M: 286 at 1, 431 at 0.5).  The other run classes lose with any cap.
+constexpr uint32_t kSingleDeepGridDiv = 2;
+
 template <int WD, int VEC, int NC, bool TDL, int IF>
 void launch_small(const BwdArgs& a, BucketSet S, const BwdGrids* g, int cus, hipStream_t s) {
+  const uint32_t div = IF == kInFlightDeep ? kSingleDeepGridDiv : 1u;
   if (a.sorted_scale) {
     static const uint32_t cap = resident(bwd_single_kernel<WD, VEC, NC, true, TDL>, cus);
-    const uint32_t grid = set_grid(S, g, &BwdGrids::single, cap);
+    const uint32_t grid = set_grid(S, g, &BwdGrids::single, cap / div);
     TBE_LAUNCH("bwd_single", (bwd_single_kernel<WD, VEC, NC, true, TDL>), dim3(grid),
                dim3(kThreads), s, a, S);
   } else {
     static const uint32_t cap = resident(bwd_single_kernel<WD, VEC, NC, false, TDL>, cus);
-    const uint32_t grid = set_grid(S, g, &BwdGrids::single, cap);
+    const uint32_t grid = set_grid(S, g, &BwdGrids::single, cap / div);
     TBE_LAUNCH("bwd_single", (bwd_single_kernel<WD, VEC, NC, false, TDL>), dim3(grid),
                dim3(kThreads), s, a, S);
   }

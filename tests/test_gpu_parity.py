@@ -433,3 +433,47 @@ def test_backward_hist_unsupported():
                     case.spec.eps, flags=te.TBE_BWD_HIST)
     assert ei.value.code == te.TBE_E_UNSUPPORTED
     tb.close()
+
+
+@pytest.mark.parametrize("name", ["C2s", "C3s", "const257"])
+def test_graph_capture_replays_equal_eager(name):
+    """A forward + backward step (preprocessing inside, one stream) captured in
+    a HIP graph: the step launches kernels only (no allocation, copy or memset),
+    so it can be captured.  Three replays, with eager steps of another plan and
+    synchronizations between them, each give the bits of the same number of
+    eager steps."""
+    _announce(name, "graph capture")
+    import table_embedding_amd as te
+    case = S.Case(_spec(name))
+    B = case.spec.B
+    tb = case.tbe()
+    ws = tb.workspace(B, case.N)
+    out = torch.empty((B, case.spec.dtot), dtype=torch.float32, device="cuda")
+
+    def step(t, w, o):
+        te.tbe_forward(t.plan, B, case.d_idx, case.d_off, case.N, case.d_psw, o)
+        te.tbe_backward_rowwise_adagrad(t.plan, B, case.d_idx, case.d_off, case.N, case.d_psw,
+                                        case.d_G, case.spec.lr, case.spec.eps, w, 0)
+    step(tb, ws, out)  # first calls outside the capture (per-kernel occupancy queries)
+    torch.cuda.synchronize()
+    case.reset_tables()
+    tb = case.tbe()
+    ws = tb.workspace(B, case.N)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        step(tb, ws, out)
+    torch.cuda.synchronize()
+    case.reset_tables()  # the eager plan gets its own copy of the initial tables
+    tb2 = case.tbe()
+    ws2 = tb2.workspace(B, case.N)
+    out2 = torch.empty_like(out)
+    for r in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        step(tb2, ws2, out2)
+        torch.cuda.synchronize()
+        assert (out.cpu().numpy().tobytes(), _tables_bytes(tb, case.spec.wdtype)) == \
+            (out2.cpu().numpy().tobytes(), _tables_bytes(tb2, case.spec.wdtype)), r
+    del g
