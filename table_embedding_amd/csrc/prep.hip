@@ -599,7 +599,7 @@ __global__ __launch_bounds__(kThreads) void sort_pass_kernel(SortPass p) {
 // coalesced, and runs are numbered group by group in slot order.  Four
 // groups per tile make the look-back chain a quarter as long.
 
-__global__ __launch_bounds__(kThreads) void rle_kernel(const uint32_t* __restrict__ key, uint32_t N,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void rle_kernel(const uint32_t* __restrict__ key, uint32_t N,
                                                        uint32_t ntiles, uint32_t* ticket,
                                                        uint64_t* st, uint32_t* err,
                                                        uint32_t* __restrict__ counters,
@@ -607,6 +607,7 @@ __global__ __launch_bounds__(kThreads) void rle_kernel(const uint32_t* __restric
                                                        uint32_t* __restrict__ run_key) {
   __shared__ uint32_t sh4[4];
   __shared__ uint32_t s_tile, s_excl;
+  __shared__ uint32_t s_rs[kTile], s_rk[kTile];  // one group's run heads, staged
   const uint32_t tile = take_ticket(ticket, &s_tile);
   uint32_t k[kRleGroups][kItems];
   uint32_t m[kRleGroups];  // run heads among this thread's 16 slots of each group
@@ -627,13 +628,15 @@ __global__ __launch_bounds__(kThreads) void rle_kernel(const uint32_t* __restric
       }
     }
   }
-  uint32_t local[kRleGroups], total = 0;
+  uint32_t local[kRleGroups], gbase[kRleGroups + 1], total = 0;
 #pragma unroll
   for (int g = 0; g < kRleGroups; ++g) {
     uint32_t tg;
-    local[g] = total + block_excl_scan(__popc(m[g]), sh4, tg);
+    gbase[g] = total;
+    local[g] = block_excl_scan(__popc(m[g]), sh4, tg);  // within the group
     total += tg;
   }
+  gbase[kRleGroups] = total;
   if (threadIdx.x < (uint32_t)kWave) {  // wave 0
     const uint32_t excl = publish_and_look_back<64>(st, tile, 1, 0, total, err);
     if (threadIdx.x == 0) {
@@ -645,19 +648,30 @@ __global__ __launch_bounds__(kThreads) void rle_kernel(const uint32_t* __restric
     }
   }
   __syncthreads();
+  const uint32_t excl = s_excl;
+  // a group's run heads go to LDS in run order, then out with coalesced
+  // stores (written straight from each thread's slots, most lanes of every
+  // store would be masked off: runs are a fraction of the slots)
 #pragma unroll
   for (int g = 0; g < kRleGroups; ++g) {
     const uint64_t i0 = (uint64_t)tile * kRleTile + (uint64_t)g * kTile +
                         (uint64_t)threadIdx.x * kItems;
-    uint32_t u = s_excl + local[g];
+    uint32_t u = local[g];
 #pragma unroll
     for (int e = 0; e < kItems; ++e) {
       if (m[g] & (1u << e)) {
-        run_start[u] = (uint32_t)(i0 + e);
-        run_key[u] = k[g][e];
+        s_rs[u] = (uint32_t)(i0 + e);
+        s_rk[u] = k[g][e];
         ++u;
       }
     }
+    __syncthreads();
+    const uint32_t ng = gbase[g + 1] - gbase[g];
+    for (uint32_t i = threadIdx.x; i < ng; i += kThreads) {
+      run_start[excl + gbase[g] + i] = s_rs[i];
+      run_key[excl + gbase[g] + i] = s_rk[i];
+    }
+    __syncthreads();  // the group's heads are out before the next group's go in
   }
 }
 
