@@ -367,8 +367,15 @@ def main():
     launches = dk["launches_per_step"]
     bytes_per_launch = comp.get(dom, 0) / launches
     achieved = bytes_per_launch / (dk["avg_launch_us"] * 1e3)  # GB/s
-    traffic = counter_traffic(dom, args.config)
+    pmc_key = args.config + ("_hist" if args.bwd_hist else "")
+    traffic = counter_traffic(dom, pmc_key)
     step_comp = sum(comp[k] for k in kernels if k in comp)
+    # counter-measured HBM bytes of the whole step: every kernel's committed
+    # FETCH_SIZE + WRITE_SIZE per launch (calibrated) times its launches per
+    # step; null unless every kernel's counters were taken on its current source
+    per_kernel = {k: counter_traffic(k, pmc_key) for k in kernels}
+    step_counter = (sum(per_kernel[k] * kernels[k]["launches_per_step"] for k in kernels)
+                    if kernels and all(v is not None for v in per_kernel.values()) else None)
     step_logi = sum(logi[k] for k in kernels if k in logi)
     lookups_s = N / (ms / 1e3)
     res = {
@@ -406,7 +413,16 @@ def main():
                 "achieved_gbs_compulsory": round(step_comp / (ms * 1e6), 1),
                 "frac_of_peak_compulsory": round(step_comp / (ms * 1e6) / HBM_PEAK_GBS, 4),
                 "logical_bytes_per_step": int(step_logi),
-                "effective_gbs_logical": round(step_logi / (ms * 1e6), 1)},
+                "effective_gbs_logical": round(step_logi / (ms * 1e6), 1),
+                "counter_bytes_per_step": None if step_counter is None else int(step_counter),
+                "counter_gbs": None if step_counter is None else
+                round(step_counter / (ms * 1e6), 1),
+                "counter_frac_of_peak": None if step_counter is None else
+                round(step_counter / (ms * 1e6) / HBM_PEAK_GBS, 4),
+                "traffic_ratio": None if step_counter is None or not step_comp else
+                round(step_counter / step_comp, 3),
+                "counter_source": "profiles/pmc_traffic.json (rocprofv3 FETCH_SIZE x2.000 + "
+                                  "WRITE_SIZE x1.000 per launch, serial schedule)"},
         "kernel_timing": {"method": "HIP events around every launch on the stream it is "
                                     "launched on, over a second pass of the same steps; "
                                     "avg_launch_us is the bracketed time minus the average "
