@@ -28,7 +28,7 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = {
     "fwd_pool": "fwd_pool.hip", "fwd_hist": "fwd_hist.hip", "bwd_single": "bwd.hip",
     "bwd_tiny": "bwd.hip", "bwd_medium": "bwd.hip", "bwd_chunk": "bwd.hip",
-    "bwd_long_update": "bwd.hip", "bwd_chunk_fused": "bwd.hip",
+    "bwd_long_update": "bwd.hip", "bwd_chunk_fused": "bwd.hip", "chunk_order": "bwd.hip",
     "bwd_hist_partial": "bwd_hist.hip", "bwd_hist_update": "bwd_hist.hip",
     "validate_check": "validate.hip",
 }
