@@ -16,6 +16,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import tbe_workloads as wl
 from tests import support as S
 
@@ -477,3 +478,47 @@ def test_graph_capture_replays_equal_eager(name):
         assert (out.cpu().numpy().tobytes(), _tables_bytes(tb, case.spec.wdtype)) == \
             (out2.cpu().numpy().tobytes(), _tables_bytes(tb2, case.spec.wdtype)), r
     del g
+
+
+def test_forward_table_over_4gib():
+    """A table of more than 4 GiB (2^25 + 1024 rows x 64 f16) beside a small one:
+    the equal-piece forward reads rows with 32-bit byte offsets, so for this plan
+    the host falls back to one bag per subgroup (64-bit addresses).  Lookups of
+    rows near the end of the big table (byte offsets past 2^32) and near its
+    start pool as the oracle pools the same rows renumbered into a compact
+    table; the default and TBE_FWD_NO_BALANCE give the same bits."""
+    import table_embedding_amd as te
+    _announce("table_over_4gib", "forward")
+    R0, D0, R1, D1, B = (1 << 25) + 1024, 64, 100, 32, 64
+    assert R0 * D0 * 2 > (1 << 32)
+    rng = np.random.default_rng(2012)
+    hot = np.concatenate([R0 - 1 - 7919 * np.arange(40), np.arange(10)]).astype(np.int64)
+    lengths = rng.integers(0, 9, size=2 * B)
+    off = np.zeros(2 * B + 1, np.int64)
+    np.cumsum(lengths, out=off[1:])
+    n0 = int(off[B])
+    idx = np.concatenate([hot[rng.integers(0, hot.size, size=n0)],
+                          rng.integers(0, R1, size=int(off[-1]) - n0)]).astype(np.int64)
+    vals = rng.uniform(-1, 1, size=(hot.size, D0)).astype(np.float16)
+    small = rng.uniform(-1, 1, size=(R1, D1)).astype(np.float16)
+    big = torch.empty((R0, D0), dtype=torch.float16, device="cuda")
+    big[torch.from_numpy(hot).cuda()] = torch.from_numpy(vals).cuda()
+    W = [big, torch.from_numpy(small).cuda()]
+    M = [torch.zeros(R0, device="cuda"), torch.zeros(R1, device="cuda")]
+    tb = te.TBE([R0, R1], [D0, D1], [0, 1], W, M)
+    d_idx, d_off = torch.from_numpy(idx).cuda(), torch.from_numpy(off).cuda()
+    got = tb.forward(B, d_idx, d_off, None, flags=te.TBE_FWD_NO_HIST)
+    got1 = tb.forward(B, d_idx, d_off, None, flags=te.TBE_FWD_NO_HIST | te.TBE_FWD_NO_BALANCE)
+    torch.cuda.synchronize()
+    assert got.cpu().numpy().tobytes() == got1.cpu().numpy().tobytes()
+    # the oracle on the touched rows, renumbered: row hot[k] of table 0 becomes row k
+    renum = {int(r): k for k, r in enumerate(hot)}
+    idx_c = idx.copy()
+    idx_c[:n0] = [renum[int(r)] for r in idx[:n0]]
+    ref = oracle.forward([hot.size, R1], [D0, D1], [0, 1], "f16",
+                         [vals.view(np.uint16), small.view(np.uint16)], B, "i64", idx_c, off)
+    err = np.abs(got.cpu().numpy().astype(np.float64) - ref) / np.maximum(1.0, np.abs(ref))
+    assert err.max() <= 1e-4, err.max()
+    tb.close()
+    del big, W, M
+    torch.cuda.empty_cache()
