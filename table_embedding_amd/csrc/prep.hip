@@ -367,6 +367,17 @@ __device__ __forceinline__ uint4 tile_span(const uint4* __restrict__ seg,
   return sg;
 }
 
+// Tile of this workgroup in the sort passes, XCD-major: workgroup i runs on
+// XCD i mod 8, and with a grid of 8 * per workgroups XCD x takes the
+// contiguous tiles [x * per, (x + 1) * per).  Neighbouring tiles write
+// neighbouring bytes (the digit counts of consecutive tiles share cache
+// lines; a digit's keys of consecutive tiles land next to each other), so
+// their partial lines merge in one L2 instead of being written back from
+// eight.
+__device__ __forceinline__ uint32_t xcd_tile() {
+  return (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+}
+
 // Counts of each digit value of one pass for every tile of the pass's input,
 // digit-major: cnt[d * ntiles + tile], digits of the row (key - key_base).
 // A wave whose 64 keys share one digit (a tile inside a hot row's run) adds
@@ -382,7 +393,7 @@ __global__ __launch_bounds__(kThreads) void radix_upsweep(const uint32_t* __rest
                                                           uint64_t* __restrict__ st, uint64_t nst) {
   __shared__ uint32_t h[kThreads / kWave][256];
   const uint32_t wave = threadIdx.x / kWave, lane = lane_id();
-  const uint32_t tile = blockIdx.x;
+  const uint32_t tile = xcd_tile();
   const bool live = tile < ctl[kCtlTiles];
   for (uint32_t i = threadIdx.x; i < (uint32_t)(4 * 256); i += kThreads) (&h[0][0])[i] = 0u;
   __syncthreads();
@@ -486,7 +497,7 @@ __global__ __launch_bounds__(kThreads) void sort_pass_kernel(SortPass p) {
   __shared__ uint32_t sh4[4];
 
   const uint32_t lane = lane_id(), wave = threadIdx.x / kWave;
-  const uint32_t tile = blockIdx.x;
+  const uint32_t tile = xcd_tile();
   if (tile >= *p.tiles) return;  // the grid is sized for the most tiles segments can need
   for (uint32_t i = threadIdx.x; i < 4 * 256; i += kThreads) (&wcnt[0][0])[i] = 0u;
   uint32_t sid, b, e;
@@ -982,6 +993,7 @@ hipError_t launch_preprocess(const PrepArgs& p, int /*num_cus*/, hipStream_t s) 
 
   // ping-pong a -> b -> a ...; the final buffers are b for an odd pass count
   const uint64_t nst = (L.st_end - L.st_rle) / 8;
+  const uint32_t sgrid = 8u * ((L.ntiles_max + 7u) / 8u);  // xcd_tile(): a multiple of 8
   for (int pass = 0; pass < L.npass; ++pass) {
     const bool ab = (pass % 2) == 0;
     SortPass sp{u32p(ab ? L.key_a : L.key_b), u32p(ab ? L.val_a : L.val_b),
@@ -989,16 +1001,16 @@ hipError_t launch_preprocess(const PrepArgs& p, int /*num_cus*/, hipStream_t s) 
                 u32p(ab ? L.val_b : L.val_a), f32p(ab ? L.sc_b : L.sc_a),
                 (uint32_t)(pass * kRadixBits), seg, tile_seg, ctl + kCtlTiles,
                 totals, u32p(L.tile_cnt), L.ntiles_max};
-    TBE_LAUNCH("radix_upsweep", radix_upsweep, dim3(L.ntiles_max), dim3(kThreads), s, sp.kin,
+    TBE_LAUNCH("radix_upsweep", radix_upsweep, dim3(sgrid), dim3(kThreads), s, sp.kin,
                seg, tile_seg, ctl, sp.shift, u32p(L.tile_cnt), L.ntiles_max,
                u64p(L.st_rle), pass == 0 ? nst : (uint64_t)0);
     TBE_LAUNCH("radix_scan", radix_scan, dim3(256), dim3(kThreads), s, u32p(L.tile_cnt),
                L.ntiles_max, ctl, totals);
     if (sc)
-      TBE_LAUNCH("radix_downsweep", sort_pass_kernel<true>, dim3(L.ntiles_max), dim3(kThreads),
+      TBE_LAUNCH("radix_downsweep", sort_pass_kernel<true>, dim3(sgrid), dim3(kThreads),
                  s, sp);
     else
-      TBE_LAUNCH("radix_downsweep", sort_pass_kernel<false>, dim3(L.ntiles_max), dim3(kThreads),
+      TBE_LAUNCH("radix_downsweep", sort_pass_kernel<false>, dim3(sgrid), dim3(kThreads),
                  s, sp);
   }
   const uint32_t* skey = u32p(L.final_in_b ? L.key_b : L.key_a);
