@@ -758,8 +758,15 @@ __device__ __forceinline__ uint32_t bucket_of_key(const uint32_t* bkb, uint32_t 
 constexpr uint32_t kHeavyChunks = 4096;
 
 __global__ __launch_bounds__(kThreads) void classify_kernel(ClsDev a) {
-  __shared__ uint32_t s_kb[kMaxTables];
-  __shared__ uint32_t s_ord[kMaxTables];
+  // dynamic LDS: the T key bases and table ids in key order (2 T words)
+  extern __shared__ uint32_t s_dyn[];
+  uint32_t* s_kb = s_dyn;
+  uint32_t* s_ord = s_dyn + a.T;
+  // the tile's single-lookup and tiny-run tasks, staged in list order and
+  // written out with coalesced stores after the classification (written
+  // straight from each thread's runs, most lanes of every store are masked
+  // and the lines fill in pieces)
+  __shared__ uint4 s_stage[kClsTile];
   __shared__ uint32_t s_bkb[kMaxBuckets + 1];
   __shared__ uint32_t sh4[4];
   __shared__ uint32_t s_tile;
@@ -837,6 +844,7 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClsDev a) {
   }
   if (mine)
     for (int q = 0; q < kNumLists; ++q) pos[q] += s_excl[q];
+  const uint32_t ex0 = s_excl[0], ex1 = s_excl[1], tot0 = s_tot[0], tot1 = s_tot[1];
   int bprev = u0 == 0 ? -1 : (int)bucket_of_key(s_bkb, a.nb, keyprev);
   // Every thread takes every step (no early exit), so that each step's long
   // runs can be placed by the whole wave or workgroup.
@@ -862,10 +870,10 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClsDev a) {
       bprev = bcur;
       if (ln == 1u) {
         // {start, row, table, bag of the lookup}
-        if (pos[0] < a.N) a.single_task[pos[0]] = make_uint4(st, row, t, bag0[e]);
+        s_stage[pos[0] - ex0] = make_uint4(st, row, t, bag0[e]);
         ++pos[0];
       } else if (ln < (uint32_t)kTinyRun) {
-        if (pos[1] < a.max_tiny) a.tiny_task[pos[1]] = make_uint4(st, ln, row, t);
+        s_stage[tot0 + pos[1] - ex1] = make_uint4(st, ln, row, t);
         ++pos[1];
       } else if (ln < (uint32_t)kLongRun) {
         if (pos[2] < a.max_med) a.med_task[pos[2]] = make_uint4(st, ln, row, t);
@@ -956,6 +964,13 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClsDev a) {
       __syncthreads();  // the list is rewritten by the next step
     }
   }
+  // singles at [0, tot0) and tiny runs at [tot0, tot0 + tot1) of the stage
+  // (tot0 + tot1 <= the tile's runs <= kClsTile)
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < tot0; i += kThreads)
+    if (ex0 + i < a.N) a.single_task[ex0 + i] = s_stage[i];
+  for (uint32_t i = threadIdx.x; i < tot1; i += kThreads)
+    if (ex1 + i < a.max_tiny) a.tiny_task[ex1 + i] = s_stage[tot0 + i];
 }
 
 }  // namespace
@@ -1026,7 +1041,8 @@ hipError_t launch_preprocess(const PrepArgs& p, int /*num_cus*/, hipStream_t s) 
            reinterpret_cast<uint4*>(ws + L.long_task), u32p(L.long_cbeg), u32p(L.remaining),
            reinterpret_cast<uint4*>(ws + L.chunk_task), p.tables, p.order, p.bucket_key_begin,
            p.T, p.nb, p.N, L.max_tiny, L.max_med, L.max_long, L.max_chunks};
-  TBE_LAUNCH("classify", classify_kernel, dim3(L.ncls_tiles), dim3(kThreads), s, c);
+  TBE_LAUNCH_SHM("classify", classify_kernel, dim3(L.ncls_tiles), dim3(kThreads),
+                 2 * sizeof(uint32_t) * (size_t)p.T, s, c);
   return hipGetLastError();
 }
 

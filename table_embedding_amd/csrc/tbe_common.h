@@ -308,6 +308,13 @@ void prof_end(hipStream_t s);
     hipLaunchKernelGGL(kernel, (grid), (block), 0, (stream), __VA_ARGS__);   \
     ::tbe::prof_end((stream));                                               \
   } while (0)
+// The same with `shm` bytes of dynamic LDS.
+#define TBE_LAUNCH_SHM(name, kernel, grid, block, shm, stream, ...)            \
+  do {                                                                       \
+    ::tbe::prof_begin((stream), (name));                                     \
+    hipLaunchKernelGGL(kernel, (grid), (block), (shm), (stream), __VA_ARGS__); \
+    ::tbe::prof_end((stream));                                               \
+  } while (0)
 
 // Forward: bags per wave.  A wave owns this many consecutive bags of one
 // table and splits them among its 64/lpr lane subgroups into contiguous runs
