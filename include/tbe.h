@@ -196,9 +196,10 @@ int tbe_preprocess(const tbe_plan* plan, int64_t B, int32_t itype, const void* i
  * Preprocesses unless TBE_BWD_PREPROCESSED, then updates each run with
  * SL < 256 in one owning program (a lane subgroup below SL 32, a workgroup
  * from 32 to 255) and runs with SL >= 256 through 256-lookup chunk partial
- * sums plus an update pass (or, with TBE_BWD_FUSED_LONG, a device-scope fence
- * and countdown so the last chunk of a run updates it; both give bit-identical
- * weights).  Weights and momentum of touched rows are updated in place;
+ * sums plus an update pass (or, with TBE_BWD_FUSED_LONG, each chunk writes
+ * its partial with device-coherent write-through atomic stores and counts down
+ * the run's remaining chunks, so that the last chunk of a run updates it; no
+ * whole-cache fence is used; both give bit-identical weights).  Weights and momentum of touched rows are updated in place;
  * untouched rows are not written.  debug_row_updates (device, nullable): one
  * uint32 per linear key, incremented once per row update.
  * By default every kernel runs on `stream`, one after another.  The run
