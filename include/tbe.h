@@ -87,7 +87,7 @@ extern "C" {
 #define TBE_FWD_NO_BALANCE 0x8u    /* generic path: one whole bag per lane subgroup */
 /* tbe_backward_rowwise_adagrad flags */
 #define TBE_BWD_PREPROCESSED 0x1u  /* the workspace already holds tbe_preprocess of these inputs */
-#define TBE_BWD_FUSED_LONG 0x2u    /* long runs: fused fence + countdown instead of a second launch */
+#define TBE_BWD_FUSED_LONG 0x2u    /* long runs: partials + countdown, last chunk updates (no second launch) */
 #define TBE_BWD_CONCURRENT 0x4u    /* run classes on three streams (fork from and join into `stream`) */
 #define TBE_BWD_ORDER_CHUNKS 0x8u  /* always walk each table's chunks in bag order (see below) */
 #define TBE_BWD_NO_ORDER_CHUNKS 0x10u /* never: walk chunks in list order */
@@ -199,7 +199,8 @@ int tbe_preprocess(const tbe_plan* plan, int64_t B, int32_t itype, const void* i
  * sums plus an update pass (or, with TBE_BWD_FUSED_LONG, each chunk writes
  * its partial with device-coherent write-through atomic stores and counts down
  * the run's remaining chunks, so that the last chunk of a run updates it; no
- * whole-cache fence is used; both give bit-identical weights).  Weights and momentum of touched rows are updated in place;
+ * whole-cache fence is used; both give bit-identical weights).  Weights and
+ * momentum of touched rows are updated in place;
  * untouched rows are not written.  debug_row_updates (device, nullable): one
  * uint32 per linear key, incremented once per row update.
  * By default every kernel runs on `stream`, one after another.  The run
