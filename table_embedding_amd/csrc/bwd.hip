@@ -148,7 +148,7 @@ __device__ __forceinline__ TableDev get_td(const BwdArgs& a, const TableDev* s_t
 // Row-wise Adagrad: M += mean_d g^2, w -= lr g / (sqrt(M) + eps).  Element-
 // wise Adagrad (HugeCTR walkthrough, step 5): A[row][d] += g[d]^2 per column,
 // w -= lr g / (sqrt(A) + eps).  SGD: w -= lr g, no state.
-template <int WD, int VEC, int NC>
+template <int WD, int VEC, int NC, bool NT>
 __device__ __forceinline__ void subgroup_row_update(const BwdArgs& a, const TableDev& td,
                                                     int64_t row, float m0, const float (*w)[VEC],
                                                     const float (*g)[VEC], const uint32_t* colc,
@@ -175,7 +175,7 @@ __device__ __forceinline__ void subgroup_row_update(const BwdArgs& a, const Tabl
 #pragma unroll
         for (int e = 0; e < VEC; ++e) o[e] = w[c][e] - a.lr * g[c][e];
       }
-      store_w<WD, VEC>(td.w, row * D + colc[c], o);
+      store_w<WD, VEC, NT>(td.w, row * D + colc[c], o);
     }
     return;
   }
@@ -189,7 +189,7 @@ __device__ __forceinline__ void subgroup_row_update(const BwdArgs& a, const Tabl
   if (!store) return;
   const float m = m0 + sq / (float)D;
   if (lane_in == 0) {
-    td.m[row] = m;
+    gstore(td.m + row, m);
     if (a.debug_count) atomicAdd(&a.debug_count[td.key_base + (uint32_t)row], 1u);
   }
   const float den = sqrtf(m) + a.eps;
@@ -199,25 +199,26 @@ __device__ __forceinline__ void subgroup_row_update(const BwdArgs& a, const Tabl
     float o[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) o[e] = w[c][e] - (a.lr * g[c][e]) / den;
-    store_w<WD, VEC>(td.w, row * D + colc[c], o);
+    store_w<WD, VEC, NT>(td.w, row * D + colc[c], o);
   }
 }
 
 // ------------------------------------------------------- single-lookup runs
-// Most runs have one lookup.  A subgroup takes two of them per step: the task
-// records (which carry the lookup's bag), then both weight rows, momenta,
-// grad_out slices and scales are loaded before the first use -- one memory
-// round trip per pair of runs after the task load.
-template <int WD, int VEC, int NC, bool SCALE, bool TDL>
+// Most runs have one lookup.  A subgroup takes P (1 or 2) of them per step:
+// the task records (which carry the lookup's bag), then every weight row,
+// momentum, grad_out slice and scale of the step is loaded before the first
+// use -- one memory round trip per step after the task load.
+template <int WD, int VEC, int NC, bool SCALE, bool TDL, bool NT, int P>
 __device__ __forceinline__ void single_pair(const BwdArgs& a, const TableDev* s_td, uint4 tk0,
                                             uint4 tk1, bool two, uint32_t lpr,
                                             uint32_t lane_in) {
+  static_assert(P == 1 || P == 2, "one or two runs per step");
   uint4 tk[2] = {tk0, tk1};  // {start, row, table, bag}
-  TableDev td[2];
-  bool ok[2];
-  int64_t row[2], b[2];
+  TableDev td[P];
+  bool ok[P];
+  int64_t row[P], b[P];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < P; ++u) {
     // sanity bounds, never false for lists the preprocessing wrote
     const uint32_t t = tk[u].z < a.T ? tk[u].z : 0u;
     td[u] = get_td<TDL>(a, s_td, t);
@@ -226,35 +227,40 @@ __device__ __forceinline__ void single_pair(const BwdArgs& a, const TableDev* s_
     row[u] = ok[u] ? (int64_t)tk[u].y : 0;
     b[u] = ok[u] ? bb : 0;
   }
-  uint32_t colc[2][NC], cold[2][NC];
-  float w[2][NC][VEC], g[2][NC][VEC], m0[2], sc[2];
+  uint32_t colc[P][NC], cold[P][NC];
+  float w[P][NC][VEC], g[P][NC][VEC], m0[P], sc[P];
+  RawW<WD, VEC> wr[P][NC];  // converted after the barrier
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < P; ++u) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       colc[u][c] = (lane_in + (uint32_t)c * lpr) * VEC;
       cold[u][c] = colc[u][c] < td[u].dim ? colc[u][c] : 0u;
-      load_w<WD, VEC>(td[u].w, row[u] * td[u].dim + cold[u][c], w[u][c]);
+      load_w_raw<WD, VEC, NT>(td[u].w, row[u] * td[u].dim + cold[u][c], wr[u][c]);
       load_f32<VEC>(a.grad + b[u] * (int64_t)a.dtot + td[u].col + cold[u][c], g[u][c]);
     }
-    m0[u] = a.opt == OPT_ROWWISE_ADAGRAD ? td[u].m[row[u]] : 0.f;
+    m0[u] = a.opt == OPT_ROWWISE_ADAGRAD ? gload(td[u].m + row[u]) : 0.f;
     sc[u] = SCALE ? a.sorted_scale[ok[u] ? tk[u].x : 0u] : 1.0f;
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < P; ++u)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) cvt_w<WD, VEC>(wr[u][c], w[u][c]);
+#pragma unroll
+  for (int u = 0; u < P; ++u) {
     if (SCALE)
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int e = 0; e < VEC; ++e) g[u][c][e] *= sc[u];
-    subgroup_row_update<WD, VEC, NC>(a, td[u], row[u], m0[u], w[u], g[u], colc[u], lpr, lane_in,
+    subgroup_row_update<WD, VEC, NC, NT>(a, td[u], row[u], m0[u], w[u], g[u], colc[u], lpr, lane_in,
                                      ok[u] && (u == 0 || two));
   }
 }
 
 // In list order: subgroup sg of the launch takes positions sg, sg + nsg, ...
-template <int WD, int VEC, int NC, bool SCALE, bool TDL>
+template <int WD, int VEC, int NC, bool SCALE, bool TDL, bool NT>
 __global__ __launch_bounds__(kThreads) void bwd_single_kernel(BwdArgs a, BucketSet S) {
   BucketDev bk;
   uint32_t bucket, lb, lg;
@@ -267,17 +273,26 @@ __global__ __launch_bounds__(kThreads) void bwd_single_kernel(BwdArgs a, BucketS
   const uint32_t sg = (lb * kThreads + threadIdx.x) >> bk.lpr_log2;
   const uint32_t beg = list_begin(a, 0, bucket);
   const uint32_t end = min(list_begin(a, 0, bucket + 1), a.max_single);
+  if constexpr (NT) {
+    // Batches whose rows are streamed past the caches: one run per step,
+    // measured faster than pairs there (8.4M lookups: 283 -> 249 us; 134M
+    // lookups: 3117 -> 2917 us).
+    for (uint32_t s = beg + sg; s < end; s += nsg_grid)
+      single_pair<WD, VEC, NC, SCALE, TDL, NT, 1>(a, s_td, a.single_task[s], a.single_task[s],
+                                                  false, lpr, lane_in);
+    return;
+  }
   for (uint32_t s = beg + sg; s < end; s += 2 * nsg_grid) {
     const uint32_t s1 = (s + nsg_grid < end) ? s + nsg_grid : s;
-    single_pair<WD, VEC, NC, SCALE, TDL>(a, s_td, a.single_task[s], a.single_task[s1], s1 != s,
-                                         lpr, lane_in);
+    single_pair<WD, VEC, NC, SCALE, TDL, NT, 2>(a, s_td, a.single_task[s], a.single_task[s1],
+                                                s1 != s, lpr, lane_in);
   }
 }
 
 // ----------------------------------------------------- tiny short runs
 // One subgroup of lpr lanes owns a run with 2 <= SL < 32: gather, Adagrad,
 // plain stores.  The next task record is prefetched.
-template <int WD, int VEC, int NC, bool TDL, int IF>
+template <int WD, int VEC, int NC, bool TDL, int IF, bool NT>
 __global__ __launch_bounds__(kThreads) void bwd_tiny_kernel(BwdArgs a, BucketSet S) {
   BucketDev bk;
   uint32_t bucket, lb, lg;
@@ -307,13 +322,13 @@ __global__ __launch_bounds__(kThreads) void bwd_tiny_kernel(BwdArgs a, BucketSet
     for (int c = 0; c < NC; ++c) {
       colc[c] = (lane_in + (uint32_t)c * lpr) * VEC;
       cold[c] = colc[c] < td.dim ? colc[c] : 0u;
-      load_w<WD, VEC>(td.w, row * td.dim + cold[c], w[c]);
+      load_w<WD, VEC, NT>(td.w, row * td.dim + cold[c], w[c]);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) g[c][e] = 0.f;
     }
-    const float m0 = a.opt == OPT_ROWWISE_ADAGRAD ? td.m[row] : 0.f;
+    const float m0 = a.opt == OPT_ROWWISE_ADAGRAD ? gload(td.m + row) : 0.f;
     gather<VEC, NC, IF>(a, td, (int64_t)t * a.B, start, start + len, 1u, cold, g);
-    subgroup_row_update<WD, VEC, NC>(a, td, row, m0, w, g, colc, lpr, lane_in, true);
+    subgroup_row_update<WD, VEC, NC, NT>(a, td, row, m0, w, g, colc, lpr, lane_in, true);
   }
 }
 
@@ -379,18 +394,18 @@ struct RowPre {
   float w[VEC];
   float m;
 };
-template <int WD, int VEC>
+template <int WD, int VEC, bool NT>
 __device__ __forceinline__ void row_prefetch(const BwdArgs& a, const TableDev& td, int64_t row,
                                              RowPre<VEC>& p) {
   const uint32_t col = threadIdx.x * VEC;
-  if (col < td.dim) load_w<WD, VEC>(td.w, row * td.dim + col, p.w);
-  p.m = a.opt == OPT_ROWWISE_ADAGRAD ? td.m[row] : 0.f;
+  if (col < td.dim) load_w<WD, VEC, NT>(td.w, row * td.dim + col, p.w);
+  p.m = a.opt == OPT_ROWWISE_ADAGRAD ? gload(td.m + row) : 0.f;
 }
 
 // The update of one row from sm.gsum, all threads of the workgroup (the
 // optimizers of subgroup_row_update).  PRE: the row's weights and momentum
 // come from row_prefetch; else they are loaded here.
-template <int WD, int VEC, int NC, bool PRE>
+template <int WD, int VEC, int NC, bool PRE, bool NT>
 __device__ __forceinline__ void wg_row_update(const BwdArgs& a, const TableDev& td, int64_t row,
                                               float sqp, WgSmem<VEC, NC>& sm,
                                               const RowPre<VEC>& pre) {
@@ -403,7 +418,7 @@ __device__ __forceinline__ void wg_row_update(const BwdArgs& a, const TableDev& 
 #pragma unroll
         for (int e = 0; e < VEC; ++e) w[e] = pre.w[e];
       } else {
-        load_w<WD, VEC>(td.w, row * D + col, w);
+        load_w<WD, VEC, NT>(td.w, row * D + col, w);
       }
       if (a.opt == OPT_ADAGRAD) {
         float acc[VEC];
@@ -419,7 +434,7 @@ __device__ __forceinline__ void wg_row_update(const BwdArgs& a, const TableDev& 
 #pragma unroll
         for (int e = 0; e < VEC; ++e) o[e] = w[e] - a.lr * sm.gsum[col + e];
       }
-      store_w<WD, VEC>(td.w, row * D + col, o);
+      store_w<WD, VEC, NT>(td.w, row * D + col, o);
     }
     __syncthreads();  // every thread has read sm before it changes
     if (threadIdx.x == 0 && a.debug_count)
@@ -431,7 +446,7 @@ __device__ __forceinline__ void wg_row_update(const BwdArgs& a, const TableDev& 
   if (lane_id() == 0) sm.wsq[threadIdx.x / kWave] = sqp;
   __syncthreads();
   const float sq = ((sm.wsq[0] + sm.wsq[1]) + sm.wsq[2]) + sm.wsq[3];
-  const float m = (PRE ? pre.m : td.m[row]) + sq / (float)D;
+  const float m = (PRE ? pre.m : gload(td.m + row)) + sq / (float)D;
   const float den = sqrtf(m) + a.eps;
   for (uint32_t col = threadIdx.x * VEC; col < D; col += kThreads * VEC) {
     float w[VEC], o[VEC];
@@ -439,15 +454,15 @@ __device__ __forceinline__ void wg_row_update(const BwdArgs& a, const TableDev& 
 #pragma unroll
       for (int e = 0; e < VEC; ++e) w[e] = pre.w[e];
     } else {
-      load_w<WD, VEC>(td.w, row * D + col, w);
+      load_w<WD, VEC, NT>(td.w, row * D + col, w);
     }
 #pragma unroll
     for (int e = 0; e < VEC; ++e) o[e] = w[e] - (a.lr * sm.gsum[col + e]) / den;
-    store_w<WD, VEC>(td.w, row * D + col, o);
+    store_w<WD, VEC, NT>(td.w, row * D + col, o);
   }
   __syncthreads();  // every thread has read td.m[row] and sm before they change
   if (threadIdx.x == 0) {
-    td.m[row] = m;
+    gstore(td.m + row, m);
     if (a.debug_count) atomicAdd(&a.debug_count[td.key_base + (uint32_t)row], 1u);
   }
 }
@@ -456,7 +471,7 @@ __device__ __forceinline__ void wg_row_update(const BwdArgs& a, const TableDev& 
 // COH: the partials were written by workgroups of other XCDs during this
 // kernel, so they are read with agent-scope atomic loads, which bypass this
 // XCD's L2 (the two-launch update reads them after a kernel boundary).
-template <int WD, int VEC, int NC, bool COH>
+template <int WD, int VEC, int NC, bool COH, bool NT>
 __device__ __forceinline__ void long_update(const BwdArgs& a, const BucketDev& bk, uint32_t l,
                                             WgSmem<VEC, NC>& sm) {
   const uint32_t lpr = bk.lpr, lane_in = threadIdx.x & (lpr - 1);
@@ -501,7 +516,7 @@ __device__ __forceinline__ void long_update(const BwdArgs& a, const BucketDev& b
   // the row is loaded by the update itself: loaded before the partials, it
   // cost the kernel a wave per SIMD (C5 150 -> 169 us)
   RowPre<VEC> unused;
-  wg_row_update<WD, VEC, NC, false>(a, td, (int64_t)task.z, sqp, sm, unused);
+  wg_row_update<WD, VEC, NC, false, NT>(a, td, (int64_t)task.z, sqp, sm, unused);
 }
 
 // Write the combined chunk partial (ascending subgroup order) to partial[c];
@@ -525,8 +540,11 @@ __device__ __forceinline__ void chunk_store(const BwdArgs& a, const BucketDev& b
 // ------------------------------------------------------- medium short runs
 // One workgroup owns a run with 32 <= SL < 256: its subgroups split the
 // lookups, the workgroup combines them in LDS and updates the row.
-template <int WD, int VEC, int NC>
-__global__ __launch_bounds__(kThreads) void bwd_medium_kernel(BwdArgs a, BucketSet S) {
+// Five waves per SIMD: the compiler's own choice for 16-bit rows is 99 VGPRs,
+// four waves; at five, f16 rows fit without spills (bf16 spills two).
+template <int WD, int VEC, int NC, bool NT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NC == 1 ? 5 : 1)))
+void bwd_medium_kernel(BwdArgs a, BucketSet S) {
   BucketDev bk;
   uint32_t bucket, lb, lg;
   set_pick(S, bk, bucket, lb, lg);
@@ -538,10 +556,10 @@ __global__ __launch_bounds__(kThreads) void bwd_medium_kernel(BwdArgs a, BucketS
     if (!span_ok(a, task.x, task.y, task.w, task.z)) continue;  // uniform; never for valid lists
     const TableDev td = a.tables[task.w];
     RowPre<VEC> pre;
-    row_prefetch<WD, VEC>(a, td, (int64_t)task.z, pre);
+    row_prefetch<WD, VEC, NT>(a, td, (int64_t)task.z, pre);
     wg_gather<VEC, NC, kInFlightShallow>(a, bk, td, task.w, task.x, task.x + task.y, sm);
     const float sqp = red_to_gsum<VEC, NC>(bk, td.dim, sm);
-    wg_row_update<WD, VEC, NC, true>(a, td, (int64_t)task.z, sqp, sm, pre);
+    wg_row_update<WD, VEC, NC, true, NT>(a, td, (int64_t)task.z, sqp, sm, pre);
   }
 }
 
@@ -654,7 +672,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a, BucketSe
   }
 }
 
-template <int WD, int VEC, int NC>
+template <int WD, int VEC, int NC, bool NT>
 __global__ __launch_bounds__(kThreads) void bwd_long_update_kernel(BwdArgs a, BucketSet S) {
   BucketDev bk;
   uint32_t bucket, lb, lg;
@@ -664,7 +682,7 @@ __global__ __launch_bounds__(kThreads) void bwd_long_update_kernel(BwdArgs a, Bu
   const uint32_t end = min(list_begin(a, 3, bucket + 1), a.max_long);
   for (uint32_t l = beg + lb; l < end; l += lg) {
     if (!long_ok(a, l)) continue;  // uniform per workgroup; never for valid lists
-    long_update<WD, VEC, NC, false>(a, bk, l, sm);
+    long_update<WD, VEC, NC, false, NT>(a, bk, l, sm);
   }
 }
 
@@ -681,7 +699,7 @@ __global__ __launch_bounds__(kThreads) void bwd_long_update_kernel(BwdArgs a, Bu
 // atomic loads (read from the coherent level, not from a stale cache).  This
 // is the release/acquire pair without the whole-cache operations, which only
 // serve to publish ordinary cached stores; none is published here.
-template <int WD, int VEC, int NC, int IF>
+template <int WD, int VEC, int NC, int IF, bool NT>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_fused_kernel(BwdArgs a, BucketSet S) {
   BucketDev bk;
   uint32_t bucket, lb, lg;
@@ -708,7 +726,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_fused_kernel(BwdArgs a, Bu
     }
     __syncthreads();
     if (sm.last) {
-      long_update<WD, VEC, NC, true>(a, bk, task.w, sm);
+      long_update<WD, VEC, NC, true, NT>(a, bk, task.w, sm);
       if (threadIdx.x == 0) {
         const uint32_t len = a.long_task[task.w].y;
         __hip_atomic_store(&a.remaining[task.w], (len + kChunk - 1) / kChunk, __ATOMIC_RELAXED,
@@ -768,70 +786,81 @@ constexpr uint32_t kBwdDeepLookups = 64u << 20;
 // 17 M: 286 at 1, 431 at 0.5).  The other run classes lose with any cap.
 constexpr uint32_t kSingleDeepGridDiv = 2;
 
-template <int WD, int VEC, int NC, bool TDL, int IF>
+template <int WD, int VEC, int NC, bool TDL, int IF, bool NT>
 void launch_small(const BwdArgs& a, BucketSet S, const BwdGrids* g, int cus, hipStream_t s) {
   const uint32_t div = IF == kInFlightDeep ? kSingleDeepGridDiv : 1u;
   if (a.sorted_scale) {
-    static const uint32_t cap = resident(bwd_single_kernel<WD, VEC, NC, true, TDL>, cus);
+    static const uint32_t cap = resident(bwd_single_kernel<WD, VEC, NC, true, TDL, NT>, cus);
     const uint32_t grid = set_grid(S, g, &BwdGrids::single, cap / div);
-    TBE_LAUNCH("bwd_single", (bwd_single_kernel<WD, VEC, NC, true, TDL>), dim3(grid),
+    TBE_LAUNCH("bwd_single", (bwd_single_kernel<WD, VEC, NC, true, TDL, NT>), dim3(grid),
                dim3(kThreads), s, a, S);
   } else {
-    static const uint32_t cap = resident(bwd_single_kernel<WD, VEC, NC, false, TDL>, cus);
+    static const uint32_t cap = resident(bwd_single_kernel<WD, VEC, NC, false, TDL, NT>, cus);
     const uint32_t grid = set_grid(S, g, &BwdGrids::single, cap / div);
-    TBE_LAUNCH("bwd_single", (bwd_single_kernel<WD, VEC, NC, false, TDL>), dim3(grid),
+    TBE_LAUNCH("bwd_single", (bwd_single_kernel<WD, VEC, NC, false, TDL, NT>), dim3(grid),
                dim3(kThreads), s, a, S);
   }
-  static const uint32_t cap_t = resident(bwd_tiny_kernel<WD, VEC, NC, TDL, IF>, cus);
+  static const uint32_t cap_t = resident(bwd_tiny_kernel<WD, VEC, NC, TDL, IF, NT>, cus);
   const uint32_t grid = set_grid(S, g, &BwdGrids::tiny, cap_t);
-  TBE_LAUNCH("bwd_tiny", (bwd_tiny_kernel<WD, VEC, NC, TDL, IF>), dim3(grid), dim3(kThreads), s,
-             a, S);
+  TBE_LAUNCH("bwd_tiny", (bwd_tiny_kernel<WD, VEC, NC, TDL, IF, NT>), dim3(grid), dim3(kThreads),
+             s, a, S);
 }
 
-template <int WD, int VEC, int NC, int IF>
+template <int WD, int VEC, int NC, int IF, bool NT>
 void launch_long(const BwdArgs& a, BucketSet S, const BwdGrids* g, bool fused, int cus,
                  hipStream_t s) {
   uint32_t grid;
   if (fused) {
-    static const uint32_t cap_f = resident(bwd_chunk_fused_kernel<WD, VEC, NC, IF>, cus);
+    static const uint32_t cap_f = resident(bwd_chunk_fused_kernel<WD, VEC, NC, IF, NT>, cus);
     grid = set_grid(S, g, &BwdGrids::chunk, cap_f, 8);
-    TBE_LAUNCH("bwd_chunk_fused", (bwd_chunk_fused_kernel<WD, VEC, NC, IF>), dim3(grid),
+    TBE_LAUNCH("bwd_chunk_fused", (bwd_chunk_fused_kernel<WD, VEC, NC, IF, NT>), dim3(grid),
                dim3(kThreads), s, a, S);
   } else {
     static const uint32_t cap_c = resident(bwd_chunk_kernel<WD, VEC, NC, IF>, cus);
     grid = set_grid(S, g, &BwdGrids::chunk, cap_c, 8);
     TBE_LAUNCH("bwd_chunk", (bwd_chunk_kernel<WD, VEC, NC, IF>), dim3(grid), dim3(kThreads), s,
                a, S);
-    static const uint32_t cap_l = resident(bwd_long_update_kernel<WD, VEC, NC>, cus);
+    static const uint32_t cap_l = resident(bwd_long_update_kernel<WD, VEC, NC, NT>, cus);
     grid = set_grid(S, g, &BwdGrids::longrun, cap_l);
-    TBE_LAUNCH("bwd_long_update", (bwd_long_update_kernel<WD, VEC, NC>), dim3(grid),
+    TBE_LAUNCH("bwd_long_update", (bwd_long_update_kernel<WD, VEC, NC, NT>), dim3(grid),
                dim3(kThreads), s, a, S);
   }
 }
 
+template <int WD, int VEC, int NC, int IF, bool NT>
+void launch_classes(const BwdArgs& a, BucketSet S, const BwdGrids* g, bool fused, int cus,
+                    const hipStream_t* ss) {
+  if (a.T <= (uint32_t)kTdCache)
+    launch_small<WD, VEC, NC, true, IF, NT>(a, S, g, cus, ss[0]);
+  else
+    launch_small<WD, VEC, NC, false, IF, NT>(a, S, g, cus, ss[0]);
+  static const uint32_t cap_m = resident(bwd_medium_kernel<WD, VEC, NC, NT>, cus);
+  const uint32_t grid = set_grid(S, g, &BwdGrids::medium, cap_m);
+  TBE_LAUNCH("bwd_medium", (bwd_medium_kernel<WD, VEC, NC, NT>), dim3(grid), dim3(kThreads),
+             ss[1], a, S);
+  launch_long<WD, VEC, NC, IF, NT>(a, S, g, fused, cus, ss[2]);
+}
+
+// Weight rows of the backward read and rewritten with non-temporal accesses
+// from this many lookups on: each touched row is read and written once per
+// step, and as ordinary accesses those lines push the grad_out rows that the
+// gathers reuse out of the caches.  Measured on MI355X (ms per step, plain /
+// non-temporal): 138 M lookups 17.01 / 16.52 (single-lookup runs 3288 ->
+// 2842 us), 17 M 2.204 / 2.176, but 2.1 M 0.338 / 0.339: there the next
+// forward re-reads the hot rows the backward wrote (forward 36.5 -> 42.3 us),
+// which non-temporal stores leave out of the caches.
+constexpr uint32_t kBwdStreamRowsLookups = 8u << 20;
+
 template <int WD, int VEC, int NC>
 hipError_t launch(const BwdArgs& a, BucketSet S, const BwdGrids* g, bool fused, int cus,
                   const hipStream_t* ss) {
-  const bool deep = a.N >= kBwdDeepLookups;
-  if (a.T <= (uint32_t)kTdCache) {
-    if (deep)
-      launch_small<WD, VEC, NC, true, kInFlightDeep>(a, S, g, cus, ss[0]);
-    else
-      launch_small<WD, VEC, NC, true, kInFlightShallow>(a, S, g, cus, ss[0]);
-  } else {
-    if (deep)
-      launch_small<WD, VEC, NC, false, kInFlightDeep>(a, S, g, cus, ss[0]);
-    else
-      launch_small<WD, VEC, NC, false, kInFlightShallow>(a, S, g, cus, ss[0]);
-  }
-  static const uint32_t cap_m = resident(bwd_medium_kernel<WD, VEC, NC>, cus);
-  const uint32_t grid = set_grid(S, g, &BwdGrids::medium, cap_m);
-  TBE_LAUNCH("bwd_medium", (bwd_medium_kernel<WD, VEC, NC>), dim3(grid), dim3(kThreads), ss[1],
-             a, S);
-  if (deep)
-    launch_long<WD, VEC, NC, kInFlightDeep>(a, S, g, fused, cus, ss[2]);
+  static_assert(kBwdDeepLookups >= kBwdStreamRowsLookups, "deep batches stream their rows");
+  if (a.N >= kBwdDeepLookups)
+    launch_classes<WD, VEC, NC, kInFlightDeep, true>(a, S, g, fused, cus, ss);
+  else if (a.N >= kBwdStreamRowsLookups)
+    launch_classes<WD, VEC, NC, kInFlightShallow, true>(a, S, g, fused, cus, ss);
   else
-    launch_long<WD, VEC, NC, kInFlightShallow>(a, S, g, fused, cus, ss[2]);
+    launch_classes<WD, VEC, NC, kInFlightShallow, false>(a, S, g, fused, cus, ss);
   return hipGetLastError();
 }
 

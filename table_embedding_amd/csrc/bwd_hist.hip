@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void bwd_hist_update_kernel(HistArgs h) {
   __syncthreads();
   if (!touched) return;  // untouched rows are not written
   const TableDev td = h.table;
-  const float m = td.m[e] + (((wsq[0] + wsq[1]) + wsq[2]) + wsq[3]) / (float)D;
+  const float m = gload(td.m + e) + (((wsq[0] + wsq[1]) + wsq[2]) + wsq[3]) / (float)D;
   const float den = sqrtf(m) + h.eps;
   if (threadIdx.x < D) {
     const int64_t idx = (int64_t)e * D + threadIdx.x;
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void bwd_hist_update_kernel(HistArgs h) {
   }
   __syncthreads();  // every thread has read td.m[e] before it changes
   if (threadIdx.x == 0) {
-    td.m[e] = m;
+    gstore(td.m + e, m);
     if (h.debug_count) atomicAdd(&h.debug_count[td.key_base + e], 1u);
   }
 }

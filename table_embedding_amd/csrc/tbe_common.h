@@ -155,21 +155,58 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Load VEC consecutive weights starting at element e of a row-major table.
-template <int WD, int VEC>
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16 or 8 bytes at p, as words; NT: a non-temporal (streaming) access, which
+// the caches keep with low priority (for rows read and rewritten once, so that
+// they do not push out data that is reused).  A compile-time choice: with a
+// run-time one the compiler merges the two loads of one address and drops the
+// hint.
+// (the pointer is cast to the global address space: a generic pointer would
+// give a flat access, which waits on two counters)
+typedef __attribute__((address_space(1))) u32x4_t g_u32x4_t;
+typedef __attribute__((address_space(1))) u32x2_t g_u32x2_t;
+template <bool NT>
+__device__ __forceinline__ u32x4_t ld16(const void* p) {
+  const g_u32x4_t* q = (const g_u32x4_t*)p;
+  if constexpr (NT) return __builtin_nontemporal_load(q); else return *q;
+}
+template <bool NT>
+__device__ __forceinline__ u32x2_t ld8(const void* p) {
+  const g_u32x2_t* q = (const g_u32x2_t*)p;
+  if constexpr (NT) return __builtin_nontemporal_load(q); else return *q;
+}
+template <bool NT>
+__device__ __forceinline__ void st16(void* p, u32x4_t x) {
+  g_u32x4_t* q = (g_u32x4_t*)p;
+  if constexpr (NT) __builtin_nontemporal_store(x, q); else *q = x;
+}
+template <bool NT>
+__device__ __forceinline__ void st8(void* p, u32x2_t x) {
+  g_u32x2_t* q = (g_u32x2_t*)p;
+  if constexpr (NT) __builtin_nontemporal_store(x, q); else *q = x;
+}
+
+// Load VEC consecutive weights starting at element e of a row-major table
+// (NT: see ld16).
+template <int WD, int VEC, bool NT = false>
 __device__ __forceinline__ void load_w(const void* w, int64_t e, float* v) {
   if constexpr (WD == WD_F32) {
     static_assert(VEC == 4, "f32 rows are read 4 at a time");
-    float4 x = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(w) + e);
-    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    const u32x4_t x = ld16<NT>(reinterpret_cast<const float*>(w) + e);
+    // components to scalars first (see load_w_buf)
+    const uint32_t c[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __builtin_bit_cast(float, c[i]);
   } else {
     const uint16_t* p = reinterpret_cast<const uint16_t*>(w) + e;
     uint32_t words[VEC / 2];
     if constexpr (VEC == 8) {
-      uint4 x = *reinterpret_cast<const uint4*>(p);
+      const u32x4_t x = ld16<NT>(p);
       words[0] = x.x; words[1] = x.y; words[2] = x.z; words[3] = x.w;
     } else {
-      uint2 x = *reinterpret_cast<const uint2*>(p);
+      const u32x2_t x = ld8<NT>(p);
       words[0] = x.x; words[1] = x.y;
     }
 #pragma unroll
@@ -191,8 +228,6 @@ __device__ __forceinline__ void load_w(const void* w, int64_t e, float* v) {
 // or past `bytes` returns zeros instead of faulting.  The descriptor's fourth
 // dword for a raw gfx9 buffer selects the 32-bit data format.
 constexpr int kBufDword3 = 0x00020000;
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            kBufDword3);
@@ -233,11 +268,57 @@ __device__ __forceinline__ void load_w_buf(__amdgpu_buffer_rsrc_t r, uint32_t by
   }
 }
 
-// Store VEC floats, rounded to the storage type, at element e.
+// load_w in two steps: the raw words of VEC weights (VEC for float32 rows,
+// VEC / 2 for 16-bit ones), then their conversion to float.  A caller that
+// keeps loads in flight behind a scheduling barrier converts after it, so
+// that no conversion makes the wave wait for its load before the barrier.
 template <int WD, int VEC>
+struct RawW {
+  uint32_t u[WD == WD_F32 ? VEC : VEC / 2];
+};
+template <int WD, int VEC, bool NT = false>
+__device__ __forceinline__ void load_w_raw(const void* w, int64_t e, RawW<WD, VEC>& r) {
+  if constexpr (WD == WD_F32) {
+    static_assert(VEC == 4, "f32 rows are read 4 at a time");
+    const u32x4_t x = ld16<NT>(reinterpret_cast<const float*>(w) + e);
+    r.u[0] = x.x; r.u[1] = x.y; r.u[2] = x.z; r.u[3] = x.w;
+  } else {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(w) + e;
+    if constexpr (VEC == 8) {
+      const u32x4_t x = ld16<NT>(p);
+      r.u[0] = x.x; r.u[1] = x.y; r.u[2] = x.z; r.u[3] = x.w;
+    } else {
+      const u32x2_t x = ld8<NT>(p);
+      r.u[0] = x.x; r.u[1] = x.y;
+    }
+  }
+}
+template <int WD, int VEC>
+__device__ __forceinline__ void cvt_w(const RawW<WD, VEC>& r, float* v) {
+  if constexpr (WD == WD_F32) {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) v[i] = __builtin_bit_cast(float, r.u[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < VEC / 2; ++i) {
+      if constexpr (WD == WD_F16) {
+        v[2 * i] = f16_bits_to_float(r.u[i] & 0xffffu);
+        v[2 * i + 1] = f16_bits_to_float(r.u[i] >> 16);
+      } else {
+        v[2 * i] = bf16_bits_to_float(r.u[i] & 0xffffu);
+        v[2 * i + 1] = bf16_bits_to_float(r.u[i] >> 16);
+      }
+    }
+  }
+}
+
+// Store VEC floats, rounded to the storage type, at element e (NT: see ld16).
+template <int WD, int VEC, bool NT = false>
 __device__ __forceinline__ void store_w(void* w, int64_t e, const float* v) {
   if constexpr (WD == WD_F32) {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(w) + e) = make_float4(v[0], v[1], v[2], v[3]);
+    const u32x4_t x = {__builtin_bit_cast(uint32_t, v[0]), __builtin_bit_cast(uint32_t, v[1]),
+                       __builtin_bit_cast(uint32_t, v[2]), __builtin_bit_cast(uint32_t, v[3])};
+    st16<NT>(reinterpret_cast<float*>(w) + e, x);
   } else {
     uint32_t words[VEC / 2];
 #pragma unroll
@@ -254,25 +335,39 @@ __device__ __forceinline__ void store_w(void* w, int64_t e, const float* v) {
     }
     uint16_t* p = reinterpret_cast<uint16_t*>(w) + e;
     if constexpr (VEC == 8)
-      *reinterpret_cast<uint4*>(p) = make_uint4(words[0], words[1], words[2], words[3]);
+      st16<NT>(p, (u32x4_t){words[0], words[1], words[2], words[3]});
     else
-      *reinterpret_cast<uint2*>(p) = make_uint2(words[0], words[1]);
+      st8<NT>(p, (u32x2_t){words[0], words[1]});
   }
 }
 
+// Float rows and scalars in device (global) memory: every pointer these take
+// points into global memory, and saying so keeps pointers that come out of
+// table descriptors (momentum, optimizer state) from becoming flat accesses.
 template <int VEC>
 __device__ __forceinline__ void load_f32(const float* p, float* v) {
 #pragma unroll
   for (int i = 0; i < VEC; i += 4) {
-    float4 x = *reinterpret_cast<const float4*>(p + i);
-    v[i] = x.x; v[i + 1] = x.y; v[i + 2] = x.z; v[i + 3] = x.w;
+    const u32x4_t x = ld16<false>(p + i);
+    const uint32_t c[4] = {x.x, x.y, x.z, x.w};  // components to scalars first
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[i + e] = __builtin_bit_cast(float, c[e]);
   }
 }
 template <int VEC>
 __device__ __forceinline__ void store_f32(float* p, const float* v) {
 #pragma unroll
   for (int i = 0; i < VEC; i += 4)
-    *reinterpret_cast<float4*>(p + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+    st16<false>(p + i, (u32x4_t){__builtin_bit_cast(uint32_t, v[i]),
+                                 __builtin_bit_cast(uint32_t, v[i + 1]),
+                                 __builtin_bit_cast(uint32_t, v[i + 2]),
+                                 __builtin_bit_cast(uint32_t, v[i + 3])});
+}
+__device__ __forceinline__ float gload(const float* p) {
+  return *(const __attribute__((address_space(1))) float*)p;
+}
+__device__ __forceinline__ void gstore(float* p, float v) {
+  *(__attribute__((address_space(1))) float*)p = v;
 }
 
 __device__ __forceinline__ int64_t load_idx(const void* a, int itype, int64_t i) {
