@@ -282,8 +282,10 @@ int tbe_validate(const tbe_plan* plan, int64_t B, int32_t itype, void* indices, 
                  int64_t num_lookups, uint32_t* err, uint32_t flags, void* stream);
 
 /* Kernel timing for benchmarks and tools, off by default.  While enabled,
- * every kernel launch of the library is bracketed by two HIP events recorded
- * on the stream it is launched on (adds a little enqueue work per launch).
+ * every kernel launch of the library carries a start and a stop HIP event
+ * bound to the dispatch itself (hipExtLaunchKernel): their difference is the
+ * kernel's execution from its dispatch's begin to its end timestamp, the span
+ * a kernel trace reports.  Not for use under stream capture.
  * tbe_prof_read waits for the recorded events, writes per-kernel-family
  * totals (name, launches, summed milliseconds) for up to max_kernels
  * families, sets *count to the number of families seen, and clears the
@@ -294,9 +296,9 @@ int tbe_prof_enable(int enable);
 int tbe_prof_read(int32_t max_kernels, char* names, int64_t* launches, double* total_ms,
                   int32_t* count);
 /* Enqueue `launches` empty kernels (one 64-thread workgroup each) on stream,
- * bracketed like every library launch while timing is enabled, under the
- * family name "empty": their average is the cost of the bracket itself
- * (dispatch latency included), to subtract from the other families'. */
+ * timed like every library launch while timing is enabled, under the family
+ * name "empty": their average is the per-launch floor of a kernel that does
+ * nothing. */
 int tbe_prof_calibrate(int32_t launches, void* stream);
 
 /* Static text for a status code. */

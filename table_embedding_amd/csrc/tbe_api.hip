@@ -275,19 +275,15 @@ hipEvent_t prof_event() {
 
 namespace tbe {
 
-void prof_begin(hipStream_t s, const char* name) {
-  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+bool prof_events(const char* name, hipEvent_t* start, hipEvent_t* stop) {
+  if (!g_prof_on.load(std::memory_order_relaxed)) return false;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   ProfRec r{name, prof_event(), prof_event()};
-  if (!r.start || !r.stop) return;
-  (void)hipEventRecord(r.start, s);
+  if (!r.start || !r.stop) return false;
   g_prof_recs.push_back(r);
-}
-
-void prof_end(hipStream_t s) {
-  if (!g_prof_on.load(std::memory_order_relaxed)) return;
-  std::lock_guard<std::mutex> lk(g_prof_mu);
-  if (!g_prof_recs.empty()) (void)hipEventRecord(g_prof_recs.back().stop, s);
+  *start = r.start;
+  *stop = r.stop;
+  return true;
 }
 
 }  // namespace tbe

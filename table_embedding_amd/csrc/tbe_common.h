@@ -4,6 +4,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -392,24 +393,23 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // ------------------------------------------------------------ host launchers
 
-// Optional per-kernel timing (tbe_prof_enable): when on, every launch is
-// bracketed by two HIP events recorded on the launch stream.
-void prof_begin(hipStream_t s, const char* name);
-void prof_end(hipStream_t s);
+// Optional per-kernel timing (tbe_prof_enable): when on, prof_events hands
+// out a start/stop event pair and the launch goes through
+// hipExtLaunchKernelGGL, which ties the two events to the dispatch's own
+// begin and end timestamps (no events enqueued around it).
+bool prof_events(const char* name, hipEvent_t* start, hipEvent_t* stop);
 
-#define TBE_LAUNCH(name, kernel, grid, block, stream, ...)                   \
-  do {                                                                       \
-    ::tbe::prof_begin((stream), (name));                                     \
-    hipLaunchKernelGGL(kernel, (grid), (block), 0, (stream), __VA_ARGS__);   \
-    ::tbe::prof_end((stream));                                               \
+#define TBE_LAUNCH_SHM(name, kernel, grid, block, shm, stream, ...)                        \
+  do {                                                                                     \
+    hipEvent_t tbe_prof_e0_ = nullptr, tbe_prof_e1_ = nullptr;                             \
+    if (::tbe::prof_events((name), &tbe_prof_e0_, &tbe_prof_e1_))                          \
+      hipExtLaunchKernelGGL(kernel, (grid), (block), (shm), (stream), tbe_prof_e0_,        \
+                            tbe_prof_e1_, 0u, ##__VA_ARGS__);                              \
+    else                                                                                   \
+      hipLaunchKernelGGL(kernel, (grid), (block), (shm), (stream), ##__VA_ARGS__);         \
   } while (0)
-// The same with `shm` bytes of dynamic LDS.
-#define TBE_LAUNCH_SHM(name, kernel, grid, block, shm, stream, ...)            \
-  do {                                                                       \
-    ::tbe::prof_begin((stream), (name));                                     \
-    hipLaunchKernelGGL(kernel, (grid), (block), (shm), (stream), __VA_ARGS__); \
-    ::tbe::prof_end((stream));                                               \
-  } while (0)
+#define TBE_LAUNCH(name, kernel, grid, block, stream, ...) \
+  TBE_LAUNCH_SHM(name, kernel, grid, block, 0u, stream, ##__VA_ARGS__)
 
 // Forward: bags per wave.  A wave owns this many consecutive bags of one
 // table and splits them among its 64/lpr lane subgroups into contiguous runs
