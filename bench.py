@@ -122,7 +122,13 @@ def byte_model(spec, st, hist_path):
     ntiles = -(-N // 4096)
     # radix passes sort the rows of each table's segment: bits of the largest table
     row_bits = max(int(np.ceil(np.log2(r))) if r > 1 else 0 for r in spec.rows)
-    npass = max(1, -(-row_bits // 8))
+    # the fewest passes of at most 10-bit digits, then the narrower digit of
+    # 8 or 10 bits covering the rows in that many passes (as the library)
+    bits = max(1, row_bits)
+    w = -(-bits // -(-bits // 10))
+    digit_bits = 8 if w <= 8 else 10
+    npass = -(-bits // digit_bits)
+    R = 1 << digit_bits
     stiles = sum(-(-s["n"] // 4096) for s in st)  # sort tiles: one table per tile
     out_bytes = B * spec.dtot * 4
     G_bytes = B * spec.dtot * 4
@@ -147,9 +153,9 @@ def byte_model(spec, st, hist_path):
     # per pass: the keys read once for the digit counts (the first pass also
     # clears the status words); the counts scanned in place; the records read
     # and written once by the scatter, plus each tile's 256 prefixes
-    comp["radix_upsweep"] = npass * (4 * N + 256 * 4 * stiles) + 8 * st_words
-    comp["radix_scan"] = npass * 2 * 256 * 4 * stiles
-    comp["radix_downsweep"] = npass * (2 * rec * N + 256 * 4 * stiles)
+    comp["radix_upsweep"] = npass * (4 * N + R * 4 * stiles) + 8 * st_words
+    comp["radix_scan"] = npass * 2 * R * 4 * stiles
+    comp["radix_downsweep"] = npass * (2 * rec * N + R * 4 * stiles)
     comp["rle"] = 4 * N + 8 * U + 4 + 16 * nrle
     comp["classify"] = (8 * U + 4 + 4 * n["single"] + 16 * (U + n_chunks) + 8 * n["long"]
                         + 16 * 8 * ncls)

@@ -24,7 +24,8 @@
 //   transpose      key = key_base[t] + I[p], bag = j and, with per-sample
 //                  weights or a mean table, scale = S[p]*(1/L), written at
 //                  the lookup's slot in its table's segment
-//   then per 8-bit digit, least significant first:
+//   then per digit of 8 or 10 bits (the fewest passes of at most 10 bits
+//   that cover the row range), least significant first:
 //   radix_upsweep  per tile, the count of each value of the digit of
 //                  (key - key_base) in the pass's input; the first one also
 //                  clears the look-back status words of rle and classify
@@ -379,10 +380,12 @@ __device__ __forceinline__ uint32_t xcd_tile() {
 }
 
 // Counts of each digit value of one pass for every tile of the pass's input,
-// digit-major: cnt[d * ntiles + tile], digits of the row (key - key_base).
-// A wave whose 64 keys share one digit (a tile inside a hot row's run) adds
-// them in one step instead of 64 conflicting LDS atomics.  With nst > 0 the
-// kernel also clears nst look-back status words of the later kernels.
+// digit-major: cnt[d * ntiles + tile], digits of DB bits of the row
+// (key - key_base).  A wave whose 64 keys share one digit (a tile inside a
+// hot row's run) adds them in one step instead of 64 conflicting LDS
+// atomics.  With nst > 0 the kernel also clears nst look-back status words of
+// the later kernels.
+template <int DB>
 __global__ __launch_bounds__(kThreads) void radix_upsweep(const uint32_t* __restrict__ keys,
                                                           const uint4* __restrict__ seg,
                                                           const uint32_t* __restrict__ tile_seg,
@@ -391,11 +394,12 @@ __global__ __launch_bounds__(kThreads) void radix_upsweep(const uint32_t* __rest
                                                           uint32_t* __restrict__ cnt,
                                                           uint32_t ntiles,
                                                           uint64_t* __restrict__ st, uint64_t nst) {
-  __shared__ uint32_t h[kThreads / kWave][256];
+  constexpr uint32_t R = 1u << DB;
+  __shared__ uint32_t h[kThreads / kWave][R];
   const uint32_t wave = threadIdx.x / kWave, lane = lane_id();
   const uint32_t tile = xcd_tile();
   const bool live = tile < ctl[kCtlTiles];
-  for (uint32_t i = threadIdx.x; i < (uint32_t)(4 * 256); i += kThreads) (&h[0][0])[i] = 0u;
+  for (uint32_t i = threadIdx.x; i < 4u * R; i += kThreads) (&h[0][0])[i] = 0u;
   __syncthreads();
   if (live) {
     uint32_t sid, b, e;
@@ -410,7 +414,7 @@ __global__ __launch_bounds__(kThreads) void radix_upsweep(const uint32_t* __rest
 #pragma unroll
     for (int r = 0; r < kItems; ++r) {
       const bool valid = wb + (uint32_t)r * kWave + lane < e;
-      const uint32_t d = ((k[r] - sg.w) >> shift) & 255u;
+      const uint32_t d = ((k[r] - sg.w) >> shift) & (R - 1u);
       const uint32_t d0 = __builtin_amdgcn_readfirstlane(d);
       const uint64_t in = __ballot(valid);
       if (__ballot(valid && d != d0) == 0) {
@@ -421,25 +425,32 @@ __global__ __launch_bounds__(kThreads) void radix_upsweep(const uint32_t* __rest
     }
   }
   __syncthreads();
-  if (live) {
-    const uint32_t d = threadIdx.x;
-    cnt[(size_t)d * ntiles + tile] = h[0][d] + h[1][d] + h[2][d] + h[3][d];
-  }
+  if (live)
+    for (uint32_t d = threadIdx.x; d < R; d += kThreads)
+      cnt[(size_t)d * ntiles + tile] = h[0][d] + h[1][d] + h[2][d] + h[3][d];
   const uint64_t stride = (uint64_t)gridDim.x * kThreads;
   for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < nst; i += stride)
     st[i] = 0ull;
 }
 
 // One workgroup per digit value d: the exclusive prefix over all tiles of the
-// counts of d (in place) and the total of d.  At a segment's first tile the
-// prefix is the count of d in all earlier segments.
-__global__ __launch_bounds__(kThreads) void radix_scan(uint32_t* __restrict__ cnt, uint32_t ntiles,
+// counts of d, written tile-major (tex[tile * 2^DB + d], so that a tile's
+// prefixes of every digit are one contiguous vector for the scatter), and the
+// total of d.  At a segment's first tile the prefix is the count of d in all
+// earlier segments.  Digits are taken XCD-major (workgroup i runs on XCD
+// i mod 8; XCD x takes the x-th eighth of the digits), so the prefixes of
+// neighbouring digits, which share cache lines, are written from one L2.
+template <int DB>
+__global__ __launch_bounds__(kThreads) void radix_scan(const uint32_t* __restrict__ cnt,
+                                                       uint32_t ntiles,
                                                        const uint32_t* __restrict__ ctl,
+                                                       uint32_t* __restrict__ tex,
                                                        uint32_t* __restrict__ totals) {
+  constexpr uint32_t R = 1u << DB;
   __shared__ uint32_t sh4[4];
-  const uint32_t d = blockIdx.x;
+  const uint32_t d = (blockIdx.x & 7u) * (R / 8u) + (blockIdx.x >> 3);
   const uint32_t nt = ctl[kCtlTiles];
-  uint32_t* row = cnt + (size_t)d * ntiles;
+  const uint32_t* row = cnt + (size_t)d * ntiles;
   uint32_t running = 0;
   for (uint32_t c = 0; c < nt; c += kThreads * 4) {
     uint32_t v[4], sum = 0;
@@ -454,14 +465,13 @@ __global__ __launch_bounds__(kThreads) void radix_scan(uint32_t* __restrict__ cn
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t i = c + threadIdx.x * 4 + e;
-      if (i < nt) row[i] = x;
+      if (i < nt) tex[(size_t)i * R + d] = x;
       x += v[e];
     }
     running += total;
   }
   if (threadIdx.x == 0) totals[d] = running;
 }
-
 
 struct SortPass {
   const uint32_t* kin;
@@ -474,8 +484,8 @@ struct SortPass {
   const uint4* seg;           // per segment {lookups, output base, first tile, key base}
   const uint32_t* tile_seg;   // segment of each tile
   const uint32_t* tiles;      // number of tiles (ctl[kCtlTiles])
-  const uint32_t* totals;     // 256 digit totals of this pass over all segments
-  const uint32_t* tile_excl;  // per digit and tile, the count in earlier tiles
+  const uint32_t* totals;     // digit totals of this pass over all segments
+  const uint32_t* tile_excl;  // per tile and digit (tile-major), the count in earlier tiles
   uint32_t ntiles;
 };
 
@@ -485,21 +495,25 @@ struct SortPass {
 // slots [b + w*1024, b + (w+1)*1024) of the tile [b, e); in round r lane l
 // holds slot b + w*1024 + r*64 + l, so (wave, round, lane) is the position
 // order and ranking by wave-private digit counters keeps the sort stable.
-// The digit is taken from the row, key - key_base.  Keys, bag ids and scales
-// pass through one LDS buffer in turn on their way to their coalesced global
-// stores.
-template <bool SC>
+// The digit (DB bits) is taken from the row, key - key_base; thread t owns
+// the Q = 2^DB / 256 consecutive digit values [tQ, tQ + Q) for the per-digit
+// prefixes.  Keys, bag ids and scales pass through one LDS buffer in turn on
+// their way to their coalesced global stores.
+template <int DB, bool SC>
 __global__ __launch_bounds__(kThreads) void sort_pass_kernel(SortPass p) {
+  constexpr uint32_t R = 1u << DB;
+  constexpr int Q = (int)(R / kThreads);
+  static_assert(Q >= 1 && R % kThreads == 0, "at least one digit value per thread");
   __shared__ uint32_t s_buf[kTile];
-  __shared__ uint32_t wcnt[kThreads / kWave][256];
-  __shared__ uint32_t gbase[256];
-  __shared__ uint32_t lstart[256];
+  __shared__ uint32_t wcnt[kThreads / kWave][R];
+  __shared__ uint32_t gbase[R];
+  __shared__ uint32_t lstart[R];
   __shared__ uint32_t sh4[4];
 
   const uint32_t lane = lane_id(), wave = threadIdx.x / kWave;
   const uint32_t tile = xcd_tile();
   if (tile >= *p.tiles) return;  // the grid is sized for the most tiles segments can need
-  for (uint32_t i = threadIdx.x; i < 4 * 256; i += kThreads) (&wcnt[0][0])[i] = 0u;
+  for (uint32_t i = threadIdx.x; i < 4u * R; i += kThreads) (&wcnt[0][0])[i] = 0u;
   uint32_t sid, b, e;
   const uint4 sg = tile_span(p.seg, p.tile_seg, tile, sid, b, e);
   const uint32_t wbase = b + wave * (kTile / 4);
@@ -515,24 +529,32 @@ __global__ __launch_bounds__(kThreads) void sort_pass_kernel(SortPass p) {
     if (SC) sc[r] = p.sin[ii];
   }
   __builtin_amdgcn_sched_barrier(0);
-  const uint32_t d_me = threadIdx.x;  // the digit this thread publishes and looks back for
-  // count of d_me in the segments before this one, and in this segment
-  const uint32_t* row = p.tile_excl + (size_t)d_me * p.ntiles;
+  const uint32_t d0 = threadIdx.x * (uint32_t)Q;  // the digits this thread publishes
+  // per owned digit: its count in the segments before this one, and in this
+  // segment; then the segment base plus the digits below it
   const uint32_t z_next = sg.z + (sg.x + kTile - 1) / kTile;
-  const uint32_t before_seg = row[sg.z];
-  const uint32_t in_seg = (z_next < *p.tiles ? row[z_next] : p.totals[d_me]) - before_seg;
+  const uint32_t* at_seg = p.tile_excl + (size_t)sg.z * R + d0;
+  const uint32_t* at_next = z_next < *p.tiles ? p.tile_excl + (size_t)z_next * R + d0
+                                              : p.totals + d0;
+  uint32_t before_seg[Q], dex[Q], sum = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    before_seg[q] = at_seg[q];
+    const uint32_t in_seg = at_next[q] - before_seg[q];
+    dex[q] = sum;
+    sum += in_seg;
+  }
   uint32_t total;
-  // segment base plus the digits below d_me (ends with a barrier)
-  const uint32_t digit_excl = sg.y + block_excl_scan(in_seg, sh4, total);
+  const uint32_t seg_excl = sg.y + block_excl_scan(sum, sh4, total);  // ends with a barrier
 
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int r = 0; r < kItems; ++r) {
     const bool valid = wbase + (uint32_t)r * kWave + lane < e;
-    const uint32_t d = ((k[r] - sg.w) >> p.shift) & 255u;
+    const uint32_t d = ((k[r] - sg.w) >> p.shift) & (R - 1u);
     uint64_t peers = __ballot(valid);
 #pragma unroll
-    for (int bit = 0; bit < kRadixBits; ++bit) {
+    for (int bit = 0; bit < DB; ++bit) {
       const bool on = (d >> bit) & 1u;
       const uint64_t bb = __ballot(on);
       peers &= on ? bb : ~bb;
@@ -543,28 +565,40 @@ __global__ __launch_bounds__(kThreads) void sort_pass_kernel(SortPass p) {
     if (valid && before == 0) wcnt[wave][d] = prev + (uint32_t)__popcll(peers);
   }
   __syncthreads();
-  uint32_t cnt = 0;
+  // per owned digit: the waves' counts become exclusive over the waves, and
+  // the digit's count in the tile feeds the tile-local starts
+  uint32_t lex[Q], lsum = 0;
 #pragma unroll
-  for (int w = 0; w < kThreads / kWave; ++w) {
-    const uint32_t c = wcnt[w][d_me];
-    wcnt[w][d_me] = cnt;
-    cnt += c;
+  for (int q = 0; q < Q; ++q) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / kWave; ++w) {
+      const uint32_t x = wcnt[w][d0 + q];
+      wcnt[w][d0 + q] = c;
+      c += x;
+    }
+    lex[q] = lsum;
+    lsum += c;
   }
-  const uint32_t ls = block_excl_scan(cnt, sh4, total);
-  lstart[d_me] = ls;
+  const uint32_t ls0 = block_excl_scan(lsum, sh4, total);
+#pragma unroll
+  for (int q = 0; q < Q; ++q) lstart[d0 + q] = ls0 + lex[q];
   __syncthreads();
-  // tile-local slots, keys into LDS while the look-back runs
+  // tile-local slots, keys into LDS while the destinations are formed
 #pragma unroll
   for (int r = 0; r < kItems; ++r) {
     const bool valid = wbase + (uint32_t)r * kWave + lane < e;
-    const uint32_t d = ((k[r] - sg.w) >> p.shift) & 255u;
+    const uint32_t d = ((k[r] - sg.w) >> p.shift) & (R - 1u);
     const uint32_t slot = lstart[d] + wcnt[wave][d] + rk[r];
     rk[r] = (valid && slot < (uint32_t)kTile) ? slot : 0xffffffffu;  // always in range when valid
     if (rk[r] != 0xffffffffu) s_buf[rk[r]] = k[r];
   }
-  const uint32_t excl = row[tile];  // count of d_me in all earlier tiles
-  // destination = gbase[digit] + tile slot
-  gbase[d_me] = digit_excl + (excl - before_seg) - ls;
+  // destination = gbase[digit] + tile slot, from the digit's count in all
+  // earlier tiles
+  const uint32_t* at_tile = p.tile_excl + (size_t)tile * R + d0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+    gbase[d0 + q] = seg_excl + dex[q] + (at_tile[q] - before_seg[q]) - (ls0 + lex[q]);
   __syncthreads();
 
   const uint32_t n = e - b;
@@ -576,7 +610,7 @@ __global__ __launch_bounds__(kThreads) void sort_pass_kernel(SortPass p) {
     dst[r] = 0xffffffffu;
     if (sl < n) {
       const uint32_t key = s_buf[sl];
-      const uint32_t g = gbase[((key - sg.w) >> p.shift) & 255u] + sl;
+      const uint32_t g = gbase[((key - sg.w) >> p.shift) & (R - 1u)] + sl;
       if (g >= sg.y && g < send) {  // always true for consistent digit counts
         dst[r] = g;
         p.kout[g] = key;
@@ -973,6 +1007,25 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClsDev a) {
     if (ex1 + i < a.max_tiny) a.tiny_task[ex1 + i] = s_stage[tot0 + i];
 }
 
+// One radix pass of DB-bit digits: counts per tile, prefixes over tiles,
+// scatter.
+template <int DB>
+void launch_sort_pass(const SortPass& sp, uint32_t* cnt, bool sc, uint32_t sgrid,
+                      const uint32_t* ctl, uint64_t* st, uint64_t nst, hipStream_t s) {
+  uint32_t* tex = const_cast<uint32_t*>(sp.tile_excl);
+  uint32_t* totals = const_cast<uint32_t*>(sp.totals);
+  TBE_LAUNCH("radix_upsweep", radix_upsweep<DB>, dim3(sgrid), dim3(kThreads), s, sp.kin, sp.seg,
+             sp.tile_seg, ctl, sp.shift, cnt, sp.ntiles, st, nst);
+  TBE_LAUNCH("radix_scan", radix_scan<DB>, dim3(1u << DB), dim3(kThreads), s, cnt, sp.ntiles, ctl,
+             tex, totals);
+  if (sc)
+    TBE_LAUNCH("radix_downsweep", (sort_pass_kernel<DB, true>), dim3(sgrid), dim3(kThreads), s,
+               sp);
+  else
+    TBE_LAUNCH("radix_downsweep", (sort_pass_kernel<DB, false>), dim3(sgrid), dim3(kThreads), s,
+               sp);
+}
+
 }  // namespace
 
 hipError_t launch_preprocess(const PrepArgs& p, int /*num_cus*/, hipStream_t s) {
@@ -1014,19 +1067,14 @@ hipError_t launch_preprocess(const PrepArgs& p, int /*num_cus*/, hipStream_t s) 
     SortPass sp{u32p(ab ? L.key_a : L.key_b), u32p(ab ? L.val_a : L.val_b),
                 f32p(ab ? L.sc_a : L.sc_b),   u32p(ab ? L.key_b : L.key_a),
                 u32p(ab ? L.val_b : L.val_a), f32p(ab ? L.sc_b : L.sc_a),
-                (uint32_t)(pass * kRadixBits), seg, tile_seg, ctl + kCtlTiles,
-                totals, u32p(L.tile_cnt), L.ntiles_max};
-    TBE_LAUNCH("radix_upsweep", radix_upsweep, dim3(sgrid), dim3(kThreads), s, sp.kin,
-               seg, tile_seg, ctl, sp.shift, u32p(L.tile_cnt), L.ntiles_max,
-               u64p(L.st_rle), pass == 0 ? nst : (uint64_t)0);
-    TBE_LAUNCH("radix_scan", radix_scan, dim3(256), dim3(kThreads), s, u32p(L.tile_cnt),
-               L.ntiles_max, ctl, totals);
-    if (sc)
-      TBE_LAUNCH("radix_downsweep", sort_pass_kernel<true>, dim3(sgrid), dim3(kThreads),
-                 s, sp);
+                (uint32_t)(pass * L.digit_bits), seg, tile_seg, ctl + kCtlTiles,
+                totals, u32p(L.tile_excl), L.ntiles_max};
+    const uint64_t clear = pass == 0 ? nst : (uint64_t)0;
+    uint32_t* cnt = u32p(L.tile_cnt);
+    if (L.digit_bits == 8)
+      launch_sort_pass<8>(sp, cnt, sc, sgrid, ctl, u64p(L.st_rle), clear, s);
     else
-      TBE_LAUNCH("radix_downsweep", sort_pass_kernel<false>, dim3(sgrid), dim3(kThreads),
-                 s, sp);
+      launch_sort_pass<10>(sp, cnt, sc, sgrid, ctl, u64p(L.st_rle), clear, s);
   }
   const uint32_t* skey = u32p(L.final_in_b ? L.key_b : L.key_a);
   const uint32_t* sbag = u32p(L.final_in_b ? L.val_b : L.val_a);

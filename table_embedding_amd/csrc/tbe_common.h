@@ -19,7 +19,7 @@ constexpr int kRleTile = kRleGroups * kTile;
 constexpr int kLongRun = 256;       // SL >= 256 takes the chunked long-run path
 constexpr int kTinyRun = 32;        // short runs below this are owned by a lane subgroup
 constexpr int kChunk = 256;         // lookups per long-run chunk
-constexpr int kRadixBits = 8;
+constexpr int kRadixMaxBits = 10;  // widest radix digit (1024 values)
 constexpr int kMaxPass = 4;         // 32-bit rows: at most four 8-bit digits
 constexpr int kMaxTables = 4096;
 // grad_out larger than this (the MALL) takes the bag-ordered chunk walk
@@ -93,9 +93,10 @@ struct WsLayout {
   size_t ctl;                                      // control block, kCtlWords uint32
   size_t seg;       // T uint4 {lookups, output base, first tile, key base}, tables in key order
   size_t tile_seg;  // ntiles_max uint32: segment of each sort tile
-  size_t totals;    // 256 digit totals of the current pass
-  size_t tile_cnt;  // 256 x ntiles_max per-tile digit counts of the current pass, then their
-                    // exclusive prefixes over all tiles
+  size_t totals;    // 2^digit_bits digit totals of the current pass
+  size_t tile_cnt;   // 2^digit_bits x ntiles_max per-tile digit counts of the current pass
+                     // (digit-major)
+  size_t tile_excl;  // their exclusive prefixes over all tiles (tile-major)
   // look-back status words (uint64), contiguous in [st_rle, st_end): the
   // run-length pass (nrle_tiles) and the classification pass (ncls_tiles x
   // kClsStride)
@@ -116,6 +117,7 @@ struct WsLayout {
   uint32_t max_chunks;      // capacity of the chunk list
   uint32_t pstride;         // floats per partial row
   int npass;                // radix passes
+  int digit_bits;           // bits per radix digit: 8 or 10
   int final_in_b;           // sorted keys end in key_b/val_b
 };
 

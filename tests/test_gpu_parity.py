@@ -78,13 +78,21 @@ def _spec(name):
         # which the whole workgroup places
         return wl.Spec("heavy_chunks", 2010, [32], [16], [0], "f32", 4096, "fixed:256",
                        "uniform", "i32", False)
+    if name == "rows_21b":
+        # 21 row bits: three 8-bit radix passes (an odd count) at a small size
+        return wl.Spec("rows_21b", 2012, [(1 << 20) + 3, 50], [8, 16], [0, 1], "f16", 300,
+                       "uniform:1:20", "uniform", "i32", True)
+    if name == "rows_25b":
+        # 25 row bits: three 10-bit radix passes
+        return wl.Spec("rows_25b", 2013, [(1 << 24) + 5], [4], [1], "f32", 128,
+                       "uniform:1:16", "uniform", "i64", False)
     raise KeyError(name)
 
 
 MAIN = ["C1", "C2s", "C3s", "C4s", "C5s"]
 EDGE = ["empty_bags", "all_empty", "one_bag", "one_row", "const31", "const32", "const255",
         "const256", "const257", "wide_f32", "wide_bf16", "many_tables", "many_bags",
-        "heavy_chunks", "cut_bags"]
+        "heavy_chunks", "cut_bags", "rows_21b", "rows_25b"]
 
 
 def _announce(name, what):
