@@ -45,12 +45,13 @@ def parse():
                     help="run tbe_validate (check only) at the start of every step")
     ap.add_argument("--bwd-hist", action="store_true",
                     help="histogram-reuse backward (one small table: C4), no preprocessing")
-    ap.add_argument("--schedule", default="serial", choices=["overlap", "fork", "serial"],
+    ap.add_argument("--schedule", default="serial", choices=["overlap", "fork", "auto", "serial"],
                     help="overlap: tbe_preprocess on a side stream during tbe_forward, then "
                          "tbe_backward_rowwise_adagrad on preprocessed data with its run "
                          "classes on three streams; fork: tbe_forward, then "
                          "tbe_backward_rowwise_adagrad (which preprocesses) with its run classes "
-                         "on three streams; serial: all on one stream")
+                         "on three streams; auto: fork below 64 Mi lookups, else serial; "
+                         "serial: all on one stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-lookups", type=int, default=3_000_000,
                     help="cap on lookups in the CPU oracle sample (whole tables)")
@@ -309,7 +310,8 @@ def main():
     out = torch.empty((spec.B, spec.dtot), dtype=torch.float32, device="cuda")
     flags = (te.TBE_BWD_FUSED_LONG if args.fused else 0) | (te.TBE_BWD_HIST if args.bwd_hist else 0)
     overlap = args.schedule == "overlap"
-    conc = 0 if args.schedule == "serial" else te.TBE_BWD_CONCURRENT
+    conc = {"serial": 0, "auto": te.TBE_BWD_CONCURRENT_AUTO}.get(args.schedule,
+                                                                te.TBE_BWD_CONCURRENT)
     hist = (spec.T == 1 and spec.rows[0] <= 64 and 64 <= spec.dims[0] <= 128
             and spec.wdtype == "f16" and not spec.weighted and N >= 64 * spec.B)
 
@@ -410,6 +412,8 @@ def main():
                             "fork": "tbe_forward, then tbe_backward_rowwise_adagrad "
                                     "(preprocessing inside) with medium runs and long runs on "
                                     "two side streams",
+                            "auto": "as fork below 64 Mi lookups, else as serial "
+                                    "(TBE_BWD_CONCURRENT_AUTO)",
                             "serial": "tbe_forward, then tbe_backward_rowwise_adagrad "
                                       "(preprocessing inside), one stream"}[args.schedule]},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),

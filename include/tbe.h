@@ -92,6 +92,7 @@ extern "C" {
 #define TBE_BWD_ORDER_CHUNKS 0x8u  /* always walk each table's chunks in bag order (see below) */
 #define TBE_BWD_NO_ORDER_CHUNKS 0x10u /* never: walk chunks in list order */
 #define TBE_BWD_HIST 0x20u       /* histogram-reuse backward (one small table; see below) */
+#define TBE_BWD_CONCURRENT_AUTO 0x40u /* TBE_BWD_CONCURRENT for batches under 64 Mi lookups only */
 
 typedef struct tbe_plan tbe_plan;
 
@@ -210,7 +211,11 @@ int tbe_preprocess(const tbe_plan* plan, int64_t B, int32_t itype, const void* i
  * into `stream` before it returns: work enqueued later on `stream` sees
  * every update, and the results are bit-identical to the one-stream order.
  * Calls that share a plan enqueue this fork and join one at a time (a
- * host-side lock).
+ * host-side lock).  TBE_BWD_CONCURRENT_AUTO forks only when the batch has
+ * fewer than 64 Mi lookups: measured on MI355X, the concurrent classes cut
+ * the backward of 2.1 M and 17 M lookup batches by 2% and 5% of the step,
+ * but slow a 138 M lookup batch by 15% (the classes compete for the
+ * last-level cache).
  * Chunk walk order: the chunks of a table that one XCD takes read about one
  * eighth of the table's grad_out rows; walking them by the bag of their first
  * lookup keeps the rows in use within that XCD's L2.  This is done when

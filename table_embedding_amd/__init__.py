@@ -12,7 +12,8 @@ from typing import Optional, Sequence
 import torch
 
 from ._lib import (  # noqa: F401
-    EXPORTS, LIB_PATH, TBE_BF16, TBE_BWD_CONCURRENT, TBE_BWD_FUSED_LONG, TBE_BWD_NO_ORDER_CHUNKS,
+    EXPORTS, LIB_PATH, TBE_BF16, TBE_BWD_CONCURRENT, TBE_BWD_CONCURRENT_AUTO, TBE_BWD_FUSED_LONG,
+    TBE_BWD_NO_ORDER_CHUNKS,
     TBE_BWD_HIST, TBE_BWD_ORDER_CHUNKS, TBE_BWD_PREPROCESSED,
     TBE_E_ALLOC,
     TBE_E_ARG, TBE_E_HIP, TBE_E_RANGE, TBE_E_UNSUPPORTED, TBE_E_WORKSPACE, TBE_F16, TBE_F32,

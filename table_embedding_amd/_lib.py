@@ -27,6 +27,7 @@ TBE_FWD_NO_HIST, TBE_FWD_REQUIRE_HIST, TBE_FWD_BALANCE, TBE_FWD_NO_BALANCE = 0x1
 TBE_BWD_PREPROCESSED, TBE_BWD_FUSED_LONG, TBE_BWD_CONCURRENT = 0x1, 0x2, 0x4
 TBE_BWD_ORDER_CHUNKS, TBE_BWD_NO_ORDER_CHUNKS = 0x8, 0x10
 TBE_BWD_HIST = 0x20
+TBE_BWD_CONCURRENT_AUTO = 0x40
 
 EXPORTS = ("tbe_plan_create", "tbe_plan_destroy", "tbe_plan_key_bases", "tbe_workspace_size",
            "tbe_workspace_views", "tbe_forward", "tbe_forward_preprocess", "tbe_preprocess",

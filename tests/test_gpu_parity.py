@@ -286,7 +286,7 @@ def test_concurrent_backward_equals_one_stream(name, fused):
     case = S.Case(_spec(name), m_nonzero=True)
     res = []
     base = te.TBE_BWD_FUSED_LONG if fused else 0
-    for flags in (base, base | te.TBE_BWD_CONCURRENT, base):
+    for flags in (base, base | te.TBE_BWD_CONCURRENT, base | te.TBE_BWD_CONCURRENT_AUTO, base):
         case.reset_tables()
         tb = case.tbe()
         tb.backward(case.spec.B, case.d_idx, case.d_off, case.d_psw, case.d_G, case.spec.lr,
@@ -294,7 +294,7 @@ def test_concurrent_backward_equals_one_stream(name, fused):
         torch.cuda.synchronize()
         res.append(_tables_bytes(tb, case.spec.wdtype))
         tb.close()
-    assert res[0] == res[1] == res[2]
+    assert res[0] == res[1] == res[2] == res[3]
 
 
 @pytest.mark.parametrize("name", ["C2s", "C3s", "empty_bags", "wide_f32"])
