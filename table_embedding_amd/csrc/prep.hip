@@ -530,22 +530,7 @@ __global__ __launch_bounds__(kThreads) void sort_pass_kernel(SortPass p) {
   }
   __builtin_amdgcn_sched_barrier(0);
   const uint32_t d0 = threadIdx.x * (uint32_t)Q;  // the digits this thread publishes
-  // per owned digit: its count in the segments before this one, and in this
-  // segment; then the segment base plus the digits below it
-  const uint32_t z_next = sg.z + (sg.x + kTile - 1) / kTile;
-  const uint32_t* at_seg = p.tile_excl + (size_t)sg.z * R + d0;
-  const uint32_t* at_next = z_next < *p.tiles ? p.tile_excl + (size_t)z_next * R + d0
-                                              : p.totals + d0;
-  uint32_t before_seg[Q], dex[Q], sum = 0;
-#pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    before_seg[q] = at_seg[q];
-    const uint32_t in_seg = at_next[q] - before_seg[q];
-    dex[q] = sum;
-    sum += in_seg;
-  }
-  uint32_t total;
-  const uint32_t seg_excl = sg.y + block_excl_scan(sum, sh4, total);  // ends with a barrier
+  __syncthreads();  // wcnt cleared
 
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
@@ -580,6 +565,7 @@ __global__ __launch_bounds__(kThreads) void sort_pass_kernel(SortPass p) {
     lex[q] = lsum;
     lsum += c;
   }
+  uint32_t total;
   const uint32_t ls0 = block_excl_scan(lsum, sh4, total);
 #pragma unroll
   for (int q = 0; q < Q; ++q) lstart[d0 + q] = ls0 + lex[q];
@@ -593,12 +579,26 @@ __global__ __launch_bounds__(kThreads) void sort_pass_kernel(SortPass p) {
     rk[r] = (valid && slot < (uint32_t)kTile) ? slot : 0xffffffffu;  // always in range when valid
     if (rk[r] != 0xffffffffu) s_buf[rk[r]] = k[r];
   }
-  // destination = gbase[digit] + tile slot, from the digit's count in all
-  // earlier tiles
+  // per owned digit: its count in the segments before this one, in this
+  // segment and in the earlier tiles of this segment (taken after the
+  // ranking, so that none of it is live across the ranking loop); then the
+  // destination base = segment base + the digits below it in the segment +
+  // the digit's count in the segment's earlier tiles - its tile-local start
+  const uint32_t z_next = sg.z + (sg.x + kTile - 1) / kTile;
+  const uint32_t* at_seg = p.tile_excl + (size_t)sg.z * R + d0;
+  const uint32_t* at_next = z_next < *p.tiles ? p.tile_excl + (size_t)z_next * R + d0
+                                              : p.totals + d0;
   const uint32_t* at_tile = p.tile_excl + (size_t)tile * R + d0;
+  uint32_t part[Q], sum = 0;
 #pragma unroll
-  for (int q = 0; q < Q; ++q)
-    gbase[d0 + q] = seg_excl + dex[q] + (at_tile[q] - before_seg[q]) - (ls0 + lex[q]);
+  for (int q = 0; q < Q; ++q) {
+    const uint32_t before_seg = at_seg[q];
+    part[q] = sum + (at_tile[q] - before_seg) - (ls0 + lex[q]);
+    sum += at_next[q] - before_seg;
+  }
+  const uint32_t seg_excl = sg.y + block_excl_scan(sum, sh4, total);  // ends with a barrier
+#pragma unroll
+  for (int q = 0; q < Q; ++q) gbase[d0 + q] = seg_excl + part[q];
   __syncthreads();
 
   const uint32_t n = e - b;
