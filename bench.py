@@ -149,11 +149,12 @@ def byte_model(spec, st, hist_path):
     ncls = -(-N // 2048)
     nrle = -(-N // 16384)  # run-length tiles
     st_words = nrle + ncls * 8  # look-back status words of rle and classify
-    comp["seg_setup"] = 2 * T * si + 16 * T + 4 * stiles
-    comp["transpose"] = N * (si + 4 * psi) + (T * B + 1) * si + N * rec
+    # the transposition's workgroup 0 also writes the segment table and tile map
+    comp["transpose"] = (N * (si + 4 * psi) + (T * B + 1) * si + N * rec
+                         + 2 * T * si + 16 * T + 4 * stiles)
     # per pass: the keys read once for the digit counts (the first pass also
     # clears the status words); the counts scanned in place; the records read
-    # and written once by the scatter, plus each tile's 256 prefixes
+    # and written once by the scatter, plus each tile's 2^b prefixes
     comp["radix_upsweep"] = npass * (4 * N + R * 4 * stiles) + 8 * st_words
     comp["radix_scan"] = npass * 2 * R * 4 * stiles
     comp["radix_downsweep"] = npass * (2 * rec * N + R * 4 * stiles)

@@ -18,10 +18,12 @@
 // at the segment's first tile, and is subtracted.
 //
 // Kernels, in launch order (256 threads each, no host readback anywhere):
-//   seg_setup      one workgroup: per segment (tables in key order) its
-//                  lookup count, output base and first tile; the segment of
-//                  every tile; clears the control block (tickets, error flag)
-//   transpose      key = key_base[t] + I[p], bag = j and, with per-sample
+//   transpose      workgroup 0 first sets up the segments (per segment,
+//                  tables in key order: lookup count, output base, first
+//                  tile; the segment of every tile; clears the control
+//                  block: tickets, error flag), every workgroup forms the
+//                  segments' output bases itself; then
+//                  key = key_base[t] + I[p], bag = j and, with per-sample
 //                  weights or a mean table, scale = S[p]*(1/L), written at
 //                  the lookup's slot in its table's segment
 //   then per digit of 8 or 10 bits (the fewest passes of at most 10 bits
@@ -218,20 +220,18 @@ __device__ __forceinline__ uint32_t take_ticket(uint32_t* tickets, uint32_t* s_t
 
 // ------------------------------------------------------------ segments
 
-// One workgroup.  Segment s is table order[s] (tables in key order); its
-// lookups are [O[t*B], O[(t+1)*B]).  Writes {lookups, output base, first
-// tile, key base} per segment, the segment of every tile (a segment of at
-// most eight tiles by its own thread, a larger one by all threads in turn:
-// one thread per segment wrote 2048 tiles in 124 us for a single table of
-// 8.4M lookups), the tile total (ctl[kCtlTiles]) and clears the tickets and
-// the error flag.
+// Run by one workgroup (workgroup 0 of the transposition).  Segment s is
+// table order[s] (tables in key order); its lookups are [O[t*B], O[(t+1)*B]).
+// Writes {lookups, output base, first tile, key base} per segment, the
+// segment of every tile (a segment of at most eight tiles by its own thread,
+// a larger one by all threads in turn: one thread per segment wrote 2048
+// tiles in 124 us for a single table of 8.4M lookups), the tile total
+// (ctl[kCtlTiles]) and clears the tickets and the error flag.  None of it is
+// read before the next kernel.
 template <typename IT>
-__global__ __launch_bounds__(kThreads) void seg_setup_kernel(PrepDev a,
-                                                             const uint32_t* __restrict__ order,
-                                                             uint4* __restrict__ seg,
-                                                             uint32_t* __restrict__ tile_seg,
-                                                             uint32_t ntiles_max,
-                                                             uint32_t* __restrict__ ctl) {
+__device__ void seg_setup_block(const PrepDev& a, const uint32_t* __restrict__ order,
+                                uint4* __restrict__ seg, uint32_t* __restrict__ tile_seg,
+                                uint32_t ntiles_max, uint32_t* __restrict__ ctl) {
   __shared__ uint32_t sh4[4];
   __shared__ uint32_t s_ot[kThreads], s_nt[kThreads];  // first tile and tiles of the batch's segments
   const IT* __restrict__ O = reinterpret_cast<const IT*>(a.offsets);
@@ -276,6 +276,29 @@ __global__ __launch_bounds__(kThreads) void seg_setup_kernel(PrepDev a,
   if (threadIdx.x == 0) ctl[kCtlTiles] = run_t < ntiles_max ? run_t : ntiles_max;
 }
 
+// Output base of every segment (the exclusive prefix of the segments'
+// lookup counts in key order, clamped into [0, N] as seg_setup_block clamps
+// it) into s_base[0, T).  Ends with a barrier.
+template <typename IT>
+__device__ void segment_bases(const PrepDev& a, const uint32_t* __restrict__ order,
+                              uint32_t* s_base, uint32_t* sh4) {
+  const IT* __restrict__ O = reinterpret_cast<const IT*>(a.offsets);
+  uint32_t run_n = 0;
+  for (uint32_t s0 = 0; s0 < a.T; s0 += kThreads) {
+    const uint32_t s = s0 + threadIdx.x;
+    uint32_t n = 0;
+    if (s < a.T) {
+      const uint32_t t = order[s];
+      n = (uint32_t)(O[(int64_t)(t + 1) * a.B] - O[(int64_t)t * a.B]);
+    }
+    uint32_t tot_n;
+    const uint64_t on_raw = (uint64_t)run_n + block_excl_scan(n, sh4, tot_n);
+    if (s < a.T) s_base[s] = on_raw < a.N ? (uint32_t)on_raw : a.N;
+    run_n += tot_n;
+  }
+  __syncthreads();
+}
+
 // ------------------------------------------------------------ transposition
 // A workgroup takes `nbp` consecutive bags (at most 256, as many as keep
 // about 2048 workgroups; table-major, so their lookups are one contiguous
@@ -290,18 +313,31 @@ __global__ __launch_bounds__(kThreads) void seg_setup_kernel(PrepDev a,
 // four short dependent chains in flight).
 constexpr uint32_t kTrBags = 256;
 
+// Each workgroup forms the segments' output bases itself (T values in
+// dynamic LDS), so the transposition needs no set-up launch before it;
+// workgroup 0 also writes the segment table, the tile map and the control
+// block for the later kernels.
 template <typename IT>
 __global__ __launch_bounds__(kThreads) void transpose_kernel(PrepDev a, uint32_t nbp,
                                                              uint32_t* __restrict__ key,
                                                              uint32_t* __restrict__ bag,
-                                                             float* __restrict__ scale) {
+                                                             float* __restrict__ scale,
+                                                             const uint32_t* __restrict__ order,
+                                                             uint4* __restrict__ seg_out,
+                                                             uint32_t* __restrict__ tile_seg,
+                                                             uint32_t ntiles_max,
+                                                             uint32_t* __restrict__ ctl) {
   __shared__ int64_t s_off[kTrBags + 1];
   __shared__ int64_t s_shift[kTrBags];  // slot of position p: p + shift (its table's)
   __shared__ uint32_t s_kb[kTrBags];
   __shared__ uint32_t s_mean[kTrBags];
+  __shared__ uint32_t sh4[4];
+  extern __shared__ uint32_t s_base[];  // T output bases, segment order
   const uint64_t nbag = (uint64_t)a.T * (uint64_t)a.B;
   const uint64_t j0 = (uint64_t)blockIdx.x * nbp;
+  if (blockIdx.x == 0) seg_setup_block<IT>(a, order, seg_out, tile_seg, ntiles_max, ctl);
   if (j0 >= nbag || nbp > kTrBags) return;
+  segment_bases<IT>(a, order, s_base, sh4);
   const uint32_t nb = (uint32_t)min((uint64_t)nbp, nbag - j0);
   const IT* __restrict__ I = reinterpret_cast<const IT*>(a.indices);
   const IT* __restrict__ O = reinterpret_cast<const IT*>(a.offsets);
@@ -310,7 +346,7 @@ __global__ __launch_bounds__(kThreads) void transpose_kernel(PrepDev a, uint32_t
     const uint64_t j = j0 + threadIdx.x;
     const uint32_t t = (uint32_t)(j / (uint64_t)a.B);
     const TableDev td = a.tables[t];
-    s_shift[threadIdx.x] = (int64_t)a.seg[a.tseg[t]].y - (int64_t)O[(int64_t)t * a.B];
+    s_shift[threadIdx.x] = (int64_t)s_base[a.tseg[t]] - (int64_t)O[(int64_t)t * a.B];
     s_kb[threadIdx.x] = td.key_base;
     s_mean[threadIdx.x] = td.pooling == POOL_MEAN ? 1u : 0u;
   }
@@ -1043,21 +1079,18 @@ hipError_t launch_preprocess(const PrepArgs& p, int /*num_cus*/, hipStream_t s) 
   uint32_t* tile_seg = u32p(L.tile_seg);
   uint32_t* totals = u32p(L.totals);
   PrepDev d{p.tables, p.T, p.nb, p.B, p.indices, p.offsets, p.psw, p.N, p.tseg, seg};
-  if (p.itype == IT_I32)
-    TBE_LAUNCH("seg_setup", seg_setup_kernel<int32_t>, dim3(1), dim3(kThreads), s, d, p.order,
-               seg, tile_seg, L.ntiles_max, ctl);
-  else
-    TBE_LAUNCH("seg_setup", seg_setup_kernel<int64_t>, dim3(1), dim3(kThreads), s, d, p.order,
-               seg, tile_seg, L.ntiles_max, ctl);
   const uint64_t nbag = (uint64_t)p.T * (uint64_t)p.B;
   const uint32_t nbp = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(kTrBags, nbag / 2048));
   const uint32_t tgrid = (uint32_t)((nbag + nbp - 1) / nbp);
+  const size_t tshm = sizeof(uint32_t) * (size_t)p.T;
   if (p.itype == IT_I32)
-    TBE_LAUNCH("transpose", transpose_kernel<int32_t>, dim3(tgrid), dim3(kThreads), s, d, nbp,
-               u32p(L.key_a), u32p(L.val_a), sc ? f32p(L.sc_a) : nullptr);
+    TBE_LAUNCH_SHM("transpose", transpose_kernel<int32_t>, dim3(tgrid), dim3(kThreads), tshm, s,
+                   d, nbp, u32p(L.key_a), u32p(L.val_a), sc ? f32p(L.sc_a) : nullptr, p.order,
+                   seg, tile_seg, L.ntiles_max, ctl);
   else
-    TBE_LAUNCH("transpose", transpose_kernel<int64_t>, dim3(tgrid), dim3(kThreads), s, d, nbp,
-               u32p(L.key_a), u32p(L.val_a), sc ? f32p(L.sc_a) : nullptr);
+    TBE_LAUNCH_SHM("transpose", transpose_kernel<int64_t>, dim3(tgrid), dim3(kThreads), tshm, s,
+                   d, nbp, u32p(L.key_a), u32p(L.val_a), sc ? f32p(L.sc_a) : nullptr, p.order,
+                   seg, tile_seg, L.ntiles_max, ctl);
 
   // ping-pong a -> b -> a ...; the final buffers are b for an odd pass count
   const uint64_t nst = (L.st_end - L.st_rle) / 8;
