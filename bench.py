@@ -147,7 +147,7 @@ def byte_model(spec, st, hist_path):
     n = {c: sum(s["n_" + c] for s in st) for c, _, _ in SL_CLASSES}
     n_chunks = sum(s["chunks"] for s in st)
     ncls = -(-N // 2048)
-    nrle = -(-N // 16384)  # run-length tiles
+    nrle = -(-N // (16384 if N >= (64 << 20) else 4096))  # run-length tiles
     st_words = nrle + ncls * 8  # look-back status words of rle and classify
     # the transposition's workgroup 0 also writes the segment table and tile map
     comp["transpose"] = (N * (si + 4 * psi) + (T * B + 1) * si + N * rec

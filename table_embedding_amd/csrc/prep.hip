@@ -675,11 +675,13 @@ __global__ __launch_bounds__(kThreads) void sort_pass_kernel(SortPass p) {
 }
 
 // --------------------------------------------------- run-length encoding
-// A tile is kRleGroups consecutive groups of 4096 sorted slots; in group g
-// thread h owns slots [tile + g*4096 + 16h, ... + 16), so every load is
-// coalesced, and runs are numbered group by group in slot order.  Four
-// groups per tile make the look-back chain a quarter as long.
+// A tile is G consecutive groups of 4096 sorted slots; in group g thread h
+// owns slots [tile + g*4096 + 16h, ... + 16), so every load is coalesced,
+// and runs are numbered group by group in slot order.  Four groups per tile
+// make the look-back chain a quarter as long (deep batches); one gives a
+// shallow batch four times the workgroups.
 
+template <int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void rle_kernel(const uint32_t* __restrict__ key, uint32_t N,
                                                        uint32_t ntiles, uint32_t* ticket,
                                                        uint64_t* st, uint32_t* err,
@@ -690,11 +692,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   __shared__ uint32_t s_tile, s_excl;
   __shared__ uint32_t s_rs[kTile], s_rk[kTile];  // one group's run heads, staged
   const uint32_t tile = take_ticket(ticket, &s_tile);
-  uint32_t k[kRleGroups][kItems];
-  uint32_t m[kRleGroups];  // run heads among this thread's 16 slots of each group
+  uint32_t k[G][kItems];
+  uint32_t m[G];  // run heads among this thread's 16 slots of each group
 #pragma unroll
-  for (int g = 0; g < kRleGroups; ++g) {
-    const uint64_t i0 = (uint64_t)tile * kRleTile + (uint64_t)g * kTile +
+  for (int g = 0; g < G; ++g) {
+    const uint64_t i0 = (uint64_t)tile * (G * kTile) + (uint64_t)g * kTile +
                         (uint64_t)threadIdx.x * kItems;
     m[g] = 0;
     if (i0 < N) {
@@ -709,15 +711,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       }
     }
   }
-  uint32_t local[kRleGroups], gbase[kRleGroups + 1], total = 0;
+  uint32_t local[G], gbase[G + 1], total = 0;
 #pragma unroll
-  for (int g = 0; g < kRleGroups; ++g) {
+  for (int g = 0; g < G; ++g) {
     uint32_t tg;
     gbase[g] = total;
     local[g] = block_excl_scan(__popc(m[g]), sh4, tg);  // within the group
     total += tg;
   }
-  gbase[kRleGroups] = total;
+  gbase[G] = total;
   if (threadIdx.x < (uint32_t)kWave) {  // wave 0
     const uint32_t excl = publish_and_look_back<64>(st, tile, 1, 0, total, err);
     if (threadIdx.x == 0) {
@@ -734,8 +736,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   // stores (written straight from each thread's slots, most lanes of every
   // store would be masked off: runs are a fraction of the slots)
 #pragma unroll
-  for (int g = 0; g < kRleGroups; ++g) {
-    const uint64_t i0 = (uint64_t)tile * kRleTile + (uint64_t)g * kTile +
+  for (int g = 0; g < G; ++g) {
+    const uint64_t i0 = (uint64_t)tile * (G * kTile) + (uint64_t)g * kTile +
                         (uint64_t)threadIdx.x * kItems;
     uint32_t u = local[g];
 #pragma unroll
@@ -1111,7 +1113,12 @@ hipError_t launch_preprocess(const PrepArgs& p, int /*num_cus*/, hipStream_t s) 
   }
   const uint32_t* skey = u32p(L.final_in_b ? L.key_b : L.key_a);
   const uint32_t* sbag = u32p(L.final_in_b ? L.val_b : L.val_a);
-  TBE_LAUNCH("rle", rle_kernel, dim3(L.nrle_tiles), dim3(kThreads), s, skey, p.N, L.nrle_tiles,
+  if (L.rle_groups == (uint32_t)kRleGroupsDeep)
+    TBE_LAUNCH("rle", rle_kernel<kRleGroupsDeep>, dim3(L.nrle_tiles), dim3(kThreads), s, skey, p.N, L.nrle_tiles,
+             ctl + kCtlRleTickets, u64p(L.st_rle), err, u32p(L.counters),
+             u32p(L.run_start), u32p(L.run_key));
+  else
+    TBE_LAUNCH("rle", rle_kernel<1>, dim3(L.nrle_tiles), dim3(kThreads), s, skey, p.N, L.nrle_tiles,
              ctl + kCtlRleTickets, u64p(L.st_rle), err, u32p(L.counters),
              u32p(L.run_start), u32p(L.run_key));
 

@@ -90,7 +90,8 @@ WsLayout layout(const tbe_plan* P, int64_t N) {
   WsLayout L{};
   const uint64_t n = (uint64_t)N;
   L.ntiles = (uint32_t)((n + kTile - 1) / kTile);
-  L.nrle_tiles = (uint32_t)((n + kRleTile - 1) / kRleTile);
+  L.rle_groups = N >= kRleDeepLookups ? (uint32_t)kRleGroupsDeep : 1u;
+  L.nrle_tiles = (uint32_t)((n + (uint64_t)L.rle_groups * kTile - 1) / ((uint64_t)L.rle_groups * kTile));
   L.ncls_tiles = (uint32_t)((n + kClsTile - 1) / kClsTile);
   L.max_tiny = (uint32_t)(n / 2 + 1);
   L.max_med = (uint32_t)(n / kTinyRun + 1);

@@ -14,8 +14,12 @@ constexpr int kThreads = 256;       // every kernel runs 256-thread workgroups (
 constexpr int kWave = 64;
 constexpr int kTile = 4096;         // keys per workgroup in the sort / run-length passes
 constexpr int kClsTile = 2048;      // runs per workgroup in the classification pass
-constexpr int kRleGroups = 4;       // 4096-key groups per run-length tile
-constexpr int kRleTile = kRleGroups * kTile;
+// 4096-key groups per run-length tile: four from kRleDeepLookups lookups on
+// (the look-back chain a quarter as long), else one (more workgroups).
+// Measured on MI355X (run-length pass per step, four groups / one): 2.1 M
+// lookups 17.0 / 11.1 us, 17 M 51.3 / 46.8 us.
+constexpr int kRleGroupsDeep = 4;
+constexpr int64_t kRleDeepLookups = 64ll << 20;
 constexpr int kLongRun = 256;       // SL >= 256 takes the chunked long-run path
 constexpr int kTinyRun = 32;        // short runs below this are owned by a lane subgroup
 constexpr int kChunk = 256;         // lookups per long-run chunk
@@ -108,7 +112,8 @@ struct WsLayout {
   size_t hist_part, hist_cnt;  // histogram backward: partial rows and row counts (or 0 bytes)
   size_t total;
   uint32_t ntiles;          // ceil(N / kTile)
-  uint32_t nrle_tiles;      // ceil(N / kRleTile): tiles of the run-length pass
+  uint32_t nrle_tiles;      // ceil(N / (rle_groups * kTile)): tiles of the run-length pass
+  uint32_t rle_groups;      // 4096-key groups per run-length tile (1 or kRleGroupsDeep)
   uint32_t ntiles_max;      // ceil(N / kTile) + T: bound on the sort tiles of the segments
   uint32_t ncls_tiles;      // ceil(N / kClsTile): runs are at most N
   uint32_t max_tiny;        // capacity of the 2 <= SL < 32 list
