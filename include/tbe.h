@@ -120,7 +120,8 @@ typedef struct {
   size_t counters;     /* uint32 {U, n_single, n_tiny, n_medium, n_long, n_chunks, then for
                           each of the five lists its nb+1 per-D-bucket begins} */
   size_t prep_error;   /* uint32, 0 after a good preprocessing; nonzero if a cross-workgroup
-                          wait of the scans gave up after its poll limit (results invalid) */
+                          wait of the scans gave up after its poll limit (results invalid;
+                          the backward then writes nothing) */
   size_t total;        /* bytes needed */
   int32_t num_buckets; /* nb */
 } tbe_ws_views;
@@ -142,11 +143,20 @@ int tbe_plan_destroy(tbe_plan* plan);
 /* Host copy of the linear key base of each table (T entries). */
 int tbe_plan_key_bases(const tbe_plan* plan, int64_t* key_base);
 
-/* Bytes of workspace needed for B bags per table and num_lookups lookups.
- * The bound uses only host-known sizes (runs <= N, chunks <= N/256 + long runs). */
+/* Bytes of workspace needed for B bags per table and num_lookups lookups
+ * (FBTriton page, "Fewer reads and synchronizations": the preprocessing's
+ * outputs and counts live in preallocated device memory, so no count is read
+ * back to size them; HugeCTR walkthrough, step 3: the sort's temporary
+ * storage is sized by a query before the call).  The bound uses only
+ * host-known sizes (runs <= N, chunks <= N/256 + long runs).  Errors:
+ * TBE_E_ARG, TBE_E_RANGE (num_lookups >= 2^31 - 1). */
 int tbe_workspace_size(const tbe_plan* plan, int64_t B, int64_t num_lookups, size_t* bytes);
 
-/* Offsets of the preprocessing results inside such a workspace. */
+/* Offsets of the preprocessing results inside such a workspace: the sorted
+ * lookups, run starts and keys, and the task lists and their device-resident
+ * counts (FBTriton page, "Backward" and "Fewer reads and synchronizations";
+ * HugeCTR walkthrough, steps 3 and 4).  Host-side; errors as
+ * tbe_workspace_size. */
 int tbe_workspace_views(const tbe_plan* plan, int64_t B, int64_t num_lookups,
                         tbe_ws_views* out);
 
@@ -204,6 +214,12 @@ int tbe_preprocess(const tbe_plan* plan, int64_t B, int32_t itype, const void* i
  * momentum of touched rows are updated in place;
  * untouched rows are not written.  debug_row_updates (device, nullable): one
  * uint32 per linear key, incremented once per row update.
+ * If a cross-workgroup wait of the preprocessing gave up (the workspace's
+ * prep_error word is nonzero: a wait exceeded its poll limit, which a
+ * correctly working device does not reach), its lists may be spoiled, and
+ * every backward kernel returns before writing anything: weights, momentum
+ * and debug counters keep their contents, and the caller can read
+ * prep_error to learn that the step was skipped.
  * By default every kernel runs on `stream`, one after another.  The run
  * classes own disjoint rows, so with TBE_BWD_CONCURRENT the call forks from
  * `stream` onto the plan's two side streams (medium runs on one, chunks and
@@ -305,6 +321,24 @@ int tbe_prof_read(int32_t max_kernels, char* names, int64_t* launches, double* t
  * name "empty": their average is the per-launch floor of a kernel that does
  * nothing. */
 int tbe_prof_calibrate(int32_t launches, void* stream);
+
+/* Test knobs, for test suites and tools only: process-wide overrides of the
+ * batch sizes from which the library picks the variants it uses on deep
+ * batches, so that small inputs can run them against a reference, and of
+ * the poll limit of the preprocessing's cross-workgroup waits, so that a
+ * wait that gives up can be forced from the host (every kernel still exits
+ * normally).  value < 0 restores the default.  Changing a knob while calls
+ * are in flight, or between tbe_workspace_size and the calls that use the
+ * workspace, is not supported.  Errors: TBE_E_ARG for an unknown knob. */
+#define TBE_KNOB_RLE_DEEP_LOOKUPS 1   /* run-length tiles of four 4096-key groups from this
+                                         many lookups on (default 64 Mi) */
+#define TBE_KNOB_BWD_DEEP_LOOKUPS 2   /* backward gathers with eight lookups in flight and
+                                         streamed weight rows from here on (default 64 Mi) */
+#define TBE_KNOB_BWD_STREAM_LOOKUPS 3 /* streamed (non-temporal) weight rows in the backward
+                                         from here on (default 8 Mi) */
+#define TBE_KNOB_WAIT_POLLS 4         /* polls before a look-back wait gives up (default
+                                         2^20; 0: a tile with predecessors gives up at once) */
+int tbe_test_knob(int32_t knob, int64_t value);
 
 /* Static text for a status code. */
 const char* tbe_status_string(int status);

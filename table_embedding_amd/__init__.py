@@ -26,7 +26,8 @@ from ._lib import (  # noqa: F401
     tbe_backward, TBE_OPT_ROWWISE_ADAGRAD, TBE_OPT_ADAGRAD, TBE_OPT_SGD,
     TBE_INVALID_OFFSET_START, TBE_INVALID_OFFSET_END, TBE_INVALID_OFFSET_ORDER,
     TBE_INVALID_OFFSET_RANGE, TBE_INVALID_INDEX,
-    tbe_workspace_size, tbe_workspace_views)
+    tbe_workspace_size, tbe_workspace_views, tbe_test_knob, TBE_KNOB_RLE_DEEP_LOOKUPS,
+    TBE_KNOB_BWD_DEEP_LOOKUPS, TBE_KNOB_BWD_STREAM_LOOKUPS, TBE_KNOB_WAIT_POLLS)
 
 
 class TBE:

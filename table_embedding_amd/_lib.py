@@ -32,9 +32,11 @@ TBE_BWD_CONCURRENT_AUTO = 0x40
 EXPORTS = ("tbe_plan_create", "tbe_plan_destroy", "tbe_plan_key_bases", "tbe_workspace_size",
            "tbe_workspace_views", "tbe_forward", "tbe_forward_preprocess", "tbe_preprocess",
            "tbe_backward_rowwise_adagrad", "tbe_backward", "tbe_validate", "tbe_prof_enable",
-           "tbe_prof_read",
-           "tbe_prof_calibrate", "tbe_status_string")
+           "tbe_prof_read", "tbe_prof_calibrate", "tbe_test_knob", "tbe_status_string")
 TBE_PROF_NAME_LEN = 32
+
+# debug_row_updates: one uint32 word per linear key
+_U32 = torch.uint32
 
 WDTYPE_OF_TORCH = {torch.float32: TBE_F32, torch.float16: TBE_F16, torch.bfloat16: TBE_BF16}
 ITYPE_OF_TORCH = {torch.int32: TBE_I32, torch.int64: TBE_I64}
@@ -85,6 +87,7 @@ def lib() -> C.CDLL:
         L.tbe_prof_enable.argtypes = [C.c_int]
         L.tbe_prof_read.argtypes = [i32, vp, vp, vp, C.POINTER(i32)]
         L.tbe_prof_calibrate.argtypes = [i32, vp]
+        L.tbe_test_knob.argtypes = [i32, i64]
         L.tbe_status_string.argtypes = [C.c_int]
         L.tbe_status_string.restype = C.c_char_p
         for n in EXPORTS[:-1]:  # every entry point but the status text returns a status
@@ -250,11 +253,20 @@ def tbe_backward_rowwise_adagrad(plan, B: int, indices, offsets, num_lookups: in
         int(num_lookups), _dptr(per_sample_weights, torch.float32, "per_sample_weights"),
         _dptr(grad_out, torch.float32, "grad_out"), float(lr), float(eps),
         _dptr(ws, None, "ws"), ws.numel() * ws.element_size(), int(flags),
-        _dptr(debug_row_updates, torch.int32, "debug_row_updates"), _stream(stream))
+        _dptr(debug_row_updates, _U32, "debug_row_updates"), _stream(stream))
     _check("tbe_backward_rowwise_adagrad", rc)
 
 
 TBE_OPT_ROWWISE_ADAGRAD, TBE_OPT_ADAGRAD, TBE_OPT_SGD = 0, 1, 2
+
+TBE_KNOB_RLE_DEEP_LOOKUPS, TBE_KNOB_BWD_DEEP_LOOKUPS = 1, 2
+TBE_KNOB_BWD_STREAM_LOOKUPS, TBE_KNOB_WAIT_POLLS = 3, 4
+
+
+def tbe_test_knob(knob: int, value: int) -> None:
+    """Test-only override of a variant threshold or the look-back poll limit
+    (value < 0 restores the default)."""
+    _check("tbe_test_knob", lib().tbe_test_knob(int(knob), int(value)))
 
 
 def tbe_backward(plan, B: int, indices, offsets, num_lookups: int, per_sample_weights,
@@ -267,7 +279,7 @@ def tbe_backward(plan, B: int, indices, offsets, num_lookups: int, per_sample_we
         int(num_lookups), _dptr(per_sample_weights, torch.float32, "per_sample_weights"),
         _dptr(grad_out, torch.float32, "grad_out"), int(optimizer), float(lr), float(eps),
         _dptr(ws, None, "ws"), ws.numel() * ws.element_size(), int(flags),
-        _dptr(debug_row_updates, torch.int32, "debug_row_updates"), _stream(stream))
+        _dptr(debug_row_updates, _U32, "debug_row_updates"), _stream(stream))
     _check("tbe_backward", rc)
 
 

@@ -67,8 +67,11 @@ __device__ __forceinline__ void gather_t(const BwdArgs& a, const TableDev& td, i
     bool ok[kInFlight];
 #pragma unroll
     for (int k = 0; k < kInFlight; ++k) {
-      ok[k] = i + (uint32_t)k * step < i1;
-      b[k] = (int64_t)nbag[k] - tB;
+      // a bag outside the table's B bags (never, for lists the preprocessing
+      // wrote) reads row 0 and is dropped
+      const int64_t bk = (int64_t)nbag[k] - tB;
+      ok[k] = i + (uint32_t)k * step < i1 && (uint64_t)bk < (uint64_t)a.B;
+      b[k] = ok[k] ? bk : 0;
       sc[k] = nsc[k];
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -123,6 +126,11 @@ __device__ __forceinline__ bool long_ok(const BwdArgs& a, uint32_t l) {
   const uint32_t cb = a.long_cbeg[l];
   return cb <= a.max_chunks && nch <= a.max_chunks - cb;
 }
+
+// A cross-workgroup wait of the preprocessing gave up, so its lists may be
+// spoiled: every backward kernel then returns before it writes anything
+// (weights, momentum, partials, debug counters all keep their contents).
+__device__ __forceinline__ bool prep_failed(const BwdArgs& a) { return *a.prep_err != 0u; }
 
 __device__ __forceinline__ uint32_t list_begin(const BwdArgs& a, int list, uint32_t bucket) {
   return a.counters[kCntBegins + list * (a.nb + 1) + bucket];
@@ -262,6 +270,7 @@ __device__ __forceinline__ void single_pair(const BwdArgs& a, const TableDev* s_
 // In list order: subgroup sg of the launch takes positions sg, sg + nsg, ...
 template <int WD, int VEC, int NC, bool SCALE, bool TDL, bool NT>
 __global__ __launch_bounds__(kThreads) void bwd_single_kernel(BwdArgs a, BucketSet S) {
+  if (prep_failed(a)) return;
   BucketDev bk;
   uint32_t bucket, lb, lg;
   set_pick(S, bk, bucket, lb, lg);
@@ -294,6 +303,7 @@ __global__ __launch_bounds__(kThreads) void bwd_single_kernel(BwdArgs a, BucketS
 // plain stores.  The next task record is prefetched.
 template <int WD, int VEC, int NC, bool TDL, int IF, bool NT>
 __global__ __launch_bounds__(kThreads) void bwd_tiny_kernel(BwdArgs a, BucketSet S) {
+  if (prep_failed(a)) return;
   BucketDev bk;
   uint32_t bucket, lb, lg;
   set_pick(S, bk, bucket, lb, lg);
@@ -545,6 +555,7 @@ __device__ __forceinline__ void chunk_store(const BwdArgs& a, const BucketDev& b
 template <int WD, int VEC, int NC, bool NT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NC == 1 ? 5 : 1)))
 void bwd_medium_kernel(BwdArgs a, BucketSet S) {
+  if (prep_failed(a)) return;
   BucketDev bk;
   uint32_t bucket, lb, lg;
   set_pick(S, bk, bucket, lb, lg);
@@ -599,6 +610,7 @@ __device__ __forceinline__ void chunk_walk(uint32_t lb, uint32_t lg, uint32_t be
 constexpr uint32_t kChunkBins = 256;
 
 __global__ __launch_bounds__(kThreads) void chunk_order_kernel(BwdArgs a) {
+  if (prep_failed(a)) return;
   __shared__ uint32_t hist[kChunkBins];
   __shared__ uint32_t sh4[4];
   const uint32_t t = blockIdx.x >> 3, x = blockIdx.x & 7u;
@@ -653,6 +665,7 @@ __global__ __launch_bounds__(kThreads) void chunk_order_kernel(BwdArgs a) {
 
 template <int WD, int VEC, int NC, int IF>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a, BucketSet S) {
+  if (prep_failed(a)) return;
   BucketDev bk;
   uint32_t bucket, lb, lg;
   set_pick(S, bk, bucket, lb, lg);
@@ -674,6 +687,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a, BucketSe
 
 template <int WD, int VEC, int NC, bool NT>
 __global__ __launch_bounds__(kThreads) void bwd_long_update_kernel(BwdArgs a, BucketSet S) {
+  if (prep_failed(a)) return;
   BucketDev bk;
   uint32_t bucket, lb, lg;
   set_pick(S, bk, bucket, lb, lg);
@@ -701,6 +715,7 @@ __global__ __launch_bounds__(kThreads) void bwd_long_update_kernel(BwdArgs a, Bu
 // serve to publish ordinary cached stores; none is published here.
 template <int WD, int VEC, int NC, int IF, bool NT>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_fused_kernel(BwdArgs a, BucketSet S) {
+  if (prep_failed(a)) return;
   BucketDev bk;
   uint32_t bucket, lb, lg;
   set_pick(S, bk, bucket, lb, lg);
@@ -774,7 +789,7 @@ uint32_t set_grid(BucketSet& S, const BwdGrids* g, uint32_t BwdGrids::*field, ui
 // lookups 40.0 -> 34.6 / 21.5 -> 18.4; 17 M lookups 292 -> 233 / 578 -> 463;
 // 138 M lookups 2408 -> 2545 / 3685 -> 3848.  Medium runs gather with four
 // always (at the same three sizes: 24.8 -> 20.5, 179 -> 146, 1449 -> 1189).
-constexpr uint32_t kBwdDeepLookups = 64u << 20;
+// The split is at kBwdDeepLookups (tbe_common.h).
 
 // Single-lookup runs of a deep batch: the persistent grid at half the
 // resident workgroups.  The workgroups sweep the row-sorted list together, so
@@ -842,22 +857,22 @@ void launch_classes(const BwdArgs& a, BucketSet S, const BwdGrids* g, bool fused
 }
 
 // Weight rows of the backward read and rewritten with non-temporal accesses
-// from this many lookups on: each touched row is read and written once per
+// from kBwdStreamRowsLookups lookups on (tbe_common.h): each touched row is read and written once per
 // step, and as ordinary accesses those lines push the grad_out rows that the
 // gathers reuse out of the caches.  Measured on MI355X (ms per step, plain /
 // non-temporal): 138 M lookups 17.01 / 16.52 (single-lookup runs 3288 ->
 // 2842 us), 17 M 2.204 / 2.176, but 2.1 M 0.338 / 0.339: there the next
 // forward re-reads the hot rows the backward wrote (forward 36.5 -> 42.3 us),
 // which non-temporal stores leave out of the caches.
-constexpr uint32_t kBwdStreamRowsLookups = 8u << 20;
 
 template <int WD, int VEC, int NC>
 hipError_t launch(const BwdArgs& a, BucketSet S, const BwdGrids* g, bool fused, int cus,
                   const hipStream_t* ss) {
   static_assert(kBwdDeepLookups >= kBwdStreamRowsLookups, "deep batches stream their rows");
-  if (a.N >= kBwdDeepLookups)
+  // (test knobs can move both thresholds; the deep variant always streams)
+  if ((int64_t)a.N >= knob_bwd_deep_lookups())
     launch_classes<WD, VEC, NC, kInFlightDeep, true>(a, S, g, fused, cus, ss);
-  else if (a.N >= kBwdStreamRowsLookups)
+  else if ((int64_t)a.N >= knob_bwd_stream_lookups())
     launch_classes<WD, VEC, NC, kInFlightShallow, true>(a, S, g, fused, cus, ss);
   else
     launch_classes<WD, VEC, NC, kInFlightShallow, false>(a, S, g, fused, cus, ss);

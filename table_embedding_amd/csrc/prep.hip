@@ -50,8 +50,11 @@
 // it meets an inclusive prefix, then publishes its own inclusive prefix.  The
 // status words are read and written with relaxed device-scope atomics; they
 // carry the counts themselves, so no other memory needs ordering.  A wait is
-// bounded: past kSpinLimit polls it sets the error flag and goes on, which
-// spoils the result but lets the kernel finish.
+// bounded: past `polls` polls (kSpinLimit unless a test knob lowers it) it
+// sets the error flag and goes on, which spoils the result but lets the
+// kernel finish; every backward kernel reads the flag first and writes
+// nothing when it is set.  With a limit of 0 a tile that has predecessors
+// gives up before its first poll.
 #include "tbe_common.h"
 
 namespace tbe {
@@ -63,7 +66,6 @@ constexpr int kClsItems = kClsTile / kThreads;  // 4 runs per thread
 constexpr uint64_t kStAgg = 1ull << 62;  // the tile's own count is published
 constexpr uint64_t kStPre = 2ull << 62;  // the inclusive prefix through the tile is published
 constexpr uint64_t kStFlags = 3ull << 62;
-constexpr uint32_t kSpinLimit = 1u << 20;
 
 struct PrepDev {
   const TableDev* tables;
@@ -95,7 +97,7 @@ __device__ __forceinline__ uint64_t st_read(uint64_t* p) {
 // passes at C5's ~10k tiles.)
 template <int GL>
 __device__ uint32_t look_back(uint64_t* st, uint32_t tile, uint32_t stride, uint32_t col,
-                              uint32_t* err) {
+                              uint32_t* err, uint32_t polls) {
   static_assert(GL == 16 || GL == 32 || GL == 64, "groups of 16, 32 or 64 lanes");
   const uint32_t lane = lane_id();
   const uint32_t i = lane & (GL - 1), base = lane & ~(uint32_t)(GL - 1);
@@ -103,6 +105,10 @@ __device__ uint32_t look_back(uint64_t* st, uint32_t tile, uint32_t stride, uint
   uint32_t excl = 0, spins = 0;
   uint32_t t = tile;  // tiles [0, t) are still to be summed (uniform in the group)
   bool fin = t == 0;
+  if (!fin && polls == 0u) {  // no poll allowed: give up at once
+    if (i == 0) atomicOr(err, 1u);
+    fin = true;
+  }
   while (__ballot(!fin)) {
     const bool have = !fin && t > i;
     const uint64_t v = have ? st_read(st + (size_t)(t - 1 - i) * stride + col) : 0ull;
@@ -127,7 +133,7 @@ __device__ uint32_t look_back(uint64_t* st, uint32_t tile, uint32_t stride, uint
       if (done) {
         fin = true;
       } else if (used == 0u) {  // the nearest predecessor has not published yet
-        if (++spins >= kSpinLimit) {
+        if (++spins >= polls) {
           if (i == 0) atomicOr(err, 1u);
           fin = true;
         }
@@ -144,7 +150,8 @@ __device__ uint32_t look_back(uint64_t* st, uint32_t tile, uint32_t stride, uint
 template <int GL>
 __device__ __forceinline__ uint32_t publish_and_look_back(uint64_t* st, uint32_t tile,
                                                           uint32_t stride, uint32_t col,
-                                                          uint32_t count, uint32_t* err) {
+                                                          uint32_t count, uint32_t* err,
+                                                          uint32_t polls) {
   uint64_t* mine = st + (size_t)tile * stride + col;
   const bool first = (lane_id() & (GL - 1)) == 0;
   if (tile == 0) {
@@ -152,7 +159,7 @@ __device__ __forceinline__ uint32_t publish_and_look_back(uint64_t* st, uint32_t
     return 0;
   }
   if (first) st_publish(mine, kStAgg | count);
-  const uint32_t excl = look_back<GL>(st, tile, stride, col, err);
+  const uint32_t excl = look_back<GL>(st, tile, stride, col, err, polls);
   if (first) st_publish(mine, kStPre | (uint64_t)(uint32_t)(excl + count));
   return excl;
 }
@@ -687,7 +694,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                                                        uint64_t* st, uint32_t* err,
                                                        uint32_t* __restrict__ counters,
                                                        uint32_t* __restrict__ run_start,
-                                                       uint32_t* __restrict__ run_key) {
+                                                       uint32_t* __restrict__ run_key,
+                                                       uint32_t polls) {
   __shared__ uint32_t sh4[4];
   __shared__ uint32_t s_tile, s_excl;
   __shared__ uint32_t s_rs[kTile], s_rk[kTile];  // one group's run heads, staged
@@ -721,7 +729,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   }
   gbase[G] = total;
   if (threadIdx.x < (uint32_t)kWave) {  // wave 0
-    const uint32_t excl = publish_and_look_back<64>(st, tile, 1, 0, total, err);
+    const uint32_t excl = publish_and_look_back<64>(st, tile, 1, 0, total, err, polls);
     if (threadIdx.x == 0) {
       s_excl = excl;
       if (tile == ntiles - 1) {
@@ -784,6 +792,7 @@ struct ClsDev {
   const uint32_t* bkb;       // nb+1 bucket key bounds
   uint32_t T, nb;
   uint32_t N, max_tiny, max_med, max_long, max_chunks;  // list capacities
+  uint32_t polls;            // look-back poll limit
 };
 
 // per-run counts of the five lists: SL = 1, 2 <= SL < 32, 32 <= SL < 256,
@@ -895,10 +904,12 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClsDev a) {
     const uint32_t w = threadIdx.x / kWave;
     if (w == 0) {
       const uint32_t q = lane_id() / 16u;
-      const uint32_t e = publish_and_look_back<16>(a.st, tile, kClsStride, q, s_tot[q], a.err);
+      const uint32_t e = publish_and_look_back<16>(a.st, tile, kClsStride, q, s_tot[q], a.err,
+                                                    a.polls);
       if ((lane_id() & 15u) == 0) s_excl[q] = e;
     } else if (w == 1) {
-      const uint32_t e = publish_and_look_back<64>(a.st, tile, kClsStride, 4, s_tot[4], a.err);
+      const uint32_t e = publish_and_look_back<64>(a.st, tile, kClsStride, 4, s_tot[4], a.err,
+                                                    a.polls);
       if (lane_id() == 0) s_excl[4] = e;
     }
   }
@@ -1076,6 +1087,7 @@ hipError_t launch_preprocess(const PrepArgs& p, int /*num_cus*/, hipStream_t s) 
   uint32_t* ctl = u32p(L.ctl);
   uint32_t* err = ctl + kCtlErr;
   const bool sc = p.need_scale != 0;
+  const uint32_t polls = knob_wait_polls();
 
   uint4* seg = reinterpret_cast<uint4*>(ws + L.seg);
   uint32_t* tile_seg = u32p(L.tile_seg);
@@ -1116,11 +1128,11 @@ hipError_t launch_preprocess(const PrepArgs& p, int /*num_cus*/, hipStream_t s) 
   if (L.rle_groups == (uint32_t)kRleGroupsDeep)
     TBE_LAUNCH("rle", rle_kernel<kRleGroupsDeep>, dim3(L.nrle_tiles), dim3(kThreads), s, skey, p.N, L.nrle_tiles,
              ctl + kCtlRleTickets, u64p(L.st_rle), err, u32p(L.counters),
-             u32p(L.run_start), u32p(L.run_key));
+             u32p(L.run_start), u32p(L.run_key), polls);
   else
     TBE_LAUNCH("rle", rle_kernel<1>, dim3(L.nrle_tiles), dim3(kThreads), s, skey, p.N, L.nrle_tiles,
              ctl + kCtlRleTickets, u64p(L.st_rle), err, u32p(L.counters),
-             u32p(L.run_start), u32p(L.run_key));
+             u32p(L.run_start), u32p(L.run_key), polls);
 
   ClsDev c{u32p(L.run_start), u32p(L.run_key), sbag, u32p(L.counters),
            ctl + kCtlClsTickets, u64p(L.st_cls), err,
@@ -1128,7 +1140,7 @@ hipError_t launch_preprocess(const PrepArgs& p, int /*num_cus*/, hipStream_t s) 
            reinterpret_cast<uint4*>(ws + L.med_task),
            reinterpret_cast<uint4*>(ws + L.long_task), u32p(L.long_cbeg), u32p(L.remaining),
            reinterpret_cast<uint4*>(ws + L.chunk_task), p.tables, p.order, p.bucket_key_begin,
-           p.T, p.nb, p.N, L.max_tiny, L.max_med, L.max_long, L.max_chunks};
+           p.T, p.nb, p.N, L.max_tiny, L.max_med, L.max_long, L.max_chunks, polls};
   TBE_LAUNCH_SHM("classify", classify_kernel, dim3(L.ncls_tiles), dim3(kThreads),
                  2 * sizeof(uint32_t) * (size_t)p.T, s, c);
   return hipGetLastError();

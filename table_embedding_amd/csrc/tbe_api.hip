@@ -90,7 +90,7 @@ WsLayout layout(const tbe_plan* P, int64_t N) {
   WsLayout L{};
   const uint64_t n = (uint64_t)N;
   L.ntiles = (uint32_t)((n + kTile - 1) / kTile);
-  L.rle_groups = N >= kRleDeepLookups ? (uint32_t)kRleGroupsDeep : 1u;
+  L.rle_groups = N >= knob_rle_deep_lookups() ? (uint32_t)kRleGroupsDeep : 1u;
   L.nrle_tiles = (uint32_t)((n + (uint64_t)L.rle_groups * kTile - 1) / ((uint64_t)L.rle_groups * kTile));
   L.ncls_tiles = (uint32_t)((n + kClsTile - 1) / kClsTile);
   L.max_tiny = (uint32_t)(n / 2 + 1);
@@ -296,6 +296,24 @@ hipEvent_t prof_event() {
 
 namespace tbe {
 
+namespace {
+// test knob overrides; a negative value means "not set"
+std::atomic<int64_t> g_knob_rle_deep{-1}, g_knob_bwd_deep{-1}, g_knob_bwd_stream{-1},
+    g_knob_polls{-1};
+int64_t knob_or(const std::atomic<int64_t>& k, int64_t dflt) {
+  const int64_t v = k.load(std::memory_order_relaxed);
+  return v < 0 ? dflt : v;
+}
+}  // namespace
+
+int64_t knob_rle_deep_lookups() { return knob_or(g_knob_rle_deep, kRleDeepLookups); }
+int64_t knob_bwd_deep_lookups() { return knob_or(g_knob_bwd_deep, kBwdDeepLookups); }
+int64_t knob_bwd_stream_lookups() { return knob_or(g_knob_bwd_stream, kBwdStreamRowsLookups); }
+uint32_t knob_wait_polls() {
+  const int64_t v = knob_or(g_knob_polls, kSpinLimit);
+  return v > (int64_t)0xffffffffll ? 0xffffffffu : (uint32_t)v;
+}
+
 bool prof_events(const char* name, hipEvent_t* start, hipEvent_t* stop) {
   if (!g_prof_on.load(std::memory_order_relaxed)) return false;
   std::lock_guard<std::mutex> lk(g_prof_mu);
@@ -310,6 +328,19 @@ bool prof_events(const char* name, hipEvent_t* start, hipEvent_t* stop) {
 }  // namespace tbe
 
 extern "C" {
+
+int tbe_test_knob(int32_t knob, int64_t value) {
+  std::atomic<int64_t>* k = nullptr;
+  switch (knob) {
+    case TBE_KNOB_RLE_DEEP_LOOKUPS: k = &tbe::g_knob_rle_deep; break;
+    case TBE_KNOB_BWD_DEEP_LOOKUPS: k = &tbe::g_knob_bwd_deep; break;
+    case TBE_KNOB_BWD_STREAM_LOOKUPS: k = &tbe::g_knob_bwd_stream; break;
+    case TBE_KNOB_WAIT_POLLS: k = &tbe::g_knob_polls; break;
+    default: return TBE_E_ARG;
+  }
+  k->store(value < 0 ? -1 : value, std::memory_order_relaxed);
+  return TBE_OK;
+}
 
 int tbe_prof_enable(int enable) {
   g_prof_on.store(enable != 0);
@@ -506,12 +537,6 @@ int tbe_plan_create(tbe_plan** out, int32_t T, const int64_t* rows, const int32_
   ok = ok && hipGetDevice(&dev) == hipSuccess &&
        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess;
   P->num_cus = cus > 0 ? cus : 256;
-  P->side[0] = P->side[1] = nullptr;
-  P->ev_fork = P->ev_join[0] = P->ev_join[1] = nullptr;
-  for (int i = 0; i < 2 && ok; ++i)
-    ok = hipStreamCreateWithFlags(&P->side[i], hipStreamNonBlocking) == hipSuccess &&
-         hipEventCreateWithFlags(&P->ev_join[i], hipEventDisableTiming) == hipSuccess;
-  ok = ok && hipEventCreateWithFlags(&P->ev_fork, hipEventDisableTiming) == hipSuccess;
   if (!ok) {
     (void)tbe_plan_destroy(P);
     return TBE_E_HIP;
@@ -690,19 +715,22 @@ int tbe_preprocess(const tbe_plan* P, int64_t B, int32_t itype, const void* indi
   return e == hipSuccess ? TBE_OK : TBE_E_HIP;
 }
 
-int tbe_backward(const tbe_plan* P, int64_t B, int32_t itype, const void* indices,
-                 const void* offsets, int64_t N, const float* psw, const float* grad_out,
-                 int32_t optimizer, float lr, float eps, void* ws, size_t ws_bytes,
-                 uint32_t flags, uint32_t* debug_row_updates, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Arguments of the backward entry points other than the workspace (TBE_OK or
+// the error code).
+int check_backward(const tbe_plan* P, int64_t B, int32_t itype, const void* indices,
+                   const void* offsets, int64_t N, const float* psw, const float* grad_out,
+                   int32_t optimizer, uint32_t flags, const uint32_t* debug_row_updates) {
   static_assert(OPT_ROWWISE_ADAGRAD == TBE_OPT_ROWWISE_ADAGRAD && OPT_ADAGRAD == TBE_OPT_ADAGRAD &&
                     OPT_SGD == TBE_OPT_SGD,
                 "optimizer codes of the header");
   if (optimizer != TBE_OPT_ROWWISE_ADAGRAD && optimizer != TBE_OPT_ADAGRAD &&
       optimizer != TBE_OPT_SGD)
     return TBE_E_ARG;
-  int rc = check_lookups(P, B, itype, indices, offsets, N);
-  if (rc) return rc;
-  rc = check_ws(P, N, ws, ws_bytes);
+  const int rc = check_lookups(P, B, itype, indices, offsets, N);
   if (rc) return rc;
   if (flags & ~(TBE_BWD_PREPROCESSED | TBE_BWD_FUSED_LONG | TBE_BWD_CONCURRENT |
                 TBE_BWD_ORDER_CHUNKS | TBE_BWD_NO_ORDER_CHUNKS | TBE_BWD_HIST |
@@ -714,6 +742,15 @@ int tbe_backward(const tbe_plan* P, int64_t B, int32_t itype, const void* indice
   if (B > 0 && (!grad_out || !aligned(grad_out, 16))) return TBE_E_ARG;
   if (psw && !aligned(psw, 4)) return TBE_E_ARG;
   if (debug_row_updates && !aligned(debug_row_updates, 4)) return TBE_E_ARG;
+  return TBE_OK;
+}
+
+// The backward's launches on `stream` into the workspace ws (arguments and
+// workspace already checked).
+int run_backward(const tbe_plan* P, int64_t B, int32_t itype, const void* indices,
+                 const void* offsets, int64_t N, const float* psw, const float* grad_out,
+                 int32_t optimizer, float lr, float eps, void* ws, uint32_t flags,
+                 uint32_t* debug_row_updates, void* stream) {
   if (N == 0) return TBE_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const WsLayout L = layout(P, N);
@@ -778,6 +815,7 @@ int tbe_backward(const tbe_plan* P, int64_t B, int32_t itype, const void* indice
   a.counters = reinterpret_cast<const uint32_t*>(w + L.counters);
   a.nb = (uint32_t)P->buckets.size();
   a.debug_count = debug_row_updates;
+  a.prep_err = reinterpret_cast<const uint32_t*>(w + L.ctl) + kCtlErr;
   a.N = (uint32_t)N;
   a.T = (uint32_t)P->T;
   a.max_single = (uint32_t)N;
@@ -827,6 +865,23 @@ int tbe_backward(const tbe_plan* P, int64_t B, int32_t itype, const void* indice
         rc_launch = TBE_E_HIP;
   }
   return rc_launch;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tbe_backward(const tbe_plan* P, int64_t B, int32_t itype, const void* indices,
+                 const void* offsets, int64_t N, const float* psw, const float* grad_out,
+                 int32_t optimizer, float lr, float eps, void* ws, size_t ws_bytes,
+                 uint32_t flags, uint32_t* debug_row_updates, void* stream) {
+  int rc = check_backward(P, B, itype, indices, offsets, N, psw, grad_out, optimizer, flags,
+                          debug_row_updates);
+  if (rc) return rc;
+  rc = check_ws(P, N, ws, ws_bytes);
+  if (rc) return rc;
+  return run_backward(P, B, itype, indices, offsets, N, psw, grad_out, optimizer, lr, eps, ws,
+                      flags, debug_row_updates, stream);
 }
 
 int tbe_backward_rowwise_adagrad(const tbe_plan* P, int64_t B, int32_t itype,

@@ -20,6 +20,23 @@ constexpr int kClsTile = 2048;      // runs per workgroup in the classification 
 // lookups 17.0 / 11.1 us, 17 M 51.3 / 46.8 us.
 constexpr int kRleGroupsDeep = 4;
 constexpr int64_t kRleDeepLookups = 64ll << 20;
+// Lookup counts from which the backward gathers keep eight lookups in flight
+// and streams its weight rows past the caches (see bwd.hip for the
+// measurements behind both).
+constexpr int64_t kBwdDeepLookups = 64ll << 20;
+constexpr int64_t kBwdStreamRowsLookups = 8ll << 20;
+// Polls after which a look-back wait of the preprocessing gives up.
+constexpr uint32_t kSpinLimit = 1u << 20;
+
+// Test knobs (tbe_test_knob): process-wide overrides of the thresholds above
+// and of the poll limit, so that small inputs can run the variants that
+// deep batches take.  Each accessor returns the override if one is set,
+// else the default.
+int64_t knob_rle_deep_lookups();
+int64_t knob_bwd_deep_lookups();
+int64_t knob_bwd_stream_lookups();
+uint32_t knob_wait_polls();
+
 constexpr int kLongRun = 256;       // SL >= 256 takes the chunked long-run path
 constexpr int kTinyRun = 32;        // short runs below this are owned by a lane subgroup
 constexpr int kChunk = 256;         // lookups per long-run chunk
@@ -486,6 +503,7 @@ struct BwdArgs {
   const uint32_t* counters;
   uint32_t nb;
   uint32_t* debug_count;     // nullable, per linear key
+  const uint32_t* prep_err;  // the preprocessing's error flag: nonzero, nothing is written
   uint32_t N, T;             // lookups and tables (task sanity bounds)
   uint32_t max_single, max_tiny, max_med, max_long, max_chunks;  // list capacities
 };

@@ -1,0 +1,104 @@
+"""The variants the library picks for deep batches (64 Mi lookups and more:
+run-length tiles of four 4096-key groups, backward gathers with eight
+lookups in flight, non-temporal weight rows; 8 Mi and more: non-temporal rows
+alone), run at scaled sizes through the test knobs and compared with the
+oracle like every other case: integer outputs of the preprocessing bit for
+bit, weights and momentum within tolerance, fused = two-launch bit for bit.
+
+Also the contract of a look-back wait that gives up: with the poll limit
+forced to 0 from the host (every kernel still exits normally), the
+preprocessing flags its error word and the backward writes nothing."""
+import contextlib
+
+import numpy as np
+import pytest
+import torch
+
+from tests import support as S
+from tests.test_gpu_parity import _announce, _spec, _tables_bytes
+
+pytestmark = pytest.mark.gpu
+
+
+@contextlib.contextmanager
+def knobs(**kv):
+    import table_embedding_amd as te
+    names = {"rle_deep": te.TBE_KNOB_RLE_DEEP_LOOKUPS, "bwd_deep": te.TBE_KNOB_BWD_DEEP_LOOKUPS,
+             "bwd_stream": te.TBE_KNOB_BWD_STREAM_LOOKUPS, "polls": te.TBE_KNOB_WAIT_POLLS}
+    try:
+        for k, v in kv.items():
+            te.tbe_test_knob(names[k], v)
+        yield
+    finally:
+        for k in names.values():
+            te.tbe_test_knob(k, -1)
+
+
+DEEP = ["C2s", "C3s", "C5s", "many_tables", "const257", "heavy_chunks", "wide_f32", "cut_bags"]
+
+
+@pytest.mark.parametrize("variant", ["deep", "stream"])
+@pytest.mark.parametrize("name", DEEP)
+def test_deep_batch_variants_parity(name, variant):
+    import table_embedding_amd as te
+    _announce(name, f"{variant} variants")
+    kv = dict(rle_deep=0, bwd_deep=0) if variant == "deep" else dict(bwd_stream=0)
+    case = S.Case(_spec(name), m_nonzero=True)
+    with knobs(**kv):
+        tb = case.tbe()
+        tb.preprocess(case.spec.B, case.d_idx, case.d_off, case.d_psw)
+        torch.cuda.synchronize()
+        S.check_preprocess(case, tb)
+        tb.close()
+        res = []
+        for flags in (0, te.TBE_BWD_FUSED_LONG):
+            case.reset_tables()
+            tb = case.tbe()
+            tb.backward(case.spec.B, case.d_idx, case.d_off, case.d_psw, case.d_G,
+                        case.spec.lr, case.spec.eps, flags=flags)
+            torch.cuda.synchronize()
+            if flags == 0:
+                S.check_backward(case, tb)
+            res.append(_tables_bytes(tb, case.spec.wdtype))
+            tb.close()
+        assert res[0] == res[1], "fused differs from two-launch"
+
+
+@pytest.mark.parametrize("name", ["C2s", "C3s", "C5s"])
+def test_wait_give_up_writes_nothing(name):
+    """Poll limit 0: every tile with predecessors gives up its look-back at
+    once; prep_error is set and neither the self-preprocessing backward nor
+    one on the preprocessed workspace writes a weight, a momentum or a debug
+    counter.  With the default limit restored the same inputs give the oracle's
+    result."""
+    import table_embedding_amd as te
+    _announce(name, "look-back give-up")
+    case = S.Case(_spec(name), m_nonzero=True)
+    spec = case.spec
+    assert case.N > 4096, "needs more than one run-length tile"
+    W0 = [w.tobytes() for w in case.W]
+    M0 = [m.tobytes() for m in case.M]
+    with knobs(polls=0):
+        for flags in (0, te.TBE_BWD_FUSED_LONG, te.TBE_BWD_PREPROCESSED):
+            case.reset_tables()
+            tb = case.tbe()
+            if flags & te.TBE_BWD_PREPROCESSED:
+                tb.preprocess(spec.B, case.d_idx, case.d_off, case.d_psw)
+            dbg = torch.zeros(sum(spec.rows), dtype=torch.uint32, device="cuda")
+            tb.backward(spec.B, case.d_idx, case.d_off, case.d_psw, case.d_G, spec.lr, spec.eps,
+                        flags=flags, debug_row_updates=dbg)
+            torch.cuda.synchronize()
+            v = te.tbe_workspace_views(tb.plan, spec.B, case.N)
+            assert int(S.read_u32(tb._ws, v["prep_error"], 1)[0]) != 0, "no give-up flagged"
+            assert [S.to_host_storage(w, spec.wdtype).tobytes() for w in tb.weights] == W0
+            assert [m.cpu().numpy().tobytes() for m in tb.momentum] == M0
+            assert not dbg.cpu().numpy().any()
+            tb.close()
+    case.reset_tables()
+    tb = case.tbe()
+    tb.backward(spec.B, case.d_idx, case.d_off, case.d_psw, case.d_G, spec.lr, spec.eps)
+    torch.cuda.synchronize()
+    v = te.tbe_workspace_views(tb.plan, spec.B, case.N)
+    assert int(S.read_u32(tb._ws, v["prep_error"], 1)[0]) == 0
+    S.check_backward(case, tb)
+    tb.close()

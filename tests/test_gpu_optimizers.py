@@ -56,7 +56,7 @@ def _run(case, optimizer, flags=0):
     d_W = [S.from_host_storage(w, spec.wdtype) for w in case.W]
     d_A = [torch.from_numpy(a.copy()).cuda() for a in A0]
     tb = te.TBE(spec.rows, spec.dims, spec.pooling, d_W, d_A)
-    dbg = torch.zeros(sum(spec.rows), dtype=torch.int32, device="cuda")
+    dbg = torch.zeros(sum(spec.rows), dtype=torch.uint32, device="cuda")
     code = {"adagrad": te.TBE_OPT_ADAGRAD, "sgd": te.TBE_OPT_SGD}[optimizer]
     tb.backward(spec.B, case.d_idx, case.d_off, case.d_psw, case.d_G, spec.lr, spec.eps,
                 flags=flags, debug_row_updates=dbg, optimizer=code)

@@ -183,7 +183,7 @@ def test_every_touched_row_updated_once(name):
     case = S.Case(_spec(name))
     tb = case.tbe()
     nkeys = sum(case.spec.rows)
-    cnt = torch.zeros(nkeys, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(nkeys, dtype=torch.uint32, device="cuda")
     tb.backward(case.spec.B, case.d_idx, case.d_off, case.d_psw, case.d_G, case.spec.lr,
                 case.spec.eps, debug_row_updates=cnt)
     torch.cuda.synchronize()
@@ -418,7 +418,7 @@ def test_backward_hist_parity(name):
     for rep in range(2):
         case.reset_tables()
         tb = case.tbe()
-        dbg = torch.zeros(sum(case.spec.rows), dtype=torch.int32, device="cuda")
+        dbg = torch.zeros(sum(case.spec.rows), dtype=torch.uint32, device="cuda")
         tb.backward(case.spec.B, case.d_idx, case.d_off, case.d_psw, case.d_G, case.spec.lr,
                     case.spec.eps, flags=te.TBE_BWD_HIST, debug_row_updates=dbg)
         torch.cuda.synchronize()
