@@ -68,6 +68,7 @@ extern "C" {
 #define TBE_E_RANGE (-4)        /* int32 indices with num_lookups or sum R_t >= 2^31; sizes >= 2^32 */
 #define TBE_E_HIP (-5)          /* the HIP runtime reported an error */
 #define TBE_E_ALLOC (-6)        /* plan creation could not allocate */
+#define TBE_E_TOO_LARGE (-7)    /* batch too large for the library's static workspace */
 
 /* weight storage types */
 #define TBE_F32 0
@@ -251,6 +252,30 @@ int tbe_backward_rowwise_adagrad(const tbe_plan* plan, int64_t B, int32_t itype,
                                  const float* per_sample_weights, const float* grad_out, float lr,
                                  float eps, void* ws, size_t ws_bytes, uint32_t flags,
                                  uint32_t* debug_row_updates, void* stream);
+
+/* tbe_backward_rowwise_adagrad for callers that cannot allocate device
+ * memory or hand in a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same preprocessing and
+ * kernels, with the workspace in a static device array of the library
+ * (TBE_STATIC_WS_BYTES per device, held from the first plan created on the
+ * device until the process ends).  The call allocates nothing and calls no
+ * allocating routine; the caller still passes every input and output.
+ * Arguments as tbe_backward_rowwise_adagrad without ws and ws_bytes; the
+ * current device must be the plan's.  Every call on a device shares that
+ * device's array and leaves its contents behind (the kernels set up all they
+ * read), so calls that overlap on one device (other streams, other plans,
+ * other threads) race and must not be issued.  Errors: those of
+ * tbe_backward_rowwise_adagrad; TBE_E_ARG with TBE_BWD_PREPROCESSED (no
+ * preprocessing result can be handed in); TBE_E_TOO_LARGE when the batch
+ * needs more than TBE_STATIC_WS_BYTES of workspace (tbe_workspace_size);
+ * TBE_E_HIP if the array's address cannot be resolved. */
+#define TBE_STATIC_WS_BYTES (256ull << 20)
+int tbe_backward_rowwise_adagrad_noalloc(const tbe_plan* plan, int64_t B, int32_t itype,
+                                         const void* indices, const void* offsets,
+                                         int64_t num_lookups, const float* per_sample_weights,
+                                         const float* grad_out, float lr, float eps,
+                                         uint32_t flags, uint32_t* debug_row_updates,
+                                         void* stream);
 
 /* Backward with a choice of optimizer epilogue: the same preprocessing and
  * run pipeline as tbe_backward_rowwise_adagrad (which is this call with

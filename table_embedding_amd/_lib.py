@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libtbe_hip.so")
 # include/tbe.h constants
 TBE_OK, TBE_E_ARG, TBE_E_UNSUPPORTED, TBE_E_WORKSPACE, TBE_E_RANGE, TBE_E_HIP, TBE_E_ALLOC = (
     0, -1, -2, -3, -4, -5, -6)
+TBE_E_TOO_LARGE = -7
+TBE_STATIC_WS_BYTES = 256 << 20
 TBE_F32, TBE_F16, TBE_BF16 = 0, 1, 2
 TBE_I32, TBE_I64 = 0, 1
 TBE_SUM, TBE_MEAN = 0, 1
@@ -31,7 +33,8 @@ TBE_BWD_CONCURRENT_AUTO = 0x40
 
 EXPORTS = ("tbe_plan_create", "tbe_plan_destroy", "tbe_plan_key_bases", "tbe_workspace_size",
            "tbe_workspace_views", "tbe_forward", "tbe_forward_preprocess", "tbe_preprocess",
-           "tbe_backward_rowwise_adagrad", "tbe_backward", "tbe_validate", "tbe_prof_enable",
+           "tbe_backward_rowwise_adagrad", "tbe_backward_rowwise_adagrad_noalloc",
+           "tbe_backward", "tbe_validate", "tbe_prof_enable",
            "tbe_prof_read", "tbe_prof_calibrate", "tbe_test_knob", "tbe_status_string")
 TBE_PROF_NAME_LEN = 32
 
@@ -81,6 +84,8 @@ def lib() -> C.CDLL:
         L.tbe_backward_rowwise_adagrad.argtypes = [vp, i64, i32, vp, vp, i64, vp, vp,
                                                    C.c_float, C.c_float, vp, C.c_size_t, u32,
                                                    vp, vp]
+        L.tbe_backward_rowwise_adagrad_noalloc.argtypes = [vp, i64, i32, vp, vp, i64, vp, vp,
+                                                           C.c_float, C.c_float, u32, vp, vp]
         L.tbe_validate.argtypes = [vp, i64, i32, vp, vp, i64, vp, u32, vp]
         L.tbe_backward.argtypes = [vp, i64, i32, vp, vp, i64, vp, vp, i32, C.c_float, C.c_float,
                                    vp, C.c_size_t, u32, vp, vp]
@@ -255,6 +260,22 @@ def tbe_backward_rowwise_adagrad(plan, B: int, indices, offsets, num_lookups: in
         _dptr(ws, None, "ws"), ws.numel() * ws.element_size(), int(flags),
         _dptr(debug_row_updates, _U32, "debug_row_updates"), _stream(stream))
     _check("tbe_backward_rowwise_adagrad", rc)
+
+
+def tbe_backward_rowwise_adagrad_noalloc(plan, B: int, indices, offsets, num_lookups: int,
+                                         per_sample_weights, grad_out: torch.Tensor, lr: float,
+                                         eps: float, flags: int = 0,
+                                         debug_row_updates: Optional[torch.Tensor] = None,
+                                         stream=None) -> None:
+    """tbe_backward_rowwise_adagrad with the library's static workspace (no
+    workspace argument; the call allocates nothing)."""
+    it = _itype(indices, offsets)
+    rc = lib().tbe_backward_rowwise_adagrad_noalloc(
+        plan, int(B), it, _dptr(indices, None, "indices"), _dptr(offsets, None, "offsets"),
+        int(num_lookups), _dptr(per_sample_weights, torch.float32, "per_sample_weights"),
+        _dptr(grad_out, torch.float32, "grad_out"), float(lr), float(eps), int(flags),
+        _dptr(debug_row_updates, _U32, "debug_row_updates"), _stream(stream))
+    _check("tbe_backward_rowwise_adagrad_noalloc", rc)
 
 
 TBE_OPT_ROWWISE_ADAGRAD, TBE_OPT_ADAGRAD, TBE_OPT_SGD = 0, 1, 2

@@ -15,7 +15,36 @@
 
 using namespace tbe;
 
+// Static workspace of tbe_backward_rowwise_adagrad_noalloc, for callers that
+// cannot allocate device memory.  One array per device, held from the
+// library's first plan on that device until the process ends; every call on a
+// device shares it.  In host code `scratch` only names the array: its device
+// address comes from hipGetSymbolAddress, once per device, at plan creation
+// (static_ws_of_current_device), and only that address is ever used.
+constexpr size_t kStaticWsBytes = 256ull << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticWsBytes];
+static_assert(kStaticWsBytes == TBE_STATIC_WS_BYTES, "static workspace size of the header");
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_static_ws_mu;
+void* g_static_ws[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device (resolved on the
+// first call for that device).
+int static_ws_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TBE_E_HIP;
+  std::lock_guard<std::mutex> lk(g_static_ws_mu);
+  if (!g_static_ws[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TBE_E_HIP;
+    g_static_ws[dev] = p;
+  }
+  *out = g_static_ws[dev];
+  return TBE_OK;
+}
 
 struct Bucket {
   uint32_t width;  // next_pow2(D) of its tables
@@ -402,6 +431,7 @@ const char* tbe_status_string(int s) {
     case TBE_E_RANGE: return "size or index range too large for the index type";
     case TBE_E_HIP: return "HIP runtime error";
     case TBE_E_ALLOC: return "allocation failed";
+    case TBE_E_TOO_LARGE: return "batch too large for the library's static workspace";
   }
   return "unknown status";
 }
@@ -537,6 +567,17 @@ int tbe_plan_create(tbe_plan** out, int32_t T, const int64_t* rows, const int32_
   ok = ok && hipGetDevice(&dev) == hipSuccess &&
        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess;
   P->num_cus = cus > 0 ? cus : 256;
+  {  // the static workspace's address on this device, so that the no-alloc
+     // backward never loads anything at call time
+    void* sw = nullptr;
+    ok = ok && static_ws_of_current_device(&sw) == TBE_OK;
+  }
+  P->side[0] = P->side[1] = nullptr;
+  P->ev_fork = P->ev_join[0] = P->ev_join[1] = nullptr;
+  for (int i = 0; i < 2 && ok; ++i)
+    ok = hipStreamCreateWithFlags(&P->side[i], hipStreamNonBlocking) == hipSuccess &&
+         hipEventCreateWithFlags(&P->ev_join[i], hipEventDisableTiming) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&P->ev_fork, hipEventDisableTiming) == hipSuccess;
   if (!ok) {
     (void)tbe_plan_destroy(P);
     return TBE_E_HIP;
@@ -882,6 +923,25 @@ int tbe_backward(const tbe_plan* P, int64_t B, int32_t itype, const void* indice
   if (rc) return rc;
   return run_backward(P, B, itype, indices, offsets, N, psw, grad_out, optimizer, lr, eps, ws,
                       flags, debug_row_updates, stream);
+}
+
+int tbe_backward_rowwise_adagrad_noalloc(const tbe_plan* P, int64_t B, int32_t itype,
+                                         const void* indices, const void* offsets, int64_t N,
+                                         const float* psw, const float* grad_out, float lr,
+                                         float eps, uint32_t flags,
+                                         uint32_t* debug_row_updates, void* stream) {
+  int rc = check_backward(P, B, itype, indices, offsets, N, psw, grad_out,
+                          TBE_OPT_ROWWISE_ADAGRAD, flags, debug_row_updates);
+  if (rc) return rc;
+  // no preprocessing result can be handed in: the static workspace is only
+  // written by this call
+  if (flags & TBE_BWD_PREPROCESSED) return TBE_E_ARG;
+  if (layout(P, N).total > kStaticWsBytes) return TBE_E_TOO_LARGE;
+  void* ws = nullptr;
+  rc = static_ws_of_current_device(&ws);
+  if (rc) return rc;
+  return run_backward(P, B, itype, indices, offsets, N, psw, grad_out, TBE_OPT_ROWWISE_ADAGRAD,
+                      lr, eps, ws, flags, debug_row_updates, stream);
 }
 
 int tbe_backward_rowwise_adagrad(const tbe_plan* P, int64_t B, int32_t itype,

@@ -47,7 +47,7 @@ def test_every_entry_point_has_declared_argument_types():
 def test_status_strings():
     import table_embedding_amd as te
     assert te.tbe_status_string(0) == "ok"
-    for code in range(-6, 0):
+    for code in range(-7, 0):
         assert te.tbe_status_string(code) not in ("ok", "unknown status")
 
 
