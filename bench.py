@@ -79,8 +79,14 @@ def parse():
                     help="headline step with the fused long-run countdown path")
     ap.add_argument("--validate", action="store_true",
                     help="run tbe_validate (check only) at the start of every step")
+    ap.add_argument("--checked", action="store_true",
+                    help="forward with the input checks fused in (tbe_forward_checked)")
     ap.add_argument("--bwd-hist", action="store_true",
                     help="histogram-reuse backward (one small table: C4), no preprocessing")
+    ap.add_argument("--hist-reuse", action="store_true",
+                    help="with --bwd-hist: the forward saves its row counts "
+                         "(tbe_forward_preprocess, TBE_FWD_SAVE_HIST) and the backward reads "
+                         "them instead of the indices")
     ap.add_argument("--schedule", default="serial", choices=["overlap", "fork", "auto", "serial"],
                     help="headline schedule. overlap: tbe_forward_preprocess (preprocessing on "
                          "a side stream during the forward), then the backward on the "
@@ -455,16 +461,23 @@ def main():
     err = torch.zeros(te.TBE_VALIDATE_WORDS, dtype=torch.int32, device="cuda")
     flush_buf = torch.empty(COLD_FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
 
+    err_u = torch.zeros(te.TBE_VALIDATE_WORDS, dtype=torch.uint32, device="cuda")
+    reuse = args.bwd_hist and args.hist_reuse
+
     def fwd(overlap):
         if args.validate:
             te.tbe_validate(tb.plan, B, d_idx, d_off, N, err)
-        if overlap:
+        if reuse:
+            tb.forward_and_preprocess(B, d_idx, d_off, psw, out, flags=te.TBE_FWD_SAVE_HIST)
+        elif overlap:
             tb.forward_and_preprocess(B, d_idx, d_off, psw, out)
+        elif args.checked:
+            te.tbe_forward_checked(tb.plan, B, d_idx, d_off, N, psw, out, err_u)
         else:
             te.tbe_forward(tb.plan, B, d_idx, d_off, N, psw, out)
 
     def bwd(flags, overlap):
-        f = flags | (te.TBE_BWD_PREPROCESSED if overlap else 0)
+        f = flags | (te.TBE_BWD_PREPROCESSED if (overlap or reuse) else 0)
         te.tbe_backward_rowwise_adagrad(tb.plan, B, d_idx, d_off, N, psw, G, spec.lr, spec.eps,
                                         ws, f)
 
@@ -569,8 +582,12 @@ def main():
                    "index_type": spec.itype, "long_run_path": "fused" if args.fused else
                    "two-launch", "schedule": args.schedule,
                    "cache": "warm" if args.warm else "cold (1 GiB scratch write before each step)",
-                   "backward": "histogram-reuse contraction" if args.bwd_hist else "run pipeline",
-                   "input_validation": bool(args.validate)},
+                   "backward": ("histogram contraction on the forward's saved counts" if reuse
+                                else "histogram contraction" if args.bwd_hist
+                                else "run pipeline"),
+                   "input_validation": ("separate pass (tbe_validate)" if args.validate
+                                        else "fused into the forward (tbe_forward_checked)"
+                                        if args.checked else "off")},
         "timing": {"mean_ms": round(head["mean_ms"], 5), "median_ms": round(head["median_ms"], 5),
                    "p10_ms": round(head["p10_ms"], 5), "p90_ms": round(head["p90_ms"], 5),
                    "fwd_ms": round(head["fwd_ms"], 5), "bwd_ms": round(head["bwd_ms"], 5),

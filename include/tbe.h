@@ -86,6 +86,8 @@ extern "C" {
 #define TBE_FWD_REQUIRE_HIST 0x2u  /* fail with TBE_E_UNSUPPORTED unless the histogram path applies */
 #define TBE_FWD_BALANCE 0x4u       /* generic path: split bag groups into equal pieces (default) */
 #define TBE_FWD_NO_BALANCE 0x8u    /* generic path: one whole bag per lane subgroup */
+#define TBE_FWD_SAVE_HIST 0x10u    /* tbe_forward_preprocess only: keep the histogram path's row
+                                      counts for TBE_BWD_HIST (see there) */
 /* tbe_backward_rowwise_adagrad flags */
 #define TBE_BWD_PREPROCESSED 0x1u  /* the workspace already holds tbe_preprocess of these inputs */
 #define TBE_BWD_FUSED_LONG 0x2u    /* long runs: partials + countdown, last chunk updates (no second launch) */
@@ -123,6 +125,8 @@ typedef struct {
   size_t prep_error;   /* uint32, 0 after a good preprocessing; nonzero if a cross-workgroup
                           wait of the scans gave up after its poll limit (results invalid;
                           the backward then writes nothing) */
+  size_t hist_counts;  /* B x E uint16 row counts per bag saved by the histogram forward
+                          (TBE_FWD_SAVE_HIST; plans with one table of <= 64 rows) */
   size_t total;        /* bytes needed */
   int32_t num_buckets; /* nb */
 } tbe_ws_views;
@@ -178,6 +182,29 @@ int tbe_forward(const tbe_plan* plan, int64_t B, int32_t itype, const void* indi
                 const void* offsets, int64_t num_lookups, const float* per_sample_weights,
                 float* out, uint32_t flags, void* stream);
 
+/* Forward with fused input checks (FBTriton page, "Forward": bounds checks
+ * fused into the forward configurations that can take them, off by default;
+ * tbe_validate is the separate pass).  The generic forward (never the
+ * histogram path) with every offset and index checked as it is read:
+ * offsets are clamped into [0, num_lookups] and, within each wave's group of
+ * consecutive bags, made non-decreasing; a lookup whose index lies outside
+ * [0, R_t) (an int64 index by its full 64-bit value) reads no row and
+ * contributes nothing, while its bag keeps its length for mean pooling.  No
+ * access then leaves the inputs and outputs, whatever they hold.  err:
+ * device, TBE_VALIDATE_WORDS uint32 with tbe_validate's layout, overwritten
+ * (cleared by the call): [0] the TBE_INVALID_* bits found, [1] lookups
+ * skipped for an index out of range (each lookup a bag reads; with valid
+ * offsets, every bad position once), [2] first bag with a finding, [3] first
+ * bad position.  Valid inputs give tbe_forward's output bit for bit (same
+ * kernels and sum order) and an error block with no finding.  With offsets
+ * out of order, the bags next to them get unspecified but finite sums.
+ * Arguments and errors as tbe_forward (TBE_FWD_REQUIRE_HIST:
+ * TBE_E_UNSUPPORTED); TBE_E_ARG for a null or misaligned err. */
+int tbe_forward_checked(const tbe_plan* plan, int64_t B, int32_t itype, const void* indices,
+                        const void* offsets, int64_t num_lookups,
+                        const float* per_sample_weights, float* out, uint32_t flags,
+                        uint32_t* err, void* stream);
+
 /* Forward and backward preprocessing of the same lookups in one call
  * (FBTriton page, "Backward": the preprocessing can move into the forward).
  * The forward runs on `stream` exactly as tbe_forward; the preprocessing of
@@ -188,6 +215,16 @@ int tbe_forward(const tbe_plan* plan, int64_t B, int32_t itype, const void* indi
  * ownership and errors as tbe_forward and tbe_preprocess (ws: device, >=
  * tbe_workspace_size bytes, 256-byte aligned).  Calls on one plan are
  * serialized on the host (the fork and join events are the plan's). */
+/* TBE_FWD_SAVE_HIST (FBTriton page, "Fusion boundaries": the small-table
+ * path saves its histogram in the forward for the backward, which reuses it
+ * without fusing the two): for a plan and batch that take the histogram
+ * forward and that TBE_BWD_HIST serves (one table of at most 64 rows, D a
+ * multiple of 16 from 64 to 128, float16, no per-sample weights, average bag
+ * length >= 64; else TBE_E_UNSUPPORTED), the forward also writes every
+ * bag's exact row counts (uint16) into ws, and no run preprocessing is
+ * launched; a later tbe_backward_rowwise_adagrad(..., TBE_BWD_HIST |
+ * TBE_BWD_PREPROCESSED) on the same lookups reads those counts instead of
+ * the indices (same bits as without them). */
 int tbe_forward_preprocess(const tbe_plan* plan, int64_t B, int32_t itype, const void* indices,
                            const void* offsets, int64_t num_lookups,
                            const float* per_sample_weights, float* out, uint32_t flags, void* ws,
@@ -244,9 +281,16 @@ int tbe_preprocess(const tbe_plan* plan, int64_t B, int32_t itype, const void* i
  * computed as one contraction over the bags, grad[e][d] = sum_j C[j][e] *
  * grad_out[j][d] with C the per-bag sums of S[p] * (1/L if mean) of row e's
  * lookups, on the matrix cores (fp32 inputs), then row-wise Adagrad on the
- * rows with a lookup; no preprocessing (the workspace's preprocessing results
- * are neither used nor written).  Sums run in another order than the run
- * pipeline's, so the two agree within rounding, not bit for bit. */
+ * rows with a lookup; no run preprocessing (the workspace's run results are
+ * neither used nor written).  With TBE_BWD_PREPROCESSED as well, the row
+ * counts that tbe_forward_preprocess(..., TBE_FWD_SAVE_HIST) saved in the
+ * workspace for this batch (B and num_lookups recorded beside them) replace
+ * the indices, for every block of 128 bags whose bags have fewer than 65536
+ * lookups; counts saved for another batch are ignored.  Without per-sample
+ * weights a coefficient is formed as a float32 count times (1/L if mean) in
+ * either case, so the results are bit-identical.  Sums run in another order
+ * than the run pipeline's, so the two agree within rounding, not bit for
+ * bit. */
 int tbe_backward_rowwise_adagrad(const tbe_plan* plan, int64_t B, int32_t itype,
                                  const void* indices, const void* offsets, int64_t num_lookups,
                                  const float* per_sample_weights, const float* grad_out, float lr,

@@ -26,13 +26,15 @@ TBE_F32, TBE_F16, TBE_BF16 = 0, 1, 2
 TBE_I32, TBE_I64 = 0, 1
 TBE_SUM, TBE_MEAN = 0, 1
 TBE_FWD_NO_HIST, TBE_FWD_REQUIRE_HIST, TBE_FWD_BALANCE, TBE_FWD_NO_BALANCE = 0x1, 0x2, 0x4, 0x8
+TBE_FWD_SAVE_HIST = 0x10
 TBE_BWD_PREPROCESSED, TBE_BWD_FUSED_LONG, TBE_BWD_CONCURRENT = 0x1, 0x2, 0x4
 TBE_BWD_ORDER_CHUNKS, TBE_BWD_NO_ORDER_CHUNKS = 0x8, 0x10
 TBE_BWD_HIST = 0x20
 TBE_BWD_CONCURRENT_AUTO = 0x40
 
 EXPORTS = ("tbe_plan_create", "tbe_plan_destroy", "tbe_plan_key_bases", "tbe_workspace_size",
-           "tbe_workspace_views", "tbe_forward", "tbe_forward_preprocess", "tbe_preprocess",
+           "tbe_workspace_views", "tbe_forward", "tbe_forward_checked", "tbe_forward_preprocess",
+           "tbe_preprocess",
            "tbe_backward_rowwise_adagrad", "tbe_backward_rowwise_adagrad_noalloc",
            "tbe_backward", "tbe_validate", "tbe_prof_enable",
            "tbe_prof_read", "tbe_prof_calibrate", "tbe_test_knob", "tbe_status_string")
@@ -56,7 +58,7 @@ class WsViews(C.Structure):
                                            "sorted_scale", "run_start", "run_key", "single_task", "tiny_task",
                                            "medium_task", "long_task", "long_cbeg",
                                            "chunk_task", "chunk_perm", "counters", "prep_error",
-                                           "total")] + [
+                                           "hist_counts", "total")] + [
         ("num_buckets", C.c_int32)]
 
 
@@ -78,6 +80,7 @@ def lib() -> C.CDLL:
         L.tbe_workspace_size.argtypes = [vp, i64, i64, C.POINTER(C.c_size_t)]
         L.tbe_workspace_views.argtypes = [vp, i64, i64, C.POINTER(WsViews)]
         L.tbe_forward.argtypes = [vp, i64, i32, vp, vp, i64, vp, vp, u32, vp]
+        L.tbe_forward_checked.argtypes = [vp, i64, i32, vp, vp, i64, vp, vp, u32, vp, vp]
         L.tbe_preprocess.argtypes = [vp, i64, i32, vp, vp, i64, vp, vp, C.c_size_t, vp]
         L.tbe_forward_preprocess.argtypes = [vp, i64, i32, vp, vp, i64, vp, vp, u32, vp,
                                              C.c_size_t, vp]
@@ -199,6 +202,23 @@ def tbe_forward(plan, B: int, indices, offsets, num_lookups: int, per_sample_wei
                            _dptr(per_sample_weights, torch.float32, "per_sample_weights"),
                            _dptr(out, torch.float32, "out"), int(flags), _stream(stream))
     _check("tbe_forward", rc)
+
+
+def tbe_forward_checked(plan, B: int, indices, offsets, num_lookups: int, per_sample_weights,
+                        out: torch.Tensor, err: torch.Tensor, flags: int = 0,
+                        stream=None) -> None:
+    """tbe_forward with the offsets and indices checked as they are read; err:
+    device uint32 tensor of TBE_VALIDATE_WORDS words (tbe_validate's layout)."""
+    it = _itype(indices, offsets)
+    if err.numel() < TBE_VALIDATE_WORDS:
+        raise ValueError("err needs TBE_VALIDATE_WORDS words")
+    rc = lib().tbe_forward_checked(plan, int(B), it, _dptr(indices, None, "indices"),
+                                   _dptr(offsets, None, "offsets"), int(num_lookups),
+                                   _dptr(per_sample_weights, torch.float32, "per_sample_weights"),
+                                   _dptr(out, torch.float32, "out"), int(flags),
+                                   _dptr(err, (torch.uint32, torch.int32), "err"),
+                                   _stream(stream))
+    _check("tbe_forward_checked", rc)
 
 
 TBE_VALIDATE_REPAIR = 0x1

@@ -20,6 +20,15 @@
 // per stripe, stripes combined in order) and applies row-wise Adagrad to rows
 // with at least one lookup.  Determinism: every sum is in a data-determined
 // order, so repeated calls give the same bits.
+//
+// Reuse of the forward's histogram (tbe_forward_preprocess with
+// TBE_FWD_SAVE_HIST, then this backward with TBE_BWD_PREPROCESSED): the
+// coefficients of a block's bags come from the saved uint16 row counts
+// (C4: 8.4 MB) instead of the indices (67 MB of int64).  Without per-sample
+// weights both paths form a bag's coefficient the same way, count times
+// (1/L if mean) as one float32 count divided by L, so they give the same
+// bits; a block with a bag of 65536 lookups or more, or counts saved for
+// another batch (the header's {B, N} differ), takes the indices.
 #include "tbe_common.h"
 
 namespace tbe {
@@ -35,6 +44,7 @@ template <typename IT>
 __global__ __launch_bounds__(kThreads) void bwd_hist_partial_kernel(HistArgs h) {
   __shared__ float coef[2][kHBags][kHRows + 1];  // [half][bag][row], padded
   __shared__ uint32_t cnt[kHRows];
+  __shared__ float s_len[kHBags];                // bag lengths of the block
   const uint32_t wave = threadIdx.x / kWave, lane = lane_id();
   const uint32_t i = lane & 15u, kq = lane >> 4;  // A row / B column; K lane group
   const IT* __restrict__ I = reinterpret_cast<const IT*>(h.indices);
@@ -45,36 +55,57 @@ __global__ __launch_bounds__(kThreads) void bwd_hist_partial_kernel(HistArgs h) 
 #pragma unroll
   for (int nt = 0; nt < kHCols / 16; ++nt) acc[nt] = (float4v){0.f, 0.f, 0.f, 0.f};
   if (threadIdx.x < (uint32_t)kHRows) cnt[threadIdx.x] = 0u;
+  // without per-sample weights a coefficient is a row count, scaled by 1/L
+  // once (mean) when it enters the contraction
+  const bool counts = h.psw == nullptr;
+  const bool use_saved = counts && h.saved != nullptr && h.saved_hdr[0] == (uint32_t)h.B &&
+                         h.saved_hdr[1] == h.N;  // uniform
   const int64_t nblk = (h.B + kHBags - 1) / kHBags;
   for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
     const int64_t j0 = blk * kHBags;
     const uint32_t nb = (uint32_t)min((int64_t)kHBags, h.B - j0);
     for (uint32_t x = threadIdx.x; x < (uint32_t)(2 * kHBags * (kHRows + 1)); x += kThreads)
       (&coef[0][0][0])[x] = 0.f;
-    __syncthreads();
-    const uint32_t bag = threadIdx.x % kHBags, half = threadIdx.x / kHBags;
-    if (bag < nb) {  // half `half` of this bag's coefficients, in lookup order
-      const int64_t lo = (int64_t)O[j0 + bag], hi = (int64_t)O[j0 + bag + 1];
-      const float fl = (float)(hi - lo);
-      const int64_t mid = lo + (hi - lo) / 2;
-      const int64_t ps = half ? mid : lo, pe0 = half ? hi : mid;
-      const int64_t pe = pe0 < (int64_t)h.N ? pe0 : (int64_t)h.N;
-      // 16 indices (and weights) in flight, then their updates in order
-      for (int64_t p0 = ps < 0 ? 0 : ps; p0 < pe; p0 += 16) {
-        int64_t r[16];
-        float sp[16];
+    bool wide = false;  // a bag whose counts a uint16 may not hold
+    if (threadIdx.x < nb) {
+      const int64_t L = (int64_t)O[j0 + threadIdx.x + 1] - (int64_t)O[j0 + threadIdx.x];
+      s_len[threadIdx.x] = (float)L;
+      wide = L >= 65536;
+    }
+    const bool from_saved = use_saved && !__syncthreads_or(wide ? 1 : 0);  // also the barrier
+    if (from_saved) {  // the block's saved counts, bag-major and coalesced
+      for (uint32_t x = threadIdx.x; x < nb * E; x += kThreads) {
+        const uint32_t b = x / E, e = x % E;
+        const uint32_t c = h.saved[(j0 + b) * (int64_t)E + e];
+        coef[0][b][e] = (float)c;
+        if (c) atomicAdd(&cnt[e], c);
+      }
+    } else {
+      const uint32_t bag = threadIdx.x % kHBags, half = threadIdx.x / kHBags;
+      if (bag < nb) {  // half `half` of this bag's coefficients, in lookup order
+        const int64_t lo = (int64_t)O[j0 + bag], hi = (int64_t)O[j0 + bag + 1];
+        const float fl = (float)(hi - lo);
+        const int64_t mid = lo + (hi - lo) / 2;
+        const int64_t ps = half ? mid : lo, pe0 = half ? hi : mid;
+        const int64_t pe = pe0 < (int64_t)h.N ? pe0 : (int64_t)h.N;
+        // 16 indices (and weights) in flight, then their updates in order
+        for (int64_t p0 = ps < 0 ? 0 : ps; p0 < pe; p0 += 16) {
+          int64_t r[16];
+          float sp[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const bool in = p0 + u < pe;
-          r[u] = in ? (int64_t)I[p0 + u] : -1;
-          sp[u] = (in && h.psw) ? h.psw[p0 + u] : 1.0f;
-        }
+          for (int u = 0; u < 16; ++u) {
+            const bool in = p0 + u < pe;
+            r[u] = in ? (int64_t)I[p0 + u] : -1;
+            sp[u] = (in && h.psw) ? h.psw[p0 + u] : 1.0f;
+          }
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          if (r[u] < 0 || r[u] >= (int64_t)E) continue;
-          // the contribution scale of the lookup, as the transposition computes it
-          coef[half][bag][r[u]] += mean ? sp[u] / fl : sp[u];
-          atomicAdd(&cnt[r[u]], 1u);
+          for (int u = 0; u < 16; ++u) {
+            if (r[u] < 0 || r[u] >= (int64_t)E) continue;
+            // with per-sample weights, the contribution scale of the lookup as the
+            // transposition computes it; else a count (exact in float32)
+            coef[half][bag][r[u]] += counts ? 1.0f : (mean ? sp[u] / fl : sp[u]);
+            atomicAdd(&cnt[r[u]], 1u);
+          }
         }
       }
     }
@@ -84,7 +115,9 @@ __global__ __launch_bounds__(kThreads) void bwd_hist_partial_kernel(HistArgs h) 
 #pragma unroll 4
       for (uint32_t ks = 0; ks < (uint32_t)kHBags / 4u; ++ks) {
         const uint32_t jb = ks * 4u + kq;  // this lane's bag in the K step
-        const float av = coef[0][jb][16u * wave + i] + coef[1][jb][16u * wave + i];
+        float av = coef[0][jb][16u * wave + i] + coef[1][jb][16u * wave + i];
+        // (an empty bag has no count to scale)
+        if (counts && mean && jb < nb && s_len[jb] > 0.f) av = av / s_len[jb];
         const bool bag_ok = jb < nb;
         const float* grow = h.grad + (j0 + (bag_ok ? jb : 0u)) * (int64_t)h.dtot + h.col;
 #pragma unroll

@@ -10,6 +10,14 @@
 // two 16-column tiles each, two K steps).  The tile is staged through LDS so
 // the float32 output leaves as coalesced 16-byte stores.  Still HBM-bound: it
 // reads the indices once and writes the output once.
+//
+// Saved histogram (FBTriton page, "Fusion boundaries": the small-table path
+// keeps its histogram for the backward instead of fusing the two): with
+// hist_save set, the lookups past a bag's first 256 are counted too, after
+// the contraction has used the capped counts, and every bag's exact row
+// counts are stored as uint16 (a count never exceeds its bag's length; the
+// backward recomputes bags of 65536 lookups or more from their indices), with
+// {B, N} in a header so that the backward uses them only for this batch.
 #include "tbe_common.h"
 
 namespace tbe {
@@ -40,6 +48,10 @@ __global__ __launch_bounds__(kThreads) void fwd_hist_kernel(FwdArgs a, uint32_t 
 
   const uint32_t wave = threadIdx.x / kWave, lane = lane_id();
   const int64_t ngroups = (a.B + kBags - 1) / kBags;
+  if (a.hist_save && blockIdx.x == 0 && threadIdx.x == 0) {
+    a.hist_hdr[0] = (uint32_t)a.B;
+    a.hist_hdr[1] = a.n;
+  }
   for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
     const int64_t b0 = g * kBags;
     const int nb = (int)((a.B - b0) < kBags ? (a.B - b0) : kBags);
@@ -86,16 +98,24 @@ __global__ __launch_bounds__(kThreads) void fwd_hist_kernel(FwdArgs a, uint32_t 
     __syncthreads();
 
     // lookups past the first kCountCap of a bag: plain gather, one wave per bag,
-    // sequential in lookup order
+    // sequential in lookup order (and counted for the saved histogram)
     for (int bi = (int)wave; bi < nb; bi += kThreads / kWave) {
       const int64_t q0 = boff[bi] + kCountCap, q1 = boff[bi + 1];
       for (int64_t q = q0; q < q1; ++q) {
         const uint32_t r = (uint32_t)load_idx(a.indices, a.itype, q);
         if (r >= E) continue;
         for (uint32_t col = lane; col < D; col += kWave) tile[bi][col] += (float)wt[col][r];
+        if (a.hist_save && lane == 0) cnt[bi][r] += 1u;  // this wave owns the bag's counts
       }
     }
     __syncthreads();
+    if (a.hist_save) {  // the group's exact counts, bag-major
+      for (uint32_t e = threadIdx.x; e < (uint32_t)nb * E; e += kThreads) {
+        const uint32_t bi = e / E, r = e % E;
+        const uint32_t c = cnt[bi][r];
+        a.hist_save[(b0 + bi) * (int64_t)E + r] = (uint16_t)(c < 65535u ? c : 65535u);
+      }
+    }
 
     // store rows b0 .. b0+nb-1 (mean divides by the bag length)
     const uint32_t q4 = D / 4;

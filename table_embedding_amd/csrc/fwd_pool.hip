@@ -32,6 +32,16 @@
 // A partial last batch repeats the last index and drops the repeats with a
 // select (the repeated row is a cache hit).  The indices of the next batch
 // load while the rows of the current one are in flight.
+//
+// Fused input checks (CHK, tbe_forward_checked; FBTriton page, "Forward":
+// bounds checks fused into the forward, off by default).  Offsets are clamped
+// into [0, N] as they are read and, inside a wave's bag group, made
+// non-decreasing by a running maximum; an index outside [0, R_t) (an int64
+// one by its full value) is replaced by row 0 and its contribution dropped,
+// so the bag keeps its length for mean pooling.  Every access then stays
+// inside the inputs and outputs.  Findings go to the error block with the
+// conventions of tbe_validate (bits, bad-index count, first bag, first bad
+// position); valid inputs give the unchecked kernel's bits.
 #include "tbe_common.h"
 
 namespace tbe {
@@ -58,7 +68,33 @@ __device__ __forceinline__ double fma_acc(double s, float v, double acc) {
   return __builtin_fma(s, (double)v, acc);
 }
 
-template <int WD, int VEC, int NC, typename IT, bool PSW>
+// Offset findings of bag j (lo = O[j], hi = O[j+1], as stored) with
+// tbe_validate's conventions: the start offset belongs to bag 0, the end
+// offset to the last bag.
+__device__ __forceinline__ uint32_t offset_bits(int64_t lo, int64_t hi, uint64_t j,
+                                                uint64_t nbag, int64_t n) {
+  uint32_t bits = 0;
+  if (j == 0 && lo != 0) bits |= kValOffsetStart;
+  if (j + 1 == nbag && hi != n) bits |= kValOffsetEnd;
+  if (lo > hi) bits |= kValOffsetOrder;
+  if (lo < 0 || lo > n || hi < 0 || hi > n) bits |= kValOffsetRange;
+  return bits;
+}
+__device__ __forceinline__ void report_offsets(uint32_t* err, uint32_t bits, uint64_t j) {
+  atomicOr(&err[kValBits], bits);
+  atomicMin(&err[kValFirstBag], (uint32_t)j);
+}
+__device__ __forceinline__ void report_index(uint32_t* err, uint32_t pos, uint64_t j) {
+  atomicOr(&err[kValBits], kValIndexRange);
+  atomicAdd(&err[kValBadIndices], 1u);
+  atomicMin(&err[kValFirstPos], pos);
+  atomicMin(&err[kValFirstBag], (uint32_t)j);
+}
+__device__ __forceinline__ int64_t clamp_n(int64_t o, int64_t n) {
+  return o < 0 ? 0 : (o > n ? n : o);
+}
+
+template <int WD, int VEC, int NC, typename IT, bool PSW, bool CHK>
 __global__ __launch_bounds__(kThreads) void fwd_bal_kernel(FwdArgs a, BucketSet S) {
   using AT = typename Acc<WD>::T;
   constexpr uint32_t kWaves = kThreads / kWave;
@@ -92,8 +128,39 @@ __global__ __launch_bounds__(kThreads) void fwd_bal_kernel(FwdArgs a, BucketSet 
 
   // offsets of the group's bags: off[q] = O[j0 + q], q = 0 .. nbw (positions < 2^31)
   uint32_t* off = s_off[wave];
-  if (lane <= nbw) off[lane] = (uint32_t)O[j0 + lane];
-  if (nbw == (uint32_t)kWave && lane == 0) off[kWave] = (uint32_t)O[j0 + kWave];
+  if constexpr (CHK) {
+    // each offset read once, checked, clamped into [0, N] and made
+    // non-decreasing by a running maximum over the group
+    const int64_t n64 = (int64_t)a.n;
+    const int64_t o = lane <= nbw ? (int64_t)O[j0 + lane] : 0;
+    const int64_t o64 = (int64_t)O[j0 + nbw];  // the group's end offset (lane nbw's, or the 65th)
+    int64_t nx = __shfl_down(o, 1, kWave);     // O[j0 + lane + 1]
+    if (lane + 1 == nbw) nx = o64;
+    const uint64_t nbag = (uint64_t)a.T * B;
+    const uint32_t bits = lane < nbw ? offset_bits(o, nx, j0 + lane, nbag, n64) : 0u;
+    const uint64_t bad = __ballot(bits != 0u);
+    if (bad) {
+      const uint32_t first = (uint32_t)__builtin_ctzll(bad);
+      uint32_t all = bits;
+#pragma unroll
+      for (int m = 1; m < kWave; m <<= 1) all |= __shfl_xor(all, m, kWave);
+      if (lane == first) report_offsets(a.err, all, j0 + lane);
+    }
+    uint32_t c = (uint32_t)clamp_n(o, n64);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {  // inclusive running maximum in lane order
+      const uint32_t y = __shfl_up(c, d, kWave);
+      if (lane >= (uint32_t)d) c = y > c ? y : c;
+    }
+    if (lane <= nbw) off[lane] = c;
+    if (nbw == (uint32_t)kWave && lane == kWave - 1) {
+      const uint32_t e = (uint32_t)clamp_n(o64, n64);
+      off[kWave] = e > c ? e : c;
+    }
+  } else {
+    if (lane <= nbw) off[lane] = (uint32_t)O[j0 + lane];
+    if (nbw == (uint32_t)kWave && lane == 0) off[kWave] = (uint32_t)O[j0 + kWave];
+  }
   wave_lds_sync();
 
   // This subgroup's piece [plo, phi) of the group's lookups: equal shares in
@@ -179,25 +246,54 @@ __global__ __launch_bounds__(kThreads) void fwd_bal_kernel(FwdArgs a, BucketSet 
   };
 
   const uint32_t pb = plo, pe = phi;
-  uint32_t nrow[kInFlight];
+  // CHK with int64 indices: the high word too (an index is valid only if it is 0)
+  constexpr bool kHi = CHK && sizeof(IT) == 8;
+  uint32_t nrow[kInFlight], nhi[kInFlight];
   float ns[kInFlight];
   if (pb < pe) {
 #pragma unroll
     for (int k = 0; k < kInFlight; ++k) {
       const uint32_t q = pb + k < pe ? pb + k : pe - 1;
       nrow[k] = buf_u32(ires, q * (uint32_t)sizeof(IT));
+      nhi[k] = kHi ? buf_u32(ires, q * (uint32_t)sizeof(IT) + 4u) : 0u;
       ns[k] = PSW ? __builtin_bit_cast(float, buf_u32(pres, q * 4u)) : 1.0f;
     }
   }
   for (uint32_t p = pb; p < pe; p += kInFlight) {
     uint32_t row[kInFlight];
     float s[kInFlight];
-    bool ok[kInFlight];
+    bool ok[kInFlight], use[kInFlight];
 #pragma unroll
     for (int k = 0; k < kInFlight; ++k) {
       row[k] = nrow[k];
       s[k] = ns[k];
       ok[k] = p + k < pe;
+      use[k] = ok[k];
+    }
+    if constexpr (CHK) {
+      bool any = false;
+#pragma unroll
+      for (int k = 0; k < kInFlight; ++k) {
+        const bool bad = ok[k] && (nhi[k] != 0u || row[k] >= td.rows);
+        use[k] = ok[k] && !bad;
+        row[k] = bad ? 0u : row[k];
+        any |= bad;
+      }
+      if (__ballot(any && lane_in == 0)) {  // rare: report each bad lookup once
+        if (lane_in == 0) {
+#pragma unroll
+          for (int k = 0; k < kInFlight; ++k) {
+            if (!ok[k] || use[k]) continue;
+            const uint32_t pos = p + (uint32_t)k;
+            uint32_t lo = 0, hi = nbw;  // its bag: the last q with off[q] <= pos
+            while (hi - lo > 1) {
+              const uint32_t mid = (lo + hi) >> 1;
+              if (off[mid] <= pos) lo = mid; else hi = mid;
+            }
+            report_index(a.err, pos, j0 + lo);
+          }
+        }
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     // NC > 1 only for rows that take all 64 lanes, which get one bag per wave,
@@ -212,6 +308,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bal_kernel(FwdArgs a, BucketSet 
         for (int k = 0; k < kInFlight; ++k) {
           const uint32_t q = p + kInFlight + k < pe ? p + kInFlight + k : pe - 1;
           nrow[k] = buf_u32(ires, q * (uint32_t)sizeof(IT));
+          nhi[k] = kHi ? buf_u32(ires, q * (uint32_t)sizeof(IT) + 4u) : 0u;
           ns[k] = PSW ? __builtin_bit_cast(float, buf_u32(pres, q * 4u)) : 1.0f;
         }
       }
@@ -227,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bal_kernel(FwdArgs a, BucketSet 
         }
 #pragma unroll
         for (int e = 0; e < VEC; ++e)
-          acc[c][e] = fma_acc(ok[k] ? AT(s[k]) : AT(0), v[k][e], acc[c][e]);
+          acc[c][e] = fma_acc(use[k] ? AT(s[k]) : AT(0), v[k][e], acc[c][e]);
       }
     }
   }
@@ -260,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bal_kernel(FwdArgs a, BucketSet 
 
 // One bag per lane subgroup (bps == 1): subgroup sg of the launch pools bag sg
 // of the bucket; the offsets and indices load straight from global memory.
-template <int WD, int VEC, int NC, typename IT, bool PSW>
+template <int WD, int VEC, int NC, typename IT, bool PSW, bool CHK>
 __global__ __launch_bounds__(kThreads) void fwd_pool_kernel(FwdArgs a, BucketSet S) {
   using AT = typename Acc<WD>::T;
   BucketDev bk;
@@ -278,8 +375,16 @@ __global__ __launch_bounds__(kThreads) void fwd_pool_kernel(FwdArgs a, BucketSet
   const IT* __restrict__ I = reinterpret_cast<const IT*>(a.indices);
   const IT* __restrict__ O = reinterpret_cast<const IT*>(a.offsets);
   const int64_t j = (int64_t)t * a.B + b;
-  const int64_t lo = O[j];
-  const int64_t hi = O[j + 1];
+  int64_t lo = O[j];
+  int64_t hi = O[j + 1];
+  if constexpr (CHK) {  // checked, then clamped into [0, N] with hi >= lo
+    const int64_t n64 = (int64_t)a.n;
+    const uint32_t bits = offset_bits(lo, hi, (uint64_t)j, (uint64_t)a.T * (uint64_t)a.B, n64);
+    if (bits && lane_in == 0) report_offsets(a.err, bits, (uint64_t)j);
+    lo = clamp_n(lo, n64);
+    hi = clamp_n(hi, n64);
+    hi = hi < lo ? lo : hi;
+  }
   const uint32_t D = td.dim;
 
   AT acc[NC][VEC];
@@ -315,6 +420,12 @@ __global__ __launch_bounds__(kThreads) void fwd_pool_kernel(FwdArgs a, BucketSet
       row[k] = nrow[k];
       s[k] = ns[k];
       ok[k] = p + k < hi;
+      if constexpr (CHK) {  // a bad index reads row 0 and contributes nothing
+        const bool bad = ok[k] && (uint64_t)row[k] >= (uint64_t)td.rows;
+        if (bad && lane_in == 0) report_index(a.err, (uint32_t)(p + k), (uint64_t)j);
+        ok[k] = ok[k] && !bad;
+        row[k] = bad ? 0 : row[k];
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -352,17 +463,23 @@ __global__ __launch_bounds__(kThreads) void fwd_pool_kernel(FwdArgs a, BucketSet
   }
 }
 
-template <int WD, int VEC, int NC, typename IT, bool PSW>
-hipError_t launch_t(const FwdArgs& a, const BucketSet& S, hipStream_t s) {
+template <int WD, int VEC, int NC, typename IT, bool PSW, bool CHK>
+hipError_t launch_c(const FwdArgs& a, const BucketSet& S, hipStream_t s) {
   const uint32_t grid = S.gbeg[S.n];
   if (grid == 0) return hipSuccess;
   if (a.split)
-    TBE_LAUNCH("fwd_pool", (fwd_bal_kernel<WD, VEC, NC, IT, PSW>), dim3(grid), dim3(kThreads), s,
-               a, S);
+    TBE_LAUNCH("fwd_pool", (fwd_bal_kernel<WD, VEC, NC, IT, PSW, CHK>), dim3(grid),
+               dim3(kThreads), s, a, S);
   else
-    TBE_LAUNCH("fwd_pool", (fwd_pool_kernel<WD, VEC, NC, IT, PSW>), dim3(grid), dim3(kThreads), s,
-               a, S);
+    TBE_LAUNCH("fwd_pool", (fwd_pool_kernel<WD, VEC, NC, IT, PSW, CHK>), dim3(grid),
+               dim3(kThreads), s, a, S);
   return hipGetLastError();
+}
+
+template <int WD, int VEC, int NC, typename IT, bool PSW>
+hipError_t launch_t(const FwdArgs& a, const BucketSet& S, hipStream_t s) {
+  return a.err ? launch_c<WD, VEC, NC, IT, PSW, true>(a, S, s)
+               : launch_c<WD, VEC, NC, IT, PSW, false>(a, S, s);
 }
 
 template <int WD, int VEC, int NC>

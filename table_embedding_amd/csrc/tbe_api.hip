@@ -180,6 +180,10 @@ WsLayout layout(const tbe_plan* P, int64_t N) {
   const bool hc = bwd_hist_capable(P);
   L.hist_part = take(hc ? (size_t)kHistMaxWorkgroups * 64 * L.pstride * 4 : 0);
   L.hist_cnt = take(hc ? (size_t)kHistMaxWorkgroups * 64 * 4 : 0);
+  // saved counts: B x E uint16 with B <= N / 64 (the histogram forward needs an
+  // average bag length of 64) and E <= 64, so at most 2 N + 128 bytes
+  L.hist_save = take(hc ? 2 * n + 128 : 0);
+  L.hist_hdr = take(hc ? 16 : 0);
   L.total = off;
   return L;
 }
@@ -629,6 +633,7 @@ int tbe_workspace_views(const tbe_plan* P, int64_t B, int64_t N, tbe_ws_views* v
   v->chunk_perm = L.chunk_perm;
   v->counters = L.counters;
   v->prep_error = L.ctl + (size_t)kCtlErr * 4;
+  v->hist_counts = L.hist_save;
   v->total = L.total;
   v->num_buckets = (int32_t)P->buckets.size();
   return TBE_OK;
@@ -651,12 +656,20 @@ int check_forward(const tbe_plan* P, int64_t B, int32_t itype, const void* indic
 }
 
 // The forward's launches on s (arguments already checked).
+// err: the error block of the checked forward (the generic kernels' CHK
+// variant, never the histogram path), or null.
 int launch_forward(const tbe_plan* P, int64_t B, int32_t itype, const void* indices,
                    const void* offsets, int64_t N, const float* psw, float* out, uint32_t flags,
-                   hipStream_t s) {
-  const bool hist = hist_eligible(P, B, N, psw);
+                   hipStream_t s, uint32_t* err = nullptr, uint16_t* hist_save = nullptr,
+                   uint32_t* hist_hdr = nullptr) {
+  const bool hist = !err && hist_eligible(P, B, N, psw);
   if (B == 0) return TBE_OK;
   FwdArgs a{P->d_tables, B, itype, indices, offsets, psw, out, P->dtot, 1u};
+  a.T = (uint32_t)P->T;
+  a.n = (uint32_t)N;
+  a.err = err;
+  a.hist_save = hist ? hist_save : nullptr;
+  a.hist_hdr = hist_hdr;
   hipError_t e = hipSuccess;
   if (hist && !(flags & TBE_FWD_NO_HIST)) {
     e = launch_forward_hist(a, (uint32_t)P->rows[0], (uint32_t)P->dims[0],
@@ -694,14 +707,39 @@ int tbe_forward(const tbe_plan* P, int64_t B, int32_t itype, const void* indices
                         reinterpret_cast<hipStream_t>(stream));
 }
 
+int tbe_forward_checked(const tbe_plan* P, int64_t B, int32_t itype, const void* indices,
+                        const void* offsets, int64_t N, const float* psw, float* out,
+                        uint32_t flags, uint32_t* err, void* stream) {
+  if (flags & TBE_FWD_REQUIRE_HIST) return TBE_E_UNSUPPORTED;  // the checks are in the generic path
+  const int rc = check_forward(P, B, itype, indices, offsets, N, psw, out, flags);
+  if (rc) return rc;
+  if (!err || !aligned(err, 4)) return TBE_E_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (launch_validate_clear(err, s) != hipSuccess) return TBE_E_HIP;
+  return launch_forward(P, B, itype, indices, offsets, N, psw, out, flags, s, err);
+}
+
 int tbe_forward_preprocess(const tbe_plan* P, int64_t B, int32_t itype, const void* indices,
                            const void* offsets, int64_t N, const float* psw, float* out,
                            uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  const bool save = (flags & TBE_FWD_SAVE_HIST) != 0;
+  flags &= ~TBE_FWD_SAVE_HIST;
   int rc = check_forward(P, B, itype, indices, offsets, N, psw, out, flags);
   if (rc) return rc;
   rc = check_ws(P, N, ws, ws_bytes);
   if (rc) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (save) {
+    // the histogram forward keeps its row counts for the histogram backward,
+    // which needs nothing else: no run preprocessing
+    if ((flags & TBE_FWD_NO_HIST) || !hist_eligible(P, B, N, psw) || !bwd_hist_capable(P))
+      return TBE_E_UNSUPPORTED;
+    const WsLayout L = layout(P, N);
+    uint8_t* w = reinterpret_cast<uint8_t*>(ws);
+    return launch_forward(P, B, itype, indices, offsets, N, psw, out, flags, s, nullptr,
+                          reinterpret_cast<uint16_t*>(w + L.hist_save),
+                          reinterpret_cast<uint32_t*>(w + L.hist_hdr));
+  }
   if (N == 0) return launch_forward(P, B, itype, indices, offsets, N, psw, out, flags, s);
   // fork before the forward, so that the side stream waits for the work
   // before it, not for it; the forward is enqueued first (one launch), then
@@ -816,6 +854,10 @@ int run_backward(const tbe_plan* P, int64_t B, int32_t itype, const void* indice
     h.pcnt = reinterpret_cast<uint32_t*>(w + L.hist_cnt);
     h.pstride = L.pstride;
     h.nwg = (uint32_t)std::min<int64_t>(kHistMaxWorkgroups, (B + 127) / 128);
+    if (flags & TBE_BWD_PREPROCESSED) {  // the forward's saved counts, when they are this batch's
+      h.saved = reinterpret_cast<const uint16_t*>(w + L.hist_save);
+      h.saved_hdr = reinterpret_cast<const uint32_t*>(w + L.hist_hdr);
+    }
     h.debug_count = debug_row_updates;
     return launch_backward_hist(h, itype, P->wdtype, s) == hipSuccess ? TBE_OK : TBE_E_HIP;
   }

@@ -127,6 +127,7 @@ struct WsLayout {
   size_t partial, counters;
   size_t chunk_perm;  // max_chunks uint32: chunk list position taken at each walk position
   size_t hist_part, hist_cnt;  // histogram backward: partial rows and row counts (or 0 bytes)
+  size_t hist_save, hist_hdr;  // row counts per bag saved by the histogram forward, {B, N}
   size_t total;
   uint32_t ntiles;          // ceil(N / kTile)
   uint32_t nrle_tiles;      // ceil(N / (rle_groups * kTile)): tiles of the run-length pass
@@ -459,6 +460,11 @@ struct FwdArgs {
   uint32_t bps;    // generic forward: bags per lane subgroup in a wave's group (1 .. 4)
   uint32_t split;  // 1: the group's lookups split evenly over its subgroups; 0: one bag each
   uint32_t n;      // lookups N (the equal-piece split needs N * index bytes < 2^32)
+  uint32_t T;      // tables
+  uint32_t* err;   // nullable: check offsets and indices as they are read (error block of
+                   // kValWords words, cleared before the launch)
+  uint16_t* hist_save;  // nullable: histogram path, each bag's row counts (B x E) written here
+  uint32_t* hist_hdr;   // with hist_save: {B, N} of the batch whose counts are saved
 };
 
 struct PrepArgs {
@@ -523,6 +529,8 @@ struct HistArgs {
   float lr, eps;
   float* part;            // nwg x E partial rows of pstride floats
   uint32_t* pcnt;         // nwg x E lookup counts
+  const uint16_t* saved;  // nullable: row counts per bag saved by the histogram forward
+  const uint32_t* saved_hdr;  // {B, N} of the saved counts (used only if they match)
   uint32_t pstride, nwg;
   uint32_t* debug_count;  // nullable, per linear key
 };
@@ -543,6 +551,9 @@ struct ValArgs {
 };
 hipError_t launch_validate(const ValArgs& v, int itype, uint32_t* err, bool repair,
                            hipStream_t s);
+// The error block to its empty state (no finding; first bag and position
+// 0xffffffff), by a one-workgroup kernel.
+hipError_t launch_validate_clear(uint32_t* err, hipStream_t s);
 
 // One forward launch for the buckets of S (S.gbeg filled: bags of bucket k
 // over workgroups [gbeg[k], gbeg[k+1])).

@@ -134,6 +134,11 @@ __global__ __launch_bounds__(kThreads) void validate_clamp_kernel(ValArgs v) {
 
 }  // namespace
 
+hipError_t launch_validate_clear(uint32_t* err, hipStream_t s) {
+  TBE_LAUNCH("validate_clear", validate_clear_kernel, dim3(1), dim3(kThreads), s, err);
+  return hipGetLastError();
+}
+
 hipError_t launch_validate(const ValArgs& v, int itype, uint32_t* err, bool repair,
                            hipStream_t s) {
   const uint64_t nbag = (uint64_t)v.T * (uint64_t)v.B;
