@@ -34,6 +34,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -67,6 +68,13 @@ KERNEL_FAMILIES = (
     ("validate_indices_kernel", "validate_check"), ("validate_clamp_kernel", "validate_repair"),
 )
 COLD_FLUSH_BYTES = 1 << 30
+
+
+def kernel_family(name):
+    """The library's kernel family of a profiler kernel name (None for others)."""
+    m = re.search(r"(\w+)\s*[<(]", name.replace("(anonymous namespace)", ""))
+    base = m.group(1) if m else name
+    return next((v for k, v in KERNEL_FAMILIES if base == k), None)
 
 
 def parse():
@@ -329,12 +337,13 @@ def cpu_baseline(spec, off, idx, W_dev, G_dev, psw_dev, cap, torch):
 
 def pmc_summary(args):
     """rocprofv3 --pmc CSV files (one run per counter set) -> bytes per launch
-    per kernel family.  Read bytes are sum_size(TCC_EA0_RDREQ_{32,64,128}B * size)
-    when those counters are present, else FETCH_SIZE; write bytes
-    TCC_EA0_WRREQ_64B * 64 + (TCC_EA0_WRREQ - TCC_EA0_WRREQ_64B) * 32, else
-    WRITE_SIZE.  Each is scaled by the factor that makes a plain 1 GiB copy
-    (--calibrate-copy, profiled the same way; kernel name containing "copy" or
-    "elementwise") read and write 1 GiB."""
+    per kernel family.  Read bytes: FETCH_SIZE, whose gfx950 expression counts
+    every L2-to-fabric read request at its size (128 B via TCC_BUBBLE, 32 B via
+    TCC_EA0_RDREQ_32B, 64 B the rest); write bytes: WRITE_SIZE (64 B and 32 B
+    requests).  Each is scaled by the factor that makes a plain 1 GiB device
+    copy (--calibrate-copy, profiled the same way: the runtime's copyBuffer
+    kernel) read and write 1 GiB.  TCC_HIT / TCC_MISS, when present,
+    give the L2 hit rate."""
     import csv
     rows = []
     for f in glob.glob(os.path.join(args.pmc_summary, "**", "*counter_collection.csv"),
@@ -345,32 +354,28 @@ def pmc_summary(args):
     for r in rows:
         name = r.get("Kernel_Name") or r.get("Kernel-Name") or ""
         key = (name, r.get("Dispatch_Id"), r.get("Correlation_Id"))
-        acc.setdefault(key, {})[r["Counter_Name"]] = acc.get(key, {}).get(
-            r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        # per-instance values (NAME[i]) and _sum reductions add up to one total
+        cn = re.sub(r"\[\d+\]$", "", r["Counter_Name"])
+        cn = cn[:-4] if cn.endswith("_sum") else cn
+        acc.setdefault(key, {})[cn] = acc.get(key, {}).get(cn, 0.0) + float(r["Counter_Value"])
 
-    def read_b(c):
-        if "TCC_EA0_RDREQ_32B" in c and "TCC_EA0_RDREQ_64B" in c:
-            b = 32 * c["TCC_EA0_RDREQ_32B"] + 64 * c["TCC_EA0_RDREQ_64B"]
-            return b + 128 * c.get("TCC_EA0_RDREQ_128B", 0.0)
+    def read_b(c):  # FETCH_SIZE is already request-size-resolved on gfx950 (32/64/128 B)
         return 1024 * c["FETCH_SIZE"] if "FETCH_SIZE" in c else None
 
     def write_b(c):
-        if "TCC_EA0_WRREQ" in c and "TCC_EA0_WRREQ_64B" in c:
-            return 64 * c["TCC_EA0_WRREQ_64B"] + 32 * (c["TCC_EA0_WRREQ"] - c["TCC_EA0_WRREQ_64B"])
         return 1024 * c["WRITE_SIZE"] if "WRITE_SIZE" in c else None
 
     fam = {}
     cal = {"read": [], "write": []}
     for (name, _, _), c in acc.items():
         r, w = read_b(c), write_b(c)
-        low = name.lower()
-        if "copy" in low or "elementwise" in low:
+        if "copyBuffer" in name:  # the runtime's blit copy of --calibrate-copy
             if r is not None:
                 cal["read"].append(r)
             if w is not None:
                 cal["write"].append(w)
             continue
-        f = next((v for k, v in KERNEL_FAMILIES if name.startswith(k)), None)
+        f = kernel_family(name)
         if f is None:
             continue
         e = fam.setdefault(f, {"read": [], "write": [], "hit": [], "miss": []})
