@@ -127,6 +127,13 @@ typedef struct {
                           the backward then writes nothing) */
   size_t hist_counts;  /* B x E uint16 row counts per bag saved by the histogram forward
                           (TBE_FWD_SAVE_HIST; plans with one table of <= 64 rows) */
+  /* The hot-row contraction's lists (zero bytes when no table of the plan can
+   * take it; written only by a backward that takes it): */
+  size_t long_flag;    /* n_long uint32: 1 for a long run that the contraction updated (its
+                          chunks are skipped), else 0 */
+  size_t dense_rows;   /* T x 64 uint32x4 {start, len, row, long index}: each table's hot rows,
+                          the first dense_count[t] entries valid */
+  size_t dense_count;  /* T uint32: hot rows per table */
   size_t total;        /* bytes needed */
   int32_t num_buckets; /* nb */
 } tbe_ws_views;
@@ -407,6 +414,8 @@ int tbe_prof_calibrate(int32_t launches, void* stream);
                                          from here on (default 8 Mi) */
 #define TBE_KNOB_WAIT_POLLS 4         /* polls before a look-back wait gives up (default
                                          2^20; 0: a tile with predecessors gives up at once) */
+#define TBE_KNOB_DENSE_LOOKUPS 5      /* the hot-row contraction of long runs from this many
+                                         lookups on (default 8 Mi) */
 int tbe_test_knob(int32_t knob, int64_t value);
 
 /* Static text for a status code. */

@@ -29,7 +29,7 @@ from ._lib import (  # noqa: F401
     tbe_workspace_size, tbe_workspace_views, tbe_test_knob, TBE_KNOB_RLE_DEEP_LOOKUPS,
     TBE_KNOB_BWD_DEEP_LOOKUPS, TBE_KNOB_BWD_STREAM_LOOKUPS, TBE_KNOB_WAIT_POLLS,
     tbe_backward_rowwise_adagrad_noalloc, TBE_E_TOO_LARGE, TBE_STATIC_WS_BYTES,
-    tbe_forward_checked, TBE_FWD_SAVE_HIST)
+    tbe_forward_checked, TBE_FWD_SAVE_HIST, TBE_KNOB_DENSE_LOOKUPS)
 
 
 class TBE:

@@ -58,7 +58,8 @@ class WsViews(C.Structure):
                                            "sorted_scale", "run_start", "run_key", "single_task", "tiny_task",
                                            "medium_task", "long_task", "long_cbeg",
                                            "chunk_task", "chunk_perm", "counters", "prep_error",
-                                           "hist_counts", "total")] + [
+                                           "hist_counts", "long_flag", "dense_rows", "dense_count",
+                                           "total")] + [
         ("num_buckets", C.c_int32)]
 
 
@@ -302,6 +303,7 @@ TBE_OPT_ROWWISE_ADAGRAD, TBE_OPT_ADAGRAD, TBE_OPT_SGD = 0, 1, 2
 
 TBE_KNOB_RLE_DEEP_LOOKUPS, TBE_KNOB_BWD_DEEP_LOOKUPS = 1, 2
 TBE_KNOB_BWD_STREAM_LOOKUPS, TBE_KNOB_WAIT_POLLS = 3, 4
+TBE_KNOB_DENSE_LOOKUPS = 5
 
 
 def tbe_test_knob(knob: int, value: int) -> None:

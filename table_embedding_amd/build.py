@@ -13,8 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libtbe_hip.so")
-SOURCES = ["tbe_api.hip", "fwd_pool.hip", "fwd_hist.hip", "prep.hip", "bwd.hip", "bwd_hist.hip",
-           "validate.hip"]
+SOURCES = ["tbe_api.hip", "fwd_pool.hip", "fwd_hist.hip", "prep.hip", "bwd.hip", "bwd_dense.hip",
+           "bwd_hist.hip", "validate.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

@@ -678,6 +678,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a, BucketSe
     const uint32_t cp = a.chunk_perm ? a.chunk_perm[c] : c;  // position of the chunk taken
     const uint4 task = a.chunk_task[cp];  // {start, len, table, long index}
     if (cp < beg || cp >= end || !chunk_ok(a, task)) continue;  // uniform; never for valid lists
+    if (a.long_flag && a.long_flag[task.w]) continue;  // a hot row: the contraction's
     const TableDev td = a.tables[task.z];
     wg_gather<VEC, NC, IF>(a, bk, td, task.z, task.x, task.x + task.y, sm);
     chunk_store<VEC, NC, false>(a, bk, td.dim, cp, sm);
@@ -696,6 +697,7 @@ __global__ __launch_bounds__(kThreads) void bwd_long_update_kernel(BwdArgs a, Bu
   const uint32_t end = min(list_begin(a, 3, bucket + 1), a.max_long);
   for (uint32_t l = beg + lb; l < end; l += lg) {
     if (!long_ok(a, l)) continue;  // uniform per workgroup; never for valid lists
+    if (a.long_flag && a.long_flag[l]) continue;  // a hot row: the contraction's
     long_update<WD, VEC, NC, false, NT>(a, bk, l, sm);
   }
 }
@@ -729,6 +731,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_fused_kernel(BwdArgs a, Bu
     const uint4 task = a.chunk_task[cp];  // {start, len, table, long index}
     if (cp < beg || cp >= end || !chunk_ok(a, task) || !long_ok(a, task.w))
       continue;  // uniform per workgroup; never for valid lists
+    if (a.long_flag && a.long_flag[task.w]) continue;  // a hot row: the contraction's
     const TableDev td = a.tables[task.z];
     wg_gather<VEC, NC, IF>(a, bk, td, task.z, task.x, task.x + task.y, sm);
     chunk_store<VEC, NC, true>(a, bk, td.dim, cp, sm);
@@ -750,6 +753,32 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_fused_kernel(BwdArgs a, Bu
     }
     __syncthreads();
   }
+}
+
+// Hot rows of the contraction (bwd_dense.hip): one workgroup per (table,
+// hot row slot); the row gradient is the sum of the contraction's dense_w
+// partials in workgroup order, then the optimizer of every row update.
+template <int WD>
+__global__ __launch_bounds__(kThreads) void dense_update_kernel(BwdArgs a) {
+  if (prep_failed(a)) return;
+  constexpr int VEC = 4;
+  __shared__ WgSmem<VEC, 1> sm;
+  const uint32_t t = blockIdx.x / kDenseRows, k = blockIdx.x % kDenseRows;
+  if (k >= min(a.dense_cnt[t], (uint32_t)kDenseRows)) return;
+  const uint4 task = a.dense_rows[(size_t)t * kDenseRows + k];  // {start, len, row, long index}
+  const TableDev td = a.tables[t];
+  if (task.z >= td.rows) return;  // never, for rows the selection wrote
+  const uint32_t D = td.dim;
+  const float* part = a.dense_part + ((size_t)t * kDenseRows + k) * a.dense_w * kDensePitch;
+  float sqp = 0.f;
+  for (uint32_t col = threadIdx.x; col < D; col += kThreads) {
+    float g = 0.f;
+    for (uint32_t w = 0; w < a.dense_w; ++w) g += part[(size_t)w * kDensePitch + col];
+    sm.gsum[col] = g;
+    sqp += g * g;
+  }
+  RowPre<VEC> unused;
+  wg_row_update<WD, VEC, 1, false, false>(a, td, (int64_t)task.z, sqp, sm, unused);
 }
 
 // Co-resident workgroups of a kernel on the whole device (queried once per
@@ -880,6 +909,17 @@ hipError_t launch(const BwdArgs& a, BucketSet S, const BwdGrids* g, bool fused, 
 }
 
 }  // namespace
+
+hipError_t launch_dense_update(const BwdArgs& a, int wd, hipStream_t s) {
+  const dim3 grid(a.T * (uint32_t)kDenseRows), block(kThreads);
+  if (wd == WD_F32)
+    TBE_LAUNCH("dense_update", dense_update_kernel<WD_F32>, grid, block, s, a);
+  else if (wd == WD_F16)
+    TBE_LAUNCH("dense_update", dense_update_kernel<WD_F16>, grid, block, s, a);
+  else
+    TBE_LAUNCH("dense_update", dense_update_kernel<WD_BF16>, grid, block, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_chunk_order(const BwdArgs& a, hipStream_t s) {
   if (a.T == 0 || !a.chunk_perm) return hipSuccess;

@@ -74,6 +74,7 @@ struct tbe_plan {
   uint32_t* d_bkb;
   void* d_mem;
   int num_cus;
+  int dense_dt;  // hot-row contraction: 16-column tiles per wave (0: no table can take it)
   // backward fork/join: two default-priority side streams and their events;
   // the lock keeps the record/wait sequence of one call from interleaving
   // with another call's on the same plan
@@ -108,6 +109,11 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 bool bwd_hist_capable(const tbe_plan* P) {
   return P->T == 1 && P->rows[0] <= 64 && P->dims[0] % 16 == 0 && P->dims[0] <= 128;
 }
+
+// The hot-row contraction: workgroups per table, and the most tables a plan
+// may have for it (its partials take T x 1 MiB of workspace).
+constexpr uint32_t kDenseWgsPerTable = 16;
+constexpr int kDenseMaxTables = 128;
 
 // TBE_BWD_CONCURRENT_AUTO forks the run classes below this many lookups.
 // Measured on MI355X (ms per step, one stream / three): 2.1 M lookups 0.333 /
@@ -184,6 +190,11 @@ WsLayout layout(const tbe_plan* P, int64_t N) {
   // average bag length of 64) and E <= 64, so at most 2 N + 128 bytes
   L.hist_save = take(hc ? 2 * n + 128 : 0);
   L.hist_hdr = take(hc ? 16 : 0);
+  const bool dc = P->dense_dt > 0;
+  L.long_flag = take(dc ? (size_t)L.max_long * 4 : 0);
+  L.dense_rows = take(dc ? (size_t)P->T * kDenseRows * 16 : 0);
+  L.dense_cnt = take(dc ? (size_t)P->T * 4 : 0);
+  L.dense_part = take(dc ? (size_t)P->T * kDenseRows * kDenseWgsPerTable * kDensePitch * 4 : 0);
   L.total = off;
   return L;
 }
@@ -332,7 +343,7 @@ namespace tbe {
 namespace {
 // test knob overrides; a negative value means "not set"
 std::atomic<int64_t> g_knob_rle_deep{-1}, g_knob_bwd_deep{-1}, g_knob_bwd_stream{-1},
-    g_knob_polls{-1};
+    g_knob_polls{-1}, g_knob_dense{-1};
 int64_t knob_or(const std::atomic<int64_t>& k, int64_t dflt) {
   const int64_t v = k.load(std::memory_order_relaxed);
   return v < 0 ? dflt : v;
@@ -342,6 +353,7 @@ int64_t knob_or(const std::atomic<int64_t>& k, int64_t dflt) {
 int64_t knob_rle_deep_lookups() { return knob_or(g_knob_rle_deep, kRleDeepLookups); }
 int64_t knob_bwd_deep_lookups() { return knob_or(g_knob_bwd_deep, kBwdDeepLookups); }
 int64_t knob_bwd_stream_lookups() { return knob_or(g_knob_bwd_stream, kBwdStreamRowsLookups); }
+int64_t knob_dense_lookups() { return knob_or(g_knob_dense, kDenseMinLookups); }
 uint32_t knob_wait_polls() {
   const int64_t v = knob_or(g_knob_polls, kSpinLimit);
   return v > (int64_t)0xffffffffll ? 0xffffffffu : (uint32_t)v;
@@ -369,6 +381,7 @@ int tbe_test_knob(int32_t knob, int64_t value) {
     case TBE_KNOB_BWD_DEEP_LOOKUPS: k = &tbe::g_knob_bwd_deep; break;
     case TBE_KNOB_BWD_STREAM_LOOKUPS: k = &tbe::g_knob_bwd_stream; break;
     case TBE_KNOB_WAIT_POLLS: k = &tbe::g_knob_polls; break;
+    case TBE_KNOB_DENSE_LOOKUPS: k = &tbe::g_knob_dense; break;
     default: return TBE_E_ARG;
   }
   k->store(value < 0 ? -1 : value, std::memory_order_relaxed);
@@ -470,6 +483,12 @@ int tbe_plan_create(tbe_plan** out, int32_t T, const int64_t* rows, const int32_
   P->dtot = (uint32_t)dtot;
   P->row_bits = 0;
   for (int t = 0; t < T; ++t) P->row_bits = std::max(P->row_bits, ilog2((uint64_t)rows[t]));
+  {  // hot-row contraction: tables with D a multiple of 16 up to kDensePitch
+    int dmax = 0;
+    for (int t = 0; t < T; ++t)
+      if (dims[t] % 16 == 0 && dims[t] <= kDensePitch) dmax = std::max(dmax, (int)dims[t]);
+    P->dense_dt = (T > kDenseMaxTables || dmax == 0) ? 0 : dmax <= 64 ? 1 : dmax <= 128 ? 2 : 4;
+  }
 
   // buckets by next_pow2(D), ascending width; tables keep ascending id inside a bucket
   std::vector<uint32_t> widths;
@@ -634,6 +653,9 @@ int tbe_workspace_views(const tbe_plan* P, int64_t B, int64_t N, tbe_ws_views* v
   v->counters = L.counters;
   v->prep_error = L.ctl + (size_t)kCtlErr * 4;
   v->hist_counts = L.hist_save;
+  v->long_flag = L.long_flag;
+  v->dense_rows = L.dense_rows;
+  v->dense_count = L.dense_cnt;
   v->total = L.total;
   v->num_buckets = (int32_t)P->buckets.size();
   return TBE_OK;
@@ -920,7 +942,22 @@ int run_backward(const tbe_plan* P, int64_t B, int32_t itype, const void* indice
         hipStreamWaitEvent(ss[2], P->ev_fork, 0) != hipSuccess)
       return TBE_E_HIP;
   }
+  // the hottest long runs by the contraction (their chunks and long-run
+  // updates are skipped), on the long runs' stream before their kernels;
+  // batches without per-sample weights only (integer counts)
+  const bool dense = P->dense_dt > 0 && psw == nullptr && N >= knob_dense_lookups();
+  if (dense) {
+    a.indices = indices;
+    a.long_flag = reinterpret_cast<uint32_t*>(w + L.long_flag);
+    a.dense_rows = reinterpret_cast<uint4*>(w + L.dense_rows);
+    a.dense_cnt = reinterpret_cast<uint32_t*>(w + L.dense_cnt);
+    a.dense_part = reinterpret_cast<float*>(w + L.dense_part);
+    a.dense_w = kDenseWgsPerTable;
+    a.dense_min_len = (uint32_t)std::max<int64_t>(kLongRun, std::min<int64_t>(B / 32, 1ll << 30));
+  }
   int rc_launch = TBE_OK;
+  if (dense && launch_dense(a, P->d_tseg, P->wdtype, itype, P->dense_dt, ss[2]) != hipSuccess)
+    rc_launch = TBE_E_HIP;
   if (launch_chunk_order(a, ss[2]) != hipSuccess) rc_launch = TBE_E_HIP;
   for (const auto& grp : bucket_groups(P)) {
     if (rc_launch != TBE_OK) break;

@@ -27,6 +27,9 @@ constexpr int64_t kBwdDeepLookups = 64ll << 20;
 constexpr int64_t kBwdStreamRowsLookups = 8ll << 20;
 // Polls after which a look-back wait of the preprocessing gives up.
 constexpr uint32_t kSpinLimit = 1u << 20;
+// Lookup count from which the backward updates the hottest long runs by the
+// hot-row contraction (bwd_dense.hip).
+constexpr int64_t kDenseMinLookups = 8ll << 20;
 
 // Test knobs (tbe_test_knob): process-wide overrides of the thresholds above
 // and of the poll limit, so that small inputs can run the variants that
@@ -36,6 +39,7 @@ int64_t knob_rle_deep_lookups();
 int64_t knob_bwd_deep_lookups();
 int64_t knob_bwd_stream_lookups();
 uint32_t knob_wait_polls();
+int64_t knob_dense_lookups();
 
 constexpr int kLongRun = 256;       // SL >= 256 takes the chunked long-run path
 constexpr int kTinyRun = 32;        // short runs below this are owned by a lane subgroup
@@ -128,6 +132,7 @@ struct WsLayout {
   size_t chunk_perm;  // max_chunks uint32: chunk list position taken at each walk position
   size_t hist_part, hist_cnt;  // histogram backward: partial rows and row counts (or 0 bytes)
   size_t hist_save, hist_hdr;  // row counts per bag saved by the histogram forward, {B, N}
+  size_t long_flag, dense_rows, dense_cnt, dense_part;  // hot-row contraction (or 0 bytes)
   size_t total;
   uint32_t ntiles;          // ceil(N / kTile)
   uint32_t nrle_tiles;      // ceil(N / (rle_groups * kTile)): tiles of the run-length pass
@@ -512,7 +517,22 @@ struct BwdArgs {
   const uint32_t* prep_err;  // the preprocessing's error flag: nonzero, nothing is written
   uint32_t N, T;             // lookups and tables (task sanity bounds)
   uint32_t max_single, max_tiny, max_med, max_long, max_chunks;  // list capacities
+  // hot-row contraction (null / 0 when off): see bwd_dense.hip
+  const void* indices;       // the batch's indices (the contraction reads them in bag order)
+  uint32_t* long_flag;       // per long run: 1 if its row is updated by the contraction
+  uint4* dense_rows;         // T x kDenseRows {start, len, row, long index} of each table's hot rows
+  uint32_t* dense_cnt;       // T: hot rows per table
+  float* dense_part;         // T x kDenseRows x dense_w partial rows of kDensePitch floats
+  uint32_t dense_w;          // workgroups per table of the contraction
+  uint32_t dense_min_len;    // smallest run length the contraction takes
 };
+
+// Hot-row contraction of the long runs: per table, up to kDenseRows long runs
+// of at least dense_min_len lookups (tables with D a multiple of 16 and at
+// most kDensePitch columns), their gradients as one counts x grad_out
+// contraction over the table's bags on the matrix cores.
+constexpr int kDenseRows = 64;
+constexpr int kDensePitch = 256;
 
 // Histogram-reuse backward of a plan with one table of at most 64 rows and
 // D <= 128, D a multiple of 16.
@@ -579,5 +599,14 @@ hipError_t launch_backward_hist(const HistArgs& h, int itype, int wd, hipStream_
 // Orders each (table, XCD residue) class of the chunk list by the bag of the
 // chunks' first lookups into a.chunk_perm (no-op when a.chunk_perm is null).
 hipError_t launch_chunk_order(const BwdArgs& a, hipStream_t s);
+// The hot-row contraction (a.long_flag set): selection of each table's hot
+// rows (tseg: segment of each table in key order), the contraction's
+// partials, and the rows' update (optimizer a.opt, weight storage wd).
+// dt: 16-column tiles per wave (the widest eligible D / 64, rounded up to 1, 2 or 4).
+hipError_t launch_dense(const BwdArgs& a, const uint32_t* tseg, int wd, int itype, int dt,
+                        hipStream_t s);
+// The update of each hot row from its partials (in bwd.hip, beside the other
+// row updates).
+hipError_t launch_dense_update(const BwdArgs& a, int wd, hipStream_t s);
 
 }  // namespace tbe

@@ -431,3 +431,64 @@ class WorkspaceLists:
             assert b[0] == 0 and b[-1] == len(tab), name
             for q in range(self.nb):
                 assert np.all(bt[tab[b[q]:b[q + 1]]] == q), name
+
+
+def expected_hot_rows(case: Case):
+    """Per table, the (row, run length) pairs that the hot-row contraction
+    takes, from the host inputs by the selection rule: among the table's long
+    runs (run length >= 256), those that reach a threshold which starts at
+    max(256, B / 32) and doubles until at most 64 runs reach it; tables whose
+    D is not a multiple of 16 or exceeds 256 take none.  Rows ascending (the
+    long list's key order within a table)."""
+    spec, B = case.spec, case.spec.B
+    min_len = max(256, min(B // 32, 1 << 30))
+    out = []
+    for t in range(spec.T):
+        D = spec.dims[t]
+        if D % 16 or D > 256:
+            out.append([])
+            continue
+        lo, hi = int(case.off[t * B]), int(case.off[(t + 1) * B])
+        rows, lens = np.unique(case.idx[lo:hi].astype(np.int64), return_counts=True)
+        keep = lens >= 256
+        rows, lens = rows[keep], lens[keep]
+        thr = min_len
+        for _ in range(32):
+            if int((lens >= thr).sum()) <= 64:
+                break
+            thr = min(thr * 2, 0xffffffff)
+        sel = lens >= thr
+        out.append(list(zip(rows[sel].tolist(), lens[sel].tolist())))
+    return out
+
+
+def check_dense(case: Case, tbe_obj):
+    """After a backward that took the hot-row contraction: each table's hot
+    rows and their count equal the host selection, each entry names its long
+    run, and long_flag marks exactly the hot runs (integers, bit for bit)."""
+    import table_embedding_amd as te
+    spec = case.spec
+    v = te.tbe_workspace_views(tbe_obj.plan, spec.B, case.N)
+    ws = tbe_obj._ws
+    nb = v["num_buckets"]
+    cnt = read_u32(ws, v["counters"], 6 + 5 * (nb + 1))
+    nl = int(cnt[4])
+    lt = read_u32x4(ws, v["long_task"], nl).astype(np.int64)
+    flag = read_u32(ws, v["long_flag"], nl)
+    dcnt = read_u32(ws, v["dense_count"], spec.T)
+    drows = read_u32x4(ws, v["dense_rows"], spec.T * 64).reshape(spec.T, 64, 4).astype(np.int64)
+    exp = expected_hot_rows(case)
+    hot = set()
+    for t in range(spec.T):
+        assert int(dcnt[t]) == len(exp[t]), f"table {t}: {int(dcnt[t])} hot rows, expected {len(exp[t])}"
+        got = drows[t, :len(exp[t])]
+        assert [(int(r[2]), int(r[1])) for r in got] == exp[t], f"table {t}: hot rows differ"
+        for r in got:
+            li = int(r[3])
+            assert 0 <= li < nl and lt[li, 3] == t and np.array_equal(lt[li, :3], r[:3]), \
+                f"table {t}: hot row {int(r[2])} does not name its long run"
+            hot.add(li)
+    want = np.zeros(nl, np.uint32)
+    want[sorted(hot)] = 1
+    assert np.array_equal(flag, want), "long_flag differs from the hot runs"
+    return sum(len(e) for e in exp)

@@ -24,7 +24,8 @@ pytestmark = pytest.mark.gpu
 def knobs(**kv):
     import table_embedding_amd as te
     names = {"rle_deep": te.TBE_KNOB_RLE_DEEP_LOOKUPS, "bwd_deep": te.TBE_KNOB_BWD_DEEP_LOOKUPS,
-             "bwd_stream": te.TBE_KNOB_BWD_STREAM_LOOKUPS, "polls": te.TBE_KNOB_WAIT_POLLS}
+             "bwd_stream": te.TBE_KNOB_BWD_STREAM_LOOKUPS, "polls": te.TBE_KNOB_WAIT_POLLS,
+             "dense": te.TBE_KNOB_DENSE_LOOKUPS}
     try:
         for k, v in kv.items():
             te.tbe_test_knob(names[k], v)
@@ -34,15 +35,32 @@ def knobs(**kv):
             te.tbe_test_knob(k, -1)
 
 
-DEEP = ["C2s", "C3s", "C5s", "many_tables", "const257", "heavy_chunks", "wide_f32", "cut_bags"]
+DEEP = ["C2s", "C3s", "C5s", "many_tables", "const257", "heavy_chunks", "wide_f32", "cut_bags",
+        "dense_mean", "dense_many"]
 
 
-@pytest.mark.parametrize("variant", ["deep", "stream"])
+def _takes_dense(spec):
+    """The backward takes the hot-row contraction (when its lookup threshold
+    is met) for batches without per-sample weights on plans of at most 128
+    tables with a table whose D is a multiple of 16 and at most 256."""
+    return (not spec.weighted and spec.T <= 128
+            and any(d % 16 == 0 and d <= 256 for d in spec.dims))
+
+
+VARIANTS = {"deep": dict(rle_deep=0, bwd_deep=0, dense=1 << 40), "stream": dict(bwd_stream=0),
+            "dense": dict(dense=0), "dense_deep": dict(rle_deep=0, bwd_deep=0, dense=0),
+            "no_dense": dict(dense=1 << 40)}
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
 @pytest.mark.parametrize("name", DEEP)
 def test_deep_batch_variants_parity(name, variant):
+    """Each variant at scaled sizes: "dense" runs the hot-row contraction of
+    the long runs (which deep batches take from 8 Mi lookups on), "no_dense"
+    keeps every long run on the chunk path."""
     import table_embedding_amd as te
     _announce(name, f"{variant} variants")
-    kv = dict(rle_deep=0, bwd_deep=0) if variant == "deep" else dict(bwd_stream=0)
+    kv = VARIANTS[variant]
     case = S.Case(_spec(name), m_nonzero=True)
     with knobs(**kv):
         tb = case.tbe()
@@ -59,6 +77,8 @@ def test_deep_batch_variants_parity(name, variant):
             torch.cuda.synchronize()
             if flags == 0:
                 S.check_backward(case, tb)
+            if kv.get("dense") == 0 and _takes_dense(case.spec):
+                S.check_dense(case, tb)
             res.append(_tables_bytes(tb, case.spec.wdtype))
             tb.close()
         assert res[0] == res[1], "fused differs from two-launch"
@@ -102,3 +122,35 @@ def test_wait_give_up_writes_nothing(name):
     assert int(S.read_u32(tb._ws, v["prep_error"], 1)[0]) == 0
     S.check_backward(case, tb)
     tb.close()
+
+
+@pytest.mark.parametrize("name", ["dense_mean", "C5s", "heavy_chunks"])
+@pytest.mark.parametrize("optimizer", ["adagrad", "sgd"])
+def test_dense_rows_with_other_optimizers(name, optimizer):
+    """The hot rows' update takes the element-wise Adagrad and SGD epilogues
+    too: against the oracle, each touched row once, fused = two-launch."""
+    import oracle
+    import table_embedding_amd as te
+    from tests.test_gpu_optimizers import _gabs, _run, epilogue_weights_ok
+    _announce(name, f"dense rows, {optimizer}")
+    case = S.Case(_spec(name))
+    spec = case.spec
+    with knobs(dense=0):
+        W, A, A0, cnt = _run(case, optimizer)
+        Wf, Af, _, _ = _run(case, optimizer, te.TBE_BWD_FUSED_LONG)
+    Wr = [w.copy() for w in case.W]
+    Ar = [a.copy() for a in A0]
+    oracle.backward(spec.rows, spec.dims, spec.pooling, spec.wdtype, Wr,
+                    Ar if optimizer == "adagrad" else None, spec.B, spec.itype, case.idx,
+                    case.off, case.psw, case.G, spec.lr, spec.eps, optimizer=optimizer)
+    for t in range(spec.T):
+        mask = np.zeros(spec.rows[t], bool)
+        mask[S.touched_rows(case, t)] = True
+        W0 = case.W[t].reshape(spec.rows[t], spec.dims[t])
+        Aref = Ar[t][mask] if optimizer == "adagrad" else None
+        ok, v = epilogue_weights_ok(W[t][mask], Wr[t].reshape(spec.rows[t], spec.dims[t])[mask],
+                                    W0[mask], spec.wdtype, optimizer, spec.lr,
+                                    _gabs(case, t)[mask], Aref)
+        assert ok, f"table {t}: weight tolerance exceeded ({v})"
+        assert np.array_equal(cnt[t], mask.astype(np.uint32)), f"table {t}: each touched row once"
+        assert W[t].tobytes() == Wf[t].tobytes() and A[t].tobytes() == Af[t].tobytes()

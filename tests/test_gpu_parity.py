@@ -78,6 +78,16 @@ def _spec(name):
         # which the whole workgroup places
         return wl.Spec("heavy_chunks", 2010, [32], [16], [0], "f32", 4096, "fixed:256",
                        "uniform", "i32", False)
+    if name == "dense_mean":
+        # hot rows of mean and sum tables without per-sample weights (integer
+        # counts times 1/L), D = 256 beside narrower tiles, and a D = 40
+        # table that cannot take the contraction
+        return wl.Spec("dense_mean", 2014, [5000, 3000, 800, 2000], [128, 64, 40, 256],
+                       [1, 0, 1, 1], "f16", 2048, "uniform:1:64", "zipf:1.2", "i64", False)
+    if name == "dense_many":
+        # 108 long runs: the hot-row threshold doubles once (55 rows reach it)
+        return wl.Spec("dense_many", 2015, [3000], [32], [0], "bf16", 4096, "fixed:64",
+                       "zipf:1.05", "i32", False)
     if name == "rows_21b":
         # 21 row bits: three 8-bit radix passes (an odd count) at a small size
         return wl.Spec("rows_21b", 2012, [(1 << 20) + 3, 50], [8, 16], [0, 1], "f16", 300,
@@ -92,7 +102,7 @@ def _spec(name):
 MAIN = ["C1", "C2s", "C3s", "C4s", "C5s"]
 EDGE = ["empty_bags", "all_empty", "one_bag", "one_row", "const31", "const32", "const255",
         "const256", "const257", "wide_f32", "wide_bf16", "many_tables", "many_bags",
-        "heavy_chunks", "cut_bags", "rows_21b", "rows_25b"]
+        "heavy_chunks", "cut_bags", "dense_mean", "rows_21b", "rows_25b"]
 
 
 def _announce(name, what):
