@@ -131,7 +131,7 @@ typedef struct {
    * take it; written only by a backward that takes it): */
   size_t long_flag;    /* n_long uint32: 1 for a long run that the contraction updated (its
                           chunks are skipped), else 0 */
-  size_t dense_rows;   /* T x 64 uint32x4 {start, len, row, long index}: each table's hot rows,
+  size_t dense_rows;   /* T x 128 uint32x4 {start, len, row, long index}: each table's hot rows,
                           the first dense_count[t] entries valid */
   size_t dense_count;  /* T uint32: hot rows per table */
   size_t total;        /* bytes needed */

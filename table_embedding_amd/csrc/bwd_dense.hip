@@ -4,43 +4,48 @@
 // section "Fusion boundaries": the backward can reuse such a histogram).
 //
 // The same algebra serves the hottest rows of a large table in the backward.
-// A run of SL lookups gathers SL grad_out rows; for the few rows of a table
-// whose runs are long enough to touch a large share of the table's bags, the
-// row gradients are one contraction over the bags,
+// A run of SL lookups gathers SL grad_out rows; for the rows of a table whose
+// runs are long enough, the row gradients are one contraction over the bags,
 //   grad[h][d] = sum_b C[b][h] * G[b][c_t + d],
-// with C[b][h] the sum of the contribution scales S[p] * (1/L_b if mean) of
-// bag b's lookups of hot row h.  Computed that way, each of the table's
-// grad_out rows is read once instead of once per lookup of every hot row (on
-// a 64-table batch of 138 M lookups the long runs' gathers read 25 GB from
-// beyond the L2 per step; their hottest rows hold about four fifths of those
-// lookups).
+// with C[b][h] the number of bag b's lookups of hot row h, and G scaled by
+// 1/L_b for a mean table.  Computed that way, each of the table's grad_out
+// rows is read once instead of once per lookup of every hot row (on a
+// 64-table batch of 138 M lookups the long runs' gathers read 25 GB from
+// beyond the L2 per step).
 //
 // dense_select_kernel (one workgroup per table): the table's long runs, in
-// the long list's key order, are the candidates; the threshold starts at
-// dense_min_len and doubles until at most kDenseRows runs reach it; those
-// runs become the table's hot rows (flagged in long_flag, so that the chunk
-// and long-run update kernels skip them).  Tables whose D is not a multiple
-// of 16 or exceeds kDensePitch take none.
+// the long list's key order, are the candidates; the threshold is the
+// smallest length of at least dense_min_len that at most kDenseRows runs
+// reach (a binary search over lengths); those runs become the table's hot
+// rows (flagged in long_flag, so that the chunk and long-run update kernels
+// skip them).  Tables whose D is not a multiple of 16 or exceeds kDensePitch
+// take none.
 //
-// dense_partial_kernel (dense_w workgroups per table, each a contiguous
-// range of the table's bags): per block of K bags (128; 64 when a wave owns
-// four column tiles), the block's lookups are read coalesced, a lookup of a
+// dense_partial_kernel (dense_w workgroups per table and column group of
+// 64 * DT columns, each a contiguous range of the table's bags): per block of
+// 64 bags, the block's lookups are read coalesced, a lookup of a
 // hot row (found in a small open-addressing table in LDS) finds its bag by
 // binary search over the block's bag boundaries, and one integer LDS atomic
 // adds it to C's count.  Integer counts are exact in any order, so the
-// result does not depend on the atomics' timing; with mean pooling the count
-// is multiplied by 1/L_b when it enters the product.  The block's grad_out
+// result does not depend on the atomics' timing.  The block's grad_out
 // operands are loaded into registers first, so they arrive while the counts
-// are built.  Then C^T [hot rows x K bags] x G [K bags x D] on
-// v_mfma_f32_16x16x4f32 (fp32: the counts enter exactly and the gradients
-// unrounded): wave w owns the 16-column tiles [w*DT, (w+1)*DT) for all row
-// tiles, so every grad_out element of the block is loaded once, and the
-// accumulators stay in registers across the workgroup's blocks.  Each
-// workgroup writes its partial rows; the update kernel (bwd.hip) adds the
-// dense_w partials of a row in workgroup order and applies the optimizer.
-// Every floating-point sum has a data-determined order, so repeated calls
-// give the same bits, and the fused and two-launch long-run paths, which both
-// leave the hot rows to this contraction, stay bit-identical.
+// are built.  Then C^T [hot rows x K bags] x G [K bags x D] on the matrix
+// cores, exact in its products: when no bag of the block has more than 255
+// lookups, every count is an integer of at most 8 bits, exact in bfloat16,
+// and each fp32 gradient is the exact sum of three bfloat16 parts (its
+// significand cut into three 8-bit pieces), so three
+// v_mfma_f32_16x16x32_bf16 per tile give the fp32 products without rounding;
+// otherwise each count is cut into four 8-bit parts and the block takes
+// four such passes.  Either way the products are exact and only the
+// fp32 accumulation rounds.
+// Wave w owns the 16-column tiles [w*DT, (w+1)*DT) for all row tiles, so
+// every grad_out element of the block is loaded once, and the accumulators
+// stay in registers across the workgroup's blocks.  Each workgroup writes its
+// partial rows; the update kernel (bwd.hip) adds the dense_w partials of a
+// row in workgroup order and applies the optimizer.  Every floating-point sum
+// has a data-determined order, so repeated calls give the same bits, and the
+// fused and two-launch long-run paths, which both leave the hot rows to this
+// contraction, stay bit-identical.
 //
 // Only batches without per-sample weights take this path: with them the
 // coefficients are float sums, which atomics would add in a varying order,
@@ -49,8 +54,6 @@
 
 namespace tbe {
 namespace {
-
-constexpr int kDBags = 128;  // bags per block (K of the block's contraction)
 
 __device__ __forceinline__ bool dense_prep_failed(const BwdArgs& a) { return *a.prep_err != 0u; }
 
@@ -75,6 +78,15 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* sh4) {
   return sh4[0] + sh4[1] + sh4[2] + sh4[3];
 }
 
+__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* sh4) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor(v, o, kWave));
+  __syncthreads();
+  if (lane_id() == 0) sh4[threadIdx.x / kWave] = v;
+  __syncthreads();
+  return max(max(sh4[0], sh4[1]), max(sh4[2], sh4[3]));
+}
+
 __global__ __launch_bounds__(kThreads) void dense_select_kernel(BwdArgs a, const uint32_t* tseg) {
   if (dense_prep_failed(a)) return;
   __shared__ uint32_t sh4[4];
@@ -85,14 +97,26 @@ __global__ __launch_bounds__(kThreads) void dense_select_kernel(BwdArgs a, const
   const uint32_t l0 = long_lower(a, tseg, 0, n_long, tseg[t]);
   const uint32_t l1 = long_lower(a, tseg, l0, n_long, tseg[t] + 1);
   const bool eligible = td.dim % 16u == 0 && td.dim <= (uint32_t)kDensePitch;
-  // the smallest doubling of dense_min_len that at most kDenseRows runs reach
+  // the smallest length >= dense_min_len that at most kDenseRows runs reach
   uint32_t thr = a.dense_min_len > 0 ? a.dense_min_len : 1u;
   if (eligible) {
-    for (int k = 0; k < 32; ++k) {
-      uint32_t c = 0;
-      for (uint32_t l = l0 + threadIdx.x; l < l1; l += kThreads) c += a.long_task[l].y >= thr;
-      if (block_sum(c, sh4) <= (uint32_t)kDenseRows) break;
-      thr = thr >= 0x80000000u ? 0xffffffffu : thr * 2u;
+    uint32_t c = 0, mx = 0;
+    for (uint32_t l = l0 + threadIdx.x; l < l1; l += kThreads) {
+      const uint32_t len = a.long_task[l].y;
+      c += len >= thr;
+      mx = max(mx, len);
+    }
+    if (block_sum(c, sh4) > (uint32_t)kDenseRows) {
+      // count(len >= t) is non-increasing in t and 0 past the longest run:
+      // binary search over (thr, longest + 1]
+      uint32_t lo = thr + 1u, hi = block_max(mx, sh4) + 1u;
+      while (lo < hi) {
+        const uint32_t mid = lo + (hi - lo) / 2u;
+        uint32_t cm = 0;
+        for (uint32_t l = l0 + threadIdx.x; l < l1; l += kThreads) cm += a.long_task[l].y >= mid;
+        if (block_sum(cm, sh4) <= (uint32_t)kDenseRows) hi = mid; else lo = mid + 1u;
+      }
+      thr = lo;
     }
   }
   if (threadIdx.x == 0) s_base = 0;
@@ -123,46 +147,68 @@ __global__ __launch_bounds__(kThreads) void dense_select_kernel(BwdArgs a, const
 }
 
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Open-addressing table of the hot rows in LDS: row -> rank, linear probing,
-// at most 64 of kHashSlots slots in use.  The longest probe distance of an
-// insert bounds every search, so a lookup reads a fixed number of slots
-// (the same for all lanes) instead of probing until an empty slot.
+// at most kDenseRows of kHashSlots slots in use.  The longest probe distance
+// of an insert bounds every search, so a lookup reads a fixed number of
+// slots (the same for all lanes) instead of probing until an empty slot.
 constexpr uint32_t kHashSlots = 1024;
 constexpr uint32_t kHashEmpty = 0xffffffffu;  // no row has this key (rows < 2^32 - 1)
 __device__ __forceinline__ uint32_t hash_slot(uint32_t row) {
   return (row * 2654435761u) >> 22;  // top 10 bits
 }
 
-constexpr int kPer = 8;  // lookups per thread in flight in the counting pass
+constexpr int kPer = 4;  // lookups per thread in flight in the counting pass
+constexpr uint32_t kMaxExactCount = 255;  // counts of at most 8 bits are exact in bfloat16
+constexpr int kRowTiles = kDenseRows / 16;
 
 // Bags per block: K of the block's contraction (a lane holds K/4 * DT
-// grad_out operands of the block in registers).
+// grad_out operands of the block in registers); a workgroup's columns are
+// one group of 64 * DT (four waves of DT 16-column tiles).
 template <int DT>
 struct DenseShape {
-  static constexpr int kBags = DT >= 4 ? 64 : 128;
-  static constexpr int kPitch = kBags + 4;  // count row pitch (words)
-  static constexpr int kSteps = kBags / 4;  // K steps of 4 bags
+  static_assert(DT == 1 || DT == 2, "one or two column tiles per wave");
+  static constexpr int kBags = 64;
+  static constexpr int kPitch = kBags + 4;  // count row pitch (words; = 4 mod 64)
+  static constexpr int kSteps = kBags / 32; // K steps of 32 bags
+  static constexpr uint32_t kGroupCols = 64u * DT;
 };
+
+// The three bfloat16 parts of x, packed for lanes' pairs (x0, x1): x = hi +
+// mid + lo exactly (truncation leaves a remainder of at most 16, then 8,
+// significant bits).  Element 2j of an 8-vector is the low half of dword j.
+__device__ __forceinline__ void split3(float x0, float x1, uint32_t& hi, uint32_t& mid,
+                                       uint32_t& lo) {
+  const uint32_t h0 = __float_as_uint(x0) & 0xffff0000u, h1 = __float_as_uint(x1) & 0xffff0000u;
+  const float r0 = x0 - __uint_as_float(h0), r1 = x1 - __uint_as_float(h1);
+  const uint32_t m0 = __float_as_uint(r0) & 0xffff0000u, m1 = __float_as_uint(r1) & 0xffff0000u;
+  const uint32_t l0 = __float_as_uint(r0 - __uint_as_float(m0)),
+                 l1 = __float_as_uint(r1 - __uint_as_float(m1));
+  hi = (h0 >> 16) | h1;
+  mid = (m0 >> 16) | m1;
+  lo = (l0 >> 16) | (l1 & 0xffff0000u);
+}
 
 template <typename IT, int DT>
 __global__ __launch_bounds__(kThreads) void dense_partial_kernel(BwdArgs a) {
   using S = DenseShape<DT>;
   if (dense_prep_failed(a)) return;
-  // counts of the block, [hot row][bag]; bag k is consumed in K step k % kSteps
-  // by lane group k / kSteps, so that a lane's A operands of four consecutive
-  // K steps are one 16-byte read, and the 16 rows of a tile fall in distinct
-  // banks (pitch = 4 mod 64 words)
+  // counts of the block, [hot row][bag] (integer atomic adds: exact in any
+  // order); the 16 rows of a tile fall in distinct banks
   __shared__ __attribute__((aligned(16))) uint32_t cnt[kDenseRows][S::kPitch];
-  __shared__ __attribute__((aligned(16))) float s_inv[S::kBags];  // mean: 1 / bag length
+  __shared__ __attribute__((aligned(16))) float s_inv[S::kBags];  // 1 / bag length (mean)
   __shared__ uint32_t s_key[kHashSlots];
   __shared__ uint8_t s_hrank[kHashSlots];
   __shared__ uint32_t s_dmax;  // longest probe distance of an insert
   __shared__ uint32_t s_off[S::kBags + 1];  // positions (< 2^31)
-  const uint32_t t = blockIdx.x / a.dense_w, w = blockIdx.x % a.dense_w;
+  // workgroup = (table, bag range, column group)
+  const uint32_t cg = blockIdx.x % a.dense_ncg, tw = blockIdx.x / a.dense_ncg;
+  const uint32_t t = tw / a.dense_w, w = tw % a.dense_w;
   const uint32_t H = min(a.dense_cnt[t], (uint32_t)kDenseRows);
-  if (H == 0) return;
   const TableDev td = a.tables[t];
+  if (H == 0 || cg * S::kGroupCols >= td.dim) return;
   const uint32_t D = td.dim;
   const bool mean = td.pooling == POOL_MEAN;
   const IT* __restrict__ I = reinterpret_cast<const IT*>(a.indices);
@@ -184,9 +230,9 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(BwdArgs a) {
   const uint32_t wave = threadIdx.x / kWave, lane = lane_id();
   const uint32_t i = lane & 15u, kq = lane >> 4;  // A row / B column; K lane group
   const uint32_t nrt = (H + 15u) / 16u;           // row tiles in use
-  float4v acc[4][DT];
+  float4v acc[kRowTiles][DT];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int rt = 0; rt < kRowTiles; ++rt)
 #pragma unroll
     for (int nt = 0; nt < DT; ++nt) acc[rt][nt] = (float4v){0.f, 0.f, 0.f, 0.f};
   // this workgroup's bags [b_lo, b_hi) of the table
@@ -195,38 +241,58 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(BwdArgs a) {
   const int64_t b_hi = B * (int64_t)(w + 1) / (int64_t)a.dense_w;
   const int64_t jt = (int64_t)t * B;  // the table's first bag
   const float* gtab = a.grad + td.col;
+  const uint32_t c0 = cg * S::kGroupCols + wave * (uint32_t)DT * 16u + i;  // this lane's first column
+  // first lookup of the current block (the previous block's end)
+  uint32_t P0 = 0;
+  if (b_lo < b_hi) {
+    const int64_t o = (int64_t)O[jt + b_lo];
+    P0 = (uint32_t)(o < 0 ? 0 : (o > N ? N : o));
+  }
   for (int64_t j0 = b_lo; j0 < b_hi; j0 += S::kBags) {
     const uint32_t nb = (uint32_t)min((int64_t)S::kBags, b_hi - j0);
-    // the block's grad_out operands of this lane (bag kq * kSteps + ks, this
-    // wave's columns), all in flight while the counts are built: a full block
-    // of columns that all exist reads at a uniform row base plus a 32-bit lane
-    // offset; otherwise the bag and column are clamped into range and the
-    // value is zeroed
-    float gv[S::kSteps][DT];
-    {
-      const uint32_t c0 = wave * (uint32_t)DT * 16u + i;  // this lane's first column
-      if (nb == (uint32_t)S::kBags && (wave + 1u) * (uint32_t)DT * 16u <= D) {
-        const float* __restrict__ gblk = gtab + j0 * (int64_t)a.dtot;
-        const uint32_t loff = kq * (uint32_t)S::kSteps * a.dtot + c0;
+    // Loads in the order they are needed (vector loads complete in order),
+    // none waited for before grad_out's are issued: the bag boundaries (bag
+    // min(x, nb) for thread x, so every index is in range), the block's first
+    // window of lookups from P0 (positions clamped to the last lookup; those
+    // past the block's end are dropped once its end is known), then grad_out.
+    const int64_t o_lo = (int64_t)O[jt + j0 + min(threadIdx.x, nb)];
+    const int64_t o_hi = (int64_t)O[jt + j0 + min(threadIdx.x + 1u, nb)];
+    uint32_t r[kPer];
+    if (N > 0) {
 #pragma unroll
-        for (int ks = 0; ks < S::kSteps; ++ks) {
-          const float* __restrict__ gk = gblk + (int64_t)ks * a.dtot;
+      for (int u = 0; u < kPer; ++u)
+        r[u] = (uint32_t)I[min(P0 + threadIdx.x + (uint32_t)u * kThreads, (uint32_t)N - 1u)];
+    }
+    // the block's grad_out operands of this lane: gv[ks][e][nt] is bag
+    // 32 ks + 8 kq + e at column c0 + 16 nt (the B operand layout of the
+    // 16x16x32 product), all in flight while the counts are built.  A full
+    // block of columns that all exist reads at a uniform row base plus a
+    // 32-bit lane offset; otherwise the bag and column are clamped into range
+    // and the value is zeroed after the counting pass.
+    float gv[S::kSteps][8][DT];
+    const bool full = nb == (uint32_t)S::kBags && c0 - i + (uint32_t)DT * 16u <= D;  // wave-uniform
+    if (full) {
+      const float* __restrict__ gblk = gtab + j0 * (int64_t)a.dtot;
+      const uint32_t loff = 8u * kq * a.dtot + c0;
 #pragma unroll
-          for (int nt = 0; nt < DT; ++nt) gv[ks][nt] = gk[loff + (uint32_t)nt * 16u];
+      for (int ks = 0; ks < S::kSteps; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float* __restrict__ gk = gblk + (int64_t)(32 * ks + e) * a.dtot;
+#pragma unroll
+          for (int nt = 0; nt < DT; ++nt) gv[ks][e][nt] = gk[loff + (uint32_t)nt * 16u];
         }
-      } else {
+    } else {
 #pragma unroll
-        for (int ks = 0; ks < S::kSteps; ++ks) {
-          const uint32_t jb = kq * (uint32_t)S::kSteps + (uint32_t)ks;
+      for (int ks = 0; ks < S::kSteps; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t jb = 32u * (uint32_t)ks + 8u * kq + (uint32_t)e;
           const float* __restrict__ grow = gtab + (j0 + min(jb, nb - 1u)) * (int64_t)a.dtot;
 #pragma unroll
-          for (int nt = 0; nt < DT; ++nt) {
-            const uint32_t col = c0 + (uint32_t)nt * 16u;
-            const uint32_t keep = (jb < nb && col < D) ? 0xffffffffu : 0u;
-            gv[ks][nt] = __uint_as_float(__float_as_uint(grow[min(col, D - 1u)]) & keep);
-          }
+          for (int nt = 0; nt < DT; ++nt)  // (zeroed outside the block below, once loaded)
+            gv[ks][e][nt] = grow[min(c0 + (uint32_t)nt * 16u, D - 1u)];
         }
-      }
     }
     {  // clear the rows in use
       const uint32_t n4 = nrt * 16u * (uint32_t)S::kPitch / 4u;
@@ -234,52 +300,36 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(BwdArgs a) {
         reinterpret_cast<uint4*>(&cnt[0][0])[x] = make_uint4(0u, 0u, 0u, 0u);
     }
     // bag boundaries, clamped to the lookups (entries past nb repeat the end
-    // of bag nb - 1); the mean's divisor from the raw offsets
-    if (threadIdx.x <= (uint32_t)S::kBags) {
-      const uint32_t x = min(threadIdx.x, nb);
-      const int64_t o = (int64_t)O[jt + j0 + x];
-      s_off[threadIdx.x] = (uint32_t)(o < 0 ? 0 : (o > N ? N : o));
-    }
+    // of bag nb - 1), and the mean's divisor from the raw offsets
+    if (threadIdx.x <= (uint32_t)S::kBags)
+      s_off[threadIdx.x] = (uint32_t)(o_lo < 0 ? 0 : (o_lo > N ? N : o_lo));
     if (threadIdx.x < (uint32_t)S::kBags) {
-      float inv = 0.f;
-      if (threadIdx.x < nb) {
-        const int64_t L = (int64_t)O[jt + j0 + threadIdx.x + 1] - (int64_t)O[jt + j0 + threadIdx.x];
-        inv = !mean ? 1.f : (L > 0 ? 1.f / (float)L : 0.f);
-      }
-      s_inv[threadIdx.x] = inv;
+      const int64_t L = o_hi - o_lo;
+      s_inv[threadIdx.x] = !mean ? 1.f : (threadIdx.x < nb && L > 0 ? 1.f / (float)L : 0.f);
     }
     __syncthreads();  // also the hash table on the first block
     const uint32_t dmax = s_dmax;
-    // counting pass: coalesced reads of the block's lookups (the next window's
-    // in flight while this one is counted); a lookup of a hot row finds its
-    // bag by binary search over the bag boundaries and adds one to its count
-    // (integer adds: the same counts in any order).  The kPer lookups of a
-    // thread go through the hash probe and each search level together, so
-    // a level costs one LDS round trip for all of them.
-    // (reads past the block's end are clamped to its last lookup and their
-    // key replaced by kHashEmpty)
-    const uint32_t P0 = s_off[0], P1 = max(s_off[nb], P0);
-    uint32_t r[kPer];
-    if (P0 < P1) {
-#pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        const uint32_t p = P0 + threadIdx.x + (uint32_t)u * kThreads;
-        const uint32_t v = (uint32_t)I[min(p, P1 - 1u)];
-        r[u] = p < P1 ? v : kHashEmpty;
-      }
-    }
+    const uint32_t P1 = max(s_off[nb], P0);  // the block's lookups are [P0, P1)
+    // counting pass (the next window's lookups in flight while this one is
+    // counted): a lookup of a hot row finds its bag by binary search over the
+    // bag boundaries and adds one to its count (integer adds: the same counts
+    // in any order).  The kPer lookups of a thread go through the hash probe
+    // and each search level together, so a level costs one LDS round trip
+    // for all of them.
     for (uint32_t q0 = P0; q0 < P1; q0 += (uint32_t)(kPer * kThreads)) {
+      // this window's lookups past the block's end are dropped here, where
+      // their values are first needed (not where they are loaded)
+#pragma unroll
+      for (int u = 0; u < kPer; ++u)
+        if (q0 + threadIdx.x + (uint32_t)u * kThreads >= P1) r[u] = kHashEmpty;
       const uint32_t qn = q0 + (uint32_t)(kPer * kThreads);
       uint32_t rn[kPer];
 #pragma unroll
       for (int u = 0; u < kPer; ++u) rn[u] = kHashEmpty;
       if (qn < P1) {
 #pragma unroll
-        for (int u = 0; u < kPer; ++u) {
-          const uint32_t p = qn + threadIdx.x + (uint32_t)u * kThreads;
-          const uint32_t v = (uint32_t)I[min(p, P1 - 1u)];
-          rn[u] = p < P1 ? v : kHashEmpty;
-        }
+        for (int u = 0; u < kPer; ++u)
+          rn[u] = (uint32_t)I[min(qn + threadIdx.x + (uint32_t)u * kThreads, P1 - 1u)];
       }
       // the hot-row slot of each lookup (kHashSlots: not hot, or past the
       // block: kHashEmpty would match an empty slot, so it is excluded)
@@ -293,11 +343,11 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(BwdArgs a) {
           slot[u] = (s_key[q] == r[u] && r[u] != kHashEmpty) ? q : slot[u];
         }
       }
+      // the last bag whose start is at or before p: m < kBags always, and
+      // s_off[m] for m >= nb is the block's end, past every p counted here
       uint32_t bag[kPer];
 #pragma unroll
       for (int u = 0; u < kPer; ++u) bag[u] = 0u;
-      // the last bag whose start is at or before p: m < kBags always, and
-      // s_off[m] for m >= nb is the block's end, past every p counted here
 #pragma unroll
       for (uint32_t step = (uint32_t)S::kBags / 2u; step > 0u; step >>= 1) {
 #pragma unroll
@@ -313,37 +363,92 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(BwdArgs a) {
 #pragma unroll
       for (int u = 0; u < kPer; ++u) r[u] = rn[u];
     }
-    __syncthreads();
-    // C^T [rows, K bags] x G [K bags, this wave's columns] on the matrix cores
-    // (A = count, times 1 / bag length for the mean)
+    // a bag of more than kMaxExactCount lookups may hold a count that one
+    // bfloat16 cannot carry
+    const bool wide = __syncthreads_or(threadIdx.x < nb &&
+                                       s_off[threadIdx.x + 1] - s_off[threadIdx.x] > kMaxExactCount);
+    if (!full) {  // bags past nb and columns past D contribute nothing
 #pragma unroll
-    for (int g = 0; g < S::kSteps / 4; ++g) {
-      const uint32_t c0 = kq * (uint32_t)S::kSteps + 4u * (uint32_t)g;
-      const float4v inv = *reinterpret_cast<const float4v*>(&s_inv[c0]);
+      for (int ks = 0; ks < S::kSteps; ++ks)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+          for (int nt = 0; nt < DT; ++nt) {
+            const uint32_t jb = 32u * (uint32_t)ks + 8u * kq + (uint32_t)e;
+            const uint32_t keep = (jb < nb && c0 + (uint32_t)nt * 16u < D) ? 0xffffffffu : 0u;
+            gv[ks][e][nt] = __uint_as_float(__float_as_uint(gv[ks][e][nt]) & keep);
+          }
+    }
+    // mean: G scaled by 1/L of its bag (one rounding, as each lookup's scale)
+    if (mean) {
+#pragma unroll
+      for (int ks = 0; ks < S::kSteps; ++ks) {
+        const float4v i0 = *reinterpret_cast<const float4v*>(&s_inv[32 * ks + 8 * kq]);
+        const float4v i1 = *reinterpret_cast<const float4v*>(&s_inv[32 * ks + 8 * kq + 4]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+          for (int nt = 0; nt < DT; ++nt) gv[ks][e][nt] *= e < 4 ? i0[e & 3] : i1[e & 3];
+      }
+    }
+    // C^T [rows, K bags] x G [K bags, this wave's columns]: per K step, the
+    // three bfloat16 parts of G against the counts, which enter exactly: as
+    // themselves when no bag exceeds kMaxExactCount, else as four 8-bit
+    // parts, one product pass each
+    const uint32_t nparts = wide ? 4u : 1u;
+#pragma unroll
+    for (int ks = 0; ks < S::kSteps; ++ks) {
+      u32x4 bh[DT], bm[DT], bl[DT];
+#pragma unroll
+      for (int nt = 0; nt < DT; ++nt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t h, m, l;
+          split3(gv[ks][2 * j][nt], gv[ks][2 * j + 1][nt], h, m, l);
+          bh[nt][j] = h;
+          bm[nt][j] = m;
+          bl[nt][j] = l;
+        }
+#pragma unroll
+      for (int rt = 0; rt < kRowTiles; ++rt) {
         if ((uint32_t)rt >= nrt) break;  // uniform
-        const uint4 c4 = *reinterpret_cast<const uint4*>(&cnt[(uint32_t)rt * 16u + i][c0]);
-        float av[4] = {(float)c4.x, (float)c4.y, (float)c4.z, (float)c4.w};
+        const uint32_t* crow = &cnt[(uint32_t)rt * 16u + i][32u * (uint32_t)ks + 8u * kq];
+        const u32x4 n0 = *reinterpret_cast<const u32x4*>(crow);
+        const u32x4 n1 = *reinterpret_cast<const u32x4*>(crow + 4);
+        for (uint32_t ap = 0; ap < nparts; ++ap) {
+          // (an integer of at most 8 significant bits is exactly the upper
+          // half of its fp32)
+          const uint32_t mask = wide ? 0xffu << (8u * ap) : 0xffffffffu;
+          float c[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (mean) av[e] *= inv[e];
+          for (int e = 0; e < 8; ++e) c[e] = (float)((e < 4 ? n0[e & 3] : n1[e & 3]) & mask);
+          u32x4 av;
 #pragma unroll
-          for (int nt = 0; nt < DT; ++nt)
-            acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], gv[4 * g + e][nt],
-                                                              acc[rt][nt], 0, 0, 0);
+          for (int j = 0; j < 4; ++j)
+            av[j] = (__float_as_uint(c[2 * j]) >> 16) | (__float_as_uint(c[2 * j + 1]) & 0xffff0000u);
+          const bf16x8 A = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+          for (int nt = 0; nt < DT; ++nt) {
+            acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                A, __builtin_bit_cast(bf16x8, bl[nt]), acc[rt][nt], 0, 0, 0);
+            acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                A, __builtin_bit_cast(bf16x8, bm[nt]), acc[rt][nt], 0, 0, 0);
+            acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                A, __builtin_bit_cast(bf16x8, bh[nt]), acc[rt][nt], 0, 0, 0);
+          }
         }
       }
     }
-    __syncthreads();  // the counts are cleared for the next block
+    P0 = s_off[nb];  // the next block's first lookup
+    __syncthreads();  // the counts are cleared (and s_off rewritten) for the next block
   }
   // partial rows of this workgroup: hot row 16 rt + 4 kq + r, column 16 (wave DT + nt) + i
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
+  for (int rt = 0; rt < kRowTiles; ++rt) {
     if ((uint32_t)rt >= nrt) break;
 #pragma unroll
     for (int nt = 0; nt < DT; ++nt) {
-      const uint32_t col = (wave * (uint32_t)DT + (uint32_t)nt) * 16u + i;
+      const uint32_t col = c0 + (uint32_t)nt * 16u;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const uint32_t row = (uint32_t)rt * 16u + 4u * kq + (uint32_t)r;
@@ -357,13 +462,11 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(BwdArgs a) {
 
 template <typename IT>
 hipError_t launch_partial(const BwdArgs& a, int dt, hipStream_t s) {
-  const dim3 grid(a.T * a.dense_w), block(kThreads);
+  const dim3 grid(a.T * a.dense_w * a.dense_ncg), block(kThreads);
   if (dt <= 1)
     TBE_LAUNCH("dense_partial", (dense_partial_kernel<IT, 1>), grid, block, s, a);
-  else if (dt == 2)
-    TBE_LAUNCH("dense_partial", (dense_partial_kernel<IT, 2>), grid, block, s, a);
   else
-    TBE_LAUNCH("dense_partial", (dense_partial_kernel<IT, 4>), grid, block, s, a);
+    TBE_LAUNCH("dense_partial", (dense_partial_kernel<IT, 2>), grid, block, s, a);
   return hipGetLastError();
 }
 

@@ -74,7 +74,8 @@ struct tbe_plan {
   uint32_t* d_bkb;
   void* d_mem;
   int num_cus;
-  int dense_dt;  // hot-row contraction: 16-column tiles per wave (0: no table can take it)
+  int dense_dt;   // hot-row contraction: 16-column tiles per wave (0: no table can take it)
+  int dense_ncg;  // and column groups of 64 * dense_dt columns
   // backward fork/join: two default-priority side streams and their events;
   // the lock keeps the record/wait sequence of one call from interleaving
   // with another call's on the same plan
@@ -487,7 +488,8 @@ int tbe_plan_create(tbe_plan** out, int32_t T, const int64_t* rows, const int32_
     int dmax = 0;
     for (int t = 0; t < T; ++t)
       if (dims[t] % 16 == 0 && dims[t] <= kDensePitch) dmax = std::max(dmax, (int)dims[t]);
-    P->dense_dt = (T > kDenseMaxTables || dmax == 0) ? 0 : dmax <= 64 ? 1 : dmax <= 128 ? 2 : 4;
+    P->dense_dt = (T > kDenseMaxTables || dmax == 0) ? 0 : dmax <= 64 ? 1 : 2;
+    P->dense_ncg = dmax > 128 ? 2 : 1;
   }
 
   // buckets by next_pow2(D), ascending width; tables keep ascending id inside a bucket
@@ -953,7 +955,8 @@ int run_backward(const tbe_plan* P, int64_t B, int32_t itype, const void* indice
     a.dense_cnt = reinterpret_cast<uint32_t*>(w + L.dense_cnt);
     a.dense_part = reinterpret_cast<float*>(w + L.dense_part);
     a.dense_w = kDenseWgsPerTable;
-    a.dense_min_len = (uint32_t)std::max<int64_t>(kLongRun, std::min<int64_t>(B / 32, 1ll << 30));
+    a.dense_ncg = (uint32_t)P->dense_ncg;
+    a.dense_min_len = (uint32_t)std::max<int64_t>(kLongRun, std::min<int64_t>(B / 256, 1ll << 30));
   }
   int rc_launch = TBE_OK;
   if (dense && launch_dense(a, P->d_tseg, P->wdtype, itype, P->dense_dt, ss[2]) != hipSuccess)

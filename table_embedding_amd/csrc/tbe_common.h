@@ -523,7 +523,8 @@ struct BwdArgs {
   uint4* dense_rows;         // T x kDenseRows {start, len, row, long index} of each table's hot rows
   uint32_t* dense_cnt;       // T: hot rows per table
   float* dense_part;         // T x kDenseRows x dense_w partial rows of kDensePitch floats
-  uint32_t dense_w;          // workgroups per table of the contraction
+  uint32_t dense_w;          // workgroups per table and column group of the contraction
+  uint32_t dense_ncg;        // column groups of the contraction (64 * dense_dt columns each)
   uint32_t dense_min_len;    // smallest run length the contraction takes
 };
 
@@ -531,7 +532,7 @@ struct BwdArgs {
 // of at least dense_min_len lookups (tables with D a multiple of 16 and at
 // most kDensePitch columns), their gradients as one counts x grad_out
 // contraction over the table's bags on the matrix cores.
-constexpr int kDenseRows = 64;
+constexpr int kDenseRows = 128;
 constexpr int kDensePitch = 256;
 
 // Histogram-reuse backward of a plan with one table of at most 64 rows and

@@ -433,15 +433,18 @@ class WorkspaceLists:
                 assert np.all(bt[tab[b[q]:b[q + 1]]] == q), name
 
 
+DENSE_ROWS = 128
+
+
 def expected_hot_rows(case: Case):
     """Per table, the (row, run length) pairs that the hot-row contraction
     takes, from the host inputs by the selection rule: among the table's long
-    runs (run length >= 256), those that reach a threshold which starts at
-    max(256, B / 32) and doubles until at most 64 runs reach it; tables whose
-    D is not a multiple of 16 or exceeds 256 take none.  Rows ascending (the
-    long list's key order within a table)."""
+    runs (run length >= 256), those that reach the smallest threshold of at
+    least max(256, B / 256) that at most 128 runs reach; tables whose D is not
+    a multiple of 16 or exceeds 256 take none.  Rows ascending (the long
+    list's key order within a table)."""
     spec, B = case.spec, case.spec.B
-    min_len = max(256, min(B // 32, 1 << 30))
+    min_len = max(256, min(B // 256, 1 << 30))
     out = []
     for t in range(spec.T):
         D = spec.dims[t]
@@ -453,11 +456,11 @@ def expected_hot_rows(case: Case):
         keep = lens >= 256
         rows, lens = rows[keep], lens[keep]
         thr = min_len
-        for _ in range(32):
-            if int((lens >= thr).sum()) <= 64:
-                break
-            thr = min(thr * 2, 0xffffffff)
+        if int((lens >= thr).sum()) > DENSE_ROWS:
+            # one more than the (DENSE_ROWS + 1)-th longest run
+            thr = int(np.sort(lens)[::-1][DENSE_ROWS]) + 1
         sel = lens >= thr
+        assert int(sel.sum()) <= DENSE_ROWS
         out.append(list(zip(rows[sel].tolist(), lens[sel].tolist())))
     return out
 
@@ -476,7 +479,8 @@ def check_dense(case: Case, tbe_obj):
     lt = read_u32x4(ws, v["long_task"], nl).astype(np.int64)
     flag = read_u32(ws, v["long_flag"], nl)
     dcnt = read_u32(ws, v["dense_count"], spec.T)
-    drows = read_u32x4(ws, v["dense_rows"], spec.T * 64).reshape(spec.T, 64, 4).astype(np.int64)
+    drows = read_u32x4(ws, v["dense_rows"], spec.T * DENSE_ROWS).reshape(
+        spec.T, DENSE_ROWS, 4).astype(np.int64)
     exp = expected_hot_rows(case)
     hot = set()
     for t in range(spec.T):

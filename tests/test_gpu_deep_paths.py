@@ -36,7 +36,7 @@ def knobs(**kv):
 
 
 DEEP = ["C2s", "C3s", "C5s", "many_tables", "const257", "heavy_chunks", "wide_f32", "cut_bags",
-        "dense_mean", "dense_many"]
+        "dense_mean", "dense_many", "dense_wide"]
 
 
 def _takes_dense(spec):
@@ -124,7 +124,7 @@ def test_wait_give_up_writes_nothing(name):
     tb.close()
 
 
-@pytest.mark.parametrize("name", ["dense_mean", "C5s", "heavy_chunks"])
+@pytest.mark.parametrize("name", ["dense_mean", "C5s", "heavy_chunks", "dense_wide"])
 @pytest.mark.parametrize("optimizer", ["adagrad", "sgd"])
 def test_dense_rows_with_other_optimizers(name, optimizer):
     """The hot rows' update takes the element-wise Adagrad and SGD epilogues

@@ -85,9 +85,14 @@ def _spec(name):
         return wl.Spec("dense_mean", 2014, [5000, 3000, 800, 2000], [128, 64, 40, 256],
                        [1, 0, 1, 1], "f16", 2048, "uniform:1:64", "zipf:1.2", "i64", False)
     if name == "dense_many":
-        # 108 long runs: the hot-row threshold doubles once (55 rows reach it)
-        return wl.Spec("dense_many", 2015, [3000], [32], [0], "bf16", 4096, "fixed:64",
+        # more long runs than the contraction takes: its threshold is searched
+        return wl.Spec("dense_many", 2015, [3000], [32], [0], "bf16", 8192, "fixed:64",
                        "zipf:1.05", "i32", False)
+    if name == "dense_wide":
+        # bags of up to 2000 lookups from 50 rows: hot-row counts above 255 in
+        # a bag, which enter the contraction in 8-bit parts
+        return wl.Spec("dense_wide", 2016, [50, 300], [64, 160], [0, 1], "f32", 512,
+                       "list:300,1,2000,5,700,0,64", "zipf:1.5", "i64", False)
     if name == "rows_21b":
         # 21 row bits: three 8-bit radix passes (an odd count) at a small size
         return wl.Spec("rows_21b", 2012, [(1 << 20) + 3, 50], [8, 16], [0, 1], "f16", 300,
@@ -102,7 +107,7 @@ def _spec(name):
 MAIN = ["C1", "C2s", "C3s", "C4s", "C5s"]
 EDGE = ["empty_bags", "all_empty", "one_bag", "one_row", "const31", "const32", "const255",
         "const256", "const257", "wide_f32", "wide_bf16", "many_tables", "many_bags",
-        "heavy_chunks", "cut_bags", "dense_mean", "rows_21b", "rows_25b"]
+        "heavy_chunks", "cut_bags", "dense_mean", "dense_wide", "rows_21b", "rows_25b"]
 
 
 def _announce(name, what):
