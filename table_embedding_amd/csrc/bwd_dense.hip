@@ -50,7 +50,7 @@
 // Only batches without per-sample weights take this path: with them the
 // coefficients are float sums, which atomics would add in a varying order,
 // and the long runs keep the chunked gather.
-#include "tbe_common.h"
+#include "count_mma.h"
 
 namespace tbe {
 namespace {
@@ -146,10 +146,6 @@ __global__ __launch_bounds__(kThreads) void dense_select_kernel(BwdArgs a, const
   if (threadIdx.x == 0) a.dense_cnt[t] = min(s_base, (uint32_t)kDenseRows);
 }
 
-typedef float float4v __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 // Open-addressing table of the hot rows in LDS: row -> rank, linear probing,
 // at most kDenseRows of kHashSlots slots in use.  The longest probe distance
 // of an insert bounds every search, so a lookup reads a fixed number of
@@ -175,21 +171,6 @@ struct DenseShape {
   static constexpr int kSteps = kBags / 32; // K steps of 32 bags
   static constexpr uint32_t kGroupCols = 64u * DT;
 };
-
-// The three bfloat16 parts of x, packed for lanes' pairs (x0, x1): x = hi +
-// mid + lo exactly (truncation leaves a remainder of at most 16, then 8,
-// significant bits).  Element 2j of an 8-vector is the low half of dword j.
-__device__ __forceinline__ void split3(float x0, float x1, uint32_t& hi, uint32_t& mid,
-                                       uint32_t& lo) {
-  const uint32_t h0 = __float_as_uint(x0) & 0xffff0000u, h1 = __float_as_uint(x1) & 0xffff0000u;
-  const float r0 = x0 - __uint_as_float(h0), r1 = x1 - __uint_as_float(h1);
-  const uint32_t m0 = __float_as_uint(r0) & 0xffff0000u, m1 = __float_as_uint(r1) & 0xffff0000u;
-  const uint32_t l0 = __float_as_uint(r0 - __uint_as_float(m0)),
-                 l1 = __float_as_uint(r1 - __uint_as_float(m1));
-  hi = (h0 >> 16) | h1;
-  mid = (m0 >> 16) | m1;
-  lo = (l0 >> 16) | (l1 & 0xffff0000u);
-}
 
 template <typename IT, int DT>
 __global__ __launch_bounds__(kThreads) void dense_partial_kernel(BwdArgs a) {
@@ -230,11 +211,11 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(BwdArgs a) {
   const uint32_t wave = threadIdx.x / kWave, lane = lane_id();
   const uint32_t i = lane & 15u, kq = lane >> 4;  // A row / B column; K lane group
   const uint32_t nrt = (H + 15u) / 16u;           // row tiles in use
-  float4v acc[kRowTiles][DT];
+  cm_f4 acc[kRowTiles][DT];
 #pragma unroll
   for (int rt = 0; rt < kRowTiles; ++rt)
 #pragma unroll
-    for (int nt = 0; nt < DT; ++nt) acc[rt][nt] = (float4v){0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < DT; ++nt) acc[rt][nt] = (cm_f4){0.f, 0.f, 0.f, 0.f};
   // this workgroup's bags [b_lo, b_hi) of the table
   const int64_t B = a.B;
   const int64_t b_lo = B * (int64_t)w / (int64_t)a.dense_w;
@@ -309,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(BwdArgs a) {
     }
     __syncthreads();  // also the hash table on the first block
     const uint32_t dmax = s_dmax;
-    const uint32_t P1 = max(s_off[nb], P0);  // the block's lookups are [P0, P1)
+    const uint32_t P1 = min(max(s_off[nb], (uint32_t)P0), (uint32_t)N);  // the block's lookups are [P0, P1)
     // counting pass (the next window's lookups in flight while this one is
     // counted): a lookup of a hot row finds its bag by binary search over the
     // bag boundaries and adds one to its count (integer adds: the same counts
@@ -383,62 +364,16 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(BwdArgs a) {
     if (mean) {
 #pragma unroll
       for (int ks = 0; ks < S::kSteps; ++ks) {
-        const float4v i0 = *reinterpret_cast<const float4v*>(&s_inv[32 * ks + 8 * kq]);
-        const float4v i1 = *reinterpret_cast<const float4v*>(&s_inv[32 * ks + 8 * kq + 4]);
+        const cm_f4 i0 = *reinterpret_cast<const cm_f4*>(&s_inv[32 * ks + 8 * kq]);
+        const cm_f4 i1 = *reinterpret_cast<const cm_f4*>(&s_inv[32 * ks + 8 * kq + 4]);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
 #pragma unroll
           for (int nt = 0; nt < DT; ++nt) gv[ks][e][nt] *= e < 4 ? i0[e & 3] : i1[e & 3];
       }
     }
-    // C^T [rows, K bags] x G [K bags, this wave's columns]: per K step, the
-    // three bfloat16 parts of G against the counts, which enter exactly: as
-    // themselves when no bag exceeds kMaxExactCount, else as four 8-bit
-    // parts, one product pass each
-    const uint32_t nparts = wide ? 4u : 1u;
-#pragma unroll
-    for (int ks = 0; ks < S::kSteps; ++ks) {
-      u32x4 bh[DT], bm[DT], bl[DT];
-#pragma unroll
-      for (int nt = 0; nt < DT; ++nt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t h, m, l;
-          split3(gv[ks][2 * j][nt], gv[ks][2 * j + 1][nt], h, m, l);
-          bh[nt][j] = h;
-          bm[nt][j] = m;
-          bl[nt][j] = l;
-        }
-#pragma unroll
-      for (int rt = 0; rt < kRowTiles; ++rt) {
-        if ((uint32_t)rt >= nrt) break;  // uniform
-        const uint32_t* crow = &cnt[(uint32_t)rt * 16u + i][32u * (uint32_t)ks + 8u * kq];
-        const u32x4 n0 = *reinterpret_cast<const u32x4*>(crow);
-        const u32x4 n1 = *reinterpret_cast<const u32x4*>(crow + 4);
-        for (uint32_t ap = 0; ap < nparts; ++ap) {
-          // (an integer of at most 8 significant bits is exactly the upper
-          // half of its fp32)
-          const uint32_t mask = wide ? 0xffu << (8u * ap) : 0xffffffffu;
-          float c[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) c[e] = (float)((e < 4 ? n0[e & 3] : n1[e & 3]) & mask);
-          u32x4 av;
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            av[j] = (__float_as_uint(c[2 * j]) >> 16) | (__float_as_uint(c[2 * j + 1]) & 0xffff0000u);
-          const bf16x8 A = __builtin_bit_cast(bf16x8, av);
-#pragma unroll
-          for (int nt = 0; nt < DT; ++nt) {
-            acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                A, __builtin_bit_cast(bf16x8, bl[nt]), acc[rt][nt], 0, 0, 0);
-            acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                A, __builtin_bit_cast(bf16x8, bm[nt]), acc[rt][nt], 0, 0, 0);
-            acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                A, __builtin_bit_cast(bf16x8, bh[nt]), acc[rt][nt], 0, 0, 0);
-          }
-        }
-      }
-    }
+    // C^T [rows, K bags] x G [K bags, this wave's columns], exact products
+    cm_counts_x_grad<S::kSteps, DT, kRowTiles, S::kPitch>(acc, cnt, gv, nrt, wide, i, kq);
     P0 = s_off[nb];  // the next block's first lookup
     __syncthreads();  // the counts are cleared (and s_off rewritten) for the next block
   }
