@@ -51,7 +51,10 @@ KERNEL_SOURCES = {
     "bwd_long_update": "bwd.hip", "bwd_chunk_fused": "bwd.hip", "chunk_order": "bwd.hip",
     "bwd_hist_partial": "bwd_hist.hip", "bwd_hist_update": "bwd_hist.hip",
     "validate_check": "validate.hip", "validate_clear": "validate.hip",
+    "dense_select": "bwd_dense.hip", "dense_partial": "bwd_dense.hip", "dense_update": "bwd.hip",
 }
+# kernels whose source includes the exact counts x grad_out product
+COUNT_MMA_KERNELS = ("dense_partial", "bwd_hist_partial")
 # rocprofv3 kernel names -> the library's kernel families (tbe_prof_read names)
 KERNEL_FAMILIES = (
     ("fwd_bal_kernel", "fwd_pool"), ("fwd_pool_kernel", "fwd_pool"),
@@ -63,7 +66,10 @@ KERNEL_FAMILIES = (
     ("bwd_medium_kernel", "bwd_medium"), ("bwd_chunk_fused_kernel", "bwd_chunk_fused"),
     ("bwd_chunk_kernel", "bwd_chunk"), ("bwd_long_update_kernel", "bwd_long_update"),
     ("bwd_hist_partial_kernel", "bwd_hist_partial"),
+    ("bwd_hist_count_kernel", "bwd_hist_partial"), ("bwd_hist_weighted_kernel", "bwd_hist_partial"),
     ("bwd_hist_update_kernel", "bwd_hist_update"),
+    ("dense_select_kernel", "dense_select"), ("dense_partial_kernel", "dense_partial"),
+    ("dense_update_kernel", "dense_update"),
     ("validate_clear_kernel", "validate_clear"), ("validate_offsets_kernel", "validate_check"),
     ("validate_indices_kernel", "validate_check"), ("validate_clamp_kernel", "validate_repair"),
 )
@@ -145,12 +151,24 @@ def device_inputs(spec, torch):
 # --------------------------------------------------------------- byte model
 
 SL_CLASSES = (("single", 1, 2), ("tiny", 2, 32), ("medium", 32, 256), ("long", 256, None))
+# the hot-row contraction of the long runs: batches without per-sample
+# weights from this many lookups on, at most this many rows per table
+DENSE_MIN_LOOKUPS = 8 << 20
+DENSE_ROWS = 128
+
+
+def dense_applies(spec, N):
+    return (not spec.weighted and N >= DENSE_MIN_LOOKUPS and spec.T <= 128
+            and any(d % 16 == 0 and d <= 256 for d in spec.dims))
 
 
 def workload_stats(spec, off, idx):
-    """Per-table lookups, unique rows and the run-length classes the backward
-    splits runs into (host, from the inputs)."""
+    """Per-table lookups, unique rows, the run-length classes the backward
+    splits runs into, and the long runs the contraction takes (the smallest
+    threshold of at least max(256, B/256) that at most 128 runs reach, on
+    tables with D a multiple of 16 up to 256) (host, from the inputs)."""
     B = spec.B
+    dense = dense_applies(spec, int(off[-1]))
     st = []
     for t in range(spec.T):
         lo, hi = int(off[t * B]), int(off[(t + 1) * B])
@@ -162,6 +180,14 @@ def workload_stats(spec, off, idx):
             s["n_" + name] = int(m.sum())
             s["N_" + name] = int(cnt[m].sum())
         s["chunks"] = int(((cnt[cnt >= 256] + 255) // 256).sum())
+        s["n_hot"] = s["N_hot"] = 0
+        if dense and spec.dims[t] % 16 == 0 and spec.dims[t] <= 256:
+            lens = cnt[cnt >= 256]
+            thr = max(256, min(B // 256, 1 << 30))
+            if int((lens >= thr).sum()) > DENSE_ROWS:
+                thr = int(np.sort(lens)[::-1][DENSE_ROWS]) + 1
+            hot = lens[lens >= thr]
+            s["n_hot"], s["N_hot"] = int(hot.size), int(hot.sum())
         st.append(s)
     return st
 
@@ -210,19 +236,22 @@ def byte_model(spec, st):
     for k in list(comp):
         logi.setdefault(k, comp[k])
     kern = {"single": "bwd_single", "tiny": "bwd_tiny", "medium": "bwd_medium",
-            "long": "bwd_chunk"}
-    for k in ("bwd_single", "bwd_tiny", "bwd_medium", "bwd_chunk", "bwd_long_update"):
+            "long": "bwd_chunk", "hot": "dense_partial"}
+    for k in ("bwd_single", "bwd_tiny", "bwd_medium", "bwd_chunk", "bwd_long_update",
+              "dense_partial", "dense_update", "dense_select"):
         comp[k] = logi[k] = 0
     for s in st:
         D = s["D"]
         rmw = 2 * D * sw + 8  # weight row and momentum, read and written once
         for cls, k in kern.items():
             lk, runs = s["N_" + cls], s["n_" + cls]
+            if cls == "long":  # the hot long runs are the contraction's
+                lk, runs = lk - s["N_hot"], runs - s["n_hot"]
             per_lookup = lk * (4 + 4 * psi)
             comp[k] += per_lookup + G_bytes * lk / max(N, 1)
             logi[k] += per_lookup + lk * 4 * D
             upd = runs * rmw
-            tgt = "bwd_long_update" if cls == "long" else k
+            tgt = {"long": "bwd_long_update", "hot": "dense_update"}.get(cls, k)
             comp[tgt] += upd
             logi[tgt] += upd
     comp["bwd_chunk_fused"] = comp["bwd_chunk"] + comp["bwd_long_update"]
@@ -249,7 +278,8 @@ def source_hash(kernel):
     f = KERNEL_SOURCES.get(kernel, "prep.hip")
     d = os.path.join(ROOT, "table_embedding_amd", "csrc")
     h = hashlib.sha256()
-    for name in (f, "tbe_common.h"):  # the kernel's file and the shared device helpers
+    names = (f, "tbe_common.h") + (("count_mma.h",) if kernel in COUNT_MMA_KERNELS else ())
+    for name in names:  # the kernel's file and the shared device helpers
         h.update(open(os.path.join(d, name), "rb").read())
     return h.hexdigest()[:16]
 

@@ -9,7 +9,7 @@ import tbe_workloads as wl
 
 BWD_KERNELS = ("transpose", "radix_upsweep", "radix_scan", "radix_downsweep", "rle", "classify",
                "chunk_order", "bwd_single", "bwd_tiny", "bwd_medium", "bwd_chunk",
-               "bwd_long_update")
+               "bwd_long_update", "dense_select", "dense_partial", "dense_update")
 
 
 def _model(spec):
@@ -49,3 +49,23 @@ def test_totals_on_a_hand_checked_problem():
     assert tot["bwd_logi"] == N * (si + 16) + TB1 * si + U * (2 * D * sw + 24) + N * 4 * D
     # run classes: row 0 three times (tiny), rows 1 and 3 once (single)
     assert st[0]["n_single"] == 2 and st[0]["n_tiny"] == 1 and st[0]["N_tiny"] == 3
+
+
+def test_hot_runs_move_between_kernels_not_out_of_the_step(monkeypatch):
+    """With the hot-row contraction in force (its lookup threshold lowered to
+    this small batch), the long runs it takes are attributed to it and the
+    step totals are unchanged; the hot rows are the longest long runs, at
+    most 128 per table."""
+    spec = wl.config("C5", rows=200000, B=2048, T=3)
+    st0, (comp0, logi0, tot0) = _model(spec)
+    assert all(s["n_hot"] == 0 for s in st0)
+    monkeypatch.setattr(bench, "DENSE_MIN_LOOKUPS", 0)
+    st, (comp, logi, tot) = _model(spec)
+    assert tot == tot0
+    assert abs(sum(comp[k] for k in BWD_KERNELS) - tot["bwd_comp"]) < 1e-6 * tot["bwd_comp"]
+    assert abs(sum(logi[k] for k in BWD_KERNELS) - tot["bwd_logi"]) < 1e-6 * tot["bwd_logi"]
+    for s in st:
+        assert 0 < s["n_hot"] <= min(128, s["n_long"]) and s["N_hot"] <= s["N_long"]
+    assert comp["dense_partial"] > 0 and comp["bwd_chunk"] < comp0["bwd_chunk"]
+    moved = comp["dense_partial"] + comp["bwd_chunk"]
+    assert abs(moved - comp0["bwd_chunk"]) < 1e-9 * comp0["bwd_chunk"]
