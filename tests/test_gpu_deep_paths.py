@@ -36,7 +36,7 @@ def knobs(**kv):
 
 
 DEEP = ["C2s", "C3s", "C5s", "many_tables", "const257", "heavy_chunks", "wide_f32", "cut_bags",
-        "dense_mean", "dense_many", "dense_wide"]
+        "dense_mean", "dense_many", "dense_half", "dense_wide"]
 
 
 def _takes_dense(spec):

@@ -86,7 +86,11 @@ def _spec(name):
                        [1, 0, 1, 1], "f16", 2048, "uniform:1:64", "zipf:1.2", "i64", False)
     if name == "dense_many":
         # more long runs than the contraction takes: its threshold is searched
-        return wl.Spec("dense_many", 2015, [3000], [32], [0], "bf16", 8192, "fixed:64",
+        return wl.Spec("dense_many", 2015, [3000], [32], [0], "bf16", 16384, "fixed:64",
+                       "zipf:1.05", "i32", False)
+    if name == "dense_half":
+        # 223 long runs, all taken: the second 128 hot rows partly filled
+        return wl.Spec("dense_half", 2017, [3000], [32], [0], "bf16", 8192, "fixed:64",
                        "zipf:1.05", "i32", False)
     if name == "dense_wide":
         # bags of up to 2000 lookups from 50 rows: hot-row counts above 255 in
