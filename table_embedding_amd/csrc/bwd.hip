@@ -757,7 +757,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_fused_kernel(BwdArgs a, Bu
 
 // Hot rows of the contraction (bwd_dense.hip): one workgroup per (table,
 // hot row slot); the row gradient is the sum of the contraction's dense_w
-// partials in workgroup order, then the optimizer of every row update.
+// partials in a fixed order (eight interleaved accumulators over workgroup
+// order, combined in a fixed tree), then the optimizer of every row update.
 template <int WD>
 __global__ __launch_bounds__(kThreads) void dense_update_kernel(BwdArgs a) {
   if (prep_failed(a)) return;
@@ -772,8 +773,19 @@ __global__ __launch_bounds__(kThreads) void dense_update_kernel(BwdArgs a) {
   const float* part = a.dense_part + ((size_t)t * kDenseRows + k) * a.dense_w * kDensePitch;
   float sqp = 0.f;
   for (uint32_t col = threadIdx.x; col < D; col += kThreads) {
-    float g = 0.f;
-    for (uint32_t w = 0; w < a.dense_w; ++w) g += part[(size_t)w * kDensePitch + col];
+    // the dense_w partials: eight interleaved accumulators (eight loads in
+    // flight), combined in a fixed tree
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    uint32_t w = 0;
+    for (; w + 8u <= a.dense_w; w += 8u) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(size_t)(w + (uint32_t)u) * kDensePitch + col];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] += v[u];
+    }
+    for (; w < a.dense_w; ++w) acc[0] += part[(size_t)w * kDensePitch + col];
+    const float g = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
     sm.gsum[col] = g;
     sqp += g * g;
   }

@@ -76,6 +76,7 @@ struct tbe_plan {
   int num_cus;
   int dense_dt;   // hot-row contraction: 16-column tiles per wave (0: no table can take it)
   int dense_ncg;  // and column groups of 64 * dense_dt columns
+  int dense_w;    // and workgroups per table and column group (bag ranges)
   // backward fork/join: two default-priority side streams and their events;
   // the lock keeps the record/wait sequence of one call from interleaving
   // with another call's on the same plan
@@ -113,7 +114,11 @@ bool bwd_hist_capable(const tbe_plan* P) {
 
 // The hot-row contraction: workgroups per table, and the most tables a plan
 // may have for it (its partials take T x 1 MiB of workspace).
-constexpr uint32_t kDenseWgsPerTable = 16;
+// Workgroups of the contraction per table (bag ranges): at least 16, and
+// together at least kDenseMinWgs, so that a plan of few tables still fills
+// the chip.
+constexpr int kDenseWgsPerTable = 16;
+constexpr int kDenseMinWgs = 512;
 constexpr int kDenseMaxTables = 128;
 
 // TBE_BWD_CONCURRENT_AUTO forks the run classes below this many lookups.
@@ -195,7 +200,7 @@ WsLayout layout(const tbe_plan* P, int64_t N) {
   L.long_flag = take(dc ? (size_t)L.max_long * 4 : 0);
   L.dense_rows = take(dc ? (size_t)P->T * kDenseRows * 16 : 0);
   L.dense_cnt = take(dc ? (size_t)P->T * 4 : 0);
-  L.dense_part = take(dc ? (size_t)P->T * kDenseRows * kDenseWgsPerTable * kDensePitch * 4 : 0);
+  L.dense_part = take(dc ? (size_t)P->T * kDenseRows * P->dense_w * kDensePitch * 4 : 0);
   L.total = off;
   return L;
 }
@@ -490,6 +495,7 @@ int tbe_plan_create(tbe_plan** out, int32_t T, const int64_t* rows, const int32_
       if (dims[t] % 16 == 0 && dims[t] <= kDensePitch) dmax = std::max(dmax, (int)dims[t]);
     P->dense_dt = (T > kDenseMaxTables || dmax == 0) ? 0 : dmax <= 64 ? 1 : 2;
     P->dense_ncg = dmax > 128 ? 2 : 1;
+    P->dense_w = std::max(kDenseWgsPerTable, kDenseMinWgs / std::max(1, (int)T));
   }
 
   // buckets by next_pow2(D), ascending width; tables keep ascending id inside a bucket
@@ -954,7 +960,7 @@ int run_backward(const tbe_plan* P, int64_t B, int32_t itype, const void* indice
     a.dense_rows = reinterpret_cast<uint4*>(w + L.dense_rows);
     a.dense_cnt = reinterpret_cast<uint32_t*>(w + L.dense_cnt);
     a.dense_part = reinterpret_cast<float*>(w + L.dense_part);
-    a.dense_w = kDenseWgsPerTable;
+    a.dense_w = (uint32_t)P->dense_w;
     a.dense_ncg = (uint32_t)P->dense_ncg;
     a.dense_min_len = (uint32_t)std::max<int64_t>(kLongRun, std::min<int64_t>(B / 256, 1ll << 30));
   }
