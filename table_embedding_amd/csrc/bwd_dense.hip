@@ -42,7 +42,7 @@
 // every grad_out element of the block is loaded once, and the accumulators
 // stay in registers across the workgroup's blocks.  Each workgroup writes its
 // partial rows; the update kernel (bwd.hip) adds the dense_w partials of a
-// row in workgroup order and applies the optimizer.  Every floating-point sum
+// row in a fixed order and applies the optimizer.  Every floating-point sum
 // has a data-determined order, so repeated calls give the same bits, and the
 // fused and two-launch long-run paths, which both leave the hot rows to this
 // contraction, stay bit-identical.
