@@ -10,8 +10,11 @@
 // bits cleared, mid = the same of x - hi, lo = (x - hi) - mid, which has at
 // most 8 significant bits left.  Three v_mfma_f32_16x16x32_bf16 (lo, mid,
 // hi) per tile then give the fp32 products without rounding; only the fp32
-// accumulation rounds.  Counts wider than 8 bits are cut into four 8-bit
-// parts (count & 0xff << 8k, each exact), one such pass per part.
+// accumulation rounds.  (This holds while the parts are normal numbers,
+// for |x| >= 2^-100; below that the lo part may be subnormal and its
+// truncation drops less than 2^-133.)  Counts wider than 8 bits are cut
+// into four 8-bit parts (count & 0xff << 8k, each exact), one such pass per
+// part.
 //
 // Operand layout of v_mfma_f32_16x16x32_bf16: lane l = 16 kq + i holds A
 // row i, K elements 8 kq .. 8 kq + 7 (element 2j in the low half of dword

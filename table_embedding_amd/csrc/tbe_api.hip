@@ -196,7 +196,11 @@ WsLayout layout(const tbe_plan* P, int64_t N) {
   // average bag length of 64) and E <= 64, so at most 2 N + 128 bytes
   L.hist_save = take(hc ? 2 * n + 128 : 0);
   L.hist_hdr = take(hc ? 16 : 0);
-  const bool dc = P->dense_dt > 0;
+  // the hot-row contraction's lists, for batches large enough to take it
+  // (the same lookup threshold as the backward's; with a smaller batch the
+  // regions are empty and the backward never takes the contraction)
+  const bool dc = P->dense_dt > 0 && N >= knob_dense_lookups();
+  L.dense = dc;
   L.long_flag = take(dc ? (size_t)L.max_long * 4 : 0);
   L.dense_rows = take(dc ? (size_t)P->T * kDenseRows * 16 : 0);
   L.dense_cnt = take(dc ? (size_t)P->T * 4 : 0);
@@ -953,7 +957,7 @@ int run_backward(const tbe_plan* P, int64_t B, int32_t itype, const void* indice
   // the hottest long runs by the contraction (their chunks and long-run
   // updates are skipped), on the long runs' stream before their kernels;
   // batches without per-sample weights only (integer counts)
-  const bool dense = P->dense_dt > 0 && psw == nullptr && N >= knob_dense_lookups();
+  const bool dense = L.dense && psw == nullptr;
   if (dense) {
     a.indices = indices;
     a.long_flag = reinterpret_cast<uint32_t*>(w + L.long_flag);

@@ -133,6 +133,7 @@ struct WsLayout {
   size_t hist_part, hist_cnt;  // histogram backward: partial rows and row counts (or 0 bytes)
   size_t hist_save, hist_hdr;  // row counts per bag saved by the histogram forward, {B, N}
   size_t long_flag, dense_rows, dense_cnt, dense_part;  // hot-row contraction (or 0 bytes)
+  bool dense;  // the contraction's regions are present (the plan and N allow it)
   size_t total;
   uint32_t ntiles;          // ceil(N / kTile)
   uint32_t nrle_tiles;      // ceil(N / (rle_groups * kTile)): tiles of the run-length pass

@@ -78,5 +78,8 @@ def test_noalloc_refuses_what_it_cannot_serve():
         te.tbe_backward_rowwise_adagrad_noalloc(tb.plan, spec.B, case.d_idx, case.d_off, big,
                                                 None, case.d_G, spec.lr, spec.eps)
     assert e.value.code == te.TBE_E_TOO_LARGE
+    # the hot-row contraction starts at 8 Mi lookups, past what the array holds
+    assert big <= 8 << 20
+    assert te.tbe_workspace_size(tb.plan, 1, 8 << 20) > te.TBE_STATIC_WS_BYTES
     torch.cuda.synchronize()
     tb.close()
