@@ -58,8 +58,10 @@ COUNT_MMA_KERNELS = ("dense_partial", "bwd_hist_partial")
 # rocprofv3 kernel names -> the library's kernel families (tbe_prof_read names)
 KERNEL_FAMILIES = (
     ("fwd_bal_kernel", "fwd_pool"), ("fwd_pool_kernel", "fwd_pool"),
-    ("fwd_hist_kernel", "fwd_hist"), ("transpose_kernel", "transpose"),
-    ("radix_upsweep", "radix_upsweep"), ("radix_scan", "radix_scan"),
+    ("fwd_hist_kernel", "fwd_hist"), ("tile_map_kernel", "tile_map"),
+    ("transpose_scatter_kernel", "transpose"),
+    ("radix_upsweep", "radix_upsweep"), ("first_upsweep", "radix_upsweep"),
+    ("radix_scan", "radix_scan"),
     ("sort_pass_kernel", "radix_downsweep"), ("rle_kernel", "rle"),
     ("classify_kernel", "classify"), ("chunk_order_kernel", "chunk_order"),
     ("bwd_single_kernel", "bwd_single"), ("bwd_tiny_kernel", "bwd_tiny"),
@@ -229,7 +231,7 @@ def byte_model(spec, st):
         comp["fwd_hist"] = N * si + (B + 1) * si + E * D * sw + B * D * 4
         logi["fwd_hist"] = logi["fwd_pool"]
     comp["transpose"] = N * (si + 4 * psi) + off_b + 8 * N
-    for k in ("radix_upsweep", "radix_scan", "radix_downsweep", "chunk_order"):
+    for k in ("tile_map", "radix_upsweep", "radix_scan", "radix_downsweep", "chunk_order"):
         comp[k] = 0
     comp["rle"] = 4 * N + 8 * U
     comp["classify"] = 8 * U

@@ -18,25 +18,25 @@
 // at the segment's first tile, and is subtracted.
 //
 // Kernels, in launch order (256 threads each, no host readback anywhere):
-//   transpose      workgroup 0 first sets up the segments (per segment,
-//                  tables in key order: lookup count, output base, first
-//                  tile; the segment of every tile; clears the control
-//                  block: tickets, error flag), every workgroup forms the
-//                  segments' output bases itself; then
-//                  key = key_base[t] + I[p], bag = j and, with per-sample
-//                  weights or a mean table, scale = S[p]*(1/L), written at
-//                  the lookup's slot in its table's segment
+//   tile_map       per segment (tables in key order) lookup count, output
+//                  base, first tile; the segment and the first lookup's bag
+//                  of every tile; clears the control block (tickets, error
+//                  flag)
 //   then per digit of 8 or 10 bits (the fewest passes of at most 10 bits
 //   that cover the row range), least significant first:
 //   radix_upsweep  per tile, the count of each value of the digit of
-//                  (key - key_base) in the pass's input; the first one also
-//                  clears the look-back status words of rle and classify
+//                  (key - key_base) in the pass's input; the first one reads
+//                  the rows from the indices, finds each tile's first bag
+//                  and clears the look-back status words of rle and classify
 //   radix_scan     per digit value, the exclusive prefix over all tiles (in
 //                  place) and the total
 //   radix_downsweep  a stable scatter of each 4096-key tile to the offsets
 //                  of the scan (a decoupled look-back instead of the count
 //                  and scan was measured 2-4x slower per pass on MI355X at 34k
-//                  tiles: C5, three passes)
+//                  tiles: C5, three passes); the first one ("transpose")
+//                  forms its tile from the lookups: key = key_base[t] + I[p],
+//                  bag = j and, with per-sample weights or a mean table,
+//                  scale = S[p]*(1/L)
 //   rle            run heads of the sorted keys -> run_start, run_key, U (tile
 //                  offsets by look-back)
 //   classify       one-lookup / tiny / medium short-run tasks, long-run tasks,
@@ -77,6 +77,7 @@ struct PrepDev {
   uint32_t N;
   const uint32_t* tseg;  // segment (position in key order) of each table
   const uint4* seg;      // per segment {lookups, output base, first tile, key base}
+  const uint2* seg2;     // per segment {first position O[t*B], table t}
 };
 
 __device__ __forceinline__ void st_publish(uint64_t* p, uint64_t v) {
@@ -226,71 +227,31 @@ __device__ __forceinline__ uint32_t take_ticket(uint32_t* tickets, uint32_t* s_t
 }
 
 // ------------------------------------------------------------ segments
+// (segment s is table order[s], tables in key order; its lookups are
+// [O[t*B], O[(t+1)*B]))
 
-// Run by one workgroup (workgroup 0 of the transposition).  Segment s is
-// table order[s] (tables in key order); its lookups are [O[t*B], O[(t+1)*B]).
-// Writes {lookups, output base, first tile, key base} per segment, the
-// segment of every tile (a segment of at most eight tiles by its own thread,
-// a larger one by all threads in turn: one thread per segment wrote 2048
-// tiles in 124 us for a single table of 8.4M lookups), the tile total
-// (ctl[kCtlTiles]) and clears the tickets and the error flag.  None of it is
-// read before the next kernel.
+// ------------------------------------------------------------ transposition
+// The transposition from bag order to row order is folded into the first
+// radix pass.  That pass's input order is the lookups' own order (bags are
+// table-major, so a table's lookups are one contiguous range), so its count
+// pass reads the indices themselves, and its scatter forms each lookup's key
+// = key_base[t] + I[p], bag id and contribution scale S[p] * (1/L if mean)
+// (FBTriton page, "Fusion boundaries": the weights scale each contribution
+// before the grouping by row) while it loads its tile, where a separate pass
+// would write all of them out in lookup order and the scatter read them back.
+// Slot i of table t's segment holds position p = O[t*B] + (i - the segment's
+// output base).
+
+// Per segment from the offsets, into dynamic LDS: lookups, output base,
+// first tile and tile count.  Offsets that keep the contract (O[T*B] = N)
+// are unchanged by the clamps; others still give segments inside [0, N) and
+// at most ntiles_max tiles.  Returns the tile total; ends with a barrier.
 template <typename IT>
-__device__ void seg_setup_block(const PrepDev& a, const uint32_t* __restrict__ order,
-                                uint4* __restrict__ seg, uint32_t* __restrict__ tile_seg,
-                                uint32_t ntiles_max, uint32_t* __restrict__ ctl) {
-  __shared__ uint32_t sh4[4];
-  __shared__ uint32_t s_ot[kThreads], s_nt[kThreads];  // first tile and tiles of the batch's segments
+__device__ uint32_t segment_table(const PrepDev& a, const uint32_t* __restrict__ order,
+                                  uint32_t* s_nc, uint32_t* s_on, uint32_t* s_ot, uint32_t* s_nt,
+                                  uint32_t* sh4) {
   const IT* __restrict__ O = reinterpret_cast<const IT*>(a.offsets);
-  for (uint32_t i = threadIdx.x; i < (uint32_t)kCtlWords; i += kThreads)
-    if (i != (uint32_t)kCtlTiles) ctl[i] = 0u;
   uint32_t run_n = 0, run_t = 0;
-  for (uint32_t s0 = 0; s0 < a.T; s0 += kThreads) {
-    const uint32_t s = s0 + threadIdx.x;
-    uint32_t n = 0, t = 0;
-    if (s < a.T) {
-      t = order[s];
-      n = (uint32_t)(O[(int64_t)(t + 1) * a.B] - O[(int64_t)t * a.B]);
-    }
-    uint32_t tot_n, tot_t;
-    const uint64_t on_raw = (uint64_t)run_n + block_excl_scan(n, sh4, tot_n);
-    // offsets that keep the contract (O[T*B] = N) are unchanged by the clamps;
-    // others still give segments inside [0, N) and at most ntiles_max tiles
-    const uint32_t on = on_raw < a.N ? (uint32_t)on_raw : a.N;
-    const uint32_t nc = on_raw < a.N ? (n < a.N - on ? n : a.N - on) : 0u;
-    const uint32_t nt = (nc + kTile - 1) / kTile;
-    const uint32_t ot = run_t + block_excl_scan(nt, sh4, tot_t);
-    if (s < a.T) {
-      seg[s] = make_uint4(nc, on, ot, a.tables[t].key_base);
-      if (nt <= 8u)
-        for (uint32_t k = 0; k < nt && ot + k < ntiles_max; ++k) tile_seg[ot + k] = s;
-    }
-    s_ot[threadIdx.x] = ot;
-    s_nt[threadIdx.x] = s < a.T ? nt : 0u;
-    __syncthreads();
-    const uint32_t nseg = a.T - s0 < kThreads ? a.T - s0 : kThreads;
-    for (uint32_t i = 0; i < nseg; ++i) {
-      const uint32_t n_i = s_nt[i];
-      if (n_i <= 8u) continue;
-      const uint32_t o_i = s_ot[i];
-      for (uint32_t k = threadIdx.x; k < n_i && o_i + k < ntiles_max; k += kThreads)
-        tile_seg[o_i + k] = s0 + i;
-    }
-    __syncthreads();  // s_ot / s_nt are rewritten by the next batch
-    run_n += tot_n;
-    run_t += tot_t;
-  }
-  if (threadIdx.x == 0) ctl[kCtlTiles] = run_t < ntiles_max ? run_t : ntiles_max;
-}
-
-// Output base of every segment (the exclusive prefix of the segments'
-// lookup counts in key order, clamped into [0, N] as seg_setup_block clamps
-// it) into s_base[0, T).  Ends with a barrier.
-template <typename IT>
-__device__ void segment_bases(const PrepDev& a, const uint32_t* __restrict__ order,
-                              uint32_t* s_base, uint32_t* sh4) {
-  const IT* __restrict__ O = reinterpret_cast<const IT*>(a.offsets);
-  uint32_t run_n = 0;
   for (uint32_t s0 = 0; s0 < a.T; s0 += kThreads) {
     const uint32_t s = s0 + threadIdx.x;
     uint32_t n = 0;
@@ -298,103 +259,104 @@ __device__ void segment_bases(const PrepDev& a, const uint32_t* __restrict__ ord
       const uint32_t t = order[s];
       n = (uint32_t)(O[(int64_t)(t + 1) * a.B] - O[(int64_t)t * a.B]);
     }
-    uint32_t tot_n;
+    uint32_t tot_n, tot_t;
     const uint64_t on_raw = (uint64_t)run_n + block_excl_scan(n, sh4, tot_n);
-    if (s < a.T) s_base[s] = on_raw < a.N ? (uint32_t)on_raw : a.N;
+    const uint32_t on = on_raw < a.N ? (uint32_t)on_raw : a.N;
+    const uint32_t nc = on_raw < a.N ? (n < a.N - on ? n : a.N - on) : 0u;
+    const uint32_t nt = (nc + kTile - 1) / kTile;
+    const uint32_t ot = run_t + block_excl_scan(nt, sh4, tot_t);
+    if (s < a.T) {
+      s_nc[s] = nc;
+      s_on[s] = on;
+      s_ot[s] = ot;
+      s_nt[s] = nt;
+    }
     run_n += tot_n;
+    run_t += tot_t;
   }
   __syncthreads();
+  return run_t;
 }
 
-// ------------------------------------------------------------ transposition
-// A workgroup takes `nbp` consecutive bags (at most 256, as many as keep
-// about 2048 workgroups; table-major, so their lookups are one contiguous
-// range) and streams that range: thread i handles positions first + i,
-// first + i + 256, ..., finds each position's bag by binary search over the
-// nbp + 1 offsets held in LDS, and writes the lookup's key and bag id (and,
-// with per-sample weights or mean pooling, its contribution scale
-// S[p] * (1/L if mean); FBTriton page, "Fusion boundaries": the weights scale
-// each contribution before the grouping by row) at its slot in its table's
-// segment.  Index loads and key / bag stores are coalesced runs, four
-// positions in flight per thread (one lane group per bag left each wave with
-// four short dependent chains in flight).
-constexpr uint32_t kTrBags = 256;
-
-// Each workgroup forms the segments' output bases itself (T values in
-// dynamic LDS), so the transposition needs no set-up launch before it;
-// workgroup 0 also writes the segment table, the tile map and the control
-// block for the later kernels.
+// The segment table, the tile map and the control block, before the first
+// count pass.  Every workgroup forms the segment table in LDS (T entries);
+// workgroup 0 writes it out (and, per segment, its first position and
+// table, so that the first pass reads its tile's lookups after one
+// dependent load) with the tile total and clears the control block
+// (tickets, error flag); the grid then writes the segment of every tile (the
+// last segment whose first tile is at or before it) and, streaming the
+// offsets once, the bag of every tile's first lookup: a non-empty bag j of
+// table t holds the first lookup of tile k of t's segment when 4096 k lies in
+// [O[j], O[j+1]) - O[t*B], so every tile gets the one bag that holds its
+// first lookup (for offsets that keep the contract).
 template <typename IT>
-__global__ __launch_bounds__(kThreads) void transpose_kernel(PrepDev a, uint32_t nbp,
-                                                             uint32_t* __restrict__ key,
-                                                             uint32_t* __restrict__ bag,
-                                                             float* __restrict__ scale,
-                                                             const uint32_t* __restrict__ order,
-                                                             uint4* __restrict__ seg_out,
-                                                             uint32_t* __restrict__ tile_seg,
-                                                             uint32_t ntiles_max,
-                                                             uint32_t* __restrict__ ctl) {
-  __shared__ int64_t s_off[kTrBags + 1];
-  __shared__ int64_t s_shift[kTrBags];  // slot of position p: p + shift (its table's)
-  __shared__ uint32_t s_kb[kTrBags];
-  __shared__ uint32_t s_mean[kTrBags];
+__global__ __launch_bounds__(kThreads) void tile_map_kernel(PrepDev a,
+                                                            const uint32_t* __restrict__ order,
+                                                            uint4* __restrict__ seg,
+                                                            uint2* __restrict__ seg2,
+                                                            uint32_t* __restrict__ tile_seg,
+                                                            uint32_t* __restrict__ tile_bag0,
+                                                            uint32_t ntiles_max,
+                                                            uint32_t* __restrict__ ctl) {
+  extern __shared__ uint32_t s_dyn[];  // 4 T words
   __shared__ uint32_t sh4[4];
-  extern __shared__ uint32_t s_base[];  // T output bases, segment order
-  const uint64_t nbag = (uint64_t)a.T * (uint64_t)a.B;
-  const uint64_t j0 = (uint64_t)blockIdx.x * nbp;
-  if (blockIdx.x == 0) seg_setup_block<IT>(a, order, seg_out, tile_seg, ntiles_max, ctl);
-  if (j0 >= nbag || nbp > kTrBags) return;
-  segment_bases<IT>(a, order, s_base, sh4);
-  const uint32_t nb = (uint32_t)min((uint64_t)nbp, nbag - j0);
-  const IT* __restrict__ I = reinterpret_cast<const IT*>(a.indices);
+  uint32_t* s_nc = s_dyn;
+  uint32_t* s_on = s_dyn + a.T;
+  uint32_t* s_ot = s_dyn + 2 * a.T;
+  uint32_t* s_nt = s_dyn + 3 * a.T;
+  const uint32_t total = segment_table<IT>(a, order, s_nc, s_on, s_ot, s_nt, sh4);
+  const uint32_t ntiles = total < ntiles_max ? total : ntiles_max;
+  if (blockIdx.x == 0) {
+    for (uint32_t i = threadIdx.x; i < (uint32_t)kCtlWords; i += kThreads)
+      if (i != (uint32_t)kCtlTiles) ctl[i] = 0u;
+    const IT* __restrict__ O = reinterpret_cast<const IT*>(a.offsets);
+    for (uint32_t s = threadIdx.x; s < a.T; s += kThreads) {
+      const uint32_t t = order[s];
+      seg[s] = make_uint4(s_nc[s], s_on[s], s_ot[s], a.tables[t].key_base);
+      seg2[s] = make_uint2((uint32_t)O[(int64_t)t * a.B], t);
+    }
+    if (threadIdx.x == 0) ctl[kCtlTiles] = ntiles;
+  }
+  const uint32_t gsz = gridDim.x * kThreads, gid = blockIdx.x * kThreads + threadIdx.x;
+  for (uint32_t i = gid; i < ntiles; i += gsz) {
+    uint32_t lo = 0, hi = a.T;  // s_ot[lo] <= i < s_ot[hi] (s_ot[T] read as past every tile)
+    while (hi - lo > 1) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if (s_ot[mid] <= i) lo = mid; else hi = mid;
+    }
+    tile_seg[i] = lo;
+  }
   const IT* __restrict__ O = reinterpret_cast<const IT*>(a.offsets);
-  for (uint32_t i = threadIdx.x; i <= nb; i += kThreads) s_off[i] = (int64_t)O[j0 + i];
-  if (threadIdx.x < nb) {
-    const uint64_t j = j0 + threadIdx.x;
-    const uint32_t t = (uint32_t)(j / (uint64_t)a.B);
-    const TableDev td = a.tables[t];
-    s_shift[threadIdx.x] = (int64_t)s_base[a.tseg[t]] - (int64_t)O[(int64_t)t * a.B];
-    s_kb[threadIdx.x] = td.key_base;
-    s_mean[threadIdx.x] = td.pooling == POOL_MEAN ? 1u : 0u;
-  }
-  __syncthreads();
-  const int64_t first = s_off[0], last = s_off[nb];
-  constexpr int U = 4;
-  for (int64_t p0 = first + threadIdx.x; p0 < last; p0 += (int64_t)U * kThreads) {
-    int64_t p[U];
-    uint32_t q[U];  // bag index in this workgroup's range
-    IT iv[U];
-    float sp[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      p[u] = p0 + (int64_t)u * kThreads;
-      const bool in = p[u] < last && p[u] >= 0 && p[u] < (int64_t)a.N;
-      iv[u] = in ? I[p[u]] : (IT)0;
-      sp[u] = (scale && a.psw && in) ? a.psw[p[u]] : 1.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      // last bag q with s_off[q] <= p (empty bags share an offset with the next)
-      uint32_t lo = 0, hi = nb;  // s_off[lo] <= p < s_off[hi]
-      while (hi - lo > 1) {
-        const uint32_t mid = (lo + hi) >> 1;
-        if (s_off[mid] <= p[u]) lo = mid; else hi = mid;
-      }
-      q[u] = lo;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (p[u] >= last || p[u] < 0 || p[u] >= (int64_t)a.N) continue;
-      const int64_t d = p[u] + s_shift[q[u]];
-      if ((uint64_t)d >= (uint64_t)a.N) continue;  // only for offsets that break the contract
-      key[d] = s_kb[q[u]] + (uint32_t)iv[u];
-      bag[d] = (uint32_t)(j0 + q[u]);
-      if (scale) {
-        const int64_t L = s_off[q[u] + 1] - s_off[q[u]];
-        scale[d] = s_mean[q[u]] ? sp[u] / (float)L : sp[u];
-      }
+  const uint64_t B = (uint64_t)a.B, nbag = (uint64_t)a.T * B;
+  for (uint64_t j = gid; j < nbag; j += gsz) {
+    const uint32_t t = (uint32_t)(j / B);
+    const uint32_t s = a.tseg[t];
+    const uint32_t nt = s < a.T ? s_nt[s] : 0u;
+    if (nt == 0) continue;
+    const int64_t base = (int64_t)O[(uint64_t)t * B];
+    const int64_t lo = (int64_t)O[j] - base, hi = (int64_t)O[j + 1] - base;
+    if (hi <= lo || hi <= 0) continue;
+    const int64_t k0 = lo <= 0 ? 0 : (lo + kTile - 1) / kTile;
+    const int64_t k1 = (hi - 1) / kTile < (int64_t)nt - 1 ? (hi - 1) / kTile : (int64_t)nt - 1;
+    for (int64_t k = k0; k <= k1; ++k) {
+      const uint64_t tile = (uint64_t)s_ot[s] + (uint64_t)k;
+      if (tile < ntiles) tile_bag0[tile] = (uint32_t)j;
     }
   }
+}
+
+// Position of slot i of a segment (pshift = its table's first position minus
+// its output base), clamped into [0, N): inside for offsets that keep the
+// contract, and in bounds for any others.
+__device__ __forceinline__ uint32_t slot_pos(int64_t pshift, uint32_t i, uint32_t N) {
+  const int64_t p = (int64_t)i + pshift;
+  return p < 0 ? 0u : (p >= (int64_t)N ? N - 1u : (uint32_t)p);
+}
+
+// The row of lookup p: an int64 index is read as its low word (rows < 2^32).
+template <typename IT>
+__device__ __forceinline__ uint32_t index_lo(const void* I, uint32_t p) {
+  return reinterpret_cast<const uint32_t*>(I)[(size_t)p * (sizeof(IT) / 4)];
 }
 
 // ------------------------------------------------------------- radix sort
@@ -476,6 +438,56 @@ __global__ __launch_bounds__(kThreads) void radix_upsweep(const uint32_t* __rest
     st[i] = 0ull;
 }
 
+// The first pass's counts, from the indices: as radix_upsweep, with the row
+// of slot i read at its position in the lookups (the first digit has shift
+// 0).
+template <typename IT, int DB>
+__global__ __launch_bounds__(kThreads) void first_upsweep(PrepDev a,
+                                                          const uint32_t* __restrict__ tile_seg,
+                                                          const uint32_t* __restrict__ ctl,
+                                                          uint32_t* __restrict__ cnt,
+                                                          uint32_t ntiles,
+                                                          uint64_t* __restrict__ st, uint64_t nst) {
+  constexpr uint32_t R = 1u << DB;
+  __shared__ uint32_t h[kThreads / kWave][R];
+  const uint32_t wave = threadIdx.x / kWave, lane = lane_id();
+  const uint32_t tile = xcd_tile();
+  const bool live = tile < ctl[kCtlTiles];
+  for (uint32_t i = threadIdx.x; i < 4u * R; i += kThreads) (&h[0][0])[i] = 0u;
+  __syncthreads();
+  if (live) {
+    uint32_t sid, b, e;
+    const uint4 sg = tile_span(a.seg, tile_seg, tile, sid, b, e);
+    const int64_t pshift = (int64_t)a.seg2[sid].x - (int64_t)sg.y;
+    const uint32_t wb = b + wave * (kTile / 4);
+    uint32_t k[kItems];
+#pragma unroll
+    for (int r = 0; r < kItems; ++r) {
+      const uint32_t i = wb + (uint32_t)r * kWave + lane;
+      k[r] = i < e ? index_lo<IT>(a.indices, slot_pos(pshift, i, a.N)) : 0u;
+    }
+#pragma unroll
+    for (int r = 0; r < kItems; ++r) {
+      const bool valid = wb + (uint32_t)r * kWave + lane < e;
+      const uint32_t d = k[r] & (R - 1u);
+      const uint32_t d0 = __builtin_amdgcn_readfirstlane(d);
+      const uint64_t in = __ballot(valid);
+      if (__ballot(valid && d != d0) == 0) {
+        if (lane == 0 && in != 0) h[wave][d0] += (uint32_t)__popcll(in);
+      } else if (valid) {
+        atomicAdd(&h[wave][d], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  if (live)
+    for (uint32_t d = threadIdx.x; d < R; d += kThreads)
+      cnt[(size_t)d * ntiles + tile] = h[0][d] + h[1][d] + h[2][d] + h[3][d];
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < nst; i += stride)
+    st[i] = 0ull;
+}
+
 // One workgroup per digit value d: the exclusive prefix over all tiles of the
 // counts of d, written tile-major (tex[tile * 2^DB + d], so that a tile's
 // prefixes of every digit are one contiguous vector for the scatter), and the
@@ -530,6 +542,15 @@ struct SortPass {
   const uint32_t* totals;     // digit totals of this pass over all segments
   const uint32_t* tile_excl;  // per tile and digit (tile-major), the count in earlier tiles
   uint32_t ntiles;
+  // the first pass only: the lookups, and the bag of each tile's first lookup
+  const void* indices;
+  const void* offsets;
+  const float* psw;
+  const TableDev* tables;
+  const uint2* seg2;          // per segment {first position O[t*B], table t}
+  const uint32_t* tile_bag0;
+  int64_t B;
+  uint32_t N, T;
 };
 
 // Stable scatter of one tile to the offsets of the scan: the count of each
@@ -542,8 +563,15 @@ struct SortPass {
 // the Q = 2^DB / 256 consecutive digit values [tQ, tQ + Q) for the per-digit
 // prefixes.  Keys, bag ids and scales pass through one LDS buffer in turn on
 // their way to their coalesced global stores.
-template <int DB, bool SC>
-__global__ __launch_bounds__(kThreads) void sort_pass_kernel(SortPass p) {
+//
+// FIRST: the first pass, which forms its tile from the lookups (the
+// transposition above).  Slot i's key and scale come from its position p;
+// its bag is the last bag j with O[j] <= p, found by binary search over the
+// offsets of the bags from the tile's first lookup's to the next tile's
+// (held in the LDS buffer, or read from global memory when there are more
+// than 4096 of them, which takes empty bags).
+template <int DB, bool SC, bool FIRST, typename IT>
+__device__ __forceinline__ void sort_pass_body(const SortPass& p) {
   constexpr uint32_t R = 1u << DB;
   constexpr int Q = (int)(R / kThreads);
   static_assert(Q >= 1 && R % kThreads == 0, "at least one digit value per thread");
@@ -556,6 +584,12 @@ __global__ __launch_bounds__(kThreads) void sort_pass_kernel(SortPass p) {
   const uint32_t lane = lane_id(), wave = threadIdx.x / kWave;
   const uint32_t tile = xcd_tile();
   if (tile >= *p.tiles) return;  // the grid is sized for the most tiles segments can need
+  // the first pass's tile bags, loaded with the segment (both need only the tile)
+  uint32_t tb0 = 0, tb1 = 0;
+  if constexpr (FIRST) {
+    tb0 = p.tile_bag0[tile];
+    tb1 = p.tile_bag0[tile + 1u < p.ntiles ? tile + 1u : tile];
+  }
   for (uint32_t i = threadIdx.x; i < 4u * R; i += kThreads) (&wcnt[0][0])[i] = 0u;
   uint32_t sid, b, e;
   const uint4 sg = tile_span(p.seg, p.tile_seg, tile, sid, b, e);
@@ -563,13 +597,95 @@ __global__ __launch_bounds__(kThreads) void sort_pass_kernel(SortPass p) {
   // the whole tile is loaded before any ranking
   uint32_t k[kItems], v[kItems], rk[kItems];
   float sc[kItems];
+  if constexpr (FIRST) {
+    const IT* __restrict__ O = reinterpret_cast<const IT*>(p.offsets);
+    const uint2 s2 = p.seg2[sid];
+    const uint32_t t = s2.y < p.T ? s2.y : 0u;
+    const uint64_t j0 = (uint64_t)t * (uint64_t)p.B;
+    const int64_t pshift = (int64_t)s2.x - (int64_t)sg.y;
+    // rows and weights in flight while the offsets load
+    float sp[kItems];
 #pragma unroll
-  for (int r = 0; r < kItems; ++r) {
-    const uint32_t i = wbase + (uint32_t)r * kWave + lane;
-    const uint32_t ii = i < e ? i : e - 1;
-    k[r] = p.kin[ii];
-    v[r] = p.vin[ii];
-    if (SC) sc[r] = p.sin[ii];
+    for (int r = 0; r < kItems; ++r) {
+      const uint32_t i = wbase + (uint32_t)r * kWave + lane;
+      const uint32_t pp = slot_pos(pshift, i < e ? i : e - 1, p.N);
+      k[r] = index_lo<IT>(p.indices, pp);
+      sp[r] = (SC && p.psw) ? p.psw[pp] : 1.0f;
+    }
+    // offsets of bags jb .. je + 1 (the clamps hold for what the count pass wrote)
+    const uint64_t jlast = j0 + (uint64_t)p.B - 1u;
+    const uint32_t z_next = sg.z + (sg.x + kTile - 1) / kTile;
+    uint64_t jb = tb0;
+    uint64_t je = tile + 1u < z_next ? (uint64_t)tb1 : jlast;
+    jb = jb < j0 ? j0 : (jb > jlast ? jlast : jb);
+    je = je < jb ? jb : (je > jlast ? jlast : je);
+    const uint32_t nw = (uint32_t)(je - jb) + 2u;
+    const bool fits = nw <= (uint32_t)kTile;  // uniform
+    // top: the largest power of two <= nw - 1; entries [nw, 2 top) are set
+    // past every position (2 top <= 4096 when the window fits), so the search
+    // below reads any entry it can reach without a bounds check
+    const uint32_t top = 1u << (31 - __builtin_clz(nw - 1u));
+    if (fits) {
+      for (uint32_t i = threadIdx.x; i < nw; i += kThreads) s_buf[i] = (uint32_t)O[jb + i];
+      for (uint32_t i = nw + threadIdx.x; i < 2u * top; i += kThreads) s_buf[i] = 0xffffffffu;
+    }
+    __syncthreads();
+    const bool mean = SC && p.tables[t].pooling == POOL_MEAN;
+    const uint32_t kb = sg.w;
+    // w[r]: the last window entry at or before the slot's position (entry 0
+    // is, and entry nw - 1 is past it, for offsets that keep the contract),
+    // so bag jb + w holds it.  In the LDS window the slots take the steps
+    // top, top / 2, ..., 1 together, so each step issues kItems independent
+    // reads.
+    uint32_t w[kItems];
+#pragma unroll
+    for (int r = 0; r < kItems; ++r) w[r] = 0;
+    if (fits) {
+      uint32_t pp[kItems];
+#pragma unroll
+      for (int r = 0; r < kItems; ++r) {
+        const uint32_t i = wbase + (uint32_t)r * kWave + lane;
+        pp[r] = slot_pos(pshift, i < e ? i : e - 1, p.N);
+      }
+      for (uint32_t step = top; step > 0; step >>= 1) {
+        uint32_t o[kItems];
+#pragma unroll
+        for (int r = 0; r < kItems; ++r) o[r] = s_buf[w[r] + step];
+#pragma unroll
+        for (int r = 0; r < kItems; ++r) w[r] = o[r] <= pp[r] ? w[r] + step : w[r];
+      }
+    } else {
+#pragma unroll 1
+      for (int r = 0; r < kItems; ++r) {
+        const uint32_t i = wbase + (uint32_t)r * kWave + lane;
+        const uint32_t pp = slot_pos(pshift, i < e ? i : e - 1, p.N);
+        uint32_t lo = 0, hi = nw - 1u;  // offset[lo] <= pp < offset[hi]
+        while (hi - lo > 1) {
+          const uint32_t mid = (lo + hi) >> 1;
+          if ((uint32_t)O[jb + mid] <= pp) lo = mid; else hi = mid;
+        }
+        w[r] = lo;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kItems; ++r) {
+      k[r] = kb + k[r];
+      v[r] = (uint32_t)(jb + w[r]);
+      if (SC) {
+        const uint32_t L = fits ? s_buf[w[r] + 1u] - s_buf[w[r]]
+                                : (uint32_t)O[jb + w[r] + 1u] - (uint32_t)O[jb + w[r]];
+        sc[r] = mean ? sp[r] / (float)L : sp[r];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < kItems; ++r) {
+      const uint32_t i = wbase + (uint32_t)r * kWave + lane;
+      const uint32_t ii = i < e ? i : e - 1;
+      k[r] = p.kin[ii];
+      v[r] = p.vin[ii];
+      if (SC) sc[r] = p.sin[ii];
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   const uint32_t d0 = threadIdx.x * (uint32_t)Q;  // the digits this thread publishes
@@ -679,6 +795,17 @@ __global__ __launch_bounds__(kThreads) void sort_pass_kernel(SortPass p) {
       if (dst[r] != 0xffffffffu)
         p.sout[dst[r]] = __builtin_bit_cast(float, s_buf[threadIdx.x + (uint32_t)r * kThreads]);
   }
+}
+
+template <int DB, bool SC>
+__global__ __launch_bounds__(kThreads) void sort_pass_kernel(SortPass p) {
+  sort_pass_body<DB, SC, false, uint32_t>(p);
+}
+
+// The first pass, with the transposition folded in.
+template <int DB, bool SC, typename IT>
+__global__ __launch_bounds__(kThreads) void transpose_scatter_kernel(SortPass p) {
+  sort_pass_body<DB, SC, true, IT>(p);
 }
 
 // --------------------------------------------------- run-length encoding
@@ -1075,6 +1202,26 @@ void launch_sort_pass(const SortPass& sp, uint32_t* cnt, bool sc, uint32_t sgrid
                sp);
 }
 
+// The first pass: counts from the lookups, prefixes, the scatter that forms
+// its tiles from the lookups (the transposition).
+template <int DB, typename IT>
+void launch_first_pass(const SortPass& sp, const PrepDev& d, uint32_t* cnt, bool sc,
+                       uint32_t sgrid, const uint32_t* ctl, uint64_t* st, uint64_t nst,
+                       hipStream_t s) {
+  uint32_t* tex = const_cast<uint32_t*>(sp.tile_excl);
+  uint32_t* totals = const_cast<uint32_t*>(sp.totals);
+  TBE_LAUNCH("radix_upsweep", (first_upsweep<IT, DB>), dim3(sgrid), dim3(kThreads), s, d,
+             sp.tile_seg, ctl, cnt, sp.ntiles, st, nst);
+  TBE_LAUNCH("radix_scan", radix_scan<DB>, dim3(1u << DB), dim3(kThreads), s, cnt, sp.ntiles, ctl,
+             tex, totals);
+  if (sc)
+    TBE_LAUNCH("transpose", (transpose_scatter_kernel<DB, true, IT>), dim3(sgrid), dim3(kThreads), s,
+               sp);
+  else
+    TBE_LAUNCH("transpose", (transpose_scatter_kernel<DB, false, IT>), dim3(sgrid), dim3(kThreads),
+               s, sp);
+}
+
 }  // namespace
 
 hipError_t launch_preprocess(const PrepArgs& p, int /*num_cus*/, hipStream_t s) {
@@ -1092,36 +1239,48 @@ hipError_t launch_preprocess(const PrepArgs& p, int /*num_cus*/, hipStream_t s) 
   uint4* seg = reinterpret_cast<uint4*>(ws + L.seg);
   uint32_t* tile_seg = u32p(L.tile_seg);
   uint32_t* totals = u32p(L.totals);
-  PrepDev d{p.tables, p.T, p.nb, p.B, p.indices, p.offsets, p.psw, p.N, p.tseg, seg};
-  const uint64_t nbag = (uint64_t)p.T * (uint64_t)p.B;
-  const uint32_t nbp = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(kTrBags, nbag / 2048));
-  const uint32_t tgrid = (uint32_t)((nbag + nbp - 1) / nbp);
-  const size_t tshm = sizeof(uint32_t) * (size_t)p.T;
-  if (p.itype == IT_I32)
-    TBE_LAUNCH_SHM("transpose", transpose_kernel<int32_t>, dim3(tgrid), dim3(kThreads), tshm, s,
-                   d, nbp, u32p(L.key_a), u32p(L.val_a), sc ? f32p(L.sc_a) : nullptr, p.order,
-                   seg, tile_seg, L.ntiles_max, ctl);
-  else
-    TBE_LAUNCH_SHM("transpose", transpose_kernel<int64_t>, dim3(tgrid), dim3(kThreads), tshm, s,
-                   d, nbp, u32p(L.key_a), u32p(L.val_a), sc ? f32p(L.sc_a) : nullptr, p.order,
-                   seg, tile_seg, L.ntiles_max, ctl);
+  uint2* seg2 = reinterpret_cast<uint2*>(ws + L.seg2);
+  PrepDev d{p.tables, p.T, p.nb, p.B, p.indices, p.offsets, p.psw, p.N, p.tseg, seg, seg2};
+  uint32_t* bag0 = u32p(L.tile_bag0);
+  {
+    // at least four bags per thread, at most 1024 workgroups
+    const uint64_t nbag = (uint64_t)p.T * (uint64_t)p.B;
+    const uint32_t mgrid = (uint32_t)std::min<uint64_t>(1024, std::max<uint64_t>(1, nbag / 1024));
+    const size_t mshm = 4 * sizeof(uint32_t) * (size_t)p.T;
+    if (p.itype == IT_I32)
+      TBE_LAUNCH_SHM("tile_map", tile_map_kernel<int32_t>, dim3(mgrid), dim3(kThreads), mshm, s,
+                     d, p.order, seg, seg2, tile_seg, bag0, L.ntiles_max, ctl);
+    else
+      TBE_LAUNCH_SHM("tile_map", tile_map_kernel<int64_t>, dim3(mgrid), dim3(kThreads), mshm, s,
+                     d, p.order, seg, seg2, tile_seg, bag0, L.ntiles_max, ctl);
+  }
 
-  // ping-pong a -> b -> a ...; the final buffers are b for an odd pass count
+  // pass 0 forms its tiles from the lookups and writes the b buffers; then
+  // ping-pong b -> a -> b ..., so the final buffers are b for an odd pass count
   const uint64_t nst = (L.st_end - L.st_rle) / 8;
   const uint32_t sgrid = 8u * ((L.ntiles_max + 7u) / 8u);  // xcd_tile(): a multiple of 8
+  uint32_t* cnt = u32p(L.tile_cnt);
   for (int pass = 0; pass < L.npass; ++pass) {
     const bool ab = (pass % 2) == 0;
     SortPass sp{u32p(ab ? L.key_a : L.key_b), u32p(ab ? L.val_a : L.val_b),
                 f32p(ab ? L.sc_a : L.sc_b),   u32p(ab ? L.key_b : L.key_a),
                 u32p(ab ? L.val_b : L.val_a), f32p(ab ? L.sc_b : L.sc_a),
                 (uint32_t)(pass * L.digit_bits), seg, tile_seg, ctl + kCtlTiles,
-                totals, u32p(L.tile_excl), L.ntiles_max};
-    const uint64_t clear = pass == 0 ? nst : (uint64_t)0;
-    uint32_t* cnt = u32p(L.tile_cnt);
-    if (L.digit_bits == 8)
-      launch_sort_pass<8>(sp, cnt, sc, sgrid, ctl, u64p(L.st_rle), clear, s);
-    else
-      launch_sort_pass<10>(sp, cnt, sc, sgrid, ctl, u64p(L.st_rle), clear, s);
+                totals, u32p(L.tile_excl), L.ntiles_max,
+                p.indices, p.offsets, p.psw, p.tables, seg2, bag0, p.B, p.N, p.T};
+    if (pass == 0) {
+      if (L.digit_bits == 8) {
+        if (p.itype == IT_I32) launch_first_pass<8, int32_t>(sp, d, cnt, sc, sgrid, ctl, u64p(L.st_rle), nst, s);
+        else launch_first_pass<8, int64_t>(sp, d, cnt, sc, sgrid, ctl, u64p(L.st_rle), nst, s);
+      } else {
+        if (p.itype == IT_I32) launch_first_pass<10, int32_t>(sp, d, cnt, sc, sgrid, ctl, u64p(L.st_rle), nst, s);
+        else launch_first_pass<10, int64_t>(sp, d, cnt, sc, sgrid, ctl, u64p(L.st_rle), nst, s);
+      }
+    } else if (L.digit_bits == 8) {
+      launch_sort_pass<8>(sp, cnt, sc, sgrid, ctl, u64p(L.st_rle), 0, s);
+    } else {
+      launch_sort_pass<10>(sp, cnt, sc, sgrid, ctl, u64p(L.st_rle), 0, s);
+    }
   }
   const uint32_t* skey = u32p(L.final_in_b ? L.key_b : L.key_a);
   const uint32_t* sbag = u32p(L.final_in_b ? L.val_b : L.val_a);

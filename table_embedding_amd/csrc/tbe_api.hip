@@ -169,7 +169,9 @@ WsLayout layout(const tbe_plan* P, int64_t N) {
   L.sc_b = take(n * 4);
   L.ctl = take((size_t)kCtlWords * 4);
   L.seg = take((size_t)P->T * 16);
+  L.seg2 = take((size_t)P->T * 8);
   L.tile_seg = take((size_t)L.ntiles_max * 4);
+  L.tile_bag0 = take((size_t)L.ntiles_max * 4);
   L.totals = take(((size_t)1 << L.digit_bits) * 4);
   L.tile_cnt = take(((size_t)1 << L.digit_bits) * L.ntiles_max * 4);
   L.tile_excl = take(((size_t)1 << L.digit_bits) * L.ntiles_max * 4);

@@ -117,7 +117,9 @@ struct WsLayout {
   size_t key_a, key_b, val_a, val_b, sc_a, sc_b;  // sort ping-pong: key, bag id, scale
   size_t ctl;                                      // control block, kCtlWords uint32
   size_t seg;       // T uint4 {lookups, output base, first tile, key base}, tables in key order
+  size_t seg2;      // T uint2 {first position O[t*B], table t}, the same order
   size_t tile_seg;  // ntiles_max uint32: segment of each sort tile
+  size_t tile_bag0;  // ntiles_max uint32: bag of each sort tile's first lookup
   size_t totals;    // 2^digit_bits digit totals of the current pass
   size_t tile_cnt;   // 2^digit_bits x ntiles_max per-tile digit counts of the current pass
                      // (digit-major)

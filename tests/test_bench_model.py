@@ -7,7 +7,7 @@ import numpy as np
 import bench
 import tbe_workloads as wl
 
-BWD_KERNELS = ("transpose", "radix_upsweep", "radix_scan", "radix_downsweep", "rle", "classify",
+BWD_KERNELS = ("tile_map", "transpose", "radix_upsweep", "radix_scan", "radix_downsweep", "rle", "classify",
                "chunk_order", "bwd_single", "bwd_tiny", "bwd_medium", "bwd_chunk",
                "bwd_long_update", "dense_select", "dense_partial", "dense_update")
 
