@@ -384,12 +384,29 @@ __device__ __forceinline__ uint32_t xcd_tile() {
   return (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
 }
 
+// Adds digit d of this lane's item (when valid) to the workgroup's counts,
+// kept in four copies h[c][.] by lane (c = lane mod 4) and shared by the
+// waves.  A hot row puts its digit in many lanes of a wave, and the LDS
+// serializes the atomics of one instruction that meet at one address; four
+// copies make those meetings a quarter as long (MI355X, C5, a count pass
+// 229 -> 170 us, against 147 us with the counting's atomics left out).  A
+// wave whose valid items all share one digit adds them with one atomic.
+template <int R>
+__device__ __forceinline__ void count_digit(uint32_t (*h)[R], uint32_t d, bool valid,
+                                            uint32_t lane) {
+  const uint32_t d0 = __builtin_amdgcn_readfirstlane(d);
+  const uint64_t in = __ballot(valid);
+  if (__ballot(valid && d != d0) == 0) {
+    if (lane == 0 && in != 0) atomicAdd(&h[0][d0], (uint32_t)__popcll(in));
+  } else if (valid) {
+    atomicAdd(&h[lane & 3u][d], 1u);
+  }
+}
+
 // Counts of each digit value of one pass for every tile of the pass's input,
 // digit-major: cnt[d * ntiles + tile], digits of DB bits of the row
-// (key - key_base).  A wave whose 64 keys share one digit (a tile inside a
-// hot row's run) adds them in one step instead of 64 conflicting LDS
-// atomics.  With nst > 0 the kernel also clears nst look-back status words of
-// the later kernels.
+// (key - key_base), counted by count_digit.  With nst > 0 the kernel also
+// clears nst look-back status words of the later kernels.
 template <int DB>
 __global__ __launch_bounds__(kThreads) void radix_upsweep(const uint32_t* __restrict__ keys,
                                                           const uint4* __restrict__ seg,
@@ -400,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void radix_upsweep(const uint32_t* __rest
                                                           uint32_t ntiles,
                                                           uint64_t* __restrict__ st, uint64_t nst) {
   constexpr uint32_t R = 1u << DB;
-  __shared__ uint32_t h[kThreads / kWave][R];
+  __shared__ uint32_t h[4][R];
   const uint32_t wave = threadIdx.x / kWave, lane = lane_id();
   const uint32_t tile = xcd_tile();
   const bool live = tile < ctl[kCtlTiles];
@@ -417,17 +434,9 @@ __global__ __launch_bounds__(kThreads) void radix_upsweep(const uint32_t* __rest
       k[r] = i < e ? keys[i] : 0u;
     }
 #pragma unroll
-    for (int r = 0; r < kItems; ++r) {
-      const bool valid = wb + (uint32_t)r * kWave + lane < e;
-      const uint32_t d = ((k[r] - sg.w) >> shift) & (R - 1u);
-      const uint32_t d0 = __builtin_amdgcn_readfirstlane(d);
-      const uint64_t in = __ballot(valid);
-      if (__ballot(valid && d != d0) == 0) {
-        if (lane == 0 && in != 0) h[wave][d0] += (uint32_t)__popcll(in);
-      } else if (valid) {
-        atomicAdd(&h[wave][d], 1u);
-      }
-    }
+    for (int r = 0; r < kItems; ++r)
+      count_digit<R>(h, ((k[r] - sg.w) >> shift) & (R - 1u),
+                     wb + (uint32_t)r * kWave + lane < e, lane);
   }
   __syncthreads();
   if (live)
@@ -449,7 +458,7 @@ __global__ __launch_bounds__(kThreads) void first_upsweep(PrepDev a,
                                                           uint32_t ntiles,
                                                           uint64_t* __restrict__ st, uint64_t nst) {
   constexpr uint32_t R = 1u << DB;
-  __shared__ uint32_t h[kThreads / kWave][R];
+  __shared__ uint32_t h[4][R];
   const uint32_t wave = threadIdx.x / kWave, lane = lane_id();
   const uint32_t tile = xcd_tile();
   const bool live = tile < ctl[kCtlTiles];
@@ -467,17 +476,8 @@ __global__ __launch_bounds__(kThreads) void first_upsweep(PrepDev a,
       k[r] = i < e ? index_lo<IT>(a.indices, slot_pos(pshift, i, a.N)) : 0u;
     }
 #pragma unroll
-    for (int r = 0; r < kItems; ++r) {
-      const bool valid = wb + (uint32_t)r * kWave + lane < e;
-      const uint32_t d = k[r] & (R - 1u);
-      const uint32_t d0 = __builtin_amdgcn_readfirstlane(d);
-      const uint64_t in = __ballot(valid);
-      if (__ballot(valid && d != d0) == 0) {
-        if (lane == 0 && in != 0) h[wave][d0] += (uint32_t)__popcll(in);
-      } else if (valid) {
-        atomicAdd(&h[wave][d], 1u);
-      }
-    }
+    for (int r = 0; r < kItems; ++r)
+      count_digit<R>(h, k[r] & (R - 1u), wb + (uint32_t)r * kWave + lane < e, lane);
   }
   __syncthreads();
   if (live)
