@@ -97,6 +97,16 @@ def _spec(name):
         # a bag, which enter the contraction in 8-bit parts
         return wl.Spec("dense_wide", 2016, [50, 300], [64, 160], [0, 1], "f32", 512,
                        "list:300,1,2000,5,700,0,64", "zipf:1.5", "i64", False)
+    if name == "sparse_bags":
+        # one bag in ten holds lookups: a 4096-lookup sort tile spans more
+        # than 4096 bags, so the first pass finds bags in global memory
+        return wl.Spec("sparse_bags", 2018, [3000, 500], [16, 32], [1, 0], "f16", 20000,
+                       "list:0,0,0,0,0,0,0,0,0,3", "zipf:1.1", "i32", True)
+    if name == "thin_bags":
+        # about 1.9 lookups per bag: a tile's window of offsets (about 2200
+        # bags) is padded to the full 4096 LDS entries
+        return wl.Spec("thin_bags", 2019, [4000, 1000], [8, 64], [0, 1], "bf16", 30000,
+                       "list:0,5,0,0,7,1,0", "zipf:1.2", "i64", True)
     if name == "rows_21b":
         # 21 row bits: three 8-bit radix passes (an odd count) at a small size
         return wl.Spec("rows_21b", 2012, [(1 << 20) + 3, 50], [8, 16], [0, 1], "f16", 300,
@@ -111,7 +121,8 @@ def _spec(name):
 MAIN = ["C1", "C2s", "C3s", "C4s", "C5s"]
 EDGE = ["empty_bags", "all_empty", "one_bag", "one_row", "const31", "const32", "const255",
         "const256", "const257", "wide_f32", "wide_bf16", "many_tables", "many_bags",
-        "heavy_chunks", "cut_bags", "dense_mean", "dense_wide", "rows_21b", "rows_25b"]
+        "heavy_chunks", "cut_bags", "dense_mean", "dense_wide", "rows_21b", "rows_25b",
+        "sparse_bags", "thin_bags"]
 
 
 def _announce(name, what):
