@@ -268,8 +268,14 @@ __device__ __forceinline__ void single_pair(const BwdArgs& a, const TableDev* s_
 }
 
 // In list order: subgroup sg of the launch takes positions sg, sg + nsg, ...
+// With streamed rows the next task record loads while the current run's rows
+// are in flight, and the one-chunk rows' registers are held to eight waves
+// per SIMD (two spill): C5 2994 -> 2874 us per launch; the prefetch at the
+// seven waves its registers would otherwise allow, 3032 us.  Wider rows keep
+// their registers (held to eight waves they spill 20 to 33).
 template <int WD, int VEC, int NC, bool SCALE, bool TDL, bool NT>
-__global__ __launch_bounds__(kThreads) void bwd_single_kernel(BwdArgs a, BucketSet S) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NT && NC == 1 ? 8 : 1)))
+void bwd_single_kernel(BwdArgs a, BucketSet S) {
   if (prep_failed(a)) return;
   BucketDev bk;
   uint32_t bucket, lb, lg;
@@ -286,9 +292,13 @@ __global__ __launch_bounds__(kThreads) void bwd_single_kernel(BwdArgs a, BucketS
     // Batches whose rows are streamed past the caches: one run per step,
     // measured faster than pairs there (8.4M lookups: 283 -> 249 us; 134M
     // lookups: 3117 -> 2917 us).
-    for (uint32_t s = beg + sg; s < end; s += nsg_grid)
-      single_pair<WD, VEC, NC, SCALE, TDL, NT, 1>(a, s_td, a.single_task[s], a.single_task[s],
-                                                  false, lpr, lane_in);
+    uint32_t s = beg + sg;
+    uint4 next = s < end ? a.single_task[s] : make_uint4(0, 0, 0, 0);
+    for (; s < end; s += nsg_grid) {
+      const uint4 tk = next;
+      if (s + nsg_grid < end) next = a.single_task[s + nsg_grid];
+      single_pair<WD, VEC, NC, SCALE, TDL, NT, 1>(a, s_td, tk, tk, false, lpr, lane_in);
+    }
     return;
   }
   for (uint32_t s = beg + sg; s < end; s += 2 * nsg_grid) {
