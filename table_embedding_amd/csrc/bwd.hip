@@ -673,6 +673,54 @@ __global__ __launch_bounds__(kThreads) void chunk_order_kernel(BwdArgs a) {
   }
 }
 
+// The chunks at the next kThreads positions of a workgroup's walk (c0,
+// c0 + cstep, ...; one per thread) that the workgroup updates, listed in walk
+// order in LDS: positions past the list, the chunks of the contraction's hot
+// rows and malformed entries (never, for lists the preprocessing wrote) are
+// dropped.  Tested one at a time, each skipped chunk cost the workgroup its
+// own chain of three dependent loads, and at C5 most chunks belong to hot
+// rows.  Returns how many were listed; ends with a barrier.
+struct ChunkBatch {
+  uint32_t cp[kThreads];
+  uint4 task[kThreads];
+  uint32_t wcnt[kThreads / kWave];
+};
+
+template <bool FUSED>
+__device__ __forceinline__ uint32_t chunk_batch(const BwdArgs& a, uint64_t c0, uint32_t cstep,
+                                                uint32_t beg, uint32_t end, ChunkBatch& cb) {
+  const uint64_t cw = c0 + (uint64_t)threadIdx.x * cstep;
+  bool take = false;
+  uint32_t cp = 0;
+  uint4 task = make_uint4(0, 0, 0, 0);
+  if (cw < end) {
+    cp = a.chunk_perm ? a.chunk_perm[cw] : (uint32_t)cw;  // position of the chunk taken
+    if (cp >= beg && cp < end) {
+      task = a.chunk_task[cp];  // {start, len, table, long index}
+      take = chunk_ok(a, task) && (!FUSED || long_ok(a, task.w)) &&
+             !(a.long_flag && a.long_flag[task.w]);  // a hot row: the contraction's
+    }
+  }
+  const uint32_t lane = lane_id(), wave = threadIdx.x / kWave;
+  const uint64_t m = __ballot(take);
+  if (lane == 0) cb.wcnt[wave] = (uint32_t)__popcll(m);
+  __syncthreads();
+  uint32_t base = 0, n = 0;
+#pragma unroll
+  for (uint32_t w = 0; w < kThreads / kWave; ++w) {
+    const uint32_t x = cb.wcnt[w];
+    base += w < wave ? x : 0u;
+    n += x;
+  }
+  if (take) {
+    const uint32_t i = base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+    cb.cp[i] = cp;
+    cb.task[i] = task;
+  }
+  __syncthreads();
+  return n;
+}
+
 template <int WD, int VEC, int NC, int IF>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a, BucketSet S) {
   if (prep_failed(a)) return;
@@ -680,19 +728,21 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a, BucketSe
   uint32_t bucket, lb, lg;
   set_pick(S, bk, bucket, lb, lg);
   __shared__ WgSmem<VEC, NC> sm;
+  __shared__ ChunkBatch cb;
   const uint32_t beg = list_begin(a, 4, bucket);
   const uint32_t end = min(list_begin(a, 4, bucket + 1), a.max_chunks);
   uint32_t c, cstep;
   chunk_walk(lb, lg, beg, c, cstep);
-  for (; c < end; c += cstep) {
-    const uint32_t cp = a.chunk_perm ? a.chunk_perm[c] : c;  // position of the chunk taken
-    const uint4 task = a.chunk_task[cp];  // {start, len, table, long index}
-    if (cp < beg || cp >= end || !chunk_ok(a, task)) continue;  // uniform; never for valid lists
-    if (a.long_flag && a.long_flag[task.w]) continue;  // a hot row: the contraction's
-    const TableDev td = a.tables[task.z];
-    wg_gather<VEC, NC, IF>(a, bk, td, task.z, task.x, task.x + task.y, sm);
-    chunk_store<VEC, NC, false>(a, bk, td.dim, cp, sm);
-    __syncthreads();
+  for (uint64_t c0 = c; c0 < end; c0 += (uint64_t)kThreads * cstep) {
+    const uint32_t n = chunk_batch<false>(a, c0, cstep, beg, end, cb);
+    for (uint32_t i = 0; i < n; ++i) {
+      const uint32_t cp = cb.cp[i];
+      const uint4 task = cb.task[i];
+      const TableDev td = a.tables[task.z];
+      wg_gather<VEC, NC, IF>(a, bk, td, task.z, task.x, task.x + task.y, sm);
+      chunk_store<VEC, NC, false>(a, bk, td.dim, cp, sm);
+      __syncthreads();
+    }
   }
 }
 
@@ -732,36 +782,37 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_fused_kernel(BwdArgs a, Bu
   uint32_t bucket, lb, lg;
   set_pick(S, bk, bucket, lb, lg);
   __shared__ WgSmem<VEC, NC> sm;
+  __shared__ ChunkBatch cb;
   const uint32_t beg = list_begin(a, 4, bucket);
   const uint32_t end = min(list_begin(a, 4, bucket + 1), a.max_chunks);
   uint32_t c, cstep;
   chunk_walk(lb, lg, beg, c, cstep);
-  for (; c < end; c += cstep) {
-    const uint32_t cp = a.chunk_perm ? a.chunk_perm[c] : c;  // position of the chunk taken
-    const uint4 task = a.chunk_task[cp];  // {start, len, table, long index}
-    if (cp < beg || cp >= end || !chunk_ok(a, task) || !long_ok(a, task.w))
-      continue;  // uniform per workgroup; never for valid lists
-    if (a.long_flag && a.long_flag[task.w]) continue;  // a hot row: the contraction's
-    const TableDev td = a.tables[task.z];
-    wg_gather<VEC, NC, IF>(a, bk, td, task.z, task.x, task.x + task.y, sm);
-    chunk_store<VEC, NC, true>(a, bk, td.dim, cp, sm);
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's write-through stores have completed
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const uint32_t old = __hip_atomic_fetch_add(&a.remaining[task.w], 0xffffffffu,
-                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      sm.last = (old == 1u) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (sm.last) {
-      long_update<WD, VEC, NC, true, NT>(a, bk, task.w, sm);
+  for (uint64_t c0 = c; c0 < end; c0 += (uint64_t)kThreads * cstep) {
+    const uint32_t nb = chunk_batch<true>(a, c0, cstep, beg, end, cb);
+    for (uint32_t bi = 0; bi < nb; ++bi) {
+      const uint32_t cp = cb.cp[bi];
+      const uint4 task = cb.task[bi];
+      const TableDev td = a.tables[task.z];
+      wg_gather<VEC, NC, IF>(a, bk, td, task.z, task.x, task.x + task.y, sm);
+      chunk_store<VEC, NC, true>(a, bk, td.dim, cp, sm);
+      __builtin_amdgcn_s_waitcnt(0);  // this thread's write-through stores have completed
+      __syncthreads();
       if (threadIdx.x == 0) {
-        const uint32_t len = a.long_task[task.w].y;
-        __hip_atomic_store(&a.remaining[task.w], (len + kChunk - 1) / kChunk, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t old = __hip_atomic_fetch_add(&a.remaining[task.w], 0xffffffffu,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm.last = (old == 1u) ? 1u : 0u;
       }
+      __syncthreads();
+      if (sm.last) {
+        long_update<WD, VEC, NC, true, NT>(a, bk, task.w, sm);
+        if (threadIdx.x == 0) {
+          const uint32_t len = a.long_task[task.w].y;
+          __hip_atomic_store(&a.remaining[task.w], (len + kChunk - 1) / kChunk, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 
