@@ -27,6 +27,7 @@ constexpr int kBags = 16;
 constexpr int kEMax = 64;
 constexpr int kDMax = 128;
 constexpr int kCountCap = 256;
+constexpr int kCntPitch = kEMax + 4;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
@@ -38,9 +39,46 @@ template <typename IT>
 __global__ __launch_bounds__(kThreads) void fwd_hist_kernel(FwdArgs a, uint32_t E, uint32_t D,
                                                             int mean) {
   __shared__ __attribute__((aligned(16))) _Float16 wt[kDMax][kEMax + 8];  // table transposed: [column][row]
-  __shared__ uint32_t cnt[kBags][kEMax];
-  __shared__ float tile[kBags][kDMax + 4];
+  // counts; a row pitch of 68 words puts the 16 rows that the product's
+  // operand reads take at once in distinct banks (a pitch of 64 put all 16
+  // in one)
+  __shared__ __attribute__((aligned(16))) uint32_t cnt[kBags][kCntPitch];
+  __shared__ __attribute__((aligned(16))) float tile[kBags][kDMax + 4];
   __shared__ uint32_t boff[kBags + 1];  // positions (< 2^31)
+
+  const IT* __restrict__ I = reinterpret_cast<const IT*>(a.indices);
+  const IT* __restrict__ O = reinterpret_cast<const IT*>(a.offsets);
+  const uint32_t N = a.n;
+
+  const uint32_t wave = threadIdx.x / kWave, lane = lane_id();
+  const int64_t ngroups = (a.B + kBags - 1) / kBags;
+  if (a.hist_save && blockIdx.x == 0 && threadIdx.x == 0) {
+    a.hist_hdr[0] = (uint32_t)a.B;
+    a.hist_hdr[1] = a.n;
+  }
+  // this workgroup's groups [g_lo, g_hi): consecutive, so that a group's
+  // first lookup is the previous group's end
+  const int64_t g_lo = ngroups * (int64_t)blockIdx.x / (int64_t)gridDim.x;
+  const int64_t g_hi = ngroups * (int64_t)(blockIdx.x + 1) / (int64_t)gridDim.x;
+  if (g_lo >= g_hi) return;
+  // The first group's boundaries and lookups are issued before the table's
+  // load, whose latency they share; those of each next group as soon as the
+  // current group's end is known, before its counting, so they arrive
+  // meanwhile.  A group's loads: its bag boundaries (bag min(x, nb) for
+  // thread x, every index in range) and its first kPer lookups per thread
+  // from P0 (positions clamped to the last lookup; those past the group's
+  // end are dropped where first used).
+  uint32_t P0;
+  {
+    const int64_t o = (int64_t)O[g_lo * kBags];
+    P0 = (uint32_t)(o < 0 ? 0 : (o > (int64_t)N ? (int64_t)N : o));
+  }
+  int64_t o_next = (int64_t)O[g_lo * kBags + min((int64_t)threadIdx.x,
+                                                  min((int64_t)kBags, a.B - g_lo * kBags))];
+  IT r[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u)
+    r[u] = N > 0 ? I[min(P0 + threadIdx.x + (uint32_t)u * kThreads, N - 1u)] : (IT)0;
 
   const TableDev td = a.tables[0];
   const uint16_t* w = reinterpret_cast<const uint16_t*>(td.w);
@@ -76,47 +114,32 @@ __global__ __launch_bounds__(kThreads) void fwd_hist_kernel(FwdArgs a, uint32_t 
       wt[col][row] = __builtin_bit_cast(_Float16, w[i]);
     }
   }
-  const IT* __restrict__ I = reinterpret_cast<const IT*>(a.indices);
-  const IT* __restrict__ O = reinterpret_cast<const IT*>(a.offsets);
-  const uint32_t N = a.n;
-
-  const uint32_t wave = threadIdx.x / kWave, lane = lane_id();
-  const int64_t ngroups = (a.B + kBags - 1) / kBags;
-  if (a.hist_save && blockIdx.x == 0 && threadIdx.x == 0) {
-    a.hist_hdr[0] = (uint32_t)a.B;
-    a.hist_hdr[1] = a.n;
-  }
-  // this workgroup's groups [g_lo, g_hi): consecutive, so that a group's
-  // first lookup is the previous group's end
-  const int64_t g_lo = ngroups * (int64_t)blockIdx.x / (int64_t)gridDim.x;
-  const int64_t g_hi = ngroups * (int64_t)(blockIdx.x + 1) / (int64_t)gridDim.x;
-  if (g_lo >= g_hi) return;
-  // Loads of the next group are issued before the current group's product
-  // and stores, so they arrive meanwhile: its bag boundaries (bag min(x, nb)
-  // for thread x, every index in range) and its first kPer lookups per
-  // thread from P0 (positions clamped to the last lookup; those past the
-  // group's end are dropped where first used).
-  uint32_t P0;
-  {
-    const int64_t o = (int64_t)O[g_lo * kBags];
-    P0 = (uint32_t)(o < 0 ? 0 : (o > (int64_t)N ? (int64_t)N : o));
-  }
-  int64_t o_next = (int64_t)O[g_lo * kBags + min((int64_t)threadIdx.x,
-                                                  min((int64_t)kBags, a.B - g_lo * kBags))];
-  IT r[kPer];
-#pragma unroll
-  for (int u = 0; u < kPer; ++u)
-    r[u] = N > 0 ? I[min(P0 + threadIdx.x + (uint32_t)u * kThreads, N - 1u)] : (IT)0;
-
   for (int64_t g = g_lo; g < g_hi; ++g) {
     const int64_t b0 = g * kBags;
     const int nb = (int)((a.B - b0) < kBags ? (a.B - b0) : kBags);
     __syncthreads();  // previous group's tile fully stored; table loaded
-    for (uint32_t i = threadIdx.x; i < kBags * kEMax; i += kThreads) (&cnt[0][0])[i] = 0u;
+    for (uint32_t i = threadIdx.x; i < kBags * kCntPitch; i += kThreads) (&cnt[0][0])[i] = 0u;
     if (threadIdx.x <= (uint32_t)kBags)
       boff[threadIdx.x] = (uint32_t)(o_next < 0 ? 0 : (o_next > (int64_t)N ? (int64_t)N : o_next));
     __syncthreads();
     const uint32_t P1 = min(max(boff[nb], P0), N);  // the group's lookups are [P0, P1)
+
+    // the next group's boundaries and first lookups, in flight from here on,
+    // through this group's counting, product and stores
+    const bool more = g + 1 < g_hi;
+    int64_t o_nn = 0;
+    IT rn[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) rn[u] = (IT)0;
+    if (more) {
+      const int64_t nbn = min((int64_t)kBags, a.B - (b0 + kBags));
+      o_nn = (int64_t)O[b0 + kBags + min((int64_t)threadIdx.x, nbn)];
+      if (N > 0) {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u)
+          rn[u] = I[min(P1 + threadIdx.x + (uint32_t)u * kThreads, N - 1u)];
+      }
+    }
 
     // histogram of each bag's first kCountCap lookups: kPer lookups per
     // thread at a time, their bags by a search over the boundaries taken
@@ -154,17 +177,6 @@ __global__ __launch_bounds__(kThreads) void fwd_hist_kernel(FwdArgs a, uint32_t 
     }
     __syncthreads();
 
-    // the next group's boundaries and first lookups, in flight from here on
-    if (g + 1 < g_hi) {
-      const int64_t nbn = min((int64_t)kBags, a.B - (b0 + kBags));
-      o_next = (int64_t)O[b0 + kBags + min((int64_t)threadIdx.x, nbn)];
-      if (N > 0) {
-#pragma unroll
-        for (int u = 0; u < kPer; ++u)
-          r[u] = I[min(P1 + threadIdx.x + (uint32_t)u * kThreads, N - 1u)];
-      }
-    }
-
     // counts[16 x 64] (fp16, exact) x table[64 x D] on MFMA, fp32 accumulate
     {
       const uint32_t i = lane & 15, kq = lane >> 4;  // A row / B column, K group
@@ -172,7 +184,13 @@ __global__ __launch_bounds__(kThreads) void fwd_hist_kernel(FwdArgs a, uint32_t 
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) av[ks][e] = (_Float16)(float)cnt[i][ks * 32 + kq * 8 + e];
+        for (int h = 0; h < 2; ++h) {
+          const uint4 c4 = *reinterpret_cast<const uint4*>(&cnt[i][ks * 32 + kq * 8 + 4 * h]);
+          av[ks][4 * h] = (_Float16)(float)c4.x;
+          av[ks][4 * h + 1] = (_Float16)(float)c4.y;
+          av[ks][4 * h + 2] = (_Float16)(float)c4.z;
+          av[ks][4 * h + 3] = (_Float16)(float)c4.w;
+        }
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const uint32_t col0 = (wave * 2 + nt) * 16;
@@ -213,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void fwd_hist_kernel(FwdArgs a, uint32_t 
     const uint32_t q4 = D / 4;
     for (uint32_t e = threadIdx.x; e < (uint32_t)nb * q4; e += kThreads) {
       const uint32_t bj = e / q4, c4 = (e % q4) * 4;
-      float4 v = make_float4(tile[bj][c4], tile[bj][c4 + 1], tile[bj][c4 + 2], tile[bj][c4 + 3]);
+      float4 v = *reinterpret_cast<const float4*>(&tile[bj][c4]);  // (rows of 528 bytes)
       const int64_t L = (int64_t)boff[bj + 1] - (int64_t)boff[bj];
       if (mean && L > 0) {
         const float fl = (float)L;
@@ -222,6 +240,11 @@ __global__ __launch_bounds__(kThreads) void fwd_hist_kernel(FwdArgs a, uint32_t 
       *reinterpret_cast<float4*>(a.out + (b0 + bj) * (int64_t)a.dtot + c4) = v;
     }
     P0 = P1;
+    if (more) {
+      o_next = o_nn;
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) r[u] = rn[u];
+    }
   }
 }
 
