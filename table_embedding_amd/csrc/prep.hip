@@ -226,10 +226,6 @@ __device__ __forceinline__ uint32_t take_ticket(uint32_t* tickets, uint32_t* s_t
   return *s_tile;
 }
 
-// ------------------------------------------------------------ segments
-// (segment s is table order[s], tables in key order; its lookups are
-// [O[t*B], O[(t+1)*B]))
-
 // ------------------------------------------------------------ transposition
 // The transposition from bag order to row order is folded into the first
 // radix pass.  That pass's input order is the lookups' own order (bags are
@@ -242,8 +238,9 @@ __device__ __forceinline__ uint32_t take_ticket(uint32_t* tickets, uint32_t* s_t
 // Slot i of table t's segment holds position p = O[t*B] + (i - the segment's
 // output base).
 
-// Per segment from the offsets, into dynamic LDS: lookups, output base,
-// first tile and tile count.  Offsets that keep the contract (O[T*B] = N)
+// Per segment (segment s is table order[s], tables in key order; its lookups
+// are [O[t*B], O[(t+1)*B])) from the offsets, into dynamic LDS: lookups,
+// output base, first tile and tile count.  Offsets that keep the contract (O[T*B] = N)
 // are unchanged by the clamps; others still give segments inside [0, N) and
 // at most ntiles_max tiles.  Returns the tile total; ends with a barrier.
 template <typename IT>
