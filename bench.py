@@ -18,8 +18,8 @@ workspace, as the pages report it: forward, backward, sum), and a pass with
 a start and a stop event bound to every kernel dispatch for per-kernel times.
 
 Prints one JSON line: lookups/s (the headline), the roofline of the dominant
-kernel on algorithmic bytes (each stream and unique row once, the byte model
-of the survey's measurement section), step-level byte fractions, per-kernel
+kernel on algorithmic bytes (each stream and unique row once: the step's
+compulsory traffic), step-level byte fractions, per-kernel
 figures, and the single-threaded CPU oracle timed on a bounded sample of the
 same workload (whole tables, one pinned core).
 
@@ -195,8 +195,7 @@ def workload_stats(spec, off, idx):
 
 
 def byte_model(spec, st):
-    """Algorithmic bytes per kernel family and step, the model of the survey's
-    measurement section (unit: one lookup; s_i index bytes, s_w weight bytes,
+    """Algorithmic bytes per kernel family and step (unit: one lookup; s_i index bytes, s_w weight bytes,
     psi = 1 with per-sample weights):
       forward   compulsory N(s_i + 4psi) + (TB+1)s_i + sum_t U_t D_t s_w + B Dtot 4
                 logical    the same with N_t D_t s_w in place of U_t D_t s_w

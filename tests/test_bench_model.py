@@ -1,6 +1,6 @@
 """bench.py's byte model: the per-kernel attribution of the algorithmic
 (each stream and unique row once) and logical bytes sums exactly to the
-step totals of the survey's formulas, and those totals equal the formulas
+step totals of its documented formulas, and those totals equal the formulas
 written out independently here on a tiny hand-checked problem."""
 import numpy as np
 
