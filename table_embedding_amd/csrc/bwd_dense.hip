@@ -22,25 +22,28 @@
 // take none.
 //
 // dense_partial_kernel (dense_w workgroups per table and column group of
-// 64 * DT columns, each a contiguous range of the table's bags): per block of
-// 64 bags, the block's lookups are read coalesced, a lookup of a
-// hot row (found in a small open-addressing table in LDS) finds its bag by
-// binary search over the block's bag boundaries, and one integer LDS atomic
-// adds it to C's count.  Integer counts are exact in any order, so the
-// result does not depend on the atomics' timing.  The block's grad_out
-// operands are loaded into registers first, so they arrive while the counts
-// are built.  Then C^T [hot rows x K bags] x G [K bags x D] on the matrix
-// cores, exact in its products: when no bag of the block has more than 255
-// lookups, every count is an integer of at most 8 bits, exact in bfloat16,
-// and each fp32 gradient is the exact sum of three bfloat16 parts (its
-// significand cut into three 8-bit pieces), so three
-// v_mfma_f32_16x16x32_bf16 per tile give the fp32 products without rounding;
-// otherwise each count is cut into four 8-bit parts and the block takes
-// four such passes.  Either way the products are exact and only the
-// fp32 accumulation rounds.
-// Wave w owns the 16-column tiles [w*DT, (w+1)*DT) for all row tiles, so
-// every grad_out element of the block is loaded once, and the accumulators
-// stay in registers across the workgroup's blocks.  Each workgroup writes its
+// 128 columns, each a contiguous range of the table's bags; eight waves, so
+// that the count pass is shared by more waves and two workgroups per CU
+// keep sixteen waves there): per block of 64 bags, the block's lookups are
+// read coalesced, four consecutive ones per thread; a lookup of a hot row
+// (found in a small open-addressing table in LDS) adds one with an integer
+// LDS atomic to its bag's count, the bag found by binary search over the
+// block's bag boundaries for a thread's first lookup and by stepping on for
+// the next three.  Integer counts are exact in any order, so the result does
+// not depend on the atomics' timing.  The block's grad_out operands are
+// loaded into registers first, so they arrive while the counts are built.
+// Then C^T [hot rows x K bags] x G [K bags x D] on the matrix cores, exact
+// in its products: when no bag of the block has more than 255 lookups,
+// every count is an integer of at most 8 bits, exact in bfloat16 (packed
+// so once per block for all waves), and each fp32 gradient is the exact
+// sum of three bfloat16 parts (its significand cut into three 8-bit
+// pieces), so three v_mfma_f32_16x16x32_bf16 per tile give the fp32
+// products without rounding; otherwise each count is cut into four 8-bit
+// parts and the block takes four such passes.  Either way the products are
+// exact and only the fp32 accumulation rounds.
+// Wave w owns the 16-column tile w of the group for all row tiles, so every
+// grad_out element of the block is loaded once, and the accumulators stay
+// in registers across the workgroup's blocks.  Each workgroup writes its
 // partial rows; the update kernel (bwd.hip) adds the dense_w partials of a
 // row in a fixed order and applies the optimizer.  Every floating-point sum
 // has a data-determined order, so repeated calls give the same bits, and the
@@ -156,29 +159,61 @@ __device__ __forceinline__ uint32_t hash_slot(uint32_t row) {
   return (row * 2654435761u) >> 22;  // top 10 bits
 }
 
-constexpr int kPer = 4;  // lookups per thread in flight in the counting pass
+constexpr int kPer = 4;  // consecutive lookups per thread in the counting pass
+static_assert(kPer == 4, "load_lookups4 loads four lookups");
+
+// Lookups p .. p + 3 (p a multiple of 4) as row ids, positions clamped to
+// the last one before `end`; one 16-byte (int32) or two (int64) vector loads
+// when the indices are 16-byte aligned and all four exist.
+template <typename IT>
+__device__ __forceinline__ void load_lookups4(const IT* __restrict__ I, uint32_t p, uint32_t end,
+                                              bool vec, uint32_t (&rr)[4]) {
+  if (vec && p + 3u < end) {
+    if constexpr (sizeof(IT) == 4) {
+      const int4 v = *reinterpret_cast<const int4*>(I + p);
+      rr[0] = (uint32_t)v.x; rr[1] = (uint32_t)v.y; rr[2] = (uint32_t)v.z; rr[3] = (uint32_t)v.w;
+    } else {
+      const longlong2 v0 = *reinterpret_cast<const longlong2*>(I + p);
+      const longlong2 v1 = *reinterpret_cast<const longlong2*>(I + p + 2u);
+      rr[0] = (uint32_t)v0.x; rr[1] = (uint32_t)v0.y; rr[2] = (uint32_t)v1.x; rr[3] = (uint32_t)v1.y;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) rr[u] = (uint32_t)I[min(p + (uint32_t)u, end - 1u)];
+  }
+}
 constexpr uint32_t kMaxExactCount = 255;  // counts of at most 8 bits are exact in bfloat16
 constexpr int kRowTiles = kDenseRows / 16;
 
-// Bags per block: K of the block's contraction (a lane holds K/4 * DT
-// grad_out operands of the block in registers); a workgroup's columns are
-// one group of 64 * DT (four waves of DT 16-column tiles).
-template <int DT>
+// Bags per block: K of the block's contraction (a lane holds K/4 grad_out
+// operands of the block in registers); a workgroup's columns are one group
+// of kGroupCols: eight waves of one 16-column tile each.
 struct DenseShape {
-  static_assert(DT == 1 || DT == 2, "one or two column tiles per wave");
+  static constexpr int kDT = 1;              // 16-column tiles per wave
+  static constexpr int kNW = 8;              // waves of the workgroup
+  static constexpr int kNT = 64 * kNW;       // threads of the workgroup
+  static constexpr int kWin = kPer * kNT;    // lookups per counting window
   static constexpr int kBags = 64;
   static constexpr int kPitch = kBags + 4;  // count row pitch (words; = 4 mod 64)
+  static constexpr int kPitchB = kBags / 2 + 4;  // bfloat16 count row pitch (words)
   static constexpr int kSteps = kBags / 32; // K steps of 32 bags
-  static constexpr uint32_t kGroupCols = 64u * DT;
+  static constexpr uint32_t kGroupCols = 16u * kDT * kNW;
 };
 
-template <typename IT, int DT>
-__global__ __launch_bounds__(kThreads) void dense_partial_kernel(BwdArgs a) {
-  using S = DenseShape<DT>;
+// Two workgroups per CU (LDS allows two): four waves per SIMD, so at most
+// 128 registers per lane.
+template <typename IT>
+__global__ __launch_bounds__(DenseShape::kNT) __attribute__((amdgpu_waves_per_eu(4)))
+void dense_partial_kernel(BwdArgs a) {
+  using S = DenseShape;
+  constexpr int DT = S::kDT;
   if (dense_prep_failed(a)) return;
   // counts of the block, [hot row][bag] (integer atomic adds: exact in any
   // order); the 16 rows of a tile fall in distinct banks
   __shared__ __attribute__((aligned(16))) uint32_t cnt[kDenseRows][S::kPitch];
+  // the same counts as packed bfloat16 (blocks whose counts fit 8 bits),
+  // converted once for the four waves' operand reads
+  __shared__ __attribute__((aligned(16))) uint32_t cbf[kDenseRows][S::kPitchB];
   __shared__ __attribute__((aligned(16))) float s_inv[S::kBags];  // 1 / bag length (mean)
   __shared__ uint32_t s_key[kHashSlots];
   __shared__ uint8_t s_hrank[kHashSlots];
@@ -195,7 +230,8 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(BwdArgs a) {
   const IT* __restrict__ I = reinterpret_cast<const IT*>(a.indices);
   const IT* __restrict__ O = reinterpret_cast<const IT*>(a.offsets);
   const int64_t N = (int64_t)a.N;
-  for (uint32_t x = threadIdx.x; x < kHashSlots; x += kThreads) s_key[x] = kHashEmpty;
+  const bool vec4 = (reinterpret_cast<uintptr_t>(I) & 15u) == 0;  // uniform
+  for (uint32_t x = threadIdx.x; x < kHashSlots; x += S::kNT) s_key[x] = kHashEmpty;
   if (threadIdx.x == 0) s_dmax = 0;
   __syncthreads();
   if (threadIdx.x < H) {  // the table's hot rows are distinct: one insert each
@@ -238,12 +274,10 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(BwdArgs a) {
     // past the block's end are dropped once its end is known), then grad_out.
     const int64_t o_lo = (int64_t)O[jt + j0 + min(threadIdx.x, nb)];
     const int64_t o_hi = (int64_t)O[jt + j0 + min(threadIdx.x + 1u, nb)];
+    // windows of kWin lookups start at P0 rounded down to a multiple of 4
+    const uint32_t qa = P0 & ~3u;
     uint32_t r[kPer];
-    if (N > 0) {
-#pragma unroll
-      for (int u = 0; u < kPer; ++u)
-        r[u] = (uint32_t)I[min(P0 + threadIdx.x + (uint32_t)u * kThreads, (uint32_t)N - 1u)];
-    }
+    if (N > 0) load_lookups4(I, qa + (uint32_t)kPer * threadIdx.x, (uint32_t)N, vec4, r);
     // the block's grad_out operands of this lane: gv[ks][e][nt] is bag
     // 32 ks + 8 kq + e at column c0 + 16 nt (the B operand layout of the
     // 16x16x32 product), all in flight while the counts are built.  A full
@@ -277,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(BwdArgs a) {
     }
     {  // clear the rows in use
       const uint32_t n4 = nrt * 16u * (uint32_t)S::kPitch / 4u;
-      for (uint32_t x = threadIdx.x; x < n4; x += kThreads)
+      for (uint32_t x = threadIdx.x; x < n4; x += S::kNT)
         reinterpret_cast<uint4*>(&cnt[0][0])[x] = make_uint4(0u, 0u, 0u, 0u);
     }
     // bag boundaries, clamped to the lookups (entries past nb repeat the end
@@ -292,28 +326,26 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(BwdArgs a) {
     const uint32_t dmax = s_dmax;
     const uint32_t P1 = min(max(s_off[nb], (uint32_t)P0), (uint32_t)N);  // the block's lookups are [P0, P1)
     // counting pass (the next window's lookups in flight while this one is
-    // counted): a lookup of a hot row finds its bag by binary search over the
-    // bag boundaries and adds one to its count (integer adds: the same counts
-    // in any order).  The kPer lookups of a thread go through the hash probe
-    // and each search level together, so a level costs one LDS round trip
-    // for all of them.
-    for (uint32_t q0 = P0; q0 < P1; q0 += (uint32_t)(kPer * kThreads)) {
-      // this window's lookups past the block's end are dropped here, where
-      // their values are first needed (not where they are loaded)
+    // counted): a lookup of a hot row adds one to its bag's count (integer
+    // adds: the same counts in any order).  A thread takes kPer consecutive
+    // lookups of the window; the first one's bag is found by binary search
+    // over the bag boundaries and each next one's by stepping on from it.
+    // The kPer lookups go through the hash probe together, so a probe step
+    // costs one LDS round trip for all of them.
+    for (uint32_t q0 = qa; q0 < P1; q0 += (uint32_t)S::kWin) {
+      const uint32_t pb = q0 + (uint32_t)kPer * threadIdx.x;  // this thread's first lookup
+      // lookups outside the block's [P0, P1) are dropped here, where their
+      // values are first needed (not where they are loaded)
 #pragma unroll
       for (int u = 0; u < kPer; ++u)
-        if (q0 + threadIdx.x + (uint32_t)u * kThreads >= P1) r[u] = kHashEmpty;
-      const uint32_t qn = q0 + (uint32_t)(kPer * kThreads);
+        if (pb + (uint32_t)u < P0 || pb + (uint32_t)u >= P1) r[u] = kHashEmpty;
+      const uint32_t qn = q0 + (uint32_t)S::kWin;
       uint32_t rn[kPer];
 #pragma unroll
       for (int u = 0; u < kPer; ++u) rn[u] = kHashEmpty;
-      if (qn < P1) {
-#pragma unroll
-        for (int u = 0; u < kPer; ++u)
-          rn[u] = (uint32_t)I[min(qn + threadIdx.x + (uint32_t)u * kThreads, P1 - 1u)];
-      }
-      // the hot-row slot of each lookup (kHashSlots: not hot, or past the
-      // block: kHashEmpty would match an empty slot, so it is excluded)
+      if (qn < P1) load_lookups4(I, qn + (uint32_t)kPer * threadIdx.x, P1, vec4, rn);
+      // the hot-row slot of each lookup (kHashSlots: not hot, or dropped:
+      // kHashEmpty would match an empty slot, so it is excluded)
       uint32_t slot[kPer];
 #pragma unroll
       for (int u = 0; u < kPer; ++u) slot[u] = kHashSlots;
@@ -324,19 +356,26 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(BwdArgs a) {
           slot[u] = (s_key[q] == r[u] && r[u] != kHashEmpty) ? q : slot[u];
         }
       }
-      // the last bag whose start is at or before p: m < kBags always, and
-      // s_off[m] for m >= nb is the block's end, past every p counted here
+      // the last bag whose start is at or before p (p clamped into the
+      // block, so the walk ends: s_off[m] for m >= nb is the block's end,
+      // past every p counted here, and m < kBags always)
       uint32_t bag[kPer];
+      {
+        const uint32_t p = min(pb, P1 - 1u);
+        uint32_t m0 = 0u;
 #pragma unroll
-      for (int u = 0; u < kPer; ++u) bag[u] = 0u;
-#pragma unroll
-      for (uint32_t step = (uint32_t)S::kBags / 2u; step > 0u; step >>= 1) {
-#pragma unroll
-        for (int u = 0; u < kPer; ++u) {
-          const uint32_t p = q0 + threadIdx.x + (uint32_t)u * kThreads;
-          const uint32_t m = bag[u] + step;
-          bag[u] = s_off[m] <= p ? m : bag[u];
+        for (uint32_t step = (uint32_t)S::kBags / 2u; step > 0u; step >>= 1) {
+          const uint32_t m = m0 + step;
+          m0 = s_off[m] <= p ? m : m0;
         }
+        bag[0] = m0;
+      }
+#pragma unroll
+      for (int u = 1; u < kPer; ++u) {
+        const uint32_t p = min(pb + (uint32_t)u, P1 - 1u);
+        uint32_t m = bag[u - 1];
+        while (m < (uint32_t)S::kBags - 1u && s_off[m + 1u] <= p) ++m;
+        bag[u] = m;
       }
 #pragma unroll
       for (int u = 0; u < kPer; ++u)
@@ -372,12 +411,21 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(BwdArgs a) {
           for (int nt = 0; nt < DT; ++nt) gv[ks][e][nt] *= e < 4 ? i0[e & 3] : i1[e & 3];
       }
     }
-    // C^T [rows, K bags] x G [K bags, this wave's columns], exact products
-    cm_counts_x_grad<S::kSteps, DT, kRowTiles, S::kPitch>(acc, cnt, gv, nrt, wide, i, kq);
+    // C^T [rows, K bags] x G [K bags, this wave's columns], exact products:
+    // the counts packed as bfloat16 once for all four waves, whole when they
+    // fit 8 bits, else in four 8-bit parts, one product pass each
+    const uint32_t nparts = wide ? 4u : 1u;
+    for (uint32_t ap = 0; ap < nparts; ++ap) {
+      if (ap > 0) __syncthreads();  // the previous part's operand reads are done
+      cm_counts_to_bf16<S::kBags, S::kPitch, S::kPitchB>(
+          cnt, cbf, nrt * 16u, wide ? 0xffu << (8u * ap) : 0xffffffffu, threadIdx.x, S::kNT);
+      __syncthreads();
+      cm_bf16_x_grad<S::kSteps, DT, kRowTiles, S::kPitchB>(acc, cbf, gv, nrt, i, kq);
+    }
     P0 = s_off[nb];  // the next block's first lookup
     __syncthreads();  // the counts are cleared (and s_off rewritten) for the next block
   }
-  // partial rows of this workgroup: hot row 16 rt + 4 kq + r, column 16 (wave DT + nt) + i
+  // partial rows of this workgroup: hot row 16 rt + 4 kq + r, column c0 + 16 nt
 #pragma unroll
   for (int rt = 0; rt < kRowTiles; ++rt) {
     if ((uint32_t)rt >= nrt) break;
@@ -396,12 +444,9 @@ __global__ __launch_bounds__(kThreads) void dense_partial_kernel(BwdArgs a) {
 }
 
 template <typename IT>
-hipError_t launch_partial(const BwdArgs& a, int dt, hipStream_t s) {
-  const dim3 grid(a.T * a.dense_w * a.dense_ncg), block(kThreads);
-  if (dt <= 1)
-    TBE_LAUNCH("dense_partial", (dense_partial_kernel<IT, 1>), grid, block, s, a);
-  else
-    TBE_LAUNCH("dense_partial", (dense_partial_kernel<IT, 2>), grid, block, s, a);
+hipError_t launch_partial(const BwdArgs& a, hipStream_t s) {
+  const dim3 grid(a.T * a.dense_w * a.dense_ncg), block(DenseShape::kNT);
+  TBE_LAUNCH("dense_partial", dense_partial_kernel<IT>, grid, block, s, a);
   return hipGetLastError();
 }
 
@@ -409,12 +454,12 @@ hipError_t launch_partial(const BwdArgs& a, int dt, hipStream_t s) {
 
 hipError_t launch_dense_update(const BwdArgs& a, int wd, hipStream_t s);
 
-hipError_t launch_dense(const BwdArgs& a, const uint32_t* tseg, int wd, int itype, int dt,
+hipError_t launch_dense(const BwdArgs& a, const uint32_t* tseg, int wd, int itype,
                         hipStream_t s) {
   if (!a.long_flag || a.T == 0) return hipSuccess;
   TBE_LAUNCH("dense_select", dense_select_kernel, dim3(a.T), dim3(kThreads), s, a, tseg);
-  const hipError_t e = itype == IT_I32 ? launch_partial<int32_t>(a, dt, s)
-                                       : launch_partial<int64_t>(a, dt, s);
+  const hipError_t e = itype == IT_I32 ? launch_partial<int32_t>(a, s)
+                                       : launch_partial<int64_t>(a, s);
   if (e != hipSuccess) return e;
   return launch_dense_update(a, wd, s);
 }

@@ -98,4 +98,81 @@ __device__ __forceinline__ void cm_counts_x_grad(cm_f4 (&acc)[RT][DT], const uin
   }
 }
 
+// The count rows [0, nrows), each count and-ed with `mask` (all bits, or one
+// 8-bit part 0xff << 8k of wider counts: at most 8 significant bits either
+// way, so exact), as packed bfloat16: cbf[row][w] holds bag 2w in its low
+// half and bag 2w + 1 in its high half, the A operand layout below.  The
+// workgroup's threads share the rows; the caller synchronizes before cbf is
+// read.
+template <int K, int P, int PB>
+__device__ __forceinline__ void cm_counts_to_bf16(const uint32_t (*cnt)[P], uint32_t (*cbf)[PB],
+                                                  uint32_t nrows, uint32_t mask, uint32_t tid,
+                                                  uint32_t nthreads) {
+  static_assert(K % 8 == 0 && P % 4 == 0 && PB % 4 == 0, "16-byte row pieces");
+  constexpr uint32_t kPieces = K / 8;  // 8 counts in, 4 words out
+  for (uint32_t x = tid; x < nrows * kPieces; x += nthreads) {
+    const uint32_t row = x / kPieces, q = x % kPieces;
+    const cm_u32x4 n0 = *reinterpret_cast<const cm_u32x4*>(&cnt[row][8u * q]);
+    const cm_u32x4 n1 = *reinterpret_cast<const cm_u32x4*>(&cnt[row][8u * q + 4u]);
+    cm_u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float c0 = (float)((j < 2 ? n0[2 * j] : n1[2 * j - 4]) & mask);
+      const float c1 = (float)((j < 2 ? n0[2 * j + 1] : n1[2 * j - 3]) & mask);
+      o[j] = (__float_as_uint(c0) >> 16) | (__float_as_uint(c1) & 0xffff0000u);
+    }
+    *reinterpret_cast<cm_u32x4*>(&cbf[row][4u * q]) = o;
+  }
+}
+
+// As cm_counts_x_grad for counts already packed as bfloat16 by
+// cm_counts_to_bf16 (row pitch PB words): each accumulator takes the lo,
+// mid and hi products in that order, as there, so the sums are the same bit
+// for bit.  Row tiles go four at a time, their products issued part by part
+// across the four, so consecutive products never wait for each other's
+// accumulator.  (Tiles past nrt in a group have zero operands: their rows
+// exist in the accumulators and are not stored.)
+template <int KSTEPS, int DT, int RT, int PB>
+__device__ __forceinline__ void cm_bf16_x_grad(cm_f4 (&acc)[RT][DT], const uint32_t (*cbf)[PB],
+                                               const float (&gv)[KSTEPS][8][DT], uint32_t nrt,
+                                               uint32_t i, uint32_t kq) {
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    cm_u32x4 bp[3][DT];  // lo, mid, hi
+#pragma unroll
+    for (int nt = 0; nt < DT; ++nt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t h, m, l;
+        cm_split3(gv[ks][2 * j][nt], gv[ks][2 * j + 1][nt], h, m, l);
+        bp[0][nt][j] = l;
+        bp[1][nt][j] = m;
+        bp[2][nt][j] = h;
+      }
+    // row tiles in groups of four: four operands in registers, and twelve
+    // products per group of which each waits only for the one four back
+    static_assert(RT % 4 == 0, "row tiles in groups of four");
+#pragma unroll
+    for (int g = 0; g < RT; g += 4) {
+      if ((uint32_t)g >= nrt) break;  // uniform
+      cm_u32x4 av[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        av[r] = (uint32_t)(g + r) < nrt
+                    ? *reinterpret_cast<const cm_u32x4*>(
+                          &cbf[(uint32_t)(g + r) * 16u + i][16u * (uint32_t)ks + 4u * kq])
+                    : (cm_u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int part = 0; part < 3; ++part)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int nt = 0; nt < DT; ++nt)
+            acc[g + r][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(cm_bf16x8, av[r]), __builtin_bit_cast(cm_bf16x8, bp[part][nt]),
+                acc[g + r][nt], 0, 0, 0);
+    }
+  }
+}
+
 }  // namespace tbe

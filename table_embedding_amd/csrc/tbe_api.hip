@@ -74,8 +74,8 @@ struct tbe_plan {
   uint32_t* d_bkb;
   void* d_mem;
   int num_cus;
-  int dense_dt;   // hot-row contraction: 16-column tiles per wave (0: no table can take it)
-  int dense_ncg;  // and column groups of 64 * dense_dt columns
+  int dense_on;   // hot-row contraction: 1 if some table can take it
+  int dense_ncg;  // and its column groups of 128 columns
   int dense_w;    // and workgroups per table and column group (bag ranges)
   // backward fork/join: two default-priority side streams and their events;
   // the lock keeps the record/wait sequence of one call from interleaving
@@ -201,7 +201,7 @@ WsLayout layout(const tbe_plan* P, int64_t N) {
   // the hot-row contraction's lists, for batches large enough to take it
   // (the same lookup threshold as the backward's; with a smaller batch the
   // regions are empty and the backward never takes the contraction)
-  const bool dc = P->dense_dt > 0 && N >= knob_dense_lookups();
+  const bool dc = P->dense_on && N >= knob_dense_lookups();
   L.dense = dc;
   L.long_flag = take(dc ? (size_t)L.max_long * 4 : 0);
   L.dense_rows = take(dc ? (size_t)P->T * kDenseRows * 16 : 0);
@@ -499,7 +499,7 @@ int tbe_plan_create(tbe_plan** out, int32_t T, const int64_t* rows, const int32_
     int dmax = 0;
     for (int t = 0; t < T; ++t)
       if (dims[t] % 16 == 0 && dims[t] <= kDensePitch) dmax = std::max(dmax, (int)dims[t]);
-    P->dense_dt = (T > kDenseMaxTables || dmax == 0) ? 0 : dmax <= 64 ? 1 : 2;
+    P->dense_on = (T > kDenseMaxTables || dmax == 0) ? 0 : 1;
     P->dense_ncg = dmax > 128 ? 2 : 1;
     P->dense_w = std::max(kDenseWgsPerTable, kDenseMinWgs / std::max(1, (int)T));
   }
@@ -971,7 +971,7 @@ int run_backward(const tbe_plan* P, int64_t B, int32_t itype, const void* indice
     a.dense_min_len = (uint32_t)std::max<int64_t>(kLongRun, std::min<int64_t>(B / 256, 1ll << 30));
   }
   int rc_launch = TBE_OK;
-  if (dense && launch_dense(a, P->d_tseg, P->wdtype, itype, P->dense_dt, ss[2]) != hipSuccess)
+  if (dense && launch_dense(a, P->d_tseg, P->wdtype, itype, ss[2]) != hipSuccess)
     rc_launch = TBE_E_HIP;
   if (launch_chunk_order(a, ss[2]) != hipSuccess) rc_launch = TBE_E_HIP;
   for (const auto& grp : bucket_groups(P)) {

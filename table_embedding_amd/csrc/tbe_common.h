@@ -527,7 +527,7 @@ struct BwdArgs {
   uint32_t* dense_cnt;       // T: hot rows per table
   float* dense_part;         // T x kDenseRows x dense_w partial rows of kDensePitch floats
   uint32_t dense_w;          // workgroups per table and column group of the contraction
-  uint32_t dense_ncg;        // column groups of the contraction (64 * dense_dt columns each)
+  uint32_t dense_ncg;        // column groups of the contraction (128 columns each)
   uint32_t dense_min_len;    // smallest run length the contraction takes
 };
 
@@ -606,8 +606,7 @@ hipError_t launch_chunk_order(const BwdArgs& a, hipStream_t s);
 // The hot-row contraction (a.long_flag set): selection of each table's hot
 // rows (tseg: segment of each table in key order), the contraction's
 // partials, and the rows' update (optimizer a.opt, weight storage wd).
-// dt: 16-column tiles per wave (the widest eligible D / 64, rounded up to 1, 2 or 4).
-hipError_t launch_dense(const BwdArgs& a, const uint32_t* tseg, int wd, int itype, int dt,
+hipError_t launch_dense(const BwdArgs& a, const uint32_t* tseg, int wd, int itype,
                         hipStream_t s);
 // The update of each hot row from its partials (in bwd.hip, beside the other
 // row updates).
