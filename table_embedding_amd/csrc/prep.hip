@@ -207,6 +207,25 @@ __device__ __forceinline__ void loadn(const uint32_t* __restrict__ a, uint64_t i
   }
 }
 
+// NI consecutive values a[i0 .. i0+NI-1] of a workspace array (i0 a multiple
+// of NI, NI * 4 bytes dividing kWsAlign) as 16-byte loads, also where the
+// group runs past the array's last entry: the array ends on a kWsAlign
+// boundary, so the group does too, and entries past the end are whatever
+// the padding holds.  (Clamping each entry instead, as loadn does, let the
+// compiler turn every group into 4-byte loads, one 64-byte line per lane
+// and instruction.)
+template <int NI>
+__device__ __forceinline__ void load_ws_group(const uint32_t* __restrict__ a, uint64_t i0,
+                                              uint32_t* v) {
+  static_assert(NI % 4 == 0 && kWsAlign % (NI * 4) == 0, "groups tile the padded array");
+  const uint4* p = reinterpret_cast<const uint4*>(a + i0);
+#pragma unroll
+  for (int q = 0; q < NI / 4; ++q) {
+    const uint4 x = p[q];
+    v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
+  }
+}
+
 // The workgroup's tile number, in the order workgroups start.  One counter
 // per class c = workgroup index mod 8, and tile = 8 * ticket + c: workgroups
 // go to the eight XCDs round-robin by index, so a class is an XCD, and one
@@ -824,23 +843,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   __shared__ uint32_t s_tile, s_excl;
   __shared__ uint32_t s_rs[kTile], s_rk[kTile];  // one group's run heads, staged
   const uint32_t tile = take_ticket(ticket, &s_tile);
-  uint32_t k[G][kItems];
+  uint32_t k[G][kItems], prev0[G];
   uint32_t m[G];  // run heads among this thread's 16 slots of each group
+  // every group's keys in flight before any is used (a group that starts
+  // at or past N loads nothing; slots past N are not counted)
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const uint64_t i0 = (uint64_t)tile * (G * kTile) + (uint64_t)g * kTile +
+                        (uint64_t)threadIdx.x * kItems;
+    prev0[g] = (i0 == 0 || i0 > N) ? 0u : key[i0 - 1];
+    if (i0 < N) {
+      load_ws_group<kItems>(key, i0, k[g]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kItems; ++e) k[g][e] = 0u;
+    }
+  }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const uint64_t i0 = (uint64_t)tile * (G * kTile) + (uint64_t)g * kTile +
                         (uint64_t)threadIdx.x * kItems;
     m[g] = 0;
-    if (i0 < N) {
-      const uint32_t prev0 = i0 == 0 ? 0u : key[i0 - 1];
-      loadn<kItems>(key, i0, N, k[g]);
-      uint32_t prev = prev0;
+    uint32_t prev = prev0[g];
 #pragma unroll
-      for (int e = 0; e < kItems; ++e) {
-        const uint64_t i = i0 + e;
-        if (i < N && (i == 0 || k[g][e] != prev)) m[g] |= 1u << e;
-        prev = k[g][e];
-      }
+    for (int e = 0; e < kItems; ++e) {
+      const uint64_t i = i0 + e;
+      if (i < N && (i == 0 || k[g][e] != prev)) m[g] |= 1u << e;
+      prev = k[g][e];
     }
   }
   uint32_t local[G], gbase[G + 1], total = 0;

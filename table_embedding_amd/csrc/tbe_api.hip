@@ -87,7 +87,7 @@ struct tbe_plan {
 
 namespace {
 
-constexpr size_t kAlign = 256;
+constexpr size_t kAlign = kWsAlign;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 

@@ -19,6 +19,10 @@ constexpr int kClsTile = 2048;      // runs per workgroup in the classification 
 // Measured on MI355X (run-length pass per step, four groups / one): 2.1 M
 // lookups 17.0 / 11.1 us, 17 M 51.3 / 46.8 us.
 constexpr int kRleGroupsDeep = 4;
+// Workspace arrays start and end on multiples of this many bytes (each one's
+// size is rounded up), so a 64-byte vector load of an aligned group that
+// starts inside an array ends inside it.
+constexpr size_t kWsAlign = 256;
 constexpr int64_t kRleDeepLookups = 64ll << 20;
 // Lookup counts from which the backward gathers keep eight lookups in flight
 // and streams its weight rows past the caches (see bwd.hip for the
