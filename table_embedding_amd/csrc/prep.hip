@@ -188,32 +188,13 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh4, u
   return wp + x - v;
 }
 
-// NI consecutive values a[i0 .. i0+NI-1] (i0 a multiple of NI, NI a multiple
-// of 4); entries at or past n repeat a[n-1] (n >= 1).  16-byte loads for a
-// full group.
-template <int NI>
-__device__ __forceinline__ void loadn(const uint32_t* __restrict__ a, uint64_t i0, uint64_t n,
-                                      uint32_t* v) {
-  if (i0 + NI <= n) {
-    const uint4* p = reinterpret_cast<const uint4*>(a + i0);
-#pragma unroll
-    for (int q = 0; q < NI / 4; ++q) {
-      const uint4 x = p[q];
-      v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < NI; ++e) v[e] = a[(i0 + e < n) ? i0 + e : n - 1];
-  }
-}
-
 // NI consecutive values a[i0 .. i0+NI-1] of a workspace array (i0 a multiple
 // of NI, NI * 4 bytes dividing kWsAlign) as 16-byte loads, also where the
 // group runs past the array's last entry: the array ends on a kWsAlign
-// boundary, so the group does too, and entries past the end are whatever
-// the padding holds.  (Clamping each entry instead, as loadn does, let the
-// compiler turn every group into 4-byte loads, one 64-byte line per lane
-// and instruction.)
+// boundary, so a group that starts inside it ends inside it, and entries
+// past the end are whatever the padding holds.  (Clamping each entry's
+// position instead let the compiler turn every group into 4-byte loads,
+// one 64-byte line per lane and instruction.)
 template <int NI>
 __device__ __forceinline__ void load_ws_group(const uint32_t* __restrict__ a, uint64_t i0,
                                               uint32_t* v) {
@@ -224,6 +205,18 @@ __device__ __forceinline__ void load_ws_group(const uint32_t* __restrict__ a, ui
     const uint4 x = p[q];
     v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
   }
+}
+
+// As load_ws_group for a group that starts below n (n entries in use), with
+// the entries at or past n replaced by a[n - 1].
+template <int NI>
+__device__ __forceinline__ void loadn(const uint32_t* __restrict__ a, uint64_t i0, uint64_t n,
+                                      uint32_t* v) {
+  load_ws_group<NI>(a, i0, v);
+  const uint32_t last = a[n - 1];  // (loaded by every lane: no branch holds
+                                   // back the loads that follow)
+#pragma unroll
+  for (int e = 0; e < NI; ++e) v[e] = i0 + e < n ? v[e] : last;
 }
 
 // The workgroup's tile number, in the order workgroups start.  One counter
@@ -959,13 +952,11 @@ __device__ __forceinline__ void run_class(uint32_t len, uint32_t* c) {
   c[4] = lg ? (len + kChunk - 1) / kChunk : 0u;
 }
 
-// lengths of runs u0 .. u0+kClsItems-1 (0 past U): run_start has U+1 entries
-__device__ __forceinline__ void run_lengths(const uint32_t* __restrict__ run_start, uint64_t u0,
+// lengths of runs u0 .. u0+kClsItems-1 (0 past U) from their starts s (run
+// u0 + e starts at s[e]; last: the start after them), run_start having U+1
+// entries
+__device__ __forceinline__ void run_lengths(const uint32_t* s, uint32_t last, uint64_t u0,
                                             uint32_t U, uint32_t* start, uint32_t* len) {
-  uint32_t s[kClsItems];
-  loadn<kClsItems>(run_start, u0, (uint64_t)U + 1, s);
-  const uint32_t last = run_start[(u0 + kClsItems <= U) ? u0 + kClsItems : U];
-  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int e = 0; e < kClsItems; ++e) {
     const uint32_t nxt = e + 1 < kClsItems ? s[e + 1] : last;
@@ -1020,9 +1011,14 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClsDev a) {
   uint32_t keyprev = 0;
   const bool mine = u0 < U;
   if (mine) {
-    run_lengths(a.run_start, u0, U, start, len);
+    // the run starts, keys, the next start and the key before, all in flight
+    // together, then the lengths
+    uint32_t s[kClsItems];
+    loadn<kClsItems>(a.run_start, u0, (uint64_t)U + 1, s);
     loadn<kClsItems>(a.run_key, u0, U, key);
+    const uint32_t last = a.run_start[(u0 + kClsItems <= U) ? u0 + kClsItems : U];
     keyprev = u0 == 0 ? 0u : a.run_key[u0 - 1];
+    run_lengths(s, last, u0, U, start, len);
 #pragma unroll
     for (int e = 0; e < kClsItems; ++e) bag0[e] = a.sorted_bag[start[e] < a.N ? start[e] : a.N - 1];
   }
