@@ -479,10 +479,12 @@ __global__ __launch_bounds__(kThreads) void first_upsweep(PrepDev a,
     const int64_t pshift = (int64_t)a.seg2[sid].x - (int64_t)sg.y;
     const uint32_t wb = b + wave * (kTile / 4);
     uint32_t k[kItems];
+    // (slots past e read slot e - 1's lookup: no branch, so all 16 loads are
+    // in flight together; they are not counted)
 #pragma unroll
     for (int r = 0; r < kItems; ++r) {
       const uint32_t i = wb + (uint32_t)r * kWave + lane;
-      k[r] = i < e ? index_lo<IT>(a.indices, slot_pos(pshift, i, a.N)) : 0u;
+      k[r] = index_lo<IT>(a.indices, slot_pos(pshift, i < e ? i : e - 1u, a.N));
     }
 #pragma unroll
     for (int r = 0; r < kItems; ++r)
