@@ -412,6 +412,28 @@ __device__ __forceinline__ void count_digit(uint32_t (*h)[R], uint32_t d, bool v
   }
 }
 
+// As count_digit for items whose equal digits tend to sit in neighbouring
+// lanes (a pass after the first: its keys are sorted by the digits below, so
+// the many copies of a hot row's key are close together): a stretch of lanes
+// with one digit adds its length with one atomic from its last lane.
+template <int R>
+__device__ __forceinline__ void count_digit_runs(uint32_t (*h)[R], uint32_t d, bool valid,
+                                                 uint32_t lane) {
+  const uint32_t dp = __shfl_up(d, 1, kWave);
+  const uint64_t in = __ballot(valid);
+  const bool pv = lane > 0 && ((in >> (lane - 1)) & 1ull);
+  const bool cont = valid && pv && dp == d;  // continues the stretch of lane - 1
+  const uint64_t cm = __ballot(cont);
+  const bool last = valid && (lane == kWave - 1 || ((cm >> (lane + 1)) & 1ull) == 0);
+  if (last) {
+    // the stretch's first lane: the highest lane at or below this one that
+    // does not continue its predecessor
+    const uint64_t heads = in & ~cm & (lane == kWave - 1 ? ~0ull : ((2ull << lane) - 1ull));
+    const uint32_t first = 63u - (uint32_t)__clzll(heads);
+    atomicAdd(&h[lane & 3u][d], lane - first + 1u);
+  }
+}
+
 // Counts of each digit value of one pass for every tile of the pass's input,
 // digit-major: cnt[d * ntiles + tile], digits of DB bits of the row
 // (key - key_base), counted by count_digit.  With nst > 0 the kernel also
@@ -437,15 +459,17 @@ __global__ __launch_bounds__(kThreads) void radix_upsweep(const uint32_t* __rest
     const uint4 sg = tile_span(seg, tile_seg, tile, sid, b, e);
     const uint32_t wb = b + wave * (kTile / 4);
     uint32_t k[kItems];
+    // (slots past e read slot e - 1: no branch around the loads; they are
+    // not counted)
 #pragma unroll
     for (int r = 0; r < kItems; ++r) {
       const uint32_t i = wb + (uint32_t)r * kWave + lane;
-      k[r] = i < e ? keys[i] : 0u;
+      k[r] = keys[i < e ? i : e - 1u];
     }
 #pragma unroll
     for (int r = 0; r < kItems; ++r)
-      count_digit<R>(h, ((k[r] - sg.w) >> shift) & (R - 1u),
-                     wb + (uint32_t)r * kWave + lane < e, lane);
+      count_digit_runs<R>(h, ((k[r] - sg.w) >> shift) & (R - 1u),
+                          wb + (uint32_t)r * kWave + lane < e, lane);
   }
   __syncthreads();
   if (live)
