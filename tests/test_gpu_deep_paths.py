@@ -84,6 +84,31 @@ def test_deep_batch_variants_parity(name, variant):
         assert res[0] == res[1], "fused differs from two-launch"
 
 
+@pytest.mark.parametrize("name", ["dense_many", "dense_mean"])
+def test_dense_unaligned_indices_bitwise(name):
+    """The contraction reads four lookups at once with 16-byte loads only when
+    the indices are 16-byte aligned; indices one element off that alignment
+    (legal: the boundary asks for element alignment) take element loads and
+    give the same bits."""
+    _announce(name, "dense, unaligned indices")
+    case = S.Case(_spec(name), m_nonzero=True)
+    spec = case.spec
+    buf = torch.empty(case.N + 1, dtype=case.d_idx.dtype, device="cuda")
+    buf[1:].copy_(case.d_idx)
+    idx_u = buf[1:]
+    assert idx_u.data_ptr() % 16 != 0 and idx_u.is_contiguous()
+    res = []
+    with knobs(dense=0):
+        for idx in (case.d_idx, idx_u):
+            case.reset_tables()
+            tb = case.tbe()
+            tb.backward(spec.B, idx, case.d_off, case.d_psw, case.d_G, spec.lr, spec.eps)
+            torch.cuda.synchronize()
+            res.append(_tables_bytes(tb, spec.wdtype))
+            tb.close()
+    assert res[0] == res[1], "unaligned indices changed the contraction's result"
+
+
 @pytest.mark.parametrize("name", ["C2s", "C3s", "C5s"])
 def test_wait_give_up_writes_nothing(name):
     """Poll limit 0: every tile with predecessors gives up its look-back at
