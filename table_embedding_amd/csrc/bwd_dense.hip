@@ -211,8 +211,8 @@ void dense_partial_kernel(BwdArgs a) {
   // counts of the block, [hot row][bag] (integer atomic adds: exact in any
   // order); the 16 rows of a tile fall in distinct banks
   __shared__ __attribute__((aligned(16))) uint32_t cnt[kDenseRows][S::kPitch];
-  // the same counts as packed bfloat16 (blocks whose counts fit 8 bits),
-  // converted once for the four waves' operand reads
+  // the counts (or one 8-bit part of them, in a block with wider counts) as
+  // packed bfloat16, converted once per block for all waves' operand reads
   __shared__ __attribute__((aligned(16))) uint32_t cbf[kDenseRows][S::kPitchB];
   __shared__ __attribute__((aligned(16))) float s_inv[S::kBags];  // 1 / bag length (mean)
   __shared__ uint32_t s_key[kHashSlots];
@@ -412,7 +412,7 @@ void dense_partial_kernel(BwdArgs a) {
       }
     }
     // C^T [rows, K bags] x G [K bags, this wave's columns], exact products:
-    // the counts packed as bfloat16 once for all four waves, whole when they
+    // the counts packed as bfloat16 once for all the waves, whole when they
     // fit 8 bits, else in four 8-bit parts, one product pass each
     const uint32_t nparts = wide ? 4u : 1u;
     for (uint32_t ap = 0; ap < nparts; ++ap) {
