@@ -407,11 +407,11 @@ int tbe_prof_calibrate(int32_t launches, void* stream);
  * are in flight, or between tbe_workspace_size and the calls that use the
  * workspace, is not supported.  Errors: TBE_E_ARG for an unknown knob. */
 #define TBE_KNOB_RLE_DEEP_LOOKUPS 1   /* run-length tiles of four 4096-key groups from this
-                                         many lookups on (default 64 Mi) */
+                                         many lookups on (default 8 Mi) */
 #define TBE_KNOB_BWD_DEEP_LOOKUPS 2   /* backward gathers with eight lookups in flight and
                                          streamed weight rows from here on (default 64 Mi) */
 #define TBE_KNOB_BWD_STREAM_LOOKUPS 3 /* streamed (non-temporal) weight rows in the backward
-                                         from here on (default 8 Mi) */
+                                         from here on (default 1 Mi) */
 #define TBE_KNOB_WAIT_POLLS 4         /* polls before a look-back wait gives up (default
                                          2^20; 0: a tile with predecessors gives up at once) */
 #define TBE_KNOB_DENSE_LOOKUPS 5      /* the hot-row contraction of long runs from this many

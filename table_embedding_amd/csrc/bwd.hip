@@ -963,9 +963,10 @@ void launch_classes(const BwdArgs& a, BucketSet S, const BwdGrids* g, bool fused
 // step, and as ordinary accesses those lines push the grad_out rows that the
 // gathers reuse out of the caches.  Measured on MI355X (ms per step, plain /
 // non-temporal): 138 M lookups 17.01 / 16.52 (single-lookup runs 3288 ->
-// 2842 us), 17 M 2.204 / 2.176, but 2.1 M 0.338 / 0.339: there the next
-// forward re-reads the hot rows the backward wrote (forward 36.5 -> 42.3 us),
-// which non-temporal stores leave out of the caches.
+// 2842 us), 17 M 2.204 / 2.176, and, with cold caches before each step,
+// 2.1 M 0.364 / 0.351 (warm steps back to back, where the next forward
+// re-reads the hot rows the backward wrote, had measured 0.338 / 0.339 on
+// earlier kernels).
 
 template <int WD, int VEC, int NC>
 hipError_t launch(const BwdArgs& a, BucketSet S, const BwdGrids* g, bool fused, int cus,

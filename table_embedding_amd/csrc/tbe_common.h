@@ -17,18 +17,18 @@ constexpr int kClsTile = 2048;      // runs per workgroup in the classification 
 // 4096-key groups per run-length tile: four from kRleDeepLookups lookups on
 // (the look-back chain a quarter as long), else one (more workgroups).
 // Measured on MI355X (run-length pass per step, four groups / one): 2.1 M
-// lookups 17.0 / 11.1 us, 17 M 51.3 / 46.8 us.
+// lookups 11.6 / 10.7 us, 17 M 32.6 / 45.5 us.
 constexpr int kRleGroupsDeep = 4;
 // Workspace arrays start and end on multiples of this many bytes (each one's
 // size is rounded up), so a 64-byte vector load of an aligned group that
 // starts inside an array ends inside it.
 constexpr size_t kWsAlign = 256;
-constexpr int64_t kRleDeepLookups = 64ll << 20;
+constexpr int64_t kRleDeepLookups = 8ll << 20;
 // Lookup counts from which the backward gathers keep eight lookups in flight
 // and streams its weight rows past the caches (see bwd.hip for the
 // measurements behind both).
 constexpr int64_t kBwdDeepLookups = 64ll << 20;
-constexpr int64_t kBwdStreamRowsLookups = 8ll << 20;
+constexpr int64_t kBwdStreamRowsLookups = 1ll << 20;
 // Polls after which a look-back wait of the preprocessing gives up.
 constexpr uint32_t kSpinLimit = 1u << 20;
 // Lookup count from which the backward updates the hottest long runs by the

@@ -1,7 +1,7 @@
 """The variants the library picks for deep batches (64 Mi lookups and more:
-run-length tiles of four 4096-key groups, backward gathers with eight
-lookups in flight, non-temporal weight rows; 8 Mi and more: non-temporal rows
-alone), run at scaled sizes through the test knobs and compared with the
+backward gathers with eight lookups in flight and non-temporal weight rows;
+8 Mi and more: run-length tiles of four 4096-key groups; 1 Mi and more:
+non-temporal rows alone), run at scaled sizes through the test knobs and compared with the
 oracle like every other case: integer outputs of the preprocessing bit for
 bit, weights and momentum within tolerance, fused = two-launch bit for bit.
 
